@@ -1,0 +1,104 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the oracle checks.
+
+Holds no arithmetic of the attention method: it only draws random tensors.
+
+Distribution: every input tensor is i.i.d. normal times ``std``; the default
+``std = 1/sqrt(d)`` follows the data generator in the equinox issue
+"Flash Attention" (#732), which draws (batch, heads, seq, dim) normals scaled
+by one over the square root of the embedding size. Values are drawn in float32
+from a CPU ``torch.Generator`` and then rounded (round-to-nearest-even) to the
+working dtype, so the GPU and the oracle see identical values.
+
+Draw order (fixed): q, k, v, tq, tk, tv, then the boolean mask, the additive
+mask, then the cotangents do, dto.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    """A named attention problem: shapes, dtype, masking and input spread."""
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool = False
+    mask_kind: str = "none"        # "none" | "bool" | "additive"
+    std: float | None = None       # None -> 1/sqrt(d)
+    seed: int = 0
+    Nk: int | None = None          # None -> N (self-attention)
+    mask_heads: int = 1            # mask head extent (1 = broadcast over heads)
+    keep: float = 0.9              # Bernoulli keep rate of the boolean mask
+    extra: dict = field(default_factory=dict, compare=False)
+
+    @property
+    def nk(self) -> int:
+        return self.N if self.Nk is None else self.Nk
+
+    @property
+    def sigma(self) -> float:
+        return 1.0 / math.sqrt(self.d) if self.std is None else self.std
+
+
+# The five workloads the method is measured on, plus the seq-length sweep.
+TINY = Workload("tiny", B=1, H=2, N=32, d=64, dtype="f32", seed=0)
+SEQ_NS = (32, 64, 128, 256, 512, 1024, 2048)
+
+
+def seq(N: int, causal: bool, dtype: str = "f16", seed: int = 1) -> Workload:
+    return Workload(f"seq_N{N}_{'causal' if causal else 'full'}_{dtype}", B=2, H=8, N=N, d=64,
+                    dtype=dtype, causal=causal, seed=seed)
+
+
+MASKED_BOOL = Workload("masked_bool", B=2, H=8, N=1024, d=64, dtype="f16", mask_kind="bool", seed=2)
+MASKED_ADD = Workload("masked_additive", B=2, H=8, N=1024, d=64, dtype="f16", mask_kind="additive",
+                      seed=2)
+WIDE = Workload("wide", B=256, H=8, N=512, d=128, dtype="bf16", seed=3)
+HVP = Workload("hvp", B=4, H=16, N=2048, d=64, dtype="bf16", causal=True, seed=4)
+
+
+def make_inputs(w: Workload, cotangents: bool = False) -> dict:
+    """Draw the inputs of workload ``w`` on the CPU.
+
+    Returns a dict of CPU tensors: q, k, v, tq, tk, tv in the working dtype
+    ([B,H,N,d] / [B,H,Nk,d]); ``mask`` ([B, mask_heads, N, Nk]; uint8 with 1 =
+    attend for "bool", the working dtype for "additive"; None for "none");
+    and when ``cotangents`` is set, ``do`` and ``dto`` (i.i.d. N(0,1)).
+    """
+    dt = DTYPES[w.dtype]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+    qshape = (w.B, w.H, w.N, w.d)
+    kshape = (w.B, w.H, w.nk, w.d)
+    out = {}
+    for name, shape in (("q", qshape), ("k", kshape), ("v", kshape),
+                        ("tq", qshape), ("tk", kshape), ("tv", kshape)):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        x.mul_(w.sigma)
+        out[name] = x.to(dt)
+    mshape = (w.B, w.mask_heads, w.N, w.nk)
+    mask = None
+    if w.mask_kind == "bool":
+        keep = torch.rand(mshape, generator=g, dtype=torch.float32) < w.keep
+        n = min(w.N, w.nk)
+        idx = torch.arange(n)
+        keep[:, :, idx, idx] = True     # every query keeps at least its own key
+        mask = keep.to(torch.uint8)
+    elif w.mask_kind == "additive":
+        mask = torch.randn(mshape, generator=g, dtype=torch.float32).to(dt)
+    elif w.mask_kind != "none":
+        raise ValueError(f"unknown mask kind {w.mask_kind!r}")
+    out["mask"] = mask
+    if cotangents:
+        out["do"] = torch.randn(qshape, generator=g, dtype=torch.float32).to(dt)
+        out["dto"] = torch.randn(qshape, generator=g, dtype=torch.float32).to(dt)
+    return out

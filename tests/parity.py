@@ -1,0 +1,63 @@
+"""Comparison bars for GPU results against the float64 oracle.
+
+Two bars apply to O and dO at once:
+  * the absolute bar the method is specified with: max-abs error <= 2e-3 for
+    float32 inputs and <= 1e-2 for bfloat16 / float16 inputs;
+  * a scale-free bar, max-abs error <= rho * max|reference|, with rho = 2^-6
+    (bf16), 2^-8 (fp16), 1e-4 (fp32). It is what gives the stress inputs
+    (unit and doubled spread) their power: at the 1/sqrt(d) spread every
+    output is below 1e-2 and the absolute bar alone would pass an all-zero
+    result. rho is 4x the unit roundoff of the working type (bf16: 2^-8, fp16:
+    2^-10 for the rounded softmax weights and outputs), covering the
+    rounding of P and P*dS to the input type before the value products plus
+    the final rounding of O and dO; fp32 has no such rounding step and keeps
+    1e-4 for accumulation order.
+lse: absolute error <= 1e-3 (16-bit) / 1e-5 (fp32), and -inf exactly where the
+reference is -inf (fully masked rows). tlse: the same two bars as dO.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ABS_TOL = {"f32": 2e-3, "f16": 1e-2, "bf16": 1e-2}
+RHO = {"f32": 1e-4, "f16": 2.0 ** -8, "bf16": 2.0 ** -6}
+LSE_TOL = {"f32": 1e-5, "f16": 1e-3, "bf16": 1e-3}
+
+
+def _np(x):
+    if hasattr(x, "detach"):
+        x = x.detach().float().cpu().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def errors(got: dict, ref: dict, dtype: str) -> dict:
+    """Per-output (max-abs error, bar); keys o, to, lse, tlse present in both."""
+    out = {}
+    for name in ("o", "to", "tlse"):
+        if name not in got or got[name] is None:
+            continue
+        g, r = _np(got[name]), _np(ref[name])
+        if not np.all(np.isfinite(g)):
+            out[name] = (float("inf"), 0.0)
+            continue
+        err = float(np.max(np.abs(g - r))) if g.size else 0.0
+        bar = min(ABS_TOL[dtype], RHO[dtype] * float(np.max(np.abs(r))) if r.size else 0.0)
+        out[name] = (err, bar)
+    if "lse" in got and got["lse"] is not None:
+        g, r = _np(got["lse"]), _np(ref["lse"])
+        inf_r = np.isneginf(r)
+        if not np.array_equal(np.isneginf(g), inf_r) or not np.all(np.isfinite(g[~inf_r])):
+            out["lse"] = (float("inf"), 0.0)
+        else:
+            err = float(np.max(np.abs(g[~inf_r] - r[~inf_r]))) if (~inf_r).any() else 0.0
+            out["lse"] = (err, LSE_TOL[dtype])
+    return out
+
+
+def failures(got: dict, ref: dict, dtype: str) -> list:
+    return [f"{k}: err {e:.3e} > bar {b:.3e}" for k, (e, b) in errors(got, ref, dtype).items() if not e <= b]
+
+
+def assert_parity(got: dict, ref: dict, dtype: str, what: str = ""):
+    bad = failures(got, ref, dtype)
+    assert not bad, f"{what}: " + "; ".join(bad)

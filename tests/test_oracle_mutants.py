@@ -1,0 +1,128 @@
+"""The parity bars have power: plausible mistakes planted in the oracle (on the CPU) fail them.
+
+Each mutant is the oracle with one mistake a kernel could plausibly make (a
+dropped term, a sign, a swapped operand, a wrong mask polarity or diagonal).
+On the stress inputs used by the GPU parity tests every mutant must fail the
+bars of ``tests/parity.py`` against the true oracle. A last test records why
+the stress inputs exist: at the 1/sqrt(d) spread the absolute bar alone
+accepts an all-zero output.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from forward_mode_autodiff_amd.inputs import Workload, make_inputs
+from oracle import oracle_fwd
+from tests.parity import ABS_TOL, failures
+
+
+def as_np(t):
+    return None if t is None else t.double().numpy()
+
+
+def run(f, x, **kw):
+    o, to, lse, tlse = f(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], **kw)
+    return {"o": o, "to": to, "lse": lse, "tlse": tlse}
+
+
+def m_drop_score_tangent(q, k, v, tq, tk, tv, **kw):
+    o, _, lse, _ = oracle_fwd(q, k, v, tq, tk, tv, **kw)
+    _, to, _, tlse = oracle_fwd(q, k, v, None, None, tv, **kw)
+    return o, to, lse, tlse
+
+
+def m_drop_tlse_o(q, k, v, tq, tk, tv, **kw):
+    o, to, lse, tlse = oracle_fwd(q, k, v, tq, tk, tv, **kw)
+    return o, to + tlse[..., None] * o, lse, tlse
+
+
+def m_sign_value_tangent(q, k, v, tq, tk, tv, **kw):
+    o, to, lse, tlse = oracle_fwd(q, k, v, tq, tk, tv, **kw)
+    _, tov, _, _ = oracle_fwd(q, k, v, None, None, tv, **kw)
+    return o, to - 2 * tov, lse, tlse
+
+
+def m_unscaled_score_tangent(q, k, v, tq, tk, tv, scale=None, **kw):
+    s = 1 / math.sqrt(q.shape[-1]) if scale is None else scale
+    return oracle_fwd(q, k, v, tq / s, tk / s, tv, scale=s, **kw)
+
+
+def m_swap_q_k_tangents(q, k, v, tq, tk, tv, **kw):
+    return oracle_fwd(q, k, v, tk, tq, tv, **kw)
+
+
+def m_uniform_weights(q, k, v, tq, tk, tv, **kw):
+    return oracle_fwd(np.zeros_like(q), k, v, np.zeros_like(tq), tk, tv, **kw)
+
+
+def m_strict_causal(q, k, v, tq, tk, tv, causal=False, **kw):
+    n = q.shape[2]
+    strict = (np.arange(n)[None, :] < np.arange(n)[:, None]).astype(np.uint8)[None, None]
+    return oracle_fwd(q, k, v, tq, tk, tv, mask=strict, mask_kind="bool", **kw)
+
+
+def m_flipped_polarity(q, k, v, tq, tk, tv, mask=None, mask_kind="bool", **kw):
+    return oracle_fwd(q, k, v, tq, tk, tv, mask=1 - mask, mask_kind=mask_kind, **kw)
+
+
+def m_mask_before_scale(q, k, v, tq, tk, tv, mask=None, mask_kind="additive", **kw):
+    s = 1 / math.sqrt(q.shape[-1])
+    return oracle_fwd(q, k, v, tq, tk, tv, mask=mask * s, mask_kind=mask_kind, **kw)
+
+
+PLAIN = [m_drop_score_tangent, m_drop_tlse_o, m_sign_value_tangent, m_unscaled_score_tangent,
+         m_swap_q_k_tangents, m_uniform_weights]
+
+
+def stress(dtype, std, causal=False, mask_kind="none", N=64, seed=0):
+    w = Workload("stress", B=1, H=2, N=N, d=64, dtype=dtype, causal=causal, mask_kind=mask_kind,
+                 std=std, seed=seed)
+    x = make_inputs(w)
+    return {k: as_np(v) for k, v in x.items()}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("std", [1.0, 2.0])
+@pytest.mark.parametrize("mutant", PLAIN, ids=lambda f: f.__name__)
+def test_plain_mutants_fail(dtype, std, mutant):
+    x = stress(dtype, std)
+    ref = run(oracle_fwd, x)
+    assert failures(run(mutant, x), ref, dtype), f"{mutant.__name__} passed the bars"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strict_causal_fails(dtype):
+    x = stress(dtype, 1.0, causal=True)
+    ref = run(oracle_fwd, x, causal=True)
+    assert failures(run(m_strict_causal, x), ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_flipped_bool_polarity_fails(dtype):
+    x = stress(dtype, 1.0, mask_kind="bool")
+    ref = run(oracle_fwd, x, mask=x["mask"], mask_kind="bool")
+    assert failures(run(m_flipped_polarity, x, mask=x["mask"], mask_kind="bool"), ref, dtype)
+
+
+def test_additive_mask_before_scale_fails():
+    x = stress("f16", 1.0, mask_kind="additive")
+    ref = run(oracle_fwd, x, mask=x["mask"], mask_kind="additive")
+    assert failures(run(m_mask_before_scale, x, mask=x["mask"], mask_kind="additive"), ref, "f16")
+
+
+def test_oracle_passes_its_own_bars():
+    x = stress("bf16", 2.0)
+    ref = run(oracle_fwd, x)
+    assert not failures(ref, ref, "bf16")
+
+
+def test_default_spread_needs_stress_inputs():
+    """At N(0,1)/sqrt(d) (seq sweep, N=2048) the absolute bar alone accepts an all-zero output."""
+    x = stress("f16", None, N=2048)
+    ref = run(oracle_fwd, x)
+    zero = {k: np.zeros_like(v) for k, v in ref.items()}
+    zero["lse"] = ref["lse"]
+    for name in ("o", "to"):
+        assert np.max(np.abs(ref[name])) < ABS_TOL["f16"]
+    assert failures(zero, ref, "f16")     # the scale-free bar still sees it
