@@ -1,0 +1,154 @@
+// Host-side argument validation for jvpattn_fwd. Pure C++: no HIP calls and
+// no pointer dereferences, so it runs (and is tested) on machines without a
+// GPU and under host sanitizers.
+#include "jvpattn.h"
+#include "jvpattn_internal.h"
+
+#include <cmath>
+#include <cstdint>
+
+namespace jvpattn {
+
+namespace {
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+  bool empty() const { return hi <= lo; }
+};
+
+Span span(const void* p, int64_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, p ? a + static_cast<uintptr_t>(bytes) : a};
+}
+
+bool overlap(Span a, Span b) {
+  if (a.empty() || b.empty()) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+int elem_bytes(int dtype) {
+  switch (dtype) {
+    case JVPATTN_F32: return 4;
+    case JVPATTN_F16: return 2;
+    case JVPATTN_BF16: return 2;
+    default: return 0;
+  }
+}
+
+int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void* v,
+              const void* tq, const void* tk, const void* tv, const void* mask,
+              const void* o, const void* to, const float* lse, const float* tlse,
+              FwdSizes* sizes) {
+  if (!p) return JVPATTN_ERR_NULL;
+  const int es = elem_bytes(p->dtype);
+  if (es == 0) return JVPATTN_ERR_DTYPE;
+  if (p->B < 0 || p->H < 0 || p->Nq < 0 || p->Nk < 0 || p->d <= 0) return JVPATTN_ERR_SHAPE;
+
+  int64_t bh, rows_q, rows_k, n_q, n_k, bytes_q, bytes_k, bytes_stats;
+  if (!mul_ok(p->B, p->H, &bh) || !mul_ok(bh, p->Nq, &rows_q) || !mul_ok(bh, p->Nk, &rows_k) ||
+      !mul_ok(rows_q, p->d, &n_q) || !mul_ok(rows_k, p->d, &n_k) || !mul_ok(n_q, es, &bytes_q) ||
+      !mul_ok(n_k, es, &bytes_k) || !mul_ok(rows_q, 4, &bytes_stats))
+    return JVPATTN_ERR_SHAPE;
+  // every grid dimension the launcher forms must stay within int32
+  if (bh > INT32_MAX) return JVPATTN_ERR_SHAPE;
+
+  if (p->d != 64 && p->d != 128) return JVPATTN_ERR_HEADDIM;
+  if (!std::isfinite(p->scale) || !(p->scale > 0.0f)) return JVPATTN_ERR_SCALE;
+
+  if (p->mask_kind != JVPATTN_MASK_NONE && p->mask_kind != JVPATTN_MASK_BOOL &&
+      p->mask_kind != JVPATTN_MASK_ADDITIVE)
+    return JVPATTN_ERR_MASK;
+  const bool has_mask = p->mask_kind != JVPATTN_MASK_NONE;
+  const bool work = rows_q > 0;
+  int64_t mask_bytes = 0;
+  int mask_es = 0;
+  if (has_mask) {
+    if (work && !mask) return JVPATTN_ERR_MASK;
+    if (p->mask_stride_b < 0 || p->mask_stride_h < 0 || p->mask_stride_q < 0) return JVPATTN_ERR_MASK;
+    mask_es = p->mask_kind == JVPATTN_MASK_BOOL ? 1 : es;
+    // extent = largest element offset + 1
+    int64_t eb, eh, eq, ext = 0;
+    if (work && p->Nk > 0) {
+      if (!mul_ok(p->B - 1, p->mask_stride_b, &eb) || !mul_ok(p->H - 1, p->mask_stride_h, &eh) ||
+          !mul_ok(p->Nq - 1, p->mask_stride_q, &eq))
+        return JVPATTN_ERR_MASK;
+      ext = eb;
+      if (ext > INT64_MAX - eh) return JVPATTN_ERR_MASK;
+      ext += eh;
+      if (ext > INT64_MAX - eq) return JVPATTN_ERR_MASK;
+      ext += eq;
+      if (ext > INT64_MAX - p->Nk) return JVPATTN_ERR_MASK;
+      ext += p->Nk;
+      if (!mul_ok(ext, mask_es, &mask_bytes)) return JVPATTN_ERR_MASK;
+    }
+  } else if (mask) {
+    return JVPATTN_ERR_MASK;
+  }
+
+  if (work) {
+    if (!q || !o || !to || !lse) return JVPATTN_ERR_NULL;
+    if (rows_k > 0 && (!k || !v)) return JVPATTN_ERR_NULL;
+  }
+
+  const void* tensors[] = {q, k, v, tq, tk, tv, o, to};
+  for (const void* t : tensors)
+    if (t && !aligned(t, 16)) return JVPATTN_ERR_ALIGN;
+  if ((lse && !aligned(lse, 4)) || (tlse && !aligned(tlse, 4))) return JVPATTN_ERR_ALIGN;
+  if (mask && !aligned(mask, mask_es > 0 ? mask_es : 1)) return JVPATTN_ERR_ALIGN;
+
+  if (work) {
+    const Span outs[] = {span(o, bytes_q), span(to, bytes_q), span(lse, bytes_stats),
+                         span(tlse, tlse ? bytes_stats : 0)};
+    const Span ins[] = {span(q, bytes_q),  span(k, bytes_k),  span(v, bytes_k), span(tq, bytes_q),
+                        span(tk, bytes_k), span(tv, bytes_k), span(mask, mask_bytes)};
+    for (int i = 0; i < 4; ++i) {
+      for (const Span& s : ins)
+        if (overlap(outs[i], s)) return JVPATTN_ERR_ALIAS;
+      for (int j = i + 1; j < 4; ++j)
+        if (overlap(outs[i], outs[j])) return JVPATTN_ERR_ALIAS;
+    }
+  }
+
+  if (sizes) {
+    sizes->rows_q = rows_q;
+    sizes->rows_k = rows_k;
+    sizes->elem_bytes = es;
+  }
+  return JVPATTN_OK;
+}
+
+}  // namespace jvpattn
+
+extern "C" int jvpattn_check_fwd(const jvpattn_params* params, const void* q, const void* k,
+                                 const void* v, const void* tq, const void* tk, const void* tv,
+                                 const void* mask, const void* o, const void* to, const float* lse,
+                                 const float* tlse) {
+  return jvpattn::check_fwd(params, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, nullptr);
+}
+
+extern "C" const char* jvpattn_strerror(int code) {
+  switch (code) {
+    case JVPATTN_OK: return "ok";
+    case JVPATTN_ERR_NULL: return "a required pointer is NULL";
+    case JVPATTN_ERR_SHAPE: return "invalid shape (negative size, d <= 0, or size overflow)";
+    case JVPATTN_ERR_DTYPE: return "unknown dtype";
+    case JVPATTN_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128)";
+    case JVPATTN_ERR_MASK: return "invalid mask (unknown kind, pointer/kind mismatch, or bad strides)";
+    case JVPATTN_ERR_ALIGN: return "misaligned pointer (tensors: 16 bytes, lse/tlse: 4 bytes)";
+    case JVPATTN_ERR_SCALE: return "scale must be finite and > 0";
+    case JVPATTN_ERR_ALIAS: return "an output overlaps an input or another output";
+    case JVPATTN_ERR_HIP: return "HIP runtime error on launch";
+    default: return "unknown error code";
+  }
+}

@@ -1,0 +1,160 @@
+"""Thin Python binding of libjvpattn.so (argument marshalling only).
+
+The names follow the C interface in include/jvpattn.h. Every step of the
+computation runs in the HIP library; PyTorch only supplies device memory and
+the current stream. There is no CPU fallback: if the library is missing the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loaded first so that the HIP runtime torch ships is the one the library binds to
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libjvpattn.so")
+
+JVPATTN_F32, JVPATTN_F16, JVPATTN_BF16 = 0, 1, 2
+JVPATTN_MASK_NONE, JVPATTN_MASK_BOOL, JVPATTN_MASK_ADDITIVE = 0, 1, 2
+ERRORS = {
+    0: "JVPATTN_OK", -1: "JVPATTN_ERR_NULL", -2: "JVPATTN_ERR_SHAPE", -3: "JVPATTN_ERR_DTYPE",
+    -4: "JVPATTN_ERR_HEADDIM", -5: "JVPATTN_ERR_MASK", -6: "JVPATTN_ERR_ALIGN", -7: "JVPATTN_ERR_SCALE",
+    -8: "JVPATTN_ERR_ALIAS", -9: "JVPATTN_ERR_HIP",
+}
+_DTYPE_CODE = {torch.float32: JVPATTN_F32, torch.float16: JVPATTN_F16, torch.bfloat16: JVPATTN_BF16}
+
+
+class jvpattn_params(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Nq", ctypes.c_int32), ("Nk", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("mask_kind", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("mask_stride_b", ctypes.c_int64), ("mask_stride_h", ctypes.c_int64),
+        ("mask_stride_q", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class JvpattnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libjvpattn.so once; raise loudly if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m forward_mode_autodiff_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, fp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)
+    P = ctypes.POINTER(jvpattn_params)
+    lib.jvpattn_check_fwd.argtypes = [P] + [vp] * 9 + [vp, vp]
+    lib.jvpattn_check_fwd.restype = ctypes.c_int
+    lib.jvpattn_fwd.argtypes = [P] + [vp] * 7 + [vp, vp, vp, vp, vp]
+    lib.jvpattn_fwd.restype = ctypes.c_int
+    lib.jvpattn_strerror.argtypes = [ctypes.c_int]
+    lib.jvpattn_strerror.restype = ctypes.c_char_p
+    lib.jvpattn_last_hip_error.argtypes = []
+    lib.jvpattn_last_hip_error.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def jvpattn_strerror(code: int) -> str:
+    return load_library().jvpattn_strerror(int(code)).decode()
+
+
+def jvpattn_check_fwd(params: jvpattn_params, q, k, v, tq, tk, tv, mask, o, to, lse, tlse) -> int:
+    """Host-only validation; pointer arguments are integers (addresses) or None."""
+    lib = load_library()
+    return lib.jvpattn_check_fwd(ctypes.byref(params), q, k, v, tq, tk, tv, mask, o, to, lse, tlse)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_params(q, k, mask=None, causal=False, scale=None) -> tuple:
+    """Fill jvpattn_params from tensors. Returns (params, mask tensor as passed to the library)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if q.dtype not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    p = jvpattn_params()
+    p.B, p.H, p.Nq, p.Nk, p.d = B, H, Nq, Nk, d
+    p.dtype = _DTYPE_CODE[q.dtype]
+    p.causal = 1 if causal else 0
+    p.scale = float(1.0 / math.sqrt(d) if scale is None else scale)
+    p.mask_kind = JVPATTN_MASK_NONE
+    if mask is not None:
+        if mask.dim() == 2:
+            mask = mask[None, None]
+        elif mask.dim() == 3:
+            mask = mask[:, None]
+        if mask.dim() != 4:
+            raise ValueError("mask must broadcast to [B, H, Nq, Nk]")
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype == torch.uint8:
+            p.mask_kind = JVPATTN_MASK_BOOL
+        elif mask.dtype == q.dtype:
+            p.mask_kind = JVPATTN_MASK_ADDITIVE
+        else:
+            raise TypeError("an additive mask must have the dtype of q")
+        if mask.shape[3] != Nk or mask.shape[2] not in (1, Nq) or mask.shape[1] not in (1, H) \
+                or mask.shape[0] not in (1, B):
+            raise ValueError(f"mask shape {tuple(mask.shape)} does not broadcast to {(B, H, Nq, Nk)}")
+        if mask.stride(3) != 1:
+            mask = mask.contiguous()
+        st = [0 if mask.shape[i] == 1 else mask.stride(i) for i in range(3)]
+        p.mask_stride_b, p.mask_stride_h, p.mask_stride_q = st
+    return p, mask
+
+
+def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, scale=None,
+                want_tlse=True, out=None):
+    """O, dO, lse, tlse = jvpattn_fwd(q, k, v, tq, tk, tv, mask, causal, scale).
+
+    q, tq: [B,H,Nq,d]; k, v, tk, tv: [B,H,Nk,d] on the GPU, one dtype
+    (float32 / float16 / bfloat16), contiguous. Tangents may be None (zero).
+    mask: None, a bool/uint8 tensor (True = attend) or an additive tensor of
+    q's dtype, broadcastable to [B,H,Nq,Nk]. Work is queued on torch's
+    current stream. ``out`` optionally supplies (o, to, lse, tlse) buffers.
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("tq", tq), ("tk", tk), ("tv", tv)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    p, mask = make_params(q, k, mask, causal, scale)
+    if out is None:
+        o = torch.empty_like(q)
+        to = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], device=q.device, dtype=torch.float32)
+        tlse = torch.empty_like(lse) if want_tlse else None
+    else:
+        o, to, lse, tlse = out
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.jvpattn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                         _ptr(mask), _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse), stream)
+    if rc != 0:
+        msg = jvpattn_strerror(rc)
+        if rc == -9:
+            msg += f" (hipError {lib.jvpattn_last_hip_error()})"
+        raise JvpattnError(rc, msg)
+    return o, to, lse, tlse

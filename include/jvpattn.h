@@ -1,0 +1,129 @@
+/*
+ * jvpattn: fused attention forward carrying dual numbers, for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What it computes. Given queries Q, keys K, values V and their tangents
+ * dQ, dK, dV (all [B, H, N, d], d fastest), one call returns
+ *
+ *   O    = softmax(scale * Q K^T + M) V               attention output
+ *   dO   = d/dt O(Q + t dQ, K + t dK, V + t dV) at 0   its Jacobian-vector product
+ *   lse  = logsumexp_j(scale * Q K^T + M)             natural log, per query row
+ *   tlse = sum_j P_ij dS_ij,  dS = scale (dQ K^T + Q dK^T)   (the JVP of lse)
+ *
+ * The operation is the one the "JVP Flash Attention" README describes: a
+ * drop-in for PyTorch's scaled_dot_product_attention (section "Usage":
+ * q, k, v and attn_mask, no dropout) that supports Jacobian-vector products
+ * (section "Description"). The per-head computation is the plain scaled
+ * dot-product attention of the naive MHSA script in the equinox issue
+ * "Flash Attention" (#732): scores divided by sqrt(key depth) by default,
+ * softmax over keys, weights applied to V.
+ *
+ * Conventions (the pages leave these open; these are SDPA's):
+ *   - boolean mask: nonzero = the key takes part, zero = excluded;
+ *   - additive mask: added after scaling, treated as a constant (no tangent);
+ *   - causal: key j is visible to query i iff j <= i (top-left aligned); with
+ *     a mask as well, both restrictions apply;
+ *   - a query row with no visible key gets O = dO = 0, lse = -inf, tlse = 0.
+ *
+ * All pointers other than `params` are device pointers (HBM) owned by the
+ * caller. Nothing is allocated and no state is kept between calls beyond the
+ * loaded code objects. Work is queued on `stream` (a hipStream_t; NULL is the
+ * null stream) and the call returns without waiting for it.
+ */
+#ifndef JVPATTN_H
+#define JVPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. One type applies to q, k, v, dq, dk, dv, o, do and, for
+ * JVPATTN_MASK_ADDITIVE, to the mask. */
+typedef enum {
+  JVPATTN_F32 = 0,   /* IEEE float32 */
+  JVPATTN_F16 = 1,   /* IEEE float16 */
+  JVPATTN_BF16 = 2   /* bfloat16 */
+} jvpattn_dtype;
+
+typedef enum {
+  JVPATTN_MASK_NONE = 0,
+  JVPATTN_MASK_BOOL = 1,      /* uint8 (torch.bool): nonzero = attend */
+  JVPATTN_MASK_ADDITIVE = 2   /* the element type above, added to scaled scores */
+} jvpattn_mask_kind;
+
+/* Return codes. Every error is detected before any work is queued, so a
+ * call that fails writes nothing -- except JVPATTN_ERR_HIP, which reports a
+ * failed kernel launch. No error crosses the interface as an exception. */
+enum {
+  JVPATTN_OK = 0,
+  JVPATTN_ERR_NULL = -1,     /* a required pointer is NULL */
+  JVPATTN_ERR_SHAPE = -2,    /* B, H, Nq, Nk < 0, or a size overflows int64 */
+  JVPATTN_ERR_DTYPE = -3,    /* dtype not one of jvpattn_dtype */
+  JVPATTN_ERR_HEADDIM = -4,  /* d not supported (supported: 64, 128) */
+  JVPATTN_ERR_MASK = -5,     /* mask_kind unknown, mask NULL/non-NULL mismatch, bad strides */
+  JVPATTN_ERR_ALIGN = -6,    /* a tensor pointer not 16-byte aligned (lse/tlse: 4-byte) */
+  JVPATTN_ERR_SCALE = -7,    /* scale not finite or not > 0 */
+  JVPATTN_ERR_ALIAS = -8,    /* an output overlaps an input or another output */
+  JVPATTN_ERR_HIP = -9       /* the HIP runtime reported an error on launch */
+};
+
+typedef struct {
+  int32_t B, H;          /* batch, heads */
+  int32_t Nq, Nk;        /* query rows, key/value rows (causal is top-left aligned when Nq != Nk) */
+  int32_t d;             /* head dimension of q, k, v (64 or 128) */
+  int32_t dtype;         /* jvpattn_dtype */
+  int32_t mask_kind;     /* jvpattn_mask_kind */
+  int32_t causal;        /* 0 or 1 */
+  /* Mask element (b, h, i, j) is at mask[b*mask_stride_b + h*mask_stride_h
+   * + i*mask_stride_q + j] (strides in elements, j contiguous). A stride of 0
+   * broadcasts that axis, e.g. a [B,1,Nq,Nk] mask has mask_stride_h = 0 and a
+   * key-padding mask [B,1,1,Nk] also has mask_stride_q = 0. Ignored when
+   * mask_kind is NONE. */
+  int64_t mask_stride_b, mask_stride_h, mask_stride_q;
+  float scale;           /* multiplies Q K^T and dQ K^T + Q dK^T; finite and > 0 (SDPA default 1/sqrt(d)) */
+} jvpattn_params;
+
+/* Host-only validation of a jvpattn_fwd call: the same checks jvpattn_fwd
+ * makes, in the same order, without touching the GPU (pointers are only
+ * compared, never dereferenced). Returns JVPATTN_OK or the error code
+ * jvpattn_fwd would return. */
+int jvpattn_check_fwd(const jvpattn_params* params,
+                      const void* q, const void* k, const void* v,
+                      const void* tq, const void* tk, const void* tv,
+                      const void* mask,
+                      const void* o, const void* to, const float* lse, const float* tlse);
+
+/* The forward pass with tangents.
+ *   q, tq, o, to : [B, H, Nq, d] contiguous, element type params->dtype
+ *   k, v, tk, tv : [B, H, Nk, d] contiguous
+ *   tq, tk, tv   : may each be NULL, meaning a zero tangent
+ *   mask         : NULL iff mask_kind == NONE; layout given by the strides
+ *   lse, tlse    : [B, H, Nq] float32; tlse may be NULL (not written)
+ * Outputs are fully overwritten and must not overlap the inputs or each
+ * other. Inputs are read only. Arithmetic: products on the matrix cores in
+ * float32 accumulation; softmax statistics in float32; for 16-bit inputs the
+ * softmax weights and their products with the score tangent are rounded to
+ * the input type before the value products; O and dO are rounded to nearest
+ * even. Float32 inputs use float32 matrix products throughout. */
+int jvpattn_fwd(const jvpattn_params* params,
+                const void* q, const void* k, const void* v,
+                const void* tq, const void* tk, const void* tv,
+                const void* mask,
+                void* o, void* to, float* lse, float* tlse,
+                void* stream);
+
+/* A static, human-readable description of a return code. */
+const char* jvpattn_strerror(int code);
+
+/* The HIP error code (hipError_t value) of the most recent JVPATTN_ERR_HIP
+ * on the calling thread, or 0. */
+int jvpattn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JVPATTN_H */

@@ -1,9 +1,13 @@
 """Comparison bars for GPU results against the float64 oracle.
 
-Two bars apply to O and dO at once:
+Two bars apply to O and dO:
   * the absolute bar the method is specified with: max-abs error <= 2e-3 for
-    float32 inputs and <= 1e-2 for bfloat16 / float16 inputs;
-  * a scale-free bar, max-abs error <= rho * max|reference|, with rho = 2^-6
+    float32 inputs and <= 1e-2 for bfloat16 / float16 inputs, on inputs with
+    the specified N(0,1)/sqrt(d) spread (``spec_spread=True``). At larger
+    spreads the outputs grow past 1 and a 16-bit output's own rounding
+    (half an ulp: 2^-8 relative for bf16) exceeds any fixed absolute bar, so
+    there only the scale-free bar applies;
+  * always, a scale-free bar, max-abs error <= rho * max|reference|, with rho = 2^-6
     (bf16), 2^-8 (fp16), 1e-4 (fp32). It is what gives the stress inputs
     (unit and doubled spread) their power: at the 1/sqrt(d) spread every
     output is below 1e-2 and the absolute bar alone would pass an all-zero
@@ -30,34 +34,38 @@ def _np(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def errors(got: dict, ref: dict, dtype: str) -> dict:
-    """Per-output (max-abs error, bar); keys o, to, lse, tlse present in both."""
+def errors(got: dict, ref: dict, dtype: str, spec_spread: bool = False) -> dict:
+    """Per-output (max-abs error, bar, max|ref|); keys o, to, lse, tlse present in both."""
     out = {}
     for name in ("o", "to", "tlse"):
         if name not in got or got[name] is None:
             continue
         g, r = _np(got[name]), _np(ref[name])
+        scale = float(np.max(np.abs(r))) if r.size else 0.0
         if not np.all(np.isfinite(g)):
-            out[name] = (float("inf"), 0.0)
+            out[name] = (float("inf"), 0.0, scale)
             continue
         err = float(np.max(np.abs(g - r))) if g.size else 0.0
-        bar = min(ABS_TOL[dtype], RHO[dtype] * float(np.max(np.abs(r))) if r.size else 0.0)
-        out[name] = (err, bar)
+        bar = RHO[dtype] * scale
+        if spec_spread:
+            bar = min(bar, ABS_TOL[dtype])
+        out[name] = (err, bar, scale)
     if "lse" in got and got["lse"] is not None:
         g, r = _np(got["lse"]), _np(ref["lse"])
         inf_r = np.isneginf(r)
         if not np.array_equal(np.isneginf(g), inf_r) or not np.all(np.isfinite(g[~inf_r])):
-            out["lse"] = (float("inf"), 0.0)
+            out["lse"] = (float("inf"), 0.0, 0.0)
         else:
             err = float(np.max(np.abs(g[~inf_r] - r[~inf_r]))) if (~inf_r).any() else 0.0
-            out["lse"] = (err, LSE_TOL[dtype])
+            out["lse"] = (err, LSE_TOL[dtype], 0.0)
     return out
 
 
-def failures(got: dict, ref: dict, dtype: str) -> list:
-    return [f"{k}: err {e:.3e} > bar {b:.3e}" for k, (e, b) in errors(got, ref, dtype).items() if not e <= b]
+def failures(got: dict, ref: dict, dtype: str, spec_spread: bool = False) -> list:
+    return [f"{k}: err {e:.3e} > bar {b:.3e} (max|ref| {m:.3e})"
+            for k, (e, b, m) in errors(got, ref, dtype, spec_spread).items() if not e <= b]
 
 
-def assert_parity(got: dict, ref: dict, dtype: str, what: str = ""):
-    bad = failures(got, ref, dtype)
+def assert_parity(got: dict, ref: dict, dtype: str, what: str = "", spec_spread: bool = False):
+    bad = failures(got, ref, dtype, spec_spread)
     assert not bad, f"{what}: " + "; ".join(bad)

@@ -1,0 +1,216 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, and rejects every invalid call before touching the device."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from forward_mode_autodiff_amd import jvpattn as J
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jvpattn.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(J.LIB_PATH), reason="libjvpattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(jvpattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    assert declared_functions() == ["jvpattn_check_fwd", "jvpattn_fwd", "jvpattn_last_hip_error",
+                                    "jvpattn_strerror"]
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", J.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+    lib = J.load_library()
+    for name in declared_functions():
+        assert getattr(lib, name) is not None
+
+
+def test_params_struct_layout():
+    assert ctypes.sizeof(J.jvpattn_params) == 64
+    assert J.jvpattn_params.mask_stride_b.offset == 32
+    assert J.jvpattn_params.scale.offset == 56
+
+
+@needs_lib
+def test_strerror_strings():
+    for code in J.ERRORS:
+        s = J.jvpattn_strerror(code)
+        assert s and s != "unknown error code"
+    assert J.jvpattn_strerror(12345) == "unknown error code"
+
+
+def good_params(**kw):
+    p = J.jvpattn_params()
+    p.B, p.H, p.Nq, p.Nk, p.d = 2, 3, 100, 90, 64
+    p.dtype, p.mask_kind, p.causal = J.JVPATTN_BF16, J.JVPATTN_MASK_NONE, 0
+    p.mask_stride_b = p.mask_stride_h = p.mask_stride_q = 0
+    p.scale = 0.125
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def ptrs(p, es=2):
+    """Fake, disjoint, 256-aligned device addresses sized for the params (never dereferenced)."""
+    nq = p.B * p.H * p.Nq * p.d * es
+    nk = p.B * p.H * p.Nk * p.d * es
+    ns = p.B * p.H * p.Nq * 4
+    base = 1 << 40
+    out = {}
+    for name, n in (("q", nq), ("k", nk), ("v", nk), ("tq", nq), ("tk", nk), ("tv", nk), ("o", nq),
+                    ("to", nq), ("lse", ns), ("tlse", ns), ("mask", p.B * p.Nq * p.Nk * 2)):
+        out[name] = base
+        base += (n + 4096) // 256 * 256 + 256
+    return out
+
+
+def call(p, P, **over):
+    a = dict(P)
+    a.update(over)
+    mask = a["mask"] if p.mask_kind != 0 else None
+    mask = over.get("mask", mask)
+    return J.jvpattn_check_fwd(p, a["q"], a["k"], a["v"], a["tq"], a["tk"], a["tv"], mask, a["o"],
+                               a["to"], a["lse"], a["tlse"])
+
+
+@needs_lib
+def test_check_accepts_valid_calls():
+    p = good_params()
+    assert call(p, ptrs(p)) == 0
+    assert call(p, ptrs(p), tq=None, tk=None, tv=None, tlse=None) == 0
+    for d in (64, 128):
+        for dt, es in ((J.JVPATTN_F32, 4), (J.JVPATTN_F16, 2), (J.JVPATTN_BF16, 2)):
+            p = good_params(d=d, dtype=dt)
+            assert call(p, ptrs(p, es)) == 0
+    p = good_params(mask_kind=J.JVPATTN_MASK_BOOL, mask_stride_b=100 * 90, mask_stride_q=90)
+    assert call(p, ptrs(p)) == 0
+    p = good_params(mask_kind=J.JVPATTN_MASK_ADDITIVE, mask_stride_b=0, mask_stride_q=0)
+    assert call(p, ptrs(p)) == 0
+    # empty problems need no pointers at all
+    p = good_params(Nq=0)
+    assert J.jvpattn_check_fwd(p, *([None] * 11)) == 0
+    p = good_params(B=0)
+    assert J.jvpattn_check_fwd(p, *([None] * 11)) == 0
+
+
+@needs_lib
+@pytest.mark.parametrize("case,code", [
+    ("params_null", -1), ("q_null", -1), ("o_null", -1), ("to_null", -1), ("lse_null", -1), ("k_null", -1),
+    ("neg_B", -2), ("neg_Nk", -2), ("d_zero", -2), ("overflow", -2),
+    ("dtype", -3), ("d_96", -4), ("d_32", -4),
+    ("kind", -5), ("mask_missing", -5), ("mask_extra", -5), ("mask_neg_stride", -5), ("mask_stride_overflow", -5),
+    ("q_misaligned", -6), ("tv_misaligned", -6), ("lse_misaligned", -6), ("mask_misaligned", -6),
+    ("scale_nan", -7), ("scale_inf", -7), ("scale_zero", -7), ("scale_neg", -7),
+    ("o_is_q", -8), ("to_overlaps_v", -8), ("lse_overlaps_tlse", -8), ("o_overlaps_mask", -8),
+])
+def test_check_rejects(case, code):
+    p = good_params()
+    P = ptrs(p)
+    over = {}
+    if case == "params_null":
+        assert J.load_library().jvpattn_check_fwd(None, *[P[n] for n in ("q", "k", "v", "tq", "tk", "tv")],
+                                                  None, P["o"], P["to"], P["lse"], P["tlse"]) == code
+        return
+    if case.endswith("_null"):
+        over[case[:-5]] = None
+    elif case == "neg_B":
+        p.B = -1
+    elif case == "neg_Nk":
+        p.Nk = -5
+    elif case == "d_zero":
+        p.d = 0
+    elif case == "overflow":
+        p.B, p.H, p.Nq = 2 ** 31 - 1, 2 ** 31 - 1, 2 ** 31 - 1
+    elif case == "dtype":
+        p.dtype = 7
+    elif case == "d_96":
+        p.d = 96
+    elif case == "d_32":
+        p.d = 32
+    elif case == "kind":
+        p.mask_kind = 3
+    elif case == "mask_missing":
+        p.mask_kind = J.JVPATTN_MASK_BOOL
+        over["mask"] = None
+    elif case == "mask_extra":
+        over["mask"] = P["mask"]
+    elif case == "mask_neg_stride":
+        p.mask_kind, p.mask_stride_q = J.JVPATTN_MASK_BOOL, -90
+    elif case == "mask_stride_overflow":
+        p.mask_kind, p.mask_stride_b = J.JVPATTN_MASK_BOOL, 2 ** 63 - 1
+    elif case == "q_misaligned":
+        over["q"] = P["q"] + 8
+    elif case == "tv_misaligned":
+        over["tv"] = P["tv"] + 4
+    elif case == "lse_misaligned":
+        over["lse"] = P["lse"] + 2
+    elif case == "mask_misaligned":
+        p.mask_kind, p.mask_stride_q = J.JVPATTN_MASK_ADDITIVE, 90
+        over["mask"] = P["mask"] + 1
+    elif case.startswith("scale_"):
+        p.scale = {"nan": float("nan"), "inf": float("inf"), "zero": 0.0, "neg": -0.125}[case[6:]]
+    elif case == "o_is_q":
+        over["o"] = P["q"]
+    elif case == "to_overlaps_v":
+        over["to"] = P["v"] + 256
+    elif case == "lse_overlaps_tlse":
+        over["tlse"] = P["lse"] + 64
+    elif case == "o_overlaps_mask":
+        p.mask_kind, p.mask_stride_q, p.mask_stride_b = J.JVPATTN_MASK_BOOL, 90, 9000
+        over["o"] = P["mask"]
+    assert call(p, P, **over) == code
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_validator_under_host_sanitizers(tmp_path):
+    """The validator is plain C++: build it with g++ and ASan/UBSan and run a driver over edge cases."""
+    drv = tmp_path / "drv.cpp"
+    drv.write_text(r'''
+#include "jvpattn.h"
+#include <cstdio>
+#include <cstdint>
+#include <cmath>
+int main() {
+  jvpattn_params p{};
+  p.B = 2; p.H = 2; p.Nq = 33; p.Nk = 17; p.d = 64; p.dtype = JVPATTN_F16; p.scale = 0.125f;
+  char* base = reinterpret_cast<char*>(uintptr_t(1) << 40);
+  auto at = [&](long i) { return base + i * (1L << 24); };
+  int bad = 0;
+  bad += jvpattn_check_fwd(&p, at(0), at(1), at(2), at(3), at(4), at(5), nullptr, at(6), at(7),
+                           (float*)at(8), (float*)at(9)) != JVPATTN_OK;
+  p.B = 2147483647; p.H = 2147483647; p.Nq = 2147483647;
+  bad += jvpattn_check_fwd(&p, at(0), at(1), at(2), at(3), at(4), at(5), nullptr, at(6), at(7),
+                           (float*)at(8), (float*)at(9)) != JVPATTN_ERR_SHAPE;
+  p.B = 2; p.H = 2; p.Nq = 33; p.mask_kind = JVPATTN_MASK_BOOL; p.mask_stride_b = INT64_MAX;
+  bad += jvpattn_check_fwd(&p, at(0), at(1), at(2), at(3), at(4), at(5), at(10), at(6), at(7),
+                           (float*)at(8), (float*)at(9)) != JVPATTN_ERR_MASK;
+  p.mask_stride_b = 0; p.scale = NAN;
+  bad += jvpattn_check_fwd(&p, at(0), at(1), at(2), at(3), at(4), at(5), at(10), at(6), at(7),
+                           (float*)at(8), (float*)at(9)) != JVPATTN_ERR_SCALE;
+  bad += jvpattn_check_fwd(nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) != JVPATTN_ERR_NULL;
+  for (int c = -10; c <= 1; ++c) bad += jvpattn_strerror(c) == nullptr;
+  std::printf("bad=%d\n", bad);
+  return bad;
+}
+''')
+    exe = tmp_path / "drv"
+    src = os.path.join(ROOT, "forward_mode_autodiff_amd", "csrc", "jvpattn_check.cpp")
+    cmd = ["g++", "-std=c++17", "-g", "-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           f"-I{ROOT}/include", f"-I{ROOT}/forward_mode_autodiff_amd/csrc", str(drv), src, "-o", str(exe)]
+    subprocess.run(cmd, check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "bad=0" in r.stdout

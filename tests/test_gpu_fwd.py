@@ -1,0 +1,270 @@
+"""Parity of the HIP forward (through the C ABI) against the float64 oracle.
+
+Inputs are seeded and synthetic (forward_mode_autodiff_amd.inputs); the
+oracle sees exactly the values the GPU sees. Bars: tests/parity.py. The
+workloads the method is specified on run in full, checked element by element
+where the oracle finishes in seconds and on sampled rows at the largest
+sizes; a stress suite (unit and doubled input spread, isolated tangent terms)
+gives the comparisons power the 1/sqrt(d) spread lacks.
+"""
+import numpy as np
+import pytest
+import torch
+
+from forward_mode_autodiff_amd import inputs as I
+from forward_mode_autodiff_amd.jvpattn import jvpattn_fwd
+from oracle import oracle_fwd
+from tests.parity import assert_parity, failures
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def to_dev(x):
+    return {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
+
+
+def gpu_run(x, causal, scale=None, tangents=("tq", "tk", "tv")):
+    d = to_dev(x)
+    t = {n: (d[n] if n in tangents else None) for n in ("tq", "tk", "tv")}
+    o, to, lse, tlse = jvpattn_fwd(d["q"], d["k"], d["v"], t["tq"], t["tk"], t["tv"], mask=d["mask"],
+                                   causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return {"o": o.float().cpu(), "to": to.float().cpu(), "lse": lse.cpu(), "tlse": tlse.cpu()}
+
+
+def f64(t):
+    return None if t is None else t.double().numpy()
+
+
+def oracle_run(x, mask_kind, causal, scale=None, tangents=("tq", "tk", "tv"), heads=None, rows=None):
+    """Oracle on all heads and rows, or on heads [(b, h), ...] and query rows `rows` only."""
+    tq, tk, tv = (f64(x[n]) if n in tangents else None for n in ("tq", "tk", "tv"))
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    mask = None
+    if x["mask"] is not None:
+        mask = x["mask"].double().numpy() if mask_kind == "additive" else x["mask"].numpy()
+    if heads is None:
+        o, to, lse, tlse = oracle_fwd(q, k, v, tq, tk, tv, mask=mask, mask_kind=mask_kind, causal=causal,
+                                      scale=scale)
+        return {"o": o, "to": to, "lse": lse, "tlse": tlse}
+    out = {n: [] for n in ("o", "to", "lse", "tlse")}
+    for b, h in heads:
+        sl = lambda a: None if a is None else a[b:b + 1, h:h + 1]
+        m = None if mask is None else mask[b:b + 1, (h if mask.shape[1] > 1 else 0):][:, :1]
+        r = oracle_fwd(sl(q)[:, :, rows], sl(k), sl(v), None if tq is None else sl(tq)[:, :, rows], sl(tk),
+                       sl(tv), mask=m, mask_kind=mask_kind, causal=causal, scale=scale, q_pos=rows)
+        for n, a in zip(("o", "to", "lse", "tlse"), r):
+            out[n].append(a[0, 0])
+    return {n: np.stack(a) for n, a in out.items()}
+
+
+def pick(got, heads, rows):
+    return {n: np.stack([got[n][b, h][rows].numpy() for b, h in heads]) for n in got}
+
+
+def check(w, x=None, scale=None, tangents=("tq", "tk", "tv")):
+    x = I.make_inputs(w) if x is None else x
+    got = gpu_run(x, w.causal, scale, tangents)
+    ref = oracle_run(x, w.mask_kind, w.causal, scale, tangents)
+    assert_parity(got, ref, w.dtype, w.name, spec_spread=w.std is None)
+    return got, ref
+
+
+# ------------------------------------------------ the specified workloads
+
+def test_tiny_f32():
+    check(I.TINY)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", I.SEQ_NS)
+def test_seq_sweep_f16(N, causal):
+    check(I.seq(N, causal))
+
+
+@pytest.mark.parametrize("N", [512, 2048])
+def test_seq_bf16(N):
+    check(I.seq(N, False, dtype="bf16"))
+
+
+@pytest.mark.parametrize("w", [I.MASKED_BOOL, I.MASKED_ADD], ids=lambda w: w.name)
+def test_masked(w):
+    check(w)
+
+
+def sampled_rows(N, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(N, size=n, replace=False).tolist()) | {0, 1, 31, 32, 127, 128, N - 1}
+    return np.array(sorted(r for r in rows if r < N))
+
+
+def test_hvp_workload_forward_sampled():
+    """B=4, H=16, N=2048, d=64, bf16, causal: every head launched, sampled heads x rows checked."""
+    w = I.HVP
+    x = I.make_inputs(w)
+    got = gpu_run(x, True)
+    heads = [(0, 0), (1, 7), (2, 12), (3, 15)]
+    rows = sampled_rows(w.N, 48, 1)
+    ref = oracle_run(x, "none", True, heads=heads, rows=rows)
+    assert_parity(pick(got, heads, rows), ref, w.dtype, w.name, spec_spread=True)
+    assert torch.isfinite(got["o"]).all() and torch.isfinite(got["to"]).all()
+
+
+def test_wide_workload_sampled():
+    """B=256, H=8, N=512, d=128, bf16: every head launched, sampled heads x rows checked."""
+    w = I.WIDE
+    x = I.make_inputs(w)
+    got = gpu_run(x, False)
+    heads = [(0, 0), (77, 3), (200, 5), (255, 7)]
+    rows = sampled_rows(w.N, 40, 2)
+    ref = oracle_run(x, "none", False, heads=heads, rows=rows)
+    assert_parity(pick(got, heads, rows), ref, w.dtype, w.name, spec_spread=True)
+    assert torch.isfinite(got["o"]).all() and torch.isfinite(got["to"]).all()
+
+
+# ------------------------------------------------ stress suite (power)
+
+STRESS_SHAPES = [(1, 2, 200, 64), (1, 1, 97, 128)]
+
+
+@pytest.mark.parametrize("std", [1.0, 2.0])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("mask_kind", ["none", "bool", "additive"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", STRESS_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_stress(shape, causal, mask_kind, dtype, std):
+    B, H, N, d = shape
+    w = I.Workload("stress", B=B, H=H, N=N, d=d, dtype=dtype, causal=causal, mask_kind=mask_kind, std=std,
+                   seed=11, mask_heads=H if mask_kind == "additive" else 1, keep=0.7)
+    check(w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("tangents", [("tv",), ("tq", "tk"), ("tq",), ("tk",), ()],
+                         ids=lambda t: "+".join(t) or "none")
+def test_term_isolation(dtype, tangents):
+    """Only some tangents given (others NULL): isolates dP V, P dV, the dQ and dK paths; none -> dO = 0."""
+    w = I.Workload("iso", B=1, H=2, N=160, d=64, dtype=dtype, std=1.0, seed=12)
+    got, _ = check(w, tangents=tangents)
+    if not tangents:
+        assert torch.all(got["to"] == 0) and torch.all(got["tlse"] == 0)
+
+
+# ------------------------------------------------ edges
+
+@pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 130, 255, 256, 257, 511, 513])
+def test_tile_boundaries(N):
+    for dtype, causal in (("bf16", False), ("f16", True)):
+        w = I.Workload(f"edge{N}", B=1, H=2, N=N, d=64, dtype=dtype, causal=causal, std=1.0, seed=N)
+        check(w)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(64, 200), (200, 64), (1, 300), (130, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rectangular(Nq, Nk, causal):
+    w = I.Workload("rect", B=1, H=2, N=Nq, Nk=Nk, d=64, dtype="bf16", causal=causal, std=1.0, seed=3)
+    check(w)
+
+
+def test_d128_f16_and_f32_ragged():
+    for dtype in ("f16", "f32"):
+        check(I.Workload("d128", B=2, H=1, N=150, d=128, dtype=dtype, causal=True, std=1.0, seed=4))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_fully_masked_rows(dtype):
+    w = I.Workload("fm", B=1, H=2, N=70, d=64, dtype=dtype, mask_kind="bool", std=1.0, seed=5, keep=0.5)
+    x = I.make_inputs(w)
+    x["mask"][0, 0, 3, :] = 0          # one row with no visible key
+    x["mask"][0, 0, 66, :] = 0
+    got, _ = check(w, x=x)
+    for r in (3, 66):
+        assert torch.all(got["o"][0, :, r] == 0) and torch.all(got["to"][0, :, r] == 0)
+        assert torch.all(torch.isneginf(got["lse"][0, :, r])) and torch.all(got["tlse"][0, :, r] == 0)
+
+
+def test_additive_minus_inf_rows():
+    w = I.Workload("addinf", B=1, H=1, N=64, d=64, dtype="f16", mask_kind="additive", std=1.0, seed=6)
+    x = I.make_inputs(w)
+    x["mask"][0, 0, 5, :] = float("-inf")
+    x["mask"][0, 0, 9, ::2] = float("-inf")
+    check(w, x=x)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("N", [32, 64])
+def test_additive_small_n_regression(dtype, N):
+    """The prior implementation's benchmark lists its additive-mask runs at N=32 and 64 as failing."""
+    check(I.Workload("addsmall", B=2, H=8, N=N, d=64, dtype=dtype, mask_kind="additive", seed=N))
+    check(I.Workload("addsmall_s", B=2, H=8, N=N, d=64, dtype=dtype, mask_kind="additive", std=1.0, seed=N))
+
+
+def test_key_padding_mask_broadcast_rows():
+    """A [B,1,1,Nk] boolean mask: mask_stride_q = 0 broadcasts one key-padding row to every query."""
+    w = I.Workload("pad", B=2, H=3, N=96, d=64, dtype="bf16", mask_kind="bool", std=1.0, seed=7)
+    x = I.make_inputs(w)
+    pad = torch.ones(2, 1, 1, 96, dtype=torch.uint8)
+    pad[0, 0, 0, 50:] = 0
+    pad[1, 0, 0, :7] = 0
+    x["mask"] = pad
+    got = gpu_run(x, False)
+    ref = oracle_run(dict(x, mask=pad.expand(2, 1, 96, 96).contiguous()), "bool", False)
+    assert_parity(got, ref, "bf16", "pad")
+
+
+def test_custom_scale():
+    w = I.Workload("scale", B=1, H=2, N=100, d=64, dtype="bf16", std=1.0, seed=8)
+    check(w, scale=0.3)
+    w = I.Workload("scale_add", B=1, H=2, N=100, d=64, dtype="f16", mask_kind="additive", std=1.0, seed=8)
+    check(w, scale=0.05)
+
+
+def test_all_4x4_bool_masks_in_one_launch():
+    """All 2^16 boolean masks of a 4x4 score block as the batch axis of one launch, causal off and on."""
+    B = 1 << 16
+    for dtype in ("f32", "bf16"):
+        w = I.Workload("mask4", B=1, H=1, N=4, d=64, dtype=dtype, std=1.0, seed=9)
+        x1 = I.make_inputs(w)
+        x = {n: x1[n].expand(B, 1, 4, 64).contiguous() for n in ("q", "k", "v", "tq", "tk", "tv")}
+        bits = ((torch.arange(B)[:, None] >> torch.arange(16)[None, :]) & 1).to(torch.uint8)
+        x["mask"] = bits.reshape(B, 1, 4, 4).contiguous()
+        for causal in (False, True):
+            got = gpu_run(x, causal)
+            # reference: the oracle for each distinct row pattern of a query row (16 x 4), gathered
+            ref = {n: np.zeros(got[n].shape) for n in got}
+            base = {n: f64(x1[n]) for n in ("q", "k", "v", "tq", "tk", "tv")}
+            pats = ((np.arange(16)[:, None] >> np.arange(4)[None, :]) & 1).astype(np.uint8)
+            for i in range(4):
+                m = np.broadcast_to(pats[:, None, None, :], (16, 1, 4, 4)).copy()
+                rep = {n: np.broadcast_to(a, (16, 1) + a.shape[2:]) for n, a in base.items()}
+                o, to, lse, tlse = oracle_fwd(rep["q"], rep["k"], rep["v"], rep["tq"], rep["tk"], rep["tv"],
+                                              mask=m, mask_kind="bool", causal=causal)
+                rowpat = (bits.numpy().reshape(B, 4, 4)[:, i, :] << np.arange(4)).sum(1)
+                for n, a in (("o", o), ("to", to), ("lse", lse), ("tlse", tlse)):
+                    ref[n][:, 0, i] = a[rowpat, 0, i]
+            assert_parity(got, ref, dtype, f"mask4 {dtype} causal={causal}")
+
+
+def test_deterministic():
+    w = I.Workload("det", B=2, H=4, N=300, d=64, dtype="bf16", causal=True, std=1.0, seed=10)
+    x = I.make_inputs(w)
+    a = gpu_run(x, True)
+    b = gpu_run(x, True)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_errors_raise_and_write_nothing():
+    from forward_mode_autodiff_amd.jvpattn import JvpattnError
+    q = torch.randn(1, 1, 8, 96, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(JvpattnError) as e:
+        jvpattn_fwd(q, q, q)
+    assert e.value.code == -4
+    q = torch.randn(1, 1, 8, 64, device=DEV, dtype=torch.bfloat16)
+    out = (torch.full_like(q, 7.0), torch.full_like(q, 7.0), torch.full((1, 1, 8), 7.0, device=DEV), None)
+    with pytest.raises(JvpattnError):
+        jvpattn_fwd(q, q, q, scale=-1.0, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 7.0) and torch.all(out[2] == 7.0)
