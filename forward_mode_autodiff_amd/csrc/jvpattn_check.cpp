@@ -64,6 +64,10 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
   if (bh > INT32_MAX) return JVPATTN_ERR_SHAPE;
 
   if (p->d != 64 && p->d != 128) return JVPATTN_ERR_HEADDIM;
+  // One head of q/k (plus a partial tile of slack) must be addressable with 31-bit byte offsets.
+  const int64_t kHeadLimit = (int64_t(1) << 31) - 1;
+  if ((int64_t(p->Nq) + 256) * p->d * es > kHeadLimit || (int64_t(p->Nk) + 256) * p->d * es > kHeadLimit)
+    return JVPATTN_ERR_SHAPE;
   if (!std::isfinite(p->scale) || !(p->scale > 0.0f)) return JVPATTN_ERR_SCALE;
 
   if (p->mask_kind != JVPATTN_MASK_NONE && p->mask_kind != JVPATTN_MASK_BOOL &&
@@ -91,6 +95,11 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
       if (ext > INT64_MAX - p->Nk) return JVPATTN_ERR_MASK;
       ext += p->Nk;
       if (!mul_ok(ext, mask_es, &mask_bytes)) return JVPATTN_ERR_MASK;
+      // one head's slice (rows past Nq included) must be addressable with 31-bit byte offsets
+      int64_t head_rows;
+      if (!mul_ok(int64_t(p->Nq) + 128, p->mask_stride_q, &head_rows) ||
+          head_rows > (kHeadLimit / mask_es) - p->Nk - 64)
+        return JVPATTN_ERR_MASK;
     }
   } else if (mask) {
     return JVPATTN_ERR_MASK;

@@ -102,51 +102,33 @@ struct F16 {
   }
 };
 
-template <int D>
-struct Tile16 {
-  static constexpr int BN = D == 64 ? 64 : 32;    // keys per LDS tile
-  static constexpr int KB = BN / 32;              // 32-key blocks per tile
-  static constexpr int NC = D / 16;               // 16-wide chunks of the head dimension
-  static constexpr int NT = D / 32;               // 32-row tiles of the output
-  static constexpr int GR = D / 8;                // 16-byte granules per K row
-  static constexpr int VG = BN / 8;               // 16-byte granules per V^T row
-  static constexpr int TENSOR_BYTES = BN * D * 2;
-  static constexpr int BUF_BYTES = 4 * TENSOR_BYTES;  // K, dK, V^T, dV^T
-  static_assert(BN * GR == 2 * kThreads, "K tile = two 16-byte granules per thread");
-  static_assert((BN / 4) * (D / 4) == kThreads, "V tile = one 4x4 block per thread");
-};
-
-// K / dK tile in LDS: row = key, 2*D bytes per row, 16-byte granules XOR-swizzled by row.
-template <int D>
-__device__ inline int k_off(int row, int g) {
-  return row * (2 * D) + ((g ^ (row & 7)) << 4);
-}
-
-// V^T / dV^T tile in LDS: row = head-dimension index, 2*BN bytes per row.
-template <int D>
-__device__ inline int vt_swz(int dd) {
-  return (dd ^ (dd >> 2)) & (Tile16<D>::VG - 1);
-}
-template <int D>
-__device__ inline int vt_off(int dd, int g) {
-  return dd * (2 * Tile16<D>::BN) + ((g ^ vt_swz<D>(dd)) << 4);
-}
-
-// Key order inside each 16-key chunk of a V^T row: bits 2 and 3 of the key
-// index swapped, so that the 8 keys lane half h holds in C registers 0..7
-// (keys 4h..4h+3 and 8+4h..8+4h+3) sit in 16 contiguous bytes.
-__device__ inline int key_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
-
 __device__ inline uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 __device__ inline uint32_t hi16(uint32_t x) { return x >> 16; }
 
-// Column c (0..3) of a 4x4 block of 16-bit values held as 4 rows of uint2.
-__device__ inline uint32_t col_pair(uint2 a, uint2 b, int c) {
-  uint32_t ea = c == 0 ? lo16(a.x) : c == 1 ? hi16(a.x) : c == 2 ? lo16(a.y) : hi16(a.y);
-  uint32_t eb = c == 0 ? lo16(b.x) : c == 1 ? hi16(b.x) : c == 2 ? lo16(b.y) : hi16(b.y);
-  return ea | (eb << 16);
+// Buffer resources: loads at byte offsets >= the record count return zero, so
+// ragged tails and absent (NULL) tangents need no branches.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ inline Rsrc make_rsrc(const void* p, int64_t bytes) {
+  const int64_t n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(n), kRsrcWord3);
+}
+__device__ inline uint4 ld128(Rsrc r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline uint2 ld64(Rsrc r, int off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// Values of lanes l and l^32 combined (both halves receive the result).
+__device__ inline float xhalf_max(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ inline float xhalf_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 template <typename V, typename P>
@@ -158,61 +140,89 @@ __device__ inline void lds_store(P* base, int off, V x) {
   *reinterpret_cast<V*>(reinterpret_cast<char*>(base) + off) = x;
 }
 
+template <int D>
+struct Tile16 {
+  static constexpr int BN = D == 64 ? 64 : 32;    // keys per LDS tile
+  static constexpr int KB = BN / 32;              // 32-key blocks per tile
+  static constexpr int NC = D / 16;               // 16-wide chunks of the head dimension
+  static constexpr int NT = D / 32;               // 32-row tiles of the output
+  static constexpr int GR = D / 8;                // 16-byte granules per row
+  static constexpr int ROW = 2 * D;               // bytes per row
+  static constexpr int TENSOR_BYTES = BN * ROW;
+  static constexpr int STAGE_BYTES = 4 * TENSOR_BYTES;  // K, dK, V, dV
+  static constexpr int LOADS = TENSOR_BYTES / (16 * kThreads);  // 16-byte loads per thread per tensor
+  static_assert(LOADS * 16 * kThreads == TENSOR_BYTES, "tile must split evenly over the workgroup");
+};
+
+// All four LDS tiles (K, dK, V, dV) are row = key, 2*D bytes per row, with the
+// 16-byte granules of a row XOR-swizzled by (row & 7). They are filled by
+// direct global->LDS loads: load slot p (16 bytes) of a tile lands at byte
+// 16*p, i.e. at (row, physical granule) = (p / GR, p % GR), so the lane that
+// owns slot p fetches logical granule (p % GR) ^ (row & 7) of that row.
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ inline lds_char* to_lds(const char* p) { return (lds_char*)(p); }
+
+// 4 keys x 16 head-dim columns -> each of 16 lanes gets one column: the LDS
+// transpose read of gfx950. In every group of 16 lanes, lane i returns
+// element (i % 4) of the 8 bytes addressed by lane 4*e + i/4, for e = 0..3.
+__device__ inline v4i16 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)to_lds(p));
+}
+
+__device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Per-row softmax state for one lane (both lanes of a query column hold the same m).
 struct RowState {
   float m;       // reference maximum in score units (-inf until a visible key is seen)
   float moff;    // m * cx, or 0 while m is -inf
   float l;       // partial sum of weights over this lane's keys
-  float mu;      // partial sum of weights * raw score tangent
+  float mu;      // partial sum of weights * score tangent (in the units of sd)
 };
 
-// Score of register r of this lane after masking, in score units:
-// MASK_NONE/BOOL: raw q.k (scale folded into cx); ADDITIVE: scale q.k + M.
-template <typename T, int MASK, bool CAUSAL>
-__device__ inline void mask_scores(f32x16& s, const FwdArgs& a, int b, int h, int qi, int k0, int hlf,
+// Score of register r of this lane after masking, in score units: raw q.k
+// (scale folded into cx) without an additive mask, scale q.k + M with one.
+// PRESCALED: s already holds scale q.k (the scale was folded into Q exactly).
+template <typename T, int MASK, bool CAUSAL, bool PRESCALED>
+__device__ inline void mask_scores(f32x16& s, const FwdArgs& a, Rsrc mr, int qi, int k0, int hlf,
                                    bool elem_mask) {
   if constexpr (MASK == JVPATTN_MASK_BOOL || MASK == JVPATTN_MASK_ADDITIVE) {
-    const bool row_ok = qi < a.Nq;
-    const int64_t row = b * a.msb + h * a.msh + int64_t(qi) * a.msq;
+    constexpr int es = MASK == JVPATTN_MASK_BOOL ? 1 : 2;
+    // byte offset of (qi, k0 + 4*hlf) in this head's mask; rows past Nq are never stored
+    const int row = (qi * int(a.msq) + k0 + 4 * hlf) * es;
     if constexpr (MASK == JVPATTN_MASK_BOOL) {
-      const uint8_t* mp = static_cast<const uint8_t*>(a.mask) + row;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
-      if (row_ok) {
-        if (a.mask_vec && k0 + 32 <= a.Nk) {
+      uint32_t w[4];
+      if (a.mask_vec && k0 + 32 <= a.Nk) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) w[g] = *reinterpret_cast<const uint32_t*>(mp + k0 + 8 * g + 4 * hlf);
-        } else {
+        for (int g = 0; g < 4; ++g) w[g] = __builtin_amdgcn_raw_buffer_load_b32(mr, row + 8 * g, 0, 0);
+      } else {
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < 4; ++g) {
+          w[g] = 0u;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int key = k0 + 8 * g + 4 * hlf + e;
-              if (key < a.Nk) w[g] |= uint32_t(mp[key] != 0) << (8 * e);
-            }
+          for (int e = 0; e < 4; ++e)
+            w[g] |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(mr, row + 8 * g + e, 0, 0)) << (8 * e);
         }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (((w[r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u) s[r] = -INFINITY;
     } else {
-      const uint16_t* mp = static_cast<const uint16_t*>(a.mask) + row;
-      uint2 w[4] = {};
-      if (row_ok) {
-        if (a.mask_vec && k0 + 32 <= a.Nk) {
+      uint2 w[4];
+      if (a.mask_vec && k0 + 32 <= a.Nk) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) w[g] = *reinterpret_cast<const uint2*>(mp + k0 + 8 * g + 4 * hlf);
-        } else {
+        for (int g = 0; g < 4; ++g) w[g] = ld64(mr, row + 16 * g);
+      } else {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            uint32_t e4[4];
+        for (int g = 0; g < 4; ++g) {
+          uint32_t e4[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int key = k0 + 8 * g + 4 * hlf + e;
-              e4[e] = key < a.Nk ? mp[key] : 0u;
-            }
-            w[g].x = e4[0] | (e4[1] << 16);
-            w[g].y = e4[2] | (e4[3] << 16);
-          }
+          for (int e = 0; e < 4; ++e) e4[e] = __builtin_amdgcn_raw_buffer_load_b16(mr, row + 16 * g + 2 * e, 0, 0);
+          w[g].x = e4[0] | (e4[1] << 16);
+          w[g].y = e4[2] | (e4[3] << 16);
         }
       }
 #pragma unroll
@@ -220,7 +230,7 @@ __device__ inline void mask_scores(f32x16& s, const FwdArgs& a, int b, int h, in
         const uint2 x = w[r >> 2];
         const uint32_t word = (r & 2) ? x.y : x.x;
         const uint16_t bits = (r & 1) ? hi16(word) : lo16(word);
-        s[r] = fmaf(s[r], a.scale, T::widen(bits));
+        s[r] = PRESCALED ? s[r] + T::widen(bits) : fmaf(s[r], a.scale, T::widen(bits));
       }
     }
   }
@@ -235,15 +245,23 @@ __device__ inline void mask_scores(f32x16& s, const FwdArgs& a, int b, int h, in
   }
 }
 
+// Mask resource of head (b, h): element (i, j) at byte (i*msq + j) * es.
+__device__ inline Rsrc mask_rsrc(const FwdArgs& a, int b, int h, int es) {
+  if (!a.mask) return make_rsrc(a.q, 0);
+  const int64_t base = (b * a.msb + h * a.msh) * es;
+  const int64_t bytes = (int64_t(a.Nq - 1) * a.msq + a.Nk) * es;
+  return make_rsrc(static_cast<const char*>(a.mask) + base, bytes);
+}
+
 // Online-softmax update for one 32-key block. On return s holds the weights
-// e = exp(s - m) and sd holds e * dS_raw (the raw, unscaled score tangent).
-// Returns true when the accumulators must be multiplied by `alpha`.
+// e = exp(s - m) and sd holds e * sd. Returns true when the accumulators must
+// be multiplied by `alpha` (the reference maximum moved).
 __device__ inline bool softmax_block(f32x16& s, f32x16& sd, RowState& st, float cx, float thr,
                                      float& alpha) {
-  float bm = s[0];
+  float bm = fmaxf(s[0], s[1]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) bm = fmaxf(bm, s[r]);
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  for (int r = 2; r < 16; r += 2) bm = fmaxf(bm, fmaxf(s[r], s[r + 1]));
+  bm = xhalf_max(bm);
   const bool need = bm > st.m + thr;
   bool rescale = false;
   alpha = 1.0f;
@@ -273,15 +291,19 @@ __device__ inline bool softmax_block(f32x16& s, f32x16& sd, RowState& st, float 
 
 // ------------------------------------------------------------- 16-bit kernel
 
-template <typename T, int D, int MASK, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd16_kernel(FwdArgs a) {
+template <typename T, int D, int MASK, bool CAUSAL, bool POW2>
+__device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   using L = Tile16<D>;
   using vec8 = typename T::vec8;
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::BUF_BYTES];
+  // Two stages in two separate arrays: with the loop unrolled by two every LDS
+  // access names its stage statically, so the in-flight direct loads into one
+  // stage are known not to alias the reads of the other.
+  __shared__ __attribute__((aligned(16))) char smem0[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem1[L::STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31;
   const int hlf = lane >> 5;
 
@@ -294,24 +316,33 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd16_kernel(FwdArg
   const int qi = qw0 + c32;
   const bool wave_live = qw0 < a.Nq;
 
-  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + int64_t(bh) * a.Nq * D;
-  const uint16_t* tqp = a.tq ? static_cast<const uint16_t*>(a.tq) + int64_t(bh) * a.Nq * D : nullptr;
-  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + int64_t(bh) * a.Nk * D;
-  const uint16_t* vp = static_cast<const uint16_t*>(a.v) + int64_t(bh) * a.Nk * D;
-  const uint16_t* tkp = a.tk ? static_cast<const uint16_t*>(a.tk) + int64_t(bh) * a.Nk * D : nullptr;
-  const uint16_t* tvp = a.tv ? static_cast<const uint16_t*>(a.tv) + int64_t(bh) * a.Nk * D : nullptr;
+  const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;   // byte offsets of this head
+  const int64_t khead = int64_t(bh) * a.Nk * L::ROW;
+  const char* qp = static_cast<const char*>(a.q) + qhead;
+  const char* kp = static_cast<const char*>(a.k) + khead;
+  const char* vp = static_cast<const char*>(a.v) + khead;
+  const char* tqp = a.tq ? static_cast<const char*>(a.tq) + qhead : qp;
+  const char* tkp = a.tk ? static_cast<const char*>(a.tk) + khead : kp;
+  const char* tvp = a.tv ? static_cast<const char*>(a.tv) + khead : vp;
+  const int64_t qbytes = int64_t(a.Nq) * L::ROW;
 
   // Q and dQ as B operands: lane holds row qi, head-dim entries hlf*D/2 + 8c .. +7.
+  // With POW2 the scale (a power of two) is folded into them: exact in bfloat16.
   vec8 qB[L::NC], tqB[L::NC];
   {
-    const bool ok = qi < a.Nq;
+    const Rsrc rq = make_rsrc(qp, qbytes), rtq = make_rsrc(tqp, a.tq ? qbytes : 0);
 #pragma unroll
     for (int c = 0; c < L::NC; ++c) {
-      const int64_t off = int64_t(qi) * D + hlf * (D / 2) + 8 * c;
-      uint4 x = ok ? *reinterpret_cast<const uint4*>(qp + off) : uint4{0, 0, 0, 0};
-      uint4 y = (ok && tqp) ? *reinterpret_cast<const uint4*>(tqp + off) : uint4{0, 0, 0, 0};
-      qB[c] = __builtin_bit_cast(vec8, x);
-      tqB[c] = __builtin_bit_cast(vec8, y);
+      const int off = qi * L::ROW + (hlf * (D / 2) + 8 * c) * 2;
+      qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
+      tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
+      if constexpr (POW2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qB[c][e] = static_cast<__bf16>(static_cast<float>(qB[c][e]) * a.scale);
+          tqB[c][e] = static_cast<__bf16>(static_cast<float>(tqB[c][e]) * a.scale);
+        }
+      }
     }
   }
 
@@ -322,139 +353,169 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd16_kernel(FwdArg
     accT[t] = f32x16{};
   }
   RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
+  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
 
   const int kv_end = CAUSAL ? min(a.Nk, q0 + kBM) : a.Nk;
   const int n_tiles = (kv_end + L::BN - 1) / L::BN;
 
-  // Staging registers for the next tile.
-  uint4 kr[2], tkr[2];
-  uint2 vr[4], tvr[4];
-  const int vdg = tid % (D / 4), vkg = tid / (D / 4);
-
-  auto load_tile = [&](int j) {
-    const int kbase = j * L::BN;
+  // Direct-load slots of this thread (byte offset inside a tile, same for all four tensors).
+  int dl_off[L::LOADS];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int gi = tid + kThreads * i;
-      const int row = gi / L::GR, g = gi % L::GR;
-      const int key = kbase + row;
-      const int64_t off = int64_t(key) * D + 8 * g;
-      kr[i] = key < a.Nk ? *reinterpret_cast<const uint4*>(kp + off) : uint4{0, 0, 0, 0};
-      tkr[i] = (key < a.Nk && tkp) ? *reinterpret_cast<const uint4*>(tkp + off) : uint4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = kbase + 4 * vkg + r;
-      const int64_t off = int64_t(key) * D + 4 * vdg;
-      vr[r] = key < a.Nk ? *reinterpret_cast<const uint2*>(vp + off) : uint2{0, 0};
-      tvr[r] = (key < a.Nk && tvp) ? *reinterpret_cast<const uint2*>(tvp + off) : uint2{0, 0};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* base = smem + buf * L::BUF_BYTES;
-    char* sk = base;
-    char* stk = base + L::TENSOR_BYTES;
-    char* sv = base + 2 * L::TENSOR_BYTES;
-    char* stv = base + 3 * L::TENSOR_BYTES;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int gi = tid + kThreads * i;
-      const int row = gi / L::GR, g = gi % L::GR;
-      lds_store<uint4>(sk, k_off<D>(row, g), kr[i]);
-      lds_store<uint4>(stk, k_off<D>(row, g), tkr[i]);
-    }
-    const int pos = key_pos(4 * vkg);
-    const int g = pos >> 3, half = (pos >> 2) & 1;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int dd = 4 * vdg + c;
-      const int off = vt_off<D>(dd, g) + 8 * half;
-      lds_store<uint2>(sv, off, uint2{col_pair(vr[0], vr[1], c), col_pair(vr[2], vr[3], c)});
-      lds_store<uint2>(stv, off, uint2{col_pair(tvr[0], tvr[1], c), col_pair(tvr[2], tvr[3], c)});
-    }
-  };
-
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  for (int i = 0; i < L::LOADS; ++i) {
+    const int p = i * kThreads + tid;
+    const int row = p / L::GR, pg = p % L::GR;
+    dl_off[i] = row * L::ROW + ((pg ^ (row & 7)) << 4);
   }
-  __syncthreads();
+  auto issue_tile = [&](int j, char* stage) {
+    const int64_t t0 = int64_t(j) * L::TENSOR_BYTES;
+    const int64_t rem = int64_t(a.Nk - j * L::BN) * L::ROW;  // bytes of this head from the tile start
+    const Rsrc rs[4] = {make_rsrc(kp + t0, rem), make_rsrc(tkp + t0, a.tk ? rem : 0),
+                        make_rsrc(vp + t0, rem), make_rsrc(tvp + t0, a.tv ? rem : 0)};
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int i = 0; i < L::LOADS; ++i) {
+        const char* dst = stage + x * L::TENSOR_BYTES + (i * kThreads + wave * 64) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[x], (__attribute__((address_space(3))) void*)to_lds(dst),
+                                                 16, dl_off[i], 0, 0, 0);
+      }
+  };
 
-  for (int j = 0; j < n_tiles; ++j) {
-    if (j + 1 < n_tiles) load_tile(j + 1);
-    const char* base = smem + (j & 1) * L::BUF_BYTES;
-    const char* sk = base;
-    const char* stk = base + L::TENSOR_BYTES;
-    const char* sv = base + 2 * L::TENSOR_BYTES;
-    const char* stv = base + 3 * L::TENSOR_BYTES;
+  // LDS read offsets of this lane (constant over the loop).
+  // K / dK A operand, chunk c: row c32 (+32 kb), logical granule hlf*NC + c.
+  int kofs[L::NC];
+#pragma unroll
+  for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ (c32 & 7)) << 4);
+  // V^T / dV^T A operand via transpose reads: lane (group g16 = lane/16, i = lane%16) addresses
+  // row 4*hlf + i/4 (+32 kb + 16 kc, and +8 for the second read), columns 32t + 16(g16&1) + 4(i&3).
+  int vofs[L::NT];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int rsw = 4 * hlf + (i16 >> 2);   // row & 7 of every row this lane addresses
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t) {
+      const int gcol = 4 * t + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      vofs[t] = rsw * L::ROW + ((gcol ^ rsw) << 4) + 8 * (i16 & 1);
+    }
+  }
 
-    if (wave_live) {
+  // S^T and dS^T of 32-key block kb of the tile at `sb`. All operands are read
+  // from LDS before the products so the reads overlap each other.
+  auto scores = [&](const char* sb, int kb, f32x16& s, f32x16& sd) {
+    vec8 ka[L::NC], tka[L::NC];
 #pragma unroll
-      for (int kb = 0; kb < L::KB; ++kb) {
-        const int k0 = j * L::BN + kb * 32;
-        if (k0 >= kv_end) break;
-        if (CAUSAL && k0 > qw0 + 31) break;
-        // S^T and dS^T for 32 keys x 32 queries.
-        f32x16 s{}, sd{};
+    for (int c = 0; c < L::NC; ++c) {
+      const int off = kb * 32 * L::ROW + kofs[c];
+      ka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb, off));
+      tka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + L::TENSOR_BYTES, off));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s = f32x16{};
+    sd = f32x16{};
 #pragma unroll
-        for (int c = 0; c < L::NC; ++c) {
-          const int off = k_off<D>(kb * 32 + c32, hlf * L::NC + c);
-          const vec8 ka = __builtin_bit_cast(vec8, lds_load<uint4>(sk, off));
-          const vec8 tka = __builtin_bit_cast(vec8, lds_load<uint4>(stk, off));
-          s = T::mfma(ka, qB[c], s);
-          sd = T::mfma(tka, qB[c], sd);
-          sd = T::mfma(ka, tqB[c], sd);
-        }
-        const bool elem_mask = (CAUSAL && k0 + 31 > qw0) || (k0 + 32 > a.Nk);
-        mask_scores<T, MASK, CAUSAL>(s, a, b, h, qi, k0, hlf, elem_mask);
-        float alpha;
-        if (softmax_block(s, sd, st, a.cx, a.thr, alpha)) {
+    for (int c = 0; c < L::NC; ++c) {
+      s = T::mfma(ka[c], qB[c], s);
+      sd = T::mfma(tka[c], qB[c], sd);
+      sd = T::mfma(ka[c], tqB[c], sd);
+    }
+  };
+  // Mask, softmax update and value products of 32-key block kb (keys from k0).
+  auto finish = [&](const char* sb, int kb, int k0, f32x16& s, f32x16& sd) {
+    // V^T and dV^T operands first: their LDS latency hides behind the softmax.
+    const char* sv = sb + 2 * L::TENSOR_BYTES;
+    const char* stv = sb + 3 * L::TENSOR_BYTES;
+    vec8 va[L::NT][2], tva[L::NT][2];
 #pragma unroll
-          for (int t = 0; t < L::NT; ++t) {
-            accO[t] *= alpha;
-            accT[t] *= alpha;
-          }
-        }
-        // Weights and weights * dS (scaled) as 16-bit B operands, keys 16kc .. 16kc+15.
-        vec8 pB[2], uB[2];
+    for (int t = 0; t < L::NT; ++t)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          uint4 pw, uw;
-          pw.x = T::pack2(s[8 * kc + 0], s[8 * kc + 1]);
-          pw.y = T::pack2(s[8 * kc + 2], s[8 * kc + 3]);
-          pw.z = T::pack2(s[8 * kc + 4], s[8 * kc + 5]);
-          pw.w = T::pack2(s[8 * kc + 6], s[8 * kc + 7]);
-          uw.x = T::pack2(sd[8 * kc + 0] * a.scale, sd[8 * kc + 1] * a.scale);
-          uw.y = T::pack2(sd[8 * kc + 2] * a.scale, sd[8 * kc + 3] * a.scale);
-          uw.z = T::pack2(sd[8 * kc + 4] * a.scale, sd[8 * kc + 5] * a.scale);
-          uw.w = T::pack2(sd[8 * kc + 6] * a.scale, sd[8 * kc + 7] * a.scale);
-          pB[kc] = __builtin_bit_cast(vec8, pw);
-          uB[kc] = __builtin_bit_cast(vec8, uw);
-        }
+      for (int kc = 0; kc < 2; ++kc) {
+        const int off = (kb * 32 + 16 * kc) * L::ROW + vofs[t];
+        va[t][kc] = __builtin_bit_cast(
+            vec8, __builtin_shufflevector(lds_read_tr(sv + off), lds_read_tr(sv + off + 8 * L::ROW), 0, 1, 2, 3, 4,
+                                          5, 6, 7));
+        tva[t][kc] = __builtin_bit_cast(
+            vec8, __builtin_shufflevector(lds_read_tr(stv + off), lds_read_tr(stv + off + 8 * L::ROW), 0, 1, 2, 3,
+                                          4, 5, 6, 7));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool elem_mask = (CAUSAL && k0 + 31 > qw0) || (k0 + 32 > a.Nk);
+    mask_scores<T, MASK, CAUSAL, POW2>(s, a, mr, qi, k0, hlf, elem_mask);
+    float alpha;
+    if (softmax_block(s, sd, st, a.cx, a.thr, alpha)) {
 #pragma unroll
-        for (int t = 0; t < L::NT; ++t) {
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc) {
-            const int off = vt_off<D>(32 * t + c32, kb * 4 + kc * 2 + hlf);
-            const vec8 va = __builtin_bit_cast(vec8, lds_load<uint4>(sv, off));
-            const vec8 tva = __builtin_bit_cast(vec8, lds_load<uint4>(stv, off));
-            accO[t] = T::mfma(va, pB[kc], accO[t]);
-            accT[t] = T::mfma(va, uB[kc], accT[t]);
-            accT[t] = T::mfma(tva, pB[kc], accT[t]);
-          }
-        }
+      for (int t = 0; t < L::NT; ++t) {
+        accO[t] *= alpha;
+        accT[t] *= alpha;
       }
     }
-    if (j + 1 < n_tiles) store_tile((j + 1) & 1);
+    // Weights and weights * dS as 16-bit B operands, keys 16kc .. 16kc+15.
+    vec8 pB[2], uB[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      uint4 pw, uw;
+      const float us = POW2 ? 1.0f : a.scale;
+      pw.x = T::pack2(s[8 * kc + 0], s[8 * kc + 1]);
+      pw.y = T::pack2(s[8 * kc + 2], s[8 * kc + 3]);
+      pw.z = T::pack2(s[8 * kc + 4], s[8 * kc + 5]);
+      pw.w = T::pack2(s[8 * kc + 6], s[8 * kc + 7]);
+      if constexpr (POW2) {
+        uw.x = T::pack2(sd[8 * kc + 0], sd[8 * kc + 1]);
+        uw.y = T::pack2(sd[8 * kc + 2], sd[8 * kc + 3]);
+        uw.z = T::pack2(sd[8 * kc + 4], sd[8 * kc + 5]);
+        uw.w = T::pack2(sd[8 * kc + 6], sd[8 * kc + 7]);
+      } else {
+        uw.x = T::pack2(sd[8 * kc + 0] * us, sd[8 * kc + 1] * us);
+        uw.y = T::pack2(sd[8 * kc + 2] * us, sd[8 * kc + 3] * us);
+        uw.z = T::pack2(sd[8 * kc + 4] * us, sd[8 * kc + 5] * us);
+        uw.w = T::pack2(sd[8 * kc + 6] * us, sd[8 * kc + 7] * us);
+      }
+      pB[kc] = __builtin_bit_cast(vec8, pw);
+      uB[kc] = __builtin_bit_cast(vec8, uw);
+    }
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        accO[t] = T::mfma(va[t][kc], pB[kc], accO[t]);
+        accT[t] = T::mfma(va[t][kc], uB[kc], accT[t]);
+        accT[t] = T::mfma(tva[t][kc], pB[kc], accT[t]);
+      }
+  };
+
+  // One tile: queue the next tile's loads into the other stage, compute on this one.
+  auto tile = [&](int j, const char* sb, char* other) {
+    if (j + 1 < n_tiles) issue_tile(j + 1, other);
+    const int k0 = j * L::BN;
+    // 32-key blocks of this tile that this wave needs (whole waves skip blocks above the diagonal)
+    const bool v0 = wave_live && !(CAUSAL && k0 > qw0 + 31);
+    const bool v1 = L::KB > 1 && wave_live && k0 + 32 < kv_end && !(CAUSAL && k0 + 32 > qw0 + 31);
+    if (v0) {
+      // Both blocks' score products are queued before the first softmax, so the
+      // matrix cores work on block 1 while the vector units work on block 0.
+      f32x16 s0, sd0, s1, sd1;
+      scores(sb, 0, s0, sd0);
+      if (v1) scores(sb, 1, s1, sd1);
+      finish(sb, 0, k0, s0, sd0);
+      if (v1) finish(sb, 1, k0 + 32, s1, sd1);
+    }
+    if (j + 1 < n_tiles) wait_vmem();
     __syncthreads();
+  };
+
+  if (n_tiles > 0) issue_tile(0, smem0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile(j, smem0, smem1);
+    if (j + 1 < n_tiles) tile(j + 1, smem1, smem0);
   }
 
   // Epilogue: combine the two lane halves of each query column, normalise, store.
-  const float l = st.l + __shfl_xor(st.l, 32);
-  const float mu = st.mu + __shfl_xor(st.mu, 32);
+  const float l = xhalf_sum(st.l);
+  const float mu = xhalf_sum(st.mu);
   if (qi < a.Nq) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const float tl = mu * a.scale * inv;
+    const float tl = POW2 ? mu * inv : mu * a.scale * inv;
     uint16_t* op = static_cast<uint16_t*>(a.o) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
     uint16_t* top = static_cast<uint16_t*>(a.to) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
 #pragma unroll
@@ -478,6 +539,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd16_kernel(FwdArg
       if (a.tlse) a.tlse[ri] = tl;
     }
   }
+}
+
+// The kernel bodies use gfx950 builtins; the host pass only needs the launch stubs.
+template <typename T, int D, int MASK, bool CAUSAL, bool POW2>
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd16_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  fwd16_body<T, D, MASK, CAUSAL, POW2>(a);
+#endif
 }
 
 // ------------------------------------------------------------- float32 kernel
@@ -505,7 +574,7 @@ __device__ inline int k32_off(int row, int g) {
 __device__ inline int vt32_off(int dd, int g) { return dd * 128 + ((g ^ (dd & 7)) << 4); }
 
 template <int D, int MASK, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd32_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
   using L = Tile32<D>;
   extern __shared__ __attribute__((aligned(16))) char smem32[];
 
@@ -553,6 +622,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd32_kernel(FwdArgs a) {
     accT[t] = f32x16{};
   }
   RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
+  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 4);
 
   const int kv_end = CAUSAL ? min(a.Nk, q0 + kBM) : a.Nk;
   const int n_tiles = (kv_end + L::BN - 1) / L::BN;
@@ -600,16 +670,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd32_kernel(FwdArgs a) {
         }
       }
       const bool elem_mask = (CAUSAL && k0 + 31 > qw0) || (k0 + 32 > a.Nk);
-      mask_scores<F16, MASK == JVPATTN_MASK_ADDITIVE ? -1 : MASK, CAUSAL>(s, a, b, h, qi, k0, hlf,
-                                                                          elem_mask);
+      mask_scores<F16, MASK == JVPATTN_MASK_ADDITIVE ? -1 : MASK, CAUSAL, false>(s, a, mr, qi, k0, hlf, elem_mask);
       if constexpr (MASK == JVPATTN_MASK_ADDITIVE) {
         // float32 additive mask: element (qi, key) for the 16 keys of this lane
-        const bool row_ok = qi < a.Nq;
-        const float* mp = static_cast<const float*>(a.mask) + b * a.msb + h * a.msh + int64_t(qi) * a.msq;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + (r >> 2) * 8 + 4 * hlf + (r & 3);
-          const float mv = (row_ok && key < a.Nk) ? mp[key] : 0.0f;
+          const float mv = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(mr, (qi * int(a.msq) + key) * 4, 0, 0));
           s[r] = fmaf(s[r], a.scale, mv);   // hidden keys are already -inf
         }
       }
@@ -641,8 +709,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd32_kernel(FwdArgs a) {
     __syncthreads();
   }
 
-  const float l = st.l + __shfl_xor(st.l, 32);
-  const float mu = st.mu + __shfl_xor(st.mu, 32);
+  const float l = xhalf_sum(st.l);
+  const float mu = xhalf_sum(st.mu);
   if (qi < a.Nq) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const float tl = mu * a.scale * inv;
@@ -671,19 +739,31 @@ __global__ __launch_bounds__(kThreads, 1) void fwd32_kernel(FwdArgs a) {
   }
 }
 
+template <int D, int MASK, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fwd32_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  fwd32_body<D, MASK, CAUSAL>(a);
+#endif
+}
+
 // ---------------------------------------------------------------- dispatch
 
 thread_local int g_last_hip_error = 0;
 
 template <int MASK, bool CAUSAL>
-hipError_t launch_typed(int dtype, int d, const FwdArgs& args, dim3 grid, hipStream_t stream) {
+hipError_t launch_typed(int dtype, int d, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
   const dim3 block(kThreads);
   if (dtype == JVPATTN_BF16) {
-    if (d == 64) hipLaunchKernelGGL((fwd16_kernel<BF16, 64, MASK, CAUSAL>), grid, block, 0, stream, args);
-    else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL>), grid, block, 0, stream, args);
+    if (pow2) {
+      if (d == 64) hipLaunchKernelGGL((fwd16_kernel<BF16, 64, MASK, CAUSAL, true>), grid, block, 0, stream, args);
+      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, true>), grid, block, 0, stream, args);
+    } else {
+      if (d == 64) hipLaunchKernelGGL((fwd16_kernel<BF16, 64, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+    }
   } else if (dtype == JVPATTN_F16) {
-    if (d == 64) hipLaunchKernelGGL((fwd16_kernel<F16, 64, MASK, CAUSAL>), grid, block, 0, stream, args);
-    else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL>), grid, block, 0, stream, args);
+    if (d == 64) hipLaunchKernelGGL((fwd16_kernel<F16, 64, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, false>), grid, block, 0, stream, args);
   } else {
     if (d == 64) {
       hipLaunchKernelGGL((fwd32_kernel<64, MASK, CAUSAL>), grid, block, Tile32<64>::BUF_BYTES, stream, args);
@@ -721,8 +801,12 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
   a.msb = p->mask_stride_b; a.msh = p->mask_stride_h; a.msq = p->mask_stride_q;
   a.scale = p->scale;
   const bool additive = p->mask_kind == JVPATTN_MASK_ADDITIVE;
-  // Scores stay raw (q.k) without an additive mask, so scale folds into cx.
-  a.cx = additive ? kLog2e : p->scale * kLog2e;
+  // bfloat16 with a power-of-two scale: the scale is folded into Q and dQ
+  // exactly (bfloat16 has float32's exponent range), scores arrive scaled.
+  int sexp = 0;
+  const bool pow2 = p->dtype == JVPATTN_BF16 && std::frexp(p->scale, &sexp) == 0.5f;
+  // Otherwise scores stay raw (q.k) without an additive mask, so scale folds into cx.
+  a.cx = (additive || pow2) ? kLog2e : p->scale * kLog2e;
   const float tau = p->dtype == JVPATTN_BF16 ? BF16::kTau : p->dtype == JVPATTN_F16 ? F16::kTau : 8.0f;
   a.thr = tau / a.cx;
   {
@@ -741,16 +825,16 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
   const bool c = p->causal != 0;
   switch (p->mask_kind) {
     case JVPATTN_MASK_NONE:
-      e = c ? launch_typed<JVPATTN_MASK_NONE, true>(p->dtype, p->d, a, grid, s)
-            : launch_typed<JVPATTN_MASK_NONE, false>(p->dtype, p->d, a, grid, s);
+      e = c ? launch_typed<JVPATTN_MASK_NONE, true>(p->dtype, p->d, pow2, a, grid, s)
+            : launch_typed<JVPATTN_MASK_NONE, false>(p->dtype, p->d, pow2, a, grid, s);
       break;
     case JVPATTN_MASK_BOOL:
-      e = c ? launch_typed<JVPATTN_MASK_BOOL, true>(p->dtype, p->d, a, grid, s)
-            : launch_typed<JVPATTN_MASK_BOOL, false>(p->dtype, p->d, a, grid, s);
+      e = c ? launch_typed<JVPATTN_MASK_BOOL, true>(p->dtype, p->d, pow2, a, grid, s)
+            : launch_typed<JVPATTN_MASK_BOOL, false>(p->dtype, p->d, pow2, a, grid, s);
       break;
     default:
-      e = c ? launch_typed<JVPATTN_MASK_ADDITIVE, true>(p->dtype, p->d, a, grid, s)
-            : launch_typed<JVPATTN_MASK_ADDITIVE, false>(p->dtype, p->d, a, grid, s);
+      e = c ? launch_typed<JVPATTN_MASK_ADDITIVE, true>(p->dtype, p->d, pow2, a, grid, s)
+            : launch_typed<JVPATTN_MASK_ADDITIVE, false>(p->dtype, p->d, pow2, a, grid, s);
       break;
   }
   if (e != hipSuccess) {

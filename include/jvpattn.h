@@ -60,10 +60,12 @@ typedef enum {
 enum {
   JVPATTN_OK = 0,
   JVPATTN_ERR_NULL = -1,     /* a required pointer is NULL */
-  JVPATTN_ERR_SHAPE = -2,    /* B, H, Nq, Nk < 0, or a size overflows int64 */
+  JVPATTN_ERR_SHAPE = -2,    /* B, H, Nq, Nk < 0, a size overflows int64, B*H > INT32_MAX, or one
+                                head of q or k (N*d*element size) exceeds 2 GiB */
   JVPATTN_ERR_DTYPE = -3,    /* dtype not one of jvpattn_dtype */
   JVPATTN_ERR_HEADDIM = -4,  /* d not supported (supported: 64, 128) */
-  JVPATTN_ERR_MASK = -5,     /* mask_kind unknown, mask NULL/non-NULL mismatch, bad strides */
+  JVPATTN_ERR_MASK = -5,     /* mask_kind unknown, mask NULL/non-NULL mismatch, negative strides,
+                                or one head's mask slice exceeds 2 GiB */
   JVPATTN_ERR_ALIGN = -6,    /* a tensor pointer not 16-byte aligned (lse/tlse: 4-byte) */
   JVPATTN_ERR_SCALE = -7,    /* scale not finite or not > 0 */
   JVPATTN_ERR_ALIAS = -8,    /* an output overlaps an input or another output */
