@@ -26,6 +26,7 @@ def workloads():
     from forward_mode_autodiff_amd import inputs as I
     return {
         "hvp": I.HVP,
+        "hvp_full": I.Workload("hvp_full", B=4, H=16, N=2048, d=64, dtype="bf16", causal=False, seed=4),
         "seq2048": I.seq(2048, False),
         "seq2048_causal": I.seq(2048, True),
         "seq2048_bf16": I.seq(2048, False, dtype="bf16"),

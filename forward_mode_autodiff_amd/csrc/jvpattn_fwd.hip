@@ -142,23 +142,37 @@ __device__ inline void lds_store(P* base, int off, V x) {
 
 template <int D>
 struct Tile16 {
-  static constexpr int BN = D == 64 ? 64 : 32;    // keys per LDS tile
-  static constexpr int KB = BN / 32;              // 32-key blocks per tile
+  static constexpr int BN = 32;                   // keys per LDS tile (one 32-key block)
   static constexpr int NC = D / 16;               // 16-wide chunks of the head dimension
   static constexpr int NT = D / 32;               // 32-row tiles of the output
   static constexpr int GR = D / 8;                // 16-byte granules per row
   static constexpr int ROW = 2 * D;               // bytes per row
   static constexpr int TENSOR_BYTES = BN * ROW;
-  static constexpr int STAGE_BYTES = 4 * TENSOR_BYTES;  // K, dK, V, dV
+  static constexpr int STAGE_BYTES = 4 * TENSOR_BYTES;          // K, dK, V, dV
   static constexpr int LOADS = TENSOR_BYTES / (16 * kThreads);  // 16-byte loads per thread per tensor
+  static constexpr int TILE_VMEM = 4 * LOADS;                   // direct loads per thread per tile
   static_assert(LOADS * 16 * kThreads == TENSOR_BYTES, "tile must split evenly over the workgroup");
 };
 
-// All four LDS tiles (K, dK, V, dV) are row = key, 2*D bytes per row, with the
-// 16-byte granules of a row XOR-swizzled by (row & 7). They are filled by
-// direct global->LDS loads: load slot p (16 bytes) of a tile lands at byte
-// 16*p, i.e. at (row, physical granule) = (p / GR, p % GR), so the lane that
-// owns slot p fetches logical granule (p % GR) ^ (row & 7) of that row.
+// LDS tiles (K, dK, V, dV) are row = key, 2*D bytes per row, with the 16-byte
+// granules of a row XOR-swizzled by swz(row). They are filled by direct
+// global->LDS loads: load slot p (16 bytes) of a tile lands at byte 16*p,
+// i.e. at (row, physical granule) = (p / GR, p % GR), so the lane that owns
+// slot p fetches logical granule (p % GR) ^ swz(row) of that row.
+#ifndef JVPATTN_SWZ
+#define JVPATTN_SWZ 1
+#endif
+__device__ inline int swz(int row) {
+#if JVPATTN_SWZ == 0
+  return row & 7;
+#elif JVPATTN_SWZ == 1
+  // 8 consecutive rows -> 8 distinct granules (K reads), and 4 consecutive rows
+  // -> 4 distinct granule pairs (transpose reads of 2 adjacent granules).
+  return ((row & 3) << 1) | ((row >> 2) & 1);
+#else
+  return (row >> 1) & 7;
+#endif
+}
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -173,7 +187,29 @@ __device__ inline v4i16 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)to_lds(p));
 }
 
-__device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N == 0 || N == 4 || N == 8 || N == 12 || N == 16, "unsupported count");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+}
+
+// Workgroup barrier for the LDS ring. The caller has already waited for its
+// own direct-to-LDS loads (wait_vmcnt); this waits for its LDS reads and
+// syncs. (A fenced __syncthreads would also drain every in-flight tile load.)
+__device__ inline void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Maximum of three values in one instruction (no NaN canonicalisation of the
+// matrix-core results the way a chain of fmaxf would need).
+__device__ inline float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // Per-row softmax state for one lane (both lanes of a query column hold the same m).
 struct RowState {
@@ -183,66 +219,88 @@ struct RowState {
   float mu;      // partial sum of weights * score tangent (in the units of sd)
 };
 
-// Score of register r of this lane after masking, in score units: raw q.k
-// (scale folded into cx) without an additive mask, scale q.k + M with one.
-// PRESCALED: s already holds scale q.k (the scale was folded into Q exactly).
-template <typename T, int MASK, bool CAUSAL, bool PRESCALED>
-__device__ inline void mask_scores(f32x16& s, const FwdArgs& a, Rsrc mr, int qi, int k0, int hlf,
-                                   bool elem_mask) {
+// Mask values of one 32-key block for this lane's 16 keys, loaded ahead of use.
+template <int MASK> struct MaskVals {};
+template <> struct MaskVals<JVPATTN_MASK_BOOL> { uint32_t w[4]; };
+template <> struct MaskVals<JVPATTN_MASK_ADDITIVE> { uint2 w[4]; };
+
+// Register r of this lane holds key k0 + 8*(r/4) + 4*hlf + r%4.
+template <int MASK>
+__device__ inline void mask_load(MaskVals<MASK>& m, const FwdArgs& a, Rsrc mr, int qi, int k0, int hlf) {
   if constexpr (MASK == JVPATTN_MASK_BOOL || MASK == JVPATTN_MASK_ADDITIVE) {
     constexpr int es = MASK == JVPATTN_MASK_BOOL ? 1 : 2;
     // byte offset of (qi, k0 + 4*hlf) in this head's mask; rows past Nq are never stored
     const int row = (qi * int(a.msq) + k0 + 4 * hlf) * es;
+    const bool vec = a.mask_vec && k0 + 32 <= a.Nk;
     if constexpr (MASK == JVPATTN_MASK_BOOL) {
-      uint32_t w[4];
-      if (a.mask_vec && k0 + 32 <= a.Nk) {
+      if (vec) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) w[g] = __builtin_amdgcn_raw_buffer_load_b32(mr, row + 8 * g, 0, 0);
+        for (int g = 0; g < 4; ++g) m.w[g] = __builtin_amdgcn_raw_buffer_load_b32(mr, row + 8 * g, 0, 0);
       } else {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          w[g] = 0u;
+          m.w[g] = 0u;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            w[g] |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(mr, row + 8 * g + e, 0, 0)) << (8 * e);
+            m.w[g] |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(mr, row + 8 * g + e, 0, 0)) << (8 * e);
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (((w[r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u) s[r] = -INFINITY;
     } else {
-      uint2 w[4];
-      if (a.mask_vec && k0 + 32 <= a.Nk) {
+      if (vec) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) w[g] = ld64(mr, row + 16 * g);
+        for (int g = 0; g < 4; ++g) m.w[g] = ld64(mr, row + 16 * g);
       } else {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           uint32_t e4[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) e4[e] = __builtin_amdgcn_raw_buffer_load_b16(mr, row + 16 * g + 2 * e, 0, 0);
-          w[g].x = e4[0] | (e4[1] << 16);
-          w[g].y = e4[2] | (e4[3] << 16);
+          m.w[g].x = e4[0] | (e4[1] << 16);
+          m.w[g].y = e4[2] | (e4[3] << 16);
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint2 x = w[r >> 2];
-        const uint32_t word = (r & 2) ? x.y : x.x;
-        const uint16_t bits = (r & 1) ? hi16(word) : lo16(word);
-        s[r] = PRESCALED ? s[r] + T::widen(bits) : fmaf(s[r], a.scale, T::widen(bits));
-      }
     }
   }
-  if (elem_mask) {
+}
+
+// Scores in score units: raw q.k without an additive mask (scale folded into
+// cx), scale q.k + M with one. PRESCALED: s already holds scale q.k.
+template <typename T, int MASK, bool PRESCALED>
+__device__ inline void mask_apply(f32x16& s, const MaskVals<MASK>& m, float scale) {
+  if constexpr (MASK == JVPATTN_MASK_BOOL) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (((m.w[r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u) s[r] = -INFINITY;
+  } else if constexpr (MASK == JVPATTN_MASK_ADDITIVE) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = k0 + (r >> 2) * 8 + 4 * hlf + (r & 3);
-      bool hide = key >= a.Nk;
-      if constexpr (CAUSAL) hide = hide || key > qi;
-      if (hide) s[r] = -INFINITY;
+      const uint2 x = m.w[r >> 2];
+      const uint32_t word = (r & 2) ? x.y : x.x;
+      const uint16_t bits = (r & 1) ? hi16(word) : lo16(word);
+      s[r] = PRESCALED ? s[r] + T::widen(bits) : fmaf(s[r], scale, T::widen(bits));
     }
   }
+}
+
+// Keys past Nk, and (causal) keys after the query, get score -inf.
+template <bool CAUSAL>
+__device__ inline void hide_keys(f32x16& s, int Nk, int qi, int k0, int hlf) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = k0 + (r >> 2) * 8 + 4 * hlf + (r & 3);
+    bool hide = key >= Nk;
+    if constexpr (CAUSAL) hide = hide || key > qi;
+    if (hide) s[r] = -INFINITY;
+  }
+}
+
+template <typename T, int MASK, bool CAUSAL, bool PRESCALED>
+__device__ inline void mask_scores(f32x16& s, const FwdArgs& a, Rsrc mr, int qi, int k0, int hlf,
+                                   bool elem_mask) {
+  MaskVals<MASK> m;
+  mask_load<MASK>(m, a, mr, qi, k0, hlf);
+  mask_apply<T, MASK, PRESCALED>(s, m, a.scale);
+  if (elem_mask) hide_keys<CAUSAL>(s, a.Nk, qi, k0, hlf);
 }
 
 // Mask resource of head (b, h): element (i, j) at byte (i*msq + j) * es.
@@ -253,53 +311,80 @@ __device__ inline Rsrc mask_rsrc(const FwdArgs& a, int b, int h, int es) {
   return make_rsrc(static_cast<const char*>(a.mask) + base, bytes);
 }
 
-// Online-softmax update for one 32-key block. On return s holds the weights
-// e = exp(s - m) and sd holds e * sd. Returns true when the accumulators must
-// be multiplied by `alpha` (the reference maximum moved).
-__device__ inline bool softmax_block(f32x16& s, f32x16& sd, RowState& st, float cx, float thr,
-                                     float& alpha) {
-  float bm = fmaxf(s[0], s[1]);
+// Largest score of this lane's query column (both lane halves).
+__device__ inline float block_max(const f32x16& s) {
+  float m = max3(s[0], s[1], s[2]);
 #pragma unroll
-  for (int r = 2; r < 16; r += 2) bm = fmaxf(bm, fmaxf(s[r], s[r + 1]));
-  bm = xhalf_max(bm);
-  const bool need = bm > st.m + thr;
-  bool rescale = false;
+  for (int r = 3; r < 15; r += 2) m = max3(m, s[r], s[r + 1]);
+  m = max3(m, s[15], s[15]);
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return max3(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[1]));
+}
+
+// Move the reference maximum when some row of the wave saw a score more than
+// thr above it. Returns alpha != 1 (and true) when accumulators must be scaled.
+__device__ inline bool update_max(float bm, RowState& st, float cx, float thr, float& alpha) {
   alpha = 1.0f;
-  if (__any(need)) {
-    const float mn = fmaxf(st.m, bm);
-    alpha = mn == -INFINITY ? 1.0f : exp2f((st.m - mn) * cx);
-    st.l *= alpha;
-    st.mu *= alpha;
-    st.m = mn;
-    st.moff = mn == -INFINITY ? 0.0f : mn * cx;
-    rescale = true;
-  }
-  float l = 0.0f, mu = 0.0f;
+  const bool need = bm > st.m + thr;
+  if (!__any(need)) return false;
+  const float mn = fmaxf(st.m, bm);
+  alpha = mn == -INFINITY ? 1.0f : exp2f((st.m - mn) * cx);
+  st.l *= alpha;
+  st.mu *= alpha;
+  st.m = mn;
+  st.moff = mn == -INFINITY ? 0.0f : mn * cx;
+  return true;
+}
+
+// Weights e = exp(s - m) (into s) and e * sd (into sd); their sums into l, mu.
+__device__ inline void exp_block(f32x16& s, f32x16& sd, RowState& st, float cx) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float e = __builtin_amdgcn_exp2f(fmaf(s[r], cx, -st.moff));
-    s[r] = e;
-    const float u = e * sd[r];
-    sd[r] = u;
-    l += e;
-    mu += u;
+    s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], cx, -st.moff));
+    sd[r] *= s[r];
   }
-  st.l += l;
-  st.mu += mu;
+  float l0 = s[0] + s[1], l1 = s[2] + s[3], m0 = sd[0] + sd[1], m1 = sd[2] + sd[3];
+#pragma unroll
+  for (int r = 4; r < 16; r += 4) {
+    l0 += s[r] + s[r + 1];
+    l1 += s[r + 2] + s[r + 3];
+    m0 += sd[r] + sd[r + 1];
+    m1 += sd[r + 2] + sd[r + 3];
+  }
+  st.l += l0 + l1;
+  st.mu += m0 + m1;
+}
+
+// Online-softmax update for one 32-key block (float32 kernel).
+__device__ inline bool softmax_block(f32x16& s, f32x16& sd, RowState& st, float cx, float thr,
+                                     float& alpha) {
+  const bool rescale = update_max(block_max(s), st, cx, thr, alpha);
+  exp_block(s, sd, st, cx);
   return rescale;
 }
 
 // ------------------------------------------------------------- 16-bit kernel
+//
+// Software pipeline per wave over 32-key blocks k: while the vector units turn
+// block k's scores into weights, the matrix cores already compute block k+1's
+// scores; block k's value products follow. The reference maximum for block
+// k+1 is settled at the end of iteration k, so the only branch in the steady
+// state (a rare rescale) sits between iterations. Blocks that need per-key
+// masking (the causal diagonal, a ragged tail) take a non-pipelined path.
+//
+// LDS holds a ring of 4 tiles, each fetched two iterations ahead; one
+// workgroup barrier per tile. The four stages are separate arrays and the
+// loop is unrolled by four, so every LDS access names its stage statically
+// and in-flight loads into other stages never force a wait.
 
 template <typename T, int D, int MASK, bool CAUSAL, bool POW2>
 __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   using L = Tile16<D>;
   using vec8 = typename T::vec8;
-  // Two stages in two separate arrays: with the loop unrolled by two every LDS
-  // access names its stage statically, so the in-flight direct loads into one
-  // stage are known not to alias the reads of the other.
-  __shared__ __attribute__((aligned(16))) char smem0[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char smem1[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage0[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage1[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage2[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage3[L::STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -357,6 +442,9 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
 
   const int kv_end = CAUSAL ? min(a.Nk, q0 + kBM) : a.Nk;
   const int n_tiles = (kv_end + L::BN - 1) / L::BN;
+  // Last block this wave needs (the causal diagonal block, or the last tile); -1 if none.
+  const int last = !wave_live ? -1 : (CAUSAL ? min(n_tiles - 1, qw0 >> 5) : n_tiles - 1);
+  auto needs_keymask = [&](int k) { return (CAUSAL && k * 32 + 31 > qw0) || (k * 32 + 32 > a.Nk); };
 
   // Direct-load slots of this thread (byte offset inside a tile, same for all four tensors).
   int dl_off[L::LOADS];
@@ -364,52 +452,58 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   for (int i = 0; i < L::LOADS; ++i) {
     const int p = i * kThreads + tid;
     const int row = p / L::GR, pg = p % L::GR;
-    dl_off[i] = row * L::ROW + ((pg ^ (row & 7)) << 4);
+    dl_off[i] = row * L::ROW + ((pg ^ swz(row)) << 4);
   }
+  // One buffer resource per tensor for the whole head: offsets past Nk rows
+  // (ragged tail) or into an absent tangent (0-byte resource) read as zeros.
+  const int64_t kbytes = int64_t(a.Nk) * L::ROW;
+  const Rsrc rk = make_rsrc(kp, kbytes), rv = make_rsrc(vp, kbytes);
+  const Rsrc rtk = make_rsrc(tkp, a.tk ? kbytes : 0), rtv = make_rsrc(tvp, a.tv ? kbytes : 0);
   auto issue_tile = [&](int j, char* stage) {
-    const int64_t t0 = int64_t(j) * L::TENSOR_BYTES;
-    const int64_t rem = int64_t(a.Nk - j * L::BN) * L::ROW;  // bytes of this head from the tile start
-    const Rsrc rs[4] = {make_rsrc(kp + t0, rem), make_rsrc(tkp + t0, a.tk ? rem : 0),
-                        make_rsrc(vp + t0, rem), make_rsrc(tvp + t0, a.tv ? rem : 0)};
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int i = 0; i < L::LOADS; ++i) {
-        const char* dst = stage + x * L::TENSOR_BYTES + (i * kThreads + wave * 64) * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[x], (__attribute__((address_space(3))) void*)to_lds(dst),
-                                                 16, dl_off[i], 0, 0, 0);
-      }
+    for (int i = 0; i < L::LOADS; ++i) {
+      const int off = j * L::TENSOR_BYTES + dl_off[i];
+      const int slot = (i * kThreads + wave * 64) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
+                                               16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rtk, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rtv, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+    }
   };
 
   // LDS read offsets of this lane (constant over the loop).
-  // K / dK A operand, chunk c: row c32 (+32 kb), logical granule hlf*NC + c.
+  // K / dK A operand, chunk c: row c32, logical granule hlf*NC + c.
   int kofs[L::NC];
 #pragma unroll
-  for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ (c32 & 7)) << 4);
+  for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ swz(c32)) << 4);
   // V^T / dV^T A operand via transpose reads: lane (group g16 = lane/16, i = lane%16) addresses
-  // row 4*hlf + i/4 (+32 kb + 16 kc, and +8 for the second read), columns 32t + 16(g16&1) + 4(i&3).
-  int vofs[L::NT];
+  // row 4*hlf + i/4 (+16 kc; vofs1 is the second read, 8 rows further), columns 32t + 16(g16&1) + 4(i&3).
+  // swz() depends on row bits 0..3 only, so +16 kc keeps the swizzle.
+  int vofs0[L::NT], vofs1[L::NT];
   {
     const int g16 = lane >> 4, i16 = lane & 15;
-    const int rsw = 4 * hlf + (i16 >> 2);   // row & 7 of every row this lane addresses
+    const int r0 = 4 * hlf + (i16 >> 2), r1 = r0 + 8;
 #pragma unroll
     for (int t = 0; t < L::NT; ++t) {
       const int gcol = 4 * t + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-      vofs[t] = rsw * L::ROW + ((gcol ^ rsw) << 4) + 8 * (i16 & 1);
+      vofs0[t] = r0 * L::ROW + ((gcol ^ swz(r0)) << 4) + 8 * (i16 & 1);
+      vofs1[t] = r1 * L::ROW + ((gcol ^ swz(r1)) << 4) + 8 * (i16 & 1);
     }
   }
 
-  // S^T and dS^T of 32-key block kb of the tile at `sb`. All operands are read
-  // from LDS before the products so the reads overlap each other.
-  auto scores = [&](const char* sb, int kb, f32x16& s, f32x16& sd) {
-    vec8 ka[L::NC], tka[L::NC];
+  // K / dK operands of the tile at `sb`, and the score products S^T, dS^T.
+  auto read_k = [&](const char* sb, vec8 (&ka)[L::NC], vec8 (&tka)[L::NC]) {
 #pragma unroll
     for (int c = 0; c < L::NC; ++c) {
-      const int off = kb * 32 * L::ROW + kofs[c];
-      ka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb, off));
-      tka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + L::TENSOR_BYTES, off));
+      ka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb, kofs[c]));
+      tka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + L::TENSOR_BYTES, kofs[c]));
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mma_s = [&](const vec8 (&ka)[L::NC], const vec8 (&tka)[L::NC], f32x16& s, f32x16& sd) {
     s = f32x16{};
     sd = f32x16{};
 #pragma unroll
@@ -419,37 +513,25 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
       sd = T::mfma(ka[c], tqB[c], sd);
     }
   };
-  // Mask, softmax update and value products of 32-key block kb (keys from k0).
-  auto finish = [&](const char* sb, int kb, int k0, f32x16& s, f32x16& sd) {
-    // V^T and dV^T operands first: their LDS latency hides behind the softmax.
-    const char* sv = sb + 2 * L::TENSOR_BYTES;
-    const char* stv = sb + 3 * L::TENSOR_BYTES;
-    vec8 va[L::NT][2], tva[L::NT][2];
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int off = (kb * 32 + 16 * kc) * L::ROW + vofs[t];
-        va[t][kc] = __builtin_bit_cast(
-            vec8, __builtin_shufflevector(lds_read_tr(sv + off), lds_read_tr(sv + off + 8 * L::ROW), 0, 1, 2, 3, 4,
-                                          5, 6, 7));
-        tva[t][kc] = __builtin_bit_cast(
-            vec8, __builtin_shufflevector(lds_read_tr(stv + off), lds_read_tr(stv + off + 8 * L::ROW), 0, 1, 2, 3,
-                                          4, 5, 6, 7));
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    const bool elem_mask = (CAUSAL && k0 + 31 > qw0) || (k0 + 32 > a.Nk);
-    mask_scores<T, MASK, CAUSAL, POW2>(s, a, mr, qi, k0, hlf, elem_mask);
+  auto scores = [&](const char* sb, f32x16& s, f32x16& sd) {
+    vec8 ka[L::NC], tka[L::NC];
+    read_k(sb, ka, tka);
+    mma_s(ka, tka, s, sd);
+  };
+  auto rescale = [&](float bm) {
     float alpha;
-    if (softmax_block(s, sd, st, a.cx, a.thr, alpha)) {
+    if (update_max(bm, st, a.cx, a.thr, alpha)) {
 #pragma unroll
       for (int t = 0; t < L::NT; ++t) {
         accO[t] *= alpha;
         accT[t] *= alpha;
       }
     }
-    // Weights and weights * dS as 16-bit B operands, keys 16kc .. 16kc+15.
-    vec8 pB[2], uB[2];
+  };
+  // Block weights: s -> e = exp(s - m), sd -> e * dS, packed as 16-bit B operands
+  // for keys 16kc .. 16kc+15; l and mu updated.
+  auto weights = [&](f32x16& s, f32x16& sd, vec8 (&pB)[2], vec8 (&uB)[2]) {
+    exp_block(s, sd, st, a.cx);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       uint4 pw, uw;
@@ -472,6 +554,25 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
       pB[kc] = __builtin_bit_cast(vec8, pw);
       uB[kc] = __builtin_bit_cast(vec8, uw);
     }
+  };
+  // V^T / dV^T operands of the tile at `sb` (transpose reads) and the value
+  // products accO += V^T P^T, accT += V^T U^T + dV^T P^T.
+  auto read_v = [&](const char* sb, vec8 (&va)[L::NT][2], vec8 (&tva)[L::NT][2]) {
+    const char* sv = sb + 2 * L::TENSOR_BYTES;
+    const char* stv = sb + 3 * L::TENSOR_BYTES;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int o0 = 16 * kc * L::ROW + vofs0[t], o1 = 16 * kc * L::ROW + vofs1[t];
+        va[t][kc] = __builtin_bit_cast(
+            vec8, __builtin_shufflevector(lds_read_tr(sv + o0), lds_read_tr(sv + o1), 0, 1, 2, 3, 4, 5, 6, 7));
+        tva[t][kc] = __builtin_bit_cast(
+            vec8, __builtin_shufflevector(lds_read_tr(stv + o0), lds_read_tr(stv + o1), 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+  };
+  auto mma_v = [&](const vec8 (&va)[L::NT][2], const vec8 (&tva)[L::NT][2], const vec8 (&pB)[2],
+                   const vec8 (&uB)[2]) {
 #pragma unroll
     for (int t = 0; t < L::NT; ++t)
 #pragma unroll
@@ -481,33 +582,117 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
         accT[t] = T::mfma(tva[t][kc], pB[kc], accT[t]);
       }
   };
-
-  // One tile: queue the next tile's loads into the other stage, compute on this one.
-  auto tile = [&](int j, const char* sb, char* other) {
-    if (j + 1 < n_tiles) issue_tile(j + 1, other);
-    const int k0 = j * L::BN;
-    // 32-key blocks of this tile that this wave needs (whole waves skip blocks above the diagonal)
-    const bool v0 = wave_live && !(CAUSAL && k0 > qw0 + 31);
-    const bool v1 = L::KB > 1 && wave_live && k0 + 32 < kv_end && !(CAUSAL && k0 + 32 > qw0 + 31);
-    if (v0) {
-      // Both blocks' score products are queued before the first softmax, so the
-      // matrix cores work on block 1 while the vector units work on block 0.
-      f32x16 s0, sd0, s1, sd1;
-      scores(sb, 0, s0, sd0);
-      if (v1) scores(sb, 1, s1, sd1);
-      finish(sb, 0, k0, s0, sd0);
-      if (v1) finish(sb, 1, k0 + 32, s1, sd1);
-    }
-    if (j + 1 < n_tiles) wait_vmem();
-    __syncthreads();
+  auto values = [&](const char* sb, const vec8 (&pB)[2], const vec8 (&uB)[2]) {
+    vec8 va[L::NT][2], tva[L::NT][2];
+    read_v(sb, va, tva);
+    mma_v(va, tva, pB, uB);
   };
 
-  if (n_tiles > 0) issue_tile(0, smem0);
-  wait_vmem();
-  __syncthreads();
-  for (int j = 0; j < n_tiles; j += 2) {
-    tile(j, smem0, smem1);
-    if (j + 1 < n_tiles) tile(j + 1, smem1, smem0);
+  // Blocks 1.. that need per-key masking start at jm: the causal diagonal, a
+  // ragged last tile, or the end of this wave's range.
+  int jm = last + 1;
+  if (CAUSAL) jm = min(jm, qw0 >> 5);
+  jm = min(jm, a.Nk >> 5);
+  jm = max(jm, 1);
+
+  // Pipelined iteration k (block k settled in sc; block k+1 needs no key mask).
+  auto fast = [&](int k, const char* cur, const char* nxt, char* dma, f32x16& sc, f32x16& sdc, f32x16& sn,
+                  f32x16& sdn) {
+    // Tile k+1 was fetched two iterations ago; tile k+2 may still be in flight.
+    if (k + 2 < n_tiles) wait_vmcnt<L::TILE_VMEM>();
+    else wait_vmcnt<0>();
+    ring_barrier();   // tile k+1 visible to all; every wave is done with tile k-1 (the `dma` stage)
+    MaskVals<MASK> mk1;
+    mask_load<MASK>(mk1, a, mr, qi, (k + 1) * 32, hlf);   // before the fetch: keeps its wait short
+    if (k + 3 < n_tiles) issue_tile(k + 3, dma);
+    // All LDS operands first (their latency hides behind the first weights),
+    // then the score products of block k+1 interleaved with block k's softmax
+    // on the vector units, then block k's value products.
+    vec8 ka[L::NC], tka[L::NC], va[L::NT][2], tva[L::NT][2], pB[2], uB[2];
+    read_k(nxt, ka, tka);
+    read_v(cur, va, tva);
+    mma_s(ka, tka, sn, sdn);
+    weights(sc, sdc, pB, uB);
+    mma_v(va, tva, pB, uB);
+    mask_apply<T, MASK, POW2>(sn, mk1, a.scale);
+    const float bm = block_max(sn);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * L::NC, 0);           // K / dK reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 * L::NT, 0);           // V / dV transpose reads
+    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);                  // first weights
+#pragma unroll
+    for (int i = 0; i < 3 * L::NC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // score product
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                 // weights
+    }
+#pragma unroll
+    for (int i = 0; i < 6 * L::NT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // value product
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                 // max of block k+1
+    }
+    rescale(bm);
+  };
+
+  f32x16 sA, sdA, sB, sdB;
+  // Prologue: tiles 0..2 in flight, wait for tile 0, settle block 0 if it needs no key mask.
+  if (n_tiles > 0) issue_tile(0, stage0);
+  if (n_tiles > 1) issue_tile(1, stage1);
+  if (n_tiles > 2) issue_tile(2, stage2);
+  if (n_tiles > 2) wait_vmcnt<2 * L::TILE_VMEM>();
+  else if (n_tiles > 1) wait_vmcnt<L::TILE_VMEM>();
+  else wait_vmcnt<0>();
+  ring_barrier();
+  bool ready = false;   // sA holds the current block's settled scores
+  if (0 <= last && !needs_keymask(0)) {
+    scores(stage0, sA, sdA);
+    MaskVals<MASK> mk;
+    mask_load<MASK>(mk, a, mr, qi, 0, hlf);
+    mask_apply<T, MASK, POW2>(sA, mk, a.scale);
+    rescale(block_max(sA));
+    ready = true;
+  }
+  const int kfast = ready ? jm - 1 : 0;   // iterations 0 .. kfast-1 are pipelined
+  int k = 0;
+  for (; k + 4 <= kfast; k += 4) {
+    fast(k, stage0, stage1, stage3, sA, sdA, sB, sdB);
+    fast(k + 1, stage1, stage2, stage0, sB, sdB, sA, sdA);
+    fast(k + 2, stage2, stage3, stage1, sA, sdA, sB, sdB);
+    fast(k + 3, stage3, stage0, stage2, sB, sdB, sA, sdA);
+  }
+  if (k < kfast) {
+    fast(k, stage0, stage1, stage3, sA, sdA, sB, sdB);
+    if (k + 1 < kfast) fast(k + 1, stage1, stage2, stage0, sB, sdB, sA, sdA);
+    if (k + 2 < kfast) fast(k + 2, stage2, stage3, stage1, sA, sdA, sB, sdB);
+  }
+  if (kfast & 1) {   // block kfast's scores were left in sB
+    sA = sB;
+    sdA = sdB;
+  }
+
+  // Remaining iterations (diagonal, ragged tail, and barrier-only ones past this
+  // wave's range), one score buffer, stage chosen at run time.
+  auto stage_of = [&](int i) -> char* {
+    i &= 3;
+    return i == 0 ? stage0 : i == 1 ? stage1 : i == 2 ? stage2 : stage3;
+  };
+  for (k = kfast; k < n_tiles; ++k) {
+    if (k + 2 < n_tiles) wait_vmcnt<L::TILE_VMEM>();
+    else wait_vmcnt<0>();
+    ring_barrier();
+    if (k + 3 < n_tiles) issue_tile(k + 3, stage_of(k + 3));
+    if (k > last) continue;
+    const char* cur = stage_of(k);
+    if (!ready) {
+      scores(cur, sA, sdA);
+      MaskVals<MASK> mk;
+      mask_load<MASK>(mk, a, mr, qi, k * 32, hlf);
+      mask_apply<T, MASK, POW2>(sA, mk, a.scale);
+      if (needs_keymask(k)) hide_keys<CAUSAL>(sA, a.Nk, qi, k * 32, hlf);
+      rescale(block_max(sA));
+    }
+    vec8 pB[2], uB[2];
+    weights(sA, sdA, pB, uB);
+    values(cur, pB, uB);
+    ready = false;   // the next block, if any, is settled at the top of the next iteration
   }
 
   // Epilogue: combine the two lane halves of each query column, normalise, store.
