@@ -29,6 +29,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "jvpattn.h"
 #include "jvpattn_internal.h"
@@ -190,8 +192,10 @@ __device__ inline v4i16 lds_read_tr(const char* p) {
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ inline void wait_vmcnt() {
-  static_assert(N == 0 || N == 4 || N == 8 || N == 12 || N == 16, "unsupported count");
+  static_assert(N == 0 || N == 2 || N == 4 || N == 6 || N == 8 || N == 12 || N == 16, "unsupported count");
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
@@ -734,6 +738,326 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd16_kernel(FwdArg
 #endif
 }
 
+// ------------------------------------------------ 16-bit ping-pong kernel (d = 64)
+//
+// Eight waves, 256 query rows per workgroup. Waves w and w+4 share a SIMD and
+// are held in opposite phases by workgroup barriers: while group A (waves
+// 0-3) issues only matrix-core work -- block i's value products and block
+// i+1's score products -- group B (waves 4-7) runs the vector work of the
+// previous iteration (mask, row maximum, exponentials, weights) and reads the
+// LDS operands for its next matrix phase; then the roles swap. The matrix
+// cores of each SIMD are fed by one wave while the other keeps the vector
+// units busy. Group B also issues the tile loads, during its matrix phases.
+//
+// Tiles of 32 keys live in a ring of 6 LDS stages (separate arrays; the loop
+// is unrolled by 6 so every access names its stage statically). Tile j is
+// loaded at iteration j-6 and first read at iteration j-2.
+
+constexpr int kPPWaves = 8;
+constexpr int kPPThreads = 64 * kPPWaves;
+constexpr int kPPBM = 32 * kPPWaves;
+constexpr int kPPStages = 6;
+
+template <typename T, int MASK, bool CAUSAL, bool POW2>
+__device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
+  constexpr int D = 64;
+  using L = Tile16<D>;
+  using vec8 = typename T::vec8;
+  static_assert(L::TILE_VMEM == 4, "group B loads a 32-key tile with 4 loads per thread");
+  __shared__ __attribute__((aligned(16))) char stage0[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage1[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage2[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage3[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage4[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage5[L::STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grp_b = wave >= 4;
+  const int c32 = lane & 31;
+  const int hlf = lane >> 5;
+
+  const int qb = a.n_qblk - 1 - int(blockIdx.x) / a.BH;
+  const int bh = int(blockIdx.x) % a.BH;
+  const int b = bh / a.H, h = bh % a.H;
+  const int q0 = qb * kPPBM;
+  const int qw0 = q0 + 32 * wave;
+  const int qi = qw0 + c32;
+  const bool wave_live = qw0 < a.Nq;
+
+  const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
+  const int64_t khead = int64_t(bh) * a.Nk * L::ROW;
+  const char* qp = static_cast<const char*>(a.q) + qhead;
+  const char* kp = static_cast<const char*>(a.k) + khead;
+  const char* vp = static_cast<const char*>(a.v) + khead;
+  const char* tqp = a.tq ? static_cast<const char*>(a.tq) + qhead : qp;
+  const char* tkp = a.tk ? static_cast<const char*>(a.tk) + khead : kp;
+  const char* tvp = a.tv ? static_cast<const char*>(a.tv) + khead : vp;
+  const int64_t qbytes = int64_t(a.Nq) * L::ROW;
+
+  vec8 qB[L::NC], tqB[L::NC];
+  {
+    const Rsrc rq = make_rsrc(qp, qbytes), rtq = make_rsrc(tqp, a.tq ? qbytes : 0);
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) {
+      const int off = qi * L::ROW + (hlf * (D / 2) + 8 * c) * 2;
+      qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
+      tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
+      if constexpr (POW2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qB[c][e] = static_cast<__bf16>(static_cast<float>(qB[c][e]) * a.scale);
+          tqB[c][e] = static_cast<__bf16>(static_cast<float>(tqB[c][e]) * a.scale);
+        }
+      }
+    }
+  }
+
+  f32x16 accO[L::NT], accT[L::NT];
+#pragma unroll
+  for (int t = 0; t < L::NT; ++t) {
+    accO[t] = f32x16{};
+    accT[t] = f32x16{};
+  }
+  RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
+  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+
+  const int kv_end = CAUSAL ? min(a.Nk, q0 + kPPBM) : a.Nk;
+  const int n_tiles = (kv_end + L::BN - 1) / L::BN;
+  const int last = !wave_live ? -1 : (CAUSAL ? min(n_tiles - 1, qw0 >> 5) : n_tiles - 1);
+  auto needs_keymask = [&](int k) { return (CAUSAL && k * 32 + 31 > qw0) || (k * 32 + 32 > a.Nk); };
+
+  // Tile loads (group B only): one 16-byte slot per tensor per thread.
+  const int tb = tid - 4 * 64;                     // 0..255 in group B
+  const int drow = (tb & 255) >> 3, dpg = tb & 7;
+  const int dl_off = drow * L::ROW + ((dpg ^ swz(drow)) << 4);
+  const int64_t kbytes = int64_t(a.Nk) * L::ROW;
+  const Rsrc rk = make_rsrc(kp, kbytes), rv = make_rsrc(vp, kbytes);
+  const Rsrc rtk = make_rsrc(tkp, a.tk ? kbytes : 0), rtv = make_rsrc(tvp, a.tv ? kbytes : 0);
+  auto issue_tile = [&](int j, char* stage) {
+    const int off = j * L::TENSOR_BYTES + dl_off;
+    const int slot = (wave - 4) * 64 * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot), 16,
+                                             off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rtk, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rv, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rtv, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+  };
+
+  int kofs[L::NC];
+#pragma unroll
+  for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ swz(c32)) << 4);
+  int vofs0[L::NT], vofs1[L::NT];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int r0 = 4 * hlf + (i16 >> 2), r1 = r0 + 8;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t) {
+      const int gcol = 4 * t + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      vofs0[t] = r0 * L::ROW + ((gcol ^ swz(r0)) << 4) + 8 * (i16 & 1);
+      vofs1[t] = r1 * L::ROW + ((gcol ^ swz(r1)) << 4) + 8 * (i16 & 1);
+    }
+  }
+
+  // Pipeline registers carried from a vector phase to the next matrix phase.
+  vec8 ka[L::NC], tka[L::NC];          // K / dK operands of the next score products
+  vec8 va[L::NT][2], tva[L::NT][2];    // V / dV operands of the next value products
+  vec8 pB[2], uB[2];                   // weights of the block whose value products come next
+  f32x16 sn, sdn;                      // scores of the block after that
+  MaskVals<MASK> mk;                   // mask values of the block to settle next
+
+  auto read_k = [&](const char* sb) {
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) {
+      ka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb, kofs[c]));
+      tka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + L::TENSOR_BYTES, kofs[c]));
+    }
+  };
+  auto read_v = [&](const char* sb) {
+    const char* sv = sb + 2 * L::TENSOR_BYTES;
+    const char* stv = sb + 3 * L::TENSOR_BYTES;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int o0 = 16 * kc * L::ROW + vofs0[t], o1 = 16 * kc * L::ROW + vofs1[t];
+        va[t][kc] = __builtin_bit_cast(
+            vec8, __builtin_shufflevector(lds_read_tr(sv + o0), lds_read_tr(sv + o1), 0, 1, 2, 3, 4, 5, 6, 7));
+        tva[t][kc] = __builtin_bit_cast(
+            vec8, __builtin_shufflevector(lds_read_tr(stv + o0), lds_read_tr(stv + o1), 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+  };
+  auto mma_s = [&]() {
+    sn = f32x16{};
+    sdn = f32x16{};
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) {
+      sn = T::mfma(ka[c], qB[c], sn);
+      sdn = T::mfma(tka[c], qB[c], sdn);
+      sdn = T::mfma(ka[c], tqB[c], sdn);
+    }
+  };
+  auto mma_v = [&]() {
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        accO[t] = T::mfma(va[t][kc], pB[kc], accO[t]);
+        accT[t] = T::mfma(va[t][kc], uB[kc], accT[t]);
+        accT[t] = T::mfma(tva[t][kc], pB[kc], accT[t]);
+      }
+  };
+  // Scores of block k (in sn): mask, reference maximum, weights into pB / uB.
+  auto settle = [&](int k) {
+    mask_apply<T, MASK, POW2>(sn, mk, a.scale);
+    if (needs_keymask(k)) hide_keys<CAUSAL>(sn, a.Nk, qi, k * 32, hlf);
+    float alpha;
+    if (update_max(block_max(sn), st, a.cx, a.thr, alpha)) {
+#pragma unroll
+      for (int t = 0; t < L::NT; ++t) {
+        accO[t] *= alpha;
+        accT[t] *= alpha;
+      }
+    }
+    exp_block(sn, sdn, st, a.cx);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      uint4 pw, uw;
+      const float us = POW2 ? 1.0f : a.scale;
+      pw.x = T::pack2(sn[8 * kc + 0], sn[8 * kc + 1]);
+      pw.y = T::pack2(sn[8 * kc + 2], sn[8 * kc + 3]);
+      pw.z = T::pack2(sn[8 * kc + 4], sn[8 * kc + 5]);
+      pw.w = T::pack2(sn[8 * kc + 6], sn[8 * kc + 7]);
+      uw.x = T::pack2(sdn[8 * kc + 0] * us, sdn[8 * kc + 1] * us);
+      uw.y = T::pack2(sdn[8 * kc + 2] * us, sdn[8 * kc + 3] * us);
+      uw.z = T::pack2(sdn[8 * kc + 4] * us, sdn[8 * kc + 5] * us);
+      uw.w = T::pack2(sdn[8 * kc + 6] * us, sdn[8 * kc + 7] * us);
+      pB[kc] = __builtin_bit_cast(vec8, pw);
+      uB[kc] = __builtin_bit_cast(vec8, uw);
+    }
+  };
+
+  // Matrix phase of iteration i: value products of block i, score products of block i+1.
+  auto matrix_phase = [&](int i) {
+    if (i > last) return;
+    if (i + 1 <= last) mma_s();
+    mma_v();
+  };
+  // Vector phase of iteration i: settle block i+1; operands K(i+2) from stk, V(i+1) from stv.
+  auto vector_phase = [&](int i, const char* stk, const char* stv) {
+    if (i + 1 > last) return;
+    read_v(stv);
+    if (i + 2 <= last) read_k(stk);
+    settle(i + 1);
+    if (i + 2 <= last) mask_load<MASK>(mk, a, mr, qi, (i + 2) * 32, hlf);
+  };
+  // Group B's wait for its loads of tile j; tiles issued after j may stay in flight.
+  auto wait_tile = [&](int j) {
+    const int newer = min(n_tiles - 1, j + 3) - j;   // tiles issued after j so far (at most 3)
+    if (newer >= 3) wait_vmcnt<12>();
+    else if (newer == 2) wait_vmcnt<8>();
+    else if (newer == 1) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+  };
+
+  // Prologue: group B loads tiles 0..5; everyone settles block 0 and reads the
+  // operands of the first matrix phase.
+  if (grp_b) {
+    if (n_tiles > 0) issue_tile(0, stage0);
+    if (n_tiles > 1) issue_tile(1, stage1);
+    if (n_tiles > 2) issue_tile(2, stage2);
+    if (n_tiles > 3) issue_tile(3, stage3);
+    if (n_tiles > 4) issue_tile(4, stage4);
+    if (n_tiles > 5) issue_tile(5, stage5);
+    const int newer = min(n_tiles - 1, 5) - 1;   // tiles issued after tile 1
+    if (newer >= 4) wait_vmcnt<16>();
+    else if (newer == 3) wait_vmcnt<12>();
+    else if (newer == 2) wait_vmcnt<8>();
+    else if (newer == 1) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+  }
+  ring_barrier();
+  if (0 <= last) {
+    read_k(stage0);
+    mma_s();
+    mask_load<MASK>(mk, a, mr, qi, 0, hlf);
+    settle(0);
+    read_v(stage0);
+    if (1 <= last) {
+      read_k(stage1);
+      mask_load<MASK>(mk, a, mr, qi, 32, hlf);
+    }
+  }
+
+  // Every wave runs matrix(i), barrier, vector(i), barrier. Group B starts
+  // one barrier late, so the two waves of each SIMD are always in opposite
+  // phases: A's vector(i) runs beside B's matrix(i), A's matrix(i+1) beside
+  // B's vector(i). Group B loads tile i+6 into stage i%6 during matrix(i)
+  // (tile i was last read in B's vector(i-1)) and waits for tile i+3 at the
+  // end of vector(i) (first read in A's vector(i+1)).
+  if (grp_b) {
+    wait_tile(2);
+    ring_barrier();
+  }
+  auto iteration = [&](int i, char* st_r, char* st_r1, char* st_r2) {
+    matrix_phase(i);
+    if (grp_b && i + kPPStages < n_tiles) issue_tile(i + kPPStages, st_r);
+    ring_barrier();
+    vector_phase(i, st_r2, st_r1);
+    if (grp_b) wait_tile(i + 3);
+    ring_barrier();
+  };
+  for (int i = 0; i < n_tiles; i += kPPStages) {
+    iteration(i, stage0, stage1, stage2);
+    if (i + 1 < n_tiles) iteration(i + 1, stage1, stage2, stage3);
+    if (i + 2 < n_tiles) iteration(i + 2, stage2, stage3, stage4);
+    if (i + 3 < n_tiles) iteration(i + 3, stage3, stage4, stage5);
+    if (i + 4 < n_tiles) iteration(i + 4, stage4, stage5, stage0);
+    if (i + 5 < n_tiles) iteration(i + 5, stage5, stage0, stage1);
+  }
+  if (!grp_b) ring_barrier();
+
+  const float l = xhalf_sum(st.l);
+  const float mu = xhalf_sum(st.mu);
+  if (qi < a.Nq) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float tl = POW2 ? mu * inv : mu * a.scale * inv;
+    uint16_t* op = static_cast<uint16_t*>(a.o) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
+    uint16_t* top = static_cast<uint16_t*>(a.to) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float ov[4], dv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ov[e] = accO[t][4 * g + e] * inv;
+          dv[e] = accT[t][4 * g + e] * inv - tl * ov[e];
+        }
+        const int dd = 32 * t + 8 * g + 4 * hlf;
+        *reinterpret_cast<uint2*>(op + dd) = uint2{T::pack2(ov[0], ov[1]), T::pack2(ov[2], ov[3])};
+        *reinterpret_cast<uint2*>(top + dd) = uint2{T::pack2(dv[0], dv[1]), T::pack2(dv[2], dv[3])};
+      }
+    }
+    if (hlf == 0) {
+      const int64_t ri = int64_t(bh) * a.Nq + qi;
+      a.lse[ri] = l > 0.0f ? (st.moff + log2f(l)) * kLn2 : -INFINITY;
+      if (a.tlse) a.tlse[ri] = tl;
+    }
+  }
+}
+
+template <typename T, int MASK, bool CAUSAL, bool POW2>
+__global__ __launch_bounds__(kPPThreads, 2) void fwd16pp_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  fwd16pp_body<T, MASK, CAUSAL, POW2>(a);
+#endif
+}
+
 // ------------------------------------------------------------- float32 kernel
 //
 // Same structure on v_mfma_f32_32x32x2_f32 (float32 products, no rounding of
@@ -936,6 +1260,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd32_kernel(FwdArgs a) {
 thread_local int g_last_hip_error = 0;
 
 template <int MASK, bool CAUSAL>
+hipError_t launch_pp(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
+  const dim3 block(kPPThreads);
+  if (dtype == JVPATTN_BF16) {
+    if (pow2) hipLaunchKernelGGL((fwd16pp_kernel<BF16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16pp_kernel<BF16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((fwd16pp_kernel<F16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+  }
+  return hipGetLastError();
+}
+
+template <int MASK, bool CAUSAL>
 hipError_t launch_typed(int dtype, int d, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
   const dim3 block(kThreads);
   if (dtype == JVPATTN_BF16) {
@@ -1001,6 +1337,16 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
     a.mask_vec = mask && (p->mask_stride_b % need == 0) && (p->mask_stride_h % need == 0) &&
                  (p->mask_stride_q % need == 0) && (base % (need * mes) == 0);
   }
+  // Kernel choice: the 4-wave kernel (128 rows per workgroup) by default; the
+  // 8-wave ping-pong kernel (256 rows, 16-bit d = 64) is measured slower at
+  // present and runs only when JVPATTN_FWD_KERNEL=pp asks for it (testing).
+  const int64_t n128 = (p->Nq + kBM - 1) / kBM, n256 = (p->Nq + kPPBM - 1) / kPPBM;
+  bool pp = false;
+  if (const char* env = std::getenv("JVPATTN_FWD_KERNEL")) {
+    if (std::strcmp(env, "pp") == 0) pp = p->d == 64 && p->dtype != JVPATTN_F32;
+    if (std::strcmp(env, "wg4") == 0) pp = false;
+  }
+  a.n_qblk = static_cast<int>(pp ? n256 : n128);
   const int64_t blocks = int64_t(a.n_qblk) * a.BH;
   if (blocks > INT32_MAX) return JVPATTN_ERR_SHAPE;
   const dim3 grid(static_cast<unsigned>(blocks));
@@ -1008,19 +1354,36 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
 
   hipError_t e;
   const bool c = p->causal != 0;
-  switch (p->mask_kind) {
-    case JVPATTN_MASK_NONE:
-      e = c ? launch_typed<JVPATTN_MASK_NONE, true>(p->dtype, p->d, pow2, a, grid, s)
-            : launch_typed<JVPATTN_MASK_NONE, false>(p->dtype, p->d, pow2, a, grid, s);
-      break;
-    case JVPATTN_MASK_BOOL:
-      e = c ? launch_typed<JVPATTN_MASK_BOOL, true>(p->dtype, p->d, pow2, a, grid, s)
-            : launch_typed<JVPATTN_MASK_BOOL, false>(p->dtype, p->d, pow2, a, grid, s);
-      break;
-    default:
-      e = c ? launch_typed<JVPATTN_MASK_ADDITIVE, true>(p->dtype, p->d, pow2, a, grid, s)
-            : launch_typed<JVPATTN_MASK_ADDITIVE, false>(p->dtype, p->d, pow2, a, grid, s);
-      break;
+  if (pp) {
+    switch (p->mask_kind) {
+      case JVPATTN_MASK_NONE:
+        e = c ? launch_pp<JVPATTN_MASK_NONE, true>(p->dtype, pow2, a, grid, s)
+              : launch_pp<JVPATTN_MASK_NONE, false>(p->dtype, pow2, a, grid, s);
+        break;
+      case JVPATTN_MASK_BOOL:
+        e = c ? launch_pp<JVPATTN_MASK_BOOL, true>(p->dtype, pow2, a, grid, s)
+              : launch_pp<JVPATTN_MASK_BOOL, false>(p->dtype, pow2, a, grid, s);
+        break;
+      default:
+        e = c ? launch_pp<JVPATTN_MASK_ADDITIVE, true>(p->dtype, pow2, a, grid, s)
+              : launch_pp<JVPATTN_MASK_ADDITIVE, false>(p->dtype, pow2, a, grid, s);
+        break;
+    }
+  } else {
+    switch (p->mask_kind) {
+      case JVPATTN_MASK_NONE:
+        e = c ? launch_typed<JVPATTN_MASK_NONE, true>(p->dtype, p->d, pow2, a, grid, s)
+              : launch_typed<JVPATTN_MASK_NONE, false>(p->dtype, p->d, pow2, a, grid, s);
+        break;
+      case JVPATTN_MASK_BOOL:
+        e = c ? launch_typed<JVPATTN_MASK_BOOL, true>(p->dtype, p->d, pow2, a, grid, s)
+              : launch_typed<JVPATTN_MASK_BOOL, false>(p->dtype, p->d, pow2, a, grid, s);
+        break;
+      default:
+        e = c ? launch_typed<JVPATTN_MASK_ADDITIVE, true>(p->dtype, p->d, pow2, a, grid, s)
+              : launch_typed<JVPATTN_MASK_ADDITIVE, false>(p->dtype, p->d, pow2, a, grid, s);
+        break;
+    }
   }
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);

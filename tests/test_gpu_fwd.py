@@ -20,6 +20,17 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
+# The library picks between an 8-wave ping-pong kernel (16-bit, d = 64, large
+# grids) and a 4-wave kernel; the override forces one so both are checked on
+# small shapes too.
+KERNELS = ["pp", "wg4"]
+
+
+@pytest.fixture(params=KERNELS)
+def kernel(request, monkeypatch):
+    monkeypatch.setenv("JVPATTN_FWD_KERNEL", request.param)
+    return request.param
+
 
 def to_dev(x):
     return {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
@@ -100,7 +111,7 @@ def sampled_rows(N, n, seed):
     return np.array(sorted(r for r in rows if r < N))
 
 
-def test_hvp_workload_forward_sampled():
+def test_hvp_workload_forward_sampled(kernel):
     """B=4, H=16, N=2048, d=64, bf16, causal: every head launched, sampled heads x rows checked."""
     w = I.HVP
     x = I.make_inputs(w)
@@ -134,7 +145,7 @@ STRESS_SHAPES = [(1, 2, 200, 64), (1, 1, 97, 128)]
 @pytest.mark.parametrize("mask_kind", ["none", "bool", "additive"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", STRESS_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_stress(shape, causal, mask_kind, dtype, std):
+def test_stress(shape, causal, mask_kind, dtype, std, kernel):
     B, H, N, d = shape
     w = I.Workload("stress", B=B, H=H, N=N, d=d, dtype=dtype, causal=causal, mask_kind=mask_kind, std=std,
                    seed=11, mask_heads=H if mask_kind == "additive" else 1, keep=0.7)
@@ -144,7 +155,7 @@ def test_stress(shape, causal, mask_kind, dtype, std):
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("tangents", [("tv",), ("tq", "tk"), ("tq",), ("tk",), ()],
                          ids=lambda t: "+".join(t) or "none")
-def test_term_isolation(dtype, tangents):
+def test_term_isolation(dtype, tangents, kernel):
     """Only some tangents given (others NULL): isolates dP V, P dV, the dQ and dK paths; none -> dO = 0."""
     w = I.Workload("iso", B=1, H=2, N=160, d=64, dtype=dtype, std=1.0, seed=12)
     got, _ = check(w, tangents=tangents)
@@ -155,7 +166,7 @@ def test_term_isolation(dtype, tangents):
 # ------------------------------------------------ edges
 
 @pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 130, 255, 256, 257, 511, 513])
-def test_tile_boundaries(N):
+def test_tile_boundaries(N, kernel):
     for dtype, causal in (("bf16", False), ("f16", True)):
         w = I.Workload(f"edge{N}", B=1, H=2, N=N, d=64, dtype=dtype, causal=causal, std=1.0, seed=N)
         check(w)
@@ -163,7 +174,7 @@ def test_tile_boundaries(N):
 
 @pytest.mark.parametrize("Nq,Nk", [(64, 200), (200, 64), (1, 300), (130, 1)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_rectangular(Nq, Nk, causal):
+def test_rectangular(Nq, Nk, causal, kernel):
     w = I.Workload("rect", B=1, H=2, N=Nq, Nk=Nk, d=64, dtype="bf16", causal=causal, std=1.0, seed=3)
     check(w)
 
@@ -174,7 +185,7 @@ def test_d128_f16_and_f32_ragged():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-def test_fully_masked_rows(dtype):
+def test_fully_masked_rows(dtype, kernel):
     w = I.Workload("fm", B=1, H=2, N=70, d=64, dtype=dtype, mask_kind="bool", std=1.0, seed=5, keep=0.5)
     x = I.make_inputs(w)
     x["mask"][0, 0, 3, :] = 0          # one row with no visible key
@@ -185,7 +196,7 @@ def test_fully_masked_rows(dtype):
         assert torch.all(torch.isneginf(got["lse"][0, :, r])) and torch.all(got["tlse"][0, :, r] == 0)
 
 
-def test_additive_minus_inf_rows():
+def test_additive_minus_inf_rows(kernel):
     w = I.Workload("addinf", B=1, H=1, N=64, d=64, dtype="f16", mask_kind="additive", std=1.0, seed=6)
     x = I.make_inputs(w)
     x["mask"][0, 0, 5, :] = float("-inf")
@@ -195,13 +206,13 @@ def test_additive_minus_inf_rows():
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("N", [32, 64])
-def test_additive_small_n_regression(dtype, N):
+def test_additive_small_n_regression(dtype, N, kernel):
     """The prior implementation's benchmark lists its additive-mask runs at N=32 and 64 as failing."""
     check(I.Workload("addsmall", B=2, H=8, N=N, d=64, dtype=dtype, mask_kind="additive", seed=N))
     check(I.Workload("addsmall_s", B=2, H=8, N=N, d=64, dtype=dtype, mask_kind="additive", std=1.0, seed=N))
 
 
-def test_key_padding_mask_broadcast_rows():
+def test_key_padding_mask_broadcast_rows(kernel):
     """A [B,1,1,Nk] boolean mask: mask_stride_q = 0 broadcasts one key-padding row to every query."""
     w = I.Workload("pad", B=2, H=3, N=96, d=64, dtype="bf16", mask_kind="bool", std=1.0, seed=7)
     x = I.make_inputs(w)
@@ -214,7 +225,7 @@ def test_key_padding_mask_broadcast_rows():
     assert_parity(got, ref, "bf16", "pad")
 
 
-def test_custom_scale():
+def test_custom_scale(kernel):
     w = I.Workload("scale", B=1, H=2, N=100, d=64, dtype="bf16", std=1.0, seed=8)
     check(w, scale=0.3)
     w = I.Workload("scale_add", B=1, H=2, N=100, d=64, dtype="f16", mask_kind="additive", std=1.0, seed=8)
@@ -247,7 +258,7 @@ def test_all_4x4_bool_masks_in_one_launch():
             assert_parity(got, ref, dtype, f"mask4 {dtype} causal={causal}")
 
 
-def test_deterministic():
+def test_deterministic(kernel):
     w = I.Workload("det", B=2, H=4, N=300, d=64, dtype="bf16", causal=True, std=1.0, seed=10)
     x = I.make_inputs(w)
     a = gpu_run(x, True)
