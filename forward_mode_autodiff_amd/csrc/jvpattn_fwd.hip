@@ -73,6 +73,14 @@ struct FwdArgs {
   float thr;          // lazy-rescale threshold in score units
 };
 
+// Maximum of three values in one instruction (no NaN canonicalisation of the
+// matrix-core results the way a chain of fmaxf would need).
+__device__ inline float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // ---------------------------------------------------------------- 16-bit types
 
 struct BF16 {
@@ -86,6 +94,14 @@ struct BF16 {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
   }
   __device__ static inline float widen(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+  // acc + the two 16-bit values of w
+  __device__ static inline float dot2sum(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                           acc, false);
+  }
+  // Weights must be rebased when a lane's 16 weights sum past 2^12 (so each is
+  // at most 2^12; bfloat16 and the float32 sums have range to spare).
+  __device__ static inline bool spill(float lane_sum, const float (&)[16]) { return !(lane_sum <= 4096.0f); }
 };
 
 struct F16 {
@@ -102,6 +118,13 @@ struct F16 {
   __device__ static inline float widen(uint16_t x) {
     return static_cast<float>(__builtin_bit_cast(_Float16, x));
   }
+  __device__ static inline float dot2sum(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+  }
+  // Weights must be rebased when a lane's 16 weights sum past 2^6, so each
+  // is at most 2^6 and the float16 products with score tangents below 2^10 in
+  // magnitude stay finite.
+  __device__ static inline bool spill(float lane_sum, const float (&)[16]) { return !(lane_sum <= 64.0f); }
 };
 
 __device__ inline uint32_t lo16(uint32_t x) { return x & 0xffffu; }
@@ -205,14 +228,11 @@ __device__ inline void wait_vmcnt() {
 // Workgroup barrier for the LDS ring. The caller has already waited for its
 // own direct-to-LDS loads (wait_vmcnt); this waits for its LDS reads and
 // syncs. (A fenced __syncthreads would also drain every in-flight tile load.)
-__device__ inline void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Maximum of three values in one instruction (no NaN canonicalisation of the
-// matrix-core results the way a chain of fmaxf would need).
-__device__ inline float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+// Builtins rather than inline assembly, so the compiler's own wait
+// insertion knows that LDS reads issued before the barrier have completed.
+__device__ inline void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
 }
 
 // Per-row softmax state for one lane (both lanes of a query column hold the same m).
@@ -356,6 +376,100 @@ __device__ inline void exp_block(f32x16& s, f32x16& sd, RowState& st, float cx) 
     m1 += sd[r + 2] + sd[r + 3];
   }
   st.l += l0 + l1;
+  st.mu += m0 + m1;
+}
+
+// Sum of 16 values as a balanced tree (independent adds, depth 4).
+__device__ inline float sum16(const float (&x)[16]) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = x[2 * i] + x[2 * i + 1];
+  const float b0 = a[0] + a[1], b1 = a[2] + a[3], b2 = a[4] + a[5], b3 = a[6] + a[7];
+  return (b0 + b1) + (b2 + b3);
+}
+
+// Online softmax of one 32-key block for the 16-bit kernels, without a row
+// maximum in the common case. The weights are first taken against the
+// current reference, e = 2^(s cx - moff). A reference only has to keep the
+// weights bounded (every accumulator is rescaled with it), so the block is
+// accepted when this lane's 16 weights sum to at most T::kSpill, which bounds
+// each of them. Otherwise -- or while the row has seen no visible key -- the
+// whole wave takes the rare path: exact block maximum over both lane halves,
+// raise the reference to it, rescale l and mu (alpha returned for the
+// accumulators), recompute the weights. A reference set this way is always a
+// score of the row, so weights of later keys far below it may underflow to 0
+// only where they are negligible against that key's weight of 1.
+//
+// s holds the scores on entry (score units) and is clobbered; sd the score
+// tangents (times us gives dS). Outputs: pB = e, uB = e dS as 16-bit B
+// operands for keys 16kc .. 16kc+15.
+struct RowState16 {
+  float moff;    // reference in log2 units; 0 until a visible key is seen
+  float l;       // this lane's partial sum of weights
+  float mu;      // this lane's partial sum of weights * dS
+  bool seen;     // some visible key has set the reference
+};
+
+// Step 1: weights e of the block (s is clobbered), l updated; returns true
+// (and alpha for the accumulators) when the reference moved.
+template <typename T>
+__device__ inline bool block_exp16(f32x16& s, RowState16& st, float cx, float (&e)[16], float& alpha) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], cx, -st.moff);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(s[r]);
+  float lt = sum16(e);
+  alpha = 1.0f;
+  const bool moved = __any(T::spill(lt, e) || !st.seen);
+  if (moved) {
+    const float bx = block_max(s);   // max over the query column of s cx - moff
+    // Raise the reference only (alpha <= 1); an unseen row takes the block's
+    // maximum as it is, unless every key so far is hidden (bx = -inf).
+    const float shift = st.seen ? fmaxf(bx, 0.0f) : (bx > -INFINITY ? bx : 0.0f);
+    alpha = __builtin_amdgcn_exp2f(-shift);
+    st.seen = st.seen || bx > -INFINITY;
+    st.moff += shift;
+    st.l *= alpha;
+    st.mu *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(s[r] - shift);
+    lt = sum16(e);
+  }
+  st.l += lt;
+  return moved;
+}
+
+// Step 2: pB = e and uB = e dS (dS = sd, times us when SCALED_U) as 16-bit B
+// operands for keys 16kc .. 16kc+15.
+template <typename T, bool SCALED_U>
+__device__ inline void block_pack16(const float (&e)[16], const f32x16& sd, float us,
+                                    typename T::vec8 (&pB)[2], typename T::vec8 (&uB)[2]) {
+  uint32_t pw[8], uw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pw[i] = T::pack2(e[2 * i], e[2 * i + 1]);
+    const float u0 = SCALED_U ? (sd[2 * i] * us) * e[2 * i] : sd[2 * i] * e[2 * i];
+    const float u1 = SCALED_U ? (sd[2 * i + 1] * us) * e[2 * i + 1] : sd[2 * i + 1] * e[2 * i + 1];
+    uw[i] = T::pack2(u0, u1);
+  }
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    pB[kc] = __builtin_bit_cast(typename T::vec8, uint4{pw[4 * kc], pw[4 * kc + 1], pw[4 * kc + 2], pw[4 * kc + 3]});
+    uB[kc] = __builtin_bit_cast(typename T::vec8, uint4{uw[4 * kc], uw[4 * kc + 1], uw[4 * kc + 2], uw[4 * kc + 3]});
+  }
+}
+
+// mu += the 16 rounded products held in uB (the values the value products use).
+template <typename T>
+__device__ inline void block_mu16(const typename T::vec8 (&uB)[2], RowState16& st) {
+  const uint4 a = __builtin_bit_cast(uint4, uB[0]), b = __builtin_bit_cast(uint4, uB[1]);
+  float m0 = T::dot2sum(a.x, 0.0f), m1 = T::dot2sum(b.x, 0.0f);
+  m0 = T::dot2sum(a.y, m0);
+  m1 = T::dot2sum(b.y, m1);
+  m0 = T::dot2sum(a.z, m0);
+  m1 = T::dot2sum(b.z, m1);
+  m0 = T::dot2sum(a.w, m0);
+  m1 = T::dot2sum(b.w, m1);
   st.mu += m0 + m1;
 }
 
@@ -820,7 +934,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
     accO[t] = f32x16{};
     accT[t] = f32x16{};
   }
-  RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
+  RowState16 st{0.0f, 0.0f, 0.0f, false};
   const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
 
   const int kv_end = CAUSAL ? min(a.Nk, q0 + kPPBM) : a.Nk;
@@ -911,48 +1025,40 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
         accT[t] = T::mfma(tva[t][kc], pB[kc], accT[t]);
       }
   };
-  // Scores of block k (in sn): mask, reference maximum, weights into pB / uB.
-  auto settle = [&](int k) {
+  // Scores of block k (in sn): mask, then weights into pB / uB. The V / dV
+  // operands of block k (stage stv) are read while the weights are packed.
+  auto settle = [&](int k, const char* stv) {
     mask_apply<T, MASK, POW2>(sn, mk, a.scale);
     if (needs_keymask(k)) hide_keys<CAUSAL>(sn, a.Nk, qi, k * 32, hlf);
-    float alpha;
-    if (update_max(block_max(sn), st, a.cx, a.thr, alpha)) {
+    float e[16], alpha;
+    if (block_exp16<T>(sn, st, a.cx, e, alpha)) {
 #pragma unroll
       for (int t = 0; t < L::NT; ++t) {
         accO[t] *= alpha;
         accT[t] *= alpha;
       }
     }
-    exp_block(sn, sdn, st, a.cx);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      uint4 pw, uw;
-      const float us = POW2 ? 1.0f : a.scale;
-      pw.x = T::pack2(sn[8 * kc + 0], sn[8 * kc + 1]);
-      pw.y = T::pack2(sn[8 * kc + 2], sn[8 * kc + 3]);
-      pw.z = T::pack2(sn[8 * kc + 4], sn[8 * kc + 5]);
-      pw.w = T::pack2(sn[8 * kc + 6], sn[8 * kc + 7]);
-      uw.x = T::pack2(sdn[8 * kc + 0] * us, sdn[8 * kc + 1] * us);
-      uw.y = T::pack2(sdn[8 * kc + 2] * us, sdn[8 * kc + 3] * us);
-      uw.z = T::pack2(sdn[8 * kc + 4] * us, sdn[8 * kc + 5] * us);
-      uw.w = T::pack2(sdn[8 * kc + 6] * us, sdn[8 * kc + 7] * us);
-      pB[kc] = __builtin_bit_cast(vec8, pw);
-      uB[kc] = __builtin_bit_cast(vec8, uw);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    read_v(stv);
+    block_pack16<T, !POW2>(e, sdn, a.scale, pB, uB);
   };
 
-  // Matrix phase of iteration i: value products of block i, score products of block i+1.
-  auto matrix_phase = [&](int i) {
+  // Matrix phase of iteration i: value products of block i (mu takes its
+  // weight products), then the score products of block i+1, whose K / dK
+  // operands (stage stn) are read first so they arrive while the value
+  // products run.
+  auto matrix_phase = [&](int i, const char* stn) {
     if (i > last) return;
-    if (i + 1 <= last) mma_s();
+    const bool more = i + 1 <= last;
+    if (more) read_k(stn);
     mma_v();
+    block_mu16<T>(uB, st);
+    if (more) mma_s();
   };
-  // Vector phase of iteration i: settle block i+1; operands K(i+2) from stk, V(i+1) from stv.
-  auto vector_phase = [&](int i, const char* stk, const char* stv) {
+  // Vector phase of iteration i: settle block i+1 (V / dV from stage stn).
+  auto vector_phase = [&](int i, const char* stn) {
     if (i + 1 > last) return;
-    read_v(stv);
-    if (i + 2 <= last) read_k(stk);
-    settle(i + 1);
+    settle(i + 1, stn);
     if (i + 2 <= last) mask_load<MASK>(mk, a, mr, qi, (i + 2) * 32, hlf);
   };
   // Group B's wait for its loads of tile j; tiles issued after j may stay in flight.
@@ -985,13 +1091,12 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
     read_k(stage0);
     mma_s();
     mask_load<MASK>(mk, a, mr, qi, 0, hlf);
-    settle(0);
-    read_v(stage0);
-    if (1 <= last) {
-      read_k(stage1);
-      mask_load<MASK>(mk, a, mr, qi, 32, hlf);
-    }
+    settle(0, stage0);
+    if (1 <= last) mask_load<MASK>(mk, a, mr, qi, 32, hlf);
   }
+  // Operands of the first matrix phase have arrived (states the loop's entry
+  // as free of pending LDS reads, as every later iteration is).
+  __builtin_amdgcn_s_waitcnt(0xc07f);
 
   // Every wave runs matrix(i), barrier, vector(i), barrier. Group B starts
   // one barrier late, so the two waves of each SIMD are always in opposite
@@ -1003,21 +1108,21 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
     wait_tile(2);
     ring_barrier();
   }
-  auto iteration = [&](int i, char* st_r, char* st_r1, char* st_r2) {
-    matrix_phase(i);
+  auto iteration = [&](int i, char* st_r, char* st_r1) {
+    matrix_phase(i, st_r1);
     if (grp_b && i + kPPStages < n_tiles) issue_tile(i + kPPStages, st_r);
     ring_barrier();
-    vector_phase(i, st_r2, st_r1);
+    vector_phase(i, st_r1);
     if (grp_b) wait_tile(i + 3);
     ring_barrier();
   };
   for (int i = 0; i < n_tiles; i += kPPStages) {
-    iteration(i, stage0, stage1, stage2);
-    if (i + 1 < n_tiles) iteration(i + 1, stage1, stage2, stage3);
-    if (i + 2 < n_tiles) iteration(i + 2, stage2, stage3, stage4);
-    if (i + 3 < n_tiles) iteration(i + 3, stage3, stage4, stage5);
-    if (i + 4 < n_tiles) iteration(i + 4, stage4, stage5, stage0);
-    if (i + 5 < n_tiles) iteration(i + 5, stage5, stage0, stage1);
+    iteration(i, stage0, stage1);
+    if (i + 1 < n_tiles) iteration(i + 1, stage1, stage2);
+    if (i + 2 < n_tiles) iteration(i + 2, stage2, stage3);
+    if (i + 3 < n_tiles) iteration(i + 3, stage3, stage4);
+    if (i + 4 < n_tiles) iteration(i + 4, stage4, stage5);
+    if (i + 5 < n_tiles) iteration(i + 5, stage5, stage0);
   }
   if (!grp_b) ring_barrier();
 
@@ -1025,7 +1130,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   const float mu = xhalf_sum(st.mu);
   if (qi < a.Nq) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const float tl = POW2 ? mu * inv : mu * a.scale * inv;
+    const float tl = mu * inv;   // mu already sums e dS
     uint16_t* op = static_cast<uint16_t*>(a.o) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
     uint16_t* top = static_cast<uint16_t*>(a.to) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
 #pragma unroll
@@ -1337,11 +1442,11 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
     a.mask_vec = mask && (p->mask_stride_b % need == 0) && (p->mask_stride_h % need == 0) &&
                  (p->mask_stride_q % need == 0) && (base % (need * mes) == 0);
   }
-  // Kernel choice: the 4-wave kernel (128 rows per workgroup) by default; the
-  // 8-wave ping-pong kernel (256 rows, 16-bit d = 64) is measured slower at
-  // present and runs only when JVPATTN_FWD_KERNEL=pp asks for it (testing).
+  // Kernel choice: the 8-wave ping-pong kernel (256 rows per workgroup) for
+  // 16-bit d = 64 when it still gives every CU a workgroup; otherwise the
+  // 4-wave kernel (128 rows). JVPATTN_FWD_KERNEL=pp|wg4 forces one (testing).
   const int64_t n128 = (p->Nq + kBM - 1) / kBM, n256 = (p->Nq + kPPBM - 1) / kPPBM;
-  bool pp = false;
+  bool pp = p->d == 64 && p->dtype != JVPATTN_F32 && n256 * a.BH >= 256;
   if (const char* env = std::getenv("JVPATTN_FWD_KERNEL")) {
     if (std::strcmp(env, "pp") == 0) pp = p->d == 64 && p->dtype != JVPATTN_F32;
     if (std::strcmp(env, "wg4") == 0) pp = false;

@@ -109,7 +109,9 @@ int jvpattn_check_fwd(const jvpattn_params* params,
  * float32 accumulation; softmax statistics in float32; for 16-bit inputs the
  * softmax weights and their products with the score tangent are rounded to
  * the input type before the value products; O and dO are rounded to nearest
- * even. Float32 inputs use float32 matrix products throughout. */
+ * even. Float32 inputs use float32 matrix products throughout. For float16
+ * the rounded products of weights and score tangents stay finite while
+ * |dS| < 1024 (weights are kept at most 64 against the running reference). */
 int jvpattn_fwd(const jvpattn_params* params,
                 const void* q, const void* k, const void* v,
                 const void* tq, const void* tk, const void* tv,
