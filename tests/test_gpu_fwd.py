@@ -232,6 +232,49 @@ def test_custom_scale(kernel):
     check(w, scale=0.05)
 
 
+# ------------------------------------------------ the running reference
+# The kernels keep one reference per row (a past maximum) and rebase it only
+# when a block's weights against it grow too large. These inputs force that
+# path on every block, across a jump that overflows float32 weights, and for
+# rows whose first visible key comes late.
+
+def _additive_rows(w, fill):
+    x = I.make_inputs(w)
+    N = w.N
+    m = torch.zeros(N, N, dtype=torch.float32)
+    fill(m)
+    x["mask"] = m.to(x["q"].dtype)[None, None].contiguous()
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_rising_scores_rebase_every_block(dtype, kernel):
+    """An additive ramp of 0.6 per key lifts each 32-key block ~19 above the last."""
+    w = I.Workload("ramp", B=1, H=2, N=512, d=64, dtype=dtype, mask_kind="additive", std=1.0, seed=21)
+    x = _additive_rows(w, lambda m: m.add_(torch.arange(w.N, dtype=torch.float32)[None, :] * 0.6))
+    check(w, x)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_score_jump_past_float32_range(dtype, kernel):
+    """+200 on key 300: weights against the old reference overflow to inf."""
+    w = I.Workload("jump", B=1, H=2, N=512, d=64, dtype=dtype, mask_kind="additive", std=1.0, seed=22)
+    x = _additive_rows(w, lambda m: m[:, 300].fill_(200.0))
+    check(w, x)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_late_first_visible_key(dtype, kernel):
+    """Even rows see nothing before key 300 and then scores 100 above the rest."""
+    w = I.Workload("late", B=1, H=2, N=512, d=64, dtype=dtype, mask_kind="additive", std=1.0, seed=23)
+
+    def fill(m):
+        m[0::2, :300] = float("-inf")
+        m[0::2, 300:] = 100.0
+    x = _additive_rows(w, fill)
+    check(w, x)
+
+
 def test_all_4x4_bool_masks_in_one_launch():
     """All 2^16 boolean masks of a 4x4 score block as the batch axis of one launch, causal off and on."""
     B = 1 << 16
