@@ -1049,11 +1049,23 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   // products run.
   auto matrix_phase = [&](int i, const char* stn) {
     if (i > last) return;
-    const bool more = i + 1 <= last;
-    if (more) read_k(stn);
+    // On a wave's last block the score products are of no use (stn holds
+    // some other tile, read harmlessly); issuing them anyway keeps the phase
+    // one straight-line block the scheduler can interleave.
+    read_k(stn);
     mma_v();
     block_mu16<T>(uB, st);
-    if (more) mma_s();
+    mma_s();
+    // The K / dK reads go out between the first value products, so their
+    // issue does not hold up the matrix cores; the score products follow.
+#pragma unroll
+    for (int j = 0; j < 2 * L::NC; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6 * L::NT - 2 * L::NC, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 3 * L::NC, 0);
   };
   // Vector phase of iteration i: settle block i+1 (V / dV from stage stn).
   auto vector_phase = [&](int i, const char* stn) {
