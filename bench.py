@@ -48,12 +48,14 @@ def algorithmic_bytes(w):
     return w.B * w.H * per_head + mask
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "forward_mode_autodiff_amd", "csrc", "jvpattn_fwd.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "forward_mode_autodiff_amd", "csrc", f)
+                  for f in ("jvpattn_fwd.hip", "jvpattn_device.h")]
 TRAFFIC_FILES = {"hvp": os.path.join(ROOT, "profiles", "hvp_fwd_bf16_causal_hbm_traffic.txt")}
 
 
 def measured_traffic(workload):
-    """HBM bytes per launch from the committed counter summary, or None if absent or the kernel changed since."""
+    """HBM bytes per launch from the committed counter summary, or None if absent or the kernel changed since
+    (the summary records a hash of the forward's device sources)."""
     import hashlib
     path = TRAFFIC_FILES.get(workload)
     if not path or not os.path.exists(path):
@@ -63,7 +65,7 @@ def measured_traffic(workload):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()[:16]
     if fields.get("kernel_source_sha256_16") != sha or "traffic_bytes_per_launch" not in fields:
         return None
     return int(float(fields["traffic_bytes_per_launch"]))

@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libjvpattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["jvpattn_fwd.hip", "jvpattn_check.cpp"]
+SOURCES = ["jvpattn_fwd.hip", "jvpattn_bwd.hip", "jvpattn_check.cpp"]
 
 
 def hipcc() -> str:

@@ -1,0 +1,786 @@
+// Reverse pass of the fused attention forward with tangents, for gfx950.
+//
+// With cotangents G of O and Gd of dO (L = <G, O> + <Gd, dO>), the forward's
+// intermediates per (query i, key j) -- P, the score tangent Sd = dS, and
+// Pd = P (Sd - tlse) -- give
+//   D    = Gd V^T                       (the cotangent of Pd)
+//   r_i  = Gd_i . O_i                   (= sum_j D_ij P_ij)
+//   dP   = G V^T + Gd dV^T + D (Sd - tlse) - r Sd
+//   del_i = G_i . O_i + Gd_i . dO_i - tlse_i r_i   (= sum_j P_ij dP_ij)
+//   Sbar  = P (dP - del)                cotangent of the scores
+//   Sdbar = P (D - r)                   cotangent of the score tangents
+//   dq  = scale (Sbar K + Sdbar dK)     dk  = scale (Sbar^T Q + Sdbar^T dQ)
+//   dtq = scale Sdbar K                 dtk = scale Sdbar^T Q
+//   dv  = P^T G + Pd^T Gd               dtv = P^T Gd
+// which is the chain rule run backwards through the forward's steps (the
+// float64 oracle runs those steps one at a time; the two agree to rounding).
+// The N x N matrices are never stored: three kernels recompute them per tile.
+//   rows: per query row r, del and -lse*log2(e) and tlse into the workspace;
+//   dkv:  one workgroup per 128 keys, looping over 32-query tiles;
+//   dq:   one workgroup per 128 queries, looping over 32-key tiles.
+// Both tile kernels use the forward's MFMA layout (32x32x16 products, C
+// registers rounded to 16 bits reused as B operands, transpose reads of the
+// LDS tiles for the accumulating products).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+
+#include "jvpattn.h"
+#include "jvpattn_device.h"
+#include "jvpattn_internal.h"
+
+namespace jvpattn {
+namespace {
+
+constexpr int kBWaves = 4;
+constexpr int kBThreads = 64 * kBWaves;
+constexpr int kBBlk = 32 * kBWaves;   // keys (dkv) or queries (dq) per workgroup
+static_assert(kBThreads == kTileThreads, "LDS tiles are laid out for 4 waves");
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* tq;
+  const void* tk;
+  const void* tv;
+  const void* mask;
+  const void* o;
+  const void* to;
+  const void* go;
+  const void* gto;
+  const float* lse;
+  const float* tlse;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dtq;
+  void* dtk;
+  void* dtv;
+  float* ws;          // [4][ws_stride]: -lse*log2e, tlse, r, del
+  int64_t ws_stride;  // floats per workspace array
+  int H, Nq, Nk, BH;
+  int n_blk;
+  int mask_vec;
+  int64_t msb, msh, msq;
+  float scale;
+  float cx;           // score units -> log2 units
+};
+
+enum { WS_NEGL = 0, WS_TLSE = 1, WS_R = 2, WS_DEL = 3 };
+
+// ------------------------------------------------------------------ rows
+// One thread per query row (d = 64: eight 16-byte granules per tensor row).
+template <typename T>
+__device__ __forceinline__ void bwd_rows_body(const BwdArgs& a, int64_t rows) {
+  const int64_t row = int64_t(blockIdx.x) * kBThreads + threadIdx.x;
+  if (row >= rows) return;
+  const uint4* o = static_cast<const uint4*>(a.o) + row * 8;
+  const uint4* to = static_cast<const uint4*>(a.to) + row * 8;
+  const uint4* g = static_cast<const uint4*>(a.go) + row * 8;
+  const uint4* gd = static_cast<const uint4*>(a.gto) + row * 8;
+  float r = 0.0f, go_o = 0.0f, gd_to = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint4 wo = o[c], wto = to[c], wg = g[c], wgd = gd[c];
+    const uint32_t xo[4] = {wo.x, wo.y, wo.z, wo.w}, xto[4] = {wto.x, wto.y, wto.z, wto.w};
+    const uint32_t xg[4] = {wg.x, wg.y, wg.z, wg.w}, xgd[4] = {wgd.x, wgd.y, wgd.z, wgd.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int hw = 0; hw < 2; ++hw) {
+        const uint16_t so = hw ? hi16(xo[i]) : lo16(xo[i]);
+        const uint16_t sto = hw ? hi16(xto[i]) : lo16(xto[i]);
+        const uint16_t sg = hw ? hi16(xg[i]) : lo16(xg[i]);
+        const uint16_t sgd = hw ? hi16(xgd[i]) : lo16(xgd[i]);
+        const float fo = T::widen(so), fgd = T::widen(sgd);
+        r = fmaf(fgd, fo, r);
+        go_o = fmaf(T::widen(sg), fo, go_o);
+        gd_to = fmaf(fgd, T::widen(sto), gd_to);
+      }
+    }
+  }
+  const float lse = a.lse[row], tl = a.tlse[row];
+  a.ws[WS_NEGL * a.ws_stride + row] = lse == -INFINITY ? -INFINITY : -lse * kLog2e;
+  a.ws[WS_TLSE * a.ws_stride + row] = tl;
+  a.ws[WS_R * a.ws_stride + row] = r;
+  a.ws[WS_DEL * a.ws_stride + row] = go_o + gd_to - tl * r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBThreads) void bwd_rows_kernel(BwdArgs a, int64_t rows) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  bwd_rows_body<T>(a, rows);
+#endif
+}
+
+// Element-wise step shared by both tile kernels. For one score element:
+// s (masked score, score units), sd (score tangent, times us gives dS),
+// x = (G V^T + Gd dV^T), dm = D, and the row's statistics.
+struct Cot {
+  float p, pd, sbar, sdbar;
+};
+__device__ inline Cot cotangents(float s, float sd, float x, float dm, float cx, float us, float negl, float tl,
+                                 float r, float del) {
+  Cot c;
+  c.p = __builtin_amdgcn_exp2f(fmaf(s, cx, negl));
+  const float sdv = sd * us;        // dS
+  const float sdu = sdv - tl;       // dS - tlse
+  c.pd = c.p * sdu;
+  const float dp = x + dm * sdu - r * sdv;
+  c.sbar = c.p * (dp - del);
+  c.sdbar = c.p * (dm - r);
+  return c;
+}
+
+// ------------------------------------------------------------------ dq
+//
+// Four waves, 32 queries each (128 per workgroup), a loop over 32-key tiles
+// of K, dK, V, dV in the forward's LDS format (ring of 4, fetched two tiles
+// ahead). Per tile and wave, with the forward's transposed layout (lane =
+// query column, 16 keys per lane):
+//   S^T = K Q^T, Sd^T = dK Q^T + K dQ^T, X^T = V G^T + dV Gd^T, D^T = V Gd^T
+// (24 products), the cotangents per element, then
+//   dq^T += K^T Sbar^T + dK^T Sdbar^T,  dtq^T += K^T Sdbar^T  (12 products).
+template <typename T, int MASK, bool CAUSAL, bool POW2>
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
+  constexpr int D = 64;
+  using L = Tile16<D>;
+  using vec8 = typename T::vec8;
+  __shared__ __attribute__((aligned(16))) char stage0[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage1[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage2[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char stage3[L::STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c32 = lane & 31;
+  const int hlf = lane >> 5;
+
+  const int qb = a.n_blk - 1 - int(blockIdx.x) / a.BH;   // heaviest first when causal
+  const int bh = int(blockIdx.x) % a.BH;
+  const int b = bh / a.H, h = bh % a.H;
+  const int q0 = qb * kBBlk;
+  const int qw0 = q0 + 32 * wave;
+  const int qi = qw0 + c32;
+  const bool wave_live = qw0 < a.Nq;
+
+  const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
+  const int64_t khead = int64_t(bh) * a.Nk * L::ROW;
+  const int64_t qbytes = int64_t(a.Nq) * L::ROW, kbytes = int64_t(a.Nk) * L::ROW;
+  auto at = [](const void* p, int64_t off) { return static_cast<const char*>(p) + off; };
+
+  // B operands of this wave's 32 queries: Q, dQ (scale folded in when exact), G, Gd.
+  vec8 qB[L::NC], tqB[L::NC], gB[L::NC], tgB[L::NC];
+  {
+    const Rsrc rq = make_rsrc(at(a.q, qhead), qbytes);
+    const Rsrc rtq = make_rsrc(a.tq ? at(a.tq, qhead) : at(a.q, qhead), a.tq ? qbytes : 0);
+    const Rsrc rg = make_rsrc(at(a.go, qhead), qbytes), rtg = make_rsrc(at(a.gto, qhead), qbytes);
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) {
+      const int off = qi * L::ROW + (hlf * (D / 2) + 8 * c) * 2;
+      qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
+      tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
+      gB[c] = __builtin_bit_cast(vec8, ld128(rg, off));
+      tgB[c] = __builtin_bit_cast(vec8, ld128(rtg, off));
+      if constexpr (POW2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qB[c][e] = static_cast<__bf16>(static_cast<float>(qB[c][e]) * a.scale);
+          tqB[c][e] = static_cast<__bf16>(static_cast<float>(tqB[c][e]) * a.scale);
+        }
+      }
+    }
+  }
+  // Row statistics of this lane's query (rows past Nq read as zero and are never stored).
+  float negl = -INFINITY, tl = 0.0f, rr = 0.0f, del = 0.0f;
+  if (qi < a.Nq) {
+    const int64_t ri = int64_t(bh) * a.Nq + qi;
+    negl = a.ws[WS_NEGL * a.ws_stride + ri];
+    tl = a.ws[WS_TLSE * a.ws_stride + ri];
+    rr = a.ws[WS_R * a.ws_stride + ri];
+    del = a.ws[WS_DEL * a.ws_stride + ri];
+  }
+  const float us = POW2 ? 1.0f : a.scale;
+
+  f32x16 accQ[L::NT], accTQ[L::NT];
+#pragma unroll
+  for (int t = 0; t < L::NT; ++t) {
+    accQ[t] = f32x16{};
+    accTQ[t] = f32x16{};
+  }
+  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+
+  const int kv_end = CAUSAL ? min(a.Nk, q0 + kBBlk) : a.Nk;
+  const int n_tiles = (kv_end + L::BN - 1) / L::BN;
+  const int last = !wave_live ? -1 : (CAUSAL ? min(n_tiles - 1, qw0 >> 5) : n_tiles - 1);
+  auto needs_keymask = [&](int k) { return (CAUSAL && k * 32 + 31 > qw0) || (k * 32 + 32 > a.Nk); };
+
+  int dl_off[L::LOADS];
+#pragma unroll
+  for (int i = 0; i < L::LOADS; ++i) {
+    const int p = i * kBThreads + tid;
+    const int row = p / L::GR, pg = p % L::GR;
+    dl_off[i] = row * L::ROW + ((pg ^ swz(row)) << 4);
+  }
+  const Rsrc rk = make_rsrc(at(a.k, khead), kbytes), rv = make_rsrc(at(a.v, khead), kbytes);
+  const Rsrc rtk = make_rsrc(a.tk ? at(a.tk, khead) : at(a.k, khead), a.tk ? kbytes : 0);
+  const Rsrc rtv = make_rsrc(a.tv ? at(a.tv, khead) : at(a.v, khead), a.tv ? kbytes : 0);
+  auto issue_tile = [&](int j, char* stage) {
+#pragma unroll
+    for (int i = 0; i < L::LOADS; ++i) {
+      const int off = j * L::TENSOR_BYTES + dl_off[i];
+      const int slot = (i * kBThreads + wave * 64) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
+                                               16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rtk, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rtv, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+    }
+  };
+
+  int kofs[L::NC];
+#pragma unroll
+  for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ swz(c32)) << 4);
+  int vofs0[L::NT], vofs1[L::NT];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int r0 = 4 * hlf + (i16 >> 2), r1 = r0 + 8;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t) {
+      const int gcol = 4 * t + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      vofs0[t] = r0 * L::ROW + ((gcol ^ swz(r0)) << 4) + 8 * (i16 & 1);
+      vofs1[t] = r1 * L::ROW + ((gcol ^ swz(r1)) << 4) + 8 * (i16 & 1);
+    }
+  }
+  // A operands (rows = keys) of tensor `tsr` of the tile at sb.
+  auto read_rows = [&](const char* sb, int tsr, vec8 (&x)[L::NC]) {
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) x[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + tsr * L::TENSOR_BYTES, kofs[c]));
+  };
+  // Transposed A operands (rows = head dimension, keys along k) of tensor `tsr`.
+  auto read_tr = [&](const char* sb, int tsr, vec8 (&x)[L::NT][2]) {
+    const char* base = sb + tsr * L::TENSOR_BYTES;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int o0 = 16 * kc * L::ROW + vofs0[t], o1 = 16 * kc * L::ROW + vofs1[t];
+        x[t][kc] = __builtin_bit_cast(
+            vec8, __builtin_shufflevector(lds_read_tr(base + o0), lds_read_tr(base + o1), 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+  };
+
+  auto tile = [&](int k, const char* sb) {
+    vec8 ka[L::NC], tka[L::NC];
+    read_rows(sb, 0, ka);
+    read_rows(sb, 1, tka);
+    f32x16 s = f32x16{}, sd = f32x16{}, x = f32x16{}, dm = f32x16{};
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) {
+      s = T::mfma(ka[c], qB[c], s);
+      sd = T::mfma(tka[c], qB[c], sd);
+      sd = T::mfma(ka[c], tqB[c], sd);
+    }
+    vec8 va[L::NC], tva[L::NC];
+    read_rows(sb, 2, va);
+    read_rows(sb, 3, tva);
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) {
+      x = T::mfma(va[c], gB[c], x);
+      x = T::mfma(tva[c], tgB[c], x);
+      dm = T::mfma(va[c], tgB[c], dm);
+    }
+    MaskVals<MASK> mk;
+    mask_load<MASK>(mk, a, mr, qi, k * 32, hlf);
+    mask_apply<T, MASK, POW2>(s, mk, a.scale);
+    if (needs_keymask(k)) hide_keys<CAUSAL>(s, a.Nk, qi, k * 32, hlf);
+    vec8 sB[2], sdB[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      uint32_t w0[4], w1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r0 = 8 * kc + 2 * i;
+        const Cot c0 = cotangents(s[r0], sd[r0], x[r0], dm[r0], a.cx, us, negl, tl, rr, del);
+        const Cot c1 = cotangents(s[r0 + 1], sd[r0 + 1], x[r0 + 1], dm[r0 + 1], a.cx, us, negl, tl, rr, del);
+        w0[i] = T::pack2(c0.sbar, c1.sbar);
+        w1[i] = T::pack2(c0.sdbar, c1.sdbar);
+      }
+      sB[kc] = __builtin_bit_cast(vec8, uint4{w0[0], w0[1], w0[2], w0[3]});
+      sdB[kc] = __builtin_bit_cast(vec8, uint4{w1[0], w1[1], w1[2], w1[3]});
+    }
+    vec8 kt[L::NT][2], tkt[L::NT][2];
+    read_tr(sb, 0, kt);
+    read_tr(sb, 1, tkt);
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        accQ[t] = T::mfma(kt[t][kc], sB[kc], accQ[t]);
+        accQ[t] = T::mfma(tkt[t][kc], sdB[kc], accQ[t]);
+        accTQ[t] = T::mfma(kt[t][kc], sdB[kc], accTQ[t]);
+      }
+  };
+
+  // Before step k's wait, tiles k and k+1 may be in flight (k+2 is issued after it).
+  auto wait_tile = [&](int j) {
+    if (j + 1 < n_tiles) wait_vmcnt<L::TILE_VMEM>();
+    else wait_vmcnt<0>();
+  };
+  if (n_tiles > 0) issue_tile(0, stage0);
+  if (n_tiles > 1) issue_tile(1, stage1);
+  auto step = [&](int k, const char* cur, char* dma) {
+    wait_tile(k);
+    ring_barrier();   // tile k visible; every wave is done with tile k-2 (stage of k+2)
+    if (k + 2 < n_tiles) issue_tile(k + 2, dma);
+    if (k <= last) tile(k, cur);
+  };
+  for (int k = 0; k < n_tiles; k += 4) {
+    step(k, stage0, stage2);
+    if (k + 1 < n_tiles) step(k + 1, stage1, stage3);
+    if (k + 2 < n_tiles) step(k + 2, stage2, stage0);
+    if (k + 3 < n_tiles) step(k + 3, stage3, stage1);
+  }
+
+  if (qi < a.Nq) {
+    uint16_t* dq = static_cast<uint16_t*>(a.dq) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
+    uint16_t* dtq = static_cast<uint16_t*>(a.dtq) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * t + 8 * g + 4 * hlf;
+        const f32x16& A = accQ[t];
+        const f32x16& B = accTQ[t];
+        *reinterpret_cast<uint2*>(dq + dd) =
+            uint2{T::pack2(A[4 * g] * a.scale, A[4 * g + 1] * a.scale), T::pack2(A[4 * g + 2] * a.scale, A[4 * g + 3] * a.scale)};
+        *reinterpret_cast<uint2*>(dtq + dd) =
+            uint2{T::pack2(B[4 * g] * a.scale, B[4 * g + 1] * a.scale), T::pack2(B[4 * g + 2] * a.scale, B[4 * g + 3] * a.scale)};
+      }
+  }
+}
+
+template <typename T, int MASK, bool CAUSAL, bool POW2>
+__global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  bwd_dq_body<T, MASK, CAUSAL, POW2>(a);
+#endif
+}
+
+// ------------------------------------------------------------------ dkv
+//
+// Four waves, 32 keys each (128 per workgroup), a loop over 32-query tiles of
+// Q, dQ, G, Gd (same LDS format) plus the four row statistics of the tile.
+// Here lane = key column and 16 queries per lane:
+//   S = Q K^T, Sd = dQ K^T + Q dK^T, X = G V^T + Gd dV^T, D = Gd V^T   (24)
+//   dk^T += Q^T Sbar + dQ^T Sdbar, dtk^T += Q^T Sdbar,
+//   dv^T += G^T P + Gd^T Pd,       dtv^T += Gd^T P                      (24)
+// Row r of a lane's C registers is query 8*(r/4) + 4*(lane/32) + r%4.
+
+// Mask values (i, key) for this lane's key and the 16 queries of its rows.
+template <int MASK> struct MaskCol {};
+template <> struct MaskCol<JVPATTN_MASK_BOOL> { uint32_t w[16]; };
+template <> struct MaskCol<JVPATTN_MASK_ADDITIVE> { uint32_t w[16]; };
+
+template <typename T, int MASK, bool CAUSAL, bool POW2>
+__device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
+  constexpr int D = 64;
+  using L = Tile16<D>;
+  using vec8 = typename T::vec8;
+  constexpr int STATS = 4 * 32 * 4;                // four statistics of 32 rows
+  constexpr int SB = L::STAGE_BYTES + STATS;
+  __shared__ __attribute__((aligned(16))) char stage0[SB];
+  __shared__ __attribute__((aligned(16))) char stage1[SB];
+  __shared__ __attribute__((aligned(16))) char stage2[SB];
+  __shared__ __attribute__((aligned(16))) char stage3[SB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c32 = lane & 31;
+  const int hlf = lane >> 5;
+
+  const int kb = int(blockIdx.x) / a.BH;   // causal: early key blocks see the most queries
+  const int bh = int(blockIdx.x) % a.BH;
+  const int b = bh / a.H, h = bh % a.H;
+  const int k0 = kb * kBBlk;
+  const int kw0 = k0 + 32 * wave;
+  const int kj = kw0 + c32;                 // this lane's key
+  const bool wave_live = kw0 < a.Nk;
+
+  const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
+  const int64_t khead = int64_t(bh) * a.Nk * L::ROW;
+  const int64_t qbytes = int64_t(a.Nq) * L::ROW, kbytes = int64_t(a.Nk) * L::ROW;
+  auto at = [](const void* p, int64_t off) { return static_cast<const char*>(p) + off; };
+
+  // B operands of this wave's 32 keys: K, dK (scale folded in when exact), V, dV.
+  vec8 kB[L::NC], tkB[L::NC], vB[L::NC], tvB[L::NC];
+  {
+    const Rsrc rk = make_rsrc(at(a.k, khead), kbytes), rv = make_rsrc(at(a.v, khead), kbytes);
+    const Rsrc rtk = make_rsrc(a.tk ? at(a.tk, khead) : at(a.k, khead), a.tk ? kbytes : 0);
+    const Rsrc rtv = make_rsrc(a.tv ? at(a.tv, khead) : at(a.v, khead), a.tv ? kbytes : 0);
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) {
+      const int off = kj * L::ROW + (hlf * (D / 2) + 8 * c) * 2;
+      kB[c] = __builtin_bit_cast(vec8, ld128(rk, off));
+      tkB[c] = __builtin_bit_cast(vec8, ld128(rtk, off));
+      vB[c] = __builtin_bit_cast(vec8, ld128(rv, off));
+      tvB[c] = __builtin_bit_cast(vec8, ld128(rtv, off));
+      if constexpr (POW2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kB[c][e] = static_cast<__bf16>(static_cast<float>(kB[c][e]) * a.scale);
+          tkB[c][e] = static_cast<__bf16>(static_cast<float>(tkB[c][e]) * a.scale);
+        }
+      }
+    }
+  }
+  const float us = POW2 ? 1.0f : a.scale;
+
+  f32x16 accK[L::NT], accTK[L::NT], accV[L::NT], accTV[L::NT];
+#pragma unroll
+  for (int t = 0; t < L::NT; ++t) {
+    accK[t] = f32x16{};
+    accTK[t] = f32x16{};
+    accV[t] = f32x16{};
+    accTV[t] = f32x16{};
+  }
+  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+
+  const int n_qt = (a.Nq + 31) / 32;
+  // causal: queries before the block's first key see none of its keys
+  const int t_begin = CAUSAL ? min(n_qt, k0 >> 5) : 0;
+  const int first = !wave_live ? n_qt : (CAUSAL ? max(t_begin, kw0 >> 5) : 0);   // first tile of this wave
+  auto needs_rowmask = [&](int t) { return (CAUSAL && t * 32 < kw0 + 32) || (t * 32 + 32 > a.Nq) || (kw0 + 32 > a.Nk); };
+
+  int dl_off[L::LOADS];
+#pragma unroll
+  for (int i = 0; i < L::LOADS; ++i) {
+    const int p = i * kBThreads + tid;
+    const int row = p / L::GR, pg = p % L::GR;
+    dl_off[i] = row * L::ROW + ((pg ^ swz(row)) << 4);
+  }
+  const Rsrc rq = make_rsrc(at(a.q, qhead), qbytes);
+  const Rsrc rtq = make_rsrc(a.tq ? at(a.tq, qhead) : at(a.q, qhead), a.tq ? qbytes : 0);
+  const Rsrc rg = make_rsrc(at(a.go, qhead), qbytes), rtg = make_rsrc(at(a.gto, qhead), qbytes);
+  // Statistics of this head's rows: wave w loads statistic w of the tile (8 lanes x 16 bytes).
+  const int64_t srow = int64_t(bh) * a.Nq;
+  const Rsrc rstat = make_rsrc(a.ws + wave * a.ws_stride + srow, int64_t(a.Nq) * 4);
+  auto issue_tile = [&](int j, char* stage) {
+#pragma unroll
+    for (int i = 0; i < L::LOADS; ++i) {
+      const int off = j * L::TENSOR_BYTES + dl_off[i];
+      const int slot = (i * kBThreads + wave * 64) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
+                                               16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rtq, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rg, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rtg, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+    }
+    // 32 floats of statistic `wave` for rows 32j .. 32j+31 (past Nq: zeros)
+    if (lane < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rstat, (__attribute__((address_space(3))) void*)to_lds(stage + L::STAGE_BYTES + wave * 128), 16,
+          j * 128 + lane * 16, 0, 0, 0);
+  };
+
+  int kofs[L::NC];
+#pragma unroll
+  for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ swz(c32)) << 4);
+  int vofs0[L::NT], vofs1[L::NT];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int r0 = 4 * hlf + (i16 >> 2), r1 = r0 + 8;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t) {
+      const int gcol = 4 * t + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      vofs0[t] = r0 * L::ROW + ((gcol ^ swz(r0)) << 4) + 8 * (i16 & 1);
+      vofs1[t] = r1 * L::ROW + ((gcol ^ swz(r1)) << 4) + 8 * (i16 & 1);
+    }
+  }
+  auto read_rows = [&](const char* sb, int tsr, vec8 (&x)[L::NC]) {
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) x[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + tsr * L::TENSOR_BYTES, kofs[c]));
+  };
+  auto read_tr = [&](const char* sb, int tsr, vec8 (&x)[L::NT][2]) {
+    const char* base = sb + tsr * L::TENSOR_BYTES;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int o0 = 16 * kc * L::ROW + vofs0[t], o1 = 16 * kc * L::ROW + vofs1[t];
+        x[t][kc] = __builtin_bit_cast(
+            vec8, __builtin_shufflevector(lds_read_tr(base + o0), lds_read_tr(base + o1), 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+  };
+
+  auto tile = [&](int t_idx, const char* sb) {
+    const int i0 = t_idx * 32;   // first query of the tile
+    vec8 qa[L::NC], tqa[L::NC];
+    read_rows(sb, 0, qa);
+    read_rows(sb, 1, tqa);
+    f32x16 s = f32x16{}, sd = f32x16{}, x = f32x16{}, dm = f32x16{};
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) {
+      s = T::mfma(qa[c], kB[c], s);
+      sd = T::mfma(tqa[c], kB[c], sd);
+      sd = T::mfma(qa[c], tkB[c], sd);
+    }
+    vec8 ga[L::NC], tga[L::NC];
+    read_rows(sb, 2, ga);
+    read_rows(sb, 3, tga);
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) {
+      x = T::mfma(ga[c], vB[c], x);
+      x = T::mfma(tga[c], tvB[c], x);
+      dm = T::mfma(tga[c], vB[c], dm);
+    }
+    // masks: element (query i, key kj); hidden entries get score -inf
+    if constexpr (MASK != JVPATTN_MASK_NONE) {
+      constexpr int es = MASK == JVPATTN_MASK_BOOL ? 1 : 2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
+        const int off = (qrow * int(a.msq) + kj) * es;
+        if constexpr (MASK == JVPATTN_MASK_BOOL) {
+          if (__builtin_amdgcn_raw_buffer_load_b8(mr, off, 0, 0) == 0) s[r] = -INFINITY;
+        } else {
+          const float m = T::widen(__builtin_amdgcn_raw_buffer_load_b16(mr, off, 0, 0));
+          s[r] = POW2 ? s[r] + m : fmaf(s[r], a.scale, m);
+        }
+      }
+    }
+    if (needs_rowmask(t_idx)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
+        bool hide = qrow >= a.Nq || kj >= a.Nk;
+        if constexpr (CAUSAL) hide = hide || kj > qrow;
+        if (hide) s[r] = -INFINITY;
+      }
+    }
+    // statistics of the 16 rows: for group g, rows 8g + 4*hlf + 0..3 (one 16-byte LDS read each)
+    const char* st = sb + L::STAGE_BYTES;
+    vec8 pB[2], pdB[2], sB[2], sdB[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      uint32_t wp[4], wpd[4], ws[4], wsd[4];
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * kc + gg;
+        const int roff = (8 * g + 4 * hlf) * 4;
+        const f32x4 ng = lds_load<f32x4>(st, WS_NEGL * 128 + roff);
+        const f32x4 tl = lds_load<f32x4>(st, WS_TLSE * 128 + roff);
+        const f32x4 rr = lds_load<f32x4>(st, WS_R * 128 + roff);
+        const f32x4 dl = lds_load<f32x4>(st, WS_DEL * 128 + roff);
+        Cot c[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          c[e] = cotangents(s[r], sd[r], x[r], dm[r], a.cx, us, ng[e], tl[e], rr[e], dl[e]);
+        }
+        wp[2 * gg] = T::pack2(c[0].p, c[1].p);
+        wp[2 * gg + 1] = T::pack2(c[2].p, c[3].p);
+        wpd[2 * gg] = T::pack2(c[0].pd, c[1].pd);
+        wpd[2 * gg + 1] = T::pack2(c[2].pd, c[3].pd);
+        ws[2 * gg] = T::pack2(c[0].sbar, c[1].sbar);
+        ws[2 * gg + 1] = T::pack2(c[2].sbar, c[3].sbar);
+        wsd[2 * gg] = T::pack2(c[0].sdbar, c[1].sdbar);
+        wsd[2 * gg + 1] = T::pack2(c[2].sdbar, c[3].sdbar);
+      }
+      pB[kc] = __builtin_bit_cast(vec8, uint4{wp[0], wp[1], wp[2], wp[3]});
+      pdB[kc] = __builtin_bit_cast(vec8, uint4{wpd[0], wpd[1], wpd[2], wpd[3]});
+      sB[kc] = __builtin_bit_cast(vec8, uint4{ws[0], ws[1], ws[2], ws[3]});
+      sdB[kc] = __builtin_bit_cast(vec8, uint4{wsd[0], wsd[1], wsd[2], wsd[3]});
+    }
+    {
+      vec8 qt[L::NT][2], tqt[L::NT][2];
+      read_tr(sb, 0, qt);
+      read_tr(sb, 1, tqt);
+#pragma unroll
+      for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          accK[t] = T::mfma(qt[t][kc], sB[kc], accK[t]);
+          accK[t] = T::mfma(tqt[t][kc], sdB[kc], accK[t]);
+          accTK[t] = T::mfma(qt[t][kc], sdB[kc], accTK[t]);
+        }
+    }
+    {
+      vec8 gt[L::NT][2], tgt[L::NT][2];
+      read_tr(sb, 2, gt);
+      read_tr(sb, 3, tgt);
+#pragma unroll
+      for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          accV[t] = T::mfma(gt[t][kc], pB[kc], accV[t]);
+          accV[t] = T::mfma(tgt[t][kc], pdB[kc], accV[t]);
+          accTV[t] = T::mfma(tgt[t][kc], pB[kc], accTV[t]);
+        }
+    }
+  };
+
+  constexpr int TILE_VMEM = L::TILE_VMEM + 1;   // four tensors + this wave's statistic
+  // All waves issue the same count (the statistic load is exec-masked, not skipped).
+  // Before step t's wait, tiles t and t+1 may be in flight (t+2 is issued after it).
+  auto wait_tile = [&](int j) {
+    if (j + 1 < n_qt) wait_vmcnt<TILE_VMEM>();
+    else wait_vmcnt<0>();
+  };
+  const int n_steps = n_qt - t_begin;
+  if (n_steps > 0) issue_tile(t_begin, stage0);
+  if (n_steps > 1) issue_tile(t_begin + 1, stage1);
+  auto step = [&](int t_idx, const char* cur, char* dma) {
+    wait_tile(t_idx);
+    ring_barrier();
+    if (t_idx + 2 < n_qt) issue_tile(t_idx + 2, dma);
+    if (t_idx >= first) tile(t_idx, cur);
+  };
+  for (int i = 0; i < n_steps; i += 4) {
+    const int t_idx = t_begin + i;
+    step(t_idx, stage0, stage2);
+    if (i + 1 < n_steps) step(t_idx + 1, stage1, stage3);
+    if (i + 2 < n_steps) step(t_idx + 2, stage2, stage0);
+    if (i + 3 < n_steps) step(t_idx + 3, stage3, stage1);
+  }
+
+  if (kj < a.Nk) {
+    const int64_t base = int64_t(bh) * a.Nk * D + int64_t(kj) * D;
+    uint16_t* dk = static_cast<uint16_t*>(a.dk) + base;
+    uint16_t* dtk = static_cast<uint16_t*>(a.dtk) + base;
+    uint16_t* dv = static_cast<uint16_t*>(a.dv) + base;
+    uint16_t* dtv = static_cast<uint16_t*>(a.dtv) + base;
+    const float sc = a.scale;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * t + 8 * g + 4 * hlf;
+        const int e = 4 * g;
+        *reinterpret_cast<uint2*>(dk + dd) = uint2{T::pack2(accK[t][e] * sc, accK[t][e + 1] * sc),
+                                                   T::pack2(accK[t][e + 2] * sc, accK[t][e + 3] * sc)};
+        *reinterpret_cast<uint2*>(dtk + dd) = uint2{T::pack2(accTK[t][e] * sc, accTK[t][e + 1] * sc),
+                                                    T::pack2(accTK[t][e + 2] * sc, accTK[t][e + 3] * sc)};
+        *reinterpret_cast<uint2*>(dv + dd) =
+            uint2{T::pack2(accV[t][e], accV[t][e + 1]), T::pack2(accV[t][e + 2], accV[t][e + 3])};
+        *reinterpret_cast<uint2*>(dtv + dd) =
+            uint2{T::pack2(accTV[t][e], accTV[t][e + 1]), T::pack2(accTV[t][e + 2], accTV[t][e + 3])};
+      }
+  }
+}
+
+template <typename T, int MASK, bool CAUSAL, bool POW2>
+__global__ __launch_bounds__(kBThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  bwd_dkv_body<T, MASK, CAUSAL, POW2>(a);
+#endif
+}
+
+// ------------------------------------------------------------------ launch
+
+template <typename T, int MASK, bool CAUSAL, bool POW2>
+hipError_t launch_tiles(BwdArgs a, hipStream_t s) {
+  const int64_t nkb = (a.Nk + kBBlk - 1) / kBBlk, nqb = (a.Nq + kBBlk - 1) / kBBlk;
+  if (nkb * a.BH > INT32_MAX || nqb * a.BH > INT32_MAX) return hipErrorInvalidValue;
+  if (nkb > 0 && a.BH > 0) {
+    BwdArgs ak = a;
+    ak.n_blk = static_cast<int>(nkb);
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, MASK, CAUSAL, POW2>), dim3(unsigned(nkb * a.BH)), dim3(kBThreads), 0, s,
+                       ak);
+  }
+  if (nqb > 0 && a.BH > 0) {
+    BwdArgs aq = a;
+    aq.n_blk = static_cast<int>(nqb);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, MASK, CAUSAL, POW2>), dim3(unsigned(nqb * a.BH)), dim3(kBThreads), 0, s,
+                       aq);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int MASK>
+hipError_t launch_mask(const BwdArgs& a, bool causal, bool pow2, hipStream_t s) {
+  if constexpr (std::is_same_v<T, BF16>) {   // the scale fold is exact only in bfloat16
+    if (pow2) return causal ? launch_tiles<T, MASK, true, true>(a, s) : launch_tiles<T, MASK, false, true>(a, s);
+  }
+  return causal ? launch_tiles<T, MASK, true, false>(a, s) : launch_tiles<T, MASK, false, false>(a, s);
+}
+
+template <typename T>
+hipError_t launch_type(const BwdArgs& a, int mask_kind, bool causal, bool pow2, hipStream_t s) {
+  switch (mask_kind) {
+    case JVPATTN_MASK_NONE: return launch_mask<T, JVPATTN_MASK_NONE>(a, causal, pow2, s);
+    case JVPATTN_MASK_BOOL: return launch_mask<T, JVPATTN_MASK_BOOL>(a, causal, pow2, s);
+    default: return launch_mask<T, JVPATTN_MASK_ADDITIVE>(a, causal, pow2, s);
+  }
+}
+
+}  // namespace
+}  // namespace jvpattn
+
+extern "C" int jvpattn_bwd(const jvpattn_params* p, const void* q, const void* k, const void* v,
+                           const void* tq, const void* tk, const void* tv, const void* mask, const void* o,
+                           const void* to, const float* lse, const float* tlse, const void* go,
+                           const void* gto, void* dq, void* dk, void* dv, void* dtq, void* dtk, void* dtv,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace jvpattn;
+  FwdSizes sz;
+  const int rc = check_bwd(p, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk, dtv,
+                           workspace, workspace_bytes, &sz);
+  if (rc != JVPATTN_OK) return rc;
+  if (sz.rows_q == 0 && sz.rows_k == 0) return JVPATTN_OK;
+
+  BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv; a.mask = mask;
+  a.o = o; a.to = to; a.go = go; a.gto = gto; a.lse = lse; a.tlse = tlse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dtq = dtq; a.dtk = dtk; a.dtv = dtv;
+  a.ws = static_cast<float*>(workspace);
+  a.ws_stride = bwd_workspace_bytes(sz.rows_q) / 16;   // bytes of one array / 4
+  a.H = p->H; a.Nq = p->Nq; a.Nk = p->Nk; a.BH = p->B * p->H;
+  a.n_blk = 0;
+  a.msb = p->mask_stride_b; a.msh = p->mask_stride_h; a.msq = p->mask_stride_q;
+  a.scale = p->scale;
+  a.mask_vec = 0;
+  {
+    const int mes = p->mask_kind == JVPATTN_MASK_BOOL ? 1 : elem_bytes(p->dtype);
+    const uintptr_t base = reinterpret_cast<uintptr_t>(mask);
+    a.mask_vec = mask && (p->mask_stride_b % 4 == 0) && (p->mask_stride_h % 4 == 0) &&
+                 (p->mask_stride_q % 4 == 0) && (base % (4 * mes) == 0);
+  }
+  const bool additive = p->mask_kind == JVPATTN_MASK_ADDITIVE;
+  int sexp = 0;
+  const bool pow2 = p->dtype == JVPATTN_BF16 && std::frexp(p->scale, &sexp) == 0.5f;
+  a.cx = (additive || pow2) ? kLog2e : p->scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (sz.rows_q > 0) {
+    const int64_t nb = (sz.rows_q + kBThreads - 1) / kBThreads;
+    if (nb > INT32_MAX) return JVPATTN_ERR_SHAPE;
+    if (p->dtype == JVPATTN_BF16)
+      hipLaunchKernelGGL((bwd_rows_kernel<BF16>), dim3(unsigned(nb)), dim3(kBThreads), 0, s, a, sz.rows_q);
+    else
+      hipLaunchKernelGGL((bwd_rows_kernel<F16>), dim3(unsigned(nb)), dim3(kBThreads), 0, s, a, sz.rows_q);
+  }
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {
+    e = p->dtype == JVPATTN_BF16 ? launch_type<BF16>(a, p->mask_kind, p->causal != 0, pow2, s)
+                                 : launch_type<F16>(a, p->mask_kind, p->causal != 0, pow2, s);
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return JVPATTN_ERR_HIP;
+  }
+  return JVPATTN_OK;
+}

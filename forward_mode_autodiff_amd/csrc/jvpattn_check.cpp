@@ -137,7 +137,86 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
   return JVPATTN_OK;
 }
 
+thread_local int g_last_hip_error = 0;
+
+int64_t bwd_workspace_bytes(int64_t rows_q) {
+  // four float32 arrays of rows_q entries, each starting on a 256-byte boundary
+  const int64_t per = (rows_q * 4 + 255) / 256 * 256;
+  return 4 * per;
+}
+
+int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void* v,
+              const void* tq, const void* tk, const void* tv, const void* mask,
+              const void* o, const void* to, const float* lse, const float* tlse,
+              const void* go, const void* gto, const void* dq, const void* dk, const void* dv,
+              const void* dtq, const void* dtk, const void* dtv, const void* workspace,
+              size_t workspace_bytes, FwdSizes* sizes) {
+  FwdSizes sz;
+  // The arguments shared with the forward, checked as the forward checks them
+  // (o, to, lse, tlse in the role of its outputs: present, aligned, disjoint
+  // from q..mask).
+  int rc = check_fwd(p, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, &sz);
+  if (rc != JVPATTN_OK) return rc;
+  if (p->dtype != JVPATTN_F16 && p->dtype != JVPATTN_BF16) return JVPATTN_ERR_DTYPE;
+  if (p->d != 64) return JVPATTN_ERR_HEADDIM;
+  const bool rows = sz.rows_q > 0, keys = sz.rows_k > 0;
+  if (rows && (!tlse || !go || !gto || !dq || !dtq)) return JVPATTN_ERR_NULL;
+  if (keys && (!dk || !dv || !dtk || !dtv)) return JVPATTN_ERR_NULL;
+  const void* vecs[] = {go, gto, dq, dk, dv, dtq, dtk, dtv};
+  for (const void* t : vecs)
+    if (t && !aligned(t, 16)) return JVPATTN_ERR_ALIGN;
+  const int64_t need = bwd_workspace_bytes(sz.rows_q);
+  if (rows) {
+    if (!workspace || static_cast<int64_t>(workspace_bytes) < need || !aligned(workspace, 256))
+      return JVPATTN_ERR_WORKSPACE;
+  }
+  const int64_t bq = sz.rows_q * p->d * sz.elem_bytes, bk = sz.rows_k * p->d * sz.elem_bytes;
+  int64_t mask_bytes = 0;
+  if (mask && rows && keys) {
+    const int mes = p->mask_kind == JVPATTN_MASK_BOOL ? 1 : sz.elem_bytes;
+    mask_bytes = ((p->B - 1) * p->mask_stride_b + (p->H - 1) * p->mask_stride_h +
+                  (p->Nq - 1) * p->mask_stride_q + p->Nk) * mes;   // check_fwd proved this fits
+  }
+  const Span ins[] = {span(q, bq),  span(k, bk),   span(v, bk),   span(tq, bq),    span(tk, bk),
+                      span(tv, bk), span(mask, mask_bytes), span(o, bq), span(to, bq),
+                      span(lse, sz.rows_q * 4), span(tlse, sz.rows_q * 4), span(go, bq), span(gto, bq)};
+  const Span outs[] = {span(dq, rows ? bq : 0),  span(dk, bk),  span(dv, bk),
+                       span(dtq, rows ? bq : 0), span(dtk, bk), span(dtv, bk)};
+  const Span ws = span(rows ? workspace : nullptr, rows ? need : 0);
+  for (int i = 0; i < 6; ++i) {
+    for (const Span& in : ins)
+      if (overlap(outs[i], in)) return JVPATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(outs[i], outs[j])) return JVPATTN_ERR_ALIAS;
+    if (overlap(outs[i], ws)) return JVPATTN_ERR_WORKSPACE;
+  }
+  for (const Span& in : ins)
+    if (overlap(ws, in)) return JVPATTN_ERR_WORKSPACE;
+  if (sizes) *sizes = sz;
+  return JVPATTN_OK;
+}
+
 }  // namespace jvpattn
+
+extern "C" int jvpattn_last_hip_error(void) { return jvpattn::g_last_hip_error; }
+
+extern "C" int64_t jvpattn_bwd_workspace_bytes(const jvpattn_params* p) {
+  if (!p) return JVPATTN_ERR_NULL;
+  if (p->B < 0 || p->H < 0 || p->Nq < 0) return JVPATTN_ERR_SHAPE;
+  int64_t bh = int64_t(p->B) * p->H;
+  if (p->Nq > 0 && bh > INT64_MAX / 4 / p->Nq) return JVPATTN_ERR_SHAPE;
+  return jvpattn::bwd_workspace_bytes(bh * p->Nq);
+}
+
+extern "C" int jvpattn_check_bwd(const jvpattn_params* params, const void* q, const void* k,
+                                 const void* v, const void* tq, const void* tk, const void* tv,
+                                 const void* mask, const void* o, const void* to, const float* lse,
+                                 const float* tlse, const void* go, const void* gto, const void* dq,
+                                 const void* dk, const void* dv, const void* dtq, const void* dtk,
+                                 const void* dtv, const void* workspace, size_t workspace_bytes) {
+  return jvpattn::check_bwd(params, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, go, gto, dq, dk, dv,
+                            dtq, dtk, dtv, workspace, workspace_bytes, nullptr);
+}
 
 extern "C" int jvpattn_check_fwd(const jvpattn_params* params, const void* q, const void* k,
                                  const void* v, const void* tq, const void* tk, const void* tv,
@@ -158,6 +237,7 @@ extern "C" const char* jvpattn_strerror(int code) {
     case JVPATTN_ERR_SCALE: return "scale must be finite and > 0";
     case JVPATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case JVPATTN_ERR_HIP: return "HIP runtime error on launch";
+    case JVPATTN_ERR_WORKSPACE: return "workspace missing, too small, not 256-byte aligned, or overlapping";
     default: return "unknown error code";
   }
 }

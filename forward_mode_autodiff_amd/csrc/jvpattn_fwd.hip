@@ -34,23 +34,16 @@
 
 #include "jvpattn.h"
 #include "jvpattn_internal.h"
+#include "jvpattn_device.h"
 
 namespace jvpattn {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kWaves = 4;             // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;      // query rows per workgroup
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+static_assert(kThreads == kTileThreads, "LDS tiles are laid out for the 4-wave kernels");
 
 struct FwdArgs {
   const void* q;
@@ -73,168 +66,6 @@ struct FwdArgs {
   float thr;          // lazy-rescale threshold in score units
 };
 
-// Maximum of three values in one instruction (no NaN canonicalisation of the
-// matrix-core results the way a chain of fmaxf would need).
-__device__ inline float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// ---------------------------------------------------------------- 16-bit types
-
-struct BF16 {
-  using vec8 = bf16x8;
-  static constexpr float kTau = 8.0f;   // weights may grow to 2^8 before a rescale
-  __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  __device__ static inline uint32_t pack2(float a, float b) {
-    f32x2 f = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
-  }
-  __device__ static inline float widen(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
-  // acc + the two 16-bit values of w
-  __device__ static inline float dot2sum(uint32_t w, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u),
-                                           acc, false);
-  }
-  // Weights must be rebased when a lane's 16 weights sum past 2^12 (so each is
-  // at most 2^12; bfloat16 and the float32 sums have range to spare).
-  __device__ static inline bool spill(float lane_sum, const float (&)[16]) { return !(lane_sum <= 4096.0f); }
-};
-
-struct F16 {
-  using vec8 = f16x8;
-  // float16 weights times score tangents must stay below 65504: keep weights <= 2^4.
-  static constexpr float kTau = 4.0f;
-  __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  __device__ static inline uint32_t pack2(float a, float b) {
-    f32x2 f = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
-  }
-  __device__ static inline float widen(uint16_t x) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, x));
-  }
-  __device__ static inline float dot2sum(uint32_t w, float acc) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
-  }
-  // Weights must be rebased when a lane's 16 weights sum past 2^6, so each
-  // is at most 2^6 and the float16 products with score tangents below 2^10 in
-  // magnitude stay finite.
-  __device__ static inline bool spill(float lane_sum, const float (&)[16]) { return !(lane_sum <= 64.0f); }
-};
-
-__device__ inline uint32_t lo16(uint32_t x) { return x & 0xffffu; }
-__device__ inline uint32_t hi16(uint32_t x) { return x >> 16; }
-
-// Buffer resources: loads at byte offsets >= the record count return zero, so
-// ragged tails and absent (NULL) tangents need no branches.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr int kRsrcWord3 = 0x00020000;
-
-__device__ inline Rsrc make_rsrc(const void* p, int64_t bytes) {
-  const int64_t n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(n), kRsrcWord3);
-}
-__device__ inline uint4 ld128(Rsrc r, int off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ inline uint2 ld64(Rsrc r, int off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-
-// Values of lanes l and l^32 combined (both halves receive the result).
-__device__ inline float xhalf_max(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ inline float xhalf_sum(float x) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-template <typename V, typename P>
-__device__ inline V lds_load(const P* base, int off) {
-  return *reinterpret_cast<const V*>(reinterpret_cast<const char*>(base) + off);
-}
-template <typename V, typename P>
-__device__ inline void lds_store(P* base, int off, V x) {
-  *reinterpret_cast<V*>(reinterpret_cast<char*>(base) + off) = x;
-}
-
-template <int D>
-struct Tile16 {
-  static constexpr int BN = 32;                   // keys per LDS tile (one 32-key block)
-  static constexpr int NC = D / 16;               // 16-wide chunks of the head dimension
-  static constexpr int NT = D / 32;               // 32-row tiles of the output
-  static constexpr int GR = D / 8;                // 16-byte granules per row
-  static constexpr int ROW = 2 * D;               // bytes per row
-  static constexpr int TENSOR_BYTES = BN * ROW;
-  static constexpr int STAGE_BYTES = 4 * TENSOR_BYTES;          // K, dK, V, dV
-  static constexpr int LOADS = TENSOR_BYTES / (16 * kThreads);  // 16-byte loads per thread per tensor
-  static constexpr int TILE_VMEM = 4 * LOADS;                   // direct loads per thread per tile
-  static_assert(LOADS * 16 * kThreads == TENSOR_BYTES, "tile must split evenly over the workgroup");
-};
-
-// LDS tiles (K, dK, V, dV) are row = key, 2*D bytes per row, with the 16-byte
-// granules of a row XOR-swizzled by swz(row). They are filled by direct
-// global->LDS loads: load slot p (16 bytes) of a tile lands at byte 16*p,
-// i.e. at (row, physical granule) = (p / GR, p % GR), so the lane that owns
-// slot p fetches logical granule (p % GR) ^ swz(row) of that row.
-#ifndef JVPATTN_SWZ
-#define JVPATTN_SWZ 1
-#endif
-__device__ inline int swz(int row) {
-#if JVPATTN_SWZ == 0
-  return row & 7;
-#elif JVPATTN_SWZ == 1
-  // 8 consecutive rows -> 8 distinct granules (K reads), and 4 consecutive rows
-  // -> 4 distinct granule pairs (transpose reads of 2 adjacent granules).
-  return ((row & 3) << 1) | ((row >> 2) & 1);
-#else
-  return (row >> 1) & 7;
-#endif
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-__device__ inline lds_char* to_lds(const char* p) { return (lds_char*)(p); }
-
-// 4 keys x 16 head-dim columns -> each of 16 lanes gets one column: the LDS
-// transpose read of gfx950. In every group of 16 lanes, lane i returns
-// element (i % 4) of the 8 bytes addressed by lane 4*e + i/4, for e = 0..3.
-__device__ inline v4i16 lds_read_tr(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)to_lds(p));
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N == 0 || N == 2 || N == 4 || N == 6 || N == 8 || N == 12 || N == 16, "unsupported count");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-}
-
-// Workgroup barrier for the LDS ring. The caller has already waited for its
-// own direct-to-LDS loads (wait_vmcnt); this waits for its LDS reads and
-// syncs. (A fenced __syncthreads would also drain every in-flight tile load.)
-// Builtins rather than inline assembly, so the compiler's own wait
-// insertion knows that LDS reads issued before the barrier have completed.
-__device__ inline void ring_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt, expcnt unconstrained
-  __builtin_amdgcn_s_barrier();
-}
-
 // Per-row softmax state for one lane (both lanes of a query column hold the same m).
 struct RowState {
   float m;       // reference maximum in score units (-inf until a visible key is seen)
@@ -243,80 +74,6 @@ struct RowState {
   float mu;      // partial sum of weights * score tangent (in the units of sd)
 };
 
-// Mask values of one 32-key block for this lane's 16 keys, loaded ahead of use.
-template <int MASK> struct MaskVals {};
-template <> struct MaskVals<JVPATTN_MASK_BOOL> { uint32_t w[4]; };
-template <> struct MaskVals<JVPATTN_MASK_ADDITIVE> { uint2 w[4]; };
-
-// Register r of this lane holds key k0 + 8*(r/4) + 4*hlf + r%4.
-template <int MASK>
-__device__ inline void mask_load(MaskVals<MASK>& m, const FwdArgs& a, Rsrc mr, int qi, int k0, int hlf) {
-  if constexpr (MASK == JVPATTN_MASK_BOOL || MASK == JVPATTN_MASK_ADDITIVE) {
-    constexpr int es = MASK == JVPATTN_MASK_BOOL ? 1 : 2;
-    // byte offset of (qi, k0 + 4*hlf) in this head's mask; rows past Nq are never stored
-    const int row = (qi * int(a.msq) + k0 + 4 * hlf) * es;
-    const bool vec = a.mask_vec && k0 + 32 <= a.Nk;
-    if constexpr (MASK == JVPATTN_MASK_BOOL) {
-      if (vec) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) m.w[g] = __builtin_amdgcn_raw_buffer_load_b32(mr, row + 8 * g, 0, 0);
-      } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          m.w[g] = 0u;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            m.w[g] |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(mr, row + 8 * g + e, 0, 0)) << (8 * e);
-        }
-      }
-    } else {
-      if (vec) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) m.w[g] = ld64(mr, row + 16 * g);
-      } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint32_t e4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) e4[e] = __builtin_amdgcn_raw_buffer_load_b16(mr, row + 16 * g + 2 * e, 0, 0);
-          m.w[g].x = e4[0] | (e4[1] << 16);
-          m.w[g].y = e4[2] | (e4[3] << 16);
-        }
-      }
-    }
-  }
-}
-
-// Scores in score units: raw q.k without an additive mask (scale folded into
-// cx), scale q.k + M with one. PRESCALED: s already holds scale q.k.
-template <typename T, int MASK, bool PRESCALED>
-__device__ inline void mask_apply(f32x16& s, const MaskVals<MASK>& m, float scale) {
-  if constexpr (MASK == JVPATTN_MASK_BOOL) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (((m.w[r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u) s[r] = -INFINITY;
-  } else if constexpr (MASK == JVPATTN_MASK_ADDITIVE) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint2 x = m.w[r >> 2];
-      const uint32_t word = (r & 2) ? x.y : x.x;
-      const uint16_t bits = (r & 1) ? hi16(word) : lo16(word);
-      s[r] = PRESCALED ? s[r] + T::widen(bits) : fmaf(s[r], scale, T::widen(bits));
-    }
-  }
-}
-
-// Keys past Nk, and (causal) keys after the query, get score -inf.
-template <bool CAUSAL>
-__device__ inline void hide_keys(f32x16& s, int Nk, int qi, int k0, int hlf) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = k0 + (r >> 2) * 8 + 4 * hlf + (r & 3);
-    bool hide = key >= Nk;
-    if constexpr (CAUSAL) hide = hide || key > qi;
-    if (hide) s[r] = -INFINITY;
-  }
-}
 
 template <typename T, int MASK, bool CAUSAL, bool PRESCALED>
 __device__ inline void mask_scores(f32x16& s, const FwdArgs& a, Rsrc mr, int qi, int k0, int hlf,
@@ -325,24 +82,6 @@ __device__ inline void mask_scores(f32x16& s, const FwdArgs& a, Rsrc mr, int qi,
   mask_load<MASK>(m, a, mr, qi, k0, hlf);
   mask_apply<T, MASK, PRESCALED>(s, m, a.scale);
   if (elem_mask) hide_keys<CAUSAL>(s, a.Nk, qi, k0, hlf);
-}
-
-// Mask resource of head (b, h): element (i, j) at byte (i*msq + j) * es.
-__device__ inline Rsrc mask_rsrc(const FwdArgs& a, int b, int h, int es) {
-  if (!a.mask) return make_rsrc(a.q, 0);
-  const int64_t base = (b * a.msb + h * a.msh) * es;
-  const int64_t bytes = (int64_t(a.Nq - 1) * a.msq + a.Nk) * es;
-  return make_rsrc(static_cast<const char*>(a.mask) + base, bytes);
-}
-
-// Largest score of this lane's query column (both lane halves).
-__device__ inline float block_max(const f32x16& s) {
-  float m = max3(s[0], s[1], s[2]);
-#pragma unroll
-  for (int r = 3; r < 15; r += 2) m = max3(m, s[r], s[r + 1]);
-  m = max3(m, s[15], s[15]);
-  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-  return max3(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[1]));
 }
 
 // Move the reference maximum when some row of the wave saw a score more than
@@ -376,100 +115,6 @@ __device__ inline void exp_block(f32x16& s, f32x16& sd, RowState& st, float cx) 
     m1 += sd[r + 2] + sd[r + 3];
   }
   st.l += l0 + l1;
-  st.mu += m0 + m1;
-}
-
-// Sum of 16 values as a balanced tree (independent adds, depth 4).
-__device__ inline float sum16(const float (&x)[16]) {
-  float a[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = x[2 * i] + x[2 * i + 1];
-  const float b0 = a[0] + a[1], b1 = a[2] + a[3], b2 = a[4] + a[5], b3 = a[6] + a[7];
-  return (b0 + b1) + (b2 + b3);
-}
-
-// Online softmax of one 32-key block for the 16-bit kernels, without a row
-// maximum in the common case. The weights are first taken against the
-// current reference, e = 2^(s cx - moff). A reference only has to keep the
-// weights bounded (every accumulator is rescaled with it), so the block is
-// accepted when this lane's 16 weights sum to at most T::kSpill, which bounds
-// each of them. Otherwise -- or while the row has seen no visible key -- the
-// whole wave takes the rare path: exact block maximum over both lane halves,
-// raise the reference to it, rescale l and mu (alpha returned for the
-// accumulators), recompute the weights. A reference set this way is always a
-// score of the row, so weights of later keys far below it may underflow to 0
-// only where they are negligible against that key's weight of 1.
-//
-// s holds the scores on entry (score units) and is clobbered; sd the score
-// tangents (times us gives dS). Outputs: pB = e, uB = e dS as 16-bit B
-// operands for keys 16kc .. 16kc+15.
-struct RowState16 {
-  float moff;    // reference in log2 units; 0 until a visible key is seen
-  float l;       // this lane's partial sum of weights
-  float mu;      // this lane's partial sum of weights * dS
-  bool seen;     // some visible key has set the reference
-};
-
-// Step 1: weights e of the block (s is clobbered), l updated; returns true
-// (and alpha for the accumulators) when the reference moved.
-template <typename T>
-__device__ inline bool block_exp16(f32x16& s, RowState16& st, float cx, float (&e)[16], float& alpha) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], cx, -st.moff);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(s[r]);
-  float lt = sum16(e);
-  alpha = 1.0f;
-  const bool moved = __any(T::spill(lt, e) || !st.seen);
-  if (moved) {
-    const float bx = block_max(s);   // max over the query column of s cx - moff
-    // Raise the reference only (alpha <= 1); an unseen row takes the block's
-    // maximum as it is, unless every key so far is hidden (bx = -inf).
-    const float shift = st.seen ? fmaxf(bx, 0.0f) : (bx > -INFINITY ? bx : 0.0f);
-    alpha = __builtin_amdgcn_exp2f(-shift);
-    st.seen = st.seen || bx > -INFINITY;
-    st.moff += shift;
-    st.l *= alpha;
-    st.mu *= alpha;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(s[r] - shift);
-    lt = sum16(e);
-  }
-  st.l += lt;
-  return moved;
-}
-
-// Step 2: pB = e and uB = e dS (dS = sd, times us when SCALED_U) as 16-bit B
-// operands for keys 16kc .. 16kc+15.
-template <typename T, bool SCALED_U>
-__device__ inline void block_pack16(const float (&e)[16], const f32x16& sd, float us,
-                                    typename T::vec8 (&pB)[2], typename T::vec8 (&uB)[2]) {
-  uint32_t pw[8], uw[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    pw[i] = T::pack2(e[2 * i], e[2 * i + 1]);
-    const float u0 = SCALED_U ? (sd[2 * i] * us) * e[2 * i] : sd[2 * i] * e[2 * i];
-    const float u1 = SCALED_U ? (sd[2 * i + 1] * us) * e[2 * i + 1] : sd[2 * i + 1] * e[2 * i + 1];
-    uw[i] = T::pack2(u0, u1);
-  }
-#pragma unroll
-  for (int kc = 0; kc < 2; ++kc) {
-    pB[kc] = __builtin_bit_cast(typename T::vec8, uint4{pw[4 * kc], pw[4 * kc + 1], pw[4 * kc + 2], pw[4 * kc + 3]});
-    uB[kc] = __builtin_bit_cast(typename T::vec8, uint4{uw[4 * kc], uw[4 * kc + 1], uw[4 * kc + 2], uw[4 * kc + 3]});
-  }
-}
-
-// mu += the 16 rounded products held in uB (the values the value products use).
-template <typename T>
-__device__ inline void block_mu16(const typename T::vec8 (&uB)[2], RowState16& st) {
-  const uint4 a = __builtin_bit_cast(uint4, uB[0]), b = __builtin_bit_cast(uint4, uB[1]);
-  float m0 = T::dot2sum(a.x, 0.0f), m1 = T::dot2sum(b.x, 0.0f);
-  m0 = T::dot2sum(a.y, m0);
-  m1 = T::dot2sum(b.y, m1);
-  m0 = T::dot2sum(a.z, m0);
-  m1 = T::dot2sum(b.z, m1);
-  m0 = T::dot2sum(a.w, m0);
-  m1 = T::dot2sum(b.w, m1);
   st.mu += m0 + m1;
 }
 
@@ -1374,8 +1019,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd32_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------- dispatch
 
-thread_local int g_last_hip_error = 0;
-
 template <int MASK, bool CAUSAL>
 hipError_t launch_pp(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
   const dim3 block(kPPThreads);
@@ -1419,8 +1062,6 @@ hipError_t launch_typed(int dtype, int d, bool pow2, const FwdArgs& args, dim3 g
 
 }  // namespace
 }  // namespace jvpattn
-
-extern "C" int jvpattn_last_hip_error(void) { return jvpattn::g_last_hip_error; }
 
 extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k, const void* v,
                            const void* tq, const void* tk, const void* tv, const void* mask, void* o,

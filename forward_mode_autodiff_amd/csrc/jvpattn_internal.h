@@ -1,6 +1,7 @@
 // Declarations shared by the validator and the launcher (host code only).
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 
 #include "jvpattn.h"
@@ -20,5 +21,20 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
               const void* tq, const void* tk, const void* tv, const void* mask,
               const void* o, const void* to, const float* lse, const float* tlse,
               FwdSizes* sizes);
+
+// Full argument check of jvpattn_bwd (the forward's checks on the shared
+// arguments, then its own); fills `sizes` on success (may be NULL).
+int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void* v,
+              const void* tq, const void* tk, const void* tv, const void* mask,
+              const void* o, const void* to, const float* lse, const float* tlse,
+              const void* go, const void* gto, const void* dq, const void* dk, const void* dv,
+              const void* dtq, const void* dtk, const void* dtv, const void* workspace,
+              size_t workspace_bytes, FwdSizes* sizes);
+
+// HIP error of the most recent JVPATTN_ERR_HIP on this thread (jvpattn_last_hip_error).
+extern thread_local int g_last_hip_error;
+
+// Workspace of jvpattn_bwd: four float32 arrays of B*H*Nq (see jvpattn_bwd.hip).
+int64_t bwd_workspace_bytes(int64_t rows_q);
 
 }  // namespace jvpattn

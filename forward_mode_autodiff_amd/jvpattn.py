@@ -21,7 +21,7 @@ JVPATTN_MASK_NONE, JVPATTN_MASK_BOOL, JVPATTN_MASK_ADDITIVE = 0, 1, 2
 ERRORS = {
     0: "JVPATTN_OK", -1: "JVPATTN_ERR_NULL", -2: "JVPATTN_ERR_SHAPE", -3: "JVPATTN_ERR_DTYPE",
     -4: "JVPATTN_ERR_HEADDIM", -5: "JVPATTN_ERR_MASK", -6: "JVPATTN_ERR_ALIGN", -7: "JVPATTN_ERR_SCALE",
-    -8: "JVPATTN_ERR_ALIAS", -9: "JVPATTN_ERR_HIP",
+    -8: "JVPATTN_ERR_ALIAS", -9: "JVPATTN_ERR_HIP", -10: "JVPATTN_ERR_WORKSPACE",
 }
 _DTYPE_CODE = {torch.float32: JVPATTN_F32, torch.float16: JVPATTN_F16, torch.bfloat16: JVPATTN_BF16}
 
@@ -64,6 +64,12 @@ def load_library(path: str = LIB_PATH):
     lib.jvpattn_strerror.restype = ctypes.c_char_p
     lib.jvpattn_last_hip_error.argtypes = []
     lib.jvpattn_last_hip_error.restype = ctypes.c_int
+    lib.jvpattn_bwd_workspace_bytes.argtypes = [P]
+    lib.jvpattn_bwd_workspace_bytes.restype = ctypes.c_int64
+    lib.jvpattn_check_bwd.argtypes = [P] + [vp] * 20 + [ctypes.c_size_t]
+    lib.jvpattn_check_bwd.restype = ctypes.c_int
+    lib.jvpattn_bwd.argtypes = [P] + [vp] * 20 + [ctypes.c_size_t, vp]
+    lib.jvpattn_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -158,3 +164,56 @@ def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, sca
             msg += f" (hipError {lib.jvpattn_last_hip_error()})"
         raise JvpattnError(rc, msg)
     return o, to, lse, tlse
+
+
+def jvpattn_bwd_workspace_bytes(params: jvpattn_params) -> int:
+    return int(load_library().jvpattn_bwd_workspace_bytes(ctypes.byref(params)))
+
+
+def jvpattn_check_bwd(params: jvpattn_params, *ptrs, workspace_bytes: int = 0) -> int:
+    """Host-only validation of a jvpattn_bwd call; ptrs are the 20 pointer arguments (integers or None)."""
+    return load_library().jvpattn_check_bwd(ctypes.byref(params), *ptrs, workspace_bytes)
+
+
+def jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, go, gto, mask=None, causal=False, scale=None,
+                out=None, workspace=None):
+    """dq, dk, dv, dtq, dtk, dtv = jvpattn_bwd(...): cotangents of q, k, v, tq, tk, tv.
+
+    For L = <go, O> + <gto, dO> with (O, dO, lse, tlse) = jvpattn_fwd(q, k, v, tq, tk, tv, mask, causal,
+    scale). Shapes and dtypes as for jvpattn_fwd; go, gto like q. ``out`` optionally supplies the six
+    output tensors, ``workspace`` a uint8 device tensor of at least jvpattn_bwd_workspace_bytes bytes.
+    Work is queued on torch's current stream.
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("tq", tq), ("tk", tk), ("tv", tv), ("o", o), ("to", to),
+                    ("go", go), ("gto", gto)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    p, mask = make_params(q, k, mask, causal, scale)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dtq, dtk, dtv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv, dtq, dtk, dtv = out
+    need = lib.jvpattn_bwd_workspace_bytes(ctypes.byref(p))
+    if need < 0:
+        raise JvpattnError(int(need), jvpattn_strerror(int(need)))
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.jvpattn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv), _ptr(mask),
+                         _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse), _ptr(go), _ptr(gto),
+                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtq), _ptr(dtk), _ptr(dtv),
+                         _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
+    if rc != 0:
+        msg = jvpattn_strerror(rc)
+        if rc == -9:
+            msg += f" (hipError {lib.jvpattn_last_hip_error()})"
+        raise JvpattnError(rc, msg)
+    return dq, dk, dv, dtq, dtk, dtv

@@ -69,7 +69,8 @@ enum {
   JVPATTN_ERR_ALIGN = -6,    /* a tensor pointer not 16-byte aligned (lse/tlse: 4-byte) */
   JVPATTN_ERR_SCALE = -7,    /* scale not finite or not > 0 */
   JVPATTN_ERR_ALIAS = -8,    /* an output overlaps an input or another output */
-  JVPATTN_ERR_HIP = -9       /* the HIP runtime reported an error on launch */
+  JVPATTN_ERR_HIP = -9,      /* the HIP runtime reported an error on launch */
+  JVPATTN_ERR_WORKSPACE = -10  /* jvpattn_bwd: workspace NULL, too small, misaligned, or overlapping */
 };
 
 typedef struct {
@@ -117,6 +118,62 @@ int jvpattn_fwd(const jvpattn_params* params,
                 const void* tq, const void* tk, const void* tv,
                 const void* mask,
                 void* o, void* to, float* lse, float* tlse,
+                void* stream);
+
+/* ------------------------------------------------------------ reverse pass
+ *
+ * The pullback of the pair (O, dO) that jvpattn_fwd returns: reverse mode
+ * taken over the forward-mode pass, which is how the "JVP Flash Attention"
+ * README (section "Description") reaches Hessian-vector products. With
+ * cotangents go of O and gto of dO, i.e. for L = <go, O> + <gto, dO>, it
+ * returns
+ *   dq, dk, dv    = dL/dq, dL/dk, dL/dv
+ *   dtq, dtk, dtv = dL/dtq, dL/dtk, dL/dtv   (the cotangents of the tangents)
+ * The additive mask is a constant: no gradient is returned for it.
+ *
+ *   params, q, k, v, tq, tk, tv, mask : exactly as given to jvpattn_fwd
+ *   o, to, lse, tlse : what jvpattn_fwd returned for them (all four required)
+ *   go, gto          : [B, H, Nq, d], the element type
+ *   dq, dtq          : [B, H, Nq, d] outputs; dk, dv, dtk, dtv: [B, H, Nk, d]
+ *   workspace        : device memory of at least
+ *                      jvpattn_bwd_workspace_bytes(params) bytes, 256-byte
+ *                      aligned, owned by the caller; contents on entry are
+ *                      ignored and overwritten (per-row statistics). Calls
+ *                      that may run at the same time need separate
+ *                      workspaces.
+ * Outputs are fully overwritten and must not overlap an input, each other
+ * or the workspace. Supported: float16 and bfloat16 with d = 64 (other
+ * element types return JVPATTN_ERR_DTYPE, other d JVPATTN_ERR_HEADDIM,
+ * before any work is queued). Arithmetic: products on the matrix cores with
+ * float32 accumulation; the recomputed softmax weights, their tangents and
+ * the score cotangents are rounded to the input type before the products
+ * that consume them; results are rounded to nearest even. */
+
+/* Bytes of workspace jvpattn_bwd needs for these parameters, or a negative
+ * JVPATTN_ERR_* code if the parameters are invalid for it. */
+int64_t jvpattn_bwd_workspace_bytes(const jvpattn_params* params);
+
+/* Host-only validation of a jvpattn_bwd call (pointers compared, never
+ * dereferenced); returns JVPATTN_OK or the code jvpattn_bwd would return. */
+int jvpattn_check_bwd(const jvpattn_params* params,
+                      const void* q, const void* k, const void* v,
+                      const void* tq, const void* tk, const void* tv,
+                      const void* mask,
+                      const void* o, const void* to, const float* lse, const float* tlse,
+                      const void* go, const void* gto,
+                      const void* dq, const void* dk, const void* dv,
+                      const void* dtq, const void* dtk, const void* dtv,
+                      const void* workspace, size_t workspace_bytes);
+
+int jvpattn_bwd(const jvpattn_params* params,
+                const void* q, const void* k, const void* v,
+                const void* tq, const void* tk, const void* tv,
+                const void* mask,
+                const void* o, const void* to, const float* lse, const float* tlse,
+                const void* go, const void* gto,
+                void* dq, void* dk, void* dv,
+                void* dtq, void* dtk, void* dtv,
+                void* workspace, size_t workspace_bytes,
                 void* stream);
 
 /* A static, human-readable description of a return code. */

@@ -23,7 +23,8 @@ def declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["jvpattn_check_fwd", "jvpattn_fwd", "jvpattn_last_hip_error",
+    assert declared_functions() == ["jvpattn_bwd", "jvpattn_bwd_workspace_bytes", "jvpattn_check_bwd",
+                                    "jvpattn_check_fwd", "jvpattn_fwd", "jvpattn_last_hip_error",
                                     "jvpattn_strerror"]
 
 
@@ -174,6 +175,99 @@ def test_check_rejects(case, code):
     assert call(p, P, **over) == code
 
 
+BWD_PTRS = ("q", "k", "v", "tq", "tk", "tv", "mask", "o", "to", "lse", "tlse", "go", "gto",
+            "dq", "dk", "dv", "dtq", "dtk", "dtv", "ws")
+
+
+def bwd_ptrs(p, es=2):
+    """Forward pointers plus cotangents, outputs and a workspace (fake, disjoint, aligned)."""
+    P = ptrs(p, es)
+    nq = p.B * p.H * p.Nq * p.d * es
+    nk = p.B * p.H * p.Nk * p.d * es
+    base = max(P.values()) + (1 << 30)
+    for name, n in (("go", nq), ("gto", nq), ("dq", nq), ("dk", nk), ("dv", nk), ("dtq", nq), ("dtk", nk),
+                    ("dtv", nk), ("ws", 1 << 20)):
+        P[name] = base
+        base += (n + 4096) // 256 * 256 + 256
+    return P
+
+
+def call_bwd(p, P, ws_bytes=None, **over):
+    a = dict(P)
+    a.update(over)
+    if p.mask_kind == 0 and "mask" not in over:
+        a["mask"] = None
+    if ws_bytes is None:
+        ws_bytes = max(J.jvpattn_bwd_workspace_bytes(p), 0)
+    return J.jvpattn_check_bwd(p, *[a[n] for n in BWD_PTRS], workspace_bytes=ws_bytes)
+
+
+@needs_lib
+def test_bwd_workspace_size():
+    p = good_params()
+    n = J.jvpattn_bwd_workspace_bytes(p)
+    rows = p.B * p.H * p.Nq
+    assert n >= 4 * 4 * rows and n % 256 == 0
+    assert J.jvpattn_bwd_workspace_bytes(good_params(B=-1)) == -2
+    assert J.jvpattn_bwd_workspace_bytes(good_params(Nq=0)) == 0
+
+
+@needs_lib
+def test_check_bwd_accepts_valid_calls():
+    for dt in (J.JVPATTN_F16, J.JVPATTN_BF16):
+        p = good_params(dtype=dt)
+        assert call_bwd(p, bwd_ptrs(p)) == 0
+        assert call_bwd(p, bwd_ptrs(p), tq=None, tk=None, tv=None) == 0
+    p = good_params(mask_kind=J.JVPATTN_MASK_BOOL, mask_stride_b=100 * 90, mask_stride_q=90, causal=1)
+    assert call_bwd(p, bwd_ptrs(p)) == 0
+    # no query rows: keys still get (zero) gradients; no workspace is needed
+    p = good_params(Nq=0)
+    P = bwd_ptrs(p)
+    assert call_bwd(p, P, q=None, o=None, to=None, lse=None, tlse=None, go=None, gto=None, dq=None, dtq=None,
+                    ws=None, ws_bytes=0) == 0
+
+
+@needs_lib
+@pytest.mark.parametrize("case,code", [
+    ("f32", -3), ("d128", -4), ("go_null", -1), ("tlse_null", -1), ("dv_null", -1), ("dq_misaligned", -6),
+    ("ws_null", -10), ("ws_small", -10), ("ws_misaligned", -10), ("ws_overlaps_go", -10), ("ws_overlaps_dk", -10),
+    ("dq_is_q", -8), ("dk_overlaps_dv", -8), ("dtv_overlaps_gto", -8), ("q_null", -1), ("scale_nan", -7),
+])
+def test_check_bwd_rejects(case, code):
+    p = good_params()
+    if case == "f32":
+        p.dtype = J.JVPATTN_F32
+        assert call_bwd(p, bwd_ptrs(p, 4)) == code
+        return
+    if case == "d128":
+        p.d = 128
+        assert call_bwd(p, bwd_ptrs(p)) == code
+        return
+    P = bwd_ptrs(p)
+    over, wsb = {}, None
+    if case.endswith("_null"):
+        over[case[:-5]] = None
+    elif case == "dq_misaligned":
+        over["dq"] = P["dq"] + 8
+    elif case == "ws_small":
+        wsb = J.jvpattn_bwd_workspace_bytes(p) - 4
+    elif case == "ws_misaligned":
+        over["ws"] = P["ws"] + 128
+    elif case == "ws_overlaps_go":
+        over["ws"] = P["go"]
+    elif case == "ws_overlaps_dk":
+        over["ws"] = P["dk"]
+    elif case == "dq_is_q":
+        over["dq"] = P["q"]
+    elif case == "dk_overlaps_dv":
+        over["dk"] = P["dv"] + 512
+    elif case == "dtv_overlaps_gto":
+        over["dtv"] = P["gto"]
+    elif case == "scale_nan":
+        p.scale = float("nan")
+    assert call_bwd(p, P, ws_bytes=wsb, **over) == code
+
+
 @pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
 def test_validator_under_host_sanitizers(tmp_path):
     """The validator is plain C++: build it with g++ and ASan/UBSan and run a driver over edge cases."""
@@ -197,6 +291,20 @@ int main() {
   p.B = 2; p.H = 2; p.Nq = 33; p.mask_kind = JVPATTN_MASK_BOOL; p.mask_stride_b = INT64_MAX;
   bad += jvpattn_check_fwd(&p, at(0), at(1), at(2), at(3), at(4), at(5), at(10), at(6), at(7),
                            (float*)at(8), (float*)at(9)) != JVPATTN_ERR_MASK;
+  {
+    jvpattn_params b = p;
+    b.mask_kind = JVPATTN_MASK_NONE; b.mask_stride_b = 0;
+    const int64_t ws = jvpattn_bwd_workspace_bytes(&b);
+    bad += ws <= 0;
+    bad += jvpattn_check_bwd(&b, at(0), at(1), at(2), at(3), at(4), at(5), nullptr, at(6), at(7), (float*)at(8),
+                             (float*)at(9), at(11), at(12), at(13), at(14), at(15), at(16), at(17), at(18),
+                             at(19), size_t(ws)) != JVPATTN_OK;
+    bad += jvpattn_check_bwd(&b, at(0), at(1), at(2), at(3), at(4), at(5), nullptr, at(6), at(7), (float*)at(8),
+                             (float*)at(9), at(11), at(12), at(13), at(14), at(15), at(16), at(17), at(18),
+                             at(19), size_t(ws) - 1) != JVPATTN_ERR_WORKSPACE;
+    b.B = 2147483647; b.H = 2147483647; b.Nq = 2147483647;
+    bad += jvpattn_bwd_workspace_bytes(&b) != JVPATTN_ERR_SHAPE;
+  }
   p.mask_stride_b = 0; p.scale = NAN;
   bad += jvpattn_check_fwd(&p, at(0), at(1), at(2), at(3), at(4), at(5), at(10), at(6), at(7),
                            (float*)at(8), (float*)at(9)) != JVPATTN_ERR_SCALE;
