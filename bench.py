@@ -6,7 +6,9 @@ A step is one jvpattn_fwd call (scores, score tangents, online softmax with
 tangent, the value products, epilogue, lse/tlse) over one batch of synthetic
 inputs already resident in HBM. The default workload is B=4, H=16, N=2048,
 d=64, bfloat16, causal. Throughput counts 12*N^2*d flops per head (half when
-causal). Prints one JSON line.
+causal). A workload name with the suffix "_bwd" (e.g. hvp_bwd) times one
+jvpattn_bwd call instead (the reverse pass for the same inputs and N(0,1)
+cotangents), counting 30*N^2*d flops per head. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -19,6 +21,7 @@ import time
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # MI355X dense matrix peak per dtype
 HBM_GBS = 8000.0
 METRIC = "JVP-attention fwd TFLOP/s (12·N²·d/head) and % MFMA peak, N=2048 d=64 bf16"
+METRIC_BWD = "JVP-attention reverse pass TFLOP/s (30·N²·d/head) and % MFMA peak, N=2048 d=64 bf16"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -71,6 +74,31 @@ def measured_traffic(workload):
     return int(float(fields["traffic_bytes_per_launch"]))
 
 
+def cpu_baseline_bwd(w, x, budget_s=12.0):
+    """Time the float64 reverse-pass oracle on whole heads of the same workload for ~budget_s."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import bwd_flop_count, oracle_bwd
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b, h = heads[done % len(heads)]
+        f64 = lambda t: t[b:b + 1, h:h + 1].double().numpy()
+        mask = None
+        if x["mask"] is not None:
+            mask = x["mask"][b:b + 1, :1].double().numpy() if w.mask_kind == "additive" else \
+                x["mask"][b:b + 1, :1].numpy()
+        oracle_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["tq"]), f64(x["tk"]), f64(x["tv"]),
+                   f64(x["do"]), f64(x["dto"]), mask=mask, mask_kind=w.mask_kind, causal=w.causal)
+        done += 1
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": bwd_flop_count(1, done, w.N, w.nk, w.d, w.causal) / dt / 1e12, "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{done} head evaluations (of {len(heads)} heads) of the same workload's reverse pass, "
+                      f"float64 numpy, {dt:.1f} s"}
+
+
 def cpu_baseline(w, x, budget_s=12.0):
     """Time the float64 oracle on whole heads of the same workload (cycling over the heads) for ~budget_s."""
     import numpy as np
@@ -97,6 +125,24 @@ def cpu_baseline(w, x, budget_s=12.0):
                       f"query rows each, float64 numpy, {dt:.1f} s"}
 
 
+def bwd_step_setup(w, x, dev):
+    """Device inputs, forward outputs and output buffers for timing jvpattn_bwd."""
+    import torch
+
+    from forward_mode_autodiff_amd.jvpattn import jvpattn_bwd, jvpattn_bwd_workspace_bytes, jvpattn_fwd, make_params
+    d = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+    o, to, lse, tlse = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=d["mask"],
+                                   causal=w.causal)
+    outs = tuple(torch.empty_like(d[n]) for n in ("q", "k", "v", "q", "k", "v"))
+    params, _ = make_params(d["q"], d["k"], d["mask"], w.causal)
+    ws = torch.empty(max(jvpattn_bwd_workspace_bytes(params), 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        jvpattn_bwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], o, to, lse, tlse, d["do"], d["dto"],
+                    mask=d["mask"], causal=w.causal, out=outs, workspace=ws)
+    return step
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,8 +165,9 @@ def main():
     from forward_mode_autodiff_amd import inputs as I
     from forward_mode_autodiff_amd.jvpattn import jvpattn_fwd, load_library
     load_library()
-    w = workloads()[args.workload]
-    x = I.make_inputs(w)
+    reverse = args.workload.endswith("_bwd")
+    w = workloads()[args.workload[:-4] if reverse else args.workload]
+    x = I.make_inputs(w, cotangents=reverse)
     dev = "cuda:0"
     d = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
     o = torch.empty_like(d["q"])
@@ -132,6 +179,9 @@ def main():
     def step():
         jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=d["mask"], causal=w.causal,
                     out=out)
+
+    if reverse:
+        step = bwd_step_setup(w, x, dev)
 
     for _ in range(args.warmup):
         step()
@@ -152,14 +202,15 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     avg_launch_ms = total_ms / args.steps
 
-    from oracle import flop_count  # the counting convention only; the oracle's arithmetic is not run here
-    flops = flop_count(w.B, w.H, w.N, w.nk, w.d, w.causal)
+    # the counting conventions only; the oracle's arithmetic is not run here
+    from oracle import bwd_flop_count, flop_count
+    flops = (bwd_flop_count if reverse else flop_count)(w.B, w.H, w.N, w.nk, w.d, w.causal)
     ms_per_step = total_ms / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     rec = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if reverse else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -171,12 +222,13 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "mask": w.mask_kind, "input_std": round(w.sigma, 6)},
+        "config": {"workload": w.name + ("_bwd" if reverse else ""), "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "mask": w.mask_kind, "input_std": round(w.sigma, 6)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload)},
+                     "frac": round(achieved / peak, 4),
+                     "traffic": None if reverse else measured_traffic(args.workload)},
         "launch_us": round(avg_launch_ms * 1e3, 2),
-        "algorithmic_GBps": round(algorithmic_bytes(w) / (avg_launch_ms * 1e-3) / 1e9, 1),
+        "algorithmic_GBps": None if reverse else round(algorithmic_bytes(w) / (avg_launch_ms * 1e-3) / 1e9, 1),
         "wall_s": round(wall, 4),
     }
     if args.copy_calibration:
@@ -187,7 +239,7 @@ def main():
         torch.cuda.synchronize()
         rec["copy_calibration_bytes"] = 256 << 20
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, x)
+        rec["cpu_baseline"] = cpu_baseline_bwd(w, x) if reverse else cpu_baseline(w, x)
     print(json.dumps(rec), flush=True)
 
 
