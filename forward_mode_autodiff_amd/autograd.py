@@ -1,0 +1,117 @@
+"""PyTorch integration: attention whose derivatives, both modes, run in libjvpattn.
+
+The "JVP Flash Attention" README presents the method as a drop-in for
+``torch.nn.functional.scaled_dot_product_attention`` (section "Usage": q, k,
+v, attn_mask; no dropout) that supports forward-mode derivatives, with a
+``fwd_dual`` entry for dual inputs, and Hessian-vector products (section
+"Description"). This module gives both entries on top of the C ABI; every
+computation is a libjvpattn call (jvpattn_fwd, jvpattn_bwd) and torch only
+supplies tensors, the autograd graph and streams.
+
+``attention(q, k, v, attn_mask=None, is_causal=False, scale=None)``
+    the output O. Reverse mode (``.backward()``, ``torch.autograd.grad``)
+    runs jvpattn_bwd with a zero cotangent for the tangent output; forward
+    mode with ``torch.autograd.forward_ad`` dual tensors runs jvpattn_fwd
+    with the tangents. (``torch.func`` transforms hand the rules tensors
+    without storage, which a library call cannot read: use ``fwd_dual`` for
+    the JVP instead of ``torch.func.jvp``.)
+
+``fwd_dual(q, k, v, tq, tk, tv, attn_mask=None, is_causal=False, scale=None)``
+    the pair (O, dO) -- the output and its JVP -- differentiable in reverse
+    mode with respect to all six inputs (jvpattn_bwd). A Hessian-vector
+    product of a loss is reverse mode over this pair.
+
+Inputs: [B, H, N, d] CUDA tensors of one dtype (float16 / bfloat16 for the
+reverse pass, which supports d = 64; the forward also takes float32 and
+d = 128). Masks as in ``jvpattn_fwd`` (bool: True = attend; additive: q's
+dtype, no gradient).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import jvpattn as J
+
+
+def _c(t):
+    return None if t is None else t.contiguous()
+
+
+class _Const:
+    """Holds the mask outside the autograd/functorch view: it is a constant of the map."""
+
+    def __init__(self, t):
+        self.t = t
+
+
+class _Attention(torch.autograd.Function):
+    """O = attention(q, k, v); lse rides along (not differentiable)."""
+
+    @staticmethod
+    def forward(q, k, v, mask, causal, scale):
+        o, to, lse, tlse = J.jvpattn_fwd(q, k, v, None, None, None, mask=mask.t, causal=causal, scale=scale)
+        return o, lse, to, tlse
+
+    @staticmethod
+    def setup_context(ctx, inputs, output):
+        q, k, v, mask, causal, scale = inputs
+        o, lse, to, tlse = output
+        ctx.save_for_backward(q, k, v, o, lse, to, tlse)
+        ctx.save_for_forward(q, k, v)
+        ctx.mask, ctx.causal, ctx.scale = mask.t, causal, scale
+        ctx.mark_non_differentiable(lse, to, tlse)
+
+    @staticmethod
+    def backward(ctx, go, _glse, _gto, _gtlse):
+        q, k, v, o, lse, to, tlse = ctx.saved_tensors
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), None, None, None)
+        dq, dk, dv, _, _, _ = J.jvpattn_bwd(q, k, v, None, None, None, o, to, lse, tlse, _c(go), None,
+                                            mask=ctx.mask, causal=ctx.causal, scale=ctx.scale, out=out)
+        return dq, dk, dv, None, None, None
+
+    @staticmethod
+    def jvp(ctx, tq, tk, tv, _tmask, _tcausal, _tscale):
+        q, k, v = ctx.saved_tensors   # in jvp: the tensors given to save_for_forward
+        o, to, lse, tlse = J.jvpattn_fwd(q, k, v, _c(tq), _c(tk), _c(tv), mask=ctx.mask, causal=ctx.causal,
+                                         scale=ctx.scale)
+        return to, None, None, None   # lse and the aux outputs are not differentiable
+
+
+class _AttentionDual(torch.autograd.Function):
+    """(O, dO) = fwd_dual(q, k, v, tq, tk, tv); lse and tlse ride along (not differentiable)."""
+
+    @staticmethod
+    def forward(q, k, v, tq, tk, tv, mask, causal, scale):
+        return J.jvpattn_fwd(q, k, v, tq, tk, tv, mask=mask.t, causal=causal, scale=scale)
+
+    @staticmethod
+    def setup_context(ctx, inputs, output):
+        q, k, v, tq, tk, tv, mask, causal, scale = inputs
+        o, to, lse, tlse = output
+        ctx.save_for_backward(q, k, v, tq, tk, tv, o, to, lse, tlse)
+        ctx.mask, ctx.causal, ctx.scale = mask.t, causal, scale
+        ctx.mark_non_differentiable(lse, tlse)
+
+    @staticmethod
+    def backward(ctx, go, gto, _glse, _gtlse):
+        q, k, v, tq, tk, tv, o, to, lse, tlse = ctx.saved_tensors
+        need = ctx.needs_input_grad
+        # outputs for the cotangents of tq, tk, tv only where they are wanted (NULL: not computed)
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+               torch.empty_like(q) if need[3] else None, torch.empty_like(k) if need[4] else None,
+               torch.empty_like(v) if need[5] else None)
+        g = J.jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, _c(go), _c(gto), mask=ctx.mask,
+                          causal=ctx.causal, scale=ctx.scale, out=out)
+        return tuple(x if need[i] else None for i, x in enumerate(g)) + (None, None, None)
+
+
+def attention(q, k, v, attn_mask=None, is_causal=False, scale=None):
+    """Scaled-dot-product attention (no dropout) with both derivative modes in libjvpattn."""
+    return _Attention.apply(q, k, v, _Const(attn_mask), bool(is_causal), scale)[0]
+
+
+def fwd_dual(q, k, v, tq, tk, tv, attn_mask=None, is_causal=False, scale=None):
+    """(O, dO): attention and its JVP along (tq, tk, tv); reverse-differentiable in all six inputs."""
+    o, to, _, _ = _AttentionDual.apply(q, k, v, _c(tq), _c(tk), _c(tv), _Const(attn_mask), bool(is_causal),
+                                       scale)
+    return o, to

@@ -81,12 +81,14 @@ __device__ __forceinline__ void bwd_rows_body(const BwdArgs& a, int64_t rows) {
   if (row >= rows) return;
   const uint4* o = static_cast<const uint4*>(a.o) + row * 8;
   const uint4* to = static_cast<const uint4*>(a.to) + row * 8;
-  const uint4* g = static_cast<const uint4*>(a.go) + row * 8;
-  const uint4* gd = static_cast<const uint4*>(a.gto) + row * 8;
+  // a NULL cotangent is zero
+  const uint4* g = a.go ? static_cast<const uint4*>(a.go) + row * 8 : nullptr;
+  const uint4* gd = a.gto ? static_cast<const uint4*>(a.gto) + row * 8 : nullptr;
   float r = 0.0f, go_o = 0.0f, gd_to = 0.0f;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const uint4 wo = o[c], wto = to[c], wg = g[c], wgd = gd[c];
+    const uint4 wo = o[c], wto = to[c];
+    const uint4 wg = g ? g[c] : uint4{0, 0, 0, 0}, wgd = gd ? gd[c] : uint4{0, 0, 0, 0};
     const uint32_t xo[4] = {wo.x, wo.y, wo.z, wo.w}, xto[4] = {wto.x, wto.y, wto.z, wto.w};
     const uint32_t xg[4] = {wg.x, wg.y, wg.z, wg.w}, xgd[4] = {wgd.x, wgd.y, wgd.z, wgd.w};
 #pragma unroll
@@ -180,7 +182,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   {
     const Rsrc rq = make_rsrc(at(a.q, qhead), qbytes);
     const Rsrc rtq = make_rsrc(a.tq ? at(a.tq, qhead) : at(a.q, qhead), a.tq ? qbytes : 0);
-    const Rsrc rg = make_rsrc(at(a.go, qhead), qbytes), rtg = make_rsrc(at(a.gto, qhead), qbytes);
+    const Rsrc rg = make_rsrc(a.go ? at(a.go, qhead) : at(a.q, qhead), a.go ? qbytes : 0);
+    const Rsrc rtg = make_rsrc(a.gto ? at(a.gto, qhead) : at(a.q, qhead), a.gto ? qbytes : 0);
 #pragma unroll
     for (int c = 0; c < L::NC; ++c) {
       const int off = qi * L::ROW + (hlf * (D / 2) + 8 * c) * 2;
@@ -363,8 +366,9 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
         const f32x16& B = accTQ[t];
         *reinterpret_cast<uint2*>(dq + dd) =
             uint2{T::pack2(A[4 * g] * a.scale, A[4 * g + 1] * a.scale), T::pack2(A[4 * g + 2] * a.scale, A[4 * g + 3] * a.scale)};
-        *reinterpret_cast<uint2*>(dtq + dd) =
-            uint2{T::pack2(B[4 * g] * a.scale, B[4 * g + 1] * a.scale), T::pack2(B[4 * g + 2] * a.scale, B[4 * g + 3] * a.scale)};
+        if (a.dtq)
+          *reinterpret_cast<uint2*>(dtq + dd) = uint2{T::pack2(B[4 * g] * a.scale, B[4 * g + 1] * a.scale),
+                                                      T::pack2(B[4 * g + 2] * a.scale, B[4 * g + 3] * a.scale)};
       }
   }
 }
@@ -471,7 +475,8 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
   }
   const Rsrc rq = make_rsrc(at(a.q, qhead), qbytes);
   const Rsrc rtq = make_rsrc(a.tq ? at(a.tq, qhead) : at(a.q, qhead), a.tq ? qbytes : 0);
-  const Rsrc rg = make_rsrc(at(a.go, qhead), qbytes), rtg = make_rsrc(at(a.gto, qhead), qbytes);
+  const Rsrc rg = make_rsrc(a.go ? at(a.go, qhead) : at(a.q, qhead), a.go ? qbytes : 0);
+  const Rsrc rtg = make_rsrc(a.gto ? at(a.gto, qhead) : at(a.q, qhead), a.gto ? qbytes : 0);
   // Statistics of this head's rows: wave w loads statistic w of the tile (8 lanes x 16 bytes).
   const int64_t srow = int64_t(bh) * a.Nq;
   const Rsrc rstat = make_rsrc(a.ws + wave * a.ws_stride + srow, int64_t(a.Nq) * 4);
@@ -672,12 +677,14 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
         const int e = 4 * g;
         *reinterpret_cast<uint2*>(dk + dd) = uint2{T::pack2(accK[t][e] * sc, accK[t][e + 1] * sc),
                                                    T::pack2(accK[t][e + 2] * sc, accK[t][e + 3] * sc)};
-        *reinterpret_cast<uint2*>(dtk + dd) = uint2{T::pack2(accTK[t][e] * sc, accTK[t][e + 1] * sc),
-                                                    T::pack2(accTK[t][e + 2] * sc, accTK[t][e + 3] * sc)};
+        if (a.dtk)
+          *reinterpret_cast<uint2*>(dtk + dd) = uint2{T::pack2(accTK[t][e] * sc, accTK[t][e + 1] * sc),
+                                                      T::pack2(accTK[t][e + 2] * sc, accTK[t][e + 3] * sc)};
         *reinterpret_cast<uint2*>(dv + dd) =
             uint2{T::pack2(accV[t][e], accV[t][e + 1]), T::pack2(accV[t][e + 2], accV[t][e + 3])};
-        *reinterpret_cast<uint2*>(dtv + dd) =
-            uint2{T::pack2(accTV[t][e], accTV[t][e + 1]), T::pack2(accTV[t][e + 2], accTV[t][e + 3])};
+        if (a.dtv)
+          *reinterpret_cast<uint2*>(dtv + dd) =
+              uint2{T::pack2(accTV[t][e], accTV[t][e + 1]), T::pack2(accTV[t][e + 2], accTV[t][e + 3])};
       }
   }
 }

@@ -160,8 +160,9 @@ int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void*
   if (p->dtype != JVPATTN_F16 && p->dtype != JVPATTN_BF16) return JVPATTN_ERR_DTYPE;
   if (p->d != 64) return JVPATTN_ERR_HEADDIM;
   const bool rows = sz.rows_q > 0, keys = sz.rows_k > 0;
-  if (rows && (!tlse || !go || !gto || !dq || !dtq)) return JVPATTN_ERR_NULL;
-  if (keys && (!dk || !dv || !dtk || !dtv)) return JVPATTN_ERR_NULL;
+  // go, gto may be NULL (zero cotangent); dtq, dtk, dtv may be NULL (not written)
+  if (rows && (!tlse || !dq)) return JVPATTN_ERR_NULL;
+  if (keys && (!dk || !dv)) return JVPATTN_ERR_NULL;
   const void* vecs[] = {go, gto, dq, dk, dv, dtq, dtk, dtv};
   for (const void* t : vecs)
     if (t && !aligned(t, 16)) return JVPATTN_ERR_ALIGN;
@@ -180,8 +181,8 @@ int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void*
   const Span ins[] = {span(q, bq),  span(k, bk),   span(v, bk),   span(tq, bq),    span(tk, bk),
                       span(tv, bk), span(mask, mask_bytes), span(o, bq), span(to, bq),
                       span(lse, sz.rows_q * 4), span(tlse, sz.rows_q * 4), span(go, bq), span(gto, bq)};
-  const Span outs[] = {span(dq, rows ? bq : 0),  span(dk, bk),  span(dv, bk),
-                       span(dtq, rows ? bq : 0), span(dtk, bk), span(dtv, bk)};
+  const Span outs[] = {span(dq, rows ? bq : 0),  span(dk, keys ? bk : 0),  span(dv, keys ? bk : 0),
+                       span(dtq, rows ? bq : 0), span(dtk, keys ? bk : 0), span(dtv, keys ? bk : 0)};
   const Span ws = span(rows ? workspace : nullptr, rows ? need : 0);
   for (int i = 0; i < 6; ++i) {
     for (const Span& in : ins)

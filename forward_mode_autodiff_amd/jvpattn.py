@@ -180,9 +180,10 @@ def jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, go, gto, mask=None, causa
     """dq, dk, dv, dtq, dtk, dtv = jvpattn_bwd(...): cotangents of q, k, v, tq, tk, tv.
 
     For L = <go, O> + <gto, dO> with (O, dO, lse, tlse) = jvpattn_fwd(q, k, v, tq, tk, tv, mask, causal,
-    scale). Shapes and dtypes as for jvpattn_fwd; go, gto like q. ``out`` optionally supplies the six
-    output tensors, ``workspace`` a uint8 device tensor of at least jvpattn_bwd_workspace_bytes bytes.
-    Work is queued on torch's current stream.
+    scale). Shapes and dtypes as for jvpattn_fwd; go, gto like q, either may be None (zero). ``out``
+    optionally supplies the six output tensors (dtq, dtk, dtv may be None: not computed);
+    ``workspace`` a uint8 device tensor of at least jvpattn_bwd_workspace_bytes bytes. Work is queued
+    on torch's current stream.
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("tq", tq), ("tk", tk), ("tv", tv), ("o", o), ("to", to),

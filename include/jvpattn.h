@@ -133,8 +133,11 @@ int jvpattn_fwd(const jvpattn_params* params,
  *
  *   params, q, k, v, tq, tk, tv, mask : exactly as given to jvpattn_fwd
  *   o, to, lse, tlse : what jvpattn_fwd returned for them (all four required)
- *   go, gto          : [B, H, Nq, d], the element type
- *   dq, dtq          : [B, H, Nq, d] outputs; dk, dv, dtk, dtv: [B, H, Nk, d]
+ *   go, gto          : [B, H, Nq, d], the element type; either may be NULL,
+ *                      meaning a zero cotangent
+ *   dq, dtq          : [B, H, Nq, d] outputs; dk, dv, dtk, dtv: [B, H, Nk, d];
+ *                      dtq, dtk, dtv may be NULL (not written), e.g. for the
+ *                      plain attention backward with gto = NULL
  *   workspace        : device memory of at least
  *                      jvpattn_bwd_workspace_bytes(params) bytes, 256-byte
  *                      aligned, owned by the caller; contents on entry are

@@ -218,6 +218,8 @@ def test_check_bwd_accepts_valid_calls():
         p = good_params(dtype=dt)
         assert call_bwd(p, bwd_ptrs(p)) == 0
         assert call_bwd(p, bwd_ptrs(p), tq=None, tk=None, tv=None) == 0
+        # zero cotangents and unwanted tangent cotangents may be NULL
+        assert call_bwd(p, bwd_ptrs(p), go=None, gto=None, dtq=None, dtk=None, dtv=None) == 0
     p = good_params(mask_kind=J.JVPATTN_MASK_BOOL, mask_stride_b=100 * 90, mask_stride_q=90, causal=1)
     assert call_bwd(p, bwd_ptrs(p)) == 0
     # no query rows: keys still get (zero) gradients; no workspace is needed
@@ -229,7 +231,7 @@ def test_check_bwd_accepts_valid_calls():
 
 @needs_lib
 @pytest.mark.parametrize("case,code", [
-    ("f32", -3), ("d128", -4), ("go_null", -1), ("tlse_null", -1), ("dv_null", -1), ("dq_misaligned", -6),
+    ("f32", -3), ("d128", -4), ("dq_null", -1), ("tlse_null", -1), ("dv_null", -1), ("dq_misaligned", -6),
     ("ws_null", -10), ("ws_small", -10), ("ws_misaligned", -10), ("ws_overlaps_go", -10), ("ws_overlaps_dk", -10),
     ("dq_is_q", -8), ("dk_overlaps_dv", -8), ("dtv_overlaps_gto", -8), ("q_null", -1), ("scale_nan", -7),
 ])

@@ -1,0 +1,104 @@
+"""The PyTorch integration routes every derivative to the right library call (CPU, no GPU).
+
+``forward_mode_autodiff_amd.autograd`` only marshals: these tests swap the two
+library entry points for the float64 oracle and check that reverse mode,
+forward mode (torch.func.jvp and forward_ad dual tensors) and reverse mode
+over the dual pair return what the oracle says, in the right places.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.autograd.forward_ad as fwAD
+
+import forward_mode_autodiff_amd.autograd as A
+from forward_mode_autodiff_amd import jvpattn as J
+from oracle import oracle_bwd, oracle_fwd
+
+
+def _np(t):
+    return None if t is None else t.detach().double().numpy()
+
+
+def fake_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, scale=None, want_tlse=True, out=None):
+    kind = "none" if mask is None else ("bool" if mask.dtype == torch.bool else "additive")
+    m = None if mask is None else (mask.numpy().astype(np.uint8) if kind == "bool" else _np(mask))
+    o, to, lse, tlse = oracle_fwd(_np(q), _np(k), _np(v), _np(tq), _np(tk), _np(tv), mask=m, mask_kind=kind,
+                                  causal=causal, scale=scale)
+    T = lambda a: torch.from_numpy(a).to(q.dtype)
+    return T(o), T(to), torch.from_numpy(lse).float(), torch.from_numpy(tlse).float()
+
+
+def fake_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, go, gto, mask=None, causal=False, scale=None, out=None,
+             workspace=None):
+    kind = "none" if mask is None else ("bool" if mask.dtype == torch.bool else "additive")
+    m = None if mask is None else (mask.numpy().astype(np.uint8) if kind == "bool" else _np(mask))
+    z = lambda t: np.zeros(q.shape) if t is None else _np(t)
+    g = oracle_bwd(_np(q), _np(k), _np(v), _np(tq), _np(tk), _np(tv), z(go), z(gto), mask=m, mask_kind=kind,
+                   causal=causal, scale=scale)
+    res = [torch.from_numpy(a).to(q.dtype) for a in g]
+    if out is not None:
+        res = [None if slot is None else r for r, slot in zip(res, out)]
+    return tuple(res)
+
+
+@pytest.fixture(autouse=True)
+def fake_library(monkeypatch):
+    monkeypatch.setattr(J, "jvpattn_fwd", fake_fwd)
+    monkeypatch.setattr(J, "jvpattn_bwd", fake_bwd)
+
+
+def inputs(seed=0, B=1, H=2, N=7, d=4):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda: torch.randn(B, H, N, d, generator=g, dtype=torch.float64)
+    return [r() for _ in range(8)]   # q, k, v, tq, tk, tv, go, gto
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_reverse_mode_of_attention(causal):
+    q, k, v, tq, tk, tv, go, _ = inputs(1)
+    q, k, v = (t.requires_grad_(True) for t in (q, k, v))
+    o = A.attention(q, k, v, is_causal=causal)
+    o.backward(go)
+    ref = oracle_bwd(_np(q), _np(k), _np(v), None, None, None, _np(go), np.zeros(q.shape), causal=causal)
+    for t, r in zip((q, k, v), ref[:3]):
+        np.testing.assert_allclose(t.grad.numpy(), r, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o.detach().numpy(), oracle_fwd(_np(q), _np(k), _np(v), causal=causal)[0], atol=1e-12)
+
+
+def test_forward_mode_dual_tensors():
+    q, k, v, tq, tk, tv, _, _ = inputs(2)
+    mask = torch.rand(1, 1, 7, 7, generator=torch.Generator().manual_seed(3)) < 0.7
+    mask[..., 0] = True
+    ro, rto, _, _ = oracle_fwd(_np(q), _np(k), _np(v), _np(tq), _np(tk), _np(tv), mask=mask.numpy().astype(np.uint8),
+                               mask_kind="bool")
+    with fwAD.dual_level():
+        duals = [fwAD.make_dual(p, t) for p, t in ((q, tq), (k, tk), (v, tv))]
+        out = A.attention(*duals, attn_mask=mask)
+        p, t = fwAD.unpack_dual(out)
+    np.testing.assert_allclose(p.numpy(), ro, atol=1e-12)
+    np.testing.assert_allclose(t.numpy(), rto, atol=1e-12)
+
+
+def test_reverse_mode_over_the_dual_pair():
+    q, k, v, tq, tk, tv, go, gto = inputs(4)
+    ins = [t.requires_grad_(True) for t in (q, k, v, tq, tk, tv)]
+    o, to = A.fwd_dual(*ins, is_causal=True, scale=0.7)
+    grads = torch.autograd.grad((o * go).sum() + (to * gto).sum(), ins)
+    ref = oracle_bwd(*[_np(t) for t in ins], _np(go), _np(gto), causal=True, scale=0.7)
+    for g, r in zip(grads, ref):
+        np.testing.assert_allclose(g.numpy(), r, rtol=0, atol=1e-12)
+
+
+def test_hessian_vector_product_matches_finite_differences():
+    """d/de grad_q f(q + e u) for f = <c, attention(q, k, v)> equals reverse mode over fwd_dual along u."""
+    q, k, v, u, _, _, c, _ = inputs(5)
+    qq = q.clone().requires_grad_(True)
+    o, to = A.fwd_dual(qq, k, v, u, None, None)
+    # grad_q <c, dO> with dO = J u is the HVP of f along u
+    hvp, = torch.autograd.grad((to * c).sum(), [qq])
+
+    def grad_f(x):
+        return torch.from_numpy(oracle_bwd(_np(x), _np(k), _np(v), None, None, None, _np(c), np.zeros(x.shape))[0])
+    eps = 1e-6
+    fd = (grad_f(q + eps * u) - grad_f(q - eps * u)) / (2 * eps)
+    np.testing.assert_allclose(hvp.numpy(), fd.numpy(), rtol=0, atol=1e-7)

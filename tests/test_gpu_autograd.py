@@ -1,0 +1,85 @@
+"""The PyTorch entries on the GPU: attention() in reverse and forward mode, fwd_dual under autograd.
+
+Values must equal the direct library calls bit for bit (the entries only
+marshal), and match the float64 oracle to the parity bars.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.autograd.forward_ad as fwAD
+
+from forward_mode_autodiff_amd import inputs as I
+from forward_mode_autodiff_amd.autograd import attention, fwd_dual
+from forward_mode_autodiff_amd.jvpattn import jvpattn_bwd, jvpattn_fwd
+from oracle import oracle_bwd, oracle_fwd
+from tests.parity import assert_parity
+from tests.test_gpu_bwd import NAMES, RHO, term_magnitudes
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def setup(causal, mask_kind="none", seed=61):
+    w = I.Workload("ag", B=1, H=2, N=160, d=64, dtype="bf16", causal=causal, std=1.0, seed=seed,
+                   mask_kind=mask_kind, keep=0.7)
+    x = I.make_inputs(w, cotangents=True)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
+    if d["mask"] is not None and mask_kind == "bool":
+        d["mask"] = d["mask"].bool()
+    return w, x, d
+
+
+def f64(t):
+    return None if t is None else t.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_reverse_mode(causal):
+    w, x, d = setup(causal)
+    q, k, v = (d[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    o = attention(q, k, v, is_causal=causal)
+    o.backward(d["do"])
+    # the same library call made directly
+    o2, to2, lse2, tlse2 = jvpattn_fwd(d["q"], d["k"], d["v"], causal=causal)
+    g = jvpattn_bwd(d["q"], d["k"], d["v"], None, None, None, o2, to2, lse2, tlse2, d["do"], None, causal=causal)
+    assert torch.equal(o.detach(), o2)
+    for t, r in zip((q, k, v), g[:3]):
+        assert torch.equal(t.grad, r)
+    ref = oracle_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), None, None, None, f64(x["do"]),
+                     np.zeros(x["q"].shape), causal=causal)
+    xz = dict(x, dto=torch.zeros_like(x["dto"]))
+    M = term_magnitudes(xz, w, (), None)
+    for n, t, r in zip(("dq", "dk", "dv"), (q, k, v), ref[:3]):
+        err = float(np.max(np.abs(t.grad.double().cpu().numpy() - r)))
+        assert err <= RHO["bf16"] * M[n], (n, err, M[n])
+
+
+def test_attention_forward_mode_dual_tensors():
+    w, x, d = setup(False, mask_kind="bool")
+    with fwAD.dual_level():
+        duals = [fwAD.make_dual(d[p], d[t]) for p, t in (("q", "tq"), ("k", "tk"), ("v", "tv"))]
+        out = attention(*duals, attn_mask=d["mask"])
+        o, to = fwAD.unpack_dual(out)
+    o2, to2, _, _ = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=d["mask"])
+    assert torch.equal(o, o2) and torch.equal(to, to2)
+    ro, rto, _, _ = oracle_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["tq"]), f64(x["tk"]), f64(x["tv"]),
+                               mask=x["mask"].numpy(), mask_kind="bool")
+    assert_parity({"o": o.float().cpu(), "to": to.float().cpu()}, {"o": ro, "to": rto}, "bf16", "dual")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_dual_reverse_mode_is_the_hvp_route(causal):
+    w, x, d = setup(causal, seed=62)
+    ins = [d[n].clone().requires_grad_(True) for n in ("q", "k", "v", "tq", "tk", "tv")]
+    o, to = fwd_dual(*ins, is_causal=causal)
+    grads = torch.autograd.grad((o.float() * d["do"].float()).sum() + (to.float() * d["dto"].float()).sum(), ins)
+    o2, to2, lse2, tlse2 = jvpattn_fwd(*[d[n] for n in ("q", "k", "v", "tq", "tk", "tv")], causal=causal)
+    direct = jvpattn_bwd(*[d[n] for n in ("q", "k", "v", "tq", "tk", "tv")], o2, to2, lse2, tlse2, d["do"],
+                         d["dto"], causal=causal)
+    for a, b in zip(grads, direct):
+        assert torch.equal(a, b)
+    ref = oracle_bwd(*[f64(x[n]) for n in ("q", "k", "v", "tq", "tk", "tv", "do", "dto")], causal=causal)
+    M = term_magnitudes(x, w, ("tq", "tk", "tv"), None)
+    for n, a, r in zip(NAMES, grads, ref):
+        err = float(np.max(np.abs(a.double().cpu().numpy() - r)))
+        assert err <= RHO["bf16"] * M[n], (n, err, M[n])

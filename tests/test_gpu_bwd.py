@@ -220,3 +220,20 @@ def test_errors_raise():
     with pytest.raises(JvpattnError):   # workspace too small
         jvpattn_bwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], o, to, lse, tlse, d["do"], d["dto"],
                     workspace=ws)
+
+
+def test_null_cotangent_and_skipped_outputs():
+    """go = NULL is a zero cotangent; NULL dtq/dtk/dtv outputs are skipped, the others unchanged."""
+    w = W("nullg", N=130, causal=True, seed=51)
+    x = I.make_inputs(w, cotangents=True)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
+    o, to, lse, tlse = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], causal=True)
+    out = (torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]), None, None, None)
+    g = jvpattn_bwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], o, to, lse, tlse, None, d["dto"],
+                    causal=True, out=out)
+    full = jvpattn_bwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], o, to, lse, tlse,
+                       torch.zeros_like(d["do"]), d["dto"], causal=True)
+    torch.cuda.synchronize()
+    assert g[3] is None and g[4] is None and g[5] is None
+    for a, b in zip(g[:3], full[:3]):
+        assert torch.equal(a, b)
