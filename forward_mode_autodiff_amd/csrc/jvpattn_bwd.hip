@@ -282,45 +282,55 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
       }
   };
 
-  auto tile = [&](int k, const char* sb) {
+  // Score-side products of the tile at sb: S^T, dS^T (scores), X^T, D^T (value side).
+  struct SPh {
+    f32x16 s, sd, x, dm;
+  };
+  auto sphase = [&](const char* sb, SPh& o) {
     vec8 ka[L::NC], tka[L::NC];
     read_rows(sb, 0, ka);
     read_rows(sb, 1, tka);
-    f32x16 s = f32x16{}, sd = f32x16{}, x = f32x16{}, dm = f32x16{};
+    o.s = f32x16{};
+    o.sd = f32x16{};
+    o.x = f32x16{};
+    o.dm = f32x16{};
 #pragma unroll
     for (int c = 0; c < L::NC; ++c) {
-      s = T::mfma(ka[c], qB[c], s);
-      sd = T::mfma(tka[c], qB[c], sd);
-      sd = T::mfma(ka[c], tqB[c], sd);
+      o.s = T::mfma(ka[c], qB[c], o.s);
+      o.sd = T::mfma(tka[c], qB[c], o.sd);
+      o.sd = T::mfma(ka[c], tqB[c], o.sd);
     }
     vec8 va[L::NC], tva[L::NC];
     read_rows(sb, 2, va);
     read_rows(sb, 3, tva);
 #pragma unroll
     for (int c = 0; c < L::NC; ++c) {
-      x = T::mfma(va[c], gB[c], x);
-      x = T::mfma(tva[c], tgB[c], x);
-      dm = T::mfma(va[c], tgB[c], dm);
+      o.x = T::mfma(va[c], gB[c], o.x);
+      o.x = T::mfma(tva[c], tgB[c], o.x);
+      o.dm = T::mfma(va[c], tgB[c], o.dm);
     }
-    MaskVals<MASK> mk;
-    mask_load<MASK>(mk, a, mr, qi, k * 32, hlf);
-    mask_apply<T, MASK, POW2>(s, mk, a.scale);
-    if (needs_keymask(k)) hide_keys<CAUSAL>(s, a.Nk, qi, k * 32, hlf);
-    vec8 sB[2], sdB[2];
+  };
+  // Element-wise step of block k: score cotangents as 16-bit B operands.
+  auto vphase = [&](int k, SPh& p, const MaskVals<MASK>& mk, bool keymask, vec8 (&sB)[2], vec8 (&sdB)[2]) {
+    mask_apply<T, MASK, POW2>(p.s, mk, a.scale);
+    if (keymask) hide_keys<CAUSAL>(p.s, a.Nk, qi, k * 32, hlf);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       uint32_t w0[4], w1[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r0 = 8 * kc + 2 * i;
-        const Cot c0 = cotangents(s[r0], sd[r0], x[r0], dm[r0], a.cx, us, negl, tl, rr, del);
-        const Cot c1 = cotangents(s[r0 + 1], sd[r0 + 1], x[r0 + 1], dm[r0 + 1], a.cx, us, negl, tl, rr, del);
+        const Cot c0 = cotangents(p.s[r0], p.sd[r0], p.x[r0], p.dm[r0], a.cx, us, negl, tl, rr, del);
+        const Cot c1 = cotangents(p.s[r0 + 1], p.sd[r0 + 1], p.x[r0 + 1], p.dm[r0 + 1], a.cx, us, negl, tl, rr, del);
         w0[i] = T::pack2(c0.sbar, c1.sbar);
         w1[i] = T::pack2(c0.sdbar, c1.sdbar);
       }
       sB[kc] = __builtin_bit_cast(vec8, uint4{w0[0], w0[1], w0[2], w0[3]});
       sdB[kc] = __builtin_bit_cast(vec8, uint4{w1[0], w1[1], w1[2], w1[3]});
     }
+  };
+  // Accumulating products with K^T, dK^T of the tile at sb.
+  auto aphase = [&](const char* sb, const vec8 (&sB)[2], const vec8 (&sdB)[2]) {
     vec8 kt[L::NT][2], tkt[L::NT][2];
     read_tr(sb, 0, kt);
     read_tr(sb, 1, tkt);
@@ -334,24 +344,99 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
       }
   };
 
-  // Before step k's wait, tiles k and k+1 may be in flight (k+2 is issued after it).
-  auto wait_tile = [&](int j) {
-    if (j + 1 < n_tiles) wait_vmcnt<L::TILE_VMEM>();
+  // Blocks 1.. that need per-key masking start at jm: the causal diagonal, a
+  // ragged last tile, or the end of this wave's range.
+  int jm = last + 1;
+  if (CAUSAL) jm = min(jm, qw0 >> 5);
+  jm = min(jm, a.Nk >> 5);
+  jm = max(jm, 1);
+
+  // Pipelined block k (block k+1 needs no key mask): the score-side products
+  // of block k+1 run on the matrix cores while the vector units turn block k
+  // into cotangents; block k's accumulating products follow. Tiles are
+  // fetched three blocks ahead into a ring of 4.
+  auto fast = [&](int k, const char* cur, const char* nxt, char* dma, SPh& pc, SPh& pn, MaskVals<MASK>& mc,
+                  MaskVals<MASK>& mn) {
+    if (k + 2 < n_tiles) wait_vmcnt<L::TILE_VMEM>();   // tile k+1 (tile k+2 may stay in flight)
     else wait_vmcnt<0>();
+    ring_barrier();
+    mask_load<MASK>(mn, a, mr, qi, (k + 1) * 32, hlf);
+    if (k + 3 < n_tiles) issue_tile(k + 3, dma);
+    sphase(nxt, pn);
+    vec8 sB[2], sdB[2];
+    vphase(k, pc, mc, false, sB, sdB);
+    aphase(cur, sB, sdB);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * L::NC, 0);   // K / dK rows of block k+1
+#pragma unroll
+    for (int i = 0; i < 3 * L::NC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // score products
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);          // cotangents of block k
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * L::NC, 0);   // V / dV rows of block k+1
+#pragma unroll
+    for (int i = 0; i < 3 * L::NC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // value-side products
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);          // cotangents of block k
+    }
   };
+
+  // Prologue: tiles 0..2 in flight; wait for tile 0; block 0's score-side
+  // products if it needs no key mask.
   if (n_tiles > 0) issue_tile(0, stage0);
   if (n_tiles > 1) issue_tile(1, stage1);
-  auto step = [&](int k, const char* cur, char* dma) {
-    wait_tile(k);
-    ring_barrier();   // tile k visible; every wave is done with tile k-2 (stage of k+2)
-    if (k + 2 < n_tiles) issue_tile(k + 2, dma);
-    if (k <= last) tile(k, cur);
+  if (n_tiles > 2) issue_tile(2, stage2);
+  if (n_tiles > 2) wait_vmcnt<2 * L::TILE_VMEM>();
+  else if (n_tiles > 1) wait_vmcnt<L::TILE_VMEM>();
+  else wait_vmcnt<0>();
+  ring_barrier();
+  SPh pa, pb;
+  MaskVals<MASK> mka, mkb;
+  bool ready = false;   // pa holds the current block's score-side products
+  if (0 <= last && !needs_keymask(0)) {
+    sphase(stage0, pa);
+    mask_load<MASK>(mka, a, mr, qi, 0, hlf);
+    ready = true;
+  }
+  const int kfast = ready ? jm - 1 : 0;   // blocks 0 .. kfast-1 are pipelined
+  int k = 0;
+  for (; k + 4 <= kfast; k += 4) {
+    fast(k, stage0, stage1, stage3, pa, pb, mka, mkb);
+    fast(k + 1, stage1, stage2, stage0, pb, pa, mkb, mka);
+    fast(k + 2, stage2, stage3, stage1, pa, pb, mka, mkb);
+    fast(k + 3, stage3, stage0, stage2, pb, pa, mkb, mka);
+  }
+  if (k < kfast) {
+    fast(k, stage0, stage1, stage3, pa, pb, mka, mkb);
+    if (k + 1 < kfast) fast(k + 1, stage1, stage2, stage0, pb, pa, mkb, mka);
+    if (k + 2 < kfast) fast(k + 2, stage2, stage3, stage1, pa, pb, mka, mkb);
+  }
+  if (kfast & 1) {   // block kfast's products were left in pb
+    pa = pb;
+    mka = mkb;
+  }
+
+  // Remaining blocks (diagonal, ragged tail, barrier-only ones past this
+  // wave's rows), one at a time, stage chosen at run time.
+  auto stage_of = [&](int i) -> char* {
+    i &= 3;
+    return i == 0 ? stage0 : i == 1 ? stage1 : i == 2 ? stage2 : stage3;
   };
-  for (int k = 0; k < n_tiles; k += 4) {
-    step(k, stage0, stage2);
-    if (k + 1 < n_tiles) step(k + 1, stage1, stage3);
-    if (k + 2 < n_tiles) step(k + 2, stage2, stage0);
-    if (k + 3 < n_tiles) step(k + 3, stage3, stage1);
+  for (k = kfast; k < n_tiles; ++k) {
+    if (k + 2 < n_tiles) wait_vmcnt<2 * L::TILE_VMEM>();   // tile k (k+1, k+2 may stay in flight)
+    else if (k + 1 < n_tiles) wait_vmcnt<L::TILE_VMEM>();
+    else wait_vmcnt<0>();
+    ring_barrier();
+    if (k + 3 < n_tiles) issue_tile(k + 3, stage_of(k + 3));
+    if (k > last) continue;
+    const char* cur = stage_of(k);
+    if (!ready) {
+      sphase(cur, pa);
+      mask_load<MASK>(mka, a, mr, qi, k * 32, hlf);
+    }
+    vec8 sB[2], sdB[2];
+    vphase(k, pa, mka, needs_keymask(k), sB, sdB);
+    aphase(cur, sB, sdB);
+    ready = false;
   }
 
   if (qi < a.Nq) {
