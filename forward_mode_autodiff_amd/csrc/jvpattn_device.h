@@ -27,12 +27,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 
-// Maximum of three values in one instruction (no NaN canonicalisation of the
-// matrix-core results the way a chain of fmaxf would need).
+// Maximum of three values. IEEE maximum (NaN-propagating) fuses into one
+// v_maximum3_f32 with no NaN canonicalisation of matrix-core results, which a
+// chain of fmaxf would need. Written as a builtin, not asm, so the compiler
+// sees the read of matrix-core destinations and inserts the wait states
+// gfx950 requires before a vector instruction may read them (it does not look
+// inside inline asm: an asm reader could see a partial accumulation).
 __device__ inline float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 // ---------------------------------------------------------------- 16-bit types
@@ -332,9 +334,11 @@ __device__ inline bool block_exp16(f32x16& s, RowState16& st, float cx, float (&
   if (moved) {
     const float bx = block_max(s);   // max over the query column of s cx - moff
     // Raise the reference only (alpha <= 1); an unseen row takes the block's
-    // maximum as it is, unless every key so far is hidden (bx = -inf).
+    // maximum as it is (up or down), unless every key so far is hidden (bx = -inf).
     const float shift = st.seen ? fmaxf(bx, 0.0f) : (bx > -INFINITY ? bx : 0.0f);
-    alpha = __builtin_amdgcn_exp2f(-shift);
+    // An unseen row has accumulated nothing (all zeros); its shift may be far
+    // below 0, where exp2(-shift) would overflow and turn those zeros into NaN.
+    alpha = st.seen ? __builtin_amdgcn_exp2f(-shift) : 0.0f;
     st.seen = st.seen || bx > -INFINITY;
     st.moff += shift;
     st.l *= alpha;

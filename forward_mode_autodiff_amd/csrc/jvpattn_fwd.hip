@@ -140,18 +140,22 @@ __device__ inline bool softmax_block(f32x16& s, f32x16& sd, RowState& st, float 
 // loop is unrolled by four, so every LDS access names its stage statically
 // and in-flight loads into other stages never force a wait.
 
-template <typename T, int D, int MASK, bool CAUSAL, bool POW2>
-__device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
+//
+// SPLIT = 2 (small grids, d = 64): two groups of four waves per workgroup
+// take the same 128 rows; group G streams the G-th half of the key blocks
+// through its own ring, then group 1 hands its row state and accumulators to
+// group 0 through LDS (x0..x3: group 1's stages, one 16 KB stage per wave;
+// xst: m, moff, l, mu per lane), which combines the two online-softmax states -- rescaling
+// each to the larger reference -- and stores. Twice the waves per row block.
+template <typename T, int D, int MASK, bool CAUSAL, bool POW2, int SPLIT, int G>
+__device__ __forceinline__ void fwd16_body(const FwdArgs& a, char* stage0, char* stage1, char* stage2, char* stage3,
+                                           char* x0, char* x1, char* x2, char* x3, float4* xst) {
   using L = Tile16<D>;
   using vec8 = typename T::vec8;
-  __shared__ __attribute__((aligned(16))) char stage0[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char stage1[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char stage2[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char stage3[L::STAGE_BYTES];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x & (kThreads - 1);   // thread within the group
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave within the group
   const int c32 = lane & 31;
   const int hlf = lane >> 5;
 
@@ -204,10 +208,19 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
 
   const int kv_end = CAUSAL ? min(a.Nk, q0 + kBM) : a.Nk;
-  const int n_tiles = (kv_end + L::BN - 1) / L::BN;
-  // Last block this wave needs (the causal diagonal block, or the last tile); -1 if none.
-  const int last = !wave_live ? -1 : (CAUSAL ? min(n_tiles - 1, qw0 >> 5) : n_tiles - 1);
-  auto needs_keymask = [&](int k) { return (CAUSAL && k * 32 + 31 > qw0) || (k * 32 + 32 > a.Nk); };
+  const int n_all = (kv_end + L::BN - 1) / L::BN;
+  // This group's key blocks kb .. kb+n_tiles-1; both groups run n_loop iterations
+  // (one barrier each), the shorter one idling through the extra ones.
+  const int n_first = SPLIT == 2 ? (n_all + 1) / 2 : n_all;
+  const int kb = G == 1 ? n_first : 0;
+  const int n_tiles = G == 1 ? n_all - n_first : n_first;
+  const int n_loop = n_first;
+  // Last block this wave needs (the causal diagonal block, or the last tile), local; -1 if none.
+  const int last_all = !wave_live ? -1 : (CAUSAL ? min(n_all - 1, qw0 >> 5) : n_all - 1);
+  const int last = last_all < kb ? -1 : min(last_all - kb, n_tiles - 1);
+  auto needs_keymask = [&](int k) {
+    return (CAUSAL && (kb + k) * 32 + 31 > qw0) || ((kb + k) * 32 + 32 > a.Nk);
+  };
 
   // Direct-load slots of this thread (byte offset inside a tile, same for all four tensors).
   int dl_off[L::LOADS];
@@ -225,7 +238,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   auto issue_tile = [&](int j, char* stage) {
 #pragma unroll
     for (int i = 0; i < L::LOADS; ++i) {
-      const int off = j * L::TENSOR_BYTES + dl_off[i];
+      const int off = (kb + j) * L::TENSOR_BYTES + dl_off[i];
       const int slot = (i * kThreads + wave * 64) * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
                                                16, off, 0, 0, 0);
@@ -354,8 +367,8 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   // Blocks 1.. that need per-key masking start at jm: the causal diagonal, a
   // ragged last tile, or the end of this wave's range.
   int jm = last + 1;
-  if (CAUSAL) jm = min(jm, qw0 >> 5);
-  jm = min(jm, a.Nk >> 5);
+  if (CAUSAL) jm = min(jm, (qw0 >> 5) - kb);
+  jm = min(jm, (a.Nk >> 5) - kb);
   jm = max(jm, 1);
 
   // Pipelined iteration k (block k settled in sc; block k+1 needs no key mask).
@@ -366,7 +379,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
     else wait_vmcnt<0>();
     ring_barrier();   // tile k+1 visible to all; every wave is done with tile k-1 (the `dma` stage)
     MaskVals<MASK> mk1;
-    mask_load<MASK>(mk1, a, mr, qi, (k + 1) * 32, hlf);   // before the fetch: keeps its wait short
+    mask_load<MASK>(mk1, a, mr, qi, (kb + k + 1) * 32, hlf);   // before the fetch: keeps its wait short
     if (k + 3 < n_tiles) issue_tile(k + 3, dma);
     // All LDS operands first (their latency hides behind the first weights),
     // then the score products of block k+1 interleaved with block k's softmax
@@ -408,7 +421,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
   if (0 <= last && !needs_keymask(0)) {
     scores(stage0, sA, sdA);
     MaskVals<MASK> mk;
-    mask_load<MASK>(mk, a, mr, qi, 0, hlf);
+    mask_load<MASK>(mk, a, mr, qi, kb * 32, hlf);
     mask_apply<T, MASK, POW2>(sA, mk, a.scale);
     rescale(block_max(sA));
     ready = true;
@@ -437,7 +450,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
     i &= 3;
     return i == 0 ? stage0 : i == 1 ? stage1 : i == 2 ? stage2 : stage3;
   };
-  for (k = kfast; k < n_tiles; ++k) {
+  for (k = kfast; k < n_loop; ++k) {
     if (k + 2 < n_tiles) wait_vmcnt<L::TILE_VMEM>();
     else wait_vmcnt<0>();
     ring_barrier();
@@ -447,15 +460,62 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
     if (!ready) {
       scores(cur, sA, sdA);
       MaskVals<MASK> mk;
-      mask_load<MASK>(mk, a, mr, qi, k * 32, hlf);
+      mask_load<MASK>(mk, a, mr, qi, (kb + k) * 32, hlf);
       mask_apply<T, MASK, POW2>(sA, mk, a.scale);
-      if (needs_keymask(k)) hide_keys<CAUSAL>(sA, a.Nk, qi, k * 32, hlf);
+      if (needs_keymask(k)) hide_keys<CAUSAL>(sA, a.Nk, qi, (kb + k) * 32, hlf);
       rescale(block_max(sA));
     }
     vec8 pB[2], uB[2];
     weights(sA, sdA, pB, uB);
     values(cur, pB, uB);
     ready = false;   // the next block, if any, is settled at the top of the next iteration
+  }
+
+  if constexpr (SPLIT == 2) {
+    // Group 1 hands over its state through its own stages, once every wave is
+    // done reading them (first barrier); group 0 combines after the second.
+    // Every tile load has completed: the last iterations wait for all of them.
+    ring_barrier();
+    float4* acc = reinterpret_cast<float4*>(wave == 0 ? x0 : wave == 1 ? x1 : wave == 2 ? x2 : x3);
+    if constexpr (G == 1) {
+#pragma unroll
+      for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          acc[((2 * t) * 4 + g) * 64 + lane] = float4{accO[t][4 * g], accO[t][4 * g + 1], accO[t][4 * g + 2],
+                                                      accO[t][4 * g + 3]};
+          acc[((2 * t + 1) * 4 + g) * 64 + lane] = float4{accT[t][4 * g], accT[t][4 * g + 1],
+                                                          accT[t][4 * g + 2], accT[t][4 * g + 3]};
+        }
+      xst[wave * 64 + lane] = float4{st.m, st.moff, st.l, st.mu};
+      ring_barrier();
+      return;
+    } else {
+      ring_barrier();
+      const float4 o = xst[wave * 64 + lane];
+      const float m = fmaxf(st.m, o.x);   // -inf only if neither half saw a visible key
+      const float a0 = st.m == -INFINITY ? 0.0f : exp2f((st.m - m) * a.cx);
+      const float a1 = o.x == -INFINITY ? 0.0f : exp2f((o.x - m) * a.cx);
+#pragma unroll
+      for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 xo = acc[((2 * t) * 4 + g) * 64 + lane];
+          const float4 xt = acc[((2 * t + 1) * 4 + g) * 64 + lane];
+          accO[t][4 * g] = accO[t][4 * g] * a0 + xo.x * a1;
+          accO[t][4 * g + 1] = accO[t][4 * g + 1] * a0 + xo.y * a1;
+          accO[t][4 * g + 2] = accO[t][4 * g + 2] * a0 + xo.z * a1;
+          accO[t][4 * g + 3] = accO[t][4 * g + 3] * a0 + xo.w * a1;
+          accT[t][4 * g] = accT[t][4 * g] * a0 + xt.x * a1;
+          accT[t][4 * g + 1] = accT[t][4 * g + 1] * a0 + xt.y * a1;
+          accT[t][4 * g + 2] = accT[t][4 * g + 2] * a0 + xt.z * a1;
+          accT[t][4 * g + 3] = accT[t][4 * g + 3] * a0 + xt.w * a1;
+        }
+      st.l = st.l * a0 + o.z * a1;
+      st.mu = st.mu * a0 + o.w * a1;
+      st.m = m;
+      st.moff = m == -INFINITY ? 0.0f : m * a.cx;
+    }
   }
 
   // Epilogue: combine the two lane halves of each query column, normalise, store.
@@ -490,10 +550,27 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a) {
 }
 
 // The kernel bodies use gfx950 builtins; the host pass only needs the launch stubs.
-template <typename T, int D, int MASK, bool CAUSAL, bool POW2>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd16_kernel(FwdArgs a) {
+template <typename T, int D, int MASK, bool CAUSAL, bool POW2, int SPLIT>
+__global__ __launch_bounds__(kThreads * SPLIT, D == 64 ? 2 : 1) void fwd16_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  fwd16_body<T, D, MASK, CAUSAL, POW2>(a);
+  using L = Tile16<D>;
+  __shared__ __attribute__((aligned(16))) char s0[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char s1[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char s2[L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char s3[L::STAGE_BYTES];
+  if constexpr (SPLIT == 1) {
+    fwd16_body<T, D, MASK, CAUSAL, POW2, 1, 0>(a, s0, s1, s2, s3, nullptr, nullptr, nullptr, nullptr, nullptr);
+  } else {
+    __shared__ __attribute__((aligned(16))) char s4[L::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char s5[L::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char s6[L::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char s7[L::STAGE_BYTES];
+    __shared__ float4 xst[kThreads];
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 8) == 0)
+      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 0>(a, s0, s1, s2, s3, s4, s5, s6, s7, xst);
+    else
+      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 1>(a, s4, s5, s6, s7, s4, s5, s6, s7, xst);
+  }
 #endif
 }
 
@@ -1031,20 +1108,30 @@ hipError_t launch_pp(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipSt
   return hipGetLastError();
 }
 
+// The 4-wave kernel for d = 64, whole key range (split = false) or halves (split = true).
+template <typename T, int MASK, bool CAUSAL, bool POW2>
+void launch_d64(bool split, const FwdArgs& args, dim3 grid, hipStream_t stream) {
+  if (split)
+    hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 2>), grid, dim3(2 * kThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 1>), grid, dim3(kThreads), 0, stream, args);
+}
+
 template <int MASK, bool CAUSAL>
-hipError_t launch_typed(int dtype, int d, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
+hipError_t launch_typed(int dtype, int d, bool pow2, bool split, const FwdArgs& args, dim3 grid,
+                        hipStream_t stream) {
   const dim3 block(kThreads);
   if (dtype == JVPATTN_BF16) {
     if (pow2) {
-      if (d == 64) hipLaunchKernelGGL((fwd16_kernel<BF16, 64, MASK, CAUSAL, true>), grid, block, 0, stream, args);
-      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, true>), grid, block, 0, stream, args);
+      if (d == 64) launch_d64<BF16, MASK, CAUSAL, true>(split, args, grid, stream);
+      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, true, 1>), grid, block, 0, stream, args);
     } else {
-      if (d == 64) hipLaunchKernelGGL((fwd16_kernel<BF16, 64, MASK, CAUSAL, false>), grid, block, 0, stream, args);
-      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+      if (d == 64) launch_d64<BF16, MASK, CAUSAL, false>(split, args, grid, stream);
+      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, false, 1>), grid, block, 0, stream, args);
     }
   } else if (dtype == JVPATTN_F16) {
-    if (d == 64) hipLaunchKernelGGL((fwd16_kernel<F16, 64, MASK, CAUSAL, false>), grid, block, 0, stream, args);
-    else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+    if (d == 64) launch_d64<F16, MASK, CAUSAL, false>(split, args, grid, stream);
+    else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, false, 1>), grid, block, 0, stream, args);
   } else {
     if (d == 64) {
       hipLaunchKernelGGL((fwd32_kernel<64, MASK, CAUSAL>), grid, block, Tile32<64>::BUF_BYTES, stream, args);
@@ -1095,14 +1182,20 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
     a.mask_vec = mask && (p->mask_stride_b % need == 0) && (p->mask_stride_h % need == 0) &&
                  (p->mask_stride_q % need == 0) && (base % (need * mes) == 0);
   }
-  // Kernel choice: the 8-wave ping-pong kernel (256 rows per workgroup) for
-  // 16-bit d = 64 when it still gives every CU a workgroup; otherwise the
-  // 4-wave kernel (128 rows). JVPATTN_FWD_KERNEL=pp|wg4 forces one (testing).
+  // Kernel choice for 16-bit d = 64: the 8-wave ping-pong kernel (256 rows per
+  // workgroup) when it still gives every CU a workgroup; else the 4-wave
+  // kernel (128 rows), with the key range split between two groups of waves
+  // when it would have fewer than two workgroups per CU. Other types and d:
+  // the 4-wave kernel (float32: its own). JVPATTN_FWD_KERNEL=pp|wg4|split
+  // forces one (testing).
   const int64_t n128 = (p->Nq + kBM - 1) / kBM, n256 = (p->Nq + kPPBM - 1) / kPPBM;
-  bool pp = p->d == 64 && p->dtype != JVPATTN_F32 && n256 * a.BH >= 256;
+  const bool d64_16 = p->d == 64 && p->dtype != JVPATTN_F32;
+  bool pp = d64_16 && n256 * a.BH >= 256;
+  bool split = d64_16 && !pp && n128 * a.BH < 512;
   if (const char* env = std::getenv("JVPATTN_FWD_KERNEL")) {
-    if (std::strcmp(env, "pp") == 0) pp = p->d == 64 && p->dtype != JVPATTN_F32;
-    if (std::strcmp(env, "wg4") == 0) pp = false;
+    if (std::strcmp(env, "pp") == 0) pp = d64_16, split = false;
+    if (std::strcmp(env, "wg4") == 0) pp = false, split = false;
+    if (std::strcmp(env, "split") == 0) pp = false, split = d64_16;
   }
   a.n_qblk = static_cast<int>(pp ? n256 : n128);
   const int64_t blocks = int64_t(a.n_qblk) * a.BH;
@@ -1130,16 +1223,16 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
   } else {
     switch (p->mask_kind) {
       case JVPATTN_MASK_NONE:
-        e = c ? launch_typed<JVPATTN_MASK_NONE, true>(p->dtype, p->d, pow2, a, grid, s)
-              : launch_typed<JVPATTN_MASK_NONE, false>(p->dtype, p->d, pow2, a, grid, s);
+        e = c ? launch_typed<JVPATTN_MASK_NONE, true>(p->dtype, p->d, pow2, split, a, grid, s)
+              : launch_typed<JVPATTN_MASK_NONE, false>(p->dtype, p->d, pow2, split, a, grid, s);
         break;
       case JVPATTN_MASK_BOOL:
-        e = c ? launch_typed<JVPATTN_MASK_BOOL, true>(p->dtype, p->d, pow2, a, grid, s)
-              : launch_typed<JVPATTN_MASK_BOOL, false>(p->dtype, p->d, pow2, a, grid, s);
+        e = c ? launch_typed<JVPATTN_MASK_BOOL, true>(p->dtype, p->d, pow2, split, a, grid, s)
+              : launch_typed<JVPATTN_MASK_BOOL, false>(p->dtype, p->d, pow2, split, a, grid, s);
         break;
       default:
-        e = c ? launch_typed<JVPATTN_MASK_ADDITIVE, true>(p->dtype, p->d, pow2, a, grid, s)
-              : launch_typed<JVPATTN_MASK_ADDITIVE, false>(p->dtype, p->d, pow2, a, grid, s);
+        e = c ? launch_typed<JVPATTN_MASK_ADDITIVE, true>(p->dtype, p->d, pow2, split, a, grid, s)
+              : launch_typed<JVPATTN_MASK_ADDITIVE, false>(p->dtype, p->d, pow2, split, a, grid, s);
         break;
     }
   }

@@ -21,9 +21,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 # The library picks between an 8-wave ping-pong kernel (16-bit, d = 64, large
-# grids) and a 4-wave kernel; the override forces one so both are checked on
-# small shapes too.
-KERNELS = ["pp", "wg4"]
+# grids), a 4-wave kernel, and the 4-wave kernel with the key range split
+# between two groups of waves (16-bit, d = 64, small grids); the override
+# forces one so each is checked on every kernel-sensitive case.
+KERNELS = ["pp", "wg4", "split"]
 
 
 @pytest.fixture(params=KERNELS)
@@ -299,6 +300,33 @@ def test_all_4x4_bool_masks_in_one_launch():
                 for n, a in (("o", o), ("to", to), ("lse", lse), ("tlse", tlse)):
                     ref[n][:, 0, i] = a[rowpat, 0, i]
             assert_parity(got, ref, dtype, f"mask4 {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_scores(kernel, causal, dtype):
+    """Scores of a few hundred, carried by head-dim entries 24..31 and 56..63 only.
+
+    The matrix cores accumulate a score block over four 16-wide chunks of the
+    head dimension; here the first three add nothing, so a row maximum read
+    before the last product has landed would be 0 while the true scores reach
+    about 200: exponentials against that reference overflow. Key 0 is set to
+    -q_0, so query row 0 (which sees only key 0 when causal) has the score
+    -|q_0|^2 scale, about -290: a first reference far below 0, which must not
+    scale the (still zero) accumulators by exp(+290). Regression test for both.
+    """
+    w = I.Workload("large_scores", B=1, H=2, N=300, d=64, dtype=dtype, causal=causal, std=1.0, seed=21)
+    x = I.make_inputs(w)
+    keep = torch.zeros(64)
+    keep[24:32] = 1.0
+    keep[56:64] = 1.0
+    for n in ("q", "k"):
+        x[n] = (x[n].float() * 12.0 * keep).to(x[n].dtype)
+    x["k"][:, :, 0] = -x["q"][:, :, 0]
+    got, ref = check(w, x=x)
+    assert np.abs(ref["lse"]).max() > 100.0
+    if causal:
+        assert ref["lse"][:, :, 0].max() < -100.0
 
 
 def test_deterministic(kernel):
