@@ -37,7 +37,9 @@ Readings taken where the pages say nothing (each is listed in the design notes):
     SDPA's ``is_causal``); with an explicit mask both restrictions apply;
   * a row whose every score is -inf ("fully masked") gives O = dO = 0,
     lse = -inf, tlse = 0;
-  * lse uses the natural logarithm.
+  * lse uses the natural logarithm;
+  * grouped key/value heads (fewer K/V heads than query heads, as SDPA's
+    ``enable_gqa``): query head h attends with key/value head h // (H // Hkv).
 No blocking, no online softmax and no fusion: the softmax is the two-pass
 definition (max, exponentials, normalise).
 """
@@ -119,9 +121,19 @@ def oracle_fwd_head(q, k, v, tq, tk, tv, bias, scale):
     return o, to, lse, tlse
 
 
+def kv_head(h, H, Hkv):
+    """Key/value head read by query head h when H query heads share Hkv key/value heads."""
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"{H} query heads cannot be grouped over {Hkv} key/value heads")
+    return h // (H // Hkv)
+
+
 def oracle_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, mask_kind=MASK_NONE,
                causal=False, scale=None, q_pos=None):
-    """Attention output and its JVP for [B, H, Nq, d] queries and [B, H, Nk, d] keys/values.
+    """Attention output and its JVP for [B, H, Nq, d] queries and [B, Hkv, Nk, d] keys/values.
+
+    Hkv = H is plain multi-head attention; a divisor of H groups the query
+    heads, query head h reading key/value head ``kv_head(h, H, Hkv)``.
 
     q, k, v, tq, tk, tv: array-likes (values already rounded to the working
         dtype; they are widened to float64 here). A tangent given as None is zero.
@@ -139,7 +151,7 @@ def oracle_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, mask_kind=MASK_NON
     tk = np.zeros_like(k) if tk is None else _f64(tk)
     tv = np.zeros_like(v) if tv is None else _f64(tv)
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    Hkv, Nk = k.shape[1], k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if q_pos is None:
@@ -157,6 +169,7 @@ def oracle_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, mask_kind=MASK_NON
     for b in range(B):
         for h in range(H):
             bias = _head_bias(mask, mask_kind, b, h, Nq, Nk, causal, q_pos)
+            g = kv_head(h, H, Hkv)
             o[b, h], to[b, h], lse[b, h], tlse[b, h] = oracle_fwd_head(
-                q[b, h], k[b, h], v[b, h], tq[b, h], tk[b, h], tv[b, h], bias, scale)
+                q[b, h], k[b, g], v[b, g], tq[b, h], tk[b, g], tv[b, g], bias, scale)
     return o, to, lse, tlse

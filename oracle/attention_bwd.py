@@ -24,7 +24,9 @@ algebraic shortcuts, no blocking):
     dO = dP V + P dV
 
 The additive mask M is a constant (no gradient). Rows whose every score is
--inf have P = 0 and contribute nothing.
+-inf have P = 0 and contribute nothing. With grouped key/value heads several
+query heads read one K/V head, so that head's cotangents are the sum of what
+each of its query heads pulls back to it (the chain rule for a shared input).
 """
 from __future__ import annotations
 
@@ -32,7 +34,7 @@ import math
 
 import numpy as np
 
-from .attention import MASK_NONE, _f64, _head_bias
+from .attention import MASK_NONE, _f64, _head_bias, kv_head
 
 
 def oracle_bwd_head(q, k, v, tq, tk, tv, go, gto, bias, scale):
@@ -80,7 +82,8 @@ def oracle_bwd(q, k, v, tq, tk, tv, go, gto, mask=None, mask_kind=MASK_NONE, cau
     """Cotangents of (Q, K, V, dQ, dK, dV) for cotangents (go, gto) of (O, dO).
 
     Shapes as in ``oracle_fwd``: q, tq, go, gto [B,H,Nq,d]; k, v, tk, tv
-    [B,H,Nk,d]; mask [Bm,Hm,Nq,Nk]. A tangent given as None is zero.
+    [B,Hkv,Nk,d] (Hkv divides H); mask [Bm,Hm,Nq,Nk]. A tangent given as None
+    is zero.
     Returns (gq, gk, gv, gtq, gtk, gtv) float64, shaped like the inputs.
     """
     q, k, v, go, gto = _f64(q), _f64(k), _f64(v), _f64(go), _f64(gto)
@@ -88,24 +91,28 @@ def oracle_bwd(q, k, v, tq, tk, tv, go, gto, mask=None, mask_kind=MASK_NONE, cau
     tk = np.zeros_like(k) if tk is None else _f64(tk)
     tv = np.zeros_like(v) if tv is None else _f64(tv)
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    Hkv, Nk = k.shape[1], k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if mask is not None:
         mask = np.asarray(mask)
     if (mask is None) != (mask_kind == MASK_NONE):
         raise ValueError("mask must be given exactly when mask_kind is not 'none'")
-    outs = [np.empty_like(q), np.empty_like(k), np.empty_like(v), np.empty_like(q), np.empty_like(k),
-            np.empty_like(v)]
+    gq, gtq = np.empty_like(q), np.empty_like(q)
+    gk, gv, gtk, gtv = np.zeros_like(k), np.zeros_like(v), np.zeros_like(k), np.zeros_like(v)
     q_pos = np.arange(Nq)
     for b in range(B):
         for h in range(H):
+            g = kv_head(h, H, Hkv)
             bias = _head_bias(mask, mask_kind, b, h, Nq, Nk, causal, q_pos)
-            r = oracle_bwd_head(q[b, h], k[b, h], v[b, h], tq[b, h], tk[b, h], tv[b, h], go[b, h], gto[b, h],
+            r = oracle_bwd_head(q[b, h], k[b, g], v[b, g], tq[b, h], tk[b, g], tv[b, g], go[b, h], gto[b, h],
                                 bias, scale)
-            for o, x in zip(outs, r):
-                o[b, h] = x
-    return tuple(outs)
+            gq[b, h], gtq[b, h] = r[0], r[3]
+            gk[b, g] += r[1]
+            gv[b, g] += r[2]
+            gtk[b, g] += r[4]
+            gtv[b, g] += r[5]
+    return gq, gk, gv, gtq, gtk, gtv
 
 
 def bwd_flop_count(B, H, Nq, Nk, d, causal):

@@ -24,10 +24,11 @@ import oracle.attention_bwd as ob
 from oracle import oracle_bwd, oracle_fwd
 
 
-def make(rng, B=2, H=2, Nq=7, Nk=9, d=5, std=1.0):
+def make(rng, B=2, H=2, Nq=7, Nk=9, d=5, std=1.0, Hkv=None):
     r = lambda *s, sd=1.0: rng.standard_normal(s) * sd
-    return dict(q=r(B, H, Nq, d, sd=std), k=r(B, H, Nk, d, sd=std), v=r(B, H, Nk, d, sd=std),
-                tq=r(B, H, Nq, d), tk=r(B, H, Nk, d), tv=r(B, H, Nk, d),
+    Hk = H if Hkv is None else Hkv
+    return dict(q=r(B, H, Nq, d, sd=std), k=r(B, Hk, Nk, d, sd=std), v=r(B, Hk, Nk, d, sd=std),
+                tq=r(B, H, Nq, d), tk=r(B, Hk, Nk, d), tv=r(B, Hk, Nk, d),
                 go=r(B, H, Nq, d), gto=r(B, H, Nq, d))
 
 
@@ -35,9 +36,11 @@ def torch_reverse_over_forward(x, attn_mask=None, is_causal=False, scale=None):
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).requires_grad_(True)
     ins = [T(x[n]) for n in ("q", "k", "v", "tq", "tk", "tv")]
     m = None if attn_mask is None else torch.from_numpy(np.ascontiguousarray(attn_mask))
+    gqa = x["k"].shape[1] != x["q"].shape[1]
     with sdpa_kernel(SDPBackend.MATH):
         o, to = torch.func.jvp(
-            lambda a, b, c: F.scaled_dot_product_attention(a, b, c, attn_mask=m, is_causal=is_causal, scale=scale),
+            lambda a, b, c: F.scaled_dot_product_attention(a, b, c, attn_mask=m, is_causal=is_causal, scale=scale,
+                                                           enable_gqa=gqa),
             tuple(ins[:3]), tuple(ins[3:]))
         L = (o * torch.from_numpy(x["go"])).sum() + (to * torch.from_numpy(x["gto"])).sum()
         g = torch.autograd.grad(L, ins)
@@ -90,15 +93,24 @@ def test_matches_torch_autograd_causal_rectangular():
     assert_close(run_bwd(x, causal=True), torch_reverse_over_forward(x, is_causal=True), 1e-11)
 
 
+@pytest.mark.parametrize("H,Hkv,causal", [(4, 2, False), (6, 2, True), (3, 1, False)],
+                         ids=["gqa2", "gqa3-causal", "mqa"])
+def test_matches_torch_autograd_grouped_heads(H, Hkv, causal):
+    # a key/value head read by several query heads collects all their cotangents
+    x = make(np.random.default_rng(37 + H), H=H, Hkv=Hkv, Nq=6, Nk=8, d=4)
+    assert_close(run_bwd(x, causal=causal), torch_reverse_over_forward(x, is_causal=causal), 1e-11)
+
+
 def loss(x, **kw):
     o, to, _, _ = oracle_fwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], **kw)
     return float(np.sum(o * x["go"]) + np.sum(to * x["gto"]))
 
 
-@pytest.mark.parametrize("kw", [{}, {"causal": True}, {"scale": 1.7}], ids=["plain", "causal", "scale"])
-def test_directional_finite_differences(kw):
+@pytest.mark.parametrize("kw,hkv", [({}, 2), ({"causal": True}, 2), ({"scale": 1.7}, 2), ({}, 1)],
+                         ids=["plain", "causal", "scale", "grouped"])
+def test_directional_finite_differences(kw, hkv):
     rng = np.random.default_rng(35)
-    x = make(rng, B=1, H=2, Nq=6, Nk=7, d=4)
+    x = make(rng, B=1, H=2, Nq=6, Nk=7, d=4, Hkv=hkv)
     g = run_bwd(x, **kw)
     for trial in range(3):
         dirs = {n: rng.standard_normal(x[n].shape) for n in ("q", "k", "v", "tq", "tk", "tv")}
@@ -197,3 +209,20 @@ def test_mutants_fail_the_autograd_pin(name, monkeypatch):
     got = ob.oracle_bwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], x["go"], x["gto"], causal=True)
     worst = max(float(np.max(np.abs(a - b))) for a, b in zip(got, ref))
     assert worst > 1e-3, f"mutant {name} passes the pin (max diff {worst:.2e})"
+
+
+def test_grouped_head_mutants_fail_the_autograd_pin(monkeypatch):
+    # two plausible grouping mistakes: interleaved instead of blocked head
+    # sharing, and keeping only the last query head's cotangent
+    x = make(np.random.default_rng(41), H=4, Hkv=2, Nq=6, Nk=7, d=4)
+    ref = torch_reverse_over_forward(x)
+    run = lambda: ob.oracle_bwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], x["go"], x["gto"])
+    with monkeypatch.context() as m:
+        m.setattr(ob, "kv_head", lambda h, H, Hkv: h % Hkv)
+        assert max(float(np.max(np.abs(a - b))) for a, b in zip(run(), ref)) > 1e-3
+    import inspect
+    src = inspect.getsource(ob.oracle_bwd).replace("gk[b, g] += r[1]", "gk[b, g] = r[1]")
+    ns = dict(ob.__dict__)
+    exec(compile(src, "<mutant>", "exec"), ns)
+    got = ns["oracle_bwd"](x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], x["go"], x["gto"])
+    assert float(np.max(np.abs(got[1] - ref[1]))) > 1e-3

@@ -44,14 +44,14 @@ def make(rng, B=2, H=3, Nq=7, Nk=9, d=5, std=1.0):
     return q, k, v, tq, tk, tv
 
 
-def torch_sdpa_jvp(q, k, v, tq, tk, tv, attn_mask=None, is_causal=False, scale=None):
+def torch_sdpa_jvp(q, k, v, tq, tk, tv, attn_mask=None, is_causal=False, scale=None, enable_gqa=False):
     """PyTorch's SDPA (MATH backend, float64 CPU) and its forward-mode derivative."""
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a))
     m = None if attn_mask is None else T(attn_mask)
     with sdpa_kernel(SDPBackend.MATH):
         o, to = torch.func.jvp(
             lambda a, b, c: F.scaled_dot_product_attention(a, b, c, attn_mask=m, is_causal=is_causal,
-                                                           scale=scale),
+                                                           scale=scale, enable_gqa=enable_gqa),
             (T(q), T(k), T(v)), (T(tq), T(tk), T(tv)))
     return o.numpy(), to.numpy()
 
@@ -106,6 +106,27 @@ def test_matches_torch_sdpa_custom_scale():
     ro, rto = torch_sdpa_jvp(*args, scale=0.37)
     np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
     np.testing.assert_allclose(to, rto, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("H,Hkv,causal", [(4, 2, False), (6, 3, True), (4, 1, False)],
+                         ids=["gqa2", "gqa3-causal", "mqa"])
+def test_matches_torch_sdpa_grouped_heads(H, Hkv, causal):
+    # grouped-query attention: SDPA's enable_gqa shares key/value head h // (H // Hkv)
+    rng = np.random.default_rng(40 + H + Hkv)
+    q, _, _, tq, _, _ = make(rng, H=H, Nq=7, Nk=9, d=5)
+    k, v, tk, tv = (rnd(rng, 2, Hkv, 9, 5) for _ in range(4))
+    o, to, _, _ = oracle_fwd(q, k, v, tq, tk, tv, causal=causal)
+    ro, rto = torch_sdpa_jvp(q, k, v, tq, tk, tv, is_causal=causal, enable_gqa=True)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(to, rto, rtol=0, atol=1e-11)
+
+
+def test_grouped_heads_reject_non_divisor():
+    rng = np.random.default_rng(44)
+    q, _, _, tq, _, _ = make(rng, H=3)
+    k = rnd(rng, 2, 2, 9, 5)
+    with pytest.raises(ValueError):
+        oracle_fwd(q, k, k, tq, k, k)
 
 
 def test_lse_matches_scipy_logsumexp():
