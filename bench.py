@@ -29,6 +29,7 @@ def workloads():
     from forward_mode_autodiff_amd import inputs as I
     return {
         "hvp": I.HVP,
+        "hvp_gqa4": I.HVP_GQA,
         "hvp_full": I.Workload("hvp_full", B=4, H=16, N=2048, d=64, dtype="bf16", causal=False, seed=4),
         "seq2048": I.seq(2048, False),
         "seq2048_causal": I.seq(2048, True),
@@ -43,12 +44,13 @@ def workloads():
 def algorithmic_bytes(w):
     """Bytes a launch must move at least: 6 inputs + 2 outputs + lse/tlse, the mask read once per batch."""
     es = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
-    per_head = (4 * w.N * w.d + 4 * w.nk * w.d) * es + 8 * w.N
+    per_q_head = 4 * w.N * w.d * es + 8 * w.N          # q, tq, o, to, lse, tlse
+    per_kv_head = 4 * w.nk * w.d * es                   # k, v, tk, tv (shared by grouped query heads)
     mask = 0
     if w.mask_kind != "none":
         mes = 1 if w.mask_kind == "bool" else es
         mask = w.B * w.mask_heads * w.N * w.nk * mes
-    return w.B * w.H * per_head + mask
+    return w.B * w.H * per_q_head + w.B * w.hkv * per_kv_head + mask
 
 
 KERNEL_SOURCES = [os.path.join(ROOT, "forward_mode_autodiff_amd", "csrc", f)
@@ -80,15 +82,17 @@ def cpu_baseline_bwd(w, x, budget_s=12.0):
 
     from oracle import bwd_flop_count, oracle_bwd
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    grp = w.H // w.hkv
     done, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         b, h = heads[done % len(heads)]
         f64 = lambda t: t[b:b + 1, h:h + 1].double().numpy()
+        f64k = lambda t: t[b:b + 1, h // grp:h // grp + 1].double().numpy()   # the K/V head h reads
         mask = None
         if x["mask"] is not None:
             mask = x["mask"][b:b + 1, :1].double().numpy() if w.mask_kind == "additive" else \
                 x["mask"][b:b + 1, :1].numpy()
-        oracle_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["tq"]), f64(x["tk"]), f64(x["tv"]),
+        oracle_bwd(f64(x["q"]), f64k(x["k"]), f64k(x["v"]), f64(x["tq"]), f64k(x["tk"]), f64k(x["tv"]),
                    f64(x["do"]), f64(x["dto"]), mask=mask, mask_kind=w.mask_kind, causal=w.causal)
         done += 1
     dt = time.perf_counter() - t0
@@ -106,7 +110,9 @@ def cpu_baseline(w, x, budget_s=12.0):
 
     from oracle import flop_count, oracle_fwd
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    grp = w.H // w.hkv
     f64 = lambda t: t[b:b + 1, h:h + 1].double().numpy()
+    f64k = lambda t: t[b:b + 1, h // grp:h // grp + 1].double().numpy()   # the K/V head h reads
     done, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         b, h = heads[done % len(heads)]
@@ -114,7 +120,7 @@ def cpu_baseline(w, x, budget_s=12.0):
         if x["mask"] is not None:
             mask = x["mask"][b:b + 1, :1].double().numpy() if w.mask_kind == "additive" else \
                 x["mask"][b:b + 1, :1].numpy()
-        oracle_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["tq"]), f64(x["tk"]), f64(x["tv"]),
+        oracle_fwd(f64(x["q"]), f64k(x["k"]), f64k(x["v"]), f64(x["tq"]), f64k(x["tk"]), f64k(x["tv"]),
                    mask=mask, mask_kind=w.mask_kind, causal=w.causal)
         done += 1
     dt = time.perf_counter() - t0
@@ -222,7 +228,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name + ("_bwd" if reverse else ""), "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+        "config": {"workload": w.name + ("_bwd" if reverse else ""), "B": w.B, "H": w.H, "Hkv": w.hkv,
+                   "N": w.N, "d": w.d,
                    "causal": w.causal, "mask": w.mask_kind, "input_std": round(w.sigma, 6)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),

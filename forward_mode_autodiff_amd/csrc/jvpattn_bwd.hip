@@ -64,6 +64,8 @@ struct BwdArgs {
   float* ws;          // [4][ws_stride]: -lse*log2e, tlse, r, del
   int64_t ws_stride;  // floats per workspace array
   int H, Nq, Nk, BH;
+  int grp;            // query heads per key/value head (grouped-query attention; 1 = one each)
+  int BHK;            // key/value heads in all: B * H / grp
   int n_blk;
   int mask_vec;
   int64_t msb, msh, msq;
@@ -173,7 +175,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   const bool wave_live = qw0 < a.Nq;
 
   const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
-  const int64_t khead = int64_t(bh) * a.Nk * L::ROW;
+  const int64_t khead = int64_t(bh / a.grp) * a.Nk * L::ROW;   // the key/value head it reads
   const int64_t qbytes = int64_t(a.Nq) * L::ROW, kbytes = int64_t(a.Nk) * L::ROW;
   auto at = [](const void* p, int64_t off) { return static_cast<const char*>(p) + off; };
 
@@ -498,16 +500,15 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
   const int c32 = lane & 31;
   const int hlf = lane >> 5;
 
-  const int kb = int(blockIdx.x) / a.BH;   // causal: early key blocks see the most queries
-  const int bh = int(blockIdx.x) % a.BH;
-  const int b = bh / a.H, h = bh % a.H;
+  const int kb = int(blockIdx.x) / a.BHK;   // causal: early key blocks see the most queries
+  const int bhk = int(blockIdx.x) % a.BHK;  // key/value head; its query heads are bhk*grp .. +grp-1
+  const int b = bhk * a.grp / a.H;
   const int k0 = kb * kBBlk;
   const int kw0 = k0 + 32 * wave;
   const int kj = kw0 + c32;                 // this lane's key
   const bool wave_live = kw0 < a.Nk;
 
-  const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
-  const int64_t khead = int64_t(bh) * a.Nk * L::ROW;
+  const int64_t khead = int64_t(bhk) * a.Nk * L::ROW;
   const int64_t qbytes = int64_t(a.Nq) * L::ROW, kbytes = int64_t(a.Nk) * L::ROW;
   auto at = [](const void* p, int64_t off) { return static_cast<const char*>(p) + off; };
 
@@ -543,212 +544,222 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
     accV[t] = f32x16{};
     accTV[t] = f32x16{};
   }
-  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+  // Grouped key/value heads: the cotangents of this head's keys sum over the
+  // grp query heads that read them, one after the other (the tile pipeline
+  // drains and restarts at each change of query head).
+  for (int g = 0; g < a.grp; ++g) {
+    const int bh = bhk * a.grp + g;
+    const int h = bh % a.H;
+    const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
+    const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
 
-  const int n_qt = (a.Nq + 31) / 32;
-  // causal: queries before the block's first key see none of its keys
-  const int t_begin = CAUSAL ? min(n_qt, k0 >> 5) : 0;
-  const int first = !wave_live ? n_qt : (CAUSAL ? max(t_begin, kw0 >> 5) : 0);   // first tile of this wave
-  auto needs_rowmask = [&](int t) { return (CAUSAL && t * 32 < kw0 + 32) || (t * 32 + 32 > a.Nq) || (kw0 + 32 > a.Nk); };
+    const int n_qt = (a.Nq + 31) / 32;
+    // causal: queries before the block's first key see none of its keys
+    const int t_begin = CAUSAL ? min(n_qt, k0 >> 5) : 0;
+    const int first = !wave_live ? n_qt : (CAUSAL ? max(t_begin, kw0 >> 5) : 0);   // first tile of this wave
+    auto needs_rowmask = [&](int t) { return (CAUSAL && t * 32 < kw0 + 32) || (t * 32 + 32 > a.Nq) || (kw0 + 32 > a.Nk); };
 
-  int dl_off[L::LOADS];
-#pragma unroll
-  for (int i = 0; i < L::LOADS; ++i) {
-    const int p = i * kBThreads + tid;
-    const int row = p / L::GR, pg = p % L::GR;
-    dl_off[i] = row * L::ROW + ((pg ^ swz(row)) << 4);
-  }
-  const Rsrc rq = make_rsrc(at(a.q, qhead), qbytes);
-  const Rsrc rtq = make_rsrc(a.tq ? at(a.tq, qhead) : at(a.q, qhead), a.tq ? qbytes : 0);
-  const Rsrc rg = make_rsrc(a.go ? at(a.go, qhead) : at(a.q, qhead), a.go ? qbytes : 0);
-  const Rsrc rtg = make_rsrc(a.gto ? at(a.gto, qhead) : at(a.q, qhead), a.gto ? qbytes : 0);
-  // Statistics of this head's rows: wave w loads statistic w of the tile (8 lanes x 16 bytes).
-  const int64_t srow = int64_t(bh) * a.Nq;
-  const Rsrc rstat = make_rsrc(a.ws + wave * a.ws_stride + srow, int64_t(a.Nq) * 4);
-  auto issue_tile = [&](int j, char* stage) {
+    int dl_off[L::LOADS];
 #pragma unroll
     for (int i = 0; i < L::LOADS; ++i) {
-      const int off = j * L::TENSOR_BYTES + dl_off[i];
-      const int slot = (i * kBThreads + wave * 64) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
-                                               16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rtq, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rg, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rtg, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+      const int p = i * kBThreads + tid;
+      const int row = p / L::GR, pg = p % L::GR;
+      dl_off[i] = row * L::ROW + ((pg ^ swz(row)) << 4);
     }
-    // 32 floats of statistic `wave` for rows 32j .. 32j+31 (past Nq: zeros)
-    if (lane < 8)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rstat, (__attribute__((address_space(3))) void*)to_lds(stage + L::STAGE_BYTES + wave * 128), 16,
-          j * 128 + lane * 16, 0, 0, 0);
-  };
+    const Rsrc rq = make_rsrc(at(a.q, qhead), qbytes);
+    const Rsrc rtq = make_rsrc(a.tq ? at(a.tq, qhead) : at(a.q, qhead), a.tq ? qbytes : 0);
+    const Rsrc rg = make_rsrc(a.go ? at(a.go, qhead) : at(a.q, qhead), a.go ? qbytes : 0);
+    const Rsrc rtg = make_rsrc(a.gto ? at(a.gto, qhead) : at(a.q, qhead), a.gto ? qbytes : 0);
+    // Statistics of this head's rows: wave w loads statistic w of the tile (8 lanes x 16 bytes).
+    const int64_t srow = int64_t(bh) * a.Nq;
+    const Rsrc rstat = make_rsrc(a.ws + wave * a.ws_stride + srow, int64_t(a.Nq) * 4);
+    auto issue_tile = [&](int j, char* stage) {
+#pragma unroll
+      for (int i = 0; i < L::LOADS; ++i) {
+        const int off = j * L::TENSOR_BYTES + dl_off[i];
+        const int slot = (i * kBThreads + wave * 64) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
+                                                 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rtq, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rg, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rtg, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+      }
+      // 32 floats of statistic `wave` for rows 32j .. 32j+31 (past Nq: zeros)
+      if (lane < 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rstat, (__attribute__((address_space(3))) void*)to_lds(stage + L::STAGE_BYTES + wave * 128), 16,
+            j * 128 + lane * 16, 0, 0, 0);
+    };
 
-  int kofs[L::NC];
+    int kofs[L::NC];
 #pragma unroll
-  for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ swz(c32)) << 4);
-  int vofs0[L::NT], vofs1[L::NT];
-  {
-    const int g16 = lane >> 4, i16 = lane & 15;
-    const int r0 = 4 * hlf + (i16 >> 2), r1 = r0 + 8;
+    for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ swz(c32)) << 4);
+    int vofs0[L::NT], vofs1[L::NT];
+    {
+      const int g16 = lane >> 4, i16 = lane & 15;
+      const int r0 = 4 * hlf + (i16 >> 2), r1 = r0 + 8;
 #pragma unroll
-    for (int t = 0; t < L::NT; ++t) {
-      const int gcol = 4 * t + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-      vofs0[t] = r0 * L::ROW + ((gcol ^ swz(r0)) << 4) + 8 * (i16 & 1);
-      vofs1[t] = r1 * L::ROW + ((gcol ^ swz(r1)) << 4) + 8 * (i16 & 1);
+      for (int t = 0; t < L::NT; ++t) {
+        const int gcol = 4 * t + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+        vofs0[t] = r0 * L::ROW + ((gcol ^ swz(r0)) << 4) + 8 * (i16 & 1);
+        vofs1[t] = r1 * L::ROW + ((gcol ^ swz(r1)) << 4) + 8 * (i16 & 1);
+      }
     }
-  }
-  auto read_rows = [&](const char* sb, int tsr, vec8 (&x)[L::NC]) {
+    auto read_rows = [&](const char* sb, int tsr, vec8 (&x)[L::NC]) {
 #pragma unroll
-    for (int c = 0; c < L::NC; ++c) x[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + tsr * L::TENSOR_BYTES, kofs[c]));
-  };
-  auto read_tr = [&](const char* sb, int tsr, vec8 (&x)[L::NT][2]) {
-    const char* base = sb + tsr * L::TENSOR_BYTES;
+      for (int c = 0; c < L::NC; ++c) x[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + tsr * L::TENSOR_BYTES, kofs[c]));
+    };
+    auto read_tr = [&](const char* sb, int tsr, vec8 (&x)[L::NT][2]) {
+      const char* base = sb + tsr * L::TENSOR_BYTES;
 #pragma unroll
-    for (int t = 0; t < L::NT; ++t)
+      for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const int o0 = 16 * kc * L::ROW + vofs0[t], o1 = 16 * kc * L::ROW + vofs1[t];
+          x[t][kc] = __builtin_bit_cast(
+              vec8, __builtin_shufflevector(lds_read_tr(base + o0), lds_read_tr(base + o1), 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+
+    auto tile = [&](int t_idx, const char* sb) {
+      const int i0 = t_idx * 32;   // first query of the tile
+      vec8 qa[L::NC], tqa[L::NC];
+      read_rows(sb, 0, qa);
+      read_rows(sb, 1, tqa);
+      f32x16 s = f32x16{}, sd = f32x16{}, x = f32x16{}, dm = f32x16{};
+#pragma unroll
+      for (int c = 0; c < L::NC; ++c) {
+        s = T::mfma(qa[c], kB[c], s);
+        sd = T::mfma(tqa[c], kB[c], sd);
+        sd = T::mfma(qa[c], tkB[c], sd);
+      }
+      vec8 ga[L::NC], tga[L::NC];
+      read_rows(sb, 2, ga);
+      read_rows(sb, 3, tga);
+#pragma unroll
+      for (int c = 0; c < L::NC; ++c) {
+        x = T::mfma(ga[c], vB[c], x);
+        x = T::mfma(tga[c], tvB[c], x);
+        dm = T::mfma(tga[c], vB[c], dm);
+      }
+      // masks: element (query i, key kj); hidden entries get score -inf
+      if constexpr (MASK != JVPATTN_MASK_NONE) {
+        constexpr int es = MASK == JVPATTN_MASK_BOOL ? 1 : 2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
+          const int off = (qrow * int(a.msq) + kj) * es;
+          if constexpr (MASK == JVPATTN_MASK_BOOL) {
+            if (__builtin_amdgcn_raw_buffer_load_b8(mr, off, 0, 0) == 0) s[r] = -INFINITY;
+          } else {
+            const float m = T::widen(__builtin_amdgcn_raw_buffer_load_b16(mr, off, 0, 0));
+            s[r] = POW2 ? s[r] + m : fmaf(s[r], a.scale, m);
+          }
+        }
+      }
+      if (needs_rowmask(t_idx)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
+          bool hide = qrow >= a.Nq || kj >= a.Nk;
+          if constexpr (CAUSAL) hide = hide || kj > qrow;
+          if (hide) s[r] = -INFINITY;
+        }
+      }
+      // statistics of the 16 rows: for group g, rows 8g + 4*hlf + 0..3 (one 16-byte LDS read each)
+      const char* st = sb + L::STAGE_BYTES;
+      vec8 pB[2], pdB[2], sB[2], sdB[2];
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        const int o0 = 16 * kc * L::ROW + vofs0[t], o1 = 16 * kc * L::ROW + vofs1[t];
-        x[t][kc] = __builtin_bit_cast(
-            vec8, __builtin_shufflevector(lds_read_tr(base + o0), lds_read_tr(base + o1), 0, 1, 2, 3, 4, 5, 6, 7));
+        uint32_t wp[4], wpd[4], ws[4], wsd[4];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const int g = 2 * kc + gg;
+          const int roff = (8 * g + 4 * hlf) * 4;
+          const f32x4 ng = lds_load<f32x4>(st, WS_NEGL * 128 + roff);
+          const f32x4 tl = lds_load<f32x4>(st, WS_TLSE * 128 + roff);
+          const f32x4 rr = lds_load<f32x4>(st, WS_R * 128 + roff);
+          const f32x4 dl = lds_load<f32x4>(st, WS_DEL * 128 + roff);
+          Cot c[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            c[e] = cotangents(s[r], sd[r], x[r], dm[r], a.cx, us, ng[e], tl[e], rr[e], dl[e]);
+          }
+          wp[2 * gg] = T::pack2(c[0].p, c[1].p);
+          wp[2 * gg + 1] = T::pack2(c[2].p, c[3].p);
+          wpd[2 * gg] = T::pack2(c[0].pd, c[1].pd);
+          wpd[2 * gg + 1] = T::pack2(c[2].pd, c[3].pd);
+          ws[2 * gg] = T::pack2(c[0].sbar, c[1].sbar);
+          ws[2 * gg + 1] = T::pack2(c[2].sbar, c[3].sbar);
+          wsd[2 * gg] = T::pack2(c[0].sdbar, c[1].sdbar);
+          wsd[2 * gg + 1] = T::pack2(c[2].sdbar, c[3].sdbar);
+        }
+        pB[kc] = __builtin_bit_cast(vec8, uint4{wp[0], wp[1], wp[2], wp[3]});
+        pdB[kc] = __builtin_bit_cast(vec8, uint4{wpd[0], wpd[1], wpd[2], wpd[3]});
+        sB[kc] = __builtin_bit_cast(vec8, uint4{ws[0], ws[1], ws[2], ws[3]});
+        sdB[kc] = __builtin_bit_cast(vec8, uint4{wsd[0], wsd[1], wsd[2], wsd[3]});
       }
-  };
+      {
+        vec8 qt[L::NT][2], tqt[L::NT][2];
+        read_tr(sb, 0, qt);
+        read_tr(sb, 1, tqt);
+#pragma unroll
+        for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc) {
+            accK[t] = T::mfma(qt[t][kc], sB[kc], accK[t]);
+            accK[t] = T::mfma(tqt[t][kc], sdB[kc], accK[t]);
+            accTK[t] = T::mfma(qt[t][kc], sdB[kc], accTK[t]);
+          }
+      }
+      {
+        vec8 gt[L::NT][2], tgt[L::NT][2];
+        read_tr(sb, 2, gt);
+        read_tr(sb, 3, tgt);
+#pragma unroll
+        for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc) {
+            accV[t] = T::mfma(gt[t][kc], pB[kc], accV[t]);
+            accV[t] = T::mfma(tgt[t][kc], pdB[kc], accV[t]);
+            accTV[t] = T::mfma(tgt[t][kc], pB[kc], accTV[t]);
+          }
+      }
+    };
 
-  auto tile = [&](int t_idx, const char* sb) {
-    const int i0 = t_idx * 32;   // first query of the tile
-    vec8 qa[L::NC], tqa[L::NC];
-    read_rows(sb, 0, qa);
-    read_rows(sb, 1, tqa);
-    f32x16 s = f32x16{}, sd = f32x16{}, x = f32x16{}, dm = f32x16{};
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      s = T::mfma(qa[c], kB[c], s);
-      sd = T::mfma(tqa[c], kB[c], sd);
-      sd = T::mfma(qa[c], tkB[c], sd);
+    constexpr int TILE_VMEM = L::TILE_VMEM + 1;   // four tensors + this wave's statistic
+    // All waves issue the same count (the statistic load is exec-masked, not skipped).
+    // Before step t's wait, tiles t and t+1 may be in flight (t+2 is issued after it).
+    auto wait_tile = [&](int j) {
+      if (j + 1 < n_qt) wait_vmcnt<TILE_VMEM>();
+      else wait_vmcnt<0>();
+    };
+    const int n_steps = n_qt - t_begin;
+    if (n_steps > 0) issue_tile(t_begin, stage0);
+    if (n_steps > 1) issue_tile(t_begin + 1, stage1);
+    auto step = [&](int t_idx, const char* cur, char* dma) {
+      wait_tile(t_idx);
+      ring_barrier();
+      if (t_idx + 2 < n_qt) issue_tile(t_idx + 2, dma);
+      if (t_idx >= first) tile(t_idx, cur);
+    };
+    for (int i = 0; i < n_steps; i += 4) {
+      const int t_idx = t_begin + i;
+      step(t_idx, stage0, stage2);
+      if (i + 1 < n_steps) step(t_idx + 1, stage1, stage3);
+      if (i + 2 < n_steps) step(t_idx + 2, stage2, stage0);
+      if (i + 3 < n_steps) step(t_idx + 3, stage3, stage1);
     }
-    vec8 ga[L::NC], tga[L::NC];
-    read_rows(sb, 2, ga);
-    read_rows(sb, 3, tga);
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      x = T::mfma(ga[c], vB[c], x);
-      x = T::mfma(tga[c], tvB[c], x);
-      dm = T::mfma(tga[c], vB[c], dm);
-    }
-    // masks: element (query i, key kj); hidden entries get score -inf
-    if constexpr (MASK != JVPATTN_MASK_NONE) {
-      constexpr int es = MASK == JVPATTN_MASK_BOOL ? 1 : 2;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
-        const int off = (qrow * int(a.msq) + kj) * es;
-        if constexpr (MASK == JVPATTN_MASK_BOOL) {
-          if (__builtin_amdgcn_raw_buffer_load_b8(mr, off, 0, 0) == 0) s[r] = -INFINITY;
-        } else {
-          const float m = T::widen(__builtin_amdgcn_raw_buffer_load_b16(mr, off, 0, 0));
-          s[r] = POW2 ? s[r] + m : fmaf(s[r], a.scale, m);
-        }
-      }
-    }
-    if (needs_rowmask(t_idx)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
-        bool hide = qrow >= a.Nq || kj >= a.Nk;
-        if constexpr (CAUSAL) hide = hide || kj > qrow;
-        if (hide) s[r] = -INFINITY;
-      }
-    }
-    // statistics of the 16 rows: for group g, rows 8g + 4*hlf + 0..3 (one 16-byte LDS read each)
-    const char* st = sb + L::STAGE_BYTES;
-    vec8 pB[2], pdB[2], sB[2], sdB[2];
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      uint32_t wp[4], wpd[4], ws[4], wsd[4];
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int g = 2 * kc + gg;
-        const int roff = (8 * g + 4 * hlf) * 4;
-        const f32x4 ng = lds_load<f32x4>(st, WS_NEGL * 128 + roff);
-        const f32x4 tl = lds_load<f32x4>(st, WS_TLSE * 128 + roff);
-        const f32x4 rr = lds_load<f32x4>(st, WS_R * 128 + roff);
-        const f32x4 dl = lds_load<f32x4>(st, WS_DEL * 128 + roff);
-        Cot c[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          c[e] = cotangents(s[r], sd[r], x[r], dm[r], a.cx, us, ng[e], tl[e], rr[e], dl[e]);
-        }
-        wp[2 * gg] = T::pack2(c[0].p, c[1].p);
-        wp[2 * gg + 1] = T::pack2(c[2].p, c[3].p);
-        wpd[2 * gg] = T::pack2(c[0].pd, c[1].pd);
-        wpd[2 * gg + 1] = T::pack2(c[2].pd, c[3].pd);
-        ws[2 * gg] = T::pack2(c[0].sbar, c[1].sbar);
-        ws[2 * gg + 1] = T::pack2(c[2].sbar, c[3].sbar);
-        wsd[2 * gg] = T::pack2(c[0].sdbar, c[1].sdbar);
-        wsd[2 * gg + 1] = T::pack2(c[2].sdbar, c[3].sdbar);
-      }
-      pB[kc] = __builtin_bit_cast(vec8, uint4{wp[0], wp[1], wp[2], wp[3]});
-      pdB[kc] = __builtin_bit_cast(vec8, uint4{wpd[0], wpd[1], wpd[2], wpd[3]});
-      sB[kc] = __builtin_bit_cast(vec8, uint4{ws[0], ws[1], ws[2], ws[3]});
-      sdB[kc] = __builtin_bit_cast(vec8, uint4{wsd[0], wsd[1], wsd[2], wsd[3]});
-    }
-    {
-      vec8 qt[L::NT][2], tqt[L::NT][2];
-      read_tr(sb, 0, qt);
-      read_tr(sb, 1, tqt);
-#pragma unroll
-      for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          accK[t] = T::mfma(qt[t][kc], sB[kc], accK[t]);
-          accK[t] = T::mfma(tqt[t][kc], sdB[kc], accK[t]);
-          accTK[t] = T::mfma(qt[t][kc], sdB[kc], accTK[t]);
-        }
-    }
-    {
-      vec8 gt[L::NT][2], tgt[L::NT][2];
-      read_tr(sb, 2, gt);
-      read_tr(sb, 3, tgt);
-#pragma unroll
-      for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          accV[t] = T::mfma(gt[t][kc], pB[kc], accV[t]);
-          accV[t] = T::mfma(tgt[t][kc], pdB[kc], accV[t]);
-          accTV[t] = T::mfma(tgt[t][kc], pB[kc], accTV[t]);
-        }
-    }
-  };
-
-  constexpr int TILE_VMEM = L::TILE_VMEM + 1;   // four tensors + this wave's statistic
-  // All waves issue the same count (the statistic load is exec-masked, not skipped).
-  // Before step t's wait, tiles t and t+1 may be in flight (t+2 is issued after it).
-  auto wait_tile = [&](int j) {
-    if (j + 1 < n_qt) wait_vmcnt<TILE_VMEM>();
-    else wait_vmcnt<0>();
-  };
-  const int n_steps = n_qt - t_begin;
-  if (n_steps > 0) issue_tile(t_begin, stage0);
-  if (n_steps > 1) issue_tile(t_begin + 1, stage1);
-  auto step = [&](int t_idx, const char* cur, char* dma) {
-    wait_tile(t_idx);
-    ring_barrier();
-    if (t_idx + 2 < n_qt) issue_tile(t_idx + 2, dma);
-    if (t_idx >= first) tile(t_idx, cur);
-  };
-  for (int i = 0; i < n_steps; i += 4) {
-    const int t_idx = t_begin + i;
-    step(t_idx, stage0, stage2);
-    if (i + 1 < n_steps) step(t_idx + 1, stage1, stage3);
-    if (i + 2 < n_steps) step(t_idx + 2, stage2, stage0);
-    if (i + 3 < n_steps) step(t_idx + 3, stage3, stage1);
+    // every wave is done reading the ring before the next head's loads land in it
+    if (g + 1 < a.grp) ring_barrier();
   }
 
   if (kj < a.Nk) {
-    const int64_t base = int64_t(bh) * a.Nk * D + int64_t(kj) * D;
+    const int64_t base = int64_t(bhk) * a.Nk * D + int64_t(kj) * D;
     uint16_t* dk = static_cast<uint16_t*>(a.dk) + base;
     uint16_t* dtk = static_cast<uint16_t*>(a.dtk) + base;
     uint16_t* dv = static_cast<uint16_t*>(a.dv) + base;
@@ -786,12 +797,12 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
 template <typename T, int MASK, bool CAUSAL, bool POW2>
 hipError_t launch_tiles(BwdArgs a, hipStream_t s) {
   const int64_t nkb = (a.Nk + kBBlk - 1) / kBBlk, nqb = (a.Nq + kBBlk - 1) / kBBlk;
-  if (nkb * a.BH > INT32_MAX || nqb * a.BH > INT32_MAX) return hipErrorInvalidValue;
-  if (nkb > 0 && a.BH > 0) {
+  if (nkb * a.BHK > INT32_MAX || nqb * a.BH > INT32_MAX) return hipErrorInvalidValue;
+  if (nkb > 0 && a.BHK > 0) {
     BwdArgs ak = a;
     ak.n_blk = static_cast<int>(nkb);
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, MASK, CAUSAL, POW2>), dim3(unsigned(nkb * a.BH)), dim3(kBThreads), 0, s,
-                       ak);
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, MASK, CAUSAL, POW2>), dim3(unsigned(nkb * a.BHK)), dim3(kBThreads), 0,
+                       s, ak);
   }
   if (nqb > 0 && a.BH > 0) {
     BwdArgs aq = a;
@@ -841,6 +852,8 @@ extern "C" int jvpattn_bwd(const jvpattn_params* p, const void* q, const void* k
   a.ws = static_cast<float*>(workspace);
   a.ws_stride = bwd_workspace_bytes(sz.rows_q) / 16;   // bytes of one array / 4
   a.H = p->H; a.Nq = p->Nq; a.Nk = p->Nk; a.BH = p->B * p->H;
+  a.grp = sz.group;
+  a.BHK = p->B * sz.hkv;
   a.n_blk = 0;
   a.msb = p->mask_stride_b; a.msh = p->mask_stride_h; a.msq = p->mask_stride_q;
   a.scale = p->scale;

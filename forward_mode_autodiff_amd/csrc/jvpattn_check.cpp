@@ -54,9 +54,14 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
   const int es = elem_bytes(p->dtype);
   if (es == 0) return JVPATTN_ERR_DTYPE;
   if (p->B < 0 || p->H < 0 || p->Nq < 0 || p->Nk < 0 || p->d <= 0) return JVPATTN_ERR_SHAPE;
+  // grouped key/value heads: Hkv divides H (0 stands for H)
+  const int hkv = p->Hkv == 0 ? p->H : p->Hkv;
+  if (hkv < 0 || hkv > p->H || (hkv == 0) != (p->H == 0) || (hkv > 0 && p->H % hkv != 0))
+    return JVPATTN_ERR_SHAPE;
 
-  int64_t bh, rows_q, rows_k, n_q, n_k, bytes_q, bytes_k, bytes_stats;
-  if (!mul_ok(p->B, p->H, &bh) || !mul_ok(bh, p->Nq, &rows_q) || !mul_ok(bh, p->Nk, &rows_k) ||
+  int64_t bh, bhk, rows_q, rows_k, n_q, n_k, bytes_q, bytes_k, bytes_stats;
+  if (!mul_ok(p->B, p->H, &bh) || !mul_ok(p->B, hkv, &bhk) || !mul_ok(bh, p->Nq, &rows_q) ||
+      !mul_ok(bhk, p->Nk, &rows_k) ||
       !mul_ok(rows_q, p->d, &n_q) || !mul_ok(rows_k, p->d, &n_k) || !mul_ok(n_q, es, &bytes_q) ||
       !mul_ok(n_k, es, &bytes_k) || !mul_ok(rows_q, 4, &bytes_stats))
     return JVPATTN_ERR_SHAPE;
@@ -133,6 +138,8 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
     sizes->rows_q = rows_q;
     sizes->rows_k = rows_k;
     sizes->elem_bytes = es;
+    sizes->hkv = hkv;
+    sizes->group = hkv > 0 ? p->H / hkv : 1;
   }
   return JVPATTN_OK;
 }
@@ -230,7 +237,8 @@ extern "C" const char* jvpattn_strerror(int code) {
   switch (code) {
     case JVPATTN_OK: return "ok";
     case JVPATTN_ERR_NULL: return "a required pointer is NULL";
-    case JVPATTN_ERR_SHAPE: return "invalid shape (negative size, d <= 0, or size overflow)";
+    case JVPATTN_ERR_SHAPE:
+      return "invalid shape (negative size, d <= 0, Hkv not a divisor of H, or size overflow)";
     case JVPATTN_ERR_DTYPE: return "unknown dtype";
     case JVPATTN_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128)";
     case JVPATTN_ERR_MASK: return "invalid mask (unknown kind, pointer/kind mismatch, or bad strides)";

@@ -58,6 +58,8 @@ struct FwdArgs {
   float* lse;
   float* tlse;
   int H, Nq, Nk, BH;
+  int grp;            // query heads per key/value head (grouped-query attention; 1 = one each)
+  int xgrp;           // grp when whole key/value groups can be kept on one XCD, else 1
   int n_qblk;
   int mask_vec;       // 1: mask rows may be read 4 keys at a time
   int64_t msb, msh, msq;
@@ -65,6 +67,24 @@ struct FwdArgs {
   float cx;           // score units -> log2 units
   float thr;          // lazy-rescale threshold in score units
 };
+
+// Workgroup -> (query block, query head). Query blocks run heaviest first
+// (causal work grows with the block index); heads are innermost, so with B*H
+// a multiple of 8 every block of a head lands on one XCD (workgroups are
+// dealt round-robin over the 8 XCDs) and its key/value tiles stay in that
+// XCD's L2. With grouped key/value heads (xgrp > 1, B*H a multiple of
+// 8*xgrp) the heads are permuted so that all query heads sharing a
+// key/value head also land on one XCD.
+__device__ inline void block_coords(const FwdArgs& a, int& qb, int& bh) {
+  qb = a.n_qblk - 1 - int(blockIdx.x) / a.BH;
+  const int r = int(blockIdx.x) % a.BH;
+  if (a.xgrp > 1) {
+    const int xcd = r & 7, j = r >> 3;
+    bh = ((j / a.xgrp) * 8 + xcd) * a.xgrp + j % a.xgrp;
+  } else {
+    bh = r;
+  }
+}
 
 // Per-row softmax state for one lane (both lanes of a query column hold the same m).
 struct RowState {
@@ -159,9 +179,8 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, char* stage0, char*
   const int c32 = lane & 31;
   const int hlf = lane >> 5;
 
-  // Heaviest query blocks first (causal work grows with the block index).
-  const int qb = a.n_qblk - 1 - int(blockIdx.x) / a.BH;
-  const int bh = int(blockIdx.x) % a.BH;
+  int qb, bh;
+  block_coords(a, qb, bh);
   const int b = bh / a.H, h = bh % a.H;
   const int q0 = qb * kBM;
   const int qw0 = q0 + 32 * wave;
@@ -169,7 +188,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, char* stage0, char*
   const bool wave_live = qw0 < a.Nq;
 
   const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;   // byte offsets of this head
-  const int64_t khead = int64_t(bh) * a.Nk * L::ROW;
+  const int64_t khead = int64_t(bh / a.grp) * a.Nk * L::ROW;   // the key/value head it reads
   const char* qp = static_cast<const char*>(a.q) + qhead;
   const char* kp = static_cast<const char*>(a.k) + khead;
   const char* vp = static_cast<const char*>(a.v) + khead;
@@ -614,8 +633,8 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   const int c32 = lane & 31;
   const int hlf = lane >> 5;
 
-  const int qb = a.n_qblk - 1 - int(blockIdx.x) / a.BH;
-  const int bh = int(blockIdx.x) % a.BH;
+  int qb, bh;
+  block_coords(a, qb, bh);
   const int b = bh / a.H, h = bh % a.H;
   const int q0 = qb * kPPBM;
   const int qw0 = q0 + 32 * wave;
@@ -623,7 +642,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   const bool wave_live = qw0 < a.Nq;
 
   const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
-  const int64_t khead = int64_t(bh) * a.Nk * L::ROW;
+  const int64_t khead = int64_t(bh / a.grp) * a.Nk * L::ROW;   // the key/value head it reads
   const char* qp = static_cast<const char*>(a.q) + qhead;
   const char* kp = static_cast<const char*>(a.k) + khead;
   const char* vp = static_cast<const char*>(a.v) + khead;
@@ -932,8 +951,8 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
   const int c32 = lane & 31;
   const int hlf = lane >> 5;
 
-  const int qb = a.n_qblk - 1 - int(blockIdx.x) / a.BH;
-  const int bh = int(blockIdx.x) % a.BH;
+  int qb, bh;
+  block_coords(a, qb, bh);
   const int b = bh / a.H, h = bh % a.H;
   const int q0 = qb * kBM;
   const int qw0 = q0 + 32 * wave;
@@ -942,10 +961,11 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
 
   const float* qp = static_cast<const float*>(a.q) + int64_t(bh) * a.Nq * D;
   const float* tqp = a.tq ? static_cast<const float*>(a.tq) + int64_t(bh) * a.Nq * D : nullptr;
-  const float* kp = static_cast<const float*>(a.k) + int64_t(bh) * a.Nk * D;
-  const float* vp = static_cast<const float*>(a.v) + int64_t(bh) * a.Nk * D;
-  const float* tkp = a.tk ? static_cast<const float*>(a.tk) + int64_t(bh) * a.Nk * D : nullptr;
-  const float* tvp = a.tv ? static_cast<const float*>(a.tv) + int64_t(bh) * a.Nk * D : nullptr;
+  const int64_t khead = int64_t(bh / a.grp) * a.Nk * D;   // the key/value head it reads
+  const float* kp = static_cast<const float*>(a.k) + khead;
+  const float* vp = static_cast<const float*>(a.v) + khead;
+  const float* tkp = a.tk ? static_cast<const float*>(a.tk) + khead : nullptr;
+  const float* tvp = a.tv ? static_cast<const float*>(a.tv) + khead : nullptr;
 
   float qB[D / 2], tqB[D / 2];
   {
@@ -1163,6 +1183,8 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
   a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv; a.mask = mask;
   a.o = o; a.to = to; a.lse = lse; a.tlse = tlse;
   a.H = p->H; a.Nq = p->Nq; a.Nk = p->Nk; a.BH = p->B * p->H;
+  a.grp = sz.group;
+  a.xgrp = (sz.group > 1 && a.BH % (8 * sz.group) == 0) ? sz.group : 1;
   a.n_qblk = (p->Nq + kBM - 1) / kBM;
   a.msb = p->mask_stride_b; a.msh = p->mask_stride_h; a.msq = p->mask_stride_q;
   a.scale = p->scale;

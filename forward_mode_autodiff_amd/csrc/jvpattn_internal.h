@@ -10,8 +10,10 @@ namespace jvpattn {
 
 struct FwdSizes {
   int64_t rows_q = 0;   // B*H*Nq
-  int64_t rows_k = 0;   // B*H*Nk
+  int64_t rows_k = 0;   // B*Hkv*Nk
   int elem_bytes = 0;
+  int hkv = 0;          // key/value heads (params->Hkv, 0 read as H)
+  int group = 1;        // query heads per key/value head, H / hkv
 };
 
 int elem_bytes(int dtype);

@@ -38,11 +38,16 @@ class Workload:
     Nk: int | None = None          # None -> N (self-attention)
     mask_heads: int = 1            # mask head extent (1 = broadcast over heads)
     keep: float = 0.9              # Bernoulli keep rate of the boolean mask
+    Hkv: int | None = None         # key/value heads (None -> H; fewer = grouped-query attention)
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
     def nk(self) -> int:
         return self.N if self.Nk is None else self.Nk
+
+    @property
+    def hkv(self) -> int:
+        return self.H if self.Hkv is None else self.Hkv
 
     @property
     def sigma(self) -> float:
@@ -64,13 +69,15 @@ MASKED_ADD = Workload("masked_additive", B=2, H=8, N=1024, d=64, dtype="f16", ma
                       seed=2)
 WIDE = Workload("wide", B=256, H=8, N=512, d=128, dtype="bf16", seed=3)
 HVP = Workload("hvp", B=4, H=16, N=2048, d=64, dtype="bf16", causal=True, seed=4)
+# The HVP shape with grouped key/value heads (4 query heads per K/V head).
+HVP_GQA = Workload("hvp_gqa4", B=4, H=16, N=2048, d=64, dtype="bf16", causal=True, seed=6, Hkv=4)
 
 
 def make_inputs(w: Workload, cotangents: bool = False) -> dict:
     """Draw the inputs of workload ``w`` on the CPU.
 
     Returns a dict of CPU tensors: q, k, v, tq, tk, tv in the working dtype
-    ([B,H,N,d] / [B,H,Nk,d]); ``mask`` ([B, mask_heads, N, Nk]; uint8 with 1 =
+    ([B,H,N,d] / [B,Hkv,Nk,d]); ``mask`` ([B, mask_heads, N, Nk]; uint8 with 1 =
     attend for "bool", the working dtype for "additive"; None for "none");
     and when ``cotangents`` is set, ``do`` and ``dto`` (i.i.d. N(0,1)).
     """
@@ -78,7 +85,7 @@ def make_inputs(w: Workload, cotangents: bool = False) -> dict:
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed)
     qshape = (w.B, w.H, w.N, w.d)
-    kshape = (w.B, w.H, w.nk, w.d)
+    kshape = (w.B, w.hkv, w.nk, w.d)
     out = {}
     for name, shape in (("q", qshape), ("k", kshape), ("v", kshape),
                         ("tq", qshape), ("tk", kshape), ("tv", kshape)):

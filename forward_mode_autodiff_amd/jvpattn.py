@@ -33,7 +33,7 @@ class jvpattn_params(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("mask_stride_b", ctypes.c_int64), ("mask_stride_h", ctypes.c_int64),
         ("mask_stride_q", ctypes.c_int64),
-        ("scale", ctypes.c_float),
+        ("scale", ctypes.c_float), ("Hkv", ctypes.c_int32),
     ]
 
 
@@ -98,6 +98,7 @@ def make_params(q, k, mask=None, causal=False, scale=None) -> tuple:
         raise TypeError(f"unsupported dtype {q.dtype}")
     p = jvpattn_params()
     p.B, p.H, p.Nq, p.Nk, p.d = B, H, Nq, Nk, d
+    p.Hkv = k.shape[1]   # key/value heads; fewer than H means grouped-query attention
     p.dtype = _DTYPE_CODE[q.dtype]
     p.causal = 1 if causal else 0
     p.scale = float(1.0 / math.sqrt(d) if scale is None else scale)
@@ -131,8 +132,9 @@ def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, sca
                 want_tlse=True, out=None):
     """O, dO, lse, tlse = jvpattn_fwd(q, k, v, tq, tk, tv, mask, causal, scale).
 
-    q, tq: [B,H,Nq,d]; k, v, tk, tv: [B,H,Nk,d] on the GPU, one dtype
-    (float32 / float16 / bfloat16), contiguous. Tangents may be None (zero).
+    q, tq: [B,H,Nq,d]; k, v, tk, tv: [B,Hkv,Nk,d] on the GPU, one dtype
+    (float32 / float16 / bfloat16), contiguous; Hkv divides H (query head h
+    reads key/value head h // (H // Hkv)). Tangents may be None (zero).
     mask: None, a bool/uint8 tensor (True = attend) or an additive tensor of
     q's dtype, broadcastable to [B,H,Nq,Nk]. Work is queued on torch's
     current stream. ``out`` optionally supplies (o, to, lse, tlse) buffers.

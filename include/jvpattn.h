@@ -60,8 +60,9 @@ typedef enum {
 enum {
   JVPATTN_OK = 0,
   JVPATTN_ERR_NULL = -1,     /* a required pointer is NULL */
-  JVPATTN_ERR_SHAPE = -2,    /* B, H, Nq, Nk < 0, a size overflows int64, B*H > INT32_MAX, or one
-                                head of q or k (N*d*element size) exceeds 2 GiB */
+  JVPATTN_ERR_SHAPE = -2,    /* B, H, Nq, Nk < 0, Hkv < 0 or not a divisor of H, a size overflows
+                                int64, B*H > INT32_MAX, or one head of q or k (N*d*element size)
+                                exceeds 2 GiB */
   JVPATTN_ERR_DTYPE = -3,    /* dtype not one of jvpattn_dtype */
   JVPATTN_ERR_HEADDIM = -4,  /* d not supported (supported: 64, 128) */
   JVPATTN_ERR_MASK = -5,     /* mask_kind unknown, mask NULL/non-NULL mismatch, negative strides,
@@ -87,6 +88,11 @@ typedef struct {
    * mask_kind is NONE. */
   int64_t mask_stride_b, mask_stride_h, mask_stride_q;
   float scale;           /* multiplies Q K^T and dQ K^T + Q dK^T; finite and > 0 (SDPA default 1/sqrt(d)) */
+  /* Heads of k, v, tk, tv (grouped-query attention, as SDPA's enable_gqa):
+   * query head h reads key/value head h / (H / Hkv), so H must be a multiple
+   * of Hkv; Hkv = 1 is multi-query attention. 0 is read as H (one key/value
+   * head per query head). */
+  int32_t Hkv;
 } jvpattn_params;
 
 /* Host-only validation of a jvpattn_fwd call: the same checks jvpattn_fwd
@@ -101,7 +107,7 @@ int jvpattn_check_fwd(const jvpattn_params* params,
 
 /* The forward pass with tangents.
  *   q, tq, o, to : [B, H, Nq, d] contiguous, element type params->dtype
- *   k, v, tk, tv : [B, H, Nk, d] contiguous
+ *   k, v, tk, tv : [B, Hkv, Nk, d] contiguous (Hkv = H unless grouped)
  *   tq, tk, tv   : may each be NULL, meaning a zero tangent
  *   mask         : NULL iff mask_kind == NONE; layout given by the strides
  *   lse, tlse    : [B, H, Nq] float32; tlse may be NULL (not written)
@@ -135,7 +141,8 @@ int jvpattn_fwd(const jvpattn_params* params,
  *   o, to, lse, tlse : what jvpattn_fwd returned for them (all four required)
  *   go, gto          : [B, H, Nq, d], the element type; either may be NULL,
  *                      meaning a zero cotangent
- *   dq, dtq          : [B, H, Nq, d] outputs; dk, dv, dtk, dtv: [B, H, Nk, d];
+ *   dq, dtq          : [B, H, Nq, d] outputs; dk, dv, dtk, dtv: [B, Hkv, Nk, d]
+ *                      (with grouped heads, each sums over its H / Hkv query heads);
  *                      dtq, dtk, dtv may be NULL (not written), e.g. for the
  *                      plain attention backward with gto = NULL
  *   workspace        : device memory of at least

@@ -43,6 +43,7 @@ def test_params_struct_layout():
     assert ctypes.sizeof(J.jvpattn_params) == 64
     assert J.jvpattn_params.mask_stride_b.offset == 32
     assert J.jvpattn_params.scale.offset == 56
+    assert J.jvpattn_params.Hkv.offset == 60
 
 
 @needs_lib
@@ -108,6 +109,21 @@ def test_check_accepts_valid_calls():
 
 
 @needs_lib
+def test_check_grouped_kv_heads():
+    # Hkv = 0 stands for H; a divisor of H shrinks k, v, tk, tv to B*Hkv heads
+    for hkv in (0, 1, 2, 3, 6):
+        p = good_params(H=6, Hkv=hkv)
+        assert call(p, ptrs(p)) == 0
+    # the K/V spans are B*Hkv heads: lse may sit right after a shrunk k (no false alias) ...
+    p = good_params(H=6, Hkv=2)
+    P = ptrs(p)
+    nk = p.B * 2 * p.Nk * p.d * 2
+    assert call(p, P, lse=P["k"] + nk) == 0
+    # ... and an overlap inside the shrunk span is still caught
+    assert call(p, P, lse=P["k"] + nk - 256) == -8
+
+
+@needs_lib
 @pytest.mark.parametrize("case,code", [
     ("params_null", -1), ("q_null", -1), ("o_null", -1), ("to_null", -1), ("lse_null", -1), ("k_null", -1),
     ("neg_B", -2), ("neg_Nk", -2), ("d_zero", -2), ("overflow", -2),
@@ -116,6 +132,7 @@ def test_check_accepts_valid_calls():
     ("q_misaligned", -6), ("tv_misaligned", -6), ("lse_misaligned", -6), ("mask_misaligned", -6),
     ("scale_nan", -7), ("scale_inf", -7), ("scale_zero", -7), ("scale_neg", -7),
     ("o_is_q", -8), ("to_overlaps_v", -8), ("lse_overlaps_tlse", -8), ("o_overlaps_mask", -8),
+    ("hkv_not_divisor", -2), ("hkv_above_h", -2), ("hkv_negative", -2),
 ])
 def test_check_rejects(case, code):
     p = good_params()
@@ -169,6 +186,10 @@ def test_check_rejects(case, code):
         over["to"] = P["v"] + 256
     elif case == "lse_overlaps_tlse":
         over["tlse"] = P["lse"] + 64
+    elif case.startswith("hkv_"):
+        p.H = 6
+        P = ptrs(p)
+        p.Hkv = {"not_divisor": 4, "above_h": 12, "negative": -2}[case[4:]]
     elif case == "o_overlaps_mask":
         p.mask_kind, p.mask_stride_q, p.mask_stride_b = J.JVPATTN_MASK_BOOL, 90, 9000
         over["o"] = P["mask"]

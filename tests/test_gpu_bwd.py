@@ -64,40 +64,49 @@ def term_magnitudes(x, w, tangents, scale, heads=None):
     z = lambda n, like: f64(x[n]) if n in tangents else np.zeros_like(like)
     tq, tk, tv = z("tq", q), z("tk", k), z("tv", v)
     B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    Hkv, Nk = k.shape[1], k.shape[2]
+    grp = H // Hkv
     sc = 1.0 / np.sqrt(d) if scale is None else scale
     mask = None
     if x["mask"] is not None:
         mask = f64(x["mask"]) if w.mask_kind == "additive" else x["mask"].numpy()
     M = {n: 0.0 for n in NAMES}
+    kside = {}   # (b, key/value head) -> summed magnitudes over the query heads that read it
     for b in range(B):
         for h in (range(H) if heads is None else heads):
+            kh = h // grp
+            k_, v_, tk_, tv_ = k[b, kh], v[b, kh], tk[b, kh], tv[b, kh]
             bias = _head_bias(mask, w.mask_kind, b, h, Nq, Nk, w.causal, np.arange(Nq))
-            S = sc * q[b, h] @ k[b, h].T + bias
+            S = sc * q[b, h] @ k_.T + bias
             P = np.zeros_like(S)
             live = ~np.all(np.isneginf(S), axis=1)
             if live.any():
                 e = np.exp(S[live] - S[live].max(1, keepdims=True))
                 P[live] = e / e.sum(1, keepdims=True)
-            Sd = sc * (tq[b, h] @ k[b, h].T + q[b, h] @ tk[b, h].T)
+            Sd = sc * (tq[b, h] @ k_.T + q[b, h] @ tk_.T)
             t = (P * Sd).sum(1, keepdims=True)
             aG, aGd = np.abs(g[b, h]), np.abs(gd[b, h])
-            aX = aG @ np.abs(v[b, h]).T + aGd @ np.abs(tv[b, h]).T
-            aD = aGd @ np.abs(v[b, h]).T
-            o = P @ v[b, h]
-            to = (P * (Sd - t)) @ v[b, h] + P @ tv[b, h]
+            aX = aG @ np.abs(v_).T + aGd @ np.abs(tv_).T
+            aD = aGd @ np.abs(v_).T
+            o = P @ v_
+            to = (P * (Sd - t)) @ v_ + P @ tv_
             r = np.abs((gd[b, h] * o).sum(1, keepdims=True))
             dl = np.abs((g[b, h] * o).sum(1, keepdims=True)) + np.abs((gd[b, h] * to).sum(1, keepdims=True)) \
                 + np.abs(t) * r
             aS = P * (aX + aD * np.abs(Sd - t) + r * np.abs(Sd) + dl)
             aSd = P * (aD + r)
-            aK, aTK, aQ, aTQ = np.abs(k[b, h]), np.abs(tk[b, h]), np.abs(q[b, h]), np.abs(tq[b, h])
+            aK, aTK, aQ, aTQ = np.abs(k_), np.abs(tk_), np.abs(q[b, h]), np.abs(tq[b, h])
             upd = {"dq": sc * (aS @ aK + aSd @ aTK), "dtq": sc * aSd @ aK,
                    "dk": sc * (aS.T @ aQ + aSd.T @ aTQ), "dtk": sc * aSd.T @ aQ,
                    "dv": P.T @ aG + np.abs(P * (Sd - t)).T @ aGd, "dtv": P.T @ aGd}
             for n, a in upd.items():
-                if a.size:
+                if n in ("dk", "dtk", "dv", "dtv"):
+                    kside[(b, kh, n)] = kside.get((b, kh, n), 0.0) + a
+                elif a.size:
                     M[n] = max(M[n], float(a.max()))
+    for (_, _, n), a in kside.items():
+        if np.size(a):
+            M[n] = max(M[n], float(np.max(a)))
     return M
 
 
@@ -237,3 +246,17 @@ def test_null_cotangent_and_skipped_outputs():
     assert g[3] is None and g[4] is None and g[5] is None
     for a, b in zip(g[:3], full[:3]):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("H,Hkv,causal,dtype", [(4, 2, False, "bf16"), (6, 3, True, "f16"), (4, 1, True, "bf16")],
+                         ids=["gqa2", "gqa2-causal-f16", "mqa-causal"])
+def test_grouped_kv_heads(H, Hkv, causal, dtype):
+    w = I.Workload(f"gqa_bwd_{H}_{Hkv}", B=2, H=H, Hkv=Hkv, N=200, d=64, dtype=dtype, causal=causal, std=1.0,
+                   seed=21)
+    check(w)
+
+
+def test_grouped_kv_heads_bool_mask_ragged():
+    w = I.Workload("gqa_bwd_bool", B=1, H=4, Hkv=2, N=157, d=64, dtype="bf16", mask_kind="bool", mask_heads=4,
+                   keep=0.6, std=1.0, seed=22)
+    check(w)

@@ -62,11 +62,13 @@ def oracle_run(x, mask_kind, causal, scale=None, tangents=("tq", "tk", "tv"), he
                                       scale=scale)
         return {"o": o, "to": to, "lse": lse, "tlse": tlse}
     out = {n: [] for n in ("o", "to", "lse", "tlse")}
+    grp = q.shape[1] // k.shape[1]
     for b, h in heads:
         sl = lambda a: None if a is None else a[b:b + 1, h:h + 1]
+        slk = lambda a: None if a is None else a[b:b + 1, h // grp:h // grp + 1]   # the K/V head h reads
         m = None if mask is None else mask[b:b + 1, (h if mask.shape[1] > 1 else 0):][:, :1]
-        r = oracle_fwd(sl(q)[:, :, rows], sl(k), sl(v), None if tq is None else sl(tq)[:, :, rows], sl(tk),
-                       sl(tv), mask=m, mask_kind=mask_kind, causal=causal, scale=scale, q_pos=rows)
+        r = oracle_fwd(sl(q)[:, :, rows], slk(k), slk(v), None if tq is None else sl(tq)[:, :, rows], slk(tk),
+                       slk(tv), mask=m, mask_kind=mask_kind, causal=causal, scale=scale, q_pos=rows)
         for n, a in zip(("o", "to", "lse", "tlse"), r):
             out[n].append(a[0, 0])
     return {n: np.stack(a) for n, a in out.items()}
@@ -350,3 +352,45 @@ def test_errors_raise_and_write_nothing():
         jvpattn_fwd(q, q, q, scale=-1.0, out=out)
     torch.cuda.synchronize()
     assert torch.all(out[0] == 7.0) and torch.all(out[2] == 7.0)
+
+
+# ------------------------------------------------ grouped key/value heads
+
+GQA_CASES = [
+    # B*H = 32 is a multiple of 8 x 4: the launcher keeps each K/V group on one XCD
+    I.Workload("gqa4_bf16_causal", B=4, H=8, Hkv=2, N=300, d=64, dtype="bf16", causal=True, std=1.0, seed=11),
+    I.Workload("gqa2_f16", B=1, H=6, Hkv=3, N=200, d=64, dtype="f16", std=1.0, seed=12),
+    I.Workload("mqa_bf16_bool", B=2, H=4, Hkv=1, N=160, d=64, dtype="bf16", mask_kind="bool", mask_heads=4,
+               keep=0.7, std=1.0, seed=13),
+    I.Workload("gqa2_d128_bf16_causal", B=1, H=4, Hkv=2, N=200, d=128, dtype="bf16", causal=True, std=1.0,
+               seed=14),
+    I.Workload("gqa2_f32", B=1, H=4, Hkv=2, N=100, d=64, dtype="f32", std=1.0, seed=15),
+]
+
+
+@pytest.mark.parametrize("w", GQA_CASES, ids=lambda w: w.name)
+def test_grouped_kv_heads(w, kernel):
+    check(w)
+
+
+def test_grouped_kv_heads_hvp_shape_sampled(kernel):
+    """B=4, H=16, Hkv=4, N=2048, d=64, bf16, causal: all heads launched, sampled heads x rows checked."""
+    w = I.HVP_GQA
+    x = I.make_inputs(w)
+    got = gpu_run(x, True)
+    heads = [(0, 0), (0, 3), (1, 6), (3, 15)]
+    rows = sampled_rows(w.N, 40, 7)
+    ref = oracle_run(x, "none", True, heads=heads, rows=rows)
+    assert_parity(pick(got, heads, rows), ref, w.dtype, w.name, spec_spread=True)
+
+
+def test_grouped_kv_heads_match_repeated_heads(kernel):
+    """Sharing one K/V head gives bit-identical results to passing it once per query head."""
+    w = I.Workload("gqa_vs_mha", B=2, H=8, Hkv=2, N=256, d=64, dtype="bf16", causal=True, std=1.0, seed=16)
+    x = to_dev(I.make_inputs(w))
+    rep = {n: x[n].repeat_interleave(4, dim=1).contiguous() for n in ("k", "v", "tk", "tv")}
+    a = jvpattn_fwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], causal=True)
+    b = jvpattn_fwd(x["q"], rep["k"], rep["v"], x["tq"], rep["tk"], rep["tv"], causal=True)
+    torch.cuda.synchronize()
+    for u, t in zip(a, b):
+        assert torch.equal(u, t)
