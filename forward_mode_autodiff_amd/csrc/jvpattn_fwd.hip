@@ -60,6 +60,7 @@ struct FwdArgs {
   int H, Nq, Nk, BH;
   int grp;            // query heads per key/value head (grouped-query attention; 1 = one each)
   int xgrp;           // grp when whole key/value groups can be kept on one XCD, else 1
+  int head_major;     // 1: the query blocks of a head run back to back on one XCD (large grids)
   int n_qblk;
   int mask_vec;       // 1: mask rows may be read 4 keys at a time
   int64_t msb, msh, msq;
@@ -68,16 +69,31 @@ struct FwdArgs {
   float thr;          // lazy-rescale threshold in score units
 };
 
-// Workgroup -> (query block, query head). Query blocks run heaviest first
-// (causal work grows with the block index); heads are innermost, so with B*H
-// a multiple of 8 every block of a head lands on one XCD (workgroups are
-// dealt round-robin over the 8 XCDs) and its key/value tiles stay in that
-// XCD's L2. With grouped key/value heads (xgrp > 1, B*H a multiple of
-// 8*xgrp) the heads are permuted so that all query heads sharing a
-// key/value head also land on one XCD.
+// Workgroup -> (query block, query head). Workgroups are dealt round-robin
+// over the 8 XCDs, each with its own L2, so the mapping decides which blocks
+// share cached key/value tiles.
+//  - Default (the grid fits on the chip in a few rounds): query blocks run
+//    heaviest first (causal work grows with the block index) and heads are
+//    innermost; with B*H a multiple of 8 every block of a head lands on one
+//    XCD, and all of them are resident together.
+//  - head_major (grids many times the chip, B*H a multiple of 8): XCD x
+//    runs heads x, x+8, ... one after the other, each head's query blocks
+//    back to back (heaviest first), so they stream the same key/value tiles
+//    at the same time and all but the first read them from L2 rather than
+//    HBM.
+// With grouped key/value heads (xgrp > 1, B*H a multiple of 8*xgrp) the heads
+// are then permuted so that all query heads sharing a key/value head also
+// land on one XCD.
 __device__ inline void block_coords(const FwdArgs& a, int& qb, int& bh) {
-  qb = a.n_qblk - 1 - int(blockIdx.x) / a.BH;
-  const int r = int(blockIdx.x) % a.BH;
+  int r;
+  if (a.head_major) {
+    const int x = int(blockIdx.x), slot = x >> 3;
+    qb = a.n_qblk - 1 - slot % a.n_qblk;
+    r = (slot / a.n_qblk) * 8 + (x & 7);
+  } else {
+    qb = a.n_qblk - 1 - int(blockIdx.x) / a.BH;
+    r = int(blockIdx.x) % a.BH;
+  }
   if (a.xgrp > 1) {
     const int xcd = r & 7, j = r >> 3;
     bh = ((j / a.xgrp) * 8 + xcd) * a.xgrp + j % a.xgrp;
@@ -1222,6 +1238,15 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
   a.n_qblk = static_cast<int>(pp ? n256 : n128);
   const int64_t blocks = int64_t(a.n_qblk) * a.BH;
   if (blocks > INT32_MAX) return JVPATTN_ERR_SHAPE;
+  // Head-major order once the grid is several times what the chip holds at
+  // once (at most 2 workgroups per CU x 256 CUs), so a head's query blocks
+  // would otherwise run far apart in time and each re-read its key/value
+  // tiles from HBM. JVPATTN_FWD_ORDER=qb|head forces one (testing).
+  a.head_major = a.n_qblk > 1 && a.BH % 8 == 0 && blocks >= 4 * 512;
+  if (const char* env = std::getenv("JVPATTN_FWD_ORDER")) {
+    if (std::strcmp(env, "qb") == 0) a.head_major = 0;
+    if (std::strcmp(env, "head") == 0) a.head_major = a.n_qblk > 1 && a.BH % 8 == 0;
+  }
   const dim3 grid(static_cast<unsigned>(blocks));
   hipStream_t s = static_cast<hipStream_t>(stream);
 

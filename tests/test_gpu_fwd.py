@@ -394,3 +394,30 @@ def test_grouped_kv_heads_match_repeated_heads(kernel):
     torch.cuda.synchronize()
     for u, t in zip(a, b):
         assert torch.equal(u, t)
+
+
+# ------------------------------------------------ workgroup order
+
+@pytest.mark.parametrize("order", ["qb", "head"])
+@pytest.mark.parametrize("w", [
+    I.Workload("order_bf16_causal", B=2, H=8, N=700, d=64, dtype="bf16", causal=True, std=1.0, seed=17),
+    I.Workload("order_gqa_f16", B=4, H=8, Hkv=2, N=520, d=64, dtype="f16", std=1.0, seed=18),
+    I.Workload("order_d128_bf16", B=1, H=8, N=300, d=128, dtype="bf16", std=1.0, seed=19),
+], ids=lambda w: w.name)
+def test_block_order(w, order, kernel, monkeypatch):
+    """Both workgroup orders (heaviest query block first over all heads, or head-major per XCD) give
+    the oracle's results on every kernel."""
+    monkeypatch.setenv("JVPATTN_FWD_ORDER", order)
+    check(w)
+
+
+def test_wide_query_block_major_sampled(monkeypatch):
+    """B=256, H=8, N=512, d=128, bf16 in the order its grid does not take by default: sampled heads."""
+    monkeypatch.setenv("JVPATTN_FWD_ORDER", "qb")
+    w = I.WIDE
+    x = I.make_inputs(w)
+    got = gpu_run(x, False)
+    heads = [(0, 0), (17, 3), (128, 7), (255, 5)]
+    rows = sampled_rows(w.N, 40, 9)
+    ref = oracle_run(x, "none", False, heads=heads, rows=rows)
+    assert_parity(pick(got, heads, rows), ref, w.dtype, w.name, spec_spread=True)
