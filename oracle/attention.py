@@ -78,7 +78,8 @@ def _head_bias(mask, mask_kind, b, h, nq_rows, Nk, causal, q_pos):
     M = np.zeros((nq_rows, Nk), dtype=np.float64)
     if mask_kind != MASK_NONE:
         mb = mask[b if mask.shape[0] > 1 else 0, h if mask.shape[1] > 1 else 0]
-        rows = mb[q_pos, :]
+        # a mask with one row is shared by every query (a key-padding mask), as in SDPA's broadcasting
+        rows = mb[np.zeros_like(q_pos) if mb.shape[0] == 1 else q_pos, :]
         if mask_kind == MASK_BOOL:
             M = np.where(rows != 0, 0.0, -np.inf)
         elif mask_kind == MASK_ADDITIVE:
@@ -137,7 +138,8 @@ def oracle_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, mask_kind=MASK_NON
 
     q, k, v, tq, tk, tv: array-likes (values already rounded to the working
         dtype; they are widened to float64 here). A tangent given as None is zero.
-    mask: [Bm, Hm, Nq_full, Nk] with Bm in {1, B}, Hm in {1, H}; uint8/bool for
+    mask: [Bm, Hm, Nm, Nk] with Bm in {1, B}, Hm in {1, H}, Nm in {1, Nq_full} (one
+        row: shared by every query, e.g. a key-padding mask); uint8/bool for
         ``mask_kind="bool"``, float for ``"additive"``; None for ``"none"``.
     causal: key j visible to query i iff j <= i.
     scale: multiplies Q K^T and the score tangent; default 1/sqrt(d).

@@ -79,6 +79,25 @@ def test_matches_torch_sdpa_bool_mask():
     np.testing.assert_allclose(to, rto, rtol=0, atol=1e-11)
 
 
+@pytest.mark.parametrize("kind", ["bool", "additive"])
+def test_matches_torch_sdpa_key_padding_mask(kind):
+    # a [B, 1, 1, Nk] mask broadcasts over heads and query rows (SDPA broadcasting)
+    rng = np.random.default_rng(45)
+    args = make(rng, Nq=6, Nk=10)
+    keep = np.ones((2, 1, 1, 10), dtype=bool)
+    keep[0, ..., 7:] = False     # right padding
+    keep[1, ..., :3] = False     # left padding
+    if kind == "bool":
+        m, mk = keep, keep.astype(np.uint8)
+    else:
+        m = np.where(keep, rng.standard_normal(keep.shape), -np.inf)
+        mk = m
+    o, to, _, _ = oracle_fwd(*args, mask=mk, mask_kind=kind)
+    ro, rto = torch_sdpa_jvp(*args, attn_mask=m)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(to, rto, rtol=0, atol=1e-11)
+
+
 def test_matches_torch_sdpa_additive_mask_per_head():
     rng = np.random.default_rng(2)
     args = make(rng, Nq=6, Nk=8, d=4)
