@@ -30,6 +30,7 @@ def workloads():
     return {
         "hvp": I.HVP,
         "hvp_gqa4": I.HVP_GQA,
+        "hvp_keypad": I.HVP_PAD,
         "hvp_full": I.Workload("hvp_full", B=4, H=16, N=2048, d=64, dtype="bf16", causal=False, seed=4),
         "seq2048": I.seq(2048, False),
         "seq2048_causal": I.seq(2048, True),
@@ -49,7 +50,8 @@ def algorithmic_bytes(w):
     mask = 0
     if w.mask_kind != "none":
         mes = 1 if w.mask_kind == "bool" else es
-        mask = w.B * w.mask_heads * w.N * w.nk * mes
+        rows = w.N if w.mask_layout == "bernoulli" else 1   # key masks: one row shared by all queries
+        mask = w.B * w.mask_heads * rows * w.nk * mes
     return w.B * w.H * per_q_head + w.B * w.hkv * per_kv_head + mask
 
 

@@ -61,6 +61,7 @@ struct FwdArgs {
   int grp;            // query heads per key/value head (grouped-query attention; 1 = one each)
   int xgrp;           // grp when whole key/value groups can be kept on one XCD, else 1
   int head_major;     // 1: the query blocks of a head run back to back on one XCD (large grids)
+  int key_range;      // 1: the mask is shared by all query rows; skip 32-key tiles it hides entirely
   int n_qblk;
   int mask_vec;       // 1: mask rows may be read 4 keys at a time
   int64_t msb, msh, msq;
@@ -99,6 +100,51 @@ __device__ inline void block_coords(const FwdArgs& a, int& qb, int& bh) {
     bh = ((j / a.xgrp) * 8 + xcd) * a.xgrp + j % a.xgrp;
   } else {
     bh = r;
+  }
+}
+
+// Tiles of 32 keys [t_lo, t_hi) that hold every key a row of this head may
+// see. With a mask shared by all query rows (row stride 0: a key-padding mask
+// [B,1,1,Nk] or [B,H,1,Nk]) the workgroup scans that one row and the loops
+// start and end at the first and last tile with a visible key, so tiles the
+// mask hides entirely are never loaded or multiplied (a row with no visible
+// key at all gets no tile). Otherwise every tile: [0, ceil(Nk/32)). Every
+// thread of the workgroup takes part; the result is uniform. ES: bytes per
+// mask element (additive masks hide a key with -inf).
+template <typename T, int MASK, int ES>
+__device__ inline void key_tiles(const FwdArgs& a, Rsrc mr, int* red, int& t_lo, int& t_hi) {
+  t_lo = 0;
+  t_hi = (a.Nk + 31) >> 5;
+  if constexpr (MASK != JVPATTN_MASK_NONE) {
+    if (!a.key_range) return;
+    if (threadIdx.x == 0) {
+      red[0] = INT32_MAX;
+      red[1] = -1;
+    }
+    __syncthreads();
+    int lo = INT32_MAX, hi = -1;
+    for (int j = threadIdx.x; j < a.Nk; j += blockDim.x) {
+      bool vis;
+      if constexpr (MASK == JVPATTN_MASK_BOOL) {
+        vis = __builtin_amdgcn_raw_buffer_load_b8(mr, j, 0, 0) != 0;
+      } else if constexpr (ES == 2) {
+        vis = T::widen(__builtin_amdgcn_raw_buffer_load_b16(mr, 2 * j, 0, 0)) != -INFINITY;
+      } else {
+        vis = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mr, 4 * j, 0, 0)) != -INFINITY;
+      }
+      if (vis) {
+        lo = min(lo, j);
+        hi = max(hi, j);
+      }
+    }
+    if (hi >= 0) {
+      atomicMin(&red[0], lo);
+      atomicMax(&red[1], hi);
+    }
+    __syncthreads();
+    hi = red[1];
+    t_lo = hi < 0 ? 0 : red[0] >> 5;
+    t_hi = hi < 0 ? 0 : (hi >> 5) + 1;
   }
 }
 
@@ -184,8 +230,9 @@ __device__ inline bool softmax_block(f32x16& s, f32x16& sd, RowState& st, float 
 // xst: m, moff, l, mu per lane), which combines the two online-softmax states -- rescaling
 // each to the larger reference -- and stores. Twice the waves per row block.
 template <typename T, int D, int MASK, bool CAUSAL, bool POW2, int SPLIT, int G>
-__device__ __forceinline__ void fwd16_body(const FwdArgs& a, char* stage0, char* stage1, char* stage2, char* stage3,
-                                           char* x0, char* x1, char* x2, char* x3, float4* xst) {
+__device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi, char* stage0, char* stage1,
+                                           char* stage2, char* stage3, char* x0, char* x1, char* x2, char* x3,
+                                           float4* xst) {
   using L = Tile16<D>;
   using vec8 = typename T::vec8;
 
@@ -242,16 +289,18 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, char* stage0, char*
   RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
   const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
 
-  const int kv_end = CAUSAL ? min(a.Nk, q0 + kBM) : a.Nk;
-  const int n_all = (kv_end + L::BN - 1) / L::BN;
-  // This group's key blocks kb .. kb+n_tiles-1; both groups run n_loop iterations
-  // (one barrier each), the shorter one idling through the extra ones.
+  const int kv_end = min(CAUSAL ? min(a.Nk, q0 + kBM) : a.Nk, 32 * t_hi);
+  const int n_all = max(0, (kv_end + L::BN - 1) / L::BN - t_lo);
+  // This group's key blocks kb .. kb+n_tiles-1 (absolute); both groups run
+  // n_loop iterations (one barrier each), the shorter one idling through the
+  // extra ones.
   const int n_first = SPLIT == 2 ? (n_all + 1) / 2 : n_all;
-  const int kb = G == 1 ? n_first : 0;
+  const int kb = t_lo + (G == 1 ? n_first : 0);
   const int n_tiles = G == 1 ? n_all - n_first : n_first;
   const int n_loop = n_first;
-  // Last block this wave needs (the causal diagonal block, or the last tile), local; -1 if none.
-  const int last_all = !wave_live ? -1 : (CAUSAL ? min(n_all - 1, qw0 >> 5) : n_all - 1);
+  // Last block this wave needs (the causal diagonal block, or the last tile), absolute, then
+  // local to this group; -1 if none.
+  const int last_all = !wave_live ? -1 : (CAUSAL ? min(t_lo + n_all - 1, qw0 >> 5) : t_lo + n_all - 1);
   const int last = last_all < kb ? -1 : min(last_all - kb, n_tiles - 1);
   auto needs_keymask = [&](int k) {
     return (CAUSAL && (kb + k) * 32 + 31 > qw0) || ((kb + k) * 32 + 32 > a.Nk);
@@ -593,8 +642,18 @@ __global__ __launch_bounds__(kThreads * SPLIT, D == 64 ? 2 : 1) void fwd16_kerne
   __shared__ __attribute__((aligned(16))) char s1[L::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) char s2[L::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) char s3[L::STAGE_BYTES];
+  // the key tiles this head may see, found once by the whole workgroup
+  __shared__ int kred[2];
+  int t_lo, t_hi;
+  {
+    int qb, bh;
+    block_coords(a, qb, bh);
+    const Rsrc mr = mask_rsrc(a, bh / a.H, bh % a.H, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+    key_tiles<T, MASK, 2>(a, mr, kred, t_lo, t_hi);
+  }
   if constexpr (SPLIT == 1) {
-    fwd16_body<T, D, MASK, CAUSAL, POW2, 1, 0>(a, s0, s1, s2, s3, nullptr, nullptr, nullptr, nullptr, nullptr);
+    fwd16_body<T, D, MASK, CAUSAL, POW2, 1, 0>(a, t_lo, t_hi, s0, s1, s2, s3, nullptr, nullptr, nullptr, nullptr,
+                                               nullptr);
   } else {
     __shared__ __attribute__((aligned(16))) char s4[L::STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) char s5[L::STAGE_BYTES];
@@ -602,9 +661,9 @@ __global__ __launch_bounds__(kThreads * SPLIT, D == 64 ? 2 : 1) void fwd16_kerne
     __shared__ __attribute__((aligned(16))) char s7[L::STAGE_BYTES];
     __shared__ float4 xst[kThreads];
     if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 8) == 0)
-      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 0>(a, s0, s1, s2, s3, s4, s5, s6, s7, xst);
+      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 0>(a, t_lo, t_hi, s0, s1, s2, s3, s4, s5, s6, s7, xst);
     else
-      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 1>(a, s4, s5, s6, s7, s4, s5, s6, s7, xst);
+      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 1>(a, t_lo, t_hi, s4, s5, s6, s7, s4, s5, s6, s7, xst);
   }
 #endif
 }
@@ -693,11 +752,15 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   }
   RowState16 st{0.0f, 0.0f, 0.0f, false};
   const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+  __shared__ int kred[2];
+  int t0, t_hi;   // key tiles [t0, t_hi) may hold visible keys; loop tile k is absolute tile t0 + k
+  key_tiles<T, MASK, 2>(a, mr, kred, t0, t_hi);
 
-  const int kv_end = CAUSAL ? min(a.Nk, q0 + kPPBM) : a.Nk;
-  const int n_tiles = (kv_end + L::BN - 1) / L::BN;
-  const int last = !wave_live ? -1 : (CAUSAL ? min(n_tiles - 1, qw0 >> 5) : n_tiles - 1);
-  auto needs_keymask = [&](int k) { return (CAUSAL && k * 32 + 31 > qw0) || (k * 32 + 32 > a.Nk); };
+  const int kv_end = min(CAUSAL ? min(a.Nk, q0 + kPPBM) : a.Nk, 32 * t_hi);
+  const int n_tiles = max(0, (kv_end + L::BN - 1) / L::BN - t0);
+  const int last = !wave_live ? -1 : (CAUSAL ? min(n_tiles - 1, (qw0 >> 5) - t0) : n_tiles - 1);
+  auto kpos = [&](int k) { return (t0 + k) * 32; };   // first key of loop tile k
+  auto needs_keymask = [&](int k) { return (CAUSAL && kpos(k) + 31 > qw0) || (kpos(k) + 32 > a.Nk); };
 
   // Tile loads (group B only): one 16-byte slot per tensor per thread.
   const int tb = tid - 4 * 64;                     // 0..255 in group B
@@ -707,7 +770,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   const Rsrc rk = make_rsrc(kp, kbytes), rv = make_rsrc(vp, kbytes);
   const Rsrc rtk = make_rsrc(tkp, a.tk ? kbytes : 0), rtv = make_rsrc(tvp, a.tv ? kbytes : 0);
   auto issue_tile = [&](int j, char* stage) {
-    const int off = j * L::TENSOR_BYTES + dl_off;
+    const int off = (t0 + j) * L::TENSOR_BYTES + dl_off;
     const int slot = (wave - 4) * 64 * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot), 16,
                                              off, 0, 0, 0);
@@ -786,7 +849,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   // operands of block k (stage stv) are read while the weights are packed.
   auto settle = [&](int k, const char* stv) {
     mask_apply<T, MASK, POW2>(sn, mk, a.scale);
-    if (needs_keymask(k)) hide_keys<CAUSAL>(sn, a.Nk, qi, k * 32, hlf);
+    if (needs_keymask(k)) hide_keys<CAUSAL>(sn, a.Nk, qi, kpos(k), hlf);
     float e[16], alpha;
     if (block_exp16<T>(sn, st, a.cx, e, alpha)) {
 #pragma unroll
@@ -828,7 +891,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   auto vector_phase = [&](int i, const char* stn) {
     if (i + 1 > last) return;
     settle(i + 1, stn);
-    if (i + 2 <= last) mask_load<MASK>(mk, a, mr, qi, (i + 2) * 32, hlf);
+    if (i + 2 <= last) mask_load<MASK>(mk, a, mr, qi, kpos(i + 2), hlf);
   };
   // Group B's wait for its loads of tile j; tiles issued after j may stay in flight.
   auto wait_tile = [&](int j) {
@@ -859,9 +922,9 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   if (0 <= last) {
     read_k(stage0);
     mma_s();
-    mask_load<MASK>(mk, a, mr, qi, 0, hlf);
+    mask_load<MASK>(mk, a, mr, qi, kpos(0), hlf);
     settle(0, stage0);
-    if (1 <= last) mask_load<MASK>(mk, a, mr, qi, 32, hlf);
+    if (1 <= last) mask_load<MASK>(mk, a, mr, qi, kpos(1), hlf);
   }
   // Operands of the first matrix phase have arrived (states the loop's entry
   // as free of pending LDS reads, as every later iteration is).
@@ -1007,16 +1070,19 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
   }
   RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
   const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 4);
+  __shared__ int kred[2];
+  int t0, t_hi;   // key tiles [t0, t_hi) may hold visible keys
+  key_tiles<F16, MASK, 4>(a, mr, kred, t0, t_hi);
 
-  const int kv_end = CAUSAL ? min(a.Nk, q0 + kBM) : a.Nk;
-  const int n_tiles = (kv_end + L::BN - 1) / L::BN;
+  const int kv_end = min(CAUSAL ? min(a.Nk, q0 + kBM) : a.Nk, 32 * t_hi);
+  const int n_tiles = max(0, (kv_end + L::BN - 1) / L::BN - t0);
   char* sk = smem32;
   char* stk = smem32 + L::TENSOR_BYTES;
   char* sv = smem32 + 2 * L::TENSOR_BYTES;
   char* stv = smem32 + 3 * L::TENSOR_BYTES;
 
   for (int j = 0; j < n_tiles; ++j) {
-    const int kbase = j * L::BN;
+    const int kbase = (t0 + j) * L::BN;
     // Global -> LDS. K rows as granules; V transposed element by element.
     for (int gi = tid; gi < L::BN * L::GR; gi += kThreads) {
       const int row = gi / L::GR, g = gi % L::GR;
@@ -1243,6 +1309,12 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
   // would otherwise run far apart in time and each re-read its key/value
   // tiles from HBM. JVPATTN_FWD_ORDER=qb|head forces one (testing).
   a.head_major = a.n_qblk > 1 && a.BH % 8 == 0 && blocks >= 4 * 512;
+  // A mask with row stride 0 is the same for every query row: scan it once per
+  // workgroup and skip the key tiles it hides entirely.
+  // JVPATTN_FWD_KEYRANGE=0 scans nothing and runs every tile (testing).
+  a.key_range = mask != nullptr && p->mask_stride_q == 0;
+  if (const char* env = std::getenv("JVPATTN_FWD_KEYRANGE"))
+    if (std::strcmp(env, "0") == 0) a.key_range = 0;
   if (const char* env = std::getenv("JVPATTN_FWD_ORDER")) {
     if (std::strcmp(env, "qb") == 0) a.head_major = 0;
     if (std::strcmp(env, "head") == 0) a.head_major = a.n_qblk > 1 && a.BH % 8 == 0;

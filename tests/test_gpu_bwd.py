@@ -260,3 +260,10 @@ def test_grouped_kv_heads_bool_mask_ragged():
     w = I.Workload("gqa_bwd_bool", B=1, H=4, Hkv=2, N=157, d=64, dtype="bf16", mask_kind="bool", mask_heads=4,
                    keep=0.6, std=1.0, seed=22)
     check(w)
+
+
+@pytest.mark.parametrize("layout,kind", [("pad_right", "bool"), ("window", "additive")])
+def test_key_masks(layout, kind):
+    w = I.Workload(f"keymask_bwd_{layout}", B=3, H=2, N=180, d=64, dtype="bf16", mask_kind=kind, mask_layout=layout,
+                   std=1.0, seed=23)
+    check(w)

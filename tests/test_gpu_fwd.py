@@ -421,3 +421,53 @@ def test_wide_query_block_major_sampled(monkeypatch):
     rows = sampled_rows(w.N, 40, 9)
     ref = oracle_run(x, "none", False, heads=heads, rows=rows)
     assert_parity(pick(got, heads, rows), ref, w.dtype, w.name, spec_spread=True)
+
+
+# ------------------------------------------------ key masks shared by all query rows
+
+KEY_MASKS = [
+    ("pad_right", "bool", False, "bf16"),
+    ("pad_left", "bool", True, "f16"),
+    ("window", "additive", False, "bf16"),
+    ("window", "bool", True, "bf16"),
+    ("pad_right", "additive", True, "f16"),
+]
+
+
+@pytest.mark.parametrize("skip", ["1", "0"], ids=["skip", "noskip"])
+@pytest.mark.parametrize("layout,kind,causal,dtype", KEY_MASKS, ids=lambda v: str(v))
+def test_key_masks(layout, kind, causal, dtype, skip, kernel, monkeypatch):
+    """[B,1,1,Nk] masks: the kernels skip the key tiles outside the visible range (or, forced, run them
+    all); results as the oracle's."""
+    monkeypatch.setenv("JVPATTN_FWD_KEYRANGE", skip)
+    w = I.Workload(f"keymask_{layout}_{kind}", B=4, H=2, N=300, d=64, dtype=dtype, causal=causal, mask_kind=kind,
+                   mask_layout=layout, std=1.0, seed=30)
+    check(w)
+
+
+@pytest.mark.parametrize("w", [
+    # one batch hides every key (rows give O = dO = 0, lse = -inf), one keeps 5, one all, one 33
+    I.Workload("keypad_lengths_bf16", B=4, H=2, N=300, d=64, dtype="bf16", mask_kind="bool",
+               mask_layout="pad_right", std=1.0, seed=31, extra={"lengths": [0, 5, 300, 33]}),
+    I.Workload("keymask_per_head_f16", B=2, H=4, N=257, d=64, dtype="f16", mask_kind="additive", mask_heads=4,
+               mask_layout="window", std=1.0, seed=32),
+    I.Workload("keymask_d128_bf16_causal", B=2, H=2, N=200, d=128, dtype="bf16", causal=True, mask_kind="bool",
+               mask_layout="pad_left", std=1.0, seed=33),
+    I.Workload("keymask_f32", B=2, H=2, N=150, d=64, dtype="f32", mask_kind="additive", mask_layout="window",
+               std=1.0, seed=34),
+    I.Workload("keymask_f32_bool_lengths", B=3, H=1, N=100, d=64, dtype="f32", mask_kind="bool",
+               mask_layout="pad_left", std=1.0, seed=35, extra={"lengths": [0, 64, 7]}),
+], ids=lambda w: w.name)
+def test_key_mask_edges(w, kernel):
+    check(w)
+
+
+def test_key_padding_hvp_shape_sampled(kernel):
+    """B=4, H=16, N=2048, d=64, bf16, right-padded key mask (2048/1536/1024/512 valid keys): sampled rows."""
+    w = I.HVP_PAD
+    x = I.make_inputs(w)
+    got = gpu_run(x, False)
+    heads = [(0, 0), (1, 5), (2, 9), (3, 15)]
+    rows = sampled_rows(w.N, 40, 10)
+    ref = oracle_run(x, "bool", False, heads=heads, rows=rows)
+    assert_parity(pick(got, heads, rows), ref, w.dtype, w.name, spec_spread=True)
