@@ -229,14 +229,22 @@ __device__ inline bool softmax_block(f32x16& s, f32x16& sd, RowState& st, float 
 // group 0 through LDS (x0..x3: group 1's stages, one 16 KB stage per wave;
 // xst: m, moff, l, mu per lane), which combines the two online-softmax states -- rescaling
 // each to the larger reference -- and stores. Twice the waves per row block.
-template <typename T, int D, int MASK, bool CAUSAL, bool POW2, int SPLIT, int G>
+//
+// WV = waves per group (32 query rows each): 4, or 2 for grids too small to
+// give every CU a 128-row block -- then 64-row blocks, twice the workgroups.
+template <typename T, int D, int MASK, bool CAUSAL, bool POW2, int SPLIT, int G, int WV>
 __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi, char* stage0, char* stage1,
                                            char* stage2, char* stage3, char* x0, char* x1, char* x2, char* x3,
                                            float4* xst) {
   using L = Tile16<D>;
   using vec8 = typename T::vec8;
+  constexpr int GT = 64 * WV;                           // threads per group
+  constexpr int BMG = 32 * WV;                          // query rows per workgroup
+  constexpr int LOADS = L::TENSOR_BYTES / (16 * GT);    // 16-byte tile loads per thread per tensor
+  constexpr int TILE_VMEM = 4 * LOADS;                  // direct loads per thread per tile
+  static_assert(LOADS * 16 * GT == L::TENSOR_BYTES, "tile must split evenly over the group");
 
-  const int tid = threadIdx.x & (kThreads - 1);   // thread within the group
+  const int tid = threadIdx.x & (GT - 1);   // thread within the group
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave within the group
   const int c32 = lane & 31;
@@ -245,7 +253,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   int qb, bh;
   block_coords(a, qb, bh);
   const int b = bh / a.H, h = bh % a.H;
-  const int q0 = qb * kBM;
+  const int q0 = qb * BMG;
   const int qw0 = q0 + 32 * wave;
   const int qi = qw0 + c32;
   const bool wave_live = qw0 < a.Nq;
@@ -289,7 +297,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
   const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
 
-  const int kv_end = min(CAUSAL ? min(a.Nk, q0 + kBM) : a.Nk, 32 * t_hi);
+  const int kv_end = min(CAUSAL ? min(a.Nk, q0 + BMG) : a.Nk, 32 * t_hi);
   const int n_all = max(0, (kv_end + L::BN - 1) / L::BN - t_lo);
   // This group's key blocks kb .. kb+n_tiles-1 (absolute); both groups run
   // n_loop iterations (one barrier each), the shorter one idling through the
@@ -307,10 +315,10 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   };
 
   // Direct-load slots of this thread (byte offset inside a tile, same for all four tensors).
-  int dl_off[L::LOADS];
+  int dl_off[LOADS];
 #pragma unroll
-  for (int i = 0; i < L::LOADS; ++i) {
-    const int p = i * kThreads + tid;
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = i * GT + tid;
     const int row = p / L::GR, pg = p % L::GR;
     dl_off[i] = row * L::ROW + ((pg ^ swz(row)) << 4);
   }
@@ -321,9 +329,9 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   const Rsrc rtk = make_rsrc(tkp, a.tk ? kbytes : 0), rtv = make_rsrc(tvp, a.tv ? kbytes : 0);
   auto issue_tile = [&](int j, char* stage) {
 #pragma unroll
-    for (int i = 0; i < L::LOADS; ++i) {
+    for (int i = 0; i < LOADS; ++i) {
       const int off = (kb + j) * L::TENSOR_BYTES + dl_off[i];
-      const int slot = (i * kThreads + wave * 64) * 16;
+      const int slot = (i * GT + wave * 64) * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
                                                16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -459,7 +467,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   auto fast = [&](int k, const char* cur, const char* nxt, char* dma, f32x16& sc, f32x16& sdc, f32x16& sn,
                   f32x16& sdn) {
     // Tile k+1 was fetched two iterations ago; tile k+2 may still be in flight.
-    if (k + 2 < n_tiles) wait_vmcnt<L::TILE_VMEM>();
+    if (k + 2 < n_tiles) wait_vmcnt<TILE_VMEM>();
     else wait_vmcnt<0>();
     ring_barrier();   // tile k+1 visible to all; every wave is done with tile k-1 (the `dma` stage)
     MaskVals<MASK> mk1;
@@ -497,8 +505,8 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   if (n_tiles > 0) issue_tile(0, stage0);
   if (n_tiles > 1) issue_tile(1, stage1);
   if (n_tiles > 2) issue_tile(2, stage2);
-  if (n_tiles > 2) wait_vmcnt<2 * L::TILE_VMEM>();
-  else if (n_tiles > 1) wait_vmcnt<L::TILE_VMEM>();
+  if (n_tiles > 2) wait_vmcnt<2 * TILE_VMEM>();
+  else if (n_tiles > 1) wait_vmcnt<TILE_VMEM>();
   else wait_vmcnt<0>();
   ring_barrier();
   bool ready = false;   // sA holds the current block's settled scores
@@ -535,7 +543,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     return i == 0 ? stage0 : i == 1 ? stage1 : i == 2 ? stage2 : stage3;
   };
   for (k = kfast; k < n_loop; ++k) {
-    if (k + 2 < n_tiles) wait_vmcnt<L::TILE_VMEM>();
+    if (k + 2 < n_tiles) wait_vmcnt<TILE_VMEM>();
     else wait_vmcnt<0>();
     ring_barrier();
     if (k + 3 < n_tiles) issue_tile(k + 3, stage_of(k + 3));
@@ -634,8 +642,8 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
 }
 
 // The kernel bodies use gfx950 builtins; the host pass only needs the launch stubs.
-template <typename T, int D, int MASK, bool CAUSAL, bool POW2, int SPLIT>
-__global__ __launch_bounds__(kThreads * SPLIT, D == 64 ? 2 : 1) void fwd16_kernel(FwdArgs a) {
+template <typename T, int D, int MASK, bool CAUSAL, bool POW2, int SPLIT, int WV>
+__global__ __launch_bounds__(64 * WV * SPLIT, (D == 64 && WV == 4) ? 2 : 1) void fwd16_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using L = Tile16<D>;
   __shared__ __attribute__((aligned(16))) char s0[L::STAGE_BYTES];
@@ -652,18 +660,18 @@ __global__ __launch_bounds__(kThreads * SPLIT, D == 64 ? 2 : 1) void fwd16_kerne
     key_tiles<T, MASK, 2>(a, mr, kred, t_lo, t_hi);
   }
   if constexpr (SPLIT == 1) {
-    fwd16_body<T, D, MASK, CAUSAL, POW2, 1, 0>(a, t_lo, t_hi, s0, s1, s2, s3, nullptr, nullptr, nullptr, nullptr,
-                                               nullptr);
+    fwd16_body<T, D, MASK, CAUSAL, POW2, 1, 0, WV>(a, t_lo, t_hi, s0, s1, s2, s3, nullptr, nullptr, nullptr,
+                                                   nullptr, nullptr);
   } else {
     __shared__ __attribute__((aligned(16))) char s4[L::STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) char s5[L::STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) char s6[L::STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) char s7[L::STAGE_BYTES];
     __shared__ float4 xst[kThreads];
-    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 8) == 0)
-      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 0>(a, t_lo, t_hi, s0, s1, s2, s3, s4, s5, s6, s7, xst);
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x / (64 * WV)) == 0)
+      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 0, WV>(a, t_lo, t_hi, s0, s1, s2, s3, s4, s5, s6, s7, xst);
     else
-      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 1>(a, t_lo, t_hi, s4, s5, s6, s7, s4, s5, s6, s7, xst);
+      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 1, WV>(a, t_lo, t_hi, s4, s5, s6, s7, s4, s5, s6, s7, xst);
   }
 #endif
 }
@@ -869,6 +877,10 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   // products run.
   auto matrix_phase = [&](int i, const char* stn) {
     if (i > last) return;
+    // This wave's matrix-core instructions go ahead of the vector work of the
+    // other wave on its SIMD (priority 2 against 0), so the matrix core does
+    // not wait for an issue slot.
+    __builtin_amdgcn_s_setprio(2);
     // On a wave's last block the score products are of no use (stn holds
     // some other tile, read harmlessly); issuing them anyway keeps the phase
     // one straight-line block the scheduler can interleave.
@@ -886,6 +898,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 6 * L::NT - 2 * L::NC, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 3 * L::NC, 0);
+    __builtin_amdgcn_s_setprio(0);
   };
   // Vector phase of iteration i: settle block i+1 (V / dV from stage stn).
   auto vector_phase = [&](int i, const char* stn) {
@@ -1210,30 +1223,34 @@ hipError_t launch_pp(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipSt
   return hipGetLastError();
 }
 
-// The 4-wave kernel for d = 64, whole key range (split = false) or halves (split = true).
+// The 4-wave kernel for d = 64: whole key range (split = 0), halves over two
+// groups of four waves (split = 1), or halves over two groups of two waves on
+// 64-row blocks (split = 2).
 template <typename T, int MASK, bool CAUSAL, bool POW2>
-void launch_d64(bool split, const FwdArgs& args, dim3 grid, hipStream_t stream) {
-  if (split)
-    hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 2>), grid, dim3(2 * kThreads), 0, stream, args);
+void launch_d64(int split, const FwdArgs& args, dim3 grid, hipStream_t stream) {
+  if (split == 2)
+    hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 2, 2>), grid, dim3(2 * 128), 0, stream, args);
+  else if (split == 1)
+    hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 2, 4>), grid, dim3(2 * kThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 1>), grid, dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 1, 4>), grid, dim3(kThreads), 0, stream, args);
 }
 
 template <int MASK, bool CAUSAL>
-hipError_t launch_typed(int dtype, int d, bool pow2, bool split, const FwdArgs& args, dim3 grid,
+hipError_t launch_typed(int dtype, int d, bool pow2, int split, const FwdArgs& args, dim3 grid,
                         hipStream_t stream) {
   const dim3 block(kThreads);
   if (dtype == JVPATTN_BF16) {
     if (pow2) {
       if (d == 64) launch_d64<BF16, MASK, CAUSAL, true>(split, args, grid, stream);
-      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, true, 1>), grid, block, 0, stream, args);
+      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, true, 1, 4>), grid, block, 0, stream, args);
     } else {
       if (d == 64) launch_d64<BF16, MASK, CAUSAL, false>(split, args, grid, stream);
-      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, false, 1>), grid, block, 0, stream, args);
+      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, false, 1, 4>), grid, block, 0, stream, args);
     }
   } else if (dtype == JVPATTN_F16) {
     if (d == 64) launch_d64<F16, MASK, CAUSAL, false>(split, args, grid, stream);
-    else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, false, 1>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, false, 1, 4>), grid, block, 0, stream, args);
   } else {
     if (d == 64) {
       hipLaunchKernelGGL((fwd32_kernel<64, MASK, CAUSAL>), grid, block, Tile32<64>::BUF_BYTES, stream, args);
@@ -1289,19 +1306,23 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
   // Kernel choice for 16-bit d = 64: the 8-wave ping-pong kernel (256 rows per
   // workgroup) when it still gives every CU a workgroup; else the 4-wave
   // kernel (128 rows), with the key range split between two groups of waves
-  // when it would have fewer than two workgroups per CU. Other types and d:
-  // the 4-wave kernel (float32: its own). JVPATTN_FWD_KERNEL=pp|wg4|split
-  // forces one (testing).
-  const int64_t n128 = (p->Nq + kBM - 1) / kBM, n256 = (p->Nq + kPPBM - 1) / kPPBM;
+  // when it would have fewer than two workgroups per CU, and on 64-row blocks
+  // (two groups of two waves) when even 128-row blocks leave CUs without one
+  // -- or, causal, fewer than two: there twice the blocks, heaviest first,
+  // even out the triangle. Other types and d: the 4-wave kernel (float32: its
+  // own). JVPATTN_FWD_KERNEL=pp|wg4|split|split64 forces one (testing).
+  const int64_t n64 = (p->Nq + 63) / 64, n128 = (p->Nq + kBM - 1) / kBM, n256 = (p->Nq + kPPBM - 1) / kPPBM;
   const bool d64_16 = p->d == 64 && p->dtype != JVPATTN_F32;
   bool pp = d64_16 && n256 * a.BH >= 256;
-  bool split = d64_16 && !pp && n128 * a.BH < 512;
+  const int64_t small = p->causal ? 512 : 256;
+  int split = !d64_16 || pp ? 0 : n128 * a.BH < small ? 2 : n128 * a.BH < 512 ? 1 : 0;
   if (const char* env = std::getenv("JVPATTN_FWD_KERNEL")) {
-    if (std::strcmp(env, "pp") == 0) pp = d64_16, split = false;
-    if (std::strcmp(env, "wg4") == 0) pp = false, split = false;
-    if (std::strcmp(env, "split") == 0) pp = false, split = d64_16;
+    if (std::strcmp(env, "pp") == 0) pp = d64_16, split = 0;
+    if (std::strcmp(env, "wg4") == 0) pp = false, split = 0;
+    if (std::strcmp(env, "split") == 0) pp = false, split = d64_16 ? 1 : 0;
+    if (std::strcmp(env, "split64") == 0) pp = false, split = d64_16 ? 2 : 0;
   }
-  a.n_qblk = static_cast<int>(pp ? n256 : n128);
+  a.n_qblk = static_cast<int>(pp ? n256 : split == 2 ? n64 : n128);
   const int64_t blocks = int64_t(a.n_qblk) * a.BH;
   if (blocks > INT32_MAX) return JVPATTN_ERR_SHAPE;
   // Head-major order once the grid is several times what the chip holds at

@@ -21,10 +21,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 # The library picks between an 8-wave ping-pong kernel (16-bit, d = 64, large
-# grids), a 4-wave kernel, and the 4-wave kernel with the key range split
-# between two groups of waves (16-bit, d = 64, small grids); the override
-# forces one so each is checked on every kernel-sensitive case.
-KERNELS = ["pp", "wg4", "split"]
+# grids), a 4-wave kernel, the 4-wave kernel with the key range split between
+# two groups of waves (16-bit, d = 64, small grids), and that split on 64-row
+# blocks with two waves per group (smallest grids); the override forces one
+# so each is checked on every kernel-sensitive case.
+KERNELS = ["pp", "wg4", "split", "split64"]
 
 
 @pytest.fixture(params=KERNELS)
