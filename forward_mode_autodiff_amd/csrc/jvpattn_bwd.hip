@@ -76,38 +76,45 @@ struct BwdArgs {
 enum { WS_NEGL = 0, WS_TLSE = 1, WS_R = 2, WS_DEL = 3 };
 
 // ------------------------------------------------------------------ rows
-// One thread per query row (d = 64: eight 16-byte granules per tensor row).
+// Eight lanes per query row (d = 64: one 16-byte granule of each tensor per
+// lane), so a wave reads 1 KB of each tensor contiguously; the row's partial
+// sums meet in three butterfly exchanges.
 template <typename T>
 __device__ __forceinline__ void bwd_rows_body(const BwdArgs& a, int64_t rows) {
-  const int64_t row = int64_t(blockIdx.x) * kBThreads + threadIdx.x;
-  if (row >= rows) return;
-  const uint4* o = static_cast<const uint4*>(a.o) + row * 8;
-  const uint4* to = static_cast<const uint4*>(a.to) + row * 8;
+  const int64_t t = int64_t(blockIdx.x) * kBThreads + threadIdx.x;
+  const int64_t row = t >> 3;
+  const int gi = threadIdx.x & 7;
+  const bool live = row < rows;
+  const int64_t at = live ? row * 8 + gi : 0;
+  const uint4 wo = live ? static_cast<const uint4*>(a.o)[at] : uint4{0, 0, 0, 0};
+  const uint4 wto = live ? static_cast<const uint4*>(a.to)[at] : uint4{0, 0, 0, 0};
   // a NULL cotangent is zero
-  const uint4* g = a.go ? static_cast<const uint4*>(a.go) + row * 8 : nullptr;
-  const uint4* gd = a.gto ? static_cast<const uint4*>(a.gto) + row * 8 : nullptr;
+  const uint4 wg = (live && a.go) ? static_cast<const uint4*>(a.go)[at] : uint4{0, 0, 0, 0};
+  const uint4 wgd = (live && a.gto) ? static_cast<const uint4*>(a.gto)[at] : uint4{0, 0, 0, 0};
+  const uint32_t xo[4] = {wo.x, wo.y, wo.z, wo.w}, xto[4] = {wto.x, wto.y, wto.z, wto.w};
+  const uint32_t xg[4] = {wg.x, wg.y, wg.z, wg.w}, xgd[4] = {wgd.x, wgd.y, wgd.z, wgd.w};
   float r = 0.0f, go_o = 0.0f, gd_to = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint4 wo = o[c], wto = to[c];
-    const uint4 wg = g ? g[c] : uint4{0, 0, 0, 0}, wgd = gd ? gd[c] : uint4{0, 0, 0, 0};
-    const uint32_t xo[4] = {wo.x, wo.y, wo.z, wo.w}, xto[4] = {wto.x, wto.y, wto.z, wto.w};
-    const uint32_t xg[4] = {wg.x, wg.y, wg.z, wg.w}, xgd[4] = {wgd.x, wgd.y, wgd.z, wgd.w};
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int hw = 0; hw < 2; ++hw) {
-        const uint16_t so = hw ? hi16(xo[i]) : lo16(xo[i]);
-        const uint16_t sto = hw ? hi16(xto[i]) : lo16(xto[i]);
-        const uint16_t sg = hw ? hi16(xg[i]) : lo16(xg[i]);
-        const uint16_t sgd = hw ? hi16(xgd[i]) : lo16(xgd[i]);
-        const float fo = T::widen(so), fgd = T::widen(sgd);
-        r = fmaf(fgd, fo, r);
-        go_o = fmaf(T::widen(sg), fo, go_o);
-        gd_to = fmaf(fgd, T::widen(sto), gd_to);
-      }
+    for (int hw = 0; hw < 2; ++hw) {
+      const uint16_t so = hw ? hi16(xo[i]) : lo16(xo[i]);
+      const uint16_t sto = hw ? hi16(xto[i]) : lo16(xto[i]);
+      const uint16_t sg = hw ? hi16(xg[i]) : lo16(xg[i]);
+      const uint16_t sgd = hw ? hi16(xgd[i]) : lo16(xgd[i]);
+      const float fo = T::widen(so), fgd = T::widen(sgd);
+      r = fmaf(fgd, fo, r);
+      go_o = fmaf(T::widen(sg), fo, go_o);
+      gd_to = fmaf(fgd, T::widen(sto), gd_to);
     }
   }
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) {
+    r += __shfl_xor(r, m, 8);
+    go_o += __shfl_xor(go_o, m, 8);
+    gd_to += __shfl_xor(gd_to, m, 8);
+  }
+  if (!live || gi != 0) return;
   const float lse = a.lse[row], tl = a.tlse[row];
   a.ws[WS_NEGL * a.ws_stride + row] = lse == -INFINITY ? -INFINITY : -lse * kLog2e;
   a.ws[WS_TLSE * a.ws_stride + row] = tl;
@@ -871,7 +878,7 @@ extern "C" int jvpattn_bwd(const jvpattn_params* p, const void* q, const void* k
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   if (sz.rows_q > 0) {
-    const int64_t nb = (sz.rows_q + kBThreads - 1) / kBThreads;
+    const int64_t nb = (sz.rows_q * 8 + kBThreads - 1) / kBThreads;   // eight lanes per row
     if (nb > INT32_MAX) return JVPATTN_ERR_SHAPE;
     if (p->dtype == JVPATTN_BF16)
       hipLaunchKernelGGL((bwd_rows_kernel<BF16>), dim3(unsigned(nb)), dim3(kBThreads), 0, s, a, sz.rows_q);
