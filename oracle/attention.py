@@ -20,10 +20,10 @@ What is computed, and where it comes from
   d/dt O(Q + t*dQ, K + t*dK, V + t*dV) at t = 0, written out here with the
   product rule and the derivative of softmax:
 
-      S   = scale * Q K^T + M            M: mask bias, constant (no tangent)
+      S   = scale * Q K^T + M            M: mask bias
       P   = softmax_j(S)
       O   = P V
-      dS  = scale * (dQ K^T + Q dK^T)
+      dS  = scale * (dQ K^T + Q dK^T) + dM   dM: tangent of an additive mask (else 0)
       dP  = P * (dS - rowsum(P * dS))    derivative of softmax
       dO  = dP V + P dV                  product rule
 
@@ -32,7 +32,8 @@ What is computed, and where it comes from
 
 Readings taken where the pages say nothing (each is listed in the design notes):
   * boolean mask: nonzero/True = the key takes part (SDPA's convention);
-  * additive mask: added after scaling, carries no tangent;
+  * additive mask: added after scaling; constant unless a tangent dM of it
+    is given (then it enters dS as the derivative of S = scale QK^T + M);
   * causal: key j is visible to query i iff j <= i (top-left aligned, as
     SDPA's ``is_causal``); with an explicit mask both restrictions apply;
   * a row whose every score is -inf ("fully masked") gives O = dO = 0,
@@ -92,13 +93,16 @@ def _head_bias(mask, mask_kind, b, h, nq_rows, Nk, causal, q_pos):
     return M
 
 
-def oracle_fwd_head(q, k, v, tq, tk, tv, bias, scale):
-    """One head. q,tq: [n, d]; k,v,tk,tv: [Nk, d]; bias: [n, Nk] (0 / -inf / value).
+def oracle_fwd_head(q, k, v, tq, tk, tv, bias, scale, tbias=None):
+    """One head. q,tq: [n, d]; k,v,tk,tv: [Nk, d]; bias: [n, Nk] (0 / -inf / value);
+    tbias: [n, Nk] tangent of an additive mask, or None.
 
     Returns (o, to, lse, tlse) in float64.
     """
     S = scale * (q @ k.T) + bias
     dS = scale * (tq @ k.T + q @ tk.T)
+    if tbias is not None:
+        dS = dS + tbias
     n, d = q.shape
     o = np.zeros((n, v.shape[1]))
     to = np.zeros((n, v.shape[1]))
@@ -130,7 +134,7 @@ def kv_head(h, H, Hkv):
 
 
 def oracle_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, mask_kind=MASK_NONE,
-               causal=False, scale=None, q_pos=None):
+               causal=False, scale=None, q_pos=None, tmask=None):
     """Attention output and its JVP for [B, H, Nq, d] queries and [B, Hkv, Nk, d] keys/values.
 
     Hkv = H is plain multi-head attention; a divisor of H groups the query
@@ -145,6 +149,7 @@ def oracle_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, mask_kind=MASK_NON
     scale: multiplies Q K^T and the score tangent; default 1/sqrt(d).
     q_pos: optional absolute indices of the given query rows (defaults to
         0..Nq-1); lets a caller evaluate a sample of rows of a large problem.
+    tmask: tangent of an additive mask, shaped like ``mask`` (additive only).
 
     Returns (o, to, lse, tlse): [B,H,Nq,d], [B,H,Nq,d], [B,H,Nq], [B,H,Nq] float64.
     """
@@ -163,6 +168,8 @@ def oracle_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, mask_kind=MASK_NON
         mask = np.asarray(mask)
     if (mask is None) != (mask_kind == MASK_NONE):
         raise ValueError("mask must be given exactly when mask_kind is not 'none'")
+    if tmask is not None and mask_kind != MASK_ADDITIVE:
+        raise ValueError("a mask tangent needs an additive mask")
     dv = v.shape[3]
     o = np.empty((B, H, Nq, dv))
     to = np.empty((B, H, Nq, dv))
@@ -171,7 +178,9 @@ def oracle_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, mask_kind=MASK_NON
     for b in range(B):
         for h in range(H):
             bias = _head_bias(mask, mask_kind, b, h, Nq, Nk, causal, q_pos)
+            # the mask's tangent, laid out as the mask; -inf entries of the mask make it irrelevant there
+            tbias = None if tmask is None else _head_bias(tmask, MASK_ADDITIVE, b, h, Nq, Nk, False, q_pos)
             g = kv_head(h, H, Hkv)
             o[b, h], to[b, h], lse[b, h], tlse[b, h] = oracle_fwd_head(
-                q[b, h], k[b, g], v[b, g], tq[b, h], tk[b, g], tv[b, g], bias, scale)
+                q[b, h], k[b, g], v[b, g], tq[b, h], tk[b, g], tv[b, g], bias, scale, tbias)
     return o, to, lse, tlse

@@ -98,6 +98,58 @@ def test_matches_torch_sdpa_key_padding_mask(kind):
     np.testing.assert_allclose(to, rto, rtol=0, atol=1e-11)
 
 
+def torch_sdpa_jvp_with_mask(q, k, v, m, tq, tk, tv, tm, is_causal=False):
+    """SDPA (MATH, float64) and its JVP with the additive mask as a differentiated input."""
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    with sdpa_kernel(SDPBackend.MATH):
+        o, to = torch.func.jvp(
+            lambda a, b, c, mm: F.scaled_dot_product_attention(a, b, c, attn_mask=mm, is_causal=is_causal),
+            (T(q), T(k), T(v), T(m)), (T(tq), T(tk), T(tv), T(tm)))
+    return o.numpy(), to.numpy()
+
+
+@pytest.mark.parametrize("layout", ["full", "key_padding"])
+def test_additive_mask_tangent_matches_torch_jvp(layout):
+    # the additive mask as a fourth differentiated input: dS gains its tangent dM
+    rng = np.random.default_rng(46)
+    q, k, v, tq, tk, tv = make(rng, Nq=6, Nk=9)
+    shape = (2, 3, 6, 9) if layout == "full" else (2, 1, 1, 9)
+    m = rnd(rng, *shape)
+    if layout == "key_padding":
+        m[0, ..., 6:] = -np.inf
+    tm = rnd(rng, *shape)
+    o, to, _, tlse = oracle_fwd(q, k, v, tq, tk, tv, mask=m, mask_kind="additive", tmask=tm)
+    ro, rto = torch_sdpa_jvp_with_mask(q, k, v, m, tq, tk, tv, tm)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(to, rto, rtol=0, atol=1e-11)
+    # tlse is still the derivative of lse, now along the mask too (central differences)
+    eps = 1e-6
+    lp = oracle_fwd(q + eps * tq, k + eps * tk, v, mask=m + eps * tm, mask_kind="additive")[2]
+    lm = oracle_fwd(q - eps * tq, k - eps * tk, v, mask=m - eps * tm, mask_kind="additive")[2]
+    fin = np.isfinite(lp)
+    np.testing.assert_allclose(tlse[fin], ((lp - lm) / (2 * eps))[fin], rtol=0, atol=1e-7)
+
+
+def test_additive_mask_tangent_row_constant_changes_nothing_but_tlse():
+    # a tangent constant along each row shifts dS uniformly: dO unchanged, tlse shifted by it
+    rng = np.random.default_rng(47)
+    args = make(rng, Nq=5, Nk=7)
+    m = rnd(rng, 2, 1, 5, 7)
+    c = rnd(rng, 2, 1, 5, 1)
+    tm = np.broadcast_to(c, m.shape).copy()
+    base = oracle_fwd(*args, mask=m, mask_kind="additive")
+    got = oracle_fwd(*args, mask=m, mask_kind="additive", tmask=tm)
+    np.testing.assert_allclose(got[1], base[1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[3], base[3] + c[..., 0], rtol=0, atol=1e-12)
+
+
+def test_additive_mask_tangent_needs_additive_mask():
+    rng = np.random.default_rng(48)
+    args = make(rng)
+    with pytest.raises(ValueError):
+        oracle_fwd(*args, tmask=np.zeros((2, 1, 7, 9)))
+
+
 def test_matches_torch_sdpa_additive_mask_per_head():
     rng = np.random.default_rng(2)
     args = make(rng, Nq=6, Nk=8, d=4)
