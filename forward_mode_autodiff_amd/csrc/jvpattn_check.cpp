@@ -144,6 +144,30 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
   return JVPATTN_OK;
 }
 
+int check_fwd_tmask(const jvpattn_params* p, const void* q, const void* k, const void* v,
+                    const void* tq, const void* tk, const void* tv, const void* mask, const void* tmask,
+                    const void* o, const void* to, const float* lse, const float* tlse, FwdSizes* sizes) {
+  FwdSizes sz;
+  const int rc = check_fwd(p, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, &sz);
+  if (rc != JVPATTN_OK) return rc;
+  if (tmask) {
+    if (p->mask_kind != JVPATTN_MASK_ADDITIVE) return JVPATTN_ERR_MASK;
+    if (!aligned(tmask, sz.elem_bytes)) return JVPATTN_ERR_ALIGN;
+    if (sz.rows_q > 0 && p->Nk > 0) {
+      // laid out as the mask: check_fwd proved this extent fits
+      const int64_t bytes = ((p->B - 1) * p->mask_stride_b + (p->H - 1) * p->mask_stride_h +
+                             (p->Nq - 1) * p->mask_stride_q + p->Nk) * sz.elem_bytes;
+      const int64_t stats = sz.rows_q * 4, outb = sz.rows_q * p->d * sz.elem_bytes;
+      const Span t = span(tmask, bytes);
+      const Span outs[] = {span(o, outb), span(to, outb), span(lse, stats), span(tlse, tlse ? stats : 0)};
+      for (const Span& x : outs)
+        if (overlap(t, x)) return JVPATTN_ERR_ALIAS;
+    }
+  }
+  if (sizes) *sizes = sz;
+  return JVPATTN_OK;
+}
+
 thread_local int g_last_hip_error = 0;
 
 int64_t bwd_workspace_bytes(int64_t rows_q) {
@@ -224,6 +248,13 @@ extern "C" int jvpattn_check_bwd(const jvpattn_params* params, const void* q, co
                                  const void* dtv, const void* workspace, size_t workspace_bytes) {
   return jvpattn::check_bwd(params, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, go, gto, dq, dk, dv,
                             dtq, dtk, dtv, workspace, workspace_bytes, nullptr);
+}
+
+extern "C" int jvpattn_check_fwd_tmask(const jvpattn_params* params, const void* q, const void* k,
+                                       const void* v, const void* tq, const void* tk, const void* tv,
+                                       const void* mask, const void* tmask, const void* o, const void* to,
+                                       const float* lse, const float* tlse) {
+  return jvpattn::check_fwd_tmask(params, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, nullptr);
 }
 
 extern "C" int jvpattn_check_fwd(const jvpattn_params* params, const void* q, const void* k,

@@ -194,13 +194,35 @@ __device__ inline void ring_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Internal mask kind: an additive mask together with its tangent dM, which
+// the score tangent gains (dS = scale (dQ K^T + Q dK^T) + dM).
+constexpr int kMaskAddT = 3;
+
 // Mask values of one 32-key block for this lane's 16 keys, loaded ahead of use.
 template <int MASK> struct MaskVals {};
 template <> struct MaskVals<JVPATTN_MASK_BOOL> { uint32_t w[4]; };
 template <> struct MaskVals<JVPATTN_MASK_ADDITIVE> { uint2 w[4]; };
+template <> struct MaskVals<kMaskAddT> { uint2 w[4]; uint2 t[4]; };   // mask, its tangent
 
 // Register r of this lane holds key k0 + 8*(r/4) + 4*hlf + r%4.
 // Args: any argument block with Nk, msq (mask row stride) and mask_vec.
+template <int MASK, typename Args>
+__device__ inline void mask_load(MaskVals<MASK>& m, const Args& a, Rsrc mr, int qi, int k0, int hlf);
+
+// Additive mask and its tangent (resource mtr, same element layout).
+template <typename Args>
+__device__ inline void mask_load_t(MaskVals<kMaskAddT>& m, const Args& a, Rsrc mr, Rsrc mtr, int qi, int k0,
+                                   int hlf) {
+  MaskVals<JVPATTN_MASK_ADDITIVE> x, y;
+  mask_load<JVPATTN_MASK_ADDITIVE>(x, a, mr, qi, k0, hlf);
+  mask_load<JVPATTN_MASK_ADDITIVE>(y, a, mtr, qi, k0, hlf);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    m.w[g] = x.w[g];
+    m.t[g] = y.w[g];
+  }
+}
+
 template <int MASK, typename Args>
 __device__ inline void mask_load(MaskVals<MASK>& m, const Args& a, Rsrc mr, int qi, int k0, int hlf) {
   if constexpr (MASK == JVPATTN_MASK_BOOL || MASK == JVPATTN_MASK_ADDITIVE) {
@@ -247,13 +269,28 @@ __device__ inline void mask_apply(f32x16& s, const MaskVals<MASK>& m, float scal
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (((m.w[r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u) s[r] = -INFINITY;
-  } else if constexpr (MASK == JVPATTN_MASK_ADDITIVE) {
+  } else if constexpr (MASK == JVPATTN_MASK_ADDITIVE || MASK == kMaskAddT) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const uint2 x = m.w[r >> 2];
       const uint32_t word = (r & 2) ? x.y : x.x;
       const uint16_t bits = (r & 1) ? hi16(word) : lo16(word);
       s[r] = PRESCALED ? s[r] + T::widen(bits) : fmaf(s[r], scale, T::widen(bits));
+    }
+  }
+}
+
+// With a mask tangent: sd (score tangent in units where sd * us = dS) gains
+// dM / us; inv_us = 1 / us. No-op for the other kinds.
+template <typename T, int MASK>
+__device__ inline void mask_tangent(f32x16& sd, const MaskVals<MASK>& m, float inv_us) {
+  if constexpr (MASK == kMaskAddT) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint2 x = m.t[r >> 2];
+      const uint32_t word = (r & 2) ? x.y : x.x;
+      const uint16_t bits = (r & 1) ? hi16(word) : lo16(word);
+      sd[r] = fmaf(T::widen(bits), inv_us, sd[r]);
     }
   }
 }
@@ -271,12 +308,14 @@ __device__ inline void hide_keys(f32x16& s, int Nk, int qi, int k0, int hlf) {
 }
 
 // Mask resource of head (b, h): element (i, j) at byte (i*msq + j) * es.
+// `base` is the mask (default) or a tensor laid out like it (its tangent).
 template <typename Args>
-__device__ inline Rsrc mask_rsrc(const Args& a, int b, int h, int es) {
-  if (!a.mask) return make_rsrc(a.q, 0);
-  const int64_t base = (b * a.msb + h * a.msh) * es;
+__device__ inline Rsrc mask_rsrc(const Args& a, int b, int h, int es, const void* base = nullptr) {
+  const void* m = base ? base : a.mask;
+  if (!m) return make_rsrc(a.q, 0);
+  const int64_t off = (b * a.msb + h * a.msh) * es;
   const int64_t bytes = (int64_t(a.Nq - 1) * a.msq + a.Nk) * es;
-  return make_rsrc(static_cast<const char*>(a.mask) + base, bytes);
+  return make_rsrc(static_cast<const char*>(m) + off, bytes);
 }
 
 // Largest score of this lane's query column (both lane halves).

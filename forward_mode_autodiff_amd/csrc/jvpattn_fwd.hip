@@ -53,6 +53,7 @@ struct FwdArgs {
   const void* tk;
   const void* tv;
   const void* mask;
+  const void* tmask;  // tangent of the additive mask (mask kind kMaskAddT), laid out as the mask
   void* o;
   void* to;
   float* lse;
@@ -66,6 +67,7 @@ struct FwdArgs {
   int mask_vec;       // 1: mask rows may be read 4 keys at a time
   int64_t msb, msh, msq;
   float scale;
+  float inv_scale;    // 1 / scale
   float cx;           // score units -> log2 units
   float thr;          // lazy-rescale threshold in score units
 };
@@ -296,6 +298,12 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   }
   RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
   const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+  const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 2, a.tmask) : mr;
+  auto load_mask = [&](MaskVals<MASK>& m, int k0) {
+    if constexpr (MASK == kMaskAddT) mask_load_t(m, a, mr, mtr, qi, k0, hlf);
+    else mask_load<MASK>(m, a, mr, qi, k0, hlf);
+  };
+  const float inv_us = POW2 ? 1.0f : a.inv_scale;   // mask tangent -> units of sd
 
   const int kv_end = min(CAUSAL ? min(a.Nk, q0 + BMG) : a.Nk, 32 * t_hi);
   const int n_all = max(0, (kv_end + L::BN - 1) / L::BN - t_lo);
@@ -471,7 +479,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     else wait_vmcnt<0>();
     ring_barrier();   // tile k+1 visible to all; every wave is done with tile k-1 (the `dma` stage)
     MaskVals<MASK> mk1;
-    mask_load<MASK>(mk1, a, mr, qi, (kb + k + 1) * 32, hlf);   // before the fetch: keeps its wait short
+    load_mask(mk1, (kb + k + 1) * 32);   // before the fetch: keeps its wait short
     if (k + 3 < n_tiles) issue_tile(k + 3, dma);
     // All LDS operands first (their latency hides behind the first weights),
     // then the score products of block k+1 interleaved with block k's softmax
@@ -483,6 +491,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     weights(sc, sdc, pB, uB);
     mma_v(va, tva, pB, uB);
     mask_apply<T, MASK, POW2>(sn, mk1, a.scale);
+    mask_tangent<T, MASK>(sdn, mk1, inv_us);
     const float bm = block_max(sn);
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * L::NC, 0);           // K / dK reads
     __builtin_amdgcn_sched_group_barrier(0x100, 8 * L::NT, 0);           // V / dV transpose reads
@@ -513,8 +522,9 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   if (0 <= last && !needs_keymask(0)) {
     scores(stage0, sA, sdA);
     MaskVals<MASK> mk;
-    mask_load<MASK>(mk, a, mr, qi, kb * 32, hlf);
+    load_mask(mk, kb * 32);
     mask_apply<T, MASK, POW2>(sA, mk, a.scale);
+    mask_tangent<T, MASK>(sdA, mk, inv_us);
     rescale(block_max(sA));
     ready = true;
   }
@@ -552,8 +562,9 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     if (!ready) {
       scores(cur, sA, sdA);
       MaskVals<MASK> mk;
-      mask_load<MASK>(mk, a, mr, qi, (kb + k) * 32, hlf);
+      load_mask(mk, (kb + k) * 32);
       mask_apply<T, MASK, POW2>(sA, mk, a.scale);
+      mask_tangent<T, MASK>(sdA, mk, inv_us);
       if (needs_keymask(k)) hide_keys<CAUSAL>(sA, a.Nk, qi, (kb + k) * 32, hlf);
       rescale(block_max(sA));
     }
@@ -760,6 +771,11 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   }
   RowState16 st{0.0f, 0.0f, 0.0f, false};
   const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+  const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 2, a.tmask) : mr;
+  auto load_mask = [&](MaskVals<MASK>& m, int k0) {
+    if constexpr (MASK == kMaskAddT) mask_load_t(m, a, mr, mtr, qi, k0, hlf);
+    else mask_load<MASK>(m, a, mr, qi, k0, hlf);
+  };
   __shared__ int kred[2];
   int t0, t_hi;   // key tiles [t0, t_hi) may hold visible keys; loop tile k is absolute tile t0 + k
   key_tiles<T, MASK, 2>(a, mr, kred, t0, t_hi);
@@ -857,6 +873,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   // operands of block k (stage stv) are read while the weights are packed.
   auto settle = [&](int k, const char* stv) {
     mask_apply<T, MASK, POW2>(sn, mk, a.scale);
+    mask_tangent<T, MASK>(sdn, mk, POW2 ? 1.0f : a.inv_scale);
     if (needs_keymask(k)) hide_keys<CAUSAL>(sn, a.Nk, qi, kpos(k), hlf);
     float e[16], alpha;
     if (block_exp16<T>(sn, st, a.cx, e, alpha)) {
@@ -904,7 +921,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   auto vector_phase = [&](int i, const char* stn) {
     if (i + 1 > last) return;
     settle(i + 1, stn);
-    if (i + 2 <= last) mask_load<MASK>(mk, a, mr, qi, kpos(i + 2), hlf);
+    if (i + 2 <= last) load_mask(mk, kpos(i + 2));
   };
   // Group B's wait for its loads of tile j; tiles issued after j may stay in flight.
   auto wait_tile = [&](int j) {
@@ -935,9 +952,9 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   if (0 <= last) {
     read_k(stage0);
     mma_s();
-    mask_load<MASK>(mk, a, mr, qi, kpos(0), hlf);
+    load_mask(mk, kpos(0));
     settle(0, stage0);
-    if (1 <= last) mask_load<MASK>(mk, a, mr, qi, kpos(1), hlf);
+    if (1 <= last) load_mask(mk, kpos(1));
   }
   // Operands of the first matrix phase have arrived (states the loop's entry
   // as free of pending LDS reads, as every later iteration is).
@@ -1083,6 +1100,7 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
   }
   RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
   const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 4);
+  const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 4, a.tmask) : mr;
   __shared__ int kred[2];
   int t0, t_hi;   // key tiles [t0, t_hi) may hold visible keys
   key_tiles<F16, MASK, 4>(a, mr, kred, t0, t_hi);
@@ -1133,8 +1151,9 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
         }
       }
       const bool elem_mask = (CAUSAL && k0 + 31 > qw0) || (k0 + 32 > a.Nk);
-      mask_scores<F16, MASK == JVPATTN_MASK_ADDITIVE ? -1 : MASK, CAUSAL, false>(s, a, mr, qi, k0, hlf, elem_mask);
-      if constexpr (MASK == JVPATTN_MASK_ADDITIVE) {
+      constexpr bool ADD = MASK == JVPATTN_MASK_ADDITIVE || MASK == kMaskAddT;
+      mask_scores<F16, ADD ? -1 : MASK, CAUSAL, false>(s, a, mr, qi, k0, hlf, elem_mask);
+      if constexpr (ADD) {
         // float32 additive mask: element (qi, key) for the 16 keys of this lane
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -1142,6 +1161,12 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
           const float mv = __uint_as_float(
               __builtin_amdgcn_raw_buffer_load_b32(mr, (qi * int(a.msq) + key) * 4, 0, 0));
           s[r] = fmaf(s[r], a.scale, mv);   // hidden keys are already -inf
+          if constexpr (MASK == kMaskAddT) {
+            // the mask's tangent joins the score tangent (sd * scale = dS)
+            const float tv = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(mtr, (qi * int(a.msq) + key) * 4, 0, 0));
+            sd[r] = fmaf(tv, a.inv_scale, sd[r]);
+          }
         }
       }
       float alpha;
@@ -1266,20 +1291,15 @@ hipError_t launch_typed(int dtype, int d, bool pow2, int split, const FwdArgs& a
   return hipGetLastError();
 }
 
-}  // namespace
-}  // namespace jvpattn
-
-extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k, const void* v,
-                           const void* tq, const void* tk, const void* tv, const void* mask, void* o,
-                           void* to, float* lse, float* tlse, void* stream) {
-  using namespace jvpattn;
-  FwdSizes sz;
-  const int rc = check_fwd(p, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, &sz);
-  if (rc != JVPATTN_OK) return rc;
+// Queue the forward for arguments already validated (sizes from the check).
+// tmask: the additive mask's tangent, or NULL.
+int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const void* k, const void* v,
+               const void* tq, const void* tk, const void* tv, const void* mask, const void* tmask, void* o,
+               void* to, float* lse, float* tlse, void* stream) {
   if (sz.rows_q == 0) return JVPATTN_OK;
 
   FwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv; a.mask = mask;
+  a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv; a.mask = mask; a.tmask = tmask;
   a.o = o; a.to = to; a.lse = lse; a.tlse = tlse;
   a.H = p->H; a.Nq = p->Nq; a.Nk = p->Nk; a.BH = p->B * p->H;
   a.grp = sz.group;
@@ -1287,6 +1307,7 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
   a.n_qblk = (p->Nq + kBM - 1) / kBM;
   a.msb = p->mask_stride_b; a.msh = p->mask_stride_h; a.msq = p->mask_stride_q;
   a.scale = p->scale;
+  a.inv_scale = 1.0f / p->scale;
   const bool additive = p->mask_kind == JVPATTN_MASK_ADDITIVE;
   // bfloat16 with a power-of-two scale: the scale is folded into Q and dQ
   // exactly (bfloat16 has float32's exponent range), scores arrive scaled.
@@ -1300,8 +1321,9 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
     const int mes = p->mask_kind == JVPATTN_MASK_BOOL ? 1 : elem_bytes(p->dtype);
     const uintptr_t base = reinterpret_cast<uintptr_t>(mask);
     const int64_t need = 4;  // keys per vector read
+    const uintptr_t tbase = reinterpret_cast<uintptr_t>(tmask);   // read with the same offsets
     a.mask_vec = mask && (p->mask_stride_b % need == 0) && (p->mask_stride_h % need == 0) &&
-                 (p->mask_stride_q % need == 0) && (base % (need * mes) == 0);
+                 (p->mask_stride_q % need == 0) && (base % (need * mes) == 0) && (tbase % (need * mes) == 0);
   }
   // Kernel choice for 16-bit d = 64: the 8-wave ping-pong kernel (256 rows per
   // workgroup) when it still gives every CU a workgroup; else the 4-wave
@@ -1356,8 +1378,12 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
               : launch_pp<JVPATTN_MASK_BOOL, false>(p->dtype, pow2, a, grid, s);
         break;
       default:
-        e = c ? launch_pp<JVPATTN_MASK_ADDITIVE, true>(p->dtype, pow2, a, grid, s)
-              : launch_pp<JVPATTN_MASK_ADDITIVE, false>(p->dtype, pow2, a, grid, s);
+        if (tmask)
+          e = c ? launch_pp<kMaskAddT, true>(p->dtype, pow2, a, grid, s)
+                : launch_pp<kMaskAddT, false>(p->dtype, pow2, a, grid, s);
+        else
+          e = c ? launch_pp<JVPATTN_MASK_ADDITIVE, true>(p->dtype, pow2, a, grid, s)
+                : launch_pp<JVPATTN_MASK_ADDITIVE, false>(p->dtype, pow2, a, grid, s);
         break;
     }
   } else {
@@ -1371,8 +1397,12 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
               : launch_typed<JVPATTN_MASK_BOOL, false>(p->dtype, p->d, pow2, split, a, grid, s);
         break;
       default:
-        e = c ? launch_typed<JVPATTN_MASK_ADDITIVE, true>(p->dtype, p->d, pow2, split, a, grid, s)
-              : launch_typed<JVPATTN_MASK_ADDITIVE, false>(p->dtype, p->d, pow2, split, a, grid, s);
+        if (tmask)
+          e = c ? launch_typed<kMaskAddT, true>(p->dtype, p->d, pow2, split, a, grid, s)
+                : launch_typed<kMaskAddT, false>(p->dtype, p->d, pow2, split, a, grid, s);
+        else
+          e = c ? launch_typed<JVPATTN_MASK_ADDITIVE, true>(p->dtype, p->d, pow2, split, a, grid, s)
+                : launch_typed<JVPATTN_MASK_ADDITIVE, false>(p->dtype, p->d, pow2, split, a, grid, s);
         break;
     }
   }
@@ -1381,4 +1411,27 @@ extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k
     return JVPATTN_ERR_HIP;
   }
   return JVPATTN_OK;
+}
+
+}  // namespace
+}  // namespace jvpattn
+
+extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k, const void* v,
+                           const void* tq, const void* tk, const void* tv, const void* mask, void* o,
+                           void* to, float* lse, float* tlse, void* stream) {
+  using namespace jvpattn;
+  FwdSizes sz;
+  const int rc = check_fwd(p, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, &sz);
+  if (rc != JVPATTN_OK) return rc;
+  return fwd_launch(p, sz, q, k, v, tq, tk, tv, mask, nullptr, o, to, lse, tlse, stream);
+}
+
+extern "C" int jvpattn_fwd_tmask(const jvpattn_params* p, const void* q, const void* k, const void* v,
+                                 const void* tq, const void* tk, const void* tv, const void* mask,
+                                 const void* tmask, void* o, void* to, float* lse, float* tlse, void* stream) {
+  using namespace jvpattn;
+  FwdSizes sz;
+  const int rc = check_fwd_tmask(p, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, &sz);
+  if (rc != JVPATTN_OK) return rc;
+  return fwd_launch(p, sz, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, stream);
 }

@@ -24,6 +24,12 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
               const void* o, const void* to, const float* lse, const float* tlse,
               FwdSizes* sizes);
 
+// check_fwd, then the additive mask's tangent tmask (NULL = zero): only with an
+// additive mask, aligned to the element size, disjoint from the outputs.
+int check_fwd_tmask(const jvpattn_params* p, const void* q, const void* k, const void* v,
+                    const void* tq, const void* tk, const void* tv, const void* mask, const void* tmask,
+                    const void* o, const void* to, const float* lse, const float* tlse, FwdSizes* sizes);
+
 // Full argument check of jvpattn_bwd (the forward's checks on the shared
 // arguments, then its own); fills `sizes` on success (may be NULL).
 int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void* v,

@@ -60,6 +60,10 @@ def load_library(path: str = LIB_PATH):
     lib.jvpattn_check_fwd.restype = ctypes.c_int
     lib.jvpattn_fwd.argtypes = [P] + [vp] * 7 + [vp, vp, vp, vp, vp]
     lib.jvpattn_fwd.restype = ctypes.c_int
+    lib.jvpattn_fwd_tmask.argtypes = [P] + [vp] * 8 + [vp, vp, vp, vp, vp]
+    lib.jvpattn_fwd_tmask.restype = ctypes.c_int
+    lib.jvpattn_check_fwd_tmask.argtypes = [P] + [vp] * 12
+    lib.jvpattn_check_fwd_tmask.restype = ctypes.c_int
     lib.jvpattn_strerror.argtypes = [ctypes.c_int]
     lib.jvpattn_strerror.restype = ctypes.c_char_p
     lib.jvpattn_last_hip_error.argtypes = []
@@ -88,6 +92,20 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _as_4d(mask):
+    """A mask as [B, H, Nq, Nk]: a 2-D mask is [Nq, Nk], a 3-D one [B, Nq, Nk]."""
+    if mask.dim() == 2:
+        return mask[None, None]
+    if mask.dim() == 3:
+        return mask[:, None]
+    return mask
+
+
+def _layout(mask):
+    """Element strides the library uses for a 4-D mask (0 where an axis has extent 1)."""
+    return tuple(0 if mask.shape[i] == 1 else mask.stride(i) for i in range(3)) + (mask.stride(3),)
+
+
 def make_params(q, k, mask=None, causal=False, scale=None) -> tuple:
     """Fill jvpattn_params from tensors. Returns (params, mask tensor as passed to the library)."""
     if q.dim() != 4 or k.dim() != 4:
@@ -104,10 +122,7 @@ def make_params(q, k, mask=None, causal=False, scale=None) -> tuple:
     p.scale = float(1.0 / math.sqrt(d) if scale is None else scale)
     p.mask_kind = JVPATTN_MASK_NONE
     if mask is not None:
-        if mask.dim() == 2:
-            mask = mask[None, None]
-        elif mask.dim() == 3:
-            mask = mask[:, None]
+        mask = _as_4d(mask)
         if mask.dim() != 4:
             raise ValueError("mask must broadcast to [B, H, Nq, Nk]")
         if mask.dtype == torch.bool:
@@ -123,21 +138,27 @@ def make_params(q, k, mask=None, causal=False, scale=None) -> tuple:
             raise ValueError(f"mask shape {tuple(mask.shape)} does not broadcast to {(B, H, Nq, Nk)}")
         if mask.stride(3) != 1:
             mask = mask.contiguous()
-        st = [0 if mask.shape[i] == 1 else mask.stride(i) for i in range(3)]
-        p.mask_stride_b, p.mask_stride_h, p.mask_stride_q = st
+        p.mask_stride_b, p.mask_stride_h, p.mask_stride_q = _layout(mask)[:3]
     return p, mask
 
 
+def jvpattn_check_fwd_tmask(params: jvpattn_params, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse) -> int:
+    """Host-only validation of a jvpattn_fwd_tmask call; pointer arguments are integers or None."""
+    return load_library().jvpattn_check_fwd_tmask(ctypes.byref(params), q, k, v, tq, tk, tv, mask, tmask, o, to,
+                                                  lse, tlse)
+
+
 def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, scale=None,
-                want_tlse=True, out=None):
+                want_tlse=True, out=None, tmask=None):
     """O, dO, lse, tlse = jvpattn_fwd(q, k, v, tq, tk, tv, mask, causal, scale).
 
     q, tq: [B,H,Nq,d]; k, v, tk, tv: [B,Hkv,Nk,d] on the GPU, one dtype
     (float32 / float16 / bfloat16), contiguous; Hkv divides H (query head h
     reads key/value head h // (H // Hkv)). Tangents may be None (zero).
     mask: None, a bool/uint8 tensor (True = attend) or an additive tensor of
-    q's dtype, broadcastable to [B,H,Nq,Nk]. Work is queued on torch's
-    current stream. ``out`` optionally supplies (o, to, lse, tlse) buffers.
+    q's dtype, broadcastable to [B,H,Nq,Nk]. ``tmask``: the tangent of an
+    additive mask, shaped like it (jvpattn_fwd_tmask). Work is queued on
+    torch's current stream. ``out`` optionally supplies (o, to, lse, tlse) buffers.
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("tq", tq), ("tk", tk), ("tv", tv)):
@@ -150,6 +171,18 @@ def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, sca
         if t.dtype != q.dtype:
             raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
     p, mask = make_params(q, k, mask, causal, scale)
+    if tmask is not None:
+        if p.mask_kind != JVPATTN_MASK_ADDITIVE:
+            raise ValueError("tmask needs an additive mask")
+        if not tmask.is_cuda or tmask.dtype != mask.dtype:
+            raise ValueError("tmask must be a GPU tensor of the mask's dtype")
+        tmask = _as_4d(tmask)
+        if tuple(tmask.shape) != tuple(mask.shape):
+            raise ValueError(f"tmask shape {tuple(tmask.shape)} differs from the mask's {tuple(mask.shape)}")
+        if _layout(tmask) != _layout(mask):
+            # the library reads both with one set of strides
+            mask, tmask = mask.contiguous(), tmask.contiguous()
+            p.mask_stride_b, p.mask_stride_h, p.mask_stride_q = _layout(mask)[:3]
     if out is None:
         o = torch.empty_like(q)
         to = torch.empty_like(q)
@@ -158,8 +191,12 @@ def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, sca
     else:
         o, to, lse, tlse = out
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = lib.jvpattn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
-                         _ptr(mask), _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse), stream)
+    if tmask is not None:
+        rc = lib.jvpattn_fwd_tmask(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                                   _ptr(mask), _ptr(tmask), _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse), stream)
+    else:
+        rc = lib.jvpattn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                             _ptr(mask), _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse), stream)
     if rc != 0:
         msg = jvpattn_strerror(rc)
         if rc == -9:

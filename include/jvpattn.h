@@ -126,6 +126,33 @@ int jvpattn_fwd(const jvpattn_params* params,
                 void* o, void* to, float* lse, float* tlse,
                 void* stream);
 
+/* The forward pass along a tangent of the additive mask as well: the same
+ * call as jvpattn_fwd, plus
+ *   tmask : the tangent dM of the additive mask, laid out exactly as `mask`
+ *           (same strides, element type params->dtype); NULL = zero.
+ * The score tangent becomes dS = scale (dQ K^T + Q dK^T) + dM, so dO, tlse
+ * are the derivatives of O, lse along (dQ, dK, dV, dM): the additive mask is
+ * the float attn_mask input of scaled_dot_product_attention, of which the
+ * "JVP Flash Attention" README (section "Usage") makes the method a drop-in.
+ * Errors as jvpattn_fwd, and JVPATTN_ERR_MASK if tmask is given without an
+ * additive mask, JVPATTN_ERR_ALIGN if it is not aligned to the element size,
+ * JVPATTN_ERR_ALIAS if it overlaps an output. jvpattn_bwd differentiates the
+ * forward without a mask tangent. */
+int jvpattn_fwd_tmask(const jvpattn_params* params,
+                      const void* q, const void* k, const void* v,
+                      const void* tq, const void* tk, const void* tv,
+                      const void* mask, const void* tmask,
+                      void* o, void* to, float* lse, float* tlse,
+                      void* stream);
+
+/* Host-only validation of a jvpattn_fwd_tmask call (pointers compared, never
+ * dereferenced); returns JVPATTN_OK or the code jvpattn_fwd_tmask would return. */
+int jvpattn_check_fwd_tmask(const jvpattn_params* params,
+                            const void* q, const void* k, const void* v,
+                            const void* tq, const void* tk, const void* tv,
+                            const void* mask, const void* tmask,
+                            const void* o, const void* to, const float* lse, const float* tlse);
+
 /* ------------------------------------------------------------ reverse pass
  *
  * The pullback of the pair (O, dO) that jvpattn_fwd returns: reverse mode

@@ -24,8 +24,8 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     assert declared_functions() == ["jvpattn_bwd", "jvpattn_bwd_workspace_bytes", "jvpattn_check_bwd",
-                                    "jvpattn_check_fwd", "jvpattn_fwd", "jvpattn_last_hip_error",
-                                    "jvpattn_strerror"]
+                                    "jvpattn_check_fwd", "jvpattn_check_fwd_tmask", "jvpattn_fwd",
+                                    "jvpattn_fwd_tmask", "jvpattn_last_hip_error", "jvpattn_strerror"]
 
 
 @needs_lib
@@ -106,6 +106,25 @@ def test_check_accepts_valid_calls():
     assert J.jvpattn_check_fwd(p, *([None] * 11)) == 0
     p = good_params(B=0)
     assert J.jvpattn_check_fwd(p, *([None] * 11)) == 0
+
+
+@needs_lib
+def test_check_mask_tangent():
+    p = good_params(mask_kind=J.JVPATTN_MASK_ADDITIVE, mask_stride_b=100 * 90, mask_stride_q=90)
+    P = ptrs(p)
+    t = P["mask"] + (1 << 30)   # a disjoint tangent laid out as the mask
+    args = lambda **o: [dict(dict(P, tmask=t), **o)[n] for n in ("q", "k", "v", "tq", "tk", "tv", "mask", "tmask",
+                                                                  "o", "to", "lse", "tlse")]
+    assert J.jvpattn_check_fwd_tmask(p, *args()) == 0
+    assert J.jvpattn_check_fwd_tmask(p, *args(tmask=None)) == 0           # zero tangent
+    assert J.jvpattn_check_fwd_tmask(p, *args(tmask=t + 1)) == -6         # misaligned
+    assert J.jvpattn_check_fwd_tmask(p, *args(o=t)) == -8                  # overlaps an output
+    pb = good_params(mask_kind=J.JVPATTN_MASK_BOOL, mask_stride_b=100 * 90, mask_stride_q=90)
+    assert J.jvpattn_check_fwd_tmask(pb, *args()) == -5                    # needs an additive mask
+    pn = good_params()
+    assert J.jvpattn_check_fwd_tmask(pn, *args(mask=None)) == -5
+    # the forward's own checks come first
+    assert J.jvpattn_check_fwd_tmask(p, *args(q=None)) == -1
 
 
 @needs_lib

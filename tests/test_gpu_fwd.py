@@ -472,3 +472,57 @@ def test_key_padding_hvp_shape_sampled(kernel):
     rows = sampled_rows(w.N, 40, 10)
     ref = oracle_run(x, "bool", False, heads=heads, rows=rows)
     assert_parity(pick(got, heads, rows), ref, w.dtype, w.name, spec_spread=True)
+
+
+# ------------------------------------------------ tangent of an additive mask
+
+def mask_tangent_for(x, seed):
+    g = torch.Generator().manual_seed(seed)
+    m = x["mask"]
+    return torch.randn(m.shape, generator=g, dtype=torch.float32).to(m.dtype)
+
+
+def check_tmask(w, seed, tangents=("tq", "tk", "tv")):
+    x = I.make_inputs(w)
+    tm = mask_tangent_for(x, seed)
+    d = to_dev(x)
+    t = {n: (d[n] if n in tangents else None) for n in ("tq", "tk", "tv")}
+    o, to, lse, tlse = jvpattn_fwd(d["q"], d["k"], d["v"], t["tq"], t["tk"], t["tv"], mask=d["mask"],
+                                   causal=w.causal, tmask=tm.to(DEV))
+    torch.cuda.synchronize()
+    got = {"o": o.float().cpu(), "to": to.float().cpu(), "lse": lse.cpu(), "tlse": tlse.cpu()}
+    tq, tk, tv = (f64(x[n]) if n in tangents else None for n in ("tq", "tk", "tv"))
+    r = oracle_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), tq, tk, tv, mask=f64(x["mask"]), mask_kind="additive",
+                   causal=w.causal, tmask=f64(tm))
+    assert_parity(got, dict(zip(("o", "to", "lse", "tlse"), r)), w.dtype, w.name, spec_spread=w.std is None)
+
+
+@pytest.mark.parametrize("w", [
+    I.Workload("tmask_f16", B=2, H=2, N=200, d=64, dtype="f16", mask_kind="additive", std=1.0, seed=40),
+    I.Workload("tmask_bf16_causal_per_head", B=1, H=3, N=177, d=64, dtype="bf16", causal=True,
+               mask_kind="additive", mask_heads=3, std=1.0, seed=41),
+    I.Workload("tmask_keywindow_bf16", B=4, H=2, N=300, d=64, dtype="bf16", mask_kind="additive",
+               mask_layout="window", std=1.0, seed=42),
+    I.Workload("tmask_d128_bf16", B=1, H=2, N=160, d=128, dtype="bf16", mask_kind="additive", std=1.0, seed=43),
+    I.Workload("tmask_f32", B=1, H=2, N=100, d=64, dtype="f32", mask_kind="additive", std=1.0, seed=44),
+    I.Workload("tmask_masked_spec", B=2, H=8, N=1024, d=64, dtype="f16", mask_kind="additive", seed=2),
+], ids=lambda w: w.name)
+def test_additive_mask_tangent(w, kernel):
+    check_tmask(w, seed=w.seed + 100)
+
+
+def test_additive_mask_tangent_alone(kernel):
+    """Only the mask moves: dO = sum_j P (dM - tlse) V."""
+    w = I.Workload("tmask_only", B=2, H=2, N=150, d=64, dtype="bf16", mask_kind="additive", std=1.0, seed=45)
+    check_tmask(w, seed=145, tangents=())
+
+
+def test_zero_mask_tangent_is_bit_identical(kernel):
+    w = I.Workload("tmask_zero", B=2, H=4, N=260, d=64, dtype="f16", mask_kind="additive", std=1.0, seed=46)
+    d = to_dev(I.make_inputs(w))
+    a = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=d["mask"])
+    b = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=d["mask"],
+                    tmask=torch.zeros_like(d["mask"]))
+    torch.cuda.synchronize()
+    for u, t in zip(a, b):
+        assert torch.equal(u, t)
