@@ -12,19 +12,22 @@ supplies tensors, the autograd graph and streams.
     the output O. Reverse mode (``.backward()``, ``torch.autograd.grad``)
     runs jvpattn_bwd with a zero cotangent for the tangent output; forward
     mode with ``torch.autograd.forward_ad`` dual tensors runs jvpattn_fwd
-    with the tangents. (``torch.func`` transforms hand the rules tensors
+    with the tangents -- an additive ``attn_mask`` may be a dual tensor too
+    (jvpattn_fwd_tmask). (``torch.func`` transforms hand the rules tensors
     without storage, which a library call cannot read: use ``fwd_dual`` for
     the JVP instead of ``torch.func.jvp``.)
 
-``fwd_dual(q, k, v, tq, tk, tv, attn_mask=None, is_causal=False, scale=None)``
-    the pair (O, dO) -- the output and its JVP -- differentiable in reverse
-    mode with respect to all six inputs (jvpattn_bwd). A Hessian-vector
-    product of a loss is reverse mode over this pair.
+``fwd_dual(q, k, v, tq, tk, tv, attn_mask=None, is_causal=False, scale=None, tmask=None)``
+    the pair (O, dO) -- the output and its JVP, along the additive mask's
+    tangent ``tmask`` as well when given -- differentiable in reverse mode
+    with respect to all six inputs (jvpattn_bwd; not with a mask tangent). A
+    Hessian-vector product of a loss is reverse mode over this pair.
 
-Inputs: [B, H, N, d] CUDA tensors of one dtype (float16 / bfloat16 for the
+Inputs: q [B, H, N, d], k and v [B, Hkv, N, d] (Hkv dividing H: grouped
+key/value heads) CUDA tensors of one dtype (float16 / bfloat16 for the
 reverse pass, which supports d = 64; the forward also takes float32 and
 d = 128). Masks as in ``jvpattn_fwd`` (bool: True = attend; additive: q's
-dtype, no gradient).
+dtype, no reverse-mode gradient).
 """
 from __future__ import annotations
 
@@ -45,11 +48,12 @@ class _Const:
 
 
 class _Attention(torch.autograd.Function):
-    """O = attention(q, k, v); lse rides along (not differentiable)."""
+    """O = attention(q, k, v); lse rides along (not differentiable). The mask is an input so
+    that forward mode sees its tangent; reverse mode gives it no gradient."""
 
     @staticmethod
     def forward(q, k, v, mask, causal, scale):
-        o, to, lse, tlse = J.jvpattn_fwd(q, k, v, None, None, None, mask=mask.t, causal=causal, scale=scale)
+        o, to, lse, tlse = J.jvpattn_fwd(q, k, v, None, None, None, mask=mask, causal=causal, scale=scale)
         return o, lse, to, tlse
 
     @staticmethod
@@ -58,7 +62,7 @@ class _Attention(torch.autograd.Function):
         o, lse, to, tlse = output
         ctx.save_for_backward(q, k, v, o, lse, to, tlse)
         ctx.save_for_forward(q, k, v)
-        ctx.mask, ctx.causal, ctx.scale = mask.t, causal, scale
+        ctx.mask, ctx.causal, ctx.scale = mask, causal, scale
         ctx.mark_non_differentiable(lse, to, tlse)
 
     @staticmethod
@@ -70,10 +74,13 @@ class _Attention(torch.autograd.Function):
         return dq, dk, dv, None, None, None
 
     @staticmethod
-    def jvp(ctx, tq, tk, tv, _tmask, _tcausal, _tscale):
+    def jvp(ctx, tq, tk, tv, tmask, _tcausal, _tscale):
         q, k, v = ctx.saved_tensors   # in jvp: the tensors given to save_for_forward
-        o, to, lse, tlse = J.jvpattn_fwd(q, k, v, _c(tq), _c(tk), _c(tv), mask=ctx.mask, causal=ctx.causal,
-                                         scale=ctx.scale)
+        m = ctx.mask
+        # an additive mask's tangent enters the score tangent; a boolean mask has none
+        tm = _c(tmask) if tmask is not None and m is not None and m.dtype != torch.bool else None
+        o, to, lse, tlse = J.jvpattn_fwd(q, k, v, _c(tq), _c(tk), _c(tv), mask=m, causal=ctx.causal,
+                                         scale=ctx.scale, tmask=tm)
         return to, None, None, None   # lse and the aux outputs are not differentiable
 
 
@@ -81,19 +88,22 @@ class _AttentionDual(torch.autograd.Function):
     """(O, dO) = fwd_dual(q, k, v, tq, tk, tv); lse and tlse ride along (not differentiable)."""
 
     @staticmethod
-    def forward(q, k, v, tq, tk, tv, mask, causal, scale):
-        return J.jvpattn_fwd(q, k, v, tq, tk, tv, mask=mask.t, causal=causal, scale=scale)
+    def forward(q, k, v, tq, tk, tv, mask, causal, scale, tmask):
+        return J.jvpattn_fwd(q, k, v, tq, tk, tv, mask=mask.t, causal=causal, scale=scale, tmask=tmask.t)
 
     @staticmethod
     def setup_context(ctx, inputs, output):
-        q, k, v, tq, tk, tv, mask, causal, scale = inputs
+        q, k, v, tq, tk, tv, mask, causal, scale, tmask = inputs
         o, to, lse, tlse = output
         ctx.save_for_backward(q, k, v, tq, tk, tv, o, to, lse, tlse)
-        ctx.mask, ctx.causal, ctx.scale = mask.t, causal, scale
+        ctx.mask, ctx.causal, ctx.scale, ctx.has_tmask = mask.t, causal, scale, tmask.t is not None
         ctx.mark_non_differentiable(lse, tlse)
 
     @staticmethod
     def backward(ctx, go, gto, _glse, _gtlse):
+        if ctx.has_tmask:
+            raise NotImplementedError("reverse mode through a mask tangent is not supported (jvpattn_bwd "
+                                      "differentiates the forward without one)")
         q, k, v, tq, tk, tv, o, to, lse, tlse = ctx.saved_tensors
         need = ctx.needs_input_grad
         # outputs for the cotangents of tq, tk, tv only where they are wanted (NULL: not computed)
@@ -102,16 +112,17 @@ class _AttentionDual(torch.autograd.Function):
                torch.empty_like(v) if need[5] else None)
         g = J.jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, _c(go), _c(gto), mask=ctx.mask,
                           causal=ctx.causal, scale=ctx.scale, out=out)
-        return tuple(x if need[i] else None for i, x in enumerate(g)) + (None, None, None)
+        return tuple(x if need[i] else None for i, x in enumerate(g)) + (None, None, None, None)
 
 
 def attention(q, k, v, attn_mask=None, is_causal=False, scale=None):
     """Scaled-dot-product attention (no dropout) with both derivative modes in libjvpattn."""
-    return _Attention.apply(q, k, v, _Const(attn_mask), bool(is_causal), scale)[0]
+    return _Attention.apply(q, k, v, attn_mask, bool(is_causal), scale)[0]
 
 
-def fwd_dual(q, k, v, tq, tk, tv, attn_mask=None, is_causal=False, scale=None):
-    """(O, dO): attention and its JVP along (tq, tk, tv); reverse-differentiable in all six inputs."""
+def fwd_dual(q, k, v, tq, tk, tv, attn_mask=None, is_causal=False, scale=None, tmask=None):
+    """(O, dO): attention and its JVP along (tq, tk, tv) and, if given, the additive mask's tangent
+    tmask; reverse-differentiable in all six inputs (without tmask)."""
     o, to, _, _ = _AttentionDual.apply(q, k, v, _c(tq), _c(tk), _c(tv), _Const(attn_mask), bool(is_causal),
-                                       scale)
+                                       scale, _Const(_c(tmask)))
     return o, to

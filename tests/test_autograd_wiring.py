@@ -19,11 +19,12 @@ def _np(t):
     return None if t is None else t.detach().double().numpy()
 
 
-def fake_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, scale=None, want_tlse=True, out=None):
+def fake_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, scale=None, want_tlse=True, out=None,
+             tmask=None):
     kind = "none" if mask is None else ("bool" if mask.dtype == torch.bool else "additive")
     m = None if mask is None else (mask.numpy().astype(np.uint8) if kind == "bool" else _np(mask))
     o, to, lse, tlse = oracle_fwd(_np(q), _np(k), _np(v), _np(tq), _np(tk), _np(tv), mask=m, mask_kind=kind,
-                                  causal=causal, scale=scale)
+                                  causal=causal, scale=scale, tmask=_np(tmask))
     T = lambda a: torch.from_numpy(a).to(q.dtype)
     return T(o), T(to), torch.from_numpy(lse).float(), torch.from_numpy(tlse).float()
 
@@ -102,3 +103,36 @@ def test_hessian_vector_product_matches_finite_differences():
     eps = 1e-6
     fd = (grad_f(q + eps * u) - grad_f(q - eps * u)) / (2 * eps)
     np.testing.assert_allclose(hvp.numpy(), fd.numpy(), rtol=0, atol=1e-7)
+
+
+def test_forward_mode_with_a_dual_additive_mask():
+    # the mask's tangent reaches the library call: the JVP along (tq, tk, tv, tm)
+    q, k, v, tq, tk, tv, _, _ = inputs(5)
+    g = torch.Generator().manual_seed(9)
+    m = torch.randn(1, 1, 7, 7, generator=g, dtype=torch.float64)
+    tm = torch.randn(1, 1, 7, 7, generator=g, dtype=torch.float64)
+    with fwAD.dual_level():
+        duals = [fwAD.make_dual(a, t) for a, t in ((q, tq), (k, tk), (v, tv), (m, tm))]
+        o, to = fwAD.unpack_dual(A.attention(*duals[:3], attn_mask=duals[3]))
+    ro, rto, _, _ = oracle_fwd(_np(q), _np(k), _np(v), _np(tq), _np(tk), _np(tv), mask=_np(m),
+                               mask_kind="additive", tmask=_np(tm))
+    np.testing.assert_allclose(_np(o), ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(_np(to), rto, rtol=0, atol=1e-12)
+    # fwd_dual takes the same tangent directly; reverse mode through it is refused
+    q.requires_grad_(True)
+    o2, to2 = A.fwd_dual(q, k, v, tq, tk, tv, attn_mask=m, tmask=tm)
+    np.testing.assert_allclose(_np(to2), rto, rtol=0, atol=1e-12)
+    with pytest.raises(NotImplementedError):
+        to2.sum().backward()
+
+
+def test_grouped_kv_heads_route_through():
+    # k, v with fewer heads than q: the library calls receive them as they are
+    g = torch.Generator().manual_seed(11)
+    r = lambda h: torch.randn(1, h, 6, 4, generator=g, dtype=torch.float64)
+    q, k, v, go = r(4), r(2), r(2), r(4)
+    q.requires_grad_(True), k.requires_grad_(True), v.requires_grad_(True)
+    A.attention(q, k, v).backward(go)
+    ref = oracle_bwd(_np(q), _np(k), _np(v), None, None, None, _np(go), np.zeros(q.shape))
+    for t, rr in zip((q, k, v), ref[:3]):
+        np.testing.assert_allclose(_np(t.grad), rr, rtol=0, atol=1e-12)
