@@ -53,6 +53,15 @@ import numpy as np
 MASK_NONE = "none"
 MASK_BOOL = "bool"
 MASK_ADDITIVE = "additive"
+MASK_BITS = "bits"
+
+
+def unpack_mask_bits(words, Nk):
+    """Boolean [..., Nk] from a bit-packed mask [..., ceil(Nk/32)] of 32-bit words:
+    key j is visible iff bit (j mod 32) of word j // 32 is set."""
+    w = np.asarray(words).astype(np.uint64)
+    j = np.arange(Nk)
+    return ((w[..., j // 32] >> (j % 32).astype(np.uint64)) & 1).astype(bool)
 
 
 def _f64(x):
@@ -83,6 +92,8 @@ def _head_bias(mask, mask_kind, b, h, nq_rows, Nk, causal, q_pos):
         rows = mb[np.zeros_like(q_pos) if mb.shape[0] == 1 else q_pos, :]
         if mask_kind == MASK_BOOL:
             M = np.where(rows != 0, 0.0, -np.inf)
+        elif mask_kind == MASK_BITS:
+            M = np.where(unpack_mask_bits(rows, Nk), 0.0, -np.inf)
         elif mask_kind == MASK_ADDITIVE:
             M = np.asarray(rows, dtype=np.float64).copy()
         else:
@@ -144,7 +155,9 @@ def oracle_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, mask_kind=MASK_NON
         dtype; they are widened to float64 here). A tangent given as None is zero.
     mask: [Bm, Hm, Nm, Nk] with Bm in {1, B}, Hm in {1, H}, Nm in {1, Nq_full} (one
         row: shared by every query, e.g. a key-padding mask); uint8/bool for
-        ``mask_kind="bool"``, float for ``"additive"``; None for ``"none"``.
+        ``mask_kind="bool"``, float for ``"additive"``, 32-bit words
+        [Bm, Hm, Nm, ceil(Nk/32)] for ``"bits"`` (a boolean mask, one bit per
+        key); None for ``"none"``.
     causal: key j visible to query i iff j <= i.
     scale: multiplies Q K^T and the score tangent; default 1/sqrt(d).
     q_pos: optional absolute indices of the given query rows (defaults to

@@ -150,6 +150,29 @@ def test_additive_mask_tangent_needs_additive_mask():
         oracle_fwd(*args, tmask=np.zeros((2, 1, 7, 9)))
 
 
+def test_bit_packed_mask_unpacks_as_numpy_unpackbits():
+    # bit j % 32 of 32-bit word j // 32: numpy's little-endian unpackbits of the words' bytes
+    rng = np.random.default_rng(49)
+    words = rng.integers(0, 2 ** 32, size=(3, 5), dtype=np.uint64).astype(np.uint32)
+    from oracle.attention import unpack_mask_bits
+    ref = np.unpackbits(words.astype("<u4").view(np.uint8), axis=-1, bitorder="little").astype(bool)
+    np.testing.assert_array_equal(unpack_mask_bits(words, 150), ref[:, :150])
+
+
+def test_bit_packed_mask_equals_bool_mask():
+    rng = np.random.default_rng(50)
+    args = make(rng, Nq=6, Nk=40)
+    keep = rng.random((2, 3, 6, 40)) < 0.6
+    keep[..., 0] = True
+    padded = np.zeros((2, 3, 6, 64), dtype=bool)
+    padded[..., :40] = keep
+    words = np.packbits(padded, axis=-1, bitorder="little").view("<u4")
+    a = oracle_fwd(*args, mask=keep.astype(np.uint8), mask_kind="bool")
+    b = oracle_fwd(*args, mask=words, mask_kind="bits")
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
 def test_matches_torch_sdpa_additive_mask_per_head():
     rng = np.random.default_rng(2)
     args = make(rng, Nq=6, Nk=8, d=4)
