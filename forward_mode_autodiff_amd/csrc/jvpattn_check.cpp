@@ -76,7 +76,7 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
   if (!std::isfinite(p->scale) || !(p->scale > 0.0f)) return JVPATTN_ERR_SCALE;
 
   if (p->mask_kind != JVPATTN_MASK_NONE && p->mask_kind != JVPATTN_MASK_BOOL &&
-      p->mask_kind != JVPATTN_MASK_ADDITIVE)
+      p->mask_kind != JVPATTN_MASK_ADDITIVE && p->mask_kind != JVPATTN_MASK_BITS)
     return JVPATTN_ERR_MASK;
   const bool has_mask = p->mask_kind != JVPATTN_MASK_NONE;
   const bool work = rows_q > 0;
@@ -85,7 +85,9 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
   if (has_mask) {
     if (work && !mask) return JVPATTN_ERR_MASK;
     if (p->mask_stride_b < 0 || p->mask_stride_h < 0 || p->mask_stride_q < 0) return JVPATTN_ERR_MASK;
-    mask_es = p->mask_kind == JVPATTN_MASK_BOOL ? 1 : es;
+    mask_es = p->mask_kind == JVPATTN_MASK_BOOL ? 1 : p->mask_kind == JVPATTN_MASK_BITS ? 4 : es;
+    // elements of one mask row: keys, or 32-bit words of 32 keys
+    const int64_t row = p->mask_kind == JVPATTN_MASK_BITS ? (int64_t(p->Nk) + 31) / 32 : p->Nk;
     // extent = largest element offset + 1
     int64_t eb, eh, eq, ext = 0;
     if (work && p->Nk > 0) {
@@ -97,13 +99,13 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
       ext += eh;
       if (ext > INT64_MAX - eq) return JVPATTN_ERR_MASK;
       ext += eq;
-      if (ext > INT64_MAX - p->Nk) return JVPATTN_ERR_MASK;
-      ext += p->Nk;
+      if (ext > INT64_MAX - row) return JVPATTN_ERR_MASK;
+      ext += row;
       if (!mul_ok(ext, mask_es, &mask_bytes)) return JVPATTN_ERR_MASK;
       // one head's slice (rows past Nq included) must be addressable with 31-bit byte offsets
       int64_t head_rows;
       if (!mul_ok(int64_t(p->Nq) + 128, p->mask_stride_q, &head_rows) ||
-          head_rows > (kHeadLimit / mask_es) - p->Nk - 64)
+          head_rows > (kHeadLimit / mask_es) - row - 64)
         return JVPATTN_ERR_MASK;
     }
   } else if (mask) {
@@ -190,6 +192,7 @@ int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void*
   if (rc != JVPATTN_OK) return rc;
   if (p->dtype != JVPATTN_F16 && p->dtype != JVPATTN_BF16) return JVPATTN_ERR_DTYPE;
   if (p->d != 64) return JVPATTN_ERR_HEADDIM;
+  if (p->mask_kind == JVPATTN_MASK_BITS) return JVPATTN_ERR_MASK;   // forward only
   const bool rows = sz.rows_q > 0, keys = sz.rows_k > 0;
   // go, gto may be NULL (zero cotangent); dtq, dtk, dtv may be NULL (not written)
   if (rows && (!tlse || !dq)) return JVPATTN_ERR_NULL;

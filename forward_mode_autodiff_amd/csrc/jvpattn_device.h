@@ -196,13 +196,14 @@ __device__ inline void ring_barrier() {
 
 // Internal mask kind: an additive mask together with its tangent dM, which
 // the score tangent gains (dS = scale (dQ K^T + Q dK^T) + dM).
-constexpr int kMaskAddT = 3;
+constexpr int kMaskAddT = 4;   // beyond the public jvpattn_mask_kind values
 
 // Mask values of one 32-key block for this lane's 16 keys, loaded ahead of use.
 template <int MASK> struct MaskVals {};
 template <> struct MaskVals<JVPATTN_MASK_BOOL> { uint32_t w[4]; };
 template <> struct MaskVals<JVPATTN_MASK_ADDITIVE> { uint2 w[4]; };
 template <> struct MaskVals<kMaskAddT> { uint2 w[4]; uint2 t[4]; };   // mask, its tangent
+template <> struct MaskVals<JVPATTN_MASK_BITS> { uint32_t w; };          // the block's word >> 4*hlf
 
 // Register r of this lane holds key k0 + 8*(r/4) + 4*hlf + r%4.
 // Args: any argument block with Nk, msq (mask row stride) and mask_vec.
@@ -225,6 +226,11 @@ __device__ inline void mask_load_t(MaskVals<kMaskAddT>& m, const Args& a, Rsrc m
 
 template <int MASK, typename Args>
 __device__ inline void mask_load(MaskVals<MASK>& m, const Args& a, Rsrc mr, int qi, int k0, int hlf) {
+  if constexpr (MASK == JVPATTN_MASK_BITS) {
+    // one 32-bit word holds the block (k0 is a multiple of 32); this lane's
+    // keys 4*hlf + 8g + e sit at bit 8g + e once shifted by 4*hlf
+    m.w = __builtin_amdgcn_raw_buffer_load_b32(mr, (qi * int(a.msq) + (k0 >> 5)) * 4, 0, 0) >> (4 * hlf);
+  }
   if constexpr (MASK == JVPATTN_MASK_BOOL || MASK == JVPATTN_MASK_ADDITIVE) {
     constexpr int es = MASK == JVPATTN_MASK_BOOL ? 1 : 2;
     // byte offset of (qi, k0 + 4*hlf) in this head's mask; rows past Nq are never stored
@@ -265,7 +271,11 @@ __device__ inline void mask_load(MaskVals<MASK>& m, const Args& a, Rsrc mr, int 
 // cx), scale q.k + M with one. PRESCALED: s already holds scale q.k.
 template <typename T, int MASK, bool PRESCALED>
 __device__ inline void mask_apply(f32x16& s, const MaskVals<MASK>& m, float scale) {
-  if constexpr (MASK == JVPATTN_MASK_BOOL) {
+  if constexpr (MASK == JVPATTN_MASK_BITS) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (((m.w >> (8 * (r >> 2) + (r & 3))) & 1u) == 0u) s[r] = -INFINITY;
+  } else if constexpr (MASK == JVPATTN_MASK_BOOL) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (((m.w[r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u) s[r] = -INFINITY;
@@ -309,12 +319,15 @@ __device__ inline void hide_keys(f32x16& s, int Nk, int qi, int k0, int hlf) {
 
 // Mask resource of head (b, h): element (i, j) at byte (i*msq + j) * es.
 // `base` is the mask (default) or a tensor laid out like it (its tangent).
+// A bit-packed mask (es = 4 with bits) has ceil(Nk/32) words per row.
 template <typename Args>
-__device__ inline Rsrc mask_rsrc(const Args& a, int b, int h, int es, const void* base = nullptr) {
+__device__ inline Rsrc mask_rsrc(const Args& a, int b, int h, int es, const void* base = nullptr,
+                                 bool bits = false) {
   const void* m = base ? base : a.mask;
   if (!m) return make_rsrc(a.q, 0);
   const int64_t off = (b * a.msb + h * a.msh) * es;
-  const int64_t bytes = (int64_t(a.Nq - 1) * a.msq + a.Nk) * es;
+  const int64_t row = bits ? (a.Nk + 31) >> 5 : a.Nk;
+  const int64_t bytes = (int64_t(a.Nq - 1) * a.msq + row) * es;
   return make_rsrc(static_cast<const char*>(m) + off, bytes);
 }
 

@@ -125,9 +125,20 @@ __device__ inline void key_tiles(const FwdArgs& a, Rsrc mr, int* red, int& t_lo,
     }
     __syncthreads();
     int lo = INT32_MAX, hi = -1;
-    for (int j = threadIdx.x; j < a.Nk; j += blockDim.x) {
+    if constexpr (MASK == JVPATTN_MASK_BITS) {
+      const int nw = (a.Nk + 31) >> 5;
+      for (int j = threadIdx.x; j < nw; j += blockDim.x) {
+        uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(mr, 4 * j, 0, 0);
+        if (j == nw - 1 && (a.Nk & 31)) w &= (1u << (a.Nk & 31)) - 1u;   // bits past Nk
+        if (w) {
+          lo = min(lo, 32 * j + int(__builtin_ctz(w)));
+          hi = max(hi, 32 * j + 31 - int(__builtin_clz(w)));
+        }
+      }
+    }
+    for (int j = threadIdx.x; MASK != JVPATTN_MASK_BITS && j < a.Nk; j += blockDim.x) {
       bool vis;
-      if constexpr (MASK == JVPATTN_MASK_BOOL) {
+      if constexpr (MASK == JVPATTN_MASK_BOOL || MASK == JVPATTN_MASK_BITS) {
         vis = __builtin_amdgcn_raw_buffer_load_b8(mr, j, 0, 0) != 0;
       } else if constexpr (ES == 2) {
         vis = T::widen(__builtin_amdgcn_raw_buffer_load_b16(mr, 2 * j, 0, 0)) != -INFINITY;
@@ -148,6 +159,13 @@ __device__ inline void key_tiles(const FwdArgs& a, Rsrc mr, int* red, int& t_lo,
     t_lo = hi < 0 ? 0 : red[0] >> 5;
     t_hi = hi < 0 ? 0 : (hi >> 5) + 1;
   }
+}
+
+// Bytes per mask element: uint8 for bool, 32-bit words for bit-packed masks,
+// else the additive values (value_bytes).
+template <int MASK>
+constexpr int mask_es(int value_bytes) {
+  return MASK == JVPATTN_MASK_BOOL ? 1 : MASK == JVPATTN_MASK_BITS ? 4 : value_bytes;
 }
 
 // Per-row softmax state for one lane (both lanes of a query column hold the same m).
@@ -297,7 +315,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     accT[t] = f32x16{};
   }
   RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
-  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+  const Rsrc mr = mask_rsrc(a, b, h, mask_es<MASK>(2), nullptr, MASK == JVPATTN_MASK_BITS);
   const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 2, a.tmask) : mr;
   auto load_mask = [&](MaskVals<MASK>& m, int k0) {
     if constexpr (MASK == kMaskAddT) mask_load_t(m, a, mr, mtr, qi, k0, hlf);
@@ -667,7 +685,7 @@ __global__ __launch_bounds__(64 * WV * SPLIT, (D == 64 && WV == 4) ? 2 : 1) void
   {
     int qb, bh;
     block_coords(a, qb, bh);
-    const Rsrc mr = mask_rsrc(a, bh / a.H, bh % a.H, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+    const Rsrc mr = mask_rsrc(a, bh / a.H, bh % a.H, mask_es<MASK>(2), nullptr, MASK == JVPATTN_MASK_BITS);
     key_tiles<T, MASK, 2>(a, mr, kred, t_lo, t_hi);
   }
   if constexpr (SPLIT == 1) {
@@ -770,7 +788,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
     accT[t] = f32x16{};
   }
   RowState16 st{0.0f, 0.0f, 0.0f, false};
-  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+  const Rsrc mr = mask_rsrc(a, b, h, mask_es<MASK>(2), nullptr, MASK == JVPATTN_MASK_BITS);
   const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 2, a.tmask) : mr;
   auto load_mask = [&](MaskVals<MASK>& m, int k0) {
     if constexpr (MASK == kMaskAddT) mask_load_t(m, a, mr, mtr, qi, k0, hlf);
@@ -1099,7 +1117,7 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
     accT[t] = f32x16{};
   }
   RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
-  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 4);
+  const Rsrc mr = mask_rsrc(a, b, h, mask_es<MASK>(4), nullptr, MASK == JVPATTN_MASK_BITS);
   const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 4, a.tmask) : mr;
   __shared__ int kred[2];
   int t0, t_hi;   // key tiles [t0, t_hi) may hold visible keys
@@ -1377,6 +1395,10 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
         e = c ? launch_pp<JVPATTN_MASK_BOOL, true>(p->dtype, pow2, a, grid, s)
               : launch_pp<JVPATTN_MASK_BOOL, false>(p->dtype, pow2, a, grid, s);
         break;
+      case JVPATTN_MASK_BITS:
+        e = c ? launch_pp<JVPATTN_MASK_BITS, true>(p->dtype, pow2, a, grid, s)
+              : launch_pp<JVPATTN_MASK_BITS, false>(p->dtype, pow2, a, grid, s);
+        break;
       default:
         if (tmask)
           e = c ? launch_pp<kMaskAddT, true>(p->dtype, pow2, a, grid, s)
@@ -1395,6 +1417,10 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
       case JVPATTN_MASK_BOOL:
         e = c ? launch_typed<JVPATTN_MASK_BOOL, true>(p->dtype, p->d, pow2, split, a, grid, s)
               : launch_typed<JVPATTN_MASK_BOOL, false>(p->dtype, p->d, pow2, split, a, grid, s);
+        break;
+      case JVPATTN_MASK_BITS:
+        e = c ? launch_typed<JVPATTN_MASK_BITS, true>(p->dtype, p->d, pow2, split, a, grid, s)
+              : launch_typed<JVPATTN_MASK_BITS, false>(p->dtype, p->d, pow2, split, a, grid, s);
         break;
       default:
         if (tmask)

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libjvpattn.so")
 
 JVPATTN_F32, JVPATTN_F16, JVPATTN_BF16 = 0, 1, 2
-JVPATTN_MASK_NONE, JVPATTN_MASK_BOOL, JVPATTN_MASK_ADDITIVE = 0, 1, 2
+JVPATTN_MASK_NONE, JVPATTN_MASK_BOOL, JVPATTN_MASK_ADDITIVE, JVPATTN_MASK_BITS = 0, 1, 2, 3
 ERRORS = {
     0: "JVPATTN_OK", -1: "JVPATTN_ERR_NULL", -2: "JVPATTN_ERR_SHAPE", -3: "JVPATTN_ERR_DTYPE",
     -4: "JVPATTN_ERR_HEADDIM", -5: "JVPATTN_ERR_MASK", -6: "JVPATTN_ERR_ALIGN", -7: "JVPATTN_ERR_SCALE",
@@ -129,11 +129,14 @@ def make_params(q, k, mask=None, causal=False, scale=None) -> tuple:
             mask = mask.view(torch.uint8)
         if mask.dtype == torch.uint8:
             p.mask_kind = JVPATTN_MASK_BOOL
+        elif mask.dtype == torch.int32:
+            p.mask_kind = JVPATTN_MASK_BITS   # bit-packed boolean mask (see pack_mask_bits)
         elif mask.dtype == q.dtype:
             p.mask_kind = JVPATTN_MASK_ADDITIVE
         else:
             raise TypeError("an additive mask must have the dtype of q")
-        if mask.shape[3] != Nk or mask.shape[2] not in (1, Nq) or mask.shape[1] not in (1, H) \
+        row = (Nk + 31) // 32 if p.mask_kind == JVPATTN_MASK_BITS else Nk
+        if mask.shape[3] != row or mask.shape[2] not in (1, Nq) or mask.shape[1] not in (1, H) \
                 or mask.shape[0] not in (1, B):
             raise ValueError(f"mask shape {tuple(mask.shape)} does not broadcast to {(B, H, Nq, Nk)}")
         if mask.stride(3) != 1:
@@ -148,6 +151,19 @@ def jvpattn_check_fwd_tmask(params: jvpattn_params, q, k, v, tq, tk, tv, mask, t
                                                   lse, tlse)
 
 
+def pack_mask_bits(mask):
+    """A boolean mask [..., Nk] as the library's bit-packed layout: int32 words [..., ceil(Nk/32)],
+    key j visible iff bit j % 32 of word j // 32 is set (8x fewer mask bytes than uint8)."""
+    m = mask.to(torch.bool)
+    nk = m.shape[-1]
+    nw = (nk + 31) // 32
+    pad = torch.zeros(*m.shape[:-1], nw * 32, dtype=torch.int64, device=m.device)
+    pad[..., :nk] = m.to(torch.int64)
+    bits = pad.reshape(*m.shape[:-1], nw, 32) << torch.arange(32, device=m.device, dtype=torch.int64)
+    words = bits.sum(-1)                                     # 0 .. 2^32 - 1
+    return torch.where(words >= 2 ** 31, words - 2 ** 32, words).to(torch.int32)
+
+
 def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, scale=None,
                 want_tlse=True, out=None, tmask=None):
     """O, dO, lse, tlse = jvpattn_fwd(q, k, v, tq, tk, tv, mask, causal, scale).
@@ -155,8 +171,9 @@ def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, sca
     q, tq: [B,H,Nq,d]; k, v, tk, tv: [B,Hkv,Nk,d] on the GPU, one dtype
     (float32 / float16 / bfloat16), contiguous; Hkv divides H (query head h
     reads key/value head h // (H // Hkv)). Tangents may be None (zero).
-    mask: None, a bool/uint8 tensor (True = attend) or an additive tensor of
-    q's dtype, broadcastable to [B,H,Nq,Nk]. ``tmask``: the tangent of an
+    mask: None, a bool/uint8 tensor (True = attend), a bit-packed boolean
+    mask (int32 words [.., ceil(Nk/32)], ``pack_mask_bits``) or an additive
+    tensor of q's dtype, broadcastable to [B,H,Nq,Nk]. ``tmask``: the tangent of an
     additive mask, shaped like it (jvpattn_fwd_tmask). Work is queued on
     torch's current stream. ``out`` optionally supplies (o, to, lse, tlse) buffers.
     """

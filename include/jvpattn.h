@@ -51,7 +51,10 @@ typedef enum {
 typedef enum {
   JVPATTN_MASK_NONE = 0,
   JVPATTN_MASK_BOOL = 1,      /* uint8 (torch.bool): nonzero = attend */
-  JVPATTN_MASK_ADDITIVE = 2   /* the element type above, added to scaled scores */
+  JVPATTN_MASK_ADDITIVE = 2,  /* the element type above, added to scaled scores */
+  JVPATTN_MASK_BITS = 3       /* a boolean mask, one bit per key: uint32 words, key j of a row
+                                 attends iff bit (j % 32) of the row's word j / 32 is set;
+                                 ceil(Nk / 32) words per row (forward only) */
 } jvpattn_mask_kind;
 
 /* Return codes. Every error is detected before any work is queued, so a
@@ -82,10 +85,11 @@ typedef struct {
   int32_t mask_kind;     /* jvpattn_mask_kind */
   int32_t causal;        /* 0 or 1 */
   /* Mask element (b, h, i, j) is at mask[b*mask_stride_b + h*mask_stride_h
-   * + i*mask_stride_q + j] (strides in elements, j contiguous). A stride of 0
-   * broadcasts that axis, e.g. a [B,1,Nq,Nk] mask has mask_stride_h = 0 and a
-   * key-padding mask [B,1,1,Nk] also has mask_stride_q = 0. Ignored when
-   * mask_kind is NONE. */
+   * + i*mask_stride_q + j] (strides in elements, j contiguous; for
+   * JVPATTN_MASK_BITS the elements are the 32-bit words and j the word index).
+   * A stride of 0 broadcasts that axis, e.g. a [B,1,Nq,Nk] mask has
+   * mask_stride_h = 0 and a key-padding mask [B,1,1,Nk] also has
+   * mask_stride_q = 0. Ignored when mask_kind is NONE. */
   int64_t mask_stride_b, mask_stride_h, mask_stride_q;
   float scale;           /* multiplies Q K^T and dQ K^T + Q dK^T; finite and > 0 (SDPA default 1/sqrt(d)) */
   /* Heads of k, v, tk, tv (grouped-query attention, as SDPA's enable_gqa):
@@ -181,7 +185,8 @@ int jvpattn_check_fwd_tmask(const jvpattn_params* params,
  * Outputs are fully overwritten and must not overlap an input, each other
  * or the workspace. Supported: float16 and bfloat16 with d = 64 (other
  * element types return JVPATTN_ERR_DTYPE, other d JVPATTN_ERR_HEADDIM,
- * before any work is queued). Arithmetic: products on the matrix cores with
+ * before any work is queued); masks NONE, BOOL and ADDITIVE (BITS returns
+ * JVPATTN_ERR_MASK). Arithmetic: products on the matrix cores with
  * float32 accumulation; the recomputed softmax weights, their tangents and
  * the score cotangents are rounded to the input type before the products
  * that consume them; results are rounded to nearest even. */

@@ -109,6 +109,22 @@ def test_check_accepts_valid_calls():
 
 
 @needs_lib
+def test_check_bit_packed_mask():
+    # rows of ceil(Nk/32) 32-bit words: Nk = 90 -> 3 words
+    p = good_params(mask_kind=J.JVPATTN_MASK_BITS, mask_stride_b=100 * 3, mask_stride_q=3)
+    P = ptrs(p)
+    assert call(p, P) == 0
+    assert call(p, P, mask=P["mask"] + 2) == -6                  # words are 4-byte aligned
+    nbytes = (2 * 100 * 3) * 4
+    assert call(p, P, o=P["mask"] + nbytes) == 0                 # right after the last word: no overlap
+    assert call(p, P, lse=P["mask"] + nbytes - 4) == -8          # overlapping the last word
+    # the reverse pass does not take them
+    pb = good_params(mask_kind=J.JVPATTN_MASK_BITS, mask_stride_b=100 * 3, mask_stride_q=3)
+    Q = bwd_ptrs(pb)
+    assert call_bwd(pb, Q) == -5
+
+
+@needs_lib
 def test_check_mask_tangent():
     p = good_params(mask_kind=J.JVPATTN_MASK_ADDITIVE, mask_stride_b=100 * 90, mask_stride_q=90)
     P = ptrs(p)
@@ -178,7 +194,7 @@ def test_check_rejects(case, code):
     elif case == "d_32":
         p.d = 32
     elif case == "kind":
-        p.mask_kind = 3
+        p.mask_kind = 5
     elif case == "mask_missing":
         p.mask_kind = J.JVPATTN_MASK_BOOL
         over["mask"] = None

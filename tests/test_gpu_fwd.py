@@ -526,3 +526,40 @@ def test_zero_mask_tangent_is_bit_identical(kernel):
     torch.cuda.synchronize()
     for u, t in zip(a, b):
         assert torch.equal(u, t)
+
+
+# ------------------------------------------------ bit-packed boolean masks
+
+@pytest.mark.parametrize("w", [
+    I.Workload("bits_full_f16", B=2, H=2, N=200, d=64, dtype="f16", mask_kind="bool", keep=0.7, std=1.0, seed=50),
+    I.Workload("bits_per_head_bf16_causal", B=1, H=3, N=257, d=64, dtype="bf16", causal=True, mask_kind="bool",
+               mask_heads=3, keep=0.6, std=1.0, seed=51),
+    I.Workload("bits_keypad_bf16", B=4, H=2, N=300, d=64, dtype="bf16", mask_kind="bool", mask_layout="pad_right",
+               std=1.0, seed=52, extra={"lengths": [0, 5, 300, 33]}),
+    I.Workload("bits_d128_bf16", B=1, H=2, N=150, d=128, dtype="bf16", mask_kind="bool", keep=0.8, std=1.0,
+               seed=53),
+    I.Workload("bits_f32_window", B=2, H=2, N=100, d=64, dtype="f32", mask_kind="bool", mask_layout="window",
+               std=1.0, seed=54),
+    I.Workload("bits_masked_spec", B=2, H=8, N=1024, d=64, dtype="f16", mask_kind="bool", seed=2),
+], ids=lambda w: w.name)
+def test_bit_packed_masks(w, kernel):
+    """A bit-packed mask gives the bool mask's results to within one rounding of each output (the two
+    builds are separate code, which the compiler may contract into fused multiply-adds differently),
+    and the oracle's."""
+    from forward_mode_autodiff_amd.jvpattn import pack_mask_bits
+    x = I.make_inputs(w)
+    d = to_dev(x)
+    bits = pack_mask_bits(d["mask"])
+    a = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=d["mask"], causal=w.causal)
+    b = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=bits, causal=w.causal)
+    torch.cuda.synchronize()
+    for u, t in zip(a, b):
+        fin = torch.isfinite(u)
+        assert torch.equal(fin, torch.isfinite(t)) and torch.equal(u[~fin], t[~fin])
+        ulp = torch.finfo(u.dtype).eps * float(u[fin].abs().max()) if fin.any() else 0.0
+        diff = (u[fin].float() - t[fin].float()).abs()
+        assert (float(diff.max()) if diff.numel() else 0.0) <= 2 * ulp
+    got = {"o": b[0].float().cpu(), "to": b[1].float().cpu(), "lse": b[2].cpu(), "tlse": b[3].cpu()}
+    r = oracle_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["tq"]), f64(x["tk"]), f64(x["tv"]),
+                   mask=bits.cpu().numpy(), mask_kind="bits", causal=w.causal)
+    assert_parity(got, dict(zip(("o", "to", "lse", "tlse"), r)), w.dtype, w.name, spec_spread=w.std is None)
