@@ -226,7 +226,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
     accQ[t] = f32x16{};
     accTQ[t] = f32x16{};
   }
-  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : MASK == JVPATTN_MASK_BITS ? 4 : 2, nullptr,
+                            MASK == JVPATTN_MASK_BITS);
 
   const int kv_end = CAUSAL ? min(a.Nk, q0 + kBBlk) : a.Nk;
   const int n_tiles = (kv_end + L::BN - 1) / L::BN;
@@ -558,7 +559,8 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
     const int bh = bhk * a.grp + g;
     const int h = bh % a.H;
     const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
-    const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : 2);
+    const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : MASK == JVPATTN_MASK_BITS ? 4 : 2,
+                              nullptr, MASK == JVPATTN_MASK_BITS);
 
     const int n_qt = (a.Nq + 31) / 32;
     // causal: queries before the block's first key see none of its keys
@@ -653,7 +655,15 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
         dm = T::mfma(tga[c], vB[c], dm);
       }
       // masks: element (query i, key kj); hidden entries get score -inf
-      if constexpr (MASK != JVPATTN_MASK_NONE) {
+      if constexpr (MASK == JVPATTN_MASK_BITS) {
+        // bit kj % 32 of the row's word kj / 32
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
+          const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(mr, (qrow * int(a.msq) + (kj >> 5)) * 4, 0, 0);
+          if (((w >> (kj & 31)) & 1u) == 0u) s[r] = -INFINITY;
+        }
+      } else if constexpr (MASK != JVPATTN_MASK_NONE) {
         constexpr int es = MASK == JVPATTN_MASK_BOOL ? 1 : 2;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -833,6 +843,7 @@ hipError_t launch_type(const BwdArgs& a, int mask_kind, bool causal, bool pow2, 
   switch (mask_kind) {
     case JVPATTN_MASK_NONE: return launch_mask<T, JVPATTN_MASK_NONE>(a, causal, pow2, s);
     case JVPATTN_MASK_BOOL: return launch_mask<T, JVPATTN_MASK_BOOL>(a, causal, pow2, s);
+    case JVPATTN_MASK_BITS: return launch_mask<T, JVPATTN_MASK_BITS>(a, causal, pow2, s);
     default: return launch_mask<T, JVPATTN_MASK_ADDITIVE>(a, causal, pow2, s);
   }
 }

@@ -192,7 +192,6 @@ int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void*
   if (rc != JVPATTN_OK) return rc;
   if (p->dtype != JVPATTN_F16 && p->dtype != JVPATTN_BF16) return JVPATTN_ERR_DTYPE;
   if (p->d != 64) return JVPATTN_ERR_HEADDIM;
-  if (p->mask_kind == JVPATTN_MASK_BITS) return JVPATTN_ERR_MASK;   // forward only
   const bool rows = sz.rows_q > 0, keys = sz.rows_k > 0;
   // go, gto may be NULL (zero cotangent); dtq, dtk, dtv may be NULL (not written)
   if (rows && (!tlse || !dq)) return JVPATTN_ERR_NULL;
@@ -208,9 +207,11 @@ int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void*
   const int64_t bq = sz.rows_q * p->d * sz.elem_bytes, bk = sz.rows_k * p->d * sz.elem_bytes;
   int64_t mask_bytes = 0;
   if (mask && rows && keys) {
-    const int mes = p->mask_kind == JVPATTN_MASK_BOOL ? 1 : sz.elem_bytes;
+    const bool bits = p->mask_kind == JVPATTN_MASK_BITS;
+    const int mes = p->mask_kind == JVPATTN_MASK_BOOL ? 1 : bits ? 4 : sz.elem_bytes;
+    const int64_t row = bits ? (int64_t(p->Nk) + 31) / 32 : p->Nk;
     mask_bytes = ((p->B - 1) * p->mask_stride_b + (p->H - 1) * p->mask_stride_h +
-                  (p->Nq - 1) * p->mask_stride_q + p->Nk) * mes;   // check_fwd proved this fits
+                  (p->Nq - 1) * p->mask_stride_q + row) * mes;   // check_fwd proved this fits
   }
   const Span ins[] = {span(q, bq),  span(k, bk),   span(v, bk),   span(tq, bq),    span(tk, bk),
                       span(tv, bk), span(mask, mask_bytes), span(o, bq), span(to, bq),

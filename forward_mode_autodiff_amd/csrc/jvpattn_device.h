@@ -229,7 +229,10 @@ __device__ inline void mask_load(MaskVals<MASK>& m, const Args& a, Rsrc mr, int 
   if constexpr (MASK == JVPATTN_MASK_BITS) {
     // one 32-bit word holds the block (k0 is a multiple of 32); this lane's
     // keys 4*hlf + 8g + e sit at bit 8g + e once shifted by 4*hlf
-    m.w = __builtin_amdgcn_raw_buffer_load_b32(mr, (qi * int(a.msq) + (k0 >> 5)) * 4, 0, 0) >> (4 * hlf);
+    // (a rotation rather than a shift: the bits read stay below bit 28, and the compiler keeps one
+    // rotate instead of folding the lane's offset into every bit extraction)
+    const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(mr, (qi * int(a.msq) + (k0 >> 5)) * 4, 0, 0);
+    m.w = __builtin_amdgcn_alignbit(w, w, 4 * hlf);
   }
   if constexpr (MASK == JVPATTN_MASK_BOOL || MASK == JVPATTN_MASK_ADDITIVE) {
     constexpr int es = MASK == JVPATTN_MASK_BOOL ? 1 : 2;
@@ -272,9 +275,12 @@ __device__ inline void mask_load(MaskVals<MASK>& m, const Args& a, Rsrc mr, int 
 template <typename T, int MASK, bool PRESCALED>
 __device__ inline void mask_apply(f32x16& s, const MaskVals<MASK>& m, float scale) {
   if constexpr (MASK == JVPATTN_MASK_BITS) {
+    // the key's bit sign-extended to all ones or zero selects the score or -inf (bitfield insert)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (((m.w >> (8 * (r >> 2) + (r & 3))) & 1u) == 0u) s[r] = -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t sel = uint32_t(__builtin_amdgcn_sbfe(int(m.w), 8 * (r >> 2) + (r & 3), 1));
+      s[r] = __uint_as_float((__float_as_uint(s[r]) & sel) | (0xff800000u & ~sel));
+    }
   } else if constexpr (MASK == JVPATTN_MASK_BOOL) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)

@@ -54,7 +54,7 @@ typedef enum {
   JVPATTN_MASK_ADDITIVE = 2,  /* the element type above, added to scaled scores */
   JVPATTN_MASK_BITS = 3       /* a boolean mask, one bit per key: uint32 words, key j of a row
                                  attends iff bit (j % 32) of the row's word j / 32 is set;
-                                 ceil(Nk / 32) words per row (forward only) */
+                                 ceil(Nk / 32) words per row */
 } jvpattn_mask_kind;
 
 /* Return codes. Every error is detected before any work is queued, so a
@@ -185,8 +185,7 @@ int jvpattn_check_fwd_tmask(const jvpattn_params* params,
  * Outputs are fully overwritten and must not overlap an input, each other
  * or the workspace. Supported: float16 and bfloat16 with d = 64 (other
  * element types return JVPATTN_ERR_DTYPE, other d JVPATTN_ERR_HEADDIM,
- * before any work is queued); masks NONE, BOOL and ADDITIVE (BITS returns
- * JVPATTN_ERR_MASK). Arithmetic: products on the matrix cores with
+ * before any work is queued); every mask kind. Arithmetic: products on the matrix cores with
  * float32 accumulation; the recomputed softmax weights, their tangents and
  * the score cotangents are rounded to the input type before the products
  * that consume them; results are rounded to nearest even. */

@@ -118,10 +118,11 @@ def test_check_bit_packed_mask():
     nbytes = (2 * 100 * 3) * 4
     assert call(p, P, o=P["mask"] + nbytes) == 0                 # right after the last word: no overlap
     assert call(p, P, lse=P["mask"] + nbytes - 4) == -8          # overlapping the last word
-    # the reverse pass does not take them
+    # the reverse pass takes them too, with the same extent in words
     pb = good_params(mask_kind=J.JVPATTN_MASK_BITS, mask_stride_b=100 * 3, mask_stride_q=3)
     Q = bwd_ptrs(pb)
-    assert call_bwd(pb, Q) == -5
+    assert call_bwd(pb, Q) == 0
+    assert call_bwd(pb, Q, dq=Q["mask"] + nbytes - 16) == -8
 
 
 @needs_lib

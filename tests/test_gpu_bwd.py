@@ -267,3 +267,24 @@ def test_key_masks(layout, kind):
     w = I.Workload(f"keymask_bwd_{layout}", B=3, H=2, N=180, d=64, dtype="bf16", mask_kind=kind, mask_layout=layout,
                    std=1.0, seed=23)
     check(w)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bit_packed_masks(causal):
+    """The reverse pass with a bit-packed mask: the bool mask's cotangents (the oracle's bar)."""
+    from forward_mode_autodiff_amd.jvpattn import pack_mask_bits
+    w = I.Workload("bits_bwd", B=2, H=2, N=190, d=64, dtype="bf16", causal=causal, mask_kind="bool", keep=0.7,
+                   std=1.0, seed=24)
+    x = I.make_inputs(w, cotangents=True)
+    xb = dict(x, mask=pack_mask_bits(x["mask"]))
+    d = {k: (None if v is None else v.to(DEV)) for k, v in xb.items()}
+    o, to, lse, tlse = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=d["mask"], causal=causal)
+    g = jvpattn_bwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], o, to, lse, tlse, d["do"], d["dto"],
+                    mask=d["mask"], causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["tq"]), f64(x["tk"]), f64(x["tv"]),
+                     f64(x["do"]), f64(x["dto"]), mask=x["mask"].numpy(), mask_kind="bool", causal=causal)
+    M = term_magnitudes(x, w, ("tq", "tk", "tv"), None)
+    for n, gg, r in zip(NAMES, g, ref):
+        err = float(np.max(np.abs(gg.float().cpu().numpy() - r)))
+        assert err <= RHO[w.dtype] * M[n], (n, err, M[n])
