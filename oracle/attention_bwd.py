@@ -37,11 +37,14 @@ import numpy as np
 from .attention import MASK_NONE, _f64, _head_bias, kv_head
 
 
-def oracle_bwd_head(q, k, v, tq, tk, tv, go, gto, bias, scale):
-    """One head. Returns the cotangents (gq, gk, gv, gtq, gtk, gtv) in float64."""
+def oracle_bwd_head(q, k, v, tq, tk, tv, go, gto, bias, scale, tbias=None):
+    """One head. Returns the cotangents (gq, gk, gv, gtq, gtk, gtv) in float64.
+    tbias: tangent of an additive mask (a constant of the map, like the mask), or None."""
     # forward, keeping the intermediates
     S = scale * (q @ k.T) + bias
     dS = scale * (tq @ k.T + q @ tk.T)
+    if tbias is not None:
+        dS = dS + tbias
     live = ~np.all(np.isneginf(S), axis=1)
     P = np.zeros_like(S)
     if np.any(live):
@@ -78,12 +81,15 @@ def oracle_bwd_head(q, k, v, tq, tk, tv, go, gto, bias, scale):
     return g_q, g_k, g_v, g_tq, g_tk, g_tv
 
 
-def oracle_bwd(q, k, v, tq, tk, tv, go, gto, mask=None, mask_kind=MASK_NONE, causal=False, scale=None):
+def oracle_bwd(q, k, v, tq, tk, tv, go, gto, mask=None, mask_kind=MASK_NONE, causal=False, scale=None,
+               tmask=None):
     """Cotangents of (Q, K, V, dQ, dK, dV) for cotangents (go, gto) of (O, dO).
 
     Shapes as in ``oracle_fwd``: q, tq, go, gto [B,H,Nq,d]; k, v, tk, tv
     [B,Hkv,Nk,d] (Hkv divides H); mask [Bm,Hm,Nq,Nk]. A tangent given as None
-    is zero.
+    is zero. tmask: tangent of an additive mask, laid out as ``mask``: the
+    forward it differentiates then carries dS + dM (no cotangent of the mask
+    or its tangent is returned).
     Returns (gq, gk, gv, gtq, gtk, gtv) float64, shaped like the inputs.
     """
     q, k, v, go, gto = _f64(q), _f64(k), _f64(v), _f64(go), _f64(gto)
@@ -105,8 +111,9 @@ def oracle_bwd(q, k, v, tq, tk, tv, go, gto, mask=None, mask_kind=MASK_NONE, cau
         for h in range(H):
             g = kv_head(h, H, Hkv)
             bias = _head_bias(mask, mask_kind, b, h, Nq, Nk, causal, q_pos)
+            tbias = None if tmask is None else _head_bias(np.asarray(tmask), "additive", b, h, Nq, Nk, False, q_pos)
             r = oracle_bwd_head(q[b, h], k[b, g], v[b, g], tq[b, h], tk[b, g], tv[b, g], go[b, h], gto[b, h],
-                                bias, scale)
+                                bias, scale, tbias)
             gq[b, h], gtq[b, h] = r[0], r[3]
             gk[b, g] += r[1]
             gv[b, g] += r[2]

@@ -226,3 +226,25 @@ def test_grouped_head_mutants_fail_the_autograd_pin(monkeypatch):
     exec(compile(src, "<mutant>", "exec"), ns)
     got = ns["oracle_bwd"](x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], x["go"], x["gto"])
     assert float(np.max(np.abs(got[1] - ref[1]))) > 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_autograd_with_mask_tangent(causal):
+    # reverse mode over the forward-mode pass along (dQ, dK, dV, dM): torch.func.jvp through SDPA with the
+    # additive mask as a differentiated input, then autograd back to the six tensors
+    rng = np.random.default_rng(42)
+    x = make(rng, Nq=6, Nk=8, d=4)
+    m = rng.standard_normal((2, 1, 6, 8))
+    m[1, ..., 5:] = -np.inf
+    tm = rng.standard_normal((2, 1, 6, 8))
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).requires_grad_(True)
+    ins = [T(x[n]) for n in ("q", "k", "v", "tq", "tk", "tv")]
+    mm, tt = torch.from_numpy(m), torch.from_numpy(tm)
+    with sdpa_kernel(SDPBackend.MATH):
+        o, to = torch.func.jvp(
+            lambda a, b, c, mk: F.scaled_dot_product_attention(a, b, c, attn_mask=mk, is_causal=causal),
+            (ins[0], ins[1], ins[2], mm), (ins[3], ins[4], ins[5], tt))
+        L = (o * torch.from_numpy(x["go"])).sum() + (to * torch.from_numpy(x["gto"])).sum()
+        ref = [t.numpy() for t in torch.autograd.grad(L, ins)]
+    got = run_bwd(x, mask=m, mask_kind="additive", causal=causal, tmask=tm)
+    assert_close(got, ref, 1e-11)
