@@ -239,10 +239,12 @@ def test_matches_torch_autograd_with_mask_tangent(causal):
     tm = rng.standard_normal((2, 1, 6, 8))
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).requires_grad_(True)
     ins = [T(x[n]) for n in ("q", "k", "v", "tq", "tk", "tv")]
-    mm, tt = torch.from_numpy(m), torch.from_numpy(tm)
+    # SDPA takes no explicit mask with is_causal: fold the causal cut into its mask (j <= i visible)
+    cut = np.where(np.arange(8)[None, :] <= np.arange(6)[:, None], 0.0, -np.inf) if causal else 0.0
+    mm, tt = torch.from_numpy(m + cut), torch.from_numpy(tm)
     with sdpa_kernel(SDPBackend.MATH):
         o, to = torch.func.jvp(
-            lambda a, b, c, mk: F.scaled_dot_product_attention(a, b, c, attn_mask=mk, is_causal=causal),
+            lambda a, b, c, mk: F.scaled_dot_product_attention(a, b, c, attn_mask=mk),
             (ins[0], ins[1], ins[2], mm), (ins[3], ins[4], ins[5], tt))
         L = (o * torch.from_numpy(x["go"])).sum() + (to * torch.from_numpy(x["gto"])).sum()
         ref = [t.numpy() for t in torch.autograd.grad(L, ins)]
