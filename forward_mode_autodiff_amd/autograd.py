@@ -20,7 +20,7 @@ supplies tensors, the autograd graph and streams.
 ``fwd_dual(q, k, v, tq, tk, tv, attn_mask=None, is_causal=False, scale=None, tmask=None)``
     the pair (O, dO) -- the output and its JVP, along the additive mask's
     tangent ``tmask`` as well when given -- differentiable in reverse mode
-    with respect to all six inputs (jvpattn_bwd; not with a mask tangent). A
+    with respect to all six inputs (jvpattn_bwd, jvpattn_bwd_tmask). A
     Hessian-vector product of a loss is reverse mode over this pair.
 
 Inputs: q [B, H, N, d], k and v [B, Hkv, N, d] (Hkv dividing H: grouped
@@ -96,14 +96,11 @@ class _AttentionDual(torch.autograd.Function):
         q, k, v, tq, tk, tv, mask, causal, scale, tmask = inputs
         o, to, lse, tlse = output
         ctx.save_for_backward(q, k, v, tq, tk, tv, o, to, lse, tlse)
-        ctx.mask, ctx.causal, ctx.scale, ctx.has_tmask = mask.t, causal, scale, tmask.t is not None
+        ctx.mask, ctx.causal, ctx.scale, ctx.tmask = mask.t, causal, scale, tmask.t
         ctx.mark_non_differentiable(lse, tlse)
 
     @staticmethod
     def backward(ctx, go, gto, _glse, _gtlse):
-        if ctx.has_tmask:
-            raise NotImplementedError("reverse mode through a mask tangent is not supported (jvpattn_bwd "
-                                      "differentiates the forward without one)")
         q, k, v, tq, tk, tv, o, to, lse, tlse = ctx.saved_tensors
         need = ctx.needs_input_grad
         # outputs for the cotangents of tq, tk, tv only where they are wanted (NULL: not computed)
@@ -111,7 +108,7 @@ class _AttentionDual(torch.autograd.Function):
                torch.empty_like(q) if need[3] else None, torch.empty_like(k) if need[4] else None,
                torch.empty_like(v) if need[5] else None)
         g = J.jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, _c(go), _c(gto), mask=ctx.mask,
-                          causal=ctx.causal, scale=ctx.scale, out=out)
+                          causal=ctx.causal, scale=ctx.scale, out=out, tmask=ctx.tmask)
         return tuple(x if need[i] else None for i, x in enumerate(g)) + (None, None, None, None)
 
 
@@ -122,7 +119,7 @@ def attention(q, k, v, attn_mask=None, is_causal=False, scale=None):
 
 def fwd_dual(q, k, v, tq, tk, tv, attn_mask=None, is_causal=False, scale=None, tmask=None):
     """(O, dO): attention and its JVP along (tq, tk, tv) and, if given, the additive mask's tangent
-    tmask; reverse-differentiable in all six inputs (without tmask)."""
+    tmask; reverse-differentiable in all six inputs."""
     o, to, _, _ = _AttentionDual.apply(q, k, v, _c(tq), _c(tk), _c(tv), _Const(attn_mask), bool(is_causal),
                                        scale, _Const(_c(tmask)))
     return o, to

@@ -49,6 +49,7 @@ struct BwdArgs {
   const void* tk;
   const void* tv;
   const void* mask;
+  const void* tmask;  // tangent of the additive mask (kind kMaskAddT), laid out as the mask
   const void* o;
   const void* to;
   const void* go;
@@ -70,6 +71,7 @@ struct BwdArgs {
   int mask_vec;
   int64_t msb, msh, msq;
   float scale;
+  float inv_scale;    // 1 / scale
   float cx;           // score units -> log2 units
 };
 
@@ -228,6 +230,11 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   }
   const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : MASK == JVPATTN_MASK_BITS ? 4 : 2, nullptr,
                             MASK == JVPATTN_MASK_BITS);
+  const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 2, a.tmask) : mr;
+  auto load_mask = [&](MaskVals<MASK>& m, int k0) {
+    if constexpr (MASK == kMaskAddT) mask_load_t(m, a, mr, mtr, qi, k0, hlf);
+    else mask_load<MASK>(m, a, mr, qi, k0, hlf);
+  };
 
   const int kv_end = CAUSAL ? min(a.Nk, q0 + kBBlk) : a.Nk;
   const int n_tiles = (kv_end + L::BN - 1) / L::BN;
@@ -323,6 +330,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   // Element-wise step of block k: score cotangents as 16-bit B operands.
   auto vphase = [&](int k, SPh& p, const MaskVals<MASK>& mk, bool keymask, vec8 (&sB)[2], vec8 (&sdB)[2]) {
     mask_apply<T, MASK, POW2>(p.s, mk, a.scale);
+    mask_tangent<T, MASK>(p.sd, mk, POW2 ? 1.0f : a.inv_scale);
     if (keymask) hide_keys<CAUSAL>(p.s, a.Nk, qi, k * 32, hlf);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -370,7 +378,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
     if (k + 2 < n_tiles) wait_vmcnt<L::TILE_VMEM>();   // tile k+1 (tile k+2 may stay in flight)
     else wait_vmcnt<0>();
     ring_barrier();
-    mask_load<MASK>(mn, a, mr, qi, (k + 1) * 32, hlf);
+    load_mask(mn, (k + 1) * 32);
     if (k + 3 < n_tiles) issue_tile(k + 3, dma);
     sphase(nxt, pn);
     vec8 sB[2], sdB[2];
@@ -404,7 +412,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   bool ready = false;   // pa holds the current block's score-side products
   if (0 <= last && !needs_keymask(0)) {
     sphase(stage0, pa);
-    mask_load<MASK>(mka, a, mr, qi, 0, hlf);
+    load_mask(mka, 0);
     ready = true;
   }
   const int kfast = ready ? jm - 1 : 0;   // blocks 0 .. kfast-1 are pipelined
@@ -441,7 +449,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
     const char* cur = stage_of(k);
     if (!ready) {
       sphase(cur, pa);
-      mask_load<MASK>(mka, a, mr, qi, k * 32, hlf);
+      load_mask(mka, k * 32);
     }
     vec8 sB[2], sdB[2];
     vphase(k, pa, mka, needs_keymask(k), sB, sdB);
@@ -561,6 +569,7 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
     const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
     const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : MASK == JVPATTN_MASK_BITS ? 4 : 2,
                               nullptr, MASK == JVPATTN_MASK_BITS);
+    const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 2, a.tmask) : mr;
 
     const int n_qt = (a.Nq + 31) / 32;
     // causal: queries before the block's first key see none of its keys
@@ -674,6 +683,9 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
           } else {
             const float m = T::widen(__builtin_amdgcn_raw_buffer_load_b16(mr, off, 0, 0));
             s[r] = POW2 ? s[r] + m : fmaf(s[r], a.scale, m);
+            if constexpr (MASK == kMaskAddT)   // the mask's tangent joins the score tangent (sd * us = dS)
+              sd[r] = fmaf(T::widen(__builtin_amdgcn_raw_buffer_load_b16(mtr, off, 0, 0)), POW2 ? 1.0f : a.inv_scale,
+                           sd[r]);
           }
         }
       }
@@ -844,27 +856,22 @@ hipError_t launch_type(const BwdArgs& a, int mask_kind, bool causal, bool pow2, 
     case JVPATTN_MASK_NONE: return launch_mask<T, JVPATTN_MASK_NONE>(a, causal, pow2, s);
     case JVPATTN_MASK_BOOL: return launch_mask<T, JVPATTN_MASK_BOOL>(a, causal, pow2, s);
     case JVPATTN_MASK_BITS: return launch_mask<T, JVPATTN_MASK_BITS>(a, causal, pow2, s);
+    case kMaskAddT: return launch_mask<T, kMaskAddT>(a, causal, pow2, s);
     default: return launch_mask<T, JVPATTN_MASK_ADDITIVE>(a, causal, pow2, s);
   }
 }
 
-}  // namespace
-}  // namespace jvpattn
-
-extern "C" int jvpattn_bwd(const jvpattn_params* p, const void* q, const void* k, const void* v,
-                           const void* tq, const void* tk, const void* tv, const void* mask, const void* o,
-                           const void* to, const float* lse, const float* tlse, const void* go,
-                           const void* gto, void* dq, void* dk, void* dv, void* dtq, void* dtk, void* dtv,
-                           void* workspace, size_t workspace_bytes, void* stream) {
-  using namespace jvpattn;
-  FwdSizes sz;
-  const int rc = check_bwd(p, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk, dtv,
-                           workspace, workspace_bytes, &sz);
-  if (rc != JVPATTN_OK) return rc;
+// Queue the reverse pass for arguments already validated; tmask: the
+// additive mask's tangent the forward carried, or NULL.
+int bwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const void* k, const void* v,
+               const void* tq, const void* tk, const void* tv, const void* mask, const void* tmask,
+               const void* o, const void* to, const float* lse, const float* tlse, const void* go,
+               const void* gto, void* dq, void* dk, void* dv, void* dtq, void* dtk, void* dtv, void* workspace,
+               void* stream) {
   if (sz.rows_q == 0 && sz.rows_k == 0) return JVPATTN_OK;
 
   BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv; a.mask = mask;
+  a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv; a.mask = mask; a.tmask = tmask;
   a.o = o; a.to = to; a.go = go; a.gto = gto; a.lse = lse; a.tlse = tlse;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dtq = dtq; a.dtk = dtk; a.dtv = dtv;
   a.ws = static_cast<float*>(workspace);
@@ -875,12 +882,14 @@ extern "C" int jvpattn_bwd(const jvpattn_params* p, const void* q, const void* k
   a.n_blk = 0;
   a.msb = p->mask_stride_b; a.msh = p->mask_stride_h; a.msq = p->mask_stride_q;
   a.scale = p->scale;
+  a.inv_scale = 1.0f / p->scale;
   a.mask_vec = 0;
   {
     const int mes = p->mask_kind == JVPATTN_MASK_BOOL ? 1 : elem_bytes(p->dtype);
     const uintptr_t base = reinterpret_cast<uintptr_t>(mask);
+    const uintptr_t tbase = reinterpret_cast<uintptr_t>(tmask);   // read with the same offsets
     a.mask_vec = mask && (p->mask_stride_b % 4 == 0) && (p->mask_stride_h % 4 == 0) &&
-                 (p->mask_stride_q % 4 == 0) && (base % (4 * mes) == 0);
+                 (p->mask_stride_q % 4 == 0) && (base % (4 * mes) == 0) && (tbase % (4 * mes) == 0);
   }
   const bool additive = p->mask_kind == JVPATTN_MASK_ADDITIVE;
   int sexp = 0;
@@ -898,12 +907,45 @@ extern "C" int jvpattn_bwd(const jvpattn_params* p, const void* q, const void* k
   }
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) {
-    e = p->dtype == JVPATTN_BF16 ? launch_type<BF16>(a, p->mask_kind, p->causal != 0, pow2, s)
-                                 : launch_type<F16>(a, p->mask_kind, p->causal != 0, pow2, s);
+    const int kind = tmask ? kMaskAddT : p->mask_kind;
+    e = p->dtype == JVPATTN_BF16 ? launch_type<BF16>(a, kind, p->causal != 0, pow2, s)
+                                 : launch_type<F16>(a, kind, p->causal != 0, pow2, s);
   }
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
     return JVPATTN_ERR_HIP;
   }
   return JVPATTN_OK;
+}
+
+}  // namespace
+}  // namespace jvpattn
+
+extern "C" int jvpattn_bwd(const jvpattn_params* p, const void* q, const void* k, const void* v,
+                           const void* tq, const void* tk, const void* tv, const void* mask, const void* o,
+                           const void* to, const float* lse, const float* tlse, const void* go,
+                           const void* gto, void* dq, void* dk, void* dv, void* dtq, void* dtk, void* dtv,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace jvpattn;
+  FwdSizes sz;
+  const int rc = check_bwd(p, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk, dtv,
+                           workspace, workspace_bytes, &sz);
+  if (rc != JVPATTN_OK) return rc;
+  return bwd_launch(p, sz, q, k, v, tq, tk, tv, mask, nullptr, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk,
+                    dtv, workspace, stream);
+}
+
+extern "C" int jvpattn_bwd_tmask(const jvpattn_params* p, const void* q, const void* k, const void* v,
+                                 const void* tq, const void* tk, const void* tv, const void* mask,
+                                 const void* tmask, const void* o, const void* to, const float* lse,
+                                 const float* tlse, const void* go, const void* gto, void* dq, void* dk, void* dv,
+                                 void* dtq, void* dtk, void* dtv, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  using namespace jvpattn;
+  FwdSizes sz;
+  const int rc = check_bwd_tmask(p, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, go, gto, dq, dk, dv, dtq,
+                                 dtk, dtv, workspace, workspace_bytes, &sz);
+  if (rc != JVPATTN_OK) return rc;
+  return bwd_launch(p, sz, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk,
+                    dtv, workspace, stream);
 }

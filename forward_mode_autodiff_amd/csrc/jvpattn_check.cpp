@@ -232,7 +232,46 @@ int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void*
   return JVPATTN_OK;
 }
 
+int check_bwd_tmask(const jvpattn_params* p, const void* q, const void* k, const void* v,
+                    const void* tq, const void* tk, const void* tv, const void* mask, const void* tmask,
+                    const void* o, const void* to, const float* lse, const float* tlse,
+                    const void* go, const void* gto, const void* dq, const void* dk, const void* dv,
+                    const void* dtq, const void* dtk, const void* dtv, const void* workspace,
+                    size_t workspace_bytes, FwdSizes* sizes) {
+  FwdSizes sz;
+  int rc = check_bwd(p, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk, dtv,
+                     workspace, workspace_bytes, &sz);
+  if (rc != JVPATTN_OK) return rc;
+  // the forward's rules for tmask (o, to, lse, tlse as the spans it must avoid) ...
+  rc = check_fwd_tmask(p, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, nullptr);
+  if (rc != JVPATTN_OK) return rc;
+  // ... and none of the reverse pass's outputs or workspace may overlap it
+  if (tmask && sz.rows_q > 0 && p->Nk > 0) {
+    const int64_t bytes = ((p->B - 1) * p->mask_stride_b + (p->H - 1) * p->mask_stride_h +
+                           (p->Nq - 1) * p->mask_stride_q + p->Nk) * sz.elem_bytes;
+    const int64_t bq = sz.rows_q * p->d * sz.elem_bytes, bk = sz.rows_k * p->d * sz.elem_bytes;
+    const Span t = span(tmask, bytes);
+    const Span outs[] = {span(dq, bq), span(dk, bk), span(dv, bk), span(dtq, bq), span(dtk, bk), span(dtv, bk)};
+    for (const Span& x : outs)
+      if (overlap(t, x)) return JVPATTN_ERR_ALIAS;
+    if (overlap(t, span(workspace, bwd_workspace_bytes(sz.rows_q)))) return JVPATTN_ERR_WORKSPACE;
+  }
+  if (sizes) *sizes = sz;
+  return JVPATTN_OK;
+}
+
 }  // namespace jvpattn
+
+extern "C" int jvpattn_check_bwd_tmask(const jvpattn_params* params, const void* q, const void* k,
+                                       const void* v, const void* tq, const void* tk, const void* tv,
+                                       const void* mask, const void* tmask, const void* o, const void* to,
+                                       const float* lse, const float* tlse, const void* go, const void* gto,
+                                       const void* dq, const void* dk, const void* dv, const void* dtq,
+                                       const void* dtk, const void* dtv, const void* workspace,
+                                       size_t workspace_bytes) {
+  return jvpattn::check_bwd_tmask(params, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, go, gto, dq, dk,
+                                  dv, dtq, dtk, dtv, workspace, workspace_bytes, nullptr);
+}
 
 extern "C" int jvpattn_last_hip_error(void) { return jvpattn::g_last_hip_error; }
 

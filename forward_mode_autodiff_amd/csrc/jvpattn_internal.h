@@ -39,6 +39,15 @@ int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void*
               const void* dtq, const void* dtk, const void* dtv, const void* workspace,
               size_t workspace_bytes, FwdSizes* sizes);
 
+// check_bwd, then the additive mask's tangent as check_fwd_tmask checks it,
+// also disjoint from the gradients and the workspace.
+int check_bwd_tmask(const jvpattn_params* p, const void* q, const void* k, const void* v,
+                    const void* tq, const void* tk, const void* tv, const void* mask, const void* tmask,
+                    const void* o, const void* to, const float* lse, const float* tlse,
+                    const void* go, const void* gto, const void* dq, const void* dk, const void* dv,
+                    const void* dtq, const void* dtk, const void* dtv, const void* workspace,
+                    size_t workspace_bytes, FwdSizes* sizes);
+
 // HIP error of the most recent JVPATTN_ERR_HIP on this thread (jvpattn_last_hip_error).
 extern thread_local int g_last_hip_error;
 

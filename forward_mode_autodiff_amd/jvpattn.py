@@ -74,6 +74,10 @@ def load_library(path: str = LIB_PATH):
     lib.jvpattn_check_bwd.restype = ctypes.c_int
     lib.jvpattn_bwd.argtypes = [P] + [vp] * 20 + [ctypes.c_size_t, vp]
     lib.jvpattn_bwd.restype = ctypes.c_int
+    lib.jvpattn_bwd_tmask.argtypes = [P] + [vp] * 21 + [ctypes.c_size_t, vp]
+    lib.jvpattn_bwd_tmask.restype = ctypes.c_int
+    lib.jvpattn_check_bwd_tmask.argtypes = [P] + [vp] * 21 + [ctypes.c_size_t]
+    lib.jvpattn_check_bwd_tmask.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -189,17 +193,7 @@ def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, sca
             raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
     p, mask = make_params(q, k, mask, causal, scale)
     if tmask is not None:
-        if p.mask_kind != JVPATTN_MASK_ADDITIVE:
-            raise ValueError("tmask needs an additive mask")
-        if not tmask.is_cuda or tmask.dtype != mask.dtype:
-            raise ValueError("tmask must be a GPU tensor of the mask's dtype")
-        tmask = _as_4d(tmask)
-        if tuple(tmask.shape) != tuple(mask.shape):
-            raise ValueError(f"tmask shape {tuple(tmask.shape)} differs from the mask's {tuple(mask.shape)}")
-        if _layout(tmask) != _layout(mask):
-            # the library reads both with one set of strides
-            mask, tmask = mask.contiguous(), tmask.contiguous()
-            p.mask_stride_b, p.mask_stride_h, p.mask_stride_q = _layout(mask)[:3]
+        mask, tmask = _tmask_like(tmask, None, p, mask)
     if out is None:
         o = torch.empty_like(q)
         to = torch.empty_like(q)
@@ -231,13 +225,30 @@ def jvpattn_check_bwd(params: jvpattn_params, *ptrs, workspace_bytes: int = 0) -
     return load_library().jvpattn_check_bwd(ctypes.byref(params), *ptrs, workspace_bytes)
 
 
+def _tmask_like(tmask, mask_in, p, mask):
+    """tmask laid out as the library-side mask (returns (mask, tmask); may make both contiguous)."""
+    if p.mask_kind != JVPATTN_MASK_ADDITIVE:
+        raise ValueError("tmask needs an additive mask")
+    if not tmask.is_cuda or tmask.dtype != mask.dtype:
+        raise ValueError("tmask must be a GPU tensor of the mask's dtype")
+    tmask = _as_4d(tmask)
+    if tuple(tmask.shape) != tuple(mask.shape):
+        raise ValueError(f"tmask shape {tuple(tmask.shape)} differs from the mask's {tuple(mask.shape)}")
+    if _layout(tmask) != _layout(mask):
+        # the library reads both with one set of strides
+        mask, tmask = mask.contiguous(), tmask.contiguous()
+        p.mask_stride_b, p.mask_stride_h, p.mask_stride_q = _layout(mask)[:3]
+    return mask, tmask
+
+
 def jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, go, gto, mask=None, causal=False, scale=None,
-                out=None, workspace=None):
+                out=None, workspace=None, tmask=None):
     """dq, dk, dv, dtq, dtk, dtv = jvpattn_bwd(...): cotangents of q, k, v, tq, tk, tv.
 
     For L = <go, O> + <gto, dO> with (O, dO, lse, tlse) = jvpattn_fwd(q, k, v, tq, tk, tv, mask, causal,
     scale). Shapes and dtypes as for jvpattn_fwd; go, gto like q, either may be None (zero). ``out``
-    optionally supplies the six output tensors (dtq, dtk, dtv may be None: not computed);
+    optionally supplies the six output tensors (dtq, dtk, dtv may be None: not computed); ``tmask``, the
+    additive mask's tangent the forward was taken along (jvpattn_bwd_tmask);
     ``workspace`` a uint8 device tensor of at least jvpattn_bwd_workspace_bytes bytes. Work is queued
     on torch's current stream.
     """
@@ -253,6 +264,8 @@ def jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, go, gto, mask=None, causa
         if t.dtype != q.dtype:
             raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
     p, mask = make_params(q, k, mask, causal, scale)
+    if tmask is not None:
+        mask, tmask = _tmask_like(tmask, None, p, mask)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         dtq, dtk, dtv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -264,10 +277,17 @@ def jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, go, gto, mask=None, causa
     if workspace is None:
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = lib.jvpattn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv), _ptr(mask),
-                         _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse), _ptr(go), _ptr(gto),
-                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtq), _ptr(dtk), _ptr(dtv),
-                         _ptr(workspace), workspace.numel() * workspace.element_size(), stream)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if tmask is not None:
+        rc = lib.jvpattn_bwd_tmask(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                                   _ptr(mask), _ptr(tmask), _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse), _ptr(go),
+                                   _ptr(gto), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtq), _ptr(dtk), _ptr(dtv),
+                                   _ptr(workspace), ws_bytes, stream)
+    else:
+        rc = lib.jvpattn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                             _ptr(mask), _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse), _ptr(go), _ptr(gto),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtq), _ptr(dtk), _ptr(dtv),
+                             _ptr(workspace), ws_bytes, stream)
     if rc != 0:
         msg = jvpattn_strerror(rc)
         if rc == -9:

@@ -141,7 +141,7 @@ int jvpattn_fwd(const jvpattn_params* params,
  * Errors as jvpattn_fwd, and JVPATTN_ERR_MASK if tmask is given without an
  * additive mask, JVPATTN_ERR_ALIGN if it is not aligned to the element size,
  * JVPATTN_ERR_ALIAS if it overlaps an output. jvpattn_bwd differentiates the
- * forward without a mask tangent. */
+ * forward without a mask tangent, jvpattn_bwd_tmask the forward with one. */
 int jvpattn_fwd_tmask(const jvpattn_params* params,
                       const void* q, const void* k, const void* v,
                       const void* tq, const void* tk, const void* tv,
@@ -216,6 +216,37 @@ int jvpattn_bwd(const jvpattn_params* params,
                 void* dtq, void* dtk, void* dtv,
                 void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/* The reverse pass of the forward taken along a tangent of the additive
+ * mask as well (jvpattn_fwd_tmask): the same call as jvpattn_bwd plus
+ *   tmask : that tangent dM, laid out exactly as `mask`; NULL = zero.
+ * The score tangent it differentiates is dS = scale (dQ K^T + Q dK^T) + dM;
+ * the mask and dM are constants of the map (no cotangent is returned for
+ * them). Errors as jvpattn_bwd, plus jvpattn_fwd_tmask's for tmask, and
+ * JVPATTN_ERR_ALIAS / JVPATTN_ERR_WORKSPACE if it overlaps a gradient or
+ * the workspace. For callers that differentiate through a mask tangent. */
+int jvpattn_bwd_tmask(const jvpattn_params* params,
+                      const void* q, const void* k, const void* v,
+                      const void* tq, const void* tk, const void* tv,
+                      const void* mask, const void* tmask,
+                      const void* o, const void* to, const float* lse, const float* tlse,
+                      const void* go, const void* gto,
+                      void* dq, void* dk, void* dv,
+                      void* dtq, void* dtk, void* dtv,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Host-only validation of a jvpattn_bwd_tmask call (pointers compared, never
+ * dereferenced); returns JVPATTN_OK or the code jvpattn_bwd_tmask would return. */
+int jvpattn_check_bwd_tmask(const jvpattn_params* params,
+                            const void* q, const void* k, const void* v,
+                            const void* tq, const void* tk, const void* tv,
+                            const void* mask, const void* tmask,
+                            const void* o, const void* to, const float* lse, const float* tlse,
+                            const void* go, const void* gto,
+                            const void* dq, const void* dk, const void* dv,
+                            const void* dtq, const void* dtk, const void* dtv,
+                            const void* workspace, size_t workspace_bytes);
 
 /* A static, human-readable description of a return code. */
 const char* jvpattn_strerror(int code);

@@ -23,9 +23,10 @@ def declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["jvpattn_bwd", "jvpattn_bwd_workspace_bytes", "jvpattn_check_bwd",
-                                    "jvpattn_check_fwd", "jvpattn_check_fwd_tmask", "jvpattn_fwd",
-                                    "jvpattn_fwd_tmask", "jvpattn_last_hip_error", "jvpattn_strerror"]
+    assert declared_functions() == ["jvpattn_bwd", "jvpattn_bwd_tmask", "jvpattn_bwd_workspace_bytes",
+                                    "jvpattn_check_bwd", "jvpattn_check_bwd_tmask", "jvpattn_check_fwd",
+                                    "jvpattn_check_fwd_tmask", "jvpattn_fwd", "jvpattn_fwd_tmask",
+                                    "jvpattn_last_hip_error", "jvpattn_strerror"]
 
 
 @needs_lib
@@ -381,3 +382,24 @@ int main() {
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "bad=0" in r.stdout
+
+
+@needs_lib
+def test_check_bwd_mask_tangent():
+    p = good_params(mask_kind=J.JVPATTN_MASK_ADDITIVE, mask_stride_b=100 * 90, mask_stride_q=90)
+    Q = bwd_ptrs(p)
+    t = Q["ws"] + (1 << 30)   # a disjoint tangent laid out as the mask
+    lib = J.load_library()
+
+    def chk(**o):
+        a = dict(Q, tmask=t)
+        a.update(o)
+        names = ("q", "k", "v", "tq", "tk", "tv", "mask", "tmask", "o", "to", "lse", "tlse", "go", "gto",
+                 "dq", "dk", "dv", "dtq", "dtk", "dtv", "ws")
+        return lib.jvpattn_check_bwd_tmask(p, *[a[n] for n in names], max(J.jvpattn_bwd_workspace_bytes(p), 0))
+    assert chk() == 0
+    assert chk(tmask=None) == 0
+    assert chk(tmask=t + 2 + 1) == -6          # misaligned
+    assert chk(dk=t) == -8                     # a gradient over it
+    assert chk(ws=t) == -10                    # the workspace over it
+    assert chk(o=t) == -8                      # a forward output over it

@@ -30,12 +30,12 @@ def fake_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, scale=
 
 
 def fake_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, go, gto, mask=None, causal=False, scale=None, out=None,
-             workspace=None):
+             workspace=None, tmask=None):
     kind = "none" if mask is None else ("bool" if mask.dtype == torch.bool else "additive")
     m = None if mask is None else (mask.numpy().astype(np.uint8) if kind == "bool" else _np(mask))
     z = lambda t: np.zeros(q.shape) if t is None else _np(t)
     g = oracle_bwd(_np(q), _np(k), _np(v), _np(tq), _np(tk), _np(tv), z(go), z(gto), mask=m, mask_kind=kind,
-                   causal=causal, scale=scale)
+                   causal=causal, scale=scale, tmask=_np(tmask))
     res = [torch.from_numpy(a).to(q.dtype) for a in g]
     if out is not None:
         res = [None if slot is None else r for r, slot in zip(res, out)]
@@ -118,12 +118,17 @@ def test_forward_mode_with_a_dual_additive_mask():
                                mask_kind="additive", tmask=_np(tm))
     np.testing.assert_allclose(_np(o), ro, rtol=0, atol=1e-12)
     np.testing.assert_allclose(_np(to), rto, rtol=0, atol=1e-12)
-    # fwd_dual takes the same tangent directly; reverse mode through it is refused
+    # fwd_dual takes the same tangent directly, and reverse mode through it carries the tangent along
     q.requires_grad_(True)
+    tq.requires_grad_(True)
     o2, to2 = A.fwd_dual(q, k, v, tq, tk, tv, attn_mask=m, tmask=tm)
     np.testing.assert_allclose(_np(to2), rto, rtol=0, atol=1e-12)
-    with pytest.raises(NotImplementedError):
-        to2.sum().backward()
+    gto = torch.ones_like(to2)
+    to2.backward(gto)
+    ref = oracle_bwd(_np(q), _np(k), _np(v), _np(tq), _np(tk), _np(tv), np.zeros(q.shape), _np(gto), mask=_np(m),
+                     mask_kind="additive", tmask=_np(tm))
+    np.testing.assert_allclose(_np(q.grad), ref[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(_np(tq.grad), ref[3], rtol=0, atol=1e-12)
 
 
 def test_grouped_kv_heads_route_through():

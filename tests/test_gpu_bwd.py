@@ -57,7 +57,7 @@ def run(w, x=None, tangents=("tq", "tk", "tv"), scale=None, heads=None):
     return got, dict(zip(NAMES, ref))
 
 
-def term_magnitudes(x, w, tangents, scale, heads=None):
+def term_magnitudes(x, w, tangents, scale, heads=None, tmask=None):
     """Per output, max over elements of the sum of absolute terms (see the module docstring)."""
     A = lambda n: None if x[n] is None else np.abs(f64(x[n]))
     q, k, v, g, gd = f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["do"]), f64(x["dto"])
@@ -84,6 +84,8 @@ def term_magnitudes(x, w, tangents, scale, heads=None):
                 e = np.exp(S[live] - S[live].max(1, keepdims=True))
                 P[live] = e / e.sum(1, keepdims=True)
             Sd = sc * (tq[b, h] @ k_.T + q[b, h] @ tk_.T)
+            if tmask is not None:   # the additive mask's tangent joins the score tangent
+                Sd = Sd + _head_bias(tmask, "additive", b, h, Nq, Nk, False, np.arange(Nq))
             t = (P * Sd).sum(1, keepdims=True)
             aG, aGd = np.abs(g[b, h]), np.abs(gd[b, h])
             aX = aG @ np.abs(v_).T + aGd @ np.abs(tv_).T
@@ -288,3 +290,28 @@ def test_bit_packed_masks(causal):
     for n, gg, r in zip(NAMES, g, ref):
         err = float(np.max(np.abs(gg.float().cpu().numpy() - r)))
         assert err <= RHO[w.dtype] * M[n], (n, err, M[n])
+
+
+@pytest.mark.parametrize("causal,dtype", [(False, "bf16"), (True, "f16")])
+def test_mask_tangent(causal, dtype):
+    """jvpattn_bwd_tmask: the reverse pass of the forward along (dQ, dK, dV, dM), against the oracle."""
+    w = I.Workload("tmask_bwd", B=2, H=2, N=170, d=64, dtype=dtype, causal=causal, mask_kind="additive",
+                   std=1.0, seed=25)
+    x = I.make_inputs(w, cotangents=True)
+    g = torch.Generator().manual_seed(26)
+    tm = torch.randn(x["mask"].shape, generator=g).to(x["mask"].dtype)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
+    o, to, lse, tlse = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=d["mask"], causal=causal,
+                                   tmask=tm.to(DEV))
+    got = jvpattn_bwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], o, to, lse, tlse, d["do"], d["dto"],
+                      mask=d["mask"], causal=causal, tmask=tm.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["tq"]), f64(x["tk"]), f64(x["tv"]),
+                     f64(x["do"]), f64(x["dto"]), mask=f64(x["mask"]), mask_kind="additive", causal=causal,
+                     tmask=f64(tm))
+    M = term_magnitudes(x, w, ("tq", "tk", "tv"), None, tmask=f64(tm))
+    for n, gg, r in zip(NAMES, got, ref):
+        gg = gg.float().cpu().numpy()
+        assert np.all(np.isfinite(gg)), n
+        err = float(np.max(np.abs(gg - r)))
+        assert err <= RHO[dtype] * M[n], (n, err, M[n])
