@@ -644,6 +644,24 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
 
     auto tile = [&](int t_idx, const char* sb) {
       const int i0 = t_idx * 32;   // first query of the tile
+      // Mask elements (query i0 + 8(r/4) + 4 hlf + r%4, key kj) are fetched before the score
+      // products so their latency hides behind them.
+      uint32_t mw[MASK == JVPATTN_MASK_NONE ? 1 : 16], tw[MASK == kMaskAddT ? 16 : 1];
+      if constexpr (MASK != JVPATTN_MASK_NONE) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
+          if constexpr (MASK == JVPATTN_MASK_BITS) {
+            mw[r] = __builtin_amdgcn_raw_buffer_load_b32(mr, (qrow * int(a.msq) + (kj >> 5)) * 4, 0, 0);
+          } else if constexpr (MASK == JVPATTN_MASK_BOOL) {
+            mw[r] = __builtin_amdgcn_raw_buffer_load_b8(mr, qrow * int(a.msq) + kj, 0, 0);
+          } else {
+            const int off = (qrow * int(a.msq) + kj) * 2;
+            mw[r] = __builtin_amdgcn_raw_buffer_load_b16(mr, off, 0, 0);
+            if constexpr (MASK == kMaskAddT) tw[r] = __builtin_amdgcn_raw_buffer_load_b16(mtr, off, 0, 0);
+          }
+        }
+      }
       vec8 qa[L::NC], tqa[L::NC];
       read_rows(sb, 0, qa);
       read_rows(sb, 1, tqa);
@@ -665,28 +683,20 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
       }
       // masks: element (query i, key kj); hidden entries get score -inf
       if constexpr (MASK == JVPATTN_MASK_BITS) {
-        // bit kj % 32 of the row's word kj / 32
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
-          const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(mr, (qrow * int(a.msq) + (kj >> 5)) * 4, 0, 0);
-          if (((w >> (kj & 31)) & 1u) == 0u) s[r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)   // bit kj % 32 of the row's word kj / 32
+          if (((mw[r] >> (kj & 31)) & 1u) == 0u) s[r] = -INFINITY;
+      } else if constexpr (MASK == JVPATTN_MASK_BOOL) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (mw[r] == 0u) s[r] = -INFINITY;
       } else if constexpr (MASK != JVPATTN_MASK_NONE) {
-        constexpr int es = MASK == JVPATTN_MASK_BOOL ? 1 : 2;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
-          const int off = (qrow * int(a.msq) + kj) * es;
-          if constexpr (MASK == JVPATTN_MASK_BOOL) {
-            if (__builtin_amdgcn_raw_buffer_load_b8(mr, off, 0, 0) == 0) s[r] = -INFINITY;
-          } else {
-            const float m = T::widen(__builtin_amdgcn_raw_buffer_load_b16(mr, off, 0, 0));
-            s[r] = POW2 ? s[r] + m : fmaf(s[r], a.scale, m);
-            if constexpr (MASK == kMaskAddT)   // the mask's tangent joins the score tangent (sd * us = dS)
-              sd[r] = fmaf(T::widen(__builtin_amdgcn_raw_buffer_load_b16(mtr, off, 0, 0)), POW2 ? 1.0f : a.inv_scale,
-                           sd[r]);
-          }
+          const float m = T::widen(uint16_t(mw[r]));
+          s[r] = POW2 ? s[r] + m : fmaf(s[r], a.scale, m);
+          if constexpr (MASK == kMaskAddT)   // the mask's tangent joins the score tangent (sd * us = dS)
+            sd[r] = fmaf(T::widen(uint16_t(tw[r])), POW2 ? 1.0f : a.inv_scale, sd[r]);
         }
       }
       if (needs_rowmask(t_idx)) {
