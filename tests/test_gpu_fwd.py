@@ -563,3 +563,27 @@ def test_bit_packed_masks(w, kernel):
     r = oracle_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["tq"]), f64(x["tk"]), f64(x["tv"]),
                    mask=bits.cpu().numpy(), mask_kind="bits", causal=w.causal)
     assert_parity(got, dict(zip(("o", "to", "lse", "tlse"), r)), w.dtype, w.name, spec_spread=w.std is None)
+
+
+# ------------------------------------------------ features combined
+
+def test_grouped_heads_with_packed_key_padding(kernel):
+    """Shared K/V heads, a bit-packed key-padding mask (with an empty batch) and causality at once."""
+    from forward_mode_autodiff_amd.jvpattn import pack_mask_bits
+    w = I.Workload("combo_gqa_bits", B=4, H=8, Hkv=2, N=260, d=64, dtype="bf16", causal=True, mask_kind="bool",
+                   mask_layout="pad_left", std=1.0, seed=60, extra={"lengths": [260, 0, 97, 33]})
+    x = I.make_inputs(w)
+    d = to_dev(x)
+    o, to, lse, tlse = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=pack_mask_bits(d["mask"]),
+                                   causal=True)
+    torch.cuda.synchronize()
+    got = {"o": o.float().cpu(), "to": to.float().cpu(), "lse": lse.cpu(), "tlse": tlse.cpu()}
+    ref = oracle_run(x, "bool", True)
+    assert_parity(got, ref, w.dtype, w.name, spec_spread=False)
+
+
+def test_grouped_heads_with_mask_tangent_per_head(kernel):
+    """Shared K/V heads with a per-head additive mask and its tangent."""
+    w = I.Workload("combo_gqa_tmask", B=2, H=4, Hkv=1, N=190, d=64, dtype="f16", mask_kind="additive", mask_heads=4,
+                   std=1.0, seed=61)
+    check_tmask(w, seed=161)
