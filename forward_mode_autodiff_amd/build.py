@@ -22,7 +22,14 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libjvpattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["jvpattn_fwd.hip", "jvpattn_bwd.hip", "jvpattn_check.cpp"]
+# (source, object name, extra defines): the forward's kernel instances build
+# once per (mask kind, causal) pair so the objects compile in parallel.
+MASK_KINDS = {"none": 0, "bool": 1, "add": 2, "bits": 3, "addt": 4}
+SOURCES = [("jvpattn_fwd.hip", "jvpattn_fwd", []), ("jvpattn_bwd.hip", "jvpattn_bwd", []),
+           ("jvpattn_check.cpp", "jvpattn_check", [])] + [
+    ("jvpattn_fwd_inst.hip", f"jvpattn_fwd_{name}_{'causal' if c else 'full'}",
+     [f"-DJVPATTN_INST_MASK={kind}", f"-DJVPATTN_INST_CAUSAL={c}"])
+    for name, kind in MASK_KINDS.items() for c in (1, 0)]
 
 
 def hipcc() -> str:
@@ -38,9 +45,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job, verbose: bool) -> str:
+    src, name, defines = job
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [hipcc(), *COMMON, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"] + DEVICE
     else:
@@ -57,7 +65,8 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    workers = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]

@@ -321,6 +321,7 @@ extern "C" const char* jvpattn_strerror(int code) {
     case JVPATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case JVPATTN_ERR_HIP: return "HIP runtime error on launch";
     case JVPATTN_ERR_WORKSPACE: return "workspace missing, too small, not 256-byte aligned, or overlapping";
+    case JVPATTN_ERR_ARG: return "argument outside its documented range";
     default: return "unknown error code";
   }
 }

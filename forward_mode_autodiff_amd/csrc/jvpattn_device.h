@@ -9,6 +9,7 @@
 #include <cstdint>
 
 #include "jvpattn.h"
+#include "jvpattn_fwd_launch.h"
 
 namespace jvpattn {
 namespace {
@@ -41,7 +42,6 @@ __device__ inline float max3(float a, float b, float c) {
 
 struct BF16 {
   using vec8 = bf16x8;
-  static constexpr float kTau = 8.0f;   // weights may grow to 2^8 before a rescale
   __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -62,8 +62,6 @@ struct BF16 {
 
 struct F16 {
   using vec8 = f16x8;
-  // float16 weights times score tangents must stay below 65504: keep weights <= 2^4.
-  static constexpr float kTau = 4.0f;
   __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
@@ -194,9 +192,6 @@ __device__ inline void ring_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Internal mask kind: an additive mask together with its tangent dM, which
-// the score tangent gains (dS = scale (dQ K^T + Q dK^T) + dM).
-constexpr int kMaskAddT = 4;   // beyond the public jvpattn_mask_kind values
 
 // Mask values of one 32-key block for this lane's 16 keys, loaded ahead of use.
 template <int MASK> struct MaskVals {};

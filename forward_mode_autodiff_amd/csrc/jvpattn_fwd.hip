@@ -1,1313 +1,26 @@
-// Fused attention forward with tangents for gfx950 (MI355X).
-//
-// One pass over the keys computes, per query row i,
-//   O_i  = sum_j P_ij V_j,               P = softmax_j(scale q_i.k_j + M_ij)
-//   dO_i = sum_j P_ij (dS_ij - tlse_i) V_j + sum_j P_ij dV_j
-//   tlse_i = sum_j P_ij dS_ij,           dS_ij = scale (dq_i.k_j + q_i.dk_j)
-// which is the Jacobian-vector product of scaled-dot-product attention (the
-// "JVP Flash Attention" README, sections "Description" and "Usage").
-//
-// Streaming form (the N x N score matrix never exists in memory): keep per
-// row a reference maximum m, l = sum e, mu = sum e dS, and two accumulators
-// accO = sum e V and accT = sum e dS V + sum e dV, with e = exp(s - m).
-// Then O = accO / l, tlse = mu / l, dO = accT / l - tlse O: dividing the
-// streamed sums by l turns e into P, so this is the closed form above; a
-// change of m multiplies every sum by the same factor and cancels.
-//
-// Mapping onto the matrix cores. Each wave owns 32 query rows and computes
-// the transposed score block S^T = K Q^T (32 keys x 32 queries) with
-// v_mfma_f32_32x32x16_{bf16,f16}. In the C layout of that instruction lane
-// l holds column l%32 -- one query -- and 16 keys in its registers, so the
-// row statistics need only in-lane reductions plus one exchange between
-// lanes l and l^32, and the 16 registers, rounded to 16 bits, are already
-// the B operand of the next product O^T += V^T P^T with no lane shuffles.
-// V and dV are stored transposed in LDS (with the key order permuted to
-// match the C layout) so that V^T A-operands are single 16-byte LDS reads.
-// The score tangent uses one chain over 2d: dS^T = dK Q^T + K dQ^T.
-// The two tangent products share one accumulator: accT += V^T (P dS)^T + dV^T P^T.
+// Forward entry points: validation (jvpattn_check.cpp), then the launch plan
+// -- kernel family, grid order, key range -- and the typed launch, whose
+// kernel instances live in jvpattn_fwd_inst.hip. What each kernel computes is
+// described in jvpattn_fwd_kernels.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 
 #include "jvpattn.h"
+#include "jvpattn_fwd_launch.h"
 #include "jvpattn_internal.h"
-#include "jvpattn_device.h"
 
 namespace jvpattn {
 namespace {
 
-constexpr int kWaves = 4;             // waves per workgroup
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;      // query rows per workgroup
-
-static_assert(kThreads == kTileThreads, "LDS tiles are laid out for the 4-wave kernels");
-
-struct FwdArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* tq;
-  const void* tk;
-  const void* tv;
-  const void* mask;
-  const void* tmask;  // tangent of the additive mask (mask kind kMaskAddT), laid out as the mask
-  void* o;
-  void* to;
-  float* lse;
-  float* tlse;
-  int H, Nq, Nk, BH;
-  int grp;            // query heads per key/value head (grouped-query attention; 1 = one each)
-  int xgrp;           // grp when whole key/value groups can be kept on one XCD, else 1
-  int head_major;     // 1: the query blocks of a head run back to back on one XCD (large grids)
-  int key_range;      // 1: the mask is shared by all query rows; skip 32-key tiles it hides entirely
-  int n_qblk;
-  int mask_vec;       // 1: mask rows may be read 4 keys at a time
-  int64_t msb, msh, msq;
-  float scale;
-  float inv_scale;    // 1 / scale
-  float cx;           // score units -> log2 units
-  float thr;          // lazy-rescale threshold in score units
-};
-
-// Workgroup -> (query block, query head). Workgroups are dealt round-robin
-// over the 8 XCDs, each with its own L2, so the mapping decides which blocks
-// share cached key/value tiles.
-//  - Default (the grid fits on the chip in a few rounds): query blocks run
-//    heaviest first (causal work grows with the block index) and heads are
-//    innermost; with B*H a multiple of 8 every block of a head lands on one
-//    XCD, and all of them are resident together.
-//  - head_major (grids many times the chip, B*H a multiple of 8): XCD x
-//    runs heads x, x+8, ... one after the other, each head's query blocks
-//    back to back (heaviest first), so they stream the same key/value tiles
-//    at the same time and all but the first read them from L2 rather than
-//    HBM.
-// With grouped key/value heads (xgrp > 1, B*H a multiple of 8*xgrp) the heads
-// are then permuted so that all query heads sharing a key/value head also
-// land on one XCD.
-__device__ inline void block_coords(const FwdArgs& a, int& qb, int& bh) {
-  int r;
-  if (a.head_major) {
-    const int x = int(blockIdx.x), slot = x >> 3;
-    qb = a.n_qblk - 1 - slot % a.n_qblk;
-    r = (slot / a.n_qblk) * 8 + (x & 7);
-  } else {
-    qb = a.n_qblk - 1 - int(blockIdx.x) / a.BH;
-    r = int(blockIdx.x) % a.BH;
-  }
-  if (a.xgrp > 1) {
-    const int xcd = r & 7, j = r >> 3;
-    bh = ((j / a.xgrp) * 8 + xcd) * a.xgrp + j % a.xgrp;
-  } else {
-    bh = r;
-  }
-}
-
-// Tiles of 32 keys [t_lo, t_hi) that hold every key a row of this head may
-// see. With a mask shared by all query rows (row stride 0: a key-padding mask
-// [B,1,1,Nk] or [B,H,1,Nk]) the workgroup scans that one row and the loops
-// start and end at the first and last tile with a visible key, so tiles the
-// mask hides entirely are never loaded or multiplied (a row with no visible
-// key at all gets no tile). Otherwise every tile: [0, ceil(Nk/32)). Every
-// thread of the workgroup takes part; the result is uniform. ES: bytes per
-// mask element (additive masks hide a key with -inf).
-template <typename T, int MASK, int ES>
-__device__ inline void key_tiles(const FwdArgs& a, Rsrc mr, int* red, int& t_lo, int& t_hi) {
-  t_lo = 0;
-  t_hi = (a.Nk + 31) >> 5;
-  if constexpr (MASK != JVPATTN_MASK_NONE) {
-    if (!a.key_range) return;
-    if (threadIdx.x == 0) {
-      red[0] = INT32_MAX;
-      red[1] = -1;
-    }
-    __syncthreads();
-    int lo = INT32_MAX, hi = -1;
-    if constexpr (MASK == JVPATTN_MASK_BITS) {
-      const int nw = (a.Nk + 31) >> 5;
-      for (int j = threadIdx.x; j < nw; j += blockDim.x) {
-        uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(mr, 4 * j, 0, 0);
-        if (j == nw - 1 && (a.Nk & 31)) w &= (1u << (a.Nk & 31)) - 1u;   // bits past Nk
-        if (w) {
-          lo = min(lo, 32 * j + int(__builtin_ctz(w)));
-          hi = max(hi, 32 * j + 31 - int(__builtin_clz(w)));
-        }
-      }
-    }
-    for (int j = threadIdx.x; MASK != JVPATTN_MASK_BITS && j < a.Nk; j += blockDim.x) {
-      bool vis;
-      if constexpr (MASK == JVPATTN_MASK_BOOL || MASK == JVPATTN_MASK_BITS) {
-        vis = __builtin_amdgcn_raw_buffer_load_b8(mr, j, 0, 0) != 0;
-      } else if constexpr (ES == 2) {
-        vis = T::widen(__builtin_amdgcn_raw_buffer_load_b16(mr, 2 * j, 0, 0)) != -INFINITY;
-      } else {
-        vis = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mr, 4 * j, 0, 0)) != -INFINITY;
-      }
-      if (vis) {
-        lo = min(lo, j);
-        hi = max(hi, j);
-      }
-    }
-    if (hi >= 0) {
-      atomicMin(&red[0], lo);
-      atomicMax(&red[1], hi);
-    }
-    __syncthreads();
-    hi = red[1];
-    t_lo = hi < 0 ? 0 : red[0] >> 5;
-    t_hi = hi < 0 ? 0 : (hi >> 5) + 1;
-  }
-}
-
-// Bytes per mask element: uint8 for bool, 32-bit words for bit-packed masks,
-// else the additive values (value_bytes).
-template <int MASK>
-constexpr int mask_es(int value_bytes) {
-  return MASK == JVPATTN_MASK_BOOL ? 1 : MASK == JVPATTN_MASK_BITS ? 4 : value_bytes;
-}
-
-// Per-row softmax state for one lane (both lanes of a query column hold the same m).
-struct RowState {
-  float m;       // reference maximum in score units (-inf until a visible key is seen)
-  float moff;    // m * cx, or 0 while m is -inf
-  float l;       // partial sum of weights over this lane's keys
-  float mu;      // partial sum of weights * score tangent (in the units of sd)
-};
-
-
-template <typename T, int MASK, bool CAUSAL, bool PRESCALED>
-__device__ inline void mask_scores(f32x16& s, const FwdArgs& a, Rsrc mr, int qi, int k0, int hlf,
-                                   bool elem_mask) {
-  MaskVals<MASK> m;
-  mask_load<MASK>(m, a, mr, qi, k0, hlf);
-  mask_apply<T, MASK, PRESCALED>(s, m, a.scale);
-  if (elem_mask) hide_keys<CAUSAL>(s, a.Nk, qi, k0, hlf);
-}
-
-// Move the reference maximum when some row of the wave saw a score more than
-// thr above it. Returns alpha != 1 (and true) when accumulators must be scaled.
-__device__ inline bool update_max(float bm, RowState& st, float cx, float thr, float& alpha) {
-  alpha = 1.0f;
-  const bool need = bm > st.m + thr;
-  if (!__any(need)) return false;
-  const float mn = fmaxf(st.m, bm);
-  alpha = mn == -INFINITY ? 1.0f : exp2f((st.m - mn) * cx);
-  st.l *= alpha;
-  st.mu *= alpha;
-  st.m = mn;
-  st.moff = mn == -INFINITY ? 0.0f : mn * cx;
-  return true;
-}
-
-// Weights e = exp(s - m) (into s) and e * sd (into sd); their sums into l, mu.
-__device__ inline void exp_block(f32x16& s, f32x16& sd, RowState& st, float cx) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], cx, -st.moff));
-    sd[r] *= s[r];
-  }
-  float l0 = s[0] + s[1], l1 = s[2] + s[3], m0 = sd[0] + sd[1], m1 = sd[2] + sd[3];
-#pragma unroll
-  for (int r = 4; r < 16; r += 4) {
-    l0 += s[r] + s[r + 1];
-    l1 += s[r + 2] + s[r + 3];
-    m0 += sd[r] + sd[r + 1];
-    m1 += sd[r + 2] + sd[r + 3];
-  }
-  st.l += l0 + l1;
-  st.mu += m0 + m1;
-}
-
-// Online-softmax update for one 32-key block (float32 kernel).
-__device__ inline bool softmax_block(f32x16& s, f32x16& sd, RowState& st, float cx, float thr,
-                                     float& alpha) {
-  const bool rescale = update_max(block_max(s), st, cx, thr, alpha);
-  exp_block(s, sd, st, cx);
-  return rescale;
-}
-
-// ------------------------------------------------------------- 16-bit kernel
-//
-// Software pipeline per wave over 32-key blocks k: while the vector units turn
-// block k's scores into weights, the matrix cores already compute block k+1's
-// scores; block k's value products follow. The reference maximum for block
-// k+1 is settled at the end of iteration k, so the only branch in the steady
-// state (a rare rescale) sits between iterations. Blocks that need per-key
-// masking (the causal diagonal, a ragged tail) take a non-pipelined path.
-//
-// LDS holds a ring of 4 tiles, each fetched two iterations ahead; one
-// workgroup barrier per tile. The four stages are separate arrays and the
-// loop is unrolled by four, so every LDS access names its stage statically
-// and in-flight loads into other stages never force a wait.
-
-//
-// SPLIT = 2 (small grids, d = 64): two groups of four waves per workgroup
-// take the same 128 rows; group G streams the G-th half of the key blocks
-// through its own ring, then group 1 hands its row state and accumulators to
-// group 0 through LDS (x0..x3: group 1's stages, one 16 KB stage per wave;
-// xst: m, moff, l, mu per lane), which combines the two online-softmax states -- rescaling
-// each to the larger reference -- and stores. Twice the waves per row block.
-//
-// WV = waves per group (32 query rows each): 4, or 2 for grids too small to
-// give every CU a 128-row block -- then 64-row blocks, twice the workgroups.
-template <typename T, int D, int MASK, bool CAUSAL, bool POW2, int SPLIT, int G, int WV>
-__device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi, char* stage0, char* stage1,
-                                           char* stage2, char* stage3, char* x0, char* x1, char* x2, char* x3,
-                                           float4* xst) {
-  using L = Tile16<D>;
-  using vec8 = typename T::vec8;
-  constexpr int GT = 64 * WV;                           // threads per group
-  constexpr int BMG = 32 * WV;                          // query rows per workgroup
-  constexpr int LOADS = L::TENSOR_BYTES / (16 * GT);    // 16-byte tile loads per thread per tensor
-  constexpr int TILE_VMEM = 4 * LOADS;                  // direct loads per thread per tile
-  static_assert(LOADS * 16 * GT == L::TENSOR_BYTES, "tile must split evenly over the group");
-
-  const int tid = threadIdx.x & (GT - 1);   // thread within the group
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave within the group
-  const int c32 = lane & 31;
-  const int hlf = lane >> 5;
-
-  int qb, bh;
-  block_coords(a, qb, bh);
-  const int b = bh / a.H, h = bh % a.H;
-  const int q0 = qb * BMG;
-  const int qw0 = q0 + 32 * wave;
-  const int qi = qw0 + c32;
-  const bool wave_live = qw0 < a.Nq;
-
-  const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;   // byte offsets of this head
-  const int64_t khead = int64_t(bh / a.grp) * a.Nk * L::ROW;   // the key/value head it reads
-  const char* qp = static_cast<const char*>(a.q) + qhead;
-  const char* kp = static_cast<const char*>(a.k) + khead;
-  const char* vp = static_cast<const char*>(a.v) + khead;
-  const char* tqp = a.tq ? static_cast<const char*>(a.tq) + qhead : qp;
-  const char* tkp = a.tk ? static_cast<const char*>(a.tk) + khead : kp;
-  const char* tvp = a.tv ? static_cast<const char*>(a.tv) + khead : vp;
-  const int64_t qbytes = int64_t(a.Nq) * L::ROW;
-
-  // Q and dQ as B operands: lane holds row qi, head-dim entries hlf*D/2 + 8c .. +7.
-  // With POW2 the scale (a power of two) is folded into them: exact in bfloat16.
-  vec8 qB[L::NC], tqB[L::NC];
-  {
-    const Rsrc rq = make_rsrc(qp, qbytes), rtq = make_rsrc(tqp, a.tq ? qbytes : 0);
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      const int off = qi * L::ROW + (hlf * (D / 2) + 8 * c) * 2;
-      qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
-      tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
-      if constexpr (POW2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qB[c][e] = static_cast<__bf16>(static_cast<float>(qB[c][e]) * a.scale);
-          tqB[c][e] = static_cast<__bf16>(static_cast<float>(tqB[c][e]) * a.scale);
-        }
-      }
-    }
-  }
-
-  f32x16 accO[L::NT], accT[L::NT];
-#pragma unroll
-  for (int t = 0; t < L::NT; ++t) {
-    accO[t] = f32x16{};
-    accT[t] = f32x16{};
-  }
-  RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
-  const Rsrc mr = mask_rsrc(a, b, h, mask_es<MASK>(2), nullptr, MASK == JVPATTN_MASK_BITS);
-  const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 2, a.tmask) : mr;
-  auto load_mask = [&](MaskVals<MASK>& m, int k0) {
-    if constexpr (MASK == kMaskAddT) mask_load_t(m, a, mr, mtr, qi, k0, hlf);
-    else mask_load<MASK>(m, a, mr, qi, k0, hlf);
-  };
-  const float inv_us = POW2 ? 1.0f : a.inv_scale;   // mask tangent -> units of sd
-
-  const int kv_end = min(CAUSAL ? min(a.Nk, q0 + BMG) : a.Nk, 32 * t_hi);
-  const int n_all = max(0, (kv_end + L::BN - 1) / L::BN - t_lo);
-  // This group's key blocks kb .. kb+n_tiles-1 (absolute); both groups run
-  // n_loop iterations (one barrier each), the shorter one idling through the
-  // extra ones.
-  const int n_first = SPLIT == 2 ? (n_all + 1) / 2 : n_all;
-  const int kb = t_lo + (G == 1 ? n_first : 0);
-  const int n_tiles = G == 1 ? n_all - n_first : n_first;
-  const int n_loop = n_first;
-  // Last block this wave needs (the causal diagonal block, or the last tile), absolute, then
-  // local to this group; -1 if none.
-  const int last_all = !wave_live ? -1 : (CAUSAL ? min(t_lo + n_all - 1, qw0 >> 5) : t_lo + n_all - 1);
-  const int last = last_all < kb ? -1 : min(last_all - kb, n_tiles - 1);
-  auto needs_keymask = [&](int k) {
-    return (CAUSAL && (kb + k) * 32 + 31 > qw0) || ((kb + k) * 32 + 32 > a.Nk);
-  };
-
-  // Direct-load slots of this thread (byte offset inside a tile, same for all four tensors).
-  int dl_off[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int p = i * GT + tid;
-    const int row = p / L::GR, pg = p % L::GR;
-    dl_off[i] = row * L::ROW + ((pg ^ swz(row)) << 4);
-  }
-  // One buffer resource per tensor for the whole head: offsets past Nk rows
-  // (ragged tail) or into an absent tangent (0-byte resource) read as zeros.
-  const int64_t kbytes = int64_t(a.Nk) * L::ROW;
-  const Rsrc rk = make_rsrc(kp, kbytes), rv = make_rsrc(vp, kbytes);
-  const Rsrc rtk = make_rsrc(tkp, a.tk ? kbytes : 0), rtv = make_rsrc(tvp, a.tv ? kbytes : 0);
-  auto issue_tile = [&](int j, char* stage) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int off = (kb + j) * L::TENSOR_BYTES + dl_off[i];
-      const int slot = (i * GT + wave * 64) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
-                                               16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rtk, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rtv, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-    }
-  };
-
-  // LDS read offsets of this lane (constant over the loop).
-  // K / dK A operand, chunk c: row c32, logical granule hlf*NC + c.
-  int kofs[L::NC];
-#pragma unroll
-  for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ swz(c32)) << 4);
-  // V^T / dV^T A operand via transpose reads: lane (group g16 = lane/16, i = lane%16) addresses
-  // row 4*hlf + i/4 (+16 kc; vofs1 is the second read, 8 rows further), columns 32t + 16(g16&1) + 4(i&3).
-  // swz() depends on row bits 0..3 only, so +16 kc keeps the swizzle.
-  int vofs0[L::NT], vofs1[L::NT];
-  {
-    const int g16 = lane >> 4, i16 = lane & 15;
-    const int r0 = 4 * hlf + (i16 >> 2), r1 = r0 + 8;
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t) {
-      const int gcol = 4 * t + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-      vofs0[t] = r0 * L::ROW + ((gcol ^ swz(r0)) << 4) + 8 * (i16 & 1);
-      vofs1[t] = r1 * L::ROW + ((gcol ^ swz(r1)) << 4) + 8 * (i16 & 1);
-    }
-  }
-
-  // K / dK operands of the tile at `sb`, and the score products S^T, dS^T.
-  auto read_k = [&](const char* sb, vec8 (&ka)[L::NC], vec8 (&tka)[L::NC]) {
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      ka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb, kofs[c]));
-      tka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + L::TENSOR_BYTES, kofs[c]));
-    }
-  };
-  auto mma_s = [&](const vec8 (&ka)[L::NC], const vec8 (&tka)[L::NC], f32x16& s, f32x16& sd) {
-    s = f32x16{};
-    sd = f32x16{};
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      s = T::mfma(ka[c], qB[c], s);
-      sd = T::mfma(tka[c], qB[c], sd);
-      sd = T::mfma(ka[c], tqB[c], sd);
-    }
-  };
-  auto scores = [&](const char* sb, f32x16& s, f32x16& sd) {
-    vec8 ka[L::NC], tka[L::NC];
-    read_k(sb, ka, tka);
-    mma_s(ka, tka, s, sd);
-  };
-  auto rescale = [&](float bm) {
-    float alpha;
-    if (update_max(bm, st, a.cx, a.thr, alpha)) {
-#pragma unroll
-      for (int t = 0; t < L::NT; ++t) {
-        accO[t] *= alpha;
-        accT[t] *= alpha;
-      }
-    }
-  };
-  // Block weights: s -> e = exp(s - m), sd -> e * dS, packed as 16-bit B operands
-  // for keys 16kc .. 16kc+15; l and mu updated.
-  auto weights = [&](f32x16& s, f32x16& sd, vec8 (&pB)[2], vec8 (&uB)[2]) {
-    exp_block(s, sd, st, a.cx);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      uint4 pw, uw;
-      const float us = POW2 ? 1.0f : a.scale;
-      pw.x = T::pack2(s[8 * kc + 0], s[8 * kc + 1]);
-      pw.y = T::pack2(s[8 * kc + 2], s[8 * kc + 3]);
-      pw.z = T::pack2(s[8 * kc + 4], s[8 * kc + 5]);
-      pw.w = T::pack2(s[8 * kc + 6], s[8 * kc + 7]);
-      if constexpr (POW2) {
-        uw.x = T::pack2(sd[8 * kc + 0], sd[8 * kc + 1]);
-        uw.y = T::pack2(sd[8 * kc + 2], sd[8 * kc + 3]);
-        uw.z = T::pack2(sd[8 * kc + 4], sd[8 * kc + 5]);
-        uw.w = T::pack2(sd[8 * kc + 6], sd[8 * kc + 7]);
-      } else {
-        uw.x = T::pack2(sd[8 * kc + 0] * us, sd[8 * kc + 1] * us);
-        uw.y = T::pack2(sd[8 * kc + 2] * us, sd[8 * kc + 3] * us);
-        uw.z = T::pack2(sd[8 * kc + 4] * us, sd[8 * kc + 5] * us);
-        uw.w = T::pack2(sd[8 * kc + 6] * us, sd[8 * kc + 7] * us);
-      }
-      pB[kc] = __builtin_bit_cast(vec8, pw);
-      uB[kc] = __builtin_bit_cast(vec8, uw);
-    }
-  };
-  // V^T / dV^T operands of the tile at `sb` (transpose reads) and the value
-  // products accO += V^T P^T, accT += V^T U^T + dV^T P^T.
-  auto read_v = [&](const char* sb, vec8 (&va)[L::NT][2], vec8 (&tva)[L::NT][2]) {
-    const char* sv = sb + 2 * L::TENSOR_BYTES;
-    const char* stv = sb + 3 * L::TENSOR_BYTES;
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int o0 = 16 * kc * L::ROW + vofs0[t], o1 = 16 * kc * L::ROW + vofs1[t];
-        va[t][kc] = __builtin_bit_cast(
-            vec8, __builtin_shufflevector(lds_read_tr(sv + o0), lds_read_tr(sv + o1), 0, 1, 2, 3, 4, 5, 6, 7));
-        tva[t][kc] = __builtin_bit_cast(
-            vec8, __builtin_shufflevector(lds_read_tr(stv + o0), lds_read_tr(stv + o1), 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-  };
-  auto mma_v = [&](const vec8 (&va)[L::NT][2], const vec8 (&tva)[L::NT][2], const vec8 (&pB)[2],
-                   const vec8 (&uB)[2]) {
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        accO[t] = T::mfma(va[t][kc], pB[kc], accO[t]);
-        accT[t] = T::mfma(va[t][kc], uB[kc], accT[t]);
-        accT[t] = T::mfma(tva[t][kc], pB[kc], accT[t]);
-      }
-  };
-  auto values = [&](const char* sb, const vec8 (&pB)[2], const vec8 (&uB)[2]) {
-    vec8 va[L::NT][2], tva[L::NT][2];
-    read_v(sb, va, tva);
-    mma_v(va, tva, pB, uB);
-  };
-
-  // Blocks 1.. that need per-key masking start at jm: the causal diagonal, a
-  // ragged last tile, or the end of this wave's range.
-  int jm = last + 1;
-  if (CAUSAL) jm = min(jm, (qw0 >> 5) - kb);
-  jm = min(jm, (a.Nk >> 5) - kb);
-  jm = max(jm, 1);
-
-  // Pipelined iteration k (block k settled in sc; block k+1 needs no key mask).
-  auto fast = [&](int k, const char* cur, const char* nxt, char* dma, f32x16& sc, f32x16& sdc, f32x16& sn,
-                  f32x16& sdn) {
-    // Tile k+1 was fetched two iterations ago; tile k+2 may still be in flight.
-    if (k + 2 < n_tiles) wait_vmcnt<TILE_VMEM>();
-    else wait_vmcnt<0>();
-    ring_barrier();   // tile k+1 visible to all; every wave is done with tile k-1 (the `dma` stage)
-    MaskVals<MASK> mk1;
-    load_mask(mk1, (kb + k + 1) * 32);   // before the fetch: keeps its wait short
-    if (k + 3 < n_tiles) issue_tile(k + 3, dma);
-    // All LDS operands first (their latency hides behind the first weights),
-    // then the score products of block k+1 interleaved with block k's softmax
-    // on the vector units, then block k's value products.
-    vec8 ka[L::NC], tka[L::NC], va[L::NT][2], tva[L::NT][2], pB[2], uB[2];
-    read_k(nxt, ka, tka);
-    read_v(cur, va, tva);
-    mma_s(ka, tka, sn, sdn);
-    weights(sc, sdc, pB, uB);
-    mma_v(va, tva, pB, uB);
-    mask_apply<T, MASK, POW2>(sn, mk1, a.scale);
-    mask_tangent<T, MASK>(sdn, mk1, inv_us);
-    const float bm = block_max(sn);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * L::NC, 0);           // K / dK reads
-    __builtin_amdgcn_sched_group_barrier(0x100, 8 * L::NT, 0);           // V / dV transpose reads
-    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);                  // first weights
-#pragma unroll
-    for (int i = 0; i < 3 * L::NC; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // score product
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                 // weights
-    }
-#pragma unroll
-    for (int i = 0; i < 6 * L::NT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // value product
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                 // max of block k+1
-    }
-    rescale(bm);
-  };
-
-  f32x16 sA, sdA, sB, sdB;
-  // Prologue: tiles 0..2 in flight, wait for tile 0, settle block 0 if it needs no key mask.
-  if (n_tiles > 0) issue_tile(0, stage0);
-  if (n_tiles > 1) issue_tile(1, stage1);
-  if (n_tiles > 2) issue_tile(2, stage2);
-  if (n_tiles > 2) wait_vmcnt<2 * TILE_VMEM>();
-  else if (n_tiles > 1) wait_vmcnt<TILE_VMEM>();
-  else wait_vmcnt<0>();
-  ring_barrier();
-  bool ready = false;   // sA holds the current block's settled scores
-  if (0 <= last && !needs_keymask(0)) {
-    scores(stage0, sA, sdA);
-    MaskVals<MASK> mk;
-    load_mask(mk, kb * 32);
-    mask_apply<T, MASK, POW2>(sA, mk, a.scale);
-    mask_tangent<T, MASK>(sdA, mk, inv_us);
-    rescale(block_max(sA));
-    ready = true;
-  }
-  const int kfast = ready ? jm - 1 : 0;   // iterations 0 .. kfast-1 are pipelined
-  int k = 0;
-  for (; k + 4 <= kfast; k += 4) {
-    fast(k, stage0, stage1, stage3, sA, sdA, sB, sdB);
-    fast(k + 1, stage1, stage2, stage0, sB, sdB, sA, sdA);
-    fast(k + 2, stage2, stage3, stage1, sA, sdA, sB, sdB);
-    fast(k + 3, stage3, stage0, stage2, sB, sdB, sA, sdA);
-  }
-  if (k < kfast) {
-    fast(k, stage0, stage1, stage3, sA, sdA, sB, sdB);
-    if (k + 1 < kfast) fast(k + 1, stage1, stage2, stage0, sB, sdB, sA, sdA);
-    if (k + 2 < kfast) fast(k + 2, stage2, stage3, stage1, sA, sdA, sB, sdB);
-  }
-  if (kfast & 1) {   // block kfast's scores were left in sB
-    sA = sB;
-    sdA = sdB;
-  }
-
-  // Remaining iterations (diagonal, ragged tail, and barrier-only ones past this
-  // wave's range), one score buffer, stage chosen at run time.
-  auto stage_of = [&](int i) -> char* {
-    i &= 3;
-    return i == 0 ? stage0 : i == 1 ? stage1 : i == 2 ? stage2 : stage3;
-  };
-  for (k = kfast; k < n_loop; ++k) {
-    if (k + 2 < n_tiles) wait_vmcnt<TILE_VMEM>();
-    else wait_vmcnt<0>();
-    ring_barrier();
-    if (k + 3 < n_tiles) issue_tile(k + 3, stage_of(k + 3));
-    if (k > last) continue;
-    const char* cur = stage_of(k);
-    if (!ready) {
-      scores(cur, sA, sdA);
-      MaskVals<MASK> mk;
-      load_mask(mk, (kb + k) * 32);
-      mask_apply<T, MASK, POW2>(sA, mk, a.scale);
-      mask_tangent<T, MASK>(sdA, mk, inv_us);
-      if (needs_keymask(k)) hide_keys<CAUSAL>(sA, a.Nk, qi, (kb + k) * 32, hlf);
-      rescale(block_max(sA));
-    }
-    vec8 pB[2], uB[2];
-    weights(sA, sdA, pB, uB);
-    values(cur, pB, uB);
-    ready = false;   // the next block, if any, is settled at the top of the next iteration
-  }
-
-  if constexpr (SPLIT == 2) {
-    // Group 1 hands over its state through its own stages, once every wave is
-    // done reading them (first barrier); group 0 combines after the second.
-    // Every tile load has completed: the last iterations wait for all of them.
-    ring_barrier();
-    float4* acc = reinterpret_cast<float4*>(wave == 0 ? x0 : wave == 1 ? x1 : wave == 2 ? x2 : x3);
-    if constexpr (G == 1) {
-#pragma unroll
-      for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          acc[((2 * t) * 4 + g) * 64 + lane] = float4{accO[t][4 * g], accO[t][4 * g + 1], accO[t][4 * g + 2],
-                                                      accO[t][4 * g + 3]};
-          acc[((2 * t + 1) * 4 + g) * 64 + lane] = float4{accT[t][4 * g], accT[t][4 * g + 1],
-                                                          accT[t][4 * g + 2], accT[t][4 * g + 3]};
-        }
-      xst[wave * 64 + lane] = float4{st.m, st.moff, st.l, st.mu};
-      ring_barrier();
-      return;
-    } else {
-      ring_barrier();
-      const float4 o = xst[wave * 64 + lane];
-      const float m = fmaxf(st.m, o.x);   // -inf only if neither half saw a visible key
-      const float a0 = st.m == -INFINITY ? 0.0f : exp2f((st.m - m) * a.cx);
-      const float a1 = o.x == -INFINITY ? 0.0f : exp2f((o.x - m) * a.cx);
-#pragma unroll
-      for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 xo = acc[((2 * t) * 4 + g) * 64 + lane];
-          const float4 xt = acc[((2 * t + 1) * 4 + g) * 64 + lane];
-          accO[t][4 * g] = accO[t][4 * g] * a0 + xo.x * a1;
-          accO[t][4 * g + 1] = accO[t][4 * g + 1] * a0 + xo.y * a1;
-          accO[t][4 * g + 2] = accO[t][4 * g + 2] * a0 + xo.z * a1;
-          accO[t][4 * g + 3] = accO[t][4 * g + 3] * a0 + xo.w * a1;
-          accT[t][4 * g] = accT[t][4 * g] * a0 + xt.x * a1;
-          accT[t][4 * g + 1] = accT[t][4 * g + 1] * a0 + xt.y * a1;
-          accT[t][4 * g + 2] = accT[t][4 * g + 2] * a0 + xt.z * a1;
-          accT[t][4 * g + 3] = accT[t][4 * g + 3] * a0 + xt.w * a1;
-        }
-      st.l = st.l * a0 + o.z * a1;
-      st.mu = st.mu * a0 + o.w * a1;
-      st.m = m;
-      st.moff = m == -INFINITY ? 0.0f : m * a.cx;
-    }
-  }
-
-  // Epilogue: combine the two lane halves of each query column, normalise, store.
-  const float l = xhalf_sum(st.l);
-  const float mu = xhalf_sum(st.mu);
-  if (qi < a.Nq) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const float tl = POW2 ? mu * inv : mu * a.scale * inv;
-    uint16_t* op = static_cast<uint16_t*>(a.o) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
-    uint16_t* top = static_cast<uint16_t*>(a.to) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float ov[4], dv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ov[e] = accO[t][4 * g + e] * inv;
-          dv[e] = accT[t][4 * g + e] * inv - tl * ov[e];
-        }
-        const int dd = 32 * t + 8 * g + 4 * hlf;
-        *reinterpret_cast<uint2*>(op + dd) = uint2{T::pack2(ov[0], ov[1]), T::pack2(ov[2], ov[3])};
-        *reinterpret_cast<uint2*>(top + dd) = uint2{T::pack2(dv[0], dv[1]), T::pack2(dv[2], dv[3])};
-      }
-    }
-    if (hlf == 0) {
-      const int64_t ri = int64_t(bh) * a.Nq + qi;
-      a.lse[ri] = l > 0.0f ? (st.moff + log2f(l)) * kLn2 : -INFINITY;
-      if (a.tlse) a.tlse[ri] = tl;
-    }
-  }
-}
-
-// The kernel bodies use gfx950 builtins; the host pass only needs the launch stubs.
-template <typename T, int D, int MASK, bool CAUSAL, bool POW2, int SPLIT, int WV>
-__global__ __launch_bounds__(64 * WV * SPLIT, (D == 64 && WV == 4) ? 2 : 1) void fwd16_kernel(FwdArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  using L = Tile16<D>;
-  __shared__ __attribute__((aligned(16))) char s0[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char s1[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char s2[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char s3[L::STAGE_BYTES];
-  // the key tiles this head may see, found once by the whole workgroup
-  __shared__ int kred[2];
-  int t_lo, t_hi;
-  {
-    int qb, bh;
-    block_coords(a, qb, bh);
-    const Rsrc mr = mask_rsrc(a, bh / a.H, bh % a.H, mask_es<MASK>(2), nullptr, MASK == JVPATTN_MASK_BITS);
-    key_tiles<T, MASK, 2>(a, mr, kred, t_lo, t_hi);
-  }
-  if constexpr (SPLIT == 1) {
-    fwd16_body<T, D, MASK, CAUSAL, POW2, 1, 0, WV>(a, t_lo, t_hi, s0, s1, s2, s3, nullptr, nullptr, nullptr,
-                                                   nullptr, nullptr);
-  } else {
-    __shared__ __attribute__((aligned(16))) char s4[L::STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) char s5[L::STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) char s6[L::STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) char s7[L::STAGE_BYTES];
-    __shared__ float4 xst[kThreads];
-    if (__builtin_amdgcn_readfirstlane(threadIdx.x / (64 * WV)) == 0)
-      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 0, WV>(a, t_lo, t_hi, s0, s1, s2, s3, s4, s5, s6, s7, xst);
-    else
-      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 1, WV>(a, t_lo, t_hi, s4, s5, s6, s7, s4, s5, s6, s7, xst);
-  }
-#endif
-}
-
-// ------------------------------------------------ 16-bit ping-pong kernel (d = 64)
-//
-// Eight waves, 256 query rows per workgroup. Waves w and w+4 share a SIMD and
-// are held in opposite phases by workgroup barriers: while group A (waves
-// 0-3) issues only matrix-core work -- block i's value products and block
-// i+1's score products -- group B (waves 4-7) runs the vector work of the
-// previous iteration (mask, row maximum, exponentials, weights) and reads the
-// LDS operands for its next matrix phase; then the roles swap. The matrix
-// cores of each SIMD are fed by one wave while the other keeps the vector
-// units busy. Group B also issues the tile loads, during its matrix phases.
-//
-// Tiles of 32 keys live in a ring of 6 LDS stages (separate arrays; the loop
-// is unrolled by 6 so every access names its stage statically). Tile j is
-// loaded at iteration j-6 and first read at iteration j-2.
-
-constexpr int kPPWaves = 8;
-constexpr int kPPThreads = 64 * kPPWaves;
-constexpr int kPPBM = 32 * kPPWaves;
-constexpr int kPPStages = 6;
-
-template <typename T, int MASK, bool CAUSAL, bool POW2>
-__device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
-  constexpr int D = 64;
-  using L = Tile16<D>;
-  using vec8 = typename T::vec8;
-  static_assert(L::TILE_VMEM == 4, "group B loads a 32-key tile with 4 loads per thread");
-  __shared__ __attribute__((aligned(16))) char stage0[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char stage1[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char stage2[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char stage3[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char stage4[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char stage5[L::STAGE_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool grp_b = wave >= 4;
-  const int c32 = lane & 31;
-  const int hlf = lane >> 5;
-
-  int qb, bh;
-  block_coords(a, qb, bh);
-  const int b = bh / a.H, h = bh % a.H;
-  const int q0 = qb * kPPBM;
-  const int qw0 = q0 + 32 * wave;
-  const int qi = qw0 + c32;
-  const bool wave_live = qw0 < a.Nq;
-
-  const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
-  const int64_t khead = int64_t(bh / a.grp) * a.Nk * L::ROW;   // the key/value head it reads
-  const char* qp = static_cast<const char*>(a.q) + qhead;
-  const char* kp = static_cast<const char*>(a.k) + khead;
-  const char* vp = static_cast<const char*>(a.v) + khead;
-  const char* tqp = a.tq ? static_cast<const char*>(a.tq) + qhead : qp;
-  const char* tkp = a.tk ? static_cast<const char*>(a.tk) + khead : kp;
-  const char* tvp = a.tv ? static_cast<const char*>(a.tv) + khead : vp;
-  const int64_t qbytes = int64_t(a.Nq) * L::ROW;
-
-  vec8 qB[L::NC], tqB[L::NC];
-  {
-    const Rsrc rq = make_rsrc(qp, qbytes), rtq = make_rsrc(tqp, a.tq ? qbytes : 0);
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      const int off = qi * L::ROW + (hlf * (D / 2) + 8 * c) * 2;
-      qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
-      tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
-      if constexpr (POW2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qB[c][e] = static_cast<__bf16>(static_cast<float>(qB[c][e]) * a.scale);
-          tqB[c][e] = static_cast<__bf16>(static_cast<float>(tqB[c][e]) * a.scale);
-        }
-      }
-    }
-  }
-
-  f32x16 accO[L::NT], accT[L::NT];
-#pragma unroll
-  for (int t = 0; t < L::NT; ++t) {
-    accO[t] = f32x16{};
-    accT[t] = f32x16{};
-  }
-  RowState16 st{0.0f, 0.0f, 0.0f, false};
-  const Rsrc mr = mask_rsrc(a, b, h, mask_es<MASK>(2), nullptr, MASK == JVPATTN_MASK_BITS);
-  const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 2, a.tmask) : mr;
-  auto load_mask = [&](MaskVals<MASK>& m, int k0) {
-    if constexpr (MASK == kMaskAddT) mask_load_t(m, a, mr, mtr, qi, k0, hlf);
-    else mask_load<MASK>(m, a, mr, qi, k0, hlf);
-  };
-  __shared__ int kred[2];
-  int t0, t_hi;   // key tiles [t0, t_hi) may hold visible keys; loop tile k is absolute tile t0 + k
-  key_tiles<T, MASK, 2>(a, mr, kred, t0, t_hi);
-
-  const int kv_end = min(CAUSAL ? min(a.Nk, q0 + kPPBM) : a.Nk, 32 * t_hi);
-  const int n_tiles = max(0, (kv_end + L::BN - 1) / L::BN - t0);
-  const int last = !wave_live ? -1 : (CAUSAL ? min(n_tiles - 1, (qw0 >> 5) - t0) : n_tiles - 1);
-  auto kpos = [&](int k) { return (t0 + k) * 32; };   // first key of loop tile k
-  auto needs_keymask = [&](int k) { return (CAUSAL && kpos(k) + 31 > qw0) || (kpos(k) + 32 > a.Nk); };
-
-  // Tile loads (group B only): one 16-byte slot per tensor per thread.
-  const int tb = tid - 4 * 64;                     // 0..255 in group B
-  const int drow = (tb & 255) >> 3, dpg = tb & 7;
-  const int dl_off = drow * L::ROW + ((dpg ^ swz(drow)) << 4);
-  const int64_t kbytes = int64_t(a.Nk) * L::ROW;
-  const Rsrc rk = make_rsrc(kp, kbytes), rv = make_rsrc(vp, kbytes);
-  const Rsrc rtk = make_rsrc(tkp, a.tk ? kbytes : 0), rtv = make_rsrc(tvp, a.tv ? kbytes : 0);
-  auto issue_tile = [&](int j, char* stage) {
-    const int off = (t0 + j) * L::TENSOR_BYTES + dl_off;
-    const int slot = (wave - 4) * 64 * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot), 16,
-                                             off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rtk, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rv, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rtv, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-  };
-
-  int kofs[L::NC];
-#pragma unroll
-  for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ swz(c32)) << 4);
-  int vofs0[L::NT], vofs1[L::NT];
-  {
-    const int g16 = lane >> 4, i16 = lane & 15;
-    const int r0 = 4 * hlf + (i16 >> 2), r1 = r0 + 8;
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t) {
-      const int gcol = 4 * t + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-      vofs0[t] = r0 * L::ROW + ((gcol ^ swz(r0)) << 4) + 8 * (i16 & 1);
-      vofs1[t] = r1 * L::ROW + ((gcol ^ swz(r1)) << 4) + 8 * (i16 & 1);
-    }
-  }
-
-  // Pipeline registers carried from a vector phase to the next matrix phase.
-  vec8 ka[L::NC], tka[L::NC];          // K / dK operands of the next score products
-  vec8 va[L::NT][2], tva[L::NT][2];    // V / dV operands of the next value products
-  vec8 pB[2], uB[2];                   // weights of the block whose value products come next
-  f32x16 sn, sdn;                      // scores of the block after that
-  MaskVals<MASK> mk;                   // mask values of the block to settle next
-
-  auto read_k = [&](const char* sb) {
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      ka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb, kofs[c]));
-      tka[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + L::TENSOR_BYTES, kofs[c]));
-    }
-  };
-  auto read_v = [&](const char* sb) {
-    const char* sv = sb + 2 * L::TENSOR_BYTES;
-    const char* stv = sb + 3 * L::TENSOR_BYTES;
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int o0 = 16 * kc * L::ROW + vofs0[t], o1 = 16 * kc * L::ROW + vofs1[t];
-        va[t][kc] = __builtin_bit_cast(
-            vec8, __builtin_shufflevector(lds_read_tr(sv + o0), lds_read_tr(sv + o1), 0, 1, 2, 3, 4, 5, 6, 7));
-        tva[t][kc] = __builtin_bit_cast(
-            vec8, __builtin_shufflevector(lds_read_tr(stv + o0), lds_read_tr(stv + o1), 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-  };
-  auto mma_s = [&]() {
-    sn = f32x16{};
-    sdn = f32x16{};
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      sn = T::mfma(ka[c], qB[c], sn);
-      sdn = T::mfma(tka[c], qB[c], sdn);
-      sdn = T::mfma(ka[c], tqB[c], sdn);
-    }
-  };
-  auto mma_v = [&]() {
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        accO[t] = T::mfma(va[t][kc], pB[kc], accO[t]);
-        accT[t] = T::mfma(va[t][kc], uB[kc], accT[t]);
-        accT[t] = T::mfma(tva[t][kc], pB[kc], accT[t]);
-      }
-  };
-  // Scores of block k (in sn): mask, then weights into pB / uB. The V / dV
-  // operands of block k (stage stv) are read while the weights are packed.
-  auto settle = [&](int k, const char* stv) {
-    mask_apply<T, MASK, POW2>(sn, mk, a.scale);
-    mask_tangent<T, MASK>(sdn, mk, POW2 ? 1.0f : a.inv_scale);
-    if (needs_keymask(k)) hide_keys<CAUSAL>(sn, a.Nk, qi, kpos(k), hlf);
-    float e[16], alpha;
-    if (block_exp16<T>(sn, st, a.cx, e, alpha)) {
-#pragma unroll
-      for (int t = 0; t < L::NT; ++t) {
-        accO[t] *= alpha;
-        accT[t] *= alpha;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    read_v(stv);
-    block_pack16<T, !POW2>(e, sdn, a.scale, pB, uB);
-  };
-
-  // Matrix phase of iteration i: value products of block i (mu takes its
-  // weight products), then the score products of block i+1, whose K / dK
-  // operands (stage stn) are read first so they arrive while the value
-  // products run.
-  auto matrix_phase = [&](int i, const char* stn) {
-    if (i > last) return;
-    // This wave's matrix-core instructions go ahead of the vector work of the
-    // other wave on its SIMD (priority 2 against 0), so the matrix core does
-    // not wait for an issue slot.
-    __builtin_amdgcn_s_setprio(2);
-    // On a wave's last block the score products are of no use (stn holds
-    // some other tile, read harmlessly); issuing them anyway keeps the phase
-    // one straight-line block the scheduler can interleave.
-    read_k(stn);
-    mma_v();
-    block_mu16<T>(uB, st);
-    mma_s();
-    // The K / dK reads go out between the first value products, so their
-    // issue does not hold up the matrix cores; the score products follow.
-#pragma unroll
-    for (int j = 0; j < 2 * L::NC; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6 * L::NT - 2 * L::NC, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 3 * L::NC, 0);
-    __builtin_amdgcn_s_setprio(0);
-  };
-  // Vector phase of iteration i: settle block i+1 (V / dV from stage stn).
-  auto vector_phase = [&](int i, const char* stn) {
-    if (i + 1 > last) return;
-    settle(i + 1, stn);
-    if (i + 2 <= last) load_mask(mk, kpos(i + 2));
-  };
-  // Group B's wait for its loads of tile j; tiles issued after j may stay in flight.
-  auto wait_tile = [&](int j) {
-    const int newer = min(n_tiles - 1, j + 3) - j;   // tiles issued after j so far (at most 3)
-    if (newer >= 3) wait_vmcnt<12>();
-    else if (newer == 2) wait_vmcnt<8>();
-    else if (newer == 1) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
-  };
-
-  // Prologue: group B loads tiles 0..5; everyone settles block 0 and reads the
-  // operands of the first matrix phase.
-  if (grp_b) {
-    if (n_tiles > 0) issue_tile(0, stage0);
-    if (n_tiles > 1) issue_tile(1, stage1);
-    if (n_tiles > 2) issue_tile(2, stage2);
-    if (n_tiles > 3) issue_tile(3, stage3);
-    if (n_tiles > 4) issue_tile(4, stage4);
-    if (n_tiles > 5) issue_tile(5, stage5);
-    const int newer = min(n_tiles - 1, 5) - 1;   // tiles issued after tile 1
-    if (newer >= 4) wait_vmcnt<16>();
-    else if (newer == 3) wait_vmcnt<12>();
-    else if (newer == 2) wait_vmcnt<8>();
-    else if (newer == 1) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
-  }
-  ring_barrier();
-  if (0 <= last) {
-    read_k(stage0);
-    mma_s();
-    load_mask(mk, kpos(0));
-    settle(0, stage0);
-    if (1 <= last) load_mask(mk, kpos(1));
-  }
-  // Operands of the first matrix phase have arrived (states the loop's entry
-  // as free of pending LDS reads, as every later iteration is).
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-
-  // Every wave runs matrix(i), barrier, vector(i), barrier. Group B starts
-  // one barrier late, so the two waves of each SIMD are always in opposite
-  // phases: A's vector(i) runs beside B's matrix(i), A's matrix(i+1) beside
-  // B's vector(i). Group B loads tile i+6 into stage i%6 during matrix(i)
-  // (tile i was last read in B's vector(i-1)) and waits for tile i+3 at the
-  // end of vector(i) (first read in A's vector(i+1)).
-  if (grp_b) {
-    wait_tile(2);
-    ring_barrier();
-  }
-  auto iteration = [&](int i, char* st_r, char* st_r1) {
-    matrix_phase(i, st_r1);
-    if (grp_b && i + kPPStages < n_tiles) issue_tile(i + kPPStages, st_r);
-    ring_barrier();
-    vector_phase(i, st_r1);
-    if (grp_b) wait_tile(i + 3);
-    ring_barrier();
-  };
-  for (int i = 0; i < n_tiles; i += kPPStages) {
-    iteration(i, stage0, stage1);
-    if (i + 1 < n_tiles) iteration(i + 1, stage1, stage2);
-    if (i + 2 < n_tiles) iteration(i + 2, stage2, stage3);
-    if (i + 3 < n_tiles) iteration(i + 3, stage3, stage4);
-    if (i + 4 < n_tiles) iteration(i + 4, stage4, stage5);
-    if (i + 5 < n_tiles) iteration(i + 5, stage5, stage0);
-  }
-  if (!grp_b) ring_barrier();
-
-  const float l = xhalf_sum(st.l);
-  const float mu = xhalf_sum(st.mu);
-  if (qi < a.Nq) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const float tl = mu * inv;   // mu already sums e dS
-    uint16_t* op = static_cast<uint16_t*>(a.o) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
-    uint16_t* top = static_cast<uint16_t*>(a.to) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float ov[4], dv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ov[e] = accO[t][4 * g + e] * inv;
-          dv[e] = accT[t][4 * g + e] * inv - tl * ov[e];
-        }
-        const int dd = 32 * t + 8 * g + 4 * hlf;
-        *reinterpret_cast<uint2*>(op + dd) = uint2{T::pack2(ov[0], ov[1]), T::pack2(ov[2], ov[3])};
-        *reinterpret_cast<uint2*>(top + dd) = uint2{T::pack2(dv[0], dv[1]), T::pack2(dv[2], dv[3])};
-      }
-    }
-    if (hlf == 0) {
-      const int64_t ri = int64_t(bh) * a.Nq + qi;
-      a.lse[ri] = l > 0.0f ? (st.moff + log2f(l)) * kLn2 : -INFINITY;
-      if (a.tlse) a.tlse[ri] = tl;
-    }
-  }
-}
-
-template <typename T, int MASK, bool CAUSAL, bool POW2>
-__global__ __launch_bounds__(kPPThreads, 2) void fwd16pp_kernel(FwdArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  fwd16pp_body<T, MASK, CAUSAL, POW2>(a);
-#endif
-}
-
-// ------------------------------------------------------------- float32 kernel
-//
-// Same structure on v_mfma_f32_32x32x2_f32 (float32 products, no rounding of
-// the weights). Each product takes 2 entries of the inner dimension: for the
-// score products lane half hlf supplies head-dim entry hlf*D/2 + i for
-// product i; for the value products, product m contracts over the keys held
-// in C register m of each lane half, so P^T and (P dS)^T are used as they are.
-
-template <int D>
-struct Tile32 {
-  static constexpr int BN = 32;                 // keys per LDS tile
-  static constexpr int NT = D / 32;
-  static constexpr int GR = D / 4;              // 16-byte granules per K row
-  static constexpr int TENSOR_BYTES = BN * D * 4;
-  static constexpr int BUF_BYTES = 4 * TENSOR_BYTES;
-};
-
-template <int D>
-__device__ inline int k32_off(int row, int g) {
-  return row * (4 * D) + ((g ^ (row & 7)) << 4);
-}
-// V^T row = head-dim index, 32 keys (128 bytes, 8 granules).
-__device__ inline int vt32_off(int dd, int g) { return dd * 128 + ((g ^ (dd & 7)) << 4); }
-
-template <int D, int MASK, bool CAUSAL>
-__device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
-  using L = Tile32<D>;
-  extern __shared__ __attribute__((aligned(16))) char smem32[];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int c32 = lane & 31;
-  const int hlf = lane >> 5;
-
-  int qb, bh;
-  block_coords(a, qb, bh);
-  const int b = bh / a.H, h = bh % a.H;
-  const int q0 = qb * kBM;
-  const int qw0 = q0 + 32 * wave;
-  const int qi = qw0 + c32;
-  const bool wave_live = qw0 < a.Nq;
-
-  const float* qp = static_cast<const float*>(a.q) + int64_t(bh) * a.Nq * D;
-  const float* tqp = a.tq ? static_cast<const float*>(a.tq) + int64_t(bh) * a.Nq * D : nullptr;
-  const int64_t khead = int64_t(bh / a.grp) * a.Nk * D;   // the key/value head it reads
-  const float* kp = static_cast<const float*>(a.k) + khead;
-  const float* vp = static_cast<const float*>(a.v) + khead;
-  const float* tkp = a.tk ? static_cast<const float*>(a.tk) + khead : nullptr;
-  const float* tvp = a.tv ? static_cast<const float*>(a.tv) + khead : nullptr;
-
-  float qB[D / 2], tqB[D / 2];
-  {
-    const bool ok = qi < a.Nq;
-#pragma unroll
-    for (int i = 0; i < D / 2; i += 4) {
-      const int64_t off = int64_t(qi) * D + hlf * (D / 2) + i;
-      f32x4 x = ok ? *reinterpret_cast<const f32x4*>(qp + off) : f32x4{};
-      f32x4 y = (ok && tqp) ? *reinterpret_cast<const f32x4*>(tqp + off) : f32x4{};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qB[i + e] = x[e];
-        tqB[i + e] = y[e];
-      }
-    }
-  }
-
-  f32x16 accO[L::NT], accT[L::NT];
-#pragma unroll
-  for (int t = 0; t < L::NT; ++t) {
-    accO[t] = f32x16{};
-    accT[t] = f32x16{};
-  }
-  RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
-  const Rsrc mr = mask_rsrc(a, b, h, mask_es<MASK>(4), nullptr, MASK == JVPATTN_MASK_BITS);
-  const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 4, a.tmask) : mr;
-  __shared__ int kred[2];
-  int t0, t_hi;   // key tiles [t0, t_hi) may hold visible keys
-  key_tiles<F16, MASK, 4>(a, mr, kred, t0, t_hi);
-
-  const int kv_end = min(CAUSAL ? min(a.Nk, q0 + kBM) : a.Nk, 32 * t_hi);
-  const int n_tiles = max(0, (kv_end + L::BN - 1) / L::BN - t0);
-  char* sk = smem32;
-  char* stk = smem32 + L::TENSOR_BYTES;
-  char* sv = smem32 + 2 * L::TENSOR_BYTES;
-  char* stv = smem32 + 3 * L::TENSOR_BYTES;
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int kbase = (t0 + j) * L::BN;
-    // Global -> LDS. K rows as granules; V transposed element by element.
-    for (int gi = tid; gi < L::BN * L::GR; gi += kThreads) {
-      const int row = gi / L::GR, g = gi % L::GR;
-      const int key = kbase + row;
-      const int64_t off = int64_t(key) * D + 4 * g;
-      const bool ok = key < a.Nk;
-      lds_store<f32x4>(sk, k32_off<D>(row, g), ok ? *reinterpret_cast<const f32x4*>(kp + off) : f32x4{});
-      lds_store<f32x4>(stk, k32_off<D>(row, g),
-                       (ok && tkp) ? *reinterpret_cast<const f32x4*>(tkp + off) : f32x4{});
-      const f32x4 x = ok ? *reinterpret_cast<const f32x4*>(vp + off) : f32x4{};
-      const f32x4 y = (ok && tvp) ? *reinterpret_cast<const f32x4*>(tvp + off) : f32x4{};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dd = 4 * g + e;
-        const int voff = vt32_off(dd, row >> 2) + 4 * (row & 3);
-        lds_store<float>(sv, voff, x[e]);
-        lds_store<float>(stv, voff, y[e]);
-      }
-    }
-    __syncthreads();
-
-    const int k0 = kbase;
-    if (wave_live && k0 < kv_end && !(CAUSAL && k0 > qw0 + 31)) {
-      f32x16 s{}, sd{};
-#pragma unroll
-      for (int i = 0; i < D / 2; i += 4) {
-        const int g = (hlf * (D / 2) + i) / 4;
-        const f32x4 ka = lds_load<f32x4>(sk, k32_off<D>(c32, g));
-        const f32x4 tka = lds_load<f32x4>(stk, k32_off<D>(c32, g));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[e], qB[i + e], s, 0, 0, 0);
-          sd = __builtin_amdgcn_mfma_f32_32x32x2f32(tka[e], qB[i + e], sd, 0, 0, 0);
-          sd = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[e], tqB[i + e], sd, 0, 0, 0);
-        }
-      }
-      const bool elem_mask = (CAUSAL && k0 + 31 > qw0) || (k0 + 32 > a.Nk);
-      constexpr bool ADD = MASK == JVPATTN_MASK_ADDITIVE || MASK == kMaskAddT;
-      mask_scores<F16, ADD ? -1 : MASK, CAUSAL, false>(s, a, mr, qi, k0, hlf, elem_mask);
-      if constexpr (ADD) {
-        // float32 additive mask: element (qi, key) for the 16 keys of this lane
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + (r >> 2) * 8 + 4 * hlf + (r & 3);
-          const float mv = __uint_as_float(
-              __builtin_amdgcn_raw_buffer_load_b32(mr, (qi * int(a.msq) + key) * 4, 0, 0));
-          s[r] = fmaf(s[r], a.scale, mv);   // hidden keys are already -inf
-          if constexpr (MASK == kMaskAddT) {
-            // the mask's tangent joins the score tangent (sd * scale = dS)
-            const float tv = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(mtr, (qi * int(a.msq) + key) * 4, 0, 0));
-            sd[r] = fmaf(tv, a.inv_scale, sd[r]);
-          }
-        }
-      }
-      float alpha;
-      if (softmax_block(s, sd, st, a.cx, a.thr, alpha)) {
-#pragma unroll
-        for (int t = 0; t < L::NT; ++t) {
-          accO[t] *= alpha;
-          accT[t] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < L::NT; ++t) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int off = vt32_off(32 * t + c32, 2 * g + hlf);
-          const f32x4 va = lds_load<f32x4>(sv, off);
-          const f32x4 tva = lds_load<f32x4>(stv, off);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int m = 4 * g + e;
-            accO[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[e], s[m], accO[t], 0, 0, 0);
-            accT[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[e], sd[m] * a.scale, accT[t], 0, 0, 0);
-            accT[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(tva[e], s[m], accT[t], 0, 0, 0);
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  const float l = xhalf_sum(st.l);
-  const float mu = xhalf_sum(st.mu);
-  if (qi < a.Nq) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const float tl = mu * a.scale * inv;
-    float* op = static_cast<float*>(a.o) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
-    float* top = static_cast<float*>(a.to) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 ov, dv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ov[e] = accO[t][4 * g + e] * inv;
-          dv[e] = accT[t][4 * g + e] * inv - tl * ov[e];
-        }
-        const int dd = 32 * t + 8 * g + 4 * hlf;
-        *reinterpret_cast<f32x4*>(op + dd) = ov;
-        *reinterpret_cast<f32x4*>(top + dd) = dv;
-      }
-    }
-    if (hlf == 0) {
-      const int64_t ri = int64_t(bh) * a.Nq + qi;
-      a.lse[ri] = l > 0.0f ? (st.moff + log2f(l)) * kLn2 : -INFINITY;
-      if (a.tlse) a.tlse[ri] = tl;
-    }
-  }
-}
-
-template <int D, int MASK, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd32_kernel(FwdArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  fwd32_body<D, MASK, CAUSAL>(a);
-#endif
-}
-
-// ---------------------------------------------------------------- dispatch
-
-template <int MASK, bool CAUSAL>
-hipError_t launch_pp(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
-  const dim3 block(kPPThreads);
-  if (dtype == JVPATTN_BF16) {
-    if (pow2) hipLaunchKernelGGL((fwd16pp_kernel<BF16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
-    else hipLaunchKernelGGL((fwd16pp_kernel<BF16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
-  } else {
-    hipLaunchKernelGGL((fwd16pp_kernel<F16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
-  }
-  return hipGetLastError();
-}
-
-// The 4-wave kernel for d = 64: whole key range (split = 0), halves over two
-// groups of four waves (split = 1), or halves over two groups of two waves on
-// 64-row blocks (split = 2).
-template <typename T, int MASK, bool CAUSAL, bool POW2>
-void launch_d64(int split, const FwdArgs& args, dim3 grid, hipStream_t stream) {
-  if (split == 2)
-    hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 2, 2>), grid, dim3(2 * 128), 0, stream, args);
-  else if (split == 1)
-    hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 2, 4>), grid, dim3(2 * kThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 1, 4>), grid, dim3(kThreads), 0, stream, args);
-}
-
-template <int MASK, bool CAUSAL>
-hipError_t launch_typed(int dtype, int d, bool pow2, int split, const FwdArgs& args, dim3 grid,
-                        hipStream_t stream) {
-  const dim3 block(kThreads);
-  if (dtype == JVPATTN_BF16) {
-    if (pow2) {
-      if (d == 64) launch_d64<BF16, MASK, CAUSAL, true>(split, args, grid, stream);
-      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, true, 1, 4>), grid, block, 0, stream, args);
-    } else {
-      if (d == 64) launch_d64<BF16, MASK, CAUSAL, false>(split, args, grid, stream);
-      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, false, 1, 4>), grid, block, 0, stream, args);
-    }
-  } else if (dtype == JVPATTN_F16) {
-    if (d == 64) launch_d64<F16, MASK, CAUSAL, false>(split, args, grid, stream);
-    else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, false, 1, 4>), grid, block, 0, stream, args);
-  } else {
-    if (d == 64) {
-      hipLaunchKernelGGL((fwd32_kernel<64, MASK, CAUSAL>), grid, block, Tile32<64>::BUF_BYTES, stream, args);
-    } else {
-      auto fn = fwd32_kernel<128, MASK, CAUSAL>;
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         Tile32<128>::BUF_BYTES);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(fn, grid, block, Tile32<128>::BUF_BYTES, stream, args);
-    }
-  }
-  return hipGetLastError();
-}
+constexpr int kBM = 128;      // query rows per 4-wave workgroup
+constexpr int kPPBM = 256;    // query rows per ping-pong workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Process-wide algorithm selection (jvpattn_fwd_set_algo); -1 = automatic.
+std::atomic<int> g_algo_kernel{-1}, g_algo_order{-1}, g_algo_key_range{-1};
 
 // Queue the forward for arguments already validated (sizes from the check).
 // tmask: the additive mask's tangent, or NULL.
@@ -1333,7 +46,7 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   const bool pow2 = p->dtype == JVPATTN_BF16 && std::frexp(p->scale, &sexp) == 0.5f;
   // Otherwise scores stay raw (q.k) without an additive mask, so scale folds into cx.
   a.cx = (additive || pow2) ? kLog2e : p->scale * kLog2e;
-  const float tau = p->dtype == JVPATTN_BF16 ? BF16::kTau : p->dtype == JVPATTN_F16 ? F16::kTau : 8.0f;
+  const float tau = p->dtype == JVPATTN_BF16 ? kTauBF16 : p->dtype == JVPATTN_F16 ? kTauF16 : kTauF32;
   a.thr = tau / a.cx;
   {
     const int mes = p->mask_kind == JVPATTN_MASK_BOOL ? 1 : elem_bytes(p->dtype);
@@ -1350,17 +63,19 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   // (two groups of two waves) when even 128-row blocks leave CUs without one
   // -- or, causal, fewer than two: there twice the blocks, heaviest first,
   // even out the triangle. Other types and d: the 4-wave kernel (float32: its
-  // own). JVPATTN_FWD_KERNEL=pp|wg4|split|split64 forces one (testing).
+  // own). jvpattn_fwd_set_algo can force a family.
   const int64_t n64 = (p->Nq + 63) / 64, n128 = (p->Nq + kBM - 1) / kBM, n256 = (p->Nq + kPPBM - 1) / kPPBM;
   const bool d64_16 = p->d == 64 && p->dtype != JVPATTN_F32;
   bool pp = d64_16 && n256 * a.BH >= 256;
   const int64_t small = p->causal ? 512 : 256;
   int split = !d64_16 || pp ? 0 : n128 * a.BH < small ? 2 : n128 * a.BH < 512 ? 1 : 0;
-  if (const char* env = std::getenv("JVPATTN_FWD_KERNEL")) {
-    if (std::strcmp(env, "pp") == 0) pp = d64_16, split = 0;
-    if (std::strcmp(env, "wg4") == 0) pp = false, split = 0;
-    if (std::strcmp(env, "split") == 0) pp = false, split = d64_16 ? 1 : 0;
-    if (std::strcmp(env, "split64") == 0) pp = false, split = d64_16 ? 2 : 0;
+  // A forced family applies where it exists (the ping-pong and split kernels: 16-bit, d = 64).
+  switch (g_algo_kernel.load(std::memory_order_relaxed)) {
+    case JVPATTN_FWD_PINGPONG: pp = d64_16, split = 0; break;
+    case JVPATTN_FWD_WG4: pp = false, split = 0; break;
+    case JVPATTN_FWD_SPLIT: pp = false, split = d64_16 ? 1 : 0; break;
+    case JVPATTN_FWD_SPLIT64: pp = false, split = d64_16 ? 2 : 0; break;
+    default: break;
   }
   a.n_qblk = static_cast<int>(pp ? n256 : split == 2 ? n64 : n128);
   const int64_t blocks = int64_t(a.n_qblk) * a.BH;
@@ -1368,69 +83,44 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   // Head-major order once the grid is several times what the chip holds at
   // once (at most 2 workgroups per CU x 256 CUs), so a head's query blocks
   // would otherwise run far apart in time and each re-read its key/value
-  // tiles from HBM. JVPATTN_FWD_ORDER=qb|head forces one (testing).
+  // tiles from HBM. jvpattn_fwd_set_algo can force either order.
   a.head_major = a.n_qblk > 1 && a.BH % 8 == 0 && blocks >= 4 * 512;
   // A mask with row stride 0 is the same for every query row: scan it once per
-  // workgroup and skip the key tiles it hides entirely.
-  // JVPATTN_FWD_KEYRANGE=0 scans nothing and runs every tile (testing).
-  a.key_range = mask != nullptr && p->mask_stride_q == 0;
-  if (const char* env = std::getenv("JVPATTN_FWD_KEYRANGE"))
-    if (std::strcmp(env, "0") == 0) a.key_range = 0;
-  if (const char* env = std::getenv("JVPATTN_FWD_ORDER")) {
-    if (std::strcmp(env, "qb") == 0) a.head_major = 0;
-    if (std::strcmp(env, "head") == 0) a.head_major = a.n_qblk > 1 && a.BH % 8 == 0;
-  }
+  // workgroup and skip the key tiles it hides entirely (unless switched off by
+  // jvpattn_fwd_set_algo: then every tile runs).
+  a.key_range = mask != nullptr && p->mask_stride_q == 0 && g_algo_key_range.load(std::memory_order_relaxed) != 0;
+  const int order = g_algo_order.load(std::memory_order_relaxed);
+  if (order == 0) a.head_major = 0;
+  if (order == 1) a.head_major = a.n_qblk > 1 && a.BH % 8 == 0;
   const dim3 grid(static_cast<unsigned>(blocks));
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  hipError_t e;
+  const int kernel = pp ? kFwdPingPong : split == 2 ? kFwdSplit64 : split == 1 ? kFwdSplit : kFwdWG4;
   const bool c = p->causal != 0;
-  if (pp) {
-    switch (p->mask_kind) {
-      case JVPATTN_MASK_NONE:
-        e = c ? launch_pp<JVPATTN_MASK_NONE, true>(p->dtype, pow2, a, grid, s)
-              : launch_pp<JVPATTN_MASK_NONE, false>(p->dtype, pow2, a, grid, s);
-        break;
-      case JVPATTN_MASK_BOOL:
-        e = c ? launch_pp<JVPATTN_MASK_BOOL, true>(p->dtype, pow2, a, grid, s)
-              : launch_pp<JVPATTN_MASK_BOOL, false>(p->dtype, pow2, a, grid, s);
-        break;
-      case JVPATTN_MASK_BITS:
-        e = c ? launch_pp<JVPATTN_MASK_BITS, true>(p->dtype, pow2, a, grid, s)
-              : launch_pp<JVPATTN_MASK_BITS, false>(p->dtype, pow2, a, grid, s);
-        break;
-      default:
-        if (tmask)
-          e = c ? launch_pp<kMaskAddT, true>(p->dtype, pow2, a, grid, s)
-                : launch_pp<kMaskAddT, false>(p->dtype, pow2, a, grid, s);
-        else
-          e = c ? launch_pp<JVPATTN_MASK_ADDITIVE, true>(p->dtype, pow2, a, grid, s)
-                : launch_pp<JVPATTN_MASK_ADDITIVE, false>(p->dtype, pow2, a, grid, s);
-        break;
-    }
-  } else {
-    switch (p->mask_kind) {
-      case JVPATTN_MASK_NONE:
-        e = c ? launch_typed<JVPATTN_MASK_NONE, true>(p->dtype, p->d, pow2, split, a, grid, s)
-              : launch_typed<JVPATTN_MASK_NONE, false>(p->dtype, p->d, pow2, split, a, grid, s);
-        break;
-      case JVPATTN_MASK_BOOL:
-        e = c ? launch_typed<JVPATTN_MASK_BOOL, true>(p->dtype, p->d, pow2, split, a, grid, s)
-              : launch_typed<JVPATTN_MASK_BOOL, false>(p->dtype, p->d, pow2, split, a, grid, s);
-        break;
-      case JVPATTN_MASK_BITS:
-        e = c ? launch_typed<JVPATTN_MASK_BITS, true>(p->dtype, p->d, pow2, split, a, grid, s)
-              : launch_typed<JVPATTN_MASK_BITS, false>(p->dtype, p->d, pow2, split, a, grid, s);
-        break;
-      default:
-        if (tmask)
-          e = c ? launch_typed<kMaskAddT, true>(p->dtype, p->d, pow2, split, a, grid, s)
-                : launch_typed<kMaskAddT, false>(p->dtype, p->d, pow2, split, a, grid, s);
-        else
-          e = c ? launch_typed<JVPATTN_MASK_ADDITIVE, true>(p->dtype, p->d, pow2, split, a, grid, s)
-                : launch_typed<JVPATTN_MASK_ADDITIVE, false>(p->dtype, p->d, pow2, split, a, grid, s);
-        break;
-    }
+  int mk = p->mask_kind;
+  if (mk == JVPATTN_MASK_ADDITIVE && tmask) mk = kMaskAddT;
+  hipError_t e;
+  switch (mk) {
+    case JVPATTN_MASK_NONE:
+      e = c ? launch_fwd<JVPATTN_MASK_NONE, true>(kernel, p->dtype, p->d, pow2, a, grid, s)
+            : launch_fwd<JVPATTN_MASK_NONE, false>(kernel, p->dtype, p->d, pow2, a, grid, s);
+      break;
+    case JVPATTN_MASK_BOOL:
+      e = c ? launch_fwd<JVPATTN_MASK_BOOL, true>(kernel, p->dtype, p->d, pow2, a, grid, s)
+            : launch_fwd<JVPATTN_MASK_BOOL, false>(kernel, p->dtype, p->d, pow2, a, grid, s);
+      break;
+    case JVPATTN_MASK_BITS:
+      e = c ? launch_fwd<JVPATTN_MASK_BITS, true>(kernel, p->dtype, p->d, pow2, a, grid, s)
+            : launch_fwd<JVPATTN_MASK_BITS, false>(kernel, p->dtype, p->d, pow2, a, grid, s);
+      break;
+    case JVPATTN_MASK_ADDITIVE:
+      e = c ? launch_fwd<JVPATTN_MASK_ADDITIVE, true>(kernel, p->dtype, p->d, pow2, a, grid, s)
+            : launch_fwd<JVPATTN_MASK_ADDITIVE, false>(kernel, p->dtype, p->d, pow2, a, grid, s);
+      break;
+    default:
+      e = c ? launch_fwd<kMaskAddT, true>(kernel, p->dtype, p->d, pow2, a, grid, s)
+            : launch_fwd<kMaskAddT, false>(kernel, p->dtype, p->d, pow2, a, grid, s);
+      break;
   }
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
@@ -1460,4 +150,14 @@ extern "C" int jvpattn_fwd_tmask(const jvpattn_params* p, const void* q, const v
   const int rc = check_fwd_tmask(p, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, &sz);
   if (rc != JVPATTN_OK) return rc;
   return fwd_launch(p, sz, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, stream);
+}
+
+extern "C" int jvpattn_fwd_set_algo(int kernel, int order, int key_range) {
+  using namespace jvpattn;
+  if (kernel < -1 || kernel > JVPATTN_FWD_SPLIT64 || order < -1 || order > 1 || key_range < -1 || key_range > 1)
+    return JVPATTN_ERR_ARG;
+  g_algo_kernel.store(kernel, std::memory_order_relaxed);
+  g_algo_order.store(order, std::memory_order_relaxed);
+  g_algo_key_range.store(key_range, std::memory_order_relaxed);
+  return JVPATTN_OK;
 }

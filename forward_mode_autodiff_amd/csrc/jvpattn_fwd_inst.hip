@@ -1,0 +1,17 @@
+// Kernel instances of the forward for one (mask kind, causal) pair, chosen
+// at compile time: the build compiles this file once per pair
+// (-DJVPATTN_INST_MASK=<kind> -DJVPATTN_INST_CAUSAL=<0|1>) so the instances
+// build in parallel.
+#include "jvpattn_fwd_kernels.h"
+
+#ifndef JVPATTN_INST_MASK
+#error "JVPATTN_INST_MASK must be defined"
+#endif
+#ifndef JVPATTN_INST_CAUSAL
+#error "JVPATTN_INST_CAUSAL must be defined"
+#endif
+
+namespace jvpattn {
+template hipError_t launch_fwd<JVPATTN_INST_MASK, (JVPATTN_INST_CAUSAL != 0)>(int, int, int, bool, const FwdArgs&,
+                                                                            dim3, hipStream_t);
+}  // namespace jvpattn

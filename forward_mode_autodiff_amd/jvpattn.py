@@ -21,8 +21,10 @@ JVPATTN_MASK_NONE, JVPATTN_MASK_BOOL, JVPATTN_MASK_ADDITIVE, JVPATTN_MASK_BITS =
 ERRORS = {
     0: "JVPATTN_OK", -1: "JVPATTN_ERR_NULL", -2: "JVPATTN_ERR_SHAPE", -3: "JVPATTN_ERR_DTYPE",
     -4: "JVPATTN_ERR_HEADDIM", -5: "JVPATTN_ERR_MASK", -6: "JVPATTN_ERR_ALIGN", -7: "JVPATTN_ERR_SCALE",
-    -8: "JVPATTN_ERR_ALIAS", -9: "JVPATTN_ERR_HIP", -10: "JVPATTN_ERR_WORKSPACE",
+    -8: "JVPATTN_ERR_ALIAS", -9: "JVPATTN_ERR_HIP", -10: "JVPATTN_ERR_WORKSPACE", -11: "JVPATTN_ERR_ARG",
 }
+JVPATTN_ALGO_AUTO = -1
+FWD_KERNELS = {"wg4": 0, "pp": 1, "split": 2, "split64": 3}   # jvpattn_fwd_kernel values
 _DTYPE_CODE = {torch.float32: JVPATTN_F32, torch.float16: JVPATTN_F16, torch.bfloat16: JVPATTN_BF16}
 
 
@@ -78,8 +80,24 @@ def load_library(path: str = LIB_PATH):
     lib.jvpattn_bwd_tmask.restype = ctypes.c_int
     lib.jvpattn_check_bwd_tmask.argtypes = [P] + [vp] * 21 + [ctypes.c_size_t]
     lib.jvpattn_check_bwd_tmask.restype = ctypes.c_int
+    lib.jvpattn_fwd_set_algo.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.jvpattn_fwd_set_algo.restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def jvpattn_fwd_set_algo(kernel=None, order=None, key_range=None) -> None:
+    """Force the forward's launch plan process-wide (None = the library's choice).
+
+    kernel: "wg4" | "pp" | "split" | "split64"; order: "qb" (heaviest query blocks first) | "head"
+    (head-major per XCD); key_range: False = never skip key tiles outside a shared mask row's range.
+    """
+    k = JVPATTN_ALGO_AUTO if kernel is None else FWD_KERNELS[kernel]
+    o = JVPATTN_ALGO_AUTO if order is None else {"qb": 0, "head": 1}[order]
+    r = JVPATTN_ALGO_AUTO if key_range is None else int(bool(key_range))
+    rc = load_library().jvpattn_fwd_set_algo(k, o, r)
+    if rc != 0:
+        raise JvpattnError(rc, jvpattn_strerror(rc))
 
 
 def jvpattn_strerror(code: int) -> str:

@@ -74,7 +74,8 @@ enum {
   JVPATTN_ERR_SCALE = -7,    /* scale not finite or not > 0 */
   JVPATTN_ERR_ALIAS = -8,    /* an output overlaps an input or another output */
   JVPATTN_ERR_HIP = -9,      /* the HIP runtime reported an error on launch */
-  JVPATTN_ERR_WORKSPACE = -10  /* jvpattn_bwd: workspace NULL, too small, misaligned, or overlapping */
+  JVPATTN_ERR_WORKSPACE = -10, /* jvpattn_bwd: workspace NULL, too small, misaligned, or overlapping */
+  JVPATTN_ERR_ARG = -11        /* jvpattn_fwd_set_algo: a value outside its documented range */
 };
 
 typedef struct {
@@ -248,6 +249,34 @@ int jvpattn_check_bwd_tmask(const jvpattn_params* params,
                             const void* dq, const void* dk, const void* dv,
                             const void* dtq, const void* dtk, const void* dtv,
                             const void* workspace, size_t workspace_bytes);
+
+/* ------------------------------------------------------ algorithm selection
+ *
+ * Kernel families of the 16-bit forward. The library picks one per call from
+ * the grid it would launch; these values force one (tuning and testing).
+ * Every family computes the same operation to the same rounding rules. */
+typedef enum {
+  JVPATTN_ALGO_AUTO = -1,
+  JVPATTN_FWD_WG4 = 0,       /* 4 waves, 128 query rows per workgroup (every d) */
+  JVPATTN_FWD_PINGPONG = 1,  /* 8 waves in two alternating groups, 256 rows (d = 64) */
+  JVPATTN_FWD_SPLIT = 2,     /* 4-wave body, key range split over two wave groups (d = 64) */
+  JVPATTN_FWD_SPLIT64 = 3    /* the same on 64-row blocks, two waves per group (d = 64) */
+} jvpattn_fwd_kernel;
+
+/* Force the forward's launch plan for later jvpattn_fwd / jvpattn_fwd_tmask
+ * calls in this process (a process-wide setting; calls already queued are
+ * unaffected). Each argument is JVPATTN_ALGO_AUTO (-1) for the library's own
+ * choice, or:
+ *   kernel    : a jvpattn_fwd_kernel value; a family that does not exist for
+ *               a call's type and head dimension falls back to the 4-wave
+ *               kernel (float32 always runs its own kernel);
+ *   order     : 0 = heaviest query blocks first over all heads, 1 = the query
+ *               blocks of each head back to back on one XCD;
+ *   key_range : 0 = never scan a mask shared by all query rows for its
+ *               visible key range (every key tile runs); 1 = automatic.
+ * Returns JVPATTN_OK, or JVPATTN_ERR_ARG (nothing changed) for a value out of
+ * range. Not meant to be changed while another thread launches forwards. */
+int jvpattn_fwd_set_algo(int kernel, int order, int key_range);
 
 /* A static, human-readable description of a return code. */
 const char* jvpattn_strerror(int code);

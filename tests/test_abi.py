@@ -25,8 +25,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     assert declared_functions() == ["jvpattn_bwd", "jvpattn_bwd_tmask", "jvpattn_bwd_workspace_bytes",
                                     "jvpattn_check_bwd", "jvpattn_check_bwd_tmask", "jvpattn_check_fwd",
-                                    "jvpattn_check_fwd_tmask", "jvpattn_fwd", "jvpattn_fwd_tmask",
-                                    "jvpattn_last_hip_error", "jvpattn_strerror"]
+                                    "jvpattn_check_fwd_tmask", "jvpattn_fwd", "jvpattn_fwd_set_algo",
+                                    "jvpattn_fwd_tmask", "jvpattn_last_hip_error", "jvpattn_strerror"]
 
 
 @needs_lib
@@ -403,3 +403,15 @@ def test_check_bwd_mask_tangent():
     assert chk(dk=t) == -8                     # a gradient over it
     assert chk(ws=t) == -10                    # the workspace over it
     assert chk(o=t) == -8                      # a forward output over it
+
+
+@needs_lib
+def test_fwd_set_algo_rejects_out_of_range_values():
+    lib = J.load_library()
+    for args in [(4, -1, -1), (-2, -1, -1), (-1, 2, -1), (-1, -1, 2), (-1, -3, -1)]:
+        assert lib.jvpattn_fwd_set_algo(*args) == -11, args
+    for args in [(-1, -1, -1), (0, 0, 0), (3, 1, 1)]:
+        assert lib.jvpattn_fwd_set_algo(*args) == 0, args
+    assert lib.jvpattn_fwd_set_algo(-1, -1, -1) == 0
+    with pytest.raises(KeyError):
+        J.jvpattn_fwd_set_algo(kernel="nope")

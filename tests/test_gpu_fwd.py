@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from forward_mode_autodiff_amd import inputs as I
-from forward_mode_autodiff_amd.jvpattn import jvpattn_fwd
+from forward_mode_autodiff_amd.jvpattn import jvpattn_fwd, jvpattn_fwd_set_algo
 from oracle import oracle_fwd
 from tests.parity import assert_parity, failures
 
@@ -28,9 +28,17 @@ DEV = "cuda:0"
 KERNELS = ["pp", "wg4", "split", "split64"]
 
 
+@pytest.fixture(autouse=True)
+def _automatic_plan():
+    """Every test starts and ends with the library's own launch plan."""
+    jvpattn_fwd_set_algo()
+    yield
+    jvpattn_fwd_set_algo()
+
+
 @pytest.fixture(params=KERNELS)
-def kernel(request, monkeypatch):
-    monkeypatch.setenv("JVPATTN_FWD_KERNEL", request.param)
+def kernel(request, _automatic_plan):
+    jvpattn_fwd_set_algo(kernel=request.param)
     return request.param
 
 
@@ -405,16 +413,16 @@ def test_grouped_kv_heads_match_repeated_heads(kernel):
     I.Workload("order_gqa_f16", B=4, H=8, Hkv=2, N=520, d=64, dtype="f16", std=1.0, seed=18),
     I.Workload("order_d128_bf16", B=1, H=8, N=300, d=128, dtype="bf16", std=1.0, seed=19),
 ], ids=lambda w: w.name)
-def test_block_order(w, order, kernel, monkeypatch):
+def test_block_order(w, order, kernel):
     """Both workgroup orders (heaviest query block first over all heads, or head-major per XCD) give
     the oracle's results on every kernel."""
-    monkeypatch.setenv("JVPATTN_FWD_ORDER", order)
+    jvpattn_fwd_set_algo(kernel=kernel, order=order)
     check(w)
 
 
-def test_wide_query_block_major_sampled(monkeypatch):
+def test_wide_query_block_major_sampled():
     """B=256, H=8, N=512, d=128, bf16 in the order its grid does not take by default: sampled heads."""
-    monkeypatch.setenv("JVPATTN_FWD_ORDER", "qb")
+    jvpattn_fwd_set_algo(order="qb")
     w = I.WIDE
     x = I.make_inputs(w)
     got = gpu_run(x, False)
@@ -437,10 +445,10 @@ KEY_MASKS = [
 
 @pytest.mark.parametrize("skip", ["1", "0"], ids=["skip", "noskip"])
 @pytest.mark.parametrize("layout,kind,causal,dtype", KEY_MASKS, ids=lambda v: str(v))
-def test_key_masks(layout, kind, causal, dtype, skip, kernel, monkeypatch):
+def test_key_masks(layout, kind, causal, dtype, skip, kernel):
     """[B,1,1,Nk] masks: the kernels skip the key tiles outside the visible range (or, forced, run them
     all); results as the oracle's."""
-    monkeypatch.setenv("JVPATTN_FWD_KEYRANGE", skip)
+    jvpattn_fwd_set_algo(kernel=kernel, key_range=skip == "1")
     w = I.Workload(f"keymask_{layout}_{kind}", B=4, H=2, N=300, d=64, dtype=dtype, causal=causal, mask_kind=kind,
                    mask_layout=layout, std=1.0, seed=30)
     check(w)
