@@ -128,11 +128,48 @@ def _layout(mask):
     return tuple(0 if mask.shape[i] == 1 else mask.stride(i) for i in range(3)) + (mask.stride(3),)
 
 
-def make_params(q, k, mask=None, causal=False, scale=None) -> tuple:
-    """Fill jvpattn_params from tensors. Returns (params, mask tensor as passed to the library)."""
+def _tensor(name, t, shape, dtype, device, optional=False):
+    """Reject a tensor the library would misread: wrong type, shape, dtype, device or layout.
+
+    Raises TypeError (not a tensor, wrong dtype) or ValueError (shape, device, non-contiguous) before
+    anything is queued; the C interface only sees raw pointers and cannot check these itself.
+    """
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, q is on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+MASK_KINDS = {"bool": JVPATTN_MASK_BOOL, "additive": JVPATTN_MASK_ADDITIVE, "bits": JVPATTN_MASK_BITS}
+
+
+def make_params(q, k, mask=None, causal=False, scale=None, mask_kind=None) -> tuple:
+    """Fill jvpattn_params from tensors. Returns (params, mask tensor as passed to the library).
+
+    mask_kind: None infers it from the mask's dtype -- bool/uint8 -> "bool", q's dtype -> "additive";
+    a bit-packed mask (int32 words, ``pack_mask_bits``) must say ``mask_kind="bits"``, so an int32 0/1
+    mask is never silently read as bits.
+    """
+    if not isinstance(q, torch.Tensor) or not isinstance(k, torch.Tensor):
+        raise TypeError("q and k must be tensors")
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be [B, H, N, d]")
     B, H, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k has shape {tuple(k.shape)}; q is {tuple(q.shape)} (batch and head dim must match)")
+    Hkv = k.shape[1]
+    if (Hkv == 0) != (H == 0) or (Hkv > 0 and H % Hkv != 0):
+        raise ValueError(f"k has {Hkv} heads, which does not divide q's {H}")
     Nk = k.shape[2]
     if q.dtype not in _DTYPE_CODE:
         raise TypeError(f"unsupported dtype {q.dtype}")
@@ -143,28 +180,66 @@ def make_params(q, k, mask=None, causal=False, scale=None) -> tuple:
     p.causal = 1 if causal else 0
     p.scale = float(1.0 / math.sqrt(d) if scale is None else scale)
     p.mask_kind = JVPATTN_MASK_NONE
-    if mask is not None:
-        mask = _as_4d(mask)
-        if mask.dim() != 4:
-            raise ValueError("mask must broadcast to [B, H, Nq, Nk]")
-        if mask.dtype == torch.bool:
-            mask = mask.view(torch.uint8)
+    if mask is None:
+        if mask_kind not in (None, "none"):
+            raise ValueError(f"mask_kind={mask_kind!r} without a mask")
+        return p, None
+    if not isinstance(mask, torch.Tensor):
+        raise TypeError("mask must be a tensor")
+    mask = _as_4d(mask)
+    if mask.dim() != 4:
+        raise ValueError("mask must broadcast to [B, H, Nq, Nk]")
+    if mask.device != q.device:
+        raise ValueError(f"mask is on {mask.device}, q is on {q.device}")
+    if mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    if mask_kind is None:
         if mask.dtype == torch.uint8:
-            p.mask_kind = JVPATTN_MASK_BOOL
-        elif mask.dtype == torch.int32:
-            p.mask_kind = JVPATTN_MASK_BITS   # bit-packed boolean mask (see pack_mask_bits)
+            mask_kind = "bool"
         elif mask.dtype == q.dtype:
-            p.mask_kind = JVPATTN_MASK_ADDITIVE
+            mask_kind = "additive"
+        elif mask.dtype == torch.int32:
+            raise TypeError("an int32 mask is read as bit-packed only with mask_kind='bits' (see pack_mask_bits)")
         else:
-            raise TypeError("an additive mask must have the dtype of q")
-        row = (Nk + 31) // 32 if p.mask_kind == JVPATTN_MASK_BITS else Nk
-        if mask.shape[3] != row or mask.shape[2] not in (1, Nq) or mask.shape[1] not in (1, H) \
-                or mask.shape[0] not in (1, B):
-            raise ValueError(f"mask shape {tuple(mask.shape)} does not broadcast to {(B, H, Nq, Nk)}")
-        if mask.stride(3) != 1:
-            mask = mask.contiguous()
-        p.mask_stride_b, p.mask_stride_h, p.mask_stride_q = _layout(mask)[:3]
+            raise TypeError(f"mask dtype {mask.dtype}: expected bool/uint8, q's dtype {q.dtype}, or int32 words "
+                            f"with mask_kind='bits'")
+    if mask_kind not in MASK_KINDS:
+        raise ValueError(f"unknown mask_kind {mask_kind!r}")
+    want = {"bool": torch.uint8, "additive": q.dtype, "bits": torch.int32}[mask_kind]
+    if mask.dtype != want:
+        raise TypeError(f"a {mask_kind} mask must have dtype {want}, got {mask.dtype}")
+    p.mask_kind = MASK_KINDS[mask_kind]
+    row = (Nk + 31) // 32 if p.mask_kind == JVPATTN_MASK_BITS else Nk
+    if mask.shape[3] != row or mask.shape[2] not in (1, Nq) or mask.shape[1] not in (1, H) \
+            or mask.shape[0] not in (1, B):
+        raise ValueError(f"mask shape {tuple(mask.shape)} does not broadcast to {(B, H, Nq, row)}")
+    if mask.stride(3) != 1:
+        mask = mask.contiguous()
+    p.mask_stride_b, p.mask_stride_h, p.mask_stride_q = _layout(mask)[:3]
     return p, mask
+
+
+def _check_inputs(q, k, v, tq, tk, tv):
+    """q, k, v (and the tangents present) consistent with each other, on q's GPU, contiguous."""
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a tensor")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise ValueError("k must be a [B, Hkv, Nk, d] tensor")
+    dev = q.device
+    _tensor("q", q, q.shape, q.dtype, None)
+    _tensor("k", k, k.shape, q.dtype, dev)
+    _tensor("v", v, k.shape, q.dtype, dev)
+    _tensor("tq", tq, q.shape, q.dtype, dev, optional=True)
+    _tensor("tk", tk, k.shape, q.dtype, dev, optional=True)
+    _tensor("tv", tv, k.shape, q.dtype, dev, optional=True)
+
+
+def _require_gpu(q):
+    """Last check before a launch: the tensors (all on q's device by now) must live on a GPU."""
+    if not q.is_cuda:
+        raise ValueError(f"q must be a GPU tensor (it is on {q.device})")
 
 
 def jvpattn_check_fwd_tmask(params: jvpattn_params, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse) -> int:
@@ -187,38 +262,38 @@ def pack_mask_bits(mask):
 
 
 def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, scale=None,
-                want_tlse=True, out=None, tmask=None):
+                want_tlse=True, out=None, tmask=None, mask_kind=None):
     """O, dO, lse, tlse = jvpattn_fwd(q, k, v, tq, tk, tv, mask, causal, scale).
 
     q, tq: [B,H,Nq,d]; k, v, tk, tv: [B,Hkv,Nk,d] on the GPU, one dtype
     (float32 / float16 / bfloat16), contiguous; Hkv divides H (query head h
     reads key/value head h // (H // Hkv)). Tangents may be None (zero).
-    mask: None, a bool/uint8 tensor (True = attend), a bit-packed boolean
-    mask (int32 words [.., ceil(Nk/32)], ``pack_mask_bits``) or an additive
-    tensor of q's dtype, broadcastable to [B,H,Nq,Nk]. ``tmask``: the tangent of an
-    additive mask, shaped like it (jvpattn_fwd_tmask). Work is queued on
-    torch's current stream. ``out`` optionally supplies (o, to, lse, tlse) buffers.
+    mask: None, a bool/uint8 tensor (True = attend), an additive tensor of q's
+    dtype, or (with ``mask_kind="bits"``) a bit-packed boolean mask of int32
+    words [.., ceil(Nk/32)] (``pack_mask_bits``), broadcastable to
+    [B,H,Nq,Nk]. ``tmask``: the tangent of an additive mask, shaped like it
+    (jvpattn_fwd_tmask). ``out`` optionally supplies (o, to, lse, tlse)
+    buffers (tlse may be None). Every tensor is checked (shape, dtype, device,
+    layout) before anything is queued; work goes on torch's current stream.
     """
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v), ("tq", tq), ("tk", tk), ("tv", tv)):
-        if t is None:
-            continue
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-        if t.dtype != q.dtype:
-            raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
-    p, mask = make_params(q, k, mask, causal, scale)
+    _check_inputs(q, k, v, tq, tk, tv)
+    p, mask = make_params(q, k, mask, causal, scale, mask_kind)
     if tmask is not None:
-        mask, tmask = _tmask_like(tmask, None, p, mask)
+        mask, tmask = _tmask_like(tmask, p, mask)
+    stats = tuple(q.shape[:3])
     if out is None:
         o = torch.empty_like(q)
         to = torch.empty_like(q)
-        lse = torch.empty(q.shape[:3], device=q.device, dtype=torch.float32)
+        lse = torch.empty(stats, device=q.device, dtype=torch.float32)
         tlse = torch.empty_like(lse) if want_tlse else None
     else:
         o, to, lse, tlse = out
+        _tensor("o", o, q.shape, q.dtype, q.device)
+        _tensor("to", to, q.shape, q.dtype, q.device)
+        _tensor("lse", lse, stats, torch.float32, q.device)
+        _tensor("tlse", tlse, stats, torch.float32, q.device, optional=True)
+    _require_gpu(q)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     if tmask is not None:
         rc = lib.jvpattn_fwd_tmask(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
@@ -243,12 +318,16 @@ def jvpattn_check_bwd(params: jvpattn_params, *ptrs, workspace_bytes: int = 0) -
     return load_library().jvpattn_check_bwd(ctypes.byref(params), *ptrs, workspace_bytes)
 
 
-def _tmask_like(tmask, mask_in, p, mask):
+def _tmask_like(tmask, p, mask):
     """tmask laid out as the library-side mask (returns (mask, tmask); may make both contiguous)."""
     if p.mask_kind != JVPATTN_MASK_ADDITIVE:
         raise ValueError("tmask needs an additive mask")
-    if not tmask.is_cuda or tmask.dtype != mask.dtype:
-        raise ValueError("tmask must be a GPU tensor of the mask's dtype")
+    if not isinstance(tmask, torch.Tensor):
+        raise TypeError("tmask must be a tensor")
+    if tmask.dtype != mask.dtype:
+        raise TypeError(f"tmask has dtype {tmask.dtype}, the mask {mask.dtype}")
+    if tmask.device != mask.device:
+        raise ValueError(f"tmask is on {tmask.device}, the mask on {mask.device}")
     tmask = _as_4d(tmask)
     if tuple(tmask.shape) != tuple(mask.shape):
         raise ValueError(f"tmask shape {tuple(tmask.shape)} differs from the mask's {tuple(mask.shape)}")
@@ -260,41 +339,46 @@ def _tmask_like(tmask, mask_in, p, mask):
 
 
 def jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, go, gto, mask=None, causal=False, scale=None,
-                out=None, workspace=None, tmask=None):
+                out=None, workspace=None, tmask=None, mask_kind=None):
     """dq, dk, dv, dtq, dtk, dtv = jvpattn_bwd(...): cotangents of q, k, v, tq, tk, tv.
 
     For L = <go, O> + <gto, dO> with (O, dO, lse, tlse) = jvpattn_fwd(q, k, v, tq, tk, tv, mask, causal,
     scale). Shapes and dtypes as for jvpattn_fwd; go, gto like q, either may be None (zero). ``out``
     optionally supplies the six output tensors (dtq, dtk, dtv may be None: not computed); ``tmask``, the
     additive mask's tangent the forward was taken along (jvpattn_bwd_tmask);
-    ``workspace`` a uint8 device tensor of at least jvpattn_bwd_workspace_bytes bytes. Work is queued
-    on torch's current stream.
+    ``workspace`` a uint8 device tensor of at least jvpattn_bwd_workspace_bytes bytes. Every tensor is
+    checked before anything is queued; work goes on torch's current stream.
     """
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v), ("tq", tq), ("tk", tk), ("tv", tv), ("o", o), ("to", to),
-                    ("go", go), ("gto", gto)):
-        if t is None:
-            continue
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-        if t.dtype != q.dtype:
-            raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
-    p, mask = make_params(q, k, mask, causal, scale)
+    _check_inputs(q, k, v, tq, tk, tv)
+    dev, stats = q.device, tuple(q.shape[:3])
+    _tensor("o", o, q.shape, q.dtype, dev)
+    _tensor("to", to, q.shape, q.dtype, dev)
+    _tensor("lse", lse, stats, torch.float32, dev)
+    _tensor("tlse", tlse, stats, torch.float32, dev)
+    _tensor("go", go, q.shape, q.dtype, dev, optional=True)
+    _tensor("gto", gto, q.shape, q.dtype, dev, optional=True)
+    p, mask = make_params(q, k, mask, causal, scale, mask_kind)
     if tmask is not None:
-        mask, tmask = _tmask_like(tmask, None, p, mask)
+        mask, tmask = _tmask_like(tmask, p, mask)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         dtq, dtk, dtv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv, dtq, dtk, dtv = out
+        for name, t, like, opt in (("dq", dq, q, False), ("dk", dk, k, False), ("dv", dv, k, False),
+                                   ("dtq", dtq, q, True), ("dtk", dtk, k, True), ("dtv", dtv, k, True)):
+            _tensor(name, t, like.shape, q.dtype, dev, optional=opt)
     need = lib.jvpattn_bwd_workspace_bytes(ctypes.byref(p))
     if need < 0:
         raise JvpattnError(int(need), jvpattn_strerror(int(need)))
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or workspace.device != dev
+                                  or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    _require_gpu(q)
     if workspace is None:
-        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
     ws_bytes = workspace.numel() * workspace.element_size()
     if tmask is not None:
         rc = lib.jvpattn_bwd_tmask(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),

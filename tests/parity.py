@@ -79,3 +79,120 @@ def failures(got: dict, ref: dict, dtype: str, spec_spread: bool = False) -> lis
 def assert_parity(got: dict, ref: dict, dtype: str, what: str = "", spec_spread: bool = False):
     bad = failures(got, ref, dtype, spec_spread)
     assert not bad, f"{what}: " + "; ".join(bad)
+
+
+# ---------------------------------------------------------------- reverse pass
+
+BWD_NAMES = ("dq", "dk", "dv", "dtq", "dtk", "dtv")
+# Elements whose term magnitude is below this fraction of the output's largest one are held to
+# that floor instead (a row with no visible key has M = 0 and must come back as exactly 0 there).
+BWD_FLOOR = 2.0 ** -20
+# Absolute rounding error of a value rounded to the working type below its normal range: half the
+# subnormal spacing (float16: normal values start at 2^-14, subnormals are spaced 2^-24). Relative
+# bars cannot cover it -- a float16 weight of 1e-6 carries an error of up to 2^-25, 3% of itself.
+SUBNORMAL_HALF_ULP = {"f16": 2.0 ** -25, "bf16": 2.0 ** -134, "f32": 2.0 ** -150}
+
+
+def bwd_term_magnitudes(q, k, v, tq, tk, tv, go, gto, bias_of, scale, heads=None, tbias_of=None):
+    """Per-element term magnitudes M of the six cotangents (float64 arrays shaped like them).
+
+    M is the reverse pass with every factor replaced by its absolute value, so M >= |ref| element by
+    element, and it exceeds |ref| where terms cancel -- e.g. the score cotangent P (dP - del), whose
+    two parts reach the kernel through different roundings (del from the 16-bit O and dO the forward
+    returned). Rounding any factor of a term to a t-bit mantissa moves that element by at most
+    2^-t times its share of M, which is what a bar rho * M_ij covers.
+
+    q, tq, go, gto: [B, H, Nq, d]; k, v, tk, tv: [B, Hkv, Nk, d] (float64; zero arrays for absent
+    tangents). bias_of(b, h) -> [Nq, Nk] additive bias (0 / -inf / mask values, causal applied);
+    tbias_of(b, h) -> the mask tangent's [Nq, Nk] or None. heads: None for every head, or a list of
+    query heads of batch 0 (then the outputs cover batch 0 and those heads, and the key-side sums
+    cover only them -- callers use it without grouped heads).
+
+    Also returns, under the key "floor", the partner magnitudes of the rounded factors summed over
+    the visible (query, key) pairs that reach each element (A: dq <- scale sum_j (|k_j| + |dk_j|),
+    dk <- scale sum_i (|q_i| + |dq_i|), dv <- sum_i (|gO_i| + |gdO_i|), and likewise for the
+    tangent cotangents): a weight, score cotangent or output below the working type's normal range
+    is off by up to half a subnormal spacing, times that partner.
+    """
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    grp = H // Hkv
+    hl = list(range(H)) if heads is None else list(heads)
+    bl = list(range(B)) if heads is None else [0]
+    nqh = len(hl) if heads is not None else H
+    nkh = len(hl) if heads is not None else Hkv
+    M = {n: np.zeros((len(bl), nqh, Nq, d)) for n in ("dq", "dtq")}
+    M.update({n: np.zeros((len(bl), nkh, Nk, d)) for n in ("dk", "dtk", "dv", "dtv")})
+    F = {n: np.zeros_like(a) for n, a in M.items()}
+    for bi, b in enumerate(bl):
+        for hi, h in enumerate(hl):
+            kh = h // grp
+            ko = hi if heads is not None else kh       # where the key-side sums go
+            qo = hi if heads is not None else h
+            k_, v_, tk_, tv_ = k[b, kh], v[b, kh], tk[b, kh], tv[b, kh]
+            S = scale * q[b, h] @ k_.T + bias_of(b, h)
+            P = np.zeros_like(S)
+            live = ~np.all(np.isneginf(S), axis=1)
+            if live.any():
+                e = np.exp(S[live] - S[live].max(1, keepdims=True))
+                P[live] = e / e.sum(1, keepdims=True)
+            Sd = scale * (tq[b, h] @ k_.T + q[b, h] @ tk_.T)
+            tb = None if tbias_of is None else tbias_of(b, h)
+            if tb is not None:
+                Sd = Sd + tb
+            t = (P * Sd).sum(1, keepdims=True)
+            g, gd = go[b, h], gto[b, h]
+            aG, aGd = np.abs(g), np.abs(gd)
+            aX = aG @ np.abs(v_).T + aGd @ np.abs(tv_).T
+            aD = aGd @ np.abs(v_).T
+            o = P @ v_
+            to = (P * (Sd - t)) @ v_ + P @ tv_
+            r = np.abs((gd * o).sum(1, keepdims=True))
+            dl = np.abs((g * o).sum(1, keepdims=True)) + np.abs((gd * to).sum(1, keepdims=True)) + np.abs(t) * r
+            aS = P * (aX + aD * np.abs(Sd - t) + r * np.abs(Sd) + dl)
+            aSd = P * (aD + r)
+            aK, aTK, aQ, aTQ = np.abs(k_), np.abs(tk_), np.abs(q[b, h]), np.abs(tq[b, h])
+            M["dq"][bi, qo] = scale * (aS @ aK + aSd @ aTK)
+            M["dtq"][bi, qo] = scale * aSd @ aK
+            M["dk"][bi, ko] += scale * (aS.T @ aQ + aSd.T @ aTQ)
+            M["dtk"][bi, ko] += scale * aSd.T @ aQ
+            M["dv"][bi, ko] += P.T @ aG + np.abs(P * (Sd - t)).T @ aGd
+            M["dtv"][bi, ko] += P.T @ aGd
+            vis = np.isfinite(S).astype(np.float64)    # visible (query, key) pairs
+            F["dq"][bi, qo] = scale * vis @ (aK + aTK)
+            F["dtq"][bi, qo] = scale * vis @ aK
+            F["dk"][bi, ko] += scale * vis.T @ (aQ + aTQ)
+            F["dtk"][bi, ko] += scale * vis.T @ aQ
+            F["dv"][bi, ko] += vis.T @ (aG + aGd)
+            F["dtv"][bi, ko] += vis.T @ aGd
+    M["floor"] = F
+    return M
+
+
+def bwd_errors(got: dict, ref: dict, M: dict, dtype: str) -> dict:
+    """Per cotangent: (worst err_ij / bar_ij, index, err, bar there, power) with
+    bar_ij = rho * max(M_ij, BWD_FLOOR * max M) + eta * (floor_ij + 1), eta = SUBNORMAL_HALF_ULP[dtype]
+    (the "+ 1": the output's own rounding). power = True when an all-zero result would fail the bar
+    (some |ref_ij| > bar_ij)."""
+    out = {}
+    for n in BWD_NAMES:
+        g, r, m = np.asarray(got[n], np.float64), np.asarray(ref[n], np.float64), M[n]
+        if r.size == 0:
+            out[n] = (0.0, None, 0.0, 0.0, True)
+            continue
+        if not np.all(np.isfinite(g)):
+            out[n] = (float("inf"), None, float("inf"), 0.0, True)
+            continue
+        bar = RHO[dtype] * np.maximum(m, BWD_FLOOR * float(m.max()))
+        bar = bar + SUBNORMAL_HALF_ULP[dtype] * (M["floor"][n] + 1)
+        ratio = np.abs(g - r) / np.where(bar > 0, bar, np.inf)
+        ratio = np.where((bar == 0) & (g != r), np.inf, ratio)
+        i = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+        power = bool(np.any(np.abs(r) > bar))
+        out[n] = (float(ratio[i]), i, float(abs(g[i] - r[i])), float(bar[i]), power)
+    return out
+
+
+def bwd_failures(got: dict, ref: dict, M: dict, dtype: str) -> list:
+    return [f"{n}: err {e:.3e} > bar {b:.3e} at {i} (worst ratio {q:.2f})"
+            for n, (q, i, e, b, _) in bwd_errors(got, ref, M, dtype).items() if not q <= 1.0]

@@ -3,7 +3,6 @@
 Values must equal the direct library calls bit for bit (the entries only
 marshal), and match the float64 oracle to the parity bars.
 """
-import numpy as np
 import pytest
 import torch
 import torch.autograd.forward_ad as fwAD
@@ -11,9 +10,9 @@ import torch.autograd.forward_ad as fwAD
 from forward_mode_autodiff_amd import inputs as I
 from forward_mode_autodiff_amd.autograd import attention, fwd_dual
 from forward_mode_autodiff_amd.jvpattn import jvpattn_bwd, jvpattn_fwd
-from oracle import oracle_bwd, oracle_fwd
-from tests.parity import assert_parity
-from tests.test_gpu_bwd import NAMES, RHO, term_magnitudes
+from oracle import oracle_fwd
+from tests.bwd_cases import magnitudes, reference
+from tests.parity import BWD_NAMES as NAMES, assert_parity, bwd_errors
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -45,13 +44,12 @@ def test_attention_reverse_mode(causal):
     assert torch.equal(o.detach(), o2)
     for t, r in zip((q, k, v), g[:3]):
         assert torch.equal(t.grad, r)
-    ref = oracle_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), None, None, None, f64(x["do"]),
-                     np.zeros(x["q"].shape), causal=causal)
     xz = dict(x, dto=torch.zeros_like(x["dto"]))
-    M = term_magnitudes(xz, w, (), None)
-    for n, t, r in zip(("dq", "dk", "dv"), (q, k, v), ref[:3]):
-        err = float(np.max(np.abs(t.grad.double().cpu().numpy() - r)))
-        assert err <= RHO["bf16"] * M[n], (n, err, M[n])
+    ref, M = reference(xz, w, ()), magnitudes(xz, w, ())
+    got = dict(ref, dq=f64(q.grad), dk=f64(k.grad), dv=f64(v.grad))
+    for n in ("dq", "dk", "dv"):
+        ratio = bwd_errors(got, ref, M, "bf16")[n][0]
+        assert ratio <= 1.0, (n, ratio)
 
 
 def test_attention_forward_mode_dual_tensors():
@@ -78,11 +76,10 @@ def test_fwd_dual_reverse_mode_is_the_hvp_route(causal):
                          d["dto"], causal=causal)
     for a, b in zip(grads, direct):
         assert torch.equal(a, b)
-    ref = oracle_bwd(*[f64(x[n]) for n in ("q", "k", "v", "tq", "tk", "tv", "do", "dto")], causal=causal)
-    M = term_magnitudes(x, w, ("tq", "tk", "tv"), None)
-    for n, a, r in zip(NAMES, grads, ref):
-        err = float(np.max(np.abs(a.double().cpu().numpy() - r)))
-        assert err <= RHO["bf16"] * M[n], (n, err, M[n])
+    ref, M = reference(x, w), magnitudes(x, w)
+    errs = bwd_errors({n: f64(a) for n, a in zip(NAMES, grads)}, ref, M, "bf16")
+    for n in NAMES:
+        assert errs[n][0] <= 1.0, (n, errs[n])
 
 
 def test_attention_forward_mode_dual_additive_mask():

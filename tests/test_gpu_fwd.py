@@ -559,7 +559,8 @@ def test_bit_packed_masks(w, kernel):
     d = to_dev(x)
     bits = pack_mask_bits(d["mask"])
     a = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=d["mask"], causal=w.causal)
-    b = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=bits, causal=w.causal)
+    b = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=bits, causal=w.causal,
+                    mask_kind="bits")
     torch.cuda.synchronize()
     for u, t in zip(a, b):
         fin = torch.isfinite(u)
@@ -583,7 +584,7 @@ def test_grouped_heads_with_packed_key_padding(kernel):
     x = I.make_inputs(w)
     d = to_dev(x)
     o, to, lse, tlse = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], mask=pack_mask_bits(d["mask"]),
-                                   causal=True)
+                                   mask_kind="bits", causal=True)
     torch.cuda.synchronize()
     got = {"o": o.float().cpu(), "to": to.float().cpu(), "lse": lse.cpu(), "tlse": tlse.cpu()}
     ref = oracle_run(x, "bool", True)
