@@ -27,6 +27,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "jvpattn.h"
@@ -958,4 +959,84 @@ extern "C" int jvpattn_bwd_tmask(const jvpattn_params* p, const void* q, const v
   if (rc != JVPATTN_OK) return rc;
   return bwd_launch(p, sz, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk,
                     dtv, workspace, stream);
+}
+
+// ------------------------------------------------- allocation-free variant
+//
+// jvpattn_bwd_noalloc keeps the four per-row arrays of the workspace in a
+// file-scope device array instead of caller memory: each GPU the library runs
+// on holds its own copy (16 MiB) until the process ends. Host code never uses
+// the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+namespace jvpattn {
+namespace {
+
+constexpr int64_t kScratchRows = int64_t(1) << 20;                 // B * H * Nq at most
+constexpr int64_t kScratchBytes = 4 * kScratchRows * 4;            // four float32 arrays of that many rows
+static_assert(kScratchBytes % 256 == 0, "each array starts on a 256-byte boundary");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+}  // namespace jvpattn
+
+static __device__ __align__(256) unsigned char scratch[jvpattn::kScratchBytes];
+
+namespace jvpattn {
+namespace {
+
+// Device address of `scratch` on device `dev`, looked up on the first call for that device.
+int scratch_of(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return JVPATTN_ERR_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess || !ptr) {
+      g_last_hip_error = static_cast<int>(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return JVPATTN_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return JVPATTN_OK;
+}
+
+}  // namespace
+}  // namespace jvpattn
+
+extern "C" int jvpattn_bwd_noalloc(const jvpattn_params* p, const void* q, const void* k, const void* v,
+                                   const void* tq, const void* tk, const void* tv, const void* mask, const void* o,
+                                   const void* to, const float* lse, const float* tlse, const void* go,
+                                   const void* gto, void* dq, void* dk, void* dv, void* dtq, void* dtk, void* dtv,
+                                   void* stream) {
+  using namespace jvpattn;
+  // The size limit first, before any runtime call.
+  const int64_t need = jvpattn_bwd_workspace_bytes(p);
+  if (need < 0) return static_cast<int>(need);
+  if (need > kScratchBytes) return JVPATTN_ERR_SCRATCH;
+  hipDevice_t dev = 0;
+  const hipError_t e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return JVPATTN_ERR_HIP;
+  }
+  void* ws = nullptr;
+  int rc = scratch_of(static_cast<int>(dev), &ws);
+  if (rc != JVPATTN_OK) return rc;
+  FwdSizes sz;
+  rc = check_bwd(p, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk, dtv, ws,
+                 static_cast<size_t>(kScratchBytes), &sz);
+  if (rc != JVPATTN_OK) return rc;
+  return bwd_launch(p, sz, q, k, v, tq, tk, tv, mask, nullptr, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk,
+                    dtv, ws, stream);
 }

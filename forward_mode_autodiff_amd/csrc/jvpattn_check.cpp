@@ -322,6 +322,7 @@ extern "C" const char* jvpattn_strerror(int code) {
     case JVPATTN_ERR_HIP: return "HIP runtime error on launch";
     case JVPATTN_ERR_WORKSPACE: return "workspace missing, too small, not 256-byte aligned, or overlapping";
     case JVPATTN_ERR_ARG: return "argument outside its documented range";
+    case JVPATTN_ERR_SCRATCH: return "B*H*Nq exceeds the fixed scratch of jvpattn_bwd_noalloc (2^20 rows)";
     default: return "unknown error code";
   }
 }

@@ -22,7 +22,9 @@ ERRORS = {
     0: "JVPATTN_OK", -1: "JVPATTN_ERR_NULL", -2: "JVPATTN_ERR_SHAPE", -3: "JVPATTN_ERR_DTYPE",
     -4: "JVPATTN_ERR_HEADDIM", -5: "JVPATTN_ERR_MASK", -6: "JVPATTN_ERR_ALIGN", -7: "JVPATTN_ERR_SCALE",
     -8: "JVPATTN_ERR_ALIAS", -9: "JVPATTN_ERR_HIP", -10: "JVPATTN_ERR_WORKSPACE", -11: "JVPATTN_ERR_ARG",
+    -12: "JVPATTN_ERR_SCRATCH",
 }
+BWD_NOALLOC_MAX_ROWS = 1 << 20   # JVPATTN_BWD_NOALLOC_MAX_ROWS
 JVPATTN_ALGO_AUTO = -1
 FWD_KERNELS = {"wg4": 0, "pp": 1, "split": 2, "split64": 3}   # jvpattn_fwd_kernel values
 _DTYPE_CODE = {torch.float32: JVPATTN_F32, torch.float16: JVPATTN_F16, torch.bfloat16: JVPATTN_BF16}
@@ -80,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     lib.jvpattn_bwd_tmask.restype = ctypes.c_int
     lib.jvpattn_check_bwd_tmask.argtypes = [P] + [vp] * 21 + [ctypes.c_size_t]
     lib.jvpattn_check_bwd_tmask.restype = ctypes.c_int
+    lib.jvpattn_bwd_noalloc.argtypes = [P] + [vp] * 19 + [vp]
+    lib.jvpattn_bwd_noalloc.restype = ctypes.c_int
     lib.jvpattn_fwd_set_algo.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.jvpattn_fwd_set_algo.restype = ctypes.c_int
     _lib = lib
@@ -98,6 +102,14 @@ def jvpattn_fwd_set_algo(kernel=None, order=None, key_range=None) -> None:
     rc = load_library().jvpattn_fwd_set_algo(k, o, r)
     if rc != 0:
         raise JvpattnError(rc, jvpattn_strerror(rc))
+
+
+def _raise_on(rc: int) -> None:
+    if rc != 0:
+        msg = jvpattn_strerror(rc)
+        if rc == -9:
+            msg += f" (hipError {load_library().jvpattn_last_hip_error()})"
+        raise JvpattnError(rc, msg)
 
 
 def jvpattn_strerror(code: int) -> str:
@@ -339,15 +351,18 @@ def _tmask_like(tmask, p, mask):
 
 
 def jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, go, gto, mask=None, causal=False, scale=None,
-                out=None, workspace=None, tmask=None, mask_kind=None):
+                out=None, workspace=None, tmask=None, mask_kind=None, noalloc=False):
     """dq, dk, dv, dtq, dtk, dtv = jvpattn_bwd(...): cotangents of q, k, v, tq, tk, tv.
 
     For L = <go, O> + <gto, dO> with (O, dO, lse, tlse) = jvpattn_fwd(q, k, v, tq, tk, tv, mask, causal,
     scale). Shapes and dtypes as for jvpattn_fwd; go, gto like q, either may be None (zero). ``out``
     optionally supplies the six output tensors (dtq, dtk, dtv may be None: not computed); ``tmask``, the
     additive mask's tangent the forward was taken along (jvpattn_bwd_tmask);
-    ``workspace`` a uint8 device tensor of at least jvpattn_bwd_workspace_bytes bytes. Every tensor is
-    checked before anything is queued; work goes on torch's current stream.
+    ``workspace`` a uint8 device tensor of at least jvpattn_bwd_workspace_bytes bytes. ``noalloc=True``
+    calls jvpattn_bwd_noalloc instead: the library's own fixed scratch replaces the workspace (no
+    device allocation by the library; B*H*Nq <= BWD_NOALLOC_MAX_ROWS; calls on one GPU must not
+    overlap; no mask tangent). Every tensor is checked before anything is queued; work goes on torch's
+    current stream.
     """
     lib = load_library()
     _check_inputs(q, k, v, tq, tk, tv)
@@ -369,6 +384,16 @@ def jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, go, gto, mask=None, causa
         for name, t, like, opt in (("dq", dq, q, False), ("dk", dk, k, False), ("dv", dv, k, False),
                                    ("dtq", dtq, q, True), ("dtk", dtk, k, True), ("dtv", dtv, k, True)):
             _tensor(name, t, like.shape, q.dtype, dev, optional=opt)
+    if noalloc:
+        if tmask is not None or workspace is not None:
+            raise ValueError("noalloc takes neither a workspace nor a mask tangent")
+        _require_gpu(q)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib.jvpattn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
+                                     _ptr(mask), _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse), _ptr(go), _ptr(gto),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtq), _ptr(dtk), _ptr(dtv), stream)
+        _raise_on(rc)
+        return dq, dk, dv, dtq, dtk, dtv
     need = lib.jvpattn_bwd_workspace_bytes(ctypes.byref(p))
     if need < 0:
         raise JvpattnError(int(need), jvpattn_strerror(int(need)))

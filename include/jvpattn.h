@@ -75,7 +75,8 @@ enum {
   JVPATTN_ERR_ALIAS = -8,    /* an output overlaps an input or another output */
   JVPATTN_ERR_HIP = -9,      /* the HIP runtime reported an error on launch */
   JVPATTN_ERR_WORKSPACE = -10, /* jvpattn_bwd: workspace NULL, too small, misaligned, or overlapping */
-  JVPATTN_ERR_ARG = -11        /* jvpattn_fwd_set_algo: a value outside its documented range */
+  JVPATTN_ERR_ARG = -11,       /* jvpattn_fwd_set_algo: a value outside its documented range */
+  JVPATTN_ERR_SCRATCH = -12    /* jvpattn_bwd_noalloc: B*H*Nq exceeds JVPATTN_BWD_NOALLOC_MAX_ROWS */
 };
 
 typedef struct {
@@ -218,6 +219,34 @@ int jvpattn_bwd(const jvpattn_params* params,
                 void* dtq, void* dtk, void* dtv,
                 void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/* The reverse pass without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Arguments, results and errors are those
+ * of jvpattn_bwd without `workspace` / `workspace_bytes`: the per-row
+ * statistics live instead in a fixed scratch array inside the library, one
+ * per GPU, allocated when the library's code is first loaded on that GPU and
+ * held until the process ends (4 float32 per query row, 16 MiB). Limits and
+ * behaviour:
+ *   - B * H * Nq <= JVPATTN_BWD_NOALLOC_MAX_ROWS, else JVPATTN_ERR_SCRATCH
+ *     (checked before anything else; nothing is queued);
+ *   - the GPU is the one `stream` belongs to (NULL: the current device);
+ *   - every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (each entry this call reads, it writes first): calls
+ *     that may overlap on one GPU -- concurrent streams, other threads --
+ *     race and must be serialised by the caller;
+ *   - no memory is allocated or freed by the call.
+ * Only the forward without a mask tangent (jvpattn_fwd) is differentiated. */
+#define JVPATTN_BWD_NOALLOC_MAX_ROWS (1 << 20)
+int jvpattn_bwd_noalloc(const jvpattn_params* params,
+                        const void* q, const void* k, const void* v,
+                        const void* tq, const void* tk, const void* tv,
+                        const void* mask,
+                        const void* o, const void* to, const float* lse, const float* tlse,
+                        const void* go, const void* gto,
+                        void* dq, void* dk, void* dv,
+                        void* dtq, void* dtk, void* dtv,
+                        void* stream);
 
 /* The reverse pass of the forward taken along a tangent of the additive
  * mask as well (jvpattn_fwd_tmask): the same call as jvpattn_bwd plus

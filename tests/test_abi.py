@@ -23,8 +23,9 @@ def declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["jvpattn_bwd", "jvpattn_bwd_tmask", "jvpattn_bwd_workspace_bytes",
-                                    "jvpattn_check_bwd", "jvpattn_check_bwd_tmask", "jvpattn_check_fwd",
+    assert declared_functions() == ["jvpattn_bwd", "jvpattn_bwd_noalloc", "jvpattn_bwd_tmask",
+                                    "jvpattn_bwd_workspace_bytes", "jvpattn_check_bwd", "jvpattn_check_bwd_tmask",
+                                    "jvpattn_check_fwd",
                                     "jvpattn_check_fwd_tmask", "jvpattn_fwd", "jvpattn_fwd_set_algo",
                                     "jvpattn_fwd_tmask", "jvpattn_last_hip_error", "jvpattn_strerror"]
 
@@ -415,3 +416,16 @@ def test_fwd_set_algo_rejects_out_of_range_values():
     assert lib.jvpattn_fwd_set_algo(-1, -1, -1) == 0
     with pytest.raises(KeyError):
         J.jvpattn_fwd_set_algo(kernel="nope")
+
+
+@needs_lib
+def test_bwd_noalloc_rejects_oversized_problems_before_touching_the_gpu():
+    """More than 2^20 query rows in all: JVPATTN_ERR_SCRATCH, decided before any runtime call."""
+    lib = J.load_library()
+    p = good_params(B=1, H=8, Nq=(1 << 17) + 1, Nk=64)
+    args = [None] * 19 + [None]
+    assert lib.jvpattn_bwd_noalloc(ctypes.byref(p), *args) == -12
+    p = good_params(B=-1)
+    assert lib.jvpattn_bwd_noalloc(ctypes.byref(p), *args) == -2
+    assert lib.jvpattn_bwd_noalloc(None, *args) == -1
+    assert "2^20" in J.jvpattn_strerror(-12)
