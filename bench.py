@@ -42,6 +42,24 @@ def workloads():
     }
 
 
+# Work conventions of the throughput figures, per head: the forward's six products of
+# Nq x Nk x d multiply-adds (S = Q K^T; the score tangent dQ K^T + Q dK^T; P V; (P dS) V; P dV) are
+# 12 Nq Nk d flops; the reverse pass's fifteen are 30 Nq Nk d. Causal work is counted as half.
+FWD_PRODUCTS, BWD_PRODUCTS = 6, 15
+
+
+def fwd_flops(B, H, Nq, Nk, d, causal):
+    """Forward work convention: 12 Nq Nk d flops per head, halved when causal."""
+    f = 2.0 * FWD_PRODUCTS * Nq * Nk * d * B * H
+    return f / 2.0 if causal else f
+
+
+def bwd_flops(B, H, Nq, Nk, d, causal):
+    """Reverse-pass work convention: 30 Nq Nk d flops per head, halved when causal."""
+    f = 2.0 * BWD_PRODUCTS * Nq * Nk * d * B * H
+    return f / 2.0 if causal else f
+
+
 def algorithmic_bytes(w):
     """Bytes a launch must move at least: 6 inputs + 2 outputs + lse/tlse, the mask read once per batch."""
     es = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
@@ -82,7 +100,7 @@ def cpu_baseline_bwd(w, x, budget_s=12.0):
     """Time the float64 reverse-pass oracle on whole heads of the same workload for ~budget_s."""
     from threadpoolctl import threadpool_info
 
-    from oracle import bwd_flop_count, oracle_bwd
+    from oracle import oracle_bwd
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     grp = w.H // w.hkv
     done, t0 = 0, time.perf_counter()
@@ -99,7 +117,7 @@ def cpu_baseline_bwd(w, x, budget_s=12.0):
         done += 1
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": bwd_flop_count(1, done, w.N, w.nk, w.d, w.causal) / dt / 1e12, "unit": "TFLOP/s",
+    return {"value": bwd_flops(1, done, w.N, w.nk, w.d, w.causal) / dt / 1e12, "unit": "TFLOP/s",
             "cores": threads, "kind": "oracle",
             "sample": f"{done} head evaluations (of {len(heads)} heads) of the same workload's reverse pass, "
                       f"float64 numpy, {dt:.1f} s"}
@@ -110,7 +128,7 @@ def cpu_baseline(w, x, budget_s=12.0):
     import numpy as np
     from threadpoolctl import threadpool_info
 
-    from oracle import flop_count, oracle_fwd
+    from oracle import oracle_fwd
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     grp = w.H // w.hkv
     f64 = lambda t: t[b:b + 1, h:h + 1].double().numpy()
@@ -126,7 +144,7 @@ def cpu_baseline(w, x, budget_s=12.0):
                    mask=mask, mask_kind=w.mask_kind, causal=w.causal)
         done += 1
     dt = time.perf_counter() - t0
-    flops = flop_count(1, done, w.N, w.nk, w.d, w.causal)
+    flops = fwd_flops(1, done, w.N, w.nk, w.d, w.causal)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} head evaluations (of {len(heads)} heads) of the same workload, all {w.N} "
@@ -210,9 +228,7 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     avg_launch_ms = total_ms / args.steps
 
-    # the counting conventions only; the oracle's arithmetic is not run here
-    from oracle import bwd_flop_count, flop_count
-    flops = (bwd_flop_count if reverse else flop_count)(w.B, w.H, w.N, w.nk, w.d, w.causal)
+    flops = (bwd_flops if reverse else fwd_flops)(w.B, w.H, w.N, w.nk, w.d, w.causal)
     ms_per_step = total_ms / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12

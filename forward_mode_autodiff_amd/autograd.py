@@ -11,11 +11,14 @@ supplies tensors, the autograd graph and streams.
 ``attention(q, k, v, attn_mask=None, is_causal=False, scale=None)``
     the output O. Reverse mode (``.backward()``, ``torch.autograd.grad``)
     runs jvpattn_bwd with a zero cotangent for the tangent output; forward
-    mode with ``torch.autograd.forward_ad`` dual tensors runs jvpattn_fwd
-    with the tangents -- an additive ``attn_mask`` may be a dual tensor too
-    (jvpattn_fwd_tmask). (``torch.func`` transforms hand the rules tensors
-    without storage, which a library call cannot read: use ``fwd_dual`` for
-    the JVP instead of ``torch.func.jvp``.)
+    mode -- ``torch.autograd.forward_ad`` dual tensors, or ``torch.func.jvp``
+    around a model that calls it (the README's use of ``JVPAttn.fwd_dual``
+    inside ``torch.func.jvp``) -- runs jvpattn_fwd with the tangents; an
+    additive ``attn_mask`` may carry a tangent too (jvpattn_fwd_tmask).
+    Under ``torch.func.jvp`` the tangent output stays differentiable in
+    reverse mode (through jvpattn_bwd), so a loss of (O, dO) can be
+    backpropagated: the HVP route. Other ``torch.func`` transforms (vmap,
+    nested jvp) are not supported and raise.
 
 ``fwd_dual(q, k, v, tq, tk, tv, attn_mask=None, is_causal=False, scale=None, tmask=None)``
     the pair (O, dO) -- the output and its JVP, along the additive mask's
@@ -33,11 +36,39 @@ from __future__ import annotations
 
 import torch
 
+from torch._C import _functorch
+
 from . import jvpattn as J
 
 
 def _c(t):
     return None if t is None else t.contiguous()
+
+
+def _jvp_level(*ts):
+    """The torch.func.jvp level whose wrapped tensors a jvp rule received, or None (forward_ad duals).
+
+    torch.func.jvp runs a custom rule with its primals and tangents wrapped one level deep; the
+    library needs the tensors with storage underneath. Nested or batched transforms are refused.
+    """
+    levels = {_functorch.maybe_get_level(t) for t in ts
+              if isinstance(t, torch.Tensor) and _functorch.is_functorch_wrapped_tensor(t)}
+    if not levels:
+        return None
+    if len(levels) > 1:
+        raise NotImplementedError("attention under nested torch.func transforms is not supported")
+    level = levels.pop()
+    for t in ts:
+        if isinstance(t, torch.Tensor) and _functorch.is_functorch_wrapped_tensor(t):
+            inner = _functorch._unwrap_for_grad(t, level)
+            if _functorch.is_functorch_wrapped_tensor(inner) or inner.data_ptr() == 0 and inner.numel():
+                raise NotImplementedError("attention under torch.func transforms other than one jvp "
+                                          "(vmap, nested jvp) is not supported")
+    return level
+
+
+def _unwrap(t, level):
+    return None if t is None else _functorch._unwrap_for_grad(t, level)
 
 
 class _Const:
@@ -78,10 +109,23 @@ class _Attention(torch.autograd.Function):
         q, k, v = ctx.saved_tensors   # in jvp: the tensors given to save_for_forward
         m = ctx.mask
         # an additive mask's tangent enters the score tangent; a boolean mask has none
-        tm = _c(tmask) if tmask is not None and m is not None and m.dtype != torch.bool else None
-        o, to, lse, tlse = J.jvpattn_fwd(q, k, v, _c(tq), _c(tk), _c(tv), mask=m, causal=ctx.causal,
-                                         scale=ctx.scale, tmask=tm)
-        return to, None, None, None   # lse and the aux outputs are not differentiable
+        if tmask is not None and (m is None or m.dtype == torch.bool):
+            tmask = None
+        level = _jvp_level(q, k, v, tq, tk, tv, m, tmask)
+        if level is None:
+            o, to, lse, tlse = J.jvpattn_fwd(q, k, v, _c(tq), _c(tk), _c(tv), mask=m, causal=ctx.causal,
+                                             scale=ctx.scale, tmask=_c(tmask))
+            return to, None, None, None   # lse and the aux outputs are not differentiable
+        # torch.func.jvp: the same call on the tensors under the wrappers, made through the (O, dO)
+        # function so that the tangent keeps a reverse-mode graph (jvpattn_bwd) below this level
+        u = lambda t: _c(_unwrap(t, level))
+        with torch.enable_grad():
+            _, to, _, _ = _AttentionDual.apply(u(q), u(k), u(v), u(tq), u(tk), u(tv), _Const(_unwrap(m, level)),
+                                               ctx.causal, ctx.scale, _Const(u(tmask)))
+        # the call above already ran through this level's interpreter (its output comes back wrapped)
+        if not (_functorch.is_functorch_wrapped_tensor(to) and _functorch.maybe_get_level(to) == level):
+            to = _functorch._wrap_for_grad(to, level)
+        return to, None, None, None
 
 
 class _AttentionDual(torch.autograd.Function):

@@ -50,6 +50,12 @@ struct BF16 {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
   }
   __device__ static inline float widen(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+  // x times a power of two s, rounded back (exact: bfloat16 has float32's exponent range)
+  __device__ static inline vec8 scale8(vec8 x, float s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = static_cast<__bf16>(static_cast<float>(x[e]) * s);
+    return x;
+  }
   // acc + the two 16-bit values of w
   __device__ static inline float dot2sum(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u),
@@ -72,12 +78,19 @@ struct F16 {
   __device__ static inline float widen(uint16_t x) {
     return static_cast<float>(__builtin_bit_cast(_Float16, x));
   }
+  // x times a power of two s, rounded back: exact unless the product falls below
+  // float16's normal range (2^-14), where it rounds to the subnormal grid (error <= 2^-25)
+  __device__ static inline vec8 scale8(vec8 x, float s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = static_cast<_Float16>(static_cast<float>(x[e]) * s);
+    return x;
+  }
   __device__ static inline float dot2sum(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
   }
   // Weights must be rebased when a lane's 16 weights sum past 2^6, so each
-  // is at most 2^6 and the float16 products with score tangents below 2^10 in
-  // magnitude stay finite.
+  // is at most 2^6 (products with score tangents past float16's range are
+  // caught by f16_range_guard).
   __device__ static inline bool spill(float lane_sum, const float (&)[16]) { return !(lane_sum <= 64.0f); }
 };
 
@@ -376,7 +389,8 @@ struct RowState16 {
 // Step 1: weights e of the block (s is clobbered), l updated; returns true
 // (and alpha for the accumulators) when the reference moved.
 template <typename T>
-__device__ inline bool block_exp16(f32x16& s, RowState16& st, float cx, float (&e)[16], float& alpha) {
+__device__ inline bool block_exp16(f32x16& s, RowState16& st, float cx, float (&e)[16], float& alpha,
+                                   float& lane_sum) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], cx, -st.moff);
 #pragma unroll
@@ -401,14 +415,54 @@ __device__ inline bool block_exp16(f32x16& s, RowState16& st, float cx, float (&
     lt = sum16(e);
   }
   st.l += lt;
+  lane_sum = lt;
   return moved;
 }
 
+// Largest magnitude of 16 values (NaN-propagating).
+__device__ inline float absmax16(const float (&x)[16]) {
+  float m = max3(__builtin_fabsf(x[0]), __builtin_fabsf(x[1]), __builtin_fabsf(x[2]));
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) m = max3(m, __builtin_fabsf(x[r]), __builtin_fabsf(x[r + 1]));
+  return __builtin_elementwise_maximum(m, __builtin_fabsf(x[15]));
+}
+
+// float16 range guard. A weight times its score tangent, rounded to float16,
+// overflows past 65504: with weights kept up to 2^6 (2^4 in the 4-wave
+// kernel) against the running reference, once |dS| reaches 2^10 (2^12).
+// lane_sum * max |dS| over the lane's 16 keys bounds every such product; when
+// a query column's bound (both lane halves) reaches 2^15, its reference rises
+// by the smallest k that brings the bound under 2^14: its weights, l (which
+// already holds this block's weights) and mu (which does not) shrink by 2^-k,
+// moff grows by k, and the returned factor 2^-k (1 for every other column)
+// tells the caller to shrink the column's accumulators, which do not hold this
+// block yet. ds_scale turns sd into dS. A non-finite bound (a non-finite
+// input) moves nothing. The check is uniform over the wave; the rescale is
+// taken only when some column needs it.
+template <typename E>
+__device__ inline float f16_range_guard(E& e, const f32x16& sd, float ds_scale, float lane_sum, float& moff,
+                                        float& l, float& mu) {
+  float a[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) a[r] = sd[r];
+  const float bound = lane_sum * (absmax16(a) * ds_scale);
+  if (!__any(!(bound < 32768.0f))) return 1.0f;
+  const float need = xhalf_max(bound);
+  const float k = (need >= 32768.0f && need <= 3.0e38f) ? ceilf(__builtin_amdgcn_logf(need)) - 14.0f : 0.0f;
+  const float f = __builtin_amdgcn_exp2f(-k);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e[r] *= f;
+  moff += k;
+  l *= f;
+  mu *= f;
+  return f;
+}
+
 // Step 2: pB = e and uB = e dS (dS = sd, times us when SCALED_U) as 16-bit B
-// operands for keys 16kc .. 16kc+15.
-template <typename T, bool SCALED_U>
-__device__ inline void block_pack16(const float (&e)[16], const f32x16& sd, float us,
-                                    typename T::vec8 (&pB)[2], typename T::vec8 (&uB)[2]) {
+// operands for keys 16kc .. 16kc+15. E: any 16-element float container.
+template <typename T, bool SCALED_U, typename E>
+__device__ inline void block_pack16(const E& e, const f32x16& sd, float us, typename T::vec8 (&pB)[2],
+                                    typename T::vec8 (&uB)[2]) {
   uint32_t pw[8], uw[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -424,9 +478,9 @@ __device__ inline void block_pack16(const float (&e)[16], const f32x16& sd, floa
   }
 }
 
-// mu += the 16 rounded products held in uB (the values the value products use).
+// Sum of the 16 rounded products held in uB (the values the value products use).
 template <typename T>
-__device__ inline void block_mu16(const typename T::vec8 (&uB)[2], RowState16& st) {
+__device__ inline float block_mu_part(const typename T::vec8 (&uB)[2]) {
   const uint4 a = __builtin_bit_cast(uint4, uB[0]), b = __builtin_bit_cast(uint4, uB[1]);
   float m0 = T::dot2sum(a.x, 0.0f), m1 = T::dot2sum(b.x, 0.0f);
   m0 = T::dot2sum(a.y, m0);
@@ -435,7 +489,13 @@ __device__ inline void block_mu16(const typename T::vec8 (&uB)[2], RowState16& s
   m1 = T::dot2sum(b.z, m1);
   m0 = T::dot2sum(a.w, m0);
   m1 = T::dot2sum(b.w, m1);
-  st.mu += m0 + m1;
+  return m0 + m1;
+}
+
+// mu += the 16 rounded products held in uB.
+template <typename T>
+__device__ inline void block_mu16(const typename T::vec8 (&uB)[2], RowState16& st) {
+  st.mu += block_mu_part<T>(uB);
 }
 
 }  // namespace

@@ -40,10 +40,12 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   a.scale = p->scale;
   a.inv_scale = 1.0f / p->scale;
   const bool additive = p->mask_kind == JVPATTN_MASK_ADDITIVE;
-  // bfloat16 with a power-of-two scale: the scale is folded into Q and dQ
-  // exactly (bfloat16 has float32's exponent range), scores arrive scaled.
+  // 16-bit types with a power-of-two scale: the scale is folded into Q and dQ
+  // once (exact in bfloat16, which has float32's exponent range; in float16
+  // exact unless a product falls below 2^-14, where it rounds to the subnormal
+  // grid), scores and score tangents arrive scaled.
   int sexp = 0;
-  const bool pow2 = p->dtype == JVPATTN_BF16 && std::frexp(p->scale, &sexp) == 0.5f;
+  const bool pow2 = p->dtype != JVPATTN_F32 && std::frexp(p->scale, &sexp) == 0.5f;
   // Otherwise scores stay raw (q.k) without an additive mask, so scale folds into cx.
   a.cx = (additive || pow2) ? kLog2e : p->scale * kLog2e;
   const float tau = p->dtype == JVPATTN_BF16 ? kTauBF16 : p->dtype == JVPATTN_F16 ? kTauF16 : kTauF32;

@@ -35,6 +35,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "jvpattn.h"
 #include "jvpattn_device.h"
@@ -198,6 +199,18 @@ __device__ inline void exp_block(f32x16& s, f32x16& sd, RowState& st, float cx) 
   st.mu += m0 + m1;
 }
 
+// Weights e = exp(s - m) (into s); their lane sum is added to l and returned.
+__device__ inline float exp_l(f32x16& s, RowState& st, float cx) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], cx, -st.moff));
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = s[r];
+  const float lt = sum16(x);
+  st.l += lt;
+  return lt;
+}
+
 // Online-softmax update for one 32-key block (float32 kernel).
 __device__ inline bool softmax_block(f32x16& s, f32x16& sd, RowState& st, float cx, float thr,
                                      float& alpha) {
@@ -267,7 +280,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   const int64_t qbytes = int64_t(a.Nq) * L::ROW;
 
   // Q and dQ as B operands: lane holds row qi, head-dim entries hlf*D/2 + 8c .. +7.
-  // With POW2 the scale (a power of two) is folded into them: exact in bfloat16.
+  // With POW2 the scale (a power of two) is folded into them (T::scale8).
   vec8 qB[L::NC], tqB[L::NC];
   {
     const Rsrc rq = make_rsrc(qp, qbytes), rtq = make_rsrc(tqp, a.tq ? qbytes : 0);
@@ -277,11 +290,8 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
       qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
       tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
       if constexpr (POW2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qB[c][e] = static_cast<__bf16>(static_cast<float>(qB[c][e]) * a.scale);
-          tqB[c][e] = static_cast<__bf16>(static_cast<float>(tqB[c][e]) * a.scale);
-        }
+        qB[c] = T::scale8(qB[c], a.scale);
+        tqB[c] = T::scale8(tqB[c], a.scale);
       }
     }
   }
@@ -403,28 +413,34 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   // Block weights: s -> e = exp(s - m), sd -> e * dS, packed as 16-bit B operands
   // for keys 16kc .. 16kc+15; l and mu updated.
   auto weights = [&](f32x16& s, f32x16& sd, vec8 (&pB)[2], vec8 (&uB)[2]) {
-    exp_block(s, sd, st, a.cx);
+    const float lsum = exp_l(s, st, a.cx);
+    if constexpr (__is_same(T, F16)) {
+      const float moff0 = st.moff;
+      const float shrink = f16_range_guard(s, sd, POW2 ? 1.0f : a.scale, lsum, st.moff, st.l, st.mu);
+      if (shrink != 1.0f) {
+        st.m += (st.moff - moff0) / a.cx;
+#pragma unroll
+        for (int t = 0; t < L::NT; ++t) {
+          accO[t] *= shrink;
+          accT[t] *= shrink;
+        }
+      }
+    }
+    // the products e dS in float32: mu sums them, then they are rounded for the value products
+    float u[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) u[r] = POW2 ? sd[r] * s[r] : (sd[r] * a.scale) * s[r];
+    st.mu += sum16(u);
+    uint32_t pw[8], uw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pw[i] = T::pack2(s[2 * i], s[2 * i + 1]);
+      uw[i] = T::pack2(u[2 * i], u[2 * i + 1]);
+    }
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      uint4 pw, uw;
-      const float us = POW2 ? 1.0f : a.scale;
-      pw.x = T::pack2(s[8 * kc + 0], s[8 * kc + 1]);
-      pw.y = T::pack2(s[8 * kc + 2], s[8 * kc + 3]);
-      pw.z = T::pack2(s[8 * kc + 4], s[8 * kc + 5]);
-      pw.w = T::pack2(s[8 * kc + 6], s[8 * kc + 7]);
-      if constexpr (POW2) {
-        uw.x = T::pack2(sd[8 * kc + 0], sd[8 * kc + 1]);
-        uw.y = T::pack2(sd[8 * kc + 2], sd[8 * kc + 3]);
-        uw.z = T::pack2(sd[8 * kc + 4], sd[8 * kc + 5]);
-        uw.w = T::pack2(sd[8 * kc + 6], sd[8 * kc + 7]);
-      } else {
-        uw.x = T::pack2(sd[8 * kc + 0] * us, sd[8 * kc + 1] * us);
-        uw.y = T::pack2(sd[8 * kc + 2] * us, sd[8 * kc + 3] * us);
-        uw.z = T::pack2(sd[8 * kc + 4] * us, sd[8 * kc + 5] * us);
-        uw.w = T::pack2(sd[8 * kc + 6] * us, sd[8 * kc + 7] * us);
-      }
-      pB[kc] = __builtin_bit_cast(vec8, pw);
-      uB[kc] = __builtin_bit_cast(vec8, uw);
+      pB[kc] = __builtin_bit_cast(vec8, uint4{pw[4 * kc], pw[4 * kc + 1], pw[4 * kc + 2], pw[4 * kc + 3]});
+      uB[kc] = __builtin_bit_cast(vec8, uint4{uw[4 * kc], uw[4 * kc + 1], uw[4 * kc + 2], uw[4 * kc + 3]});
     }
   };
   // V^T / dV^T operands of the tile at `sb` (transpose reads) and the value
@@ -622,7 +638,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   const float mu = xhalf_sum(st.mu);
   if (qi < a.Nq) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const float tl = POW2 ? mu * inv : mu * a.scale * inv;
+    const float tl = mu * inv;   // mu sums e dS (float32 products)
     uint16_t* op = static_cast<uint16_t*>(a.o) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
     uint16_t* top = static_cast<uint16_t*>(a.to) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
 #pragma unroll
@@ -750,11 +766,8 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
       qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
       tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
       if constexpr (POW2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qB[c][e] = static_cast<__bf16>(static_cast<float>(qB[c][e]) * a.scale);
-          tqB[c][e] = static_cast<__bf16>(static_cast<float>(tqB[c][e]) * a.scale);
-        }
+        qB[c] = T::scale8(qB[c], a.scale);
+        tqB[c] = T::scale8(tqB[c], a.scale);
       }
     }
   }
@@ -871,12 +884,22 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
     mask_apply<T, MASK, POW2>(sn, mk, a.scale);
     mask_tangent<T, MASK>(sdn, mk, POW2 ? 1.0f : a.inv_scale);
     if (needs_keymask(k)) hide_keys<CAUSAL>(sn, a.Nk, qi, kpos(k), hlf);
-    float e[16], alpha;
-    if (block_exp16<T>(sn, st, a.cx, e, alpha)) {
+    float e[16], alpha, lsum;
+    if (block_exp16<T>(sn, st, a.cx, e, alpha, lsum)) {
 #pragma unroll
       for (int t = 0; t < L::NT; ++t) {
         accO[t] *= alpha;
         accT[t] *= alpha;
+      }
+    }
+    if constexpr (__is_same(T, F16)) {
+      const float shrink = f16_range_guard(e, sdn, POW2 ? 1.0f : a.scale, lsum, st.moff, st.l, st.mu);
+      if (shrink != 1.0f) {
+#pragma unroll
+        for (int t = 0; t < L::NT; ++t) {
+          accO[t] *= shrink;
+          accT[t] *= shrink;
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1239,7 +1262,8 @@ hipError_t launch_pp(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipSt
     if (pow2) hipLaunchKernelGGL((fwd16pp_kernel<BF16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
     else hipLaunchKernelGGL((fwd16pp_kernel<BF16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
   } else {
-    hipLaunchKernelGGL((fwd16pp_kernel<F16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+    if (pow2) hipLaunchKernelGGL((fwd16pp_kernel<F16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16pp_kernel<F16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
   }
   return hipGetLastError();
 }
@@ -1270,8 +1294,13 @@ hipError_t launch_typed(int dtype, int d, bool pow2, int split, const FwdArgs& a
       else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, false, 1, 4>), grid, block, 0, stream, args);
     }
   } else if (dtype == JVPATTN_F16) {
-    if (d == 64) launch_d64<F16, MASK, CAUSAL, false>(split, args, grid, stream);
-    else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, false, 1, 4>), grid, block, 0, stream, args);
+    if (pow2) {
+      if (d == 64) launch_d64<F16, MASK, CAUSAL, true>(split, args, grid, stream);
+      else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, true, 1, 4>), grid, block, 0, stream, args);
+    } else {
+      if (d == 64) launch_d64<F16, MASK, CAUSAL, false>(split, args, grid, stream);
+      else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, false, 1, 4>), grid, block, 0, stream, args);
+    }
   } else {
     if (d == 64) {
       hipLaunchKernelGGL((fwd32_kernel<64, MASK, CAUSAL>), grid, block, Tile32<64>::BUF_BYTES, stream, args);

@@ -68,17 +68,6 @@ def _f64(x):
     return None if x is None else np.asarray(x, dtype=np.float64)
 
 
-def flop_count(B, H, Nq, Nk, d, causal):
-    """Work convention for throughput: 12*Nq*Nk*d per head, halved when causal.
-
-    Counting rule fixed for this method's throughput figure; the pages' own
-    TFLOP/s columns ("Full results" tables of the README) are consistent with
-    it for B*H*d near 1024.
-    """
-    f = 12.0 * Nq * Nk * d * B * H
-    return f / 2.0 if causal else f
-
-
 def _head_bias(mask, mask_kind, b, h, nq_rows, Nk, causal, q_pos):
     """Additive bias M for one head: 0 where a key is visible, -inf where not.
 

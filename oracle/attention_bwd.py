@@ -121,8 +121,3 @@ def oracle_bwd(q, k, v, tq, tk, tv, go, gto, mask=None, mask_kind=MASK_NONE, cau
             gtv[b, g] += r[5]
     return gq, gk, gv, gtq, gtk, gtv
 
-
-def bwd_flop_count(B, H, Nq, Nk, d, causal):
-    """Work convention for the backward: 15 products of Nq*Nk*d (30*Nq*Nk*d flops) per head, halved when causal."""
-    f = 30.0 * Nq * Nk * d * B * H
-    return f / 2.0 if causal else f

@@ -2,8 +2,9 @@
 
 ``forward_mode_autodiff_amd.autograd`` only marshals: these tests swap the two
 library entry points for the float64 oracle and check that reverse mode,
-forward mode (torch.func.jvp and forward_ad dual tensors) and reverse mode
-over the dual pair return what the oracle says, in the right places.
+forward mode (forward_ad dual tensors, and torch.func.jvp around a function
+that calls attention()), reverse mode over the dual pair and reverse mode
+through torch.func.jvp return what the oracle says, in the right places.
 """
 import numpy as np
 import pytest
@@ -141,3 +142,42 @@ def test_grouped_kv_heads_route_through():
     ref = oracle_bwd(_np(q), _np(k), _np(v), None, None, None, _np(go), np.zeros(q.shape))
     for t, rr in zip((q, k, v), ref[:3]):
         np.testing.assert_allclose(_np(t.grad), rr, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------ torch.func.jvp (the README's route)
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_torch_func_jvp_gives_the_oracle_jvp(causal):
+    q, k, v, tq, tk, tv, _, _ = inputs(11)
+    o, to = torch.func.jvp(lambda a, b, c: A.attention(a, b, c, is_causal=causal), (q, k, v), (tq, tk, tv))
+    ro, rto, _, _ = oracle_fwd(_np(q), _np(k), _np(v), _np(tq), _np(tk), _np(tv), causal=causal)
+    np.testing.assert_allclose(o.numpy(), ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(to.numpy(), rto, rtol=0, atol=1e-12)
+
+
+def test_torch_func_jvp_with_closed_over_keys_and_an_additive_mask():
+    """Tangent along q only (k, v closed over: their tangents are zero); the mask is a constant."""
+    q, k, v, tq, _, _, _, _ = inputs(12)
+    mask = torch.randn(1, 1, 7, 7, generator=torch.Generator().manual_seed(13), dtype=torch.float64)
+    o, to = torch.func.jvp(lambda a: A.attention(a, k, v, attn_mask=mask), (q,), (tq,))
+    ro, rto, _, _ = oracle_fwd(_np(q), _np(k), _np(v), _np(tq), None, None, mask=_np(mask), mask_kind="additive")
+    np.testing.assert_allclose(o.numpy(), ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(to.numpy(), rto, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_reverse_mode_through_torch_func_jvp(causal):
+    """A loss of (O, dO) from torch.func.jvp, backpropagated to q, k, v: the oracle's reverse pass."""
+    q, k, v, tq, tk, tv, go, gto = inputs(14)
+    qq, kk, vv = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o, to = torch.func.jvp(lambda a, b, c: A.attention(a, b, c, is_causal=causal), (qq, kk, vv), (tq, tk, tv))
+    g = torch.autograd.grad((o * go).sum() + (to * gto).sum(), (qq, kk, vv))
+    ref = oracle_bwd(_np(q), _np(k), _np(v), _np(tq), _np(tk), _np(tv), _np(go), _np(gto), causal=causal)
+    for a, r in zip(g, ref[:3]):
+        np.testing.assert_allclose(a.numpy(), r, rtol=0, atol=1e-12)
+
+
+def test_other_torch_func_transforms_raise():
+    q, k, v, *_ = inputs(15)
+    with pytest.raises(Exception, match="vmap"):
+        torch.func.vmap(lambda a: A.attention(a[None], k, v))(q[0])

@@ -109,3 +109,21 @@ def test_attention_reverse_mode_grouped_kv_heads():
     torch.cuda.synchronize()
     for t, r in zip((q, k, v), g[:3]):
         assert torch.equal(t.grad, r)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_torch_func_jvp_route(causal):
+    """torch.func.jvp around attention(): O and dO equal the direct jvpattn_fwd call bit for bit, and a
+    loss of both backpropagates to the direct jvpattn_bwd call's gradients (the HVP route)."""
+    w, x, d = setup(causal, seed=66)
+    q, k, v = (d[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    o, to = torch.func.jvp(lambda a, b, c: attention(a, b, c, is_causal=causal), (q, k, v),
+                           (d["tq"], d["tk"], d["tv"]))
+    o2, to2, lse2, tlse2 = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], causal=causal)
+    assert torch.equal(o.detach(), o2) and torch.equal(to.detach(), to2)
+    grads = torch.autograd.grad((o.float() * d["do"].float()).sum() + (to.float() * d["dto"].float()).sum(),
+                                (q, k, v))
+    ref, M = reference(x, w), magnitudes(x, w)
+    errs = bwd_errors(dict(ref, dq=f64(grads[0]), dk=f64(grads[1]), dv=f64(grads[2])), ref, M, "bf16")
+    for n in ("dq", "dk", "dv"):
+        assert errs[n][0] <= 1.0, (n, errs[n])

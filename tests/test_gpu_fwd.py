@@ -340,6 +340,22 @@ def test_large_scores(kernel, causal, dtype):
         assert ref["lse"][:, :, 0].max() < -100.0
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("log2_ds", [11, 13])
+def test_f16_large_score_tangents(kernel, causal, log2_ds):
+    """float16 score tangents of |dS| ~ 2^11 and 2^13 (dQ and dK scaled up): a weight times its score
+    tangent, rounded to float16, would pass 65504 with weights kept up to 2^4 .. 2^6; the kernels
+    must lower the weights instead of overflowing, and still match the oracle."""
+    w = I.Workload("f16_big_ds", B=1, H=2, N=300, d=64, dtype="f16", causal=causal, std=1.0, seed=22 + log2_ds)
+    x = I.make_inputs(w)
+    for n in ("tq", "tk"):
+        x[n] = (x[n].float() * 2.0 ** (log2_ds - 1)).to(torch.float16)
+    got, ref = check(w, x=x)
+    ds = 0.125 * (x["tq"].double() @ x["k"].double().transpose(-1, -2) + x["q"].double() @ x["tk"].double().transpose(-1, -2))
+    assert ds.abs().max() > 2.0 ** (log2_ds + 1)
+    assert np.all(np.isfinite(got["to"].numpy()))
+
+
 def test_deterministic(kernel):
     w = I.Workload("det", B=2, H=4, N=300, d=64, dtype="bf16", causal=True, std=1.0, seed=10)
     x = I.make_inputs(w)
