@@ -32,6 +32,12 @@ def workloads():
         "hvp_gqa4": I.HVP_GQA,
         "hvp_keypad": I.HVP_PAD,
         "hvp_full": I.Workload("hvp_full", B=4, H=16, N=2048, d=64, dtype="bf16", causal=False, seed=4),
+        # the HVP shape under structured per-row masks (per-row [B,1,N,N] bool): a sliding window of
+        # 256 keys each side, and 512-key diagonal blocks (packed sequences); non-causal
+        "hvp_window": I.Workload("hvp_window", B=4, H=16, N=2048, d=64, dtype="bf16", seed=9, mask_kind="bool",
+                                 mask_layout="sliding", extra={"window": 256}),
+        "hvp_blockdiag": I.Workload("hvp_blockdiag", B=4, H=16, N=2048, d=64, dtype="bf16", seed=10,
+                                    mask_kind="bool", mask_layout="blockdiag", extra={"block": 512}),
         "seq2048": I.seq(2048, False),
         "seq2048_causal": I.seq(2048, True),
         "seq2048_bf16": I.seq(2048, False, dtype="bf16"),
@@ -68,7 +74,8 @@ def algorithmic_bytes(w):
     mask = 0
     if w.mask_kind != "none":
         mes = 1 if w.mask_kind == "bool" else es
-        rows = w.N if w.mask_layout == "bernoulli" else 1   # key masks: one row shared by all queries
+        # key masks: one row shared by all queries; the others hold one row per query
+        rows = 1 if w.mask_layout in ("pad_right", "pad_left", "window") else w.N
         mask = w.B * w.mask_heads * rows * w.nk * mes
     return w.B * w.H * per_q_head + w.B * w.hkv * per_kv_head + mask
 

@@ -42,6 +42,7 @@ __device__ inline float max3(float a, float b, float c) {
 
 struct BF16 {
   using vec8 = bf16x8;
+  static constexpr uint32_t kNegInf16 = 0xff80u;   // -inf
   __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -68,6 +69,7 @@ struct BF16 {
 
 struct F16 {
   using vec8 = f16x8;
+  static constexpr uint32_t kNegInf16 = 0xfc00u;   // -inf
   __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
@@ -316,6 +318,32 @@ __device__ inline void mask_tangent(f32x16& sd, const MaskVals<MASK>& m, float i
       const uint16_t bits = (r & 1) ? hi16(word) : lo16(word);
       sd[r] = fmaf(T::widen(bits), inv_us, sd[r]);
     }
+  }
+}
+
+// Whether the mask values m (this lane's 16 keys of a 32-key block) leave any
+// key visible: nonzero bool bytes or bits, additive values other than -inf.
+// A block no lane of a wave sees (the mask hides all 32 x 32 entries) adds
+// nothing to that wave's rows, so the wave skips its softmax and value
+// products. Causal and ragged-tail hiding are not looked at (those blocks
+// then just run).
+template <typename T, int MASK>
+__device__ inline bool mask_any_visible(const MaskVals<MASK>& m) {
+  if constexpr (MASK == JVPATTN_MASK_BOOL) {
+    return ((m.w[0] | m.w[1]) | (m.w[2] | m.w[3])) != 0u;
+  } else if constexpr (MASK == JVPATTN_MASK_BITS) {
+    return (m.w & 0x0f0f0f0fu) != 0u;   // this lane's keys sit at bits 8g + e, e < 4
+  } else if constexpr (MASK == JVPATTN_MASK_ADDITIVE || MASK == kMaskAddT) {
+    constexpr uint32_t ninf = T::kNegInf16 | (T::kNegInf16 << 16);
+    uint32_t all = m.w[0].x & m.w[0].y, any = m.w[0].x | m.w[0].y;
+#pragma unroll
+    for (int g = 1; g < 4; ++g) {
+      all &= m.w[g].x & m.w[g].y;
+      any |= m.w[g].x | m.w[g].y;
+    }
+    return !(all == ninf && any == ninf);   // some value differs from -inf
+  } else {
+    return true;
   }
 }
 

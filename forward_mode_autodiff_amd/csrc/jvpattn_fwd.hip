@@ -88,12 +88,24 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   // tiles from HBM. jvpattn_fwd_set_algo can force either order.
   a.head_major = a.n_qblk > 1 && a.BH % 8 == 0 && blocks >= 4 * 512;
   // A mask with row stride 0 is the same for every query row: scan it once per
-  // workgroup and skip the key tiles it hides entirely (unless switched off by
-  // jvpattn_fwd_set_algo: then every tile runs).
-  a.key_range = mask != nullptr && p->mask_stride_q == 0 && g_algo_key_range.load(std::memory_order_relaxed) != 0;
+  // workgroup and skip the key tiles it hides entirely. jvpattn_fwd_set_algo
+  // can switch off both mask early-outs (then every block runs).
+  const bool mask_skips = g_algo_key_range.load(std::memory_order_relaxed) != 0;
+  a.key_range = mask != nullptr && p->mask_stride_q == 0 && mask_skips;
+  // Any mask: a wave skips the softmax and value products of a 32 x 32 block
+  // its mask hides entirely (decided from the mask values it loads anyway).
+  a.skip_hidden = mask_skips ? 1 : 0;
+
   const int order = g_algo_order.load(std::memory_order_relaxed);
   if (order == 0) a.head_major = 0;
   if (order == 1) a.head_major = a.n_qblk > 1 && a.BH % 8 == 0;
+  // A mask with one row per query, on the ping-pong kernel (large grids): each
+  // workgroup finds the key tiles some of its rows can see, scanning from both
+  // ends until it meets a visible key; its Q loads are in flight meanwhile.
+  // The small-grid kernels skip only the blocks a mask hides from a whole
+  // wave: there the scan, one memory round trip before each workgroup's first
+  // tile, costs more than it saves on a dense mask.
+  a.row_range = mask != nullptr && p->mask_stride_q != 0 && mask_skips && pp;
   const dim3 grid(static_cast<unsigned>(blocks));
   hipStream_t s = static_cast<hipStream_t>(stream);
 

@@ -84,19 +84,128 @@ __device__ inline void block_coords(const FwdArgs& a, int& qb, int& bh) {
   }
 }
 
+// Whether query row q (< Nq) of this head sees any key of 32-key tile t under
+// a mask with one row per query (row stride msq). Keys past Nk do not count
+// (their bytes belong to row padding or the next row).
+template <typename T, int MASK, int ES>
+__device__ inline bool row_tile_visible(const FwdArgs& a, Rsrc mr, int q, int t) {
+  const int k0 = 32 * t;
+  const int nk = min(32, a.Nk - k0);   // keys of this tile inside Nk (>= 1)
+  if constexpr (MASK == JVPATTN_MASK_BITS) {
+    uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(mr, (q * int(a.msq) + t) * 4, 0, 0);
+    if (nk < 32) w &= (1u << nk) - 1u;
+    return w != 0u;
+  } else if constexpr (MASK == JVPATTN_MASK_BOOL) {
+    const int base = q * int(a.msq) + k0;
+    uint32_t any = 0u;
+    if (a.mask_vec) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(mr, base + 4 * i, 0, 0);
+        if (4 * i + 4 > nk) w = 4 * i >= nk ? 0u : w & ((1u << (8 * (nk - 4 * i))) - 1u);
+        any |= w;
+      }
+    } else {
+      for (int j = 0; j < nk; ++j) any |= __builtin_amdgcn_raw_buffer_load_b8(mr, base + j, 0, 0);
+    }
+    return any != 0u;
+  } else {   // additive (and its tangent's kind): a key is hidden by -inf
+    const int base = (q * int(a.msq) + k0) * ES;
+    bool vis = false;
+    if constexpr (ES == 2) {
+      if (a.mask_vec) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(mr, base + 4 * i, 0, 0);
+          vis = vis || (2 * i < nk && (w & 0xffffu) != T::kNegInf16) || (2 * i + 1 < nk && (w >> 16) != T::kNegInf16);
+        }
+      } else {
+        for (int j = 0; j < nk; ++j)
+          vis = vis || uint32_t(__builtin_amdgcn_raw_buffer_load_b16(mr, base + 2 * j, 0, 0)) != T::kNegInf16;
+      }
+    } else {
+      for (int j = 0; j < nk; ++j)
+        vis = vis || __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mr, base + 4 * j, 0, 0)) != -INFINITY;
+    }
+    return vis;
+  }
+}
+
+// The key tiles [t_lo, t_hi) within [0, tmax) that hold a key visible to some
+// row q0 .. q0+nrows-1 (< Nq) under a mask with one row per query. The
+// workgroup checks R tiles at a time from each end (both ends together in the
+// first round) and stops at the first visible tile from the front and from
+// the back, so the cost grows with the hidden tiles skipped, and a mask with
+// visible keys near both ends (a dense random mask) costs one round. No
+// visible key: t_lo = t_hi = 0. Every thread takes part; the result is uniform.
+template <typename T, int MASK, int ES>
+__device__ inline void row_tiles(const FwdArgs& a, Rsrc mr, int* red, int q0, int nrows, int tmax, int& t_lo,
+                                 int& t_hi) {
+  constexpr int R = MASK == JVPATTN_MASK_BITS ? 8 : MASK == JVPATTN_MASK_BOOL ? 4 : 2;   // tiles per round
+  const int nthr = int(blockDim.x), tid = int(threadIdx.x);
+  nrows = max(0, min(nrows, a.Nq - q0));
+  const int pairs = R * nrows;   // (row, tile) checks per end per round
+  int lo_base = 0, hi_top = tmax;
+  t_lo = -1;
+  t_hi = -1;
+  while (t_lo < 0 || t_hi < 0) {
+    if (tid == 0) {
+      red[0] = INT32_MAX;
+      red[1] = -1;
+    }
+    __syncthreads();
+    int lo = INT32_MAX, hi = -1;
+    for (int p = tid; p < pairs; p += nthr) {
+      const int r = p % nrows, j = p / nrows;
+      if (t_lo < 0) {
+        const int t = lo_base + j;
+        if (t < tmax && row_tile_visible<T, MASK, ES>(a, mr, q0 + r, t)) lo = min(lo, t);
+      }
+      if (t_hi < 0) {
+        const int t = hi_top - 1 - j;
+        if (t >= 0 && row_tile_visible<T, MASK, ES>(a, mr, q0 + r, t)) hi = max(hi, t);
+      }
+    }
+    if (lo != INT32_MAX) atomicMin(&red[0], lo);
+    if (hi >= 0) atomicMax(&red[1], hi);
+    __syncthreads();
+    const int glo = red[0], ghi = red[1];
+    __syncthreads();
+    if (t_lo < 0) {
+      if (glo != INT32_MAX) t_lo = glo;
+      lo_base += R;
+      if (t_lo < 0 && lo_base >= tmax) t_lo = tmax;   // nothing visible from the front
+    }
+    if (t_hi < 0) {
+      if (ghi >= 0) t_hi = ghi + 1;
+      hi_top -= R;
+      if (t_hi < 0 && hi_top <= 0) t_hi = 0;
+    }
+  }
+  if (t_lo >= t_hi) t_lo = t_hi = 0;
+}
+
 // Tiles of 32 keys [t_lo, t_hi) that hold every key a row of this head may
 // see. With a mask shared by all query rows (row stride 0: a key-padding mask
 // [B,1,1,Nk] or [B,H,1,Nk]) the workgroup scans that one row and the loops
 // start and end at the first and last tile with a visible key, so tiles the
 // mask hides entirely are never loaded or multiplied (a row with no visible
-// key at all gets no tile). Otherwise every tile: [0, ceil(Nk/32)). Every
-// thread of the workgroup takes part; the result is uniform. ES: bytes per
-// mask element (additive masks hide a key with -inf).
+// key at all gets no tile). With one mask row per query (row_range), the
+// range of tiles visible to some row of this workgroup's rows q0 .. q0+nrows-1
+// (row_tiles). Otherwise every tile: [0, ceil(Nk/32)). Every thread of the
+// workgroup takes part; the result is uniform. ES: bytes per mask element
+// (additive masks hide a key with -inf).
 template <typename T, int MASK, int ES>
-__device__ inline void key_tiles(const FwdArgs& a, Rsrc mr, int* red, int& t_lo, int& t_hi) {
+__device__ inline void key_tiles(const FwdArgs& a, Rsrc mr, int* red, int& t_lo, int& t_hi, int q0, int nrows,
+                                 bool causal) {
   t_lo = 0;
   t_hi = (a.Nk + 31) >> 5;
   if constexpr (MASK != JVPATTN_MASK_NONE) {
+    if (a.row_range) {   // one mask row per query: this workgroup's rows, tile by tile from both ends
+      const int tmax = causal ? min(t_hi, (q0 + nrows + 31) >> 5) : t_hi;
+      row_tiles<T, MASK, ES>(a, mr, red, q0, nrows, tmax, t_lo, t_hi);
+      return;
+    }
     if (!a.key_range) return;
     if (threadIdx.x == 0) {
       red[0] = INT32_MAX;
@@ -483,6 +592,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   jm = min(jm, (a.Nk >> 5) - kb);
   jm = max(jm, 1);
 
+  bool hidden = false;   // the mask hides the current block from all of this wave's rows
   // Pipelined iteration k (block k settled in sc; block k+1 needs no key mask).
   auto fast = [&](int k, const char* cur, const char* nxt, char* dma, f32x16& sc, f32x16& sdc, f32x16& sn,
                   f32x16& sdn) {
@@ -500,8 +610,18 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     read_k(nxt, ka, tka);
     read_v(cur, va, tva);
     mma_s(ka, tka, sn, sdn);
-    weights(sc, sdc, pB, uB);
+    // a block the mask hides from all of this wave's rows needs no softmax: its weights are zeros
+    if (MASK != JVPATTN_MASK_NONE && hidden) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        pB[kc] = vec8{};
+        uB[kc] = vec8{};
+      }
+    } else {
+      weights(sc, sdc, pB, uB);
+    }
     mma_v(va, tva, pB, uB);
+    if constexpr (MASK != JVPATTN_MASK_NONE) hidden = a.skip_hidden && !__any(mask_any_visible<T, MASK>(mk1));
     mask_apply<T, MASK, POW2>(sn, mk1, a.scale);
     mask_tangent<T, MASK>(sdn, mk1, inv_us);
     const float bm = block_max(sn);
@@ -535,6 +655,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     scores(stage0, sA, sdA);
     MaskVals<MASK> mk;
     load_mask(mk, kb * 32);
+    if constexpr (MASK != JVPATTN_MASK_NONE) hidden = a.skip_hidden && !__any(mask_any_visible<T, MASK>(mk));
     mask_apply<T, MASK, POW2>(sA, mk, a.scale);
     mask_tangent<T, MASK>(sdA, mk, inv_us);
     rescale(block_max(sA));
@@ -575,15 +696,17 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
       scores(cur, sA, sdA);
       MaskVals<MASK> mk;
       load_mask(mk, (kb + k) * 32);
+      if constexpr (MASK != JVPATTN_MASK_NONE) hidden = a.skip_hidden && !__any(mask_any_visible<T, MASK>(mk));
       mask_apply<T, MASK, POW2>(sA, mk, a.scale);
       mask_tangent<T, MASK>(sdA, mk, inv_us);
       if (needs_keymask(k)) hide_keys<CAUSAL>(sA, a.Nk, qi, (kb + k) * 32, hlf);
       rescale(block_max(sA));
     }
+    ready = false;   // the next block, if any, is settled at the top of the next iteration
+    if (MASK != JVPATTN_MASK_NONE && hidden) continue;
     vec8 pB[2], uB[2];
     weights(sA, sdA, pB, uB);
-    values(cur, pB, uB);
-    ready = false;   // the next block, if any, is settled at the top of the next iteration
+    values(cur, pB, uB);   // the next block, if any, is settled at the top of the next iteration
   }
 
   if constexpr (SPLIT == 2) {
@@ -680,7 +803,7 @@ __global__ __launch_bounds__(64 * WV * SPLIT, (D == 64 && WV == 4) ? 2 : 1) void
     int qb, bh;
     block_coords(a, qb, bh);
     const Rsrc mr = mask_rsrc(a, bh / a.H, bh % a.H, mask_es<MASK>(2), nullptr, MASK == JVPATTN_MASK_BITS);
-    key_tiles<T, MASK, 2>(a, mr, kred, t_lo, t_hi);
+    key_tiles<T, MASK, 2>(a, mr, kred, t_lo, t_hi, qb * 32 * WV, 32 * WV, CAUSAL);
   }
   if constexpr (SPLIT == 1) {
     fwd16_body<T, D, MASK, CAUSAL, POW2, 1, 0, WV>(a, t_lo, t_hi, s0, s1, s2, s3, nullptr, nullptr, nullptr,
@@ -787,7 +910,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   };
   __shared__ int kred[2];
   int t0, t_hi;   // key tiles [t0, t_hi) may hold visible keys; loop tile k is absolute tile t0 + k
-  key_tiles<T, MASK, 2>(a, mr, kred, t0, t_hi);
+  key_tiles<T, MASK, 2>(a, mr, kred, t0, t_hi, q0, kPPBM, CAUSAL);
 
   const int kv_end = min(CAUSAL ? min(a.Nk, q0 + kPPBM) : a.Nk, 32 * t_hi);
   const int n_tiles = max(0, (kv_end + L::BN - 1) / L::BN - t0);
@@ -881,6 +1004,18 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   // Scores of block k (in sn): mask, then weights into pB / uB. The V / dV
   // operands of block k (stage stv) are read while the weights are packed.
   auto settle = [&](int k, const char* stv) {
+    // a block the mask hides from all of this wave's rows needs no softmax: its weights are zeros
+    // (the value products then add nothing)
+    if (MASK != JVPATTN_MASK_NONE && a.skip_hidden && !__any(mask_any_visible<T, MASK>(mk))) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_v(stv);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        pB[kc] = vec8{};
+        uB[kc] = vec8{};
+      }
+      return;
+    }
     mask_apply<T, MASK, POW2>(sn, mk, a.scale);
     mask_tangent<T, MASK>(sdn, mk, POW2 ? 1.0f : a.inv_scale);
     if (needs_keymask(k)) hide_keys<CAUSAL>(sn, a.Nk, qi, kpos(k), hlf);
@@ -1122,7 +1257,7 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
   const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 4, a.tmask) : mr;
   __shared__ int kred[2];
   int t0, t_hi;   // key tiles [t0, t_hi) may hold visible keys
-  key_tiles<F16, MASK, 4>(a, mr, kred, t0, t_hi);
+  key_tiles<F16, MASK, 4>(a, mr, kred, t0, t_hi, q0, kBM, CAUSAL);
 
   const int kv_end = min(CAUSAL ? min(a.Nk, q0 + kBM) : a.Nk, 32 * t_hi);
   const int n_tiles = max(0, (kv_end + L::BN - 1) / L::BN - t0);

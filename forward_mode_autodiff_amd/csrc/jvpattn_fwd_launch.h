@@ -45,6 +45,8 @@ struct FwdArgs {
   int xgrp;           // grp when whole key/value groups can be kept on one XCD, else 1
   int head_major;     // 1: the query blocks of a head run back to back on one XCD (large grids)
   int key_range;      // 1: the mask is shared by all query rows; skip 32-key tiles it hides entirely
+  int skip_hidden;    // 1: a wave skips the softmax and value products of a block its mask hides entirely
+  int row_range;      // 1: one mask row per query; run only the key tiles visible to some row of the workgroup
   int n_qblk;
   int mask_vec;       // 1: mask rows may be read 4 keys at a time
   int64_t msb, msh, msq;

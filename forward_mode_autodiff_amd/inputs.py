@@ -40,9 +40,13 @@ class Workload:
     keep: float = 0.9              # Bernoulli keep rate of the boolean mask
     Hkv: int | None = None         # key/value heads (None -> H; fewer = grouped-query attention)
     # Mask layout: "bernoulli" (independent keep draws per element, diagonal
-    # kept) or a key mask shared by all query rows ([B, mask_heads, 1, Nk]):
+    # kept); a key mask shared by all query rows ([B, mask_heads, 1, Nk]):
     # "pad_right" (keys below a drawn length visible), "pad_left" (the last
-    # drawn-length keys visible), "window" (a drawn contiguous key range).
+    # drawn-length keys visible), "window" (a drawn contiguous key range); or
+    # a structured mask per query row ([B, mask_heads, N, Nk]): "sliding"
+    # (key j visible to query i iff |i - j| < extra["window"]) and
+    # "blockdiag" (iff i // extra["block"] == j // extra["block"], packed
+    # sequences).
     mask_layout: str = "bernoulli"
     extra: dict = field(default_factory=dict, compare=False)
 
@@ -129,7 +133,20 @@ def make_inputs(w: Workload, cotangents: bool = False) -> dict:
     mask = None
     if w.mask_kind not in ("none", "bool", "additive"):
         raise ValueError(f"unknown mask kind {w.mask_kind!r}")
-    if w.mask_kind != "none" and w.mask_layout != "bernoulli":
+    if w.mask_kind != "none" and w.mask_layout in ("sliding", "blockdiag"):
+        i = torch.arange(w.N)[:, None]
+        j = torch.arange(w.nk)[None, :]
+        if w.mask_layout == "sliding":
+            keep = (i - j).abs() < int(w.extra["window"])
+        else:
+            keep = (i // int(w.extra["block"])) == (j // int(w.extra["block"]))
+        keep = keep.expand(w.B, w.mask_heads, w.N, w.nk)
+        if w.mask_kind == "bool":
+            mask = keep.to(torch.uint8).contiguous()
+        else:
+            vals = torch.randn(keep.shape, generator=g, dtype=torch.float32)
+            mask = torch.where(keep, vals, torch.full_like(vals, -math.inf)).to(dt)
+    elif w.mask_kind != "none" and w.mask_layout != "bernoulli":
         keep = key_mask(w, g)
         if w.mask_kind == "bool":
             mask = keep.to(torch.uint8)

@@ -94,7 +94,8 @@ def jvpattn_fwd_set_algo(kernel=None, order=None, key_range=None) -> None:
     """Force the forward's launch plan process-wide (None = the library's choice).
 
     kernel: "wg4" | "pp" | "split" | "split64"; order: "qb" (heaviest query blocks first) | "head"
-    (head-major per XCD); key_range: False = never skip key tiles outside a shared mask row's range.
+    (head-major per XCD); key_range: False = no mask early-outs (neither the key range of a mask
+    shared by all rows nor the blocks a mask hides from a whole wave are skipped).
     """
     k = JVPATTN_ALGO_AUTO if kernel is None else FWD_KERNELS[kernel]
     o = JVPATTN_ALGO_AUTO if order is None else {"qb": 0, "head": 1}[order]

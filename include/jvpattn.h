@@ -301,8 +301,10 @@ typedef enum {
  *               kernel (float32 always runs its own kernel);
  *   order     : 0 = heaviest query blocks first over all heads, 1 = the query
  *               blocks of each head back to back on one XCD;
- *   key_range : 0 = never scan a mask shared by all query rows for its
- *               visible key range (every key tile runs); 1 = automatic.
+ *   key_range : 0 = no mask early-outs: neither the scan of a mask shared by
+ *               all query rows for its visible key range, nor the skip of
+ *               32 x 32 blocks a mask hides from all 32 rows of a wave
+ *               (every block runs); 1 = automatic.
  * Returns JVPATTN_OK, or JVPATTN_ERR_ARG (nothing changed) for a value out of
  * range. Not meant to be changed while another thread launches forwards. */
 int jvpattn_fwd_set_algo(int kernel, int order, int key_range);
