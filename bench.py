@@ -44,6 +44,11 @@ def workloads():
         "masked_bool": I.MASKED_BOOL,
         "masked_additive": I.MASKED_ADD,
         "wide": I.WIDE,
+        # the HVP shape at the other head dimensions (d = 32 and 96 run padded d = 64 / 128 kernels)
+        "hvp_d32": I.Workload("hvp_d32", B=4, H=16, N=2048, d=32, dtype="bf16", causal=True, seed=11),
+        "hvp_d96": I.Workload("hvp_d96", B=4, H=16, N=2048, d=96, dtype="bf16", causal=True, seed=12),
+        "hvp_d128": I.Workload("hvp_d128", B=4, H=16, N=2048, d=128, dtype="bf16", causal=True, seed=13),
+        "hvp_d256": I.Workload("hvp_d256", B=4, H=16, N=2048, d=256, dtype="bf16", causal=True, seed=14),
         "tiny": I.TINY,
     }
 

@@ -40,9 +40,13 @@ def hipcc() -> str:
 
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
-# Device code: gfx950 only; packed fp32 instructions disabled.
+# Device code: gfx950 only; packed fp32 instructions disabled. The matrix
+# products take their accumulators in VGPRs where the register budget allows
+# (amdgpu-mfma-vgpr-form): the loop-carried accumulators of the d = 128 and
+# d = 256 kernels then stop bouncing between AGPRs and VGPRs and no longer
+# spill; the d = 64 ping-pong kernel's code is unchanged by it.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-munsafe-fp-atomics"]
 
 
 def _compile(job, verbose: bool) -> str:

@@ -68,9 +68,12 @@ int check_fwd(const jvpattn_params* p, const void* q, const void* k, const void*
   // every grid dimension the launcher forms must stay within int32
   if (bh > INT32_MAX) return JVPATTN_ERR_SHAPE;
 
-  if (p->d != 64 && p->d != 128) return JVPATTN_ERR_HEADDIM;
-  // One head of q/k (plus a partial tile of slack) must be addressable with 31-bit byte offsets.
-  const int64_t kHeadLimit = (int64_t(1) << 31) - 1;
+  if (p->d != 32 && p->d != 64 && p->d != 96 && p->d != 128 && p->d != 256) return JVPATTN_ERR_HEADDIM;
+  if (p->d == 256 && p->dtype == JVPATTN_F32) return JVPATTN_ERR_HEADDIM;   // 16-bit types only
+  // One head of q/k (plus a partial tile of slack) must be addressable with 31-bit byte offsets,
+  // and stay below the offset the kernels use to read zeros past a head's end (0x7ffffff0:
+  // the padding columns of d = 32 and 96).
+  const int64_t kHeadLimit = (int64_t(1) << 31) - 256;
   if ((int64_t(p->Nq) + 256) * p->d * es > kHeadLimit || (int64_t(p->Nk) + 256) * p->d * es > kHeadLimit)
     return JVPATTN_ERR_SHAPE;
   if (!std::isfinite(p->scale) || !(p->scale > 0.0f)) return JVPATTN_ERR_SCALE;
@@ -314,7 +317,7 @@ extern "C" const char* jvpattn_strerror(int code) {
     case JVPATTN_ERR_SHAPE:
       return "invalid shape (negative size, d <= 0, Hkv not a divisor of H, or size overflow)";
     case JVPATTN_ERR_DTYPE: return "unknown dtype";
-    case JVPATTN_ERR_HEADDIM: return "unsupported head dimension (supported: 64, 128)";
+    case JVPATTN_ERR_HEADDIM: return "unsupported head dimension (forward: 32, 64, 96, 128, and 256 for 16-bit types; reverse pass: 64)";
     case JVPATTN_ERR_MASK: return "invalid mask (unknown kind, pointer/kind mismatch, or bad strides)";
     case JVPATTN_ERR_ALIGN: return "misaligned pointer (tensors: 16 bytes, lse/tlse: 4 bytes)";
     case JVPATTN_ERR_SCALE: return "scale must be finite and > 0";

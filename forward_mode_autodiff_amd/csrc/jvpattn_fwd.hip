@@ -33,6 +33,12 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   a.q = q; a.k = k; a.v = v; a.tq = tq; a.tk = tk; a.tv = tv; a.mask = mask; a.tmask = tmask;
   a.o = o; a.to = to; a.lse = lse; a.tlse = tlse;
   a.H = p->H; a.Nq = p->Nq; a.Nk = p->Nk; a.BH = p->B * p->H;
+  // Head dimensions run on kernels built for 64, 128 or 256 columns; d = 32
+  // and 96 run zero-padded to the next one (the padding reads as zeros, is
+  // never stored, and adds nothing to any product).
+  const int dphys = p->d <= 64 ? 64 : p->d <= 128 ? 128 : 256;
+  a.dh = p->d;
+  a.grow = p->d * elem_bytes(p->dtype);
   a.grp = sz.group;
   a.xgrp = (sz.group > 1 && a.BH % (8 * sz.group) == 0) ? sz.group : 1;
   a.n_qblk = (p->Nq + kBM - 1) / kBM;
@@ -67,7 +73,7 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   // even out the triangle. Other types and d: the 4-wave kernel (float32: its
   // own). jvpattn_fwd_set_algo can force a family.
   const int64_t n64 = (p->Nq + 63) / 64, n128 = (p->Nq + kBM - 1) / kBM, n256 = (p->Nq + kPPBM - 1) / kPPBM;
-  const bool d64_16 = p->d == 64 && p->dtype != JVPATTN_F32;
+  const bool d64_16 = dphys == 64 && p->dtype != JVPATTN_F32;
   bool pp = d64_16 && n256 * a.BH >= 256;
   const int64_t small = p->causal ? 512 : 256;
   int split = !d64_16 || pp ? 0 : n128 * a.BH < small ? 2 : n128 * a.BH < 512 ? 1 : 0;
@@ -79,7 +85,8 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
     case JVPATTN_FWD_SPLIT64: pp = false, split = d64_16 ? 2 : 0; break;
     default: break;
   }
-  a.n_qblk = static_cast<int>(pp ? n256 : split == 2 ? n64 : n128);
+  // d = 256 runs its own kernel on 64-row blocks
+  a.n_qblk = static_cast<int>(dphys == 256 ? n64 : pp ? n256 : split == 2 ? n64 : n128);
   const int64_t blocks = int64_t(a.n_qblk) * a.BH;
   if (blocks > INT32_MAX) return JVPATTN_ERR_SHAPE;
   // Head-major order once the grid is several times what the chip holds at
@@ -116,24 +123,24 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   hipError_t e;
   switch (mk) {
     case JVPATTN_MASK_NONE:
-      e = c ? launch_fwd<JVPATTN_MASK_NONE, true>(kernel, p->dtype, p->d, pow2, a, grid, s)
-            : launch_fwd<JVPATTN_MASK_NONE, false>(kernel, p->dtype, p->d, pow2, a, grid, s);
+      e = c ? launch_fwd<JVPATTN_MASK_NONE, true>(kernel, p->dtype, dphys, pow2, a, grid, s)
+            : launch_fwd<JVPATTN_MASK_NONE, false>(kernel, p->dtype, dphys, pow2, a, grid, s);
       break;
     case JVPATTN_MASK_BOOL:
-      e = c ? launch_fwd<JVPATTN_MASK_BOOL, true>(kernel, p->dtype, p->d, pow2, a, grid, s)
-            : launch_fwd<JVPATTN_MASK_BOOL, false>(kernel, p->dtype, p->d, pow2, a, grid, s);
+      e = c ? launch_fwd<JVPATTN_MASK_BOOL, true>(kernel, p->dtype, dphys, pow2, a, grid, s)
+            : launch_fwd<JVPATTN_MASK_BOOL, false>(kernel, p->dtype, dphys, pow2, a, grid, s);
       break;
     case JVPATTN_MASK_BITS:
-      e = c ? launch_fwd<JVPATTN_MASK_BITS, true>(kernel, p->dtype, p->d, pow2, a, grid, s)
-            : launch_fwd<JVPATTN_MASK_BITS, false>(kernel, p->dtype, p->d, pow2, a, grid, s);
+      e = c ? launch_fwd<JVPATTN_MASK_BITS, true>(kernel, p->dtype, dphys, pow2, a, grid, s)
+            : launch_fwd<JVPATTN_MASK_BITS, false>(kernel, p->dtype, dphys, pow2, a, grid, s);
       break;
     case JVPATTN_MASK_ADDITIVE:
-      e = c ? launch_fwd<JVPATTN_MASK_ADDITIVE, true>(kernel, p->dtype, p->d, pow2, a, grid, s)
-            : launch_fwd<JVPATTN_MASK_ADDITIVE, false>(kernel, p->dtype, p->d, pow2, a, grid, s);
+      e = c ? launch_fwd<JVPATTN_MASK_ADDITIVE, true>(kernel, p->dtype, dphys, pow2, a, grid, s)
+            : launch_fwd<JVPATTN_MASK_ADDITIVE, false>(kernel, p->dtype, dphys, pow2, a, grid, s);
       break;
     default:
-      e = c ? launch_fwd<kMaskAddT, true>(kernel, p->dtype, p->d, pow2, a, grid, s)
-            : launch_fwd<kMaskAddT, false>(kernel, p->dtype, p->d, pow2, a, grid, s);
+      e = c ? launch_fwd<kMaskAddT, true>(kernel, p->dtype, dphys, pow2, a, grid, s)
+            : launch_fwd<kMaskAddT, false>(kernel, p->dtype, dphys, pow2, a, grid, s);
       break;
   }
   if (e != hipSuccess) {

@@ -44,6 +44,9 @@
 namespace jvpattn {
 namespace {
 
+// A buffer offset past every record (one head is at most 2 GiB - 256 rows): loads read zeros.
+constexpr int kOutOfRange = 0x7ffffff0;
+
 constexpr int kWaves = 4;             // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;      // query rows per workgroup
@@ -378,15 +381,17 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   const int qi = qw0 + c32;
   const bool wave_live = qw0 < a.Nq;
 
-  const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;   // byte offsets of this head
-  const int64_t khead = int64_t(bh / a.grp) * a.Nk * L::ROW;   // the key/value head it reads
+  // Global rows hold a.dh <= D logical columns (a.grow bytes); the kernel works on D columns, the
+  // ones past a.dh read as zeros (an out-of-range buffer offset) and are never stored.
+  const int64_t qhead = int64_t(bh) * a.Nq * a.grow;   // byte offsets of this head
+  const int64_t khead = int64_t(bh / a.grp) * a.Nk * a.grow;   // the key/value head it reads
   const char* qp = static_cast<const char*>(a.q) + qhead;
   const char* kp = static_cast<const char*>(a.k) + khead;
   const char* vp = static_cast<const char*>(a.v) + khead;
   const char* tqp = a.tq ? static_cast<const char*>(a.tq) + qhead : qp;
   const char* tkp = a.tk ? static_cast<const char*>(a.tk) + khead : kp;
   const char* tvp = a.tv ? static_cast<const char*>(a.tv) + khead : vp;
-  const int64_t qbytes = int64_t(a.Nq) * L::ROW;
+  const int64_t qbytes = int64_t(a.Nq) * a.grow;
 
   // Q and dQ as B operands: lane holds row qi, head-dim entries hlf*D/2 + 8c .. +7.
   // With POW2 the scale (a power of two) is folded into them (T::scale8).
@@ -395,7 +400,8 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     const Rsrc rq = make_rsrc(qp, qbytes), rtq = make_rsrc(tqp, a.tq ? qbytes : 0);
 #pragma unroll
     for (int c = 0; c < L::NC; ++c) {
-      const int off = qi * L::ROW + (hlf * (D / 2) + 8 * c) * 2;
+      const int col = hlf * (D / 2) + 8 * c;
+      const int off = col < a.dh ? qi * a.grow + col * 2 : kOutOfRange;
       qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
       tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
       if constexpr (POW2) {
@@ -437,23 +443,25 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     return (CAUSAL && (kb + k) * 32 + 31 > qw0) || ((kb + k) * 32 + 32 > a.Nk);
   };
 
-  // Direct-load slots of this thread (byte offset inside a tile, same for all four tensors).
+  // Direct-load slots of this thread: global byte offset inside a 32-key tile (same for all four
+  // tensors; kOutOfRange for granules past the logical columns), slot p of the LDS tile.
   int dl_off[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int p = i * GT + tid;
-    const int row = p / L::GR, pg = p % L::GR;
-    dl_off[i] = row * L::ROW + ((pg ^ swz(row)) << 4);
+    const int row = p / L::GR, pg = p % L::GR, lg = pg ^ swz(row);
+    dl_off[i] = lg < (a.dh >> 3) ? row * a.grow + (lg << 4) : kOutOfRange;
   }
+  const int tile_g = L::BN * a.grow;   // global bytes of one 32-key tile
   // One buffer resource per tensor for the whole head: offsets past Nk rows
   // (ragged tail) or into an absent tangent (0-byte resource) read as zeros.
-  const int64_t kbytes = int64_t(a.Nk) * L::ROW;
+  const int64_t kbytes = int64_t(a.Nk) * a.grow;
   const Rsrc rk = make_rsrc(kp, kbytes), rv = make_rsrc(vp, kbytes);
   const Rsrc rtk = make_rsrc(tkp, a.tk ? kbytes : 0), rtv = make_rsrc(tvp, a.tv ? kbytes : 0);
   auto issue_tile = [&](int j, char* stage) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int off = (kb + j) * L::TENSOR_BYTES + dl_off[i];
+      const int off = dl_off[i] == kOutOfRange ? kOutOfRange : (kb + j) * tile_g + dl_off[i];
       const int slot = (i * GT + wave * 64) * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
                                                16, off, 0, 0, 0);
@@ -509,15 +517,25 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     read_k(sb, ka, tka);
     mma_s(ka, tka, s, sd);
   };
-  auto rescale = [&](float bm) {
-    float alpha;
-    if (update_max(bm, st, a.cx, a.thr, alpha)) {
+  // At d = 128 the scaling goes tile by tile, each under its own opaque copy
+  // of the flag: scaled in one block, all 128 accumulator registers would be
+  // copied out of the AGPRs at once and the kernel would spill.
+  auto rescale_acc = [&](bool rs, float alpha) {   // rs: uniform over the wave; alpha: per lane
 #pragma unroll
-      for (int t = 0; t < L::NT; ++t) {
+    for (int t = 0; t < L::NT; ++t) {
+      int rst = __builtin_amdgcn_readfirstlane(static_cast<int>(rs));
+      if constexpr (D > 64) asm volatile("" : "+s"(rst));
+      if (rst) {
         accO[t] *= alpha;
         accT[t] *= alpha;
       }
     }
+  };
+  auto rescale = [&](float bm) {
+    float alpha;
+    const bool rs = update_max(bm, st, a.cx, a.thr, alpha);
+    if constexpr (D > 64) rescale_acc(rs, alpha);
+    else if (rs) rescale_acc(true, alpha);
   };
   // Block weights: s -> e = exp(s - m), sd -> e * dS, packed as 16-bit B operands
   // for keys 16kc .. 16kc+15; l and mu updated.
@@ -526,14 +544,9 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     if constexpr (__is_same(T, F16)) {
       const float moff0 = st.moff;
       const float shrink = f16_range_guard(s, sd, POW2 ? 1.0f : a.scale, lsum, st.moff, st.l, st.mu);
-      if (shrink != 1.0f) {
-        st.m += (st.moff - moff0) / a.cx;
-#pragma unroll
-        for (int t = 0; t < L::NT; ++t) {
-          accO[t] *= shrink;
-          accT[t] *= shrink;
-        }
-      }
+      if (shrink != 1.0f) st.m += (st.moff - moff0) / a.cx;
+      if constexpr (D > 64) rescale_acc(__any(shrink != 1.0f), shrink);   // shrink is 1 on the other lanes
+      else if (shrink != 1.0f) rescale_acc(true, shrink);
     }
     // the products e dS in float32: mu sums them, then they are rounded for the value products
     float u[16];
@@ -762,8 +775,8 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   if (qi < a.Nq) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const float tl = mu * inv;   // mu sums e dS (float32 products)
-    uint16_t* op = static_cast<uint16_t*>(a.o) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
-    uint16_t* top = static_cast<uint16_t*>(a.to) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
+    uint16_t* op = static_cast<uint16_t*>(a.o) + (int64_t(bh) * a.Nq + qi) * a.dh;
+    uint16_t* top = static_cast<uint16_t*>(a.to) + (int64_t(bh) * a.Nq + qi) * a.dh;
 #pragma unroll
     for (int t = 0; t < L::NT; ++t) {
 #pragma unroll
@@ -775,8 +788,10 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
           dv[e] = accT[t][4 * g + e] * inv - tl * ov[e];
         }
         const int dd = 32 * t + 8 * g + 4 * hlf;
-        *reinterpret_cast<uint2*>(op + dd) = uint2{T::pack2(ov[0], ov[1]), T::pack2(ov[2], ov[3])};
-        *reinterpret_cast<uint2*>(top + dd) = uint2{T::pack2(dv[0], dv[1]), T::pack2(dv[2], dv[3])};
+        if (dd < a.dh) {
+          *reinterpret_cast<uint2*>(op + dd) = uint2{T::pack2(ov[0], ov[1]), T::pack2(ov[2], ov[3])};
+          *reinterpret_cast<uint2*>(top + dd) = uint2{T::pack2(dv[0], dv[1]), T::pack2(dv[2], dv[3])};
+        }
       }
     }
     if (hlf == 0) {
@@ -870,22 +885,23 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   const int qi = qw0 + c32;
   const bool wave_live = qw0 < a.Nq;
 
-  const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
-  const int64_t khead = int64_t(bh / a.grp) * a.Nk * L::ROW;   // the key/value head it reads
+  const int64_t qhead = int64_t(bh) * a.Nq * a.grow;   // global rows: a.dh columns (see fwd16_body)
+  const int64_t khead = int64_t(bh / a.grp) * a.Nk * a.grow;   // the key/value head it reads
   const char* qp = static_cast<const char*>(a.q) + qhead;
   const char* kp = static_cast<const char*>(a.k) + khead;
   const char* vp = static_cast<const char*>(a.v) + khead;
   const char* tqp = a.tq ? static_cast<const char*>(a.tq) + qhead : qp;
   const char* tkp = a.tk ? static_cast<const char*>(a.tk) + khead : kp;
   const char* tvp = a.tv ? static_cast<const char*>(a.tv) + khead : vp;
-  const int64_t qbytes = int64_t(a.Nq) * L::ROW;
+  const int64_t qbytes = int64_t(a.Nq) * a.grow;
 
   vec8 qB[L::NC], tqB[L::NC];
   {
     const Rsrc rq = make_rsrc(qp, qbytes), rtq = make_rsrc(tqp, a.tq ? qbytes : 0);
 #pragma unroll
     for (int c = 0; c < L::NC; ++c) {
-      const int off = qi * L::ROW + (hlf * (D / 2) + 8 * c) * 2;
+      const int col = hlf * (D / 2) + 8 * c;
+      const int off = col < a.dh ? qi * a.grow + col * 2 : kOutOfRange;
       qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
       tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
       if constexpr (POW2) {
@@ -921,12 +937,14 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   // Tile loads (group B only): one 16-byte slot per tensor per thread.
   const int tb = tid - 4 * 64;                     // 0..255 in group B
   const int drow = (tb & 255) >> 3, dpg = tb & 7;
-  const int dl_off = drow * L::ROW + ((dpg ^ swz(drow)) << 4);
-  const int64_t kbytes = int64_t(a.Nk) * L::ROW;
+  const int dlg = dpg ^ swz(drow);
+  const int dl_off = dlg < (a.dh >> 3) ? drow * a.grow + (dlg << 4) : kOutOfRange;   // global, in a tile
+  const int tile_g = L::BN * a.grow;
+  const int64_t kbytes = int64_t(a.Nk) * a.grow;
   const Rsrc rk = make_rsrc(kp, kbytes), rv = make_rsrc(vp, kbytes);
   const Rsrc rtk = make_rsrc(tkp, a.tk ? kbytes : 0), rtv = make_rsrc(tvp, a.tv ? kbytes : 0);
   auto issue_tile = [&](int j, char* stage) {
-    const int off = (t0 + j) * L::TENSOR_BYTES + dl_off;
+    const int off = dl_off == kOutOfRange ? kOutOfRange : (t0 + j) * tile_g + dl_off;
     const int slot = (wave - 4) * 64 * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot), 16,
                                              off, 0, 0, 0);
@@ -1147,8 +1165,8 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   if (qi < a.Nq) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const float tl = mu * inv;   // mu already sums e dS
-    uint16_t* op = static_cast<uint16_t*>(a.o) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
-    uint16_t* top = static_cast<uint16_t*>(a.to) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
+    uint16_t* op = static_cast<uint16_t*>(a.o) + (int64_t(bh) * a.Nq + qi) * a.dh;
+    uint16_t* top = static_cast<uint16_t*>(a.to) + (int64_t(bh) * a.Nq + qi) * a.dh;
 #pragma unroll
     for (int t = 0; t < L::NT; ++t) {
 #pragma unroll
@@ -1160,8 +1178,10 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
           dv[e] = accT[t][4 * g + e] * inv - tl * ov[e];
         }
         const int dd = 32 * t + 8 * g + 4 * hlf;
-        *reinterpret_cast<uint2*>(op + dd) = uint2{T::pack2(ov[0], ov[1]), T::pack2(ov[2], ov[3])};
-        *reinterpret_cast<uint2*>(top + dd) = uint2{T::pack2(dv[0], dv[1]), T::pack2(dv[2], dv[3])};
+        if (dd < a.dh) {
+          *reinterpret_cast<uint2*>(op + dd) = uint2{T::pack2(ov[0], ov[1]), T::pack2(ov[2], ov[3])};
+          *reinterpret_cast<uint2*>(top + dd) = uint2{T::pack2(dv[0], dv[1]), T::pack2(dv[2], dv[3])};
+        }
       }
     }
     if (hlf == 0) {
@@ -1176,6 +1196,313 @@ template <typename T, int MASK, bool CAUSAL, bool POW2>
 __global__ __launch_bounds__(kPPThreads, 2) void fwd16pp_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   fwd16pp_body<T, MASK, CAUSAL, POW2>(a);
+#endif
+}
+
+// ------------------------------------------ 16-bit kernel for wide heads (d = 256)
+//
+// Four waves, 64 query rows: waves 2r and 2r+1 (a pair) share the 32 rows of
+// row block r, and wave 2r+ch owns half ch of the head dimension, both as a
+// contraction half for the scores and as the 128 output columns of O and dO
+// it accumulates. Per 32-key block a wave forms its partial S and dS over its
+// half, the pair swaps partials through LDS, and both add them (float32
+// addition commutes, so both hold the same S and dS bit for bit and run the
+// same softmax). A wave thus holds half of Q, dQ and half of the output
+// accumulators, and no product is computed twice. Keys stream through a
+// 2-stage LDS ring (a stage of K, dK, V, dV is 64 KB at d = 256): tile k+1 is
+// fetched while block k is computed. Softmax (lazy rescale) and the value
+// products are the 4-wave kernel's steps; one wave per SIMD.
+constexpr int kWideBM = 64;                          // query rows per workgroup
+constexpr int kWideXchg = 2 * 16 * 64 * 4;           // bytes of one wave's partial S, dS
+
+template <typename T, int MASK, bool CAUSAL, bool POW2>
+__device__ __forceinline__ void fwd16w_body(const FwdArgs& a, int t_lo, int t_hi, char* stage0, char* stage1,
+                                            char* xchg) {
+  constexpr int D = 256;
+  using L = Tile16<D>;
+  using vec8 = typename T::vec8;
+  constexpr int LOADS = L::TENSOR_BYTES / (16 * kThreads);   // 16-byte loads per thread per tensor
+  static_assert(LOADS * 16 * kThreads == L::TENSOR_BYTES, "tile must split evenly over the workgroup");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c32 = lane & 31;
+  const int hlf = lane >> 5;
+
+  int qb, bh;
+  block_coords(a, qb, bh);
+  const int b = bh / a.H, h = bh % a.H;
+  constexpr int NT = L::NT / 2;        // accumulator tiles of this wave's column half
+  const int ch = wave & 1;             // column half: output columns 128 ch .. 128 ch + 127
+  const int q0 = qb * kWideBM;
+  const int qw0 = q0 + 32 * (wave >> 1);
+  const int qi = qw0 + c32;
+  const bool wave_live = qw0 < a.Nq;
+
+  const int64_t qhead = int64_t(bh) * a.Nq * a.grow;
+  const int64_t khead = int64_t(bh / a.grp) * a.Nk * a.grow;
+  const char* qp = static_cast<const char*>(a.q) + qhead;
+  const char* kp = static_cast<const char*>(a.k) + khead;
+  const char* vp = static_cast<const char*>(a.v) + khead;
+  const char* tqp = a.tq ? static_cast<const char*>(a.tq) + qhead : qp;
+  const char* tkp = a.tk ? static_cast<const char*>(a.tk) + khead : kp;
+  const char* tvp = a.tv ? static_cast<const char*>(a.tv) + khead : vp;
+  const int64_t qbytes = int64_t(a.Nq) * a.grow;
+
+  constexpr int NCH = L::NC / 2;       // score chunks of this wave's contraction half
+  vec8 qB[NCH], tqB[NCH];
+  {
+    const Rsrc rq = make_rsrc(qp, qbytes), rtq = make_rsrc(tqp, a.tq ? qbytes : 0);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int col = hlf * (D / 2) + 8 * (NCH * ch + c);
+      const int off = col < a.dh ? qi * a.grow + col * 2 : kOutOfRange;
+      qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
+      tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
+      if constexpr (POW2) {
+        qB[c] = T::scale8(qB[c], a.scale);
+        tqB[c] = T::scale8(tqB[c], a.scale);
+      }
+    }
+  }
+
+  f32x16 accO[NT], accT[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    accO[t] = f32x16{};
+    accT[t] = f32x16{};
+  }
+  RowState st{-INFINITY, 0.0f, 0.0f, 0.0f};
+  const Rsrc mr = mask_rsrc(a, b, h, mask_es<MASK>(2), nullptr, MASK == JVPATTN_MASK_BITS);
+  const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 2, a.tmask) : mr;
+  const float inv_us = POW2 ? 1.0f : a.inv_scale;   // mask tangent -> units of sd
+
+  const int kv_end = min(CAUSAL ? min(a.Nk, q0 + kWideBM) : a.Nk, 32 * t_hi);
+  const int n_tiles = max(0, (kv_end + L::BN - 1) / L::BN - t_lo);
+  const int last = !wave_live ? -1 : (CAUSAL ? min(n_tiles - 1, (qw0 >> 5) - t_lo) : n_tiles - 1);
+  auto kpos = [&](int k) { return (t_lo + k) * 32; };
+  auto needs_keymask = [&](int k) { return (CAUSAL && kpos(k) + 31 > qw0) || (kpos(k) + 32 > a.Nk); };
+
+  int dl_off[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = i * kThreads + tid;
+    const int row = p / L::GR, pg = p % L::GR, lg = pg ^ swz(row);
+    dl_off[i] = lg < (a.dh >> 3) ? row * a.grow + (lg << 4) : kOutOfRange;
+  }
+  const int tile_g = L::BN * a.grow;
+  const int64_t kbytes = int64_t(a.Nk) * a.grow;
+  const Rsrc rk = make_rsrc(kp, kbytes), rv = make_rsrc(vp, kbytes);
+  const Rsrc rtk = make_rsrc(tkp, a.tk ? kbytes : 0), rtv = make_rsrc(tvp, a.tv ? kbytes : 0);
+  auto issue_tile = [&](int j, char* stage) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int off = dl_off[i] == kOutOfRange ? kOutOfRange : (t_lo + j) * tile_g + dl_off[i];
+      const int slot = (i * kThreads + wave * 64) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
+                                               16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rtk, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rtv, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+    }
+  };
+
+  int kofs[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + NCH * ch + c) ^ swz(c32)) << 4);
+  int vofs0[NT], vofs1[NT];   // this wave's column half: 32-column tiles 4 ch .. 4 ch + 3
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int r0 = 4 * hlf + (i16 >> 2), r1 = r0 + 8;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int gcol = 4 * (NT * ch + t) + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      vofs0[t] = r0 * L::ROW + ((gcol ^ swz(r0)) << 4) + 8 * (i16 & 1);
+      vofs1[t] = r1 * L::ROW + ((gcol ^ swz(r1)) << 4) + 8 * (i16 & 1);
+    }
+  }
+
+  auto scores = [&](const char* sb, f32x16& s, f32x16& sd) {
+    s = f32x16{};
+    sd = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const vec8 ka = __builtin_bit_cast(vec8, lds_load<uint4>(sb, kofs[c]));
+      const vec8 tka = __builtin_bit_cast(vec8, lds_load<uint4>(sb + L::TENSOR_BYTES, kofs[c]));
+      s = T::mfma(ka, qB[c], s);
+      sd = T::mfma(tka, qB[c], sd);
+      sd = T::mfma(ka, tqB[c], sd);
+    }
+  };
+  // partial S, dS of this wave: 8 granules of 16 bytes per lane, lane-contiguous
+  char* xmine = xchg + wave * kWideXchg;
+  const char* xpeer = xchg + (wave ^ 1) * kWideXchg;
+  auto put_partial = [&](const f32x16& s, const f32x16& sd) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<float4*>(xmine + (j * 64 + lane) * 16) = float4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
+      *reinterpret_cast<float4*>(xmine + ((4 + j) * 64 + lane) * 16) =
+          float4{sd[4 * j], sd[4 * j + 1], sd[4 * j + 2], sd[4 * j + 3]};
+    }
+  };
+  auto add_peer = [&](f32x16& s, f32x16& sd) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 ps = *reinterpret_cast<const float4*>(xpeer + (j * 64 + lane) * 16);
+      const float4 pd = *reinterpret_cast<const float4*>(xpeer + ((4 + j) * 64 + lane) * 16);
+      s[4 * j] += ps.x;
+      s[4 * j + 1] += ps.y;
+      s[4 * j + 2] += ps.z;
+      s[4 * j + 3] += ps.w;
+      sd[4 * j] += pd.x;
+      sd[4 * j + 1] += pd.y;
+      sd[4 * j + 2] += pd.z;
+      sd[4 * j + 3] += pd.w;
+    }
+  };
+  // Value products. A pending rescale of the accumulators (alpha, when rs) is
+  // applied tile by tile just before that tile's products: scaled in one
+  // place, all 128 accumulator registers would be copied out of the AGPRs at
+  // once. The flag goes through an empty asm per tile so that the compiler
+  // keeps the four conditional blocks apart.
+  auto values = [&](const char* sb, const vec8 (&pB)[2], const vec8 (&uB)[2], bool rs, float alpha) {
+    const char* sv = sb + 2 * L::TENSOR_BYTES;
+    const char* stv = sb + 3 * L::TENSOR_BYTES;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      int rst = __builtin_amdgcn_readfirstlane(static_cast<int>(rs));
+      asm volatile("" : "+s"(rst));
+      if (rst) {
+        accO[t] *= alpha;
+        accT[t] *= alpha;
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int o0 = 16 * kc * L::ROW + vofs0[t], o1 = 16 * kc * L::ROW + vofs1[t];
+        const vec8 va = __builtin_bit_cast(
+            vec8, __builtin_shufflevector(lds_read_tr(sv + o0), lds_read_tr(sv + o1), 0, 1, 2, 3, 4, 5, 6, 7));
+        const vec8 tva = __builtin_bit_cast(
+            vec8, __builtin_shufflevector(lds_read_tr(stv + o0), lds_read_tr(stv + o1), 0, 1, 2, 3, 4, 5, 6, 7));
+        accO[t] = T::mfma(va, pB[kc], accO[t]);
+        accT[t] = T::mfma(va, uB[kc], accT[t]);
+        accT[t] = T::mfma(tva, pB[kc], accT[t]);
+      }
+    }
+  };
+
+  // Every wave passes both barriers of every iteration (the pairs' row blocks
+  // differ in causal extent and in mask visibility); the two waves of a pair
+  // take the same branches, as they read the same rows.
+  if (n_tiles > 0) issue_tile(0, stage0);
+  for (int k = 0; k < n_tiles; ++k) {
+    char* cur = (k & 1) ? stage1 : stage0;
+    char* nxt = (k & 1) ? stage0 : stage1;
+    wait_vmcnt<0>();   // this thread's loads of tile k
+    ring_barrier();    // tile k visible to all; every wave is done with tile k-1 (stage nxt) and its swap
+    if (k + 1 < n_tiles) issue_tile(k + 1, nxt);
+    bool live = k <= last;
+    MaskVals<MASK> mk;
+    if (live) {
+      if constexpr (MASK == kMaskAddT) mask_load_t(mk, a, mr, mtr, qi, kpos(k), hlf);
+      else mask_load<MASK>(mk, a, mr, qi, kpos(k), hlf);
+      if (MASK != JVPATTN_MASK_NONE && a.skip_hidden && !__any(mask_any_visible<T, MASK>(mk))) live = false;
+    }
+    f32x16 s, sd;
+    if (live) {
+      scores(cur, s, sd);
+      put_partial(s, sd);
+    }
+    ring_barrier();    // both partials of each pair in LDS
+    if (!live) continue;
+    add_peer(s, sd);
+    mask_apply<T, MASK, POW2>(s, mk, a.scale);
+    mask_tangent<T, MASK>(sd, mk, inv_us);
+    if (needs_keymask(k)) hide_keys<CAUSAL>(s, a.Nk, qi, kpos(k), hlf);
+    float alpha;
+    bool rs = update_max(block_max(s), st, a.cx, a.thr, alpha);
+    const float lsum = exp_l(s, st, a.cx);
+    if constexpr (__is_same(T, F16)) {
+      const float moff0 = st.moff;
+      const float shrink = f16_range_guard(s, sd, POW2 ? 1.0f : a.scale, lsum, st.moff, st.l, st.mu);
+      if (shrink != 1.0f) st.m += (st.moff - moff0) / a.cx;
+      alpha *= shrink;                    // alpha and shrink are 1 on lanes that keep their scale
+      rs = rs || __any(shrink != 1.0f);   // uniform over the wave, like update_max's result
+    }
+    float u[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) u[r] = POW2 ? sd[r] * s[r] : (sd[r] * a.scale) * s[r];
+    st.mu += sum16(u);
+    vec8 pB[2], uB[2];
+    {
+      uint32_t pw[8], uw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pw[i] = T::pack2(s[2 * i], s[2 * i + 1]);
+        uw[i] = T::pack2(u[2 * i], u[2 * i + 1]);
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        pB[kc] = __builtin_bit_cast(vec8, uint4{pw[4 * kc], pw[4 * kc + 1], pw[4 * kc + 2], pw[4 * kc + 3]});
+        uB[kc] = __builtin_bit_cast(vec8, uint4{uw[4 * kc], uw[4 * kc + 1], uw[4 * kc + 2], uw[4 * kc + 3]});
+      }
+    }
+    values(cur, pB, uB, rs, alpha);
+  }
+
+  const float l = xhalf_sum(st.l);
+  const float mu = xhalf_sum(st.mu);
+  if (qi < a.Nq) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float tl = mu * inv;   // mu sums e dS (float32 products)
+    uint16_t* op = static_cast<uint16_t*>(a.o) + (int64_t(bh) * a.Nq + qi) * a.dh;
+    uint16_t* top = static_cast<uint16_t*>(a.to) + (int64_t(bh) * a.Nq + qi) * a.dh;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float ov[4], dv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ov[e] = accO[t][4 * g + e] * inv;
+          dv[e] = accT[t][4 * g + e] * inv - tl * ov[e];
+        }
+        const int dd = 32 * (NT * ch + t) + 8 * g + 4 * hlf;
+        if (dd < a.dh) {
+          *reinterpret_cast<uint2*>(op + dd) = uint2{T::pack2(ov[0], ov[1]), T::pack2(ov[2], ov[3])};
+          *reinterpret_cast<uint2*>(top + dd) = uint2{T::pack2(dv[0], dv[1]), T::pack2(dv[2], dv[3])};
+        }
+      }
+    }
+    if (hlf == 0 && ch == 0) {   // both waves of the pair hold the same row statistics
+      const int64_t ri = int64_t(bh) * a.Nq + qi;
+      a.lse[ri] = l > 0.0f ? (st.moff + log2f(l)) * kLn2 : -INFINITY;
+      if (a.tlse) a.tlse[ri] = tl;
+    }
+  }
+}
+
+template <typename T, int MASK, bool CAUSAL, bool POW2>
+__global__ __launch_bounds__(kThreads, 1) void fwd16w_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using L = Tile16<256>;
+  // 2 x 64 KB ring + 4 x 8 KB partials: the whole 160 KB of a CU's LDS, so the
+  // key-range scratch of key_tiles lives in the partials' space (it is read
+  // before the first ring barrier, and the partials are written after it)
+  static_assert(2 * L::STAGE_BYTES + 4 * kWideXchg <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE_BYTES + 4 * kWideXchg];
+  char* xchg = smem + 2 * L::STAGE_BYTES;
+  int t_lo, t_hi;
+  {
+    int qb, bh;
+    block_coords(a, qb, bh);
+    const Rsrc mr = mask_rsrc(a, bh / a.H, bh % a.H, mask_es<MASK>(2), nullptr, MASK == JVPATTN_MASK_BITS);
+    key_tiles<T, MASK, 2>(a, mr, reinterpret_cast<int*>(xchg), t_lo, t_hi, qb * kWideBM, kWideBM, CAUSAL);
+  }
+  fwd16w_body<T, MASK, CAUSAL, POW2>(a, t_lo, t_hi, smem, smem + L::STAGE_BYTES, xchg);
 #endif
 }
 
@@ -1222,9 +1549,10 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
   const int qi = qw0 + c32;
   const bool wave_live = qw0 < a.Nq;
 
-  const float* qp = static_cast<const float*>(a.q) + int64_t(bh) * a.Nq * D;
-  const float* tqp = a.tq ? static_cast<const float*>(a.tq) + int64_t(bh) * a.Nq * D : nullptr;
-  const int64_t khead = int64_t(bh / a.grp) * a.Nk * D;   // the key/value head it reads
+  // global rows hold a.dh <= D logical columns; the others read as zeros and are never stored
+  const float* qp = static_cast<const float*>(a.q) + int64_t(bh) * a.Nq * a.dh;
+  const float* tqp = a.tq ? static_cast<const float*>(a.tq) + int64_t(bh) * a.Nq * a.dh : nullptr;
+  const int64_t khead = int64_t(bh / a.grp) * a.Nk * a.dh;   // the key/value head it reads
   const float* kp = static_cast<const float*>(a.k) + khead;
   const float* vp = static_cast<const float*>(a.v) + khead;
   const float* tkp = a.tk ? static_cast<const float*>(a.tk) + khead : nullptr;
@@ -1232,10 +1560,10 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
 
   float qB[D / 2], tqB[D / 2];
   {
-    const bool ok = qi < a.Nq;
 #pragma unroll
     for (int i = 0; i < D / 2; i += 4) {
-      const int64_t off = int64_t(qi) * D + hlf * (D / 2) + i;
+      const bool ok = qi < a.Nq && hlf * (D / 2) + i < a.dh;
+      const int64_t off = int64_t(qi) * a.dh + hlf * (D / 2) + i;
       f32x4 x = ok ? *reinterpret_cast<const f32x4*>(qp + off) : f32x4{};
       f32x4 y = (ok && tqp) ? *reinterpret_cast<const f32x4*>(tqp + off) : f32x4{};
 #pragma unroll
@@ -1272,8 +1600,8 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
     for (int gi = tid; gi < L::BN * L::GR; gi += kThreads) {
       const int row = gi / L::GR, g = gi % L::GR;
       const int key = kbase + row;
-      const int64_t off = int64_t(key) * D + 4 * g;
-      const bool ok = key < a.Nk;
+      const int64_t off = int64_t(key) * a.dh + 4 * g;
+      const bool ok = key < a.Nk && 4 * g < a.dh;
       lds_store<f32x4>(sk, k32_off<D>(row, g), ok ? *reinterpret_cast<const f32x4*>(kp + off) : f32x4{});
       lds_store<f32x4>(stk, k32_off<D>(row, g),
                        (ok && tkp) ? *reinterpret_cast<const f32x4*>(tkp + off) : f32x4{});
@@ -1356,8 +1684,8 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
   if (qi < a.Nq) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const float tl = mu * a.scale * inv;
-    float* op = static_cast<float*>(a.o) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
-    float* top = static_cast<float*>(a.to) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
+    float* op = static_cast<float*>(a.o) + (int64_t(bh) * a.Nq + qi) * a.dh;
+    float* top = static_cast<float*>(a.to) + (int64_t(bh) * a.Nq + qi) * a.dh;
 #pragma unroll
     for (int t = 0; t < L::NT; ++t) {
 #pragma unroll
@@ -1369,8 +1697,10 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
           dv[e] = accT[t][4 * g + e] * inv - tl * ov[e];
         }
         const int dd = 32 * t + 8 * g + 4 * hlf;
-        *reinterpret_cast<f32x4*>(op + dd) = ov;
-        *reinterpret_cast<f32x4*>(top + dd) = dv;
+        if (dd < a.dh) {
+          *reinterpret_cast<f32x4*>(op + dd) = ov;
+          *reinterpret_cast<f32x4*>(top + dd) = dv;
+        }
       }
     }
     if (hlf == 0) {
@@ -1420,6 +1750,16 @@ template <int MASK, bool CAUSAL>
 hipError_t launch_typed(int dtype, int d, bool pow2, int split, const FwdArgs& args, dim3 grid,
                         hipStream_t stream) {
   const dim3 block(kThreads);
+  if (d == 256) {   // 16-bit only (the check rejects float32)
+    if (dtype == JVPATTN_BF16) {
+      if (pow2) hipLaunchKernelGGL((fwd16w_kernel<BF16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
+      else hipLaunchKernelGGL((fwd16w_kernel<BF16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+    } else {
+      if (pow2) hipLaunchKernelGGL((fwd16w_kernel<F16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
+      else hipLaunchKernelGGL((fwd16w_kernel<F16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+    }
+    return hipGetLastError();
+  }
   if (dtype == JVPATTN_BF16) {
     if (pow2) {
       if (d == 64) launch_d64<BF16, MASK, CAUSAL, true>(split, args, grid, stream);

@@ -41,6 +41,8 @@ struct FwdArgs {
   float* lse;
   float* tlse;
   int H, Nq, Nk, BH;
+  int dh;             // logical head dimension (columns of every global row)
+  int grow;           // bytes of one global row: dh * element size
   int grp;            // query heads per key/value head (grouped-query attention; 1 = one each)
   int xgrp;           // grp when whole key/value groups can be kept on one XCD, else 1
   int head_major;     // 1: the query blocks of a head run back to back on one XCD (large grids)

@@ -67,7 +67,8 @@ enum {
                                 int64, B*H > INT32_MAX, or one head of q or k (N*d*element size)
                                 exceeds 2 GiB */
   JVPATTN_ERR_DTYPE = -3,    /* dtype not one of jvpattn_dtype */
-  JVPATTN_ERR_HEADDIM = -4,  /* d not supported (supported: 64, 128) */
+  JVPATTN_ERR_HEADDIM = -4,  /* d not supported (forward: 32, 64, 96, 128, and 256 for float16 /
+                                bfloat16; reverse pass: 64) */
   JVPATTN_ERR_MASK = -5,     /* mask_kind unknown, mask NULL/non-NULL mismatch, negative strides,
                                 or one head's mask slice exceeds 2 GiB */
   JVPATTN_ERR_ALIGN = -6,    /* a tensor pointer not 16-byte aligned (lse/tlse: 4-byte) */
@@ -82,7 +83,7 @@ enum {
 typedef struct {
   int32_t B, H;          /* batch, heads */
   int32_t Nq, Nk;        /* query rows, key/value rows (causal is top-left aligned when Nq != Nk) */
-  int32_t d;             /* head dimension of q, k, v (64 or 128) */
+  int32_t d;             /* head dimension of q, k, v: 32, 64, 96, 128, or 256 (16-bit types) */
   int32_t dtype;         /* jvpattn_dtype */
   int32_t mask_kind;     /* jvpattn_mask_kind */
   int32_t causal;        /* 0 or 1 */

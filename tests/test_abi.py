@@ -95,8 +95,10 @@ def test_check_accepts_valid_calls():
     p = good_params()
     assert call(p, ptrs(p)) == 0
     assert call(p, ptrs(p), tq=None, tk=None, tv=None, tlse=None) == 0
-    for d in (64, 128):
+    for d in (32, 64, 96, 128, 256):
         for dt, es in ((J.JVPATTN_F32, 4), (J.JVPATTN_F16, 2), (J.JVPATTN_BF16, 2)):
+            if d == 256 and dt == J.JVPATTN_F32:
+                continue   # rejected: see test_check_rejects
             p = good_params(d=d, dtype=dt)
             assert call(p, ptrs(p, es)) == 0
     p = good_params(mask_kind=J.JVPATTN_MASK_BOOL, mask_stride_b=100 * 90, mask_stride_q=90)
@@ -165,7 +167,7 @@ def test_check_grouped_kv_heads():
 @pytest.mark.parametrize("case,code", [
     ("params_null", -1), ("q_null", -1), ("o_null", -1), ("to_null", -1), ("lse_null", -1), ("k_null", -1),
     ("neg_B", -2), ("neg_Nk", -2), ("d_zero", -2), ("overflow", -2),
-    ("dtype", -3), ("d_96", -4), ("d_32", -4),
+    ("dtype", -3), ("d_48", -4), ("d_512", -4), ("d_256_f32", -4),
     ("kind", -5), ("mask_missing", -5), ("mask_extra", -5), ("mask_neg_stride", -5), ("mask_stride_overflow", -5),
     ("q_misaligned", -6), ("tv_misaligned", -6), ("lse_misaligned", -6), ("mask_misaligned", -6),
     ("scale_nan", -7), ("scale_inf", -7), ("scale_zero", -7), ("scale_neg", -7),
@@ -192,10 +194,12 @@ def test_check_rejects(case, code):
         p.B, p.H, p.Nq = 2 ** 31 - 1, 2 ** 31 - 1, 2 ** 31 - 1
     elif case == "dtype":
         p.dtype = 7
-    elif case == "d_96":
-        p.d = 96
-    elif case == "d_32":
-        p.d = 32
+    elif case == "d_48":
+        p.d = 48
+    elif case == "d_512":
+        p.d = 512
+    elif case == "d_256_f32":
+        p.d, p.dtype = 256, J.JVPATTN_F32
     elif case == "kind":
         p.mask_kind = 5
     elif case == "mask_missing":

@@ -175,6 +175,82 @@ def test_term_isolation(dtype, tangents, kernel):
         assert torch.all(got["to"] == 0) and torch.all(got["tlse"] == 0)
 
 
+# ------------------------------------------------ head dimensions 32, 96, 256
+# d = 32 and 96 run the d = 64 and d = 128 kernels with the missing head-dim
+# columns read as zeros; d = 256 (16-bit types) has a kernel of its own whose
+# wave pairs split the head dimension and swap partial scores.
+
+HEAD_DIMS = [32, 96, 256]
+
+
+def _dtypes(d):
+    return ("bf16", "f16") if d == 256 else ("bf16", "f16", "f32")
+
+
+@pytest.mark.parametrize("std", [1.0, 2.0])
+@pytest.mark.parametrize("mask_kind", ["none", "bool", "additive"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_head_dim_stress(d, causal, mask_kind, std):
+    for dtype in _dtypes(d):
+        w = I.Workload(f"d{d}", B=1, H=2, N=200, d=d, dtype=dtype, causal=causal, mask_kind=mask_kind, std=std,
+                       seed=100 + d, mask_heads=2 if mask_kind == "additive" else 1, keep=0.7)
+        check(w)
+
+
+@pytest.mark.parametrize("mask_kind", ["none", "bool"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_32_every_kernel(causal, mask_kind, kernel):
+    for dtype in ("bf16", "f16"):
+        w = I.Workload("d32k", B=1, H=2, N=300, d=32, dtype=dtype, causal=causal, mask_kind=mask_kind, std=1.0,
+                       seed=131, keep=0.7)
+        check(w)
+
+
+@pytest.mark.parametrize("N", [1, 31, 33, 63, 64, 65, 127, 129, 255, 257])
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_head_dim_tile_boundaries(d, N):
+    for dtype, causal in (("bf16", False), ("f16", True)):
+        w = I.Workload(f"d{d}edge{N}", B=1, H=2, N=N, d=d, dtype=dtype, causal=causal, std=1.0, seed=N + d)
+        check(w)
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_head_dim_rectangular_grouped(d):
+    for Nq, Nk, causal in ((70, 200, False), (200, 70, True), (1, 130, True)):
+        w = I.Workload(f"d{d}rect", B=2, H=4, Hkv=2, N=Nq, Nk=Nk, d=d, dtype="bf16", causal=causal, std=1.0,
+                       seed=5 + d)
+        check(w)
+
+
+@pytest.mark.parametrize("case", ["ramp", "jump", "late"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [96, 256])
+def test_head_dim_running_reference(d, dtype, case):
+    """The rebase paths of the d = 128 and d = 256 kernels: rising scores, a jump past the float32
+    range, rows whose first visible key comes late (as in the d = 64 tests below)."""
+    w = I.Workload(f"d{d}{case}", B=1, H=2, N=512, d=d, dtype=dtype, mask_kind="additive", std=1.0, seed=24 + d)
+
+    def late(m):
+        m[0::2, :300] = float("-inf")
+        m[0::2, 300:] = 100.0
+    fill = {"ramp": lambda m: m.add_(torch.arange(w.N, dtype=torch.float32)[None, :] * 0.6),
+            "jump": lambda m: m[:, 300].fill_(200.0), "late": late}[case]
+    check(w, _additive_rows(w, fill))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [96, 256])
+def test_head_dim_f16_large_score_tangents(d, causal):
+    """|dS| ~ 2^13 in float16: weights are lowered (and the accumulators with them) instead of overflowing."""
+    w = I.Workload(f"d{d}big_ds", B=1, H=2, N=300, d=d, dtype="f16", causal=causal, std=1.0, seed=40 + d)
+    x = I.make_inputs(w)
+    for n in ("tq", "tk"):
+        x[n] = (x[n].float() * 2.0 ** 12).to(torch.float16)
+    got, _ = check(w, x=x)
+    assert np.all(np.isfinite(got["to"].numpy()))
+
+
 # ------------------------------------------------ edges
 
 @pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 130, 255, 256, 257, 511, 513])
@@ -367,7 +443,7 @@ def test_deterministic(kernel):
 
 def test_errors_raise_and_write_nothing():
     from forward_mode_autodiff_amd.jvpattn import JvpattnError
-    q = torch.randn(1, 1, 8, 96, device=DEV, dtype=torch.bfloat16)
+    q = torch.randn(1, 1, 8, 48, device=DEV, dtype=torch.bfloat16)   # an unsupported head dimension
     with pytest.raises(JvpattnError) as e:
         jvpattn_fwd(q, q, q)
     assert e.value.code == -4
