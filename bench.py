@@ -85,18 +85,22 @@ def algorithmic_bytes(w):
     return w.B * w.H * per_q_head + w.B * w.hkv * per_kv_head + mask
 
 
-KERNEL_SOURCES = [os.path.join(ROOT, "forward_mode_autodiff_amd", "csrc", f)
-                  for f in ("jvpattn_fwd.hip", "jvpattn_device.h")]
-TRAFFIC_FILES = {"hvp": os.path.join(ROOT, "profiles", "hvp_fwd_bf16_causal_hbm_traffic.txt")}
+# The forward's device sources and build flags: a counter summary taken before any of them changed
+# no longer describes the kernel.
+KERNEL_SOURCES = [os.path.join(ROOT, "forward_mode_autodiff_amd", f)
+                  for f in ("csrc/jvpattn_fwd.hip", "csrc/jvpattn_fwd_inst.hip", "csrc/jvpattn_fwd_kernels.h",
+                            "csrc/jvpattn_fwd_launch.h", "csrc/jvpattn_device.h", "build.py")]
 
 
 def measured_traffic(workload):
-    """HBM bytes per launch from the committed counter summary, or None if absent or the kernel changed since
-    (the summary records a hash of the forward's device sources)."""
+    """HBM bytes per launch from the committed counter summary of this workload (profiles/<kernel>__<workload>.txt),
+    or None if absent or the kernel changed since (the summary records a hash of the forward's sources)."""
+    import glob
     import hashlib
-    path = TRAFFIC_FILES.get(workload)
-    if not path or not os.path.exists(path):
+    found = glob.glob(os.path.join(ROOT, "profiles", f"*__{workload}.txt"))
+    if len(found) != 1:
         return None
+    path = found[0]
     fields = {}
     for line in open(path):
         if ":" in line:
