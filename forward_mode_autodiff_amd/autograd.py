@@ -28,8 +28,8 @@ supplies tensors, the autograd graph and streams.
 
 Inputs: q [B, H, N, d], k and v [B, Hkv, N, d] (Hkv dividing H: grouped
 key/value heads) CUDA tensors of one dtype (float16 / bfloat16 for the
-reverse pass, which supports d = 64; the forward also takes float32 and
-d = 128). Masks as in ``jvpattn_fwd`` (bool: True = attend; additive: q's
+reverse pass, which supports d = 64 and 128; the forward also takes float32,
+and d = 32, 96 and 256 -- 256 in 16-bit types only). Masks as in ``jvpattn_fwd`` (bool: True = attend; additive: q's
 dtype, no reverse-mode gradient).
 """
 from __future__ import annotations

@@ -29,7 +29,9 @@ SOURCES = [("jvpattn_fwd.hip", "jvpattn_fwd", []), ("jvpattn_bwd.hip", "jvpattn_
            ("jvpattn_check.cpp", "jvpattn_check", [])] + [
     ("jvpattn_fwd_inst.hip", f"jvpattn_fwd_{name}_{'causal' if c else 'full'}",
      [f"-DJVPATTN_INST_MASK={kind}", f"-DJVPATTN_INST_CAUSAL={c}"])
-    for name, kind in MASK_KINDS.items() for c in (1, 0)]
+    for name, kind in MASK_KINDS.items() for c in (1, 0)] + [
+    ("jvpattn_bwd_inst.hip", f"jvpattn_bwd_d{d}_{side}", [f"-DJVPATTN_BWD_D={d}", f"-DJVPATTN_BWD_PART={part}"])
+    for d in (64, 128) for part, side in ((0, "dkv"), (1, "dq"))]
 
 
 def hipcc() -> str:
@@ -40,13 +42,17 @@ def hipcc() -> str:
 
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
-# Device code: gfx950 only; packed fp32 instructions disabled. The matrix
-# products take their accumulators in VGPRs where the register budget allows
-# (amdgpu-mfma-vgpr-form): the loop-carried accumulators of the d = 128 and
-# d = 256 kernels then stop bouncing between AGPRs and VGPRs and no longer
-# spill; the d = 64 ping-pong kernel's code is unchanged by it.
+# Device code: gfx950 only; packed fp32 instructions disabled.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-munsafe-fp-atomics"]
+          "-munsafe-fp-atomics"]
+# The matrix products take their accumulators in VGPRs where the register
+# budget allows (amdgpu-mfma-vgpr-form): loop-carried accumulators then stop
+# bouncing between AGPRs and VGPRs, and the forward's d = 128 / 256 kernels
+# and the reverse pass's masked ones no longer spill (the d = 64 ping-pong
+# kernel's code is unchanged by it). The reverse pass's d = 128 key-side
+# object builds without it: the compiler fails on two of its instances.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+VGPR_FORM_OBJECTS = ("jvpattn_fwd", "jvpattn_bwd_d64", "jvpattn_bwd_d128_dq")
 
 
 def _compile(job, verbose: bool) -> str:
@@ -54,7 +60,7 @@ def _compile(job, verbose: bool) -> str:
     obj = os.path.join(BUILD, name + ".o")
     cmd = [hipcc(), *COMMON, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
-        cmd[1:1] = ["-x", "hip"] + DEVICE
+        cmd[1:1] = ["-x", "hip"] + DEVICE + (VGPR_FORM if name.startswith(VGPR_FORM_OBJECTS) else [])
     else:
         cmd[1:1] = ["-x", "c++"]
     if verbose:

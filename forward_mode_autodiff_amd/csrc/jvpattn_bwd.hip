@@ -28,849 +28,16 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
-#include <type_traits>
 
 #include "jvpattn.h"
-#include "jvpattn_device.h"
+#include "jvpattn_bwd_launch.h"
+#include "jvpattn_fwd_launch.h"
 #include "jvpattn_internal.h"
 
 namespace jvpattn {
 namespace {
 
-constexpr int kBWaves = 4;
-constexpr int kBThreads = 64 * kBWaves;
-constexpr int kBBlk = 32 * kBWaves;   // keys (dkv) or queries (dq) per workgroup
-static_assert(kBThreads == kTileThreads, "LDS tiles are laid out for 4 waves");
-
-struct BwdArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* tq;
-  const void* tk;
-  const void* tv;
-  const void* mask;
-  const void* tmask;  // tangent of the additive mask (kind kMaskAddT), laid out as the mask
-  const void* o;
-  const void* to;
-  const void* go;
-  const void* gto;
-  const float* lse;
-  const float* tlse;
-  void* dq;
-  void* dk;
-  void* dv;
-  void* dtq;
-  void* dtk;
-  void* dtv;
-  float* ws;          // [4][ws_stride]: -lse*log2e, tlse, r, del
-  int64_t ws_stride;  // floats per workspace array
-  int H, Nq, Nk, BH;
-  int grp;            // query heads per key/value head (grouped-query attention; 1 = one each)
-  int BHK;            // key/value heads in all: B * H / grp
-  int n_blk;
-  int mask_vec;
-  int64_t msb, msh, msq;
-  float scale;
-  float inv_scale;    // 1 / scale
-  float cx;           // score units -> log2 units
-};
-
-enum { WS_NEGL = 0, WS_TLSE = 1, WS_R = 2, WS_DEL = 3 };
-
-// ------------------------------------------------------------------ rows
-// Eight lanes per query row (d = 64: one 16-byte granule of each tensor per
-// lane), so a wave reads 1 KB of each tensor contiguously; the row's partial
-// sums meet in three butterfly exchanges.
-template <typename T>
-__device__ __forceinline__ void bwd_rows_body(const BwdArgs& a, int64_t rows) {
-  const int64_t t = int64_t(blockIdx.x) * kBThreads + threadIdx.x;
-  const int64_t row = t >> 3;
-  const int gi = threadIdx.x & 7;
-  const bool live = row < rows;
-  const int64_t at = live ? row * 8 + gi : 0;
-  const uint4 wo = live ? static_cast<const uint4*>(a.o)[at] : uint4{0, 0, 0, 0};
-  const uint4 wto = live ? static_cast<const uint4*>(a.to)[at] : uint4{0, 0, 0, 0};
-  // a NULL cotangent is zero
-  const uint4 wg = (live && a.go) ? static_cast<const uint4*>(a.go)[at] : uint4{0, 0, 0, 0};
-  const uint4 wgd = (live && a.gto) ? static_cast<const uint4*>(a.gto)[at] : uint4{0, 0, 0, 0};
-  const uint32_t xo[4] = {wo.x, wo.y, wo.z, wo.w}, xto[4] = {wto.x, wto.y, wto.z, wto.w};
-  const uint32_t xg[4] = {wg.x, wg.y, wg.z, wg.w}, xgd[4] = {wgd.x, wgd.y, wgd.z, wgd.w};
-  float r = 0.0f, go_o = 0.0f, gd_to = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int hw = 0; hw < 2; ++hw) {
-      const uint16_t so = hw ? hi16(xo[i]) : lo16(xo[i]);
-      const uint16_t sto = hw ? hi16(xto[i]) : lo16(xto[i]);
-      const uint16_t sg = hw ? hi16(xg[i]) : lo16(xg[i]);
-      const uint16_t sgd = hw ? hi16(xgd[i]) : lo16(xgd[i]);
-      const float fo = T::widen(so), fgd = T::widen(sgd);
-      r = fmaf(fgd, fo, r);
-      go_o = fmaf(T::widen(sg), fo, go_o);
-      gd_to = fmaf(fgd, T::widen(sto), gd_to);
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < 8; m <<= 1) {
-    r += __shfl_xor(r, m, 8);
-    go_o += __shfl_xor(go_o, m, 8);
-    gd_to += __shfl_xor(gd_to, m, 8);
-  }
-  if (!live || gi != 0) return;
-  const float lse = a.lse[row], tl = a.tlse[row];
-  a.ws[WS_NEGL * a.ws_stride + row] = lse == -INFINITY ? -INFINITY : -lse * kLog2e;
-  a.ws[WS_TLSE * a.ws_stride + row] = tl;
-  a.ws[WS_R * a.ws_stride + row] = r;
-  a.ws[WS_DEL * a.ws_stride + row] = go_o + gd_to - tl * r;
-}
-
-template <typename T>
-__global__ __launch_bounds__(kBThreads) void bwd_rows_kernel(BwdArgs a, int64_t rows) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  bwd_rows_body<T>(a, rows);
-#endif
-}
-
-// Element-wise step shared by both tile kernels. For one score element:
-// s (masked score, score units), sd (score tangent, times us gives dS),
-// x = (G V^T + Gd dV^T), dm = D, and the row's statistics.
-struct Cot {
-  float p, pd, sbar, sdbar;
-};
-__device__ inline Cot cotangents(float s, float sd, float x, float dm, float cx, float us, float negl, float tl,
-                                 float r, float del) {
-  Cot c;
-  c.p = __builtin_amdgcn_exp2f(fmaf(s, cx, negl));
-  const float sdv = sd * us;        // dS
-  const float sdu = sdv - tl;       // dS - tlse
-  c.pd = c.p * sdu;
-  const float dp = x + dm * sdu - r * sdv;
-  c.sbar = c.p * (dp - del);
-  c.sdbar = c.p * (dm - r);
-  return c;
-}
-
-// ------------------------------------------------------------------ dq
-//
-// Four waves, 32 queries each (128 per workgroup), a loop over 32-key tiles
-// of K, dK, V, dV in the forward's LDS format (ring of 4, fetched two tiles
-// ahead). Per tile and wave, with the forward's transposed layout (lane =
-// query column, 16 keys per lane):
-//   S^T = K Q^T, Sd^T = dK Q^T + K dQ^T, X^T = V G^T + dV Gd^T, D^T = V Gd^T
-// (24 products), the cotangents per element, then
-//   dq^T += K^T Sbar^T + dK^T Sdbar^T,  dtq^T += K^T Sdbar^T  (12 products).
-template <typename T, int MASK, bool CAUSAL, bool POW2>
-__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
-  constexpr int D = 64;
-  using L = Tile16<D>;
-  using vec8 = typename T::vec8;
-  __shared__ __attribute__((aligned(16))) char stage0[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char stage1[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char stage2[L::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char stage3[L::STAGE_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c32 = lane & 31;
-  const int hlf = lane >> 5;
-
-  const int qb = a.n_blk - 1 - int(blockIdx.x) / a.BH;   // heaviest first when causal
-  const int bh = int(blockIdx.x) % a.BH;
-  const int b = bh / a.H, h = bh % a.H;
-  const int q0 = qb * kBBlk;
-  const int qw0 = q0 + 32 * wave;
-  const int qi = qw0 + c32;
-  const bool wave_live = qw0 < a.Nq;
-
-  const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
-  const int64_t khead = int64_t(bh / a.grp) * a.Nk * L::ROW;   // the key/value head it reads
-  const int64_t qbytes = int64_t(a.Nq) * L::ROW, kbytes = int64_t(a.Nk) * L::ROW;
-  auto at = [](const void* p, int64_t off) { return static_cast<const char*>(p) + off; };
-
-  // B operands of this wave's 32 queries: Q, dQ (scale folded in when exact), G, Gd.
-  vec8 qB[L::NC], tqB[L::NC], gB[L::NC], tgB[L::NC];
-  {
-    const Rsrc rq = make_rsrc(at(a.q, qhead), qbytes);
-    const Rsrc rtq = make_rsrc(a.tq ? at(a.tq, qhead) : at(a.q, qhead), a.tq ? qbytes : 0);
-    const Rsrc rg = make_rsrc(a.go ? at(a.go, qhead) : at(a.q, qhead), a.go ? qbytes : 0);
-    const Rsrc rtg = make_rsrc(a.gto ? at(a.gto, qhead) : at(a.q, qhead), a.gto ? qbytes : 0);
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      const int off = qi * L::ROW + (hlf * (D / 2) + 8 * c) * 2;
-      qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
-      tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
-      gB[c] = __builtin_bit_cast(vec8, ld128(rg, off));
-      tgB[c] = __builtin_bit_cast(vec8, ld128(rtg, off));
-      if constexpr (POW2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qB[c][e] = static_cast<__bf16>(static_cast<float>(qB[c][e]) * a.scale);
-          tqB[c][e] = static_cast<__bf16>(static_cast<float>(tqB[c][e]) * a.scale);
-        }
-      }
-    }
-  }
-  // Row statistics of this lane's query (rows past Nq read as zero and are never stored).
-  float negl = -INFINITY, tl = 0.0f, rr = 0.0f, del = 0.0f;
-  if (qi < a.Nq) {
-    const int64_t ri = int64_t(bh) * a.Nq + qi;
-    negl = a.ws[WS_NEGL * a.ws_stride + ri];
-    tl = a.ws[WS_TLSE * a.ws_stride + ri];
-    rr = a.ws[WS_R * a.ws_stride + ri];
-    del = a.ws[WS_DEL * a.ws_stride + ri];
-  }
-  const float us = POW2 ? 1.0f : a.scale;
-
-  f32x16 accQ[L::NT], accTQ[L::NT];
-#pragma unroll
-  for (int t = 0; t < L::NT; ++t) {
-    accQ[t] = f32x16{};
-    accTQ[t] = f32x16{};
-  }
-  const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : MASK == JVPATTN_MASK_BITS ? 4 : 2, nullptr,
-                            MASK == JVPATTN_MASK_BITS);
-  const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 2, a.tmask) : mr;
-  auto load_mask = [&](MaskVals<MASK>& m, int k0) {
-    if constexpr (MASK == kMaskAddT) mask_load_t(m, a, mr, mtr, qi, k0, hlf);
-    else mask_load<MASK>(m, a, mr, qi, k0, hlf);
-  };
-
-  const int kv_end = CAUSAL ? min(a.Nk, q0 + kBBlk) : a.Nk;
-  const int n_tiles = (kv_end + L::BN - 1) / L::BN;
-  const int last = !wave_live ? -1 : (CAUSAL ? min(n_tiles - 1, qw0 >> 5) : n_tiles - 1);
-  auto needs_keymask = [&](int k) { return (CAUSAL && k * 32 + 31 > qw0) || (k * 32 + 32 > a.Nk); };
-
-  int dl_off[L::LOADS];
-#pragma unroll
-  for (int i = 0; i < L::LOADS; ++i) {
-    const int p = i * kBThreads + tid;
-    const int row = p / L::GR, pg = p % L::GR;
-    dl_off[i] = row * L::ROW + ((pg ^ swz(row)) << 4);
-  }
-  const Rsrc rk = make_rsrc(at(a.k, khead), kbytes), rv = make_rsrc(at(a.v, khead), kbytes);
-  const Rsrc rtk = make_rsrc(a.tk ? at(a.tk, khead) : at(a.k, khead), a.tk ? kbytes : 0);
-  const Rsrc rtv = make_rsrc(a.tv ? at(a.tv, khead) : at(a.v, khead), a.tv ? kbytes : 0);
-  auto issue_tile = [&](int j, char* stage) {
-#pragma unroll
-    for (int i = 0; i < L::LOADS; ++i) {
-      const int off = j * L::TENSOR_BYTES + dl_off[i];
-      const int slot = (i * kBThreads + wave * 64) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
-                                               16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rtk, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rtv, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-    }
-  };
-
-  int kofs[L::NC];
-#pragma unroll
-  for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ swz(c32)) << 4);
-  int vofs0[L::NT], vofs1[L::NT];
-  {
-    const int g16 = lane >> 4, i16 = lane & 15;
-    const int r0 = 4 * hlf + (i16 >> 2), r1 = r0 + 8;
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t) {
-      const int gcol = 4 * t + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-      vofs0[t] = r0 * L::ROW + ((gcol ^ swz(r0)) << 4) + 8 * (i16 & 1);
-      vofs1[t] = r1 * L::ROW + ((gcol ^ swz(r1)) << 4) + 8 * (i16 & 1);
-    }
-  }
-  // A operands (rows = keys) of tensor `tsr` of the tile at sb.
-  auto read_rows = [&](const char* sb, int tsr, vec8 (&x)[L::NC]) {
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) x[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + tsr * L::TENSOR_BYTES, kofs[c]));
-  };
-  // Transposed A operands (rows = head dimension, keys along k) of tensor `tsr`.
-  auto read_tr = [&](const char* sb, int tsr, vec8 (&x)[L::NT][2]) {
-    const char* base = sb + tsr * L::TENSOR_BYTES;
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int o0 = 16 * kc * L::ROW + vofs0[t], o1 = 16 * kc * L::ROW + vofs1[t];
-        x[t][kc] = __builtin_bit_cast(
-            vec8, __builtin_shufflevector(lds_read_tr(base + o0), lds_read_tr(base + o1), 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-  };
-
-  // Score-side products of the tile at sb: S^T, dS^T (scores), X^T, D^T (value side).
-  struct SPh {
-    f32x16 s, sd, x, dm;
-  };
-  auto sphase = [&](const char* sb, SPh& o) {
-    vec8 ka[L::NC], tka[L::NC];
-    read_rows(sb, 0, ka);
-    read_rows(sb, 1, tka);
-    o.s = f32x16{};
-    o.sd = f32x16{};
-    o.x = f32x16{};
-    o.dm = f32x16{};
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      o.s = T::mfma(ka[c], qB[c], o.s);
-      o.sd = T::mfma(tka[c], qB[c], o.sd);
-      o.sd = T::mfma(ka[c], tqB[c], o.sd);
-    }
-    vec8 va[L::NC], tva[L::NC];
-    read_rows(sb, 2, va);
-    read_rows(sb, 3, tva);
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      o.x = T::mfma(va[c], gB[c], o.x);
-      o.x = T::mfma(tva[c], tgB[c], o.x);
-      o.dm = T::mfma(va[c], tgB[c], o.dm);
-    }
-  };
-  // Element-wise step of block k: score cotangents as 16-bit B operands.
-  auto vphase = [&](int k, SPh& p, const MaskVals<MASK>& mk, bool keymask, vec8 (&sB)[2], vec8 (&sdB)[2]) {
-    mask_apply<T, MASK, POW2>(p.s, mk, a.scale);
-    mask_tangent<T, MASK>(p.sd, mk, POW2 ? 1.0f : a.inv_scale);
-    if (keymask) hide_keys<CAUSAL>(p.s, a.Nk, qi, k * 32, hlf);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      uint32_t w0[4], w1[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r0 = 8 * kc + 2 * i;
-        const Cot c0 = cotangents(p.s[r0], p.sd[r0], p.x[r0], p.dm[r0], a.cx, us, negl, tl, rr, del);
-        const Cot c1 = cotangents(p.s[r0 + 1], p.sd[r0 + 1], p.x[r0 + 1], p.dm[r0 + 1], a.cx, us, negl, tl, rr, del);
-        w0[i] = T::pack2(c0.sbar, c1.sbar);
-        w1[i] = T::pack2(c0.sdbar, c1.sdbar);
-      }
-      sB[kc] = __builtin_bit_cast(vec8, uint4{w0[0], w0[1], w0[2], w0[3]});
-      sdB[kc] = __builtin_bit_cast(vec8, uint4{w1[0], w1[1], w1[2], w1[3]});
-    }
-  };
-  // Accumulating products with K^T, dK^T of the tile at sb.
-  auto aphase = [&](const char* sb, const vec8 (&sB)[2], const vec8 (&sdB)[2]) {
-    vec8 kt[L::NT][2], tkt[L::NT][2];
-    read_tr(sb, 0, kt);
-    read_tr(sb, 1, tkt);
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        accQ[t] = T::mfma(kt[t][kc], sB[kc], accQ[t]);
-        accQ[t] = T::mfma(tkt[t][kc], sdB[kc], accQ[t]);
-        accTQ[t] = T::mfma(kt[t][kc], sdB[kc], accTQ[t]);
-      }
-  };
-
-  // Blocks 1.. that need per-key masking start at jm: the causal diagonal, a
-  // ragged last tile, or the end of this wave's range.
-  int jm = last + 1;
-  if (CAUSAL) jm = min(jm, qw0 >> 5);
-  jm = min(jm, a.Nk >> 5);
-  jm = max(jm, 1);
-
-  // Pipelined block k (block k+1 needs no key mask): the score-side products
-  // of block k+1 run on the matrix cores while the vector units turn block k
-  // into cotangents; block k's accumulating products follow. Tiles are
-  // fetched three blocks ahead into a ring of 4.
-  auto fast = [&](int k, const char* cur, const char* nxt, char* dma, SPh& pc, SPh& pn, MaskVals<MASK>& mc,
-                  MaskVals<MASK>& mn) {
-    if (k + 2 < n_tiles) wait_vmcnt<L::TILE_VMEM>();   // tile k+1 (tile k+2 may stay in flight)
-    else wait_vmcnt<0>();
-    ring_barrier();
-    load_mask(mn, (k + 1) * 32);
-    if (k + 3 < n_tiles) issue_tile(k + 3, dma);
-    sphase(nxt, pn);
-    vec8 sB[2], sdB[2];
-    vphase(k, pc, mc, false, sB, sdB);
-    aphase(cur, sB, sdB);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * L::NC, 0);   // K / dK rows of block k+1
-#pragma unroll
-    for (int i = 0; i < 3 * L::NC; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // score products
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);          // cotangents of block k
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * L::NC, 0);   // V / dV rows of block k+1
-#pragma unroll
-    for (int i = 0; i < 3 * L::NC; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // value-side products
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);          // cotangents of block k
-    }
-  };
-
-  // Prologue: tiles 0..2 in flight; wait for tile 0; block 0's score-side
-  // products if it needs no key mask.
-  if (n_tiles > 0) issue_tile(0, stage0);
-  if (n_tiles > 1) issue_tile(1, stage1);
-  if (n_tiles > 2) issue_tile(2, stage2);
-  if (n_tiles > 2) wait_vmcnt<2 * L::TILE_VMEM>();
-  else if (n_tiles > 1) wait_vmcnt<L::TILE_VMEM>();
-  else wait_vmcnt<0>();
-  ring_barrier();
-  SPh pa, pb;
-  MaskVals<MASK> mka, mkb;
-  bool ready = false;   // pa holds the current block's score-side products
-  if (0 <= last && !needs_keymask(0)) {
-    sphase(stage0, pa);
-    load_mask(mka, 0);
-    ready = true;
-  }
-  const int kfast = ready ? jm - 1 : 0;   // blocks 0 .. kfast-1 are pipelined
-  int k = 0;
-  for (; k + 4 <= kfast; k += 4) {
-    fast(k, stage0, stage1, stage3, pa, pb, mka, mkb);
-    fast(k + 1, stage1, stage2, stage0, pb, pa, mkb, mka);
-    fast(k + 2, stage2, stage3, stage1, pa, pb, mka, mkb);
-    fast(k + 3, stage3, stage0, stage2, pb, pa, mkb, mka);
-  }
-  if (k < kfast) {
-    fast(k, stage0, stage1, stage3, pa, pb, mka, mkb);
-    if (k + 1 < kfast) fast(k + 1, stage1, stage2, stage0, pb, pa, mkb, mka);
-    if (k + 2 < kfast) fast(k + 2, stage2, stage3, stage1, pa, pb, mka, mkb);
-  }
-  if (kfast & 1) {   // block kfast's products were left in pb
-    pa = pb;
-    mka = mkb;
-  }
-
-  // Remaining blocks (diagonal, ragged tail, barrier-only ones past this
-  // wave's rows), one at a time, stage chosen at run time.
-  auto stage_of = [&](int i) -> char* {
-    i &= 3;
-    return i == 0 ? stage0 : i == 1 ? stage1 : i == 2 ? stage2 : stage3;
-  };
-  for (k = kfast; k < n_tiles; ++k) {
-    if (k + 2 < n_tiles) wait_vmcnt<2 * L::TILE_VMEM>();   // tile k (k+1, k+2 may stay in flight)
-    else if (k + 1 < n_tiles) wait_vmcnt<L::TILE_VMEM>();
-    else wait_vmcnt<0>();
-    ring_barrier();
-    if (k + 3 < n_tiles) issue_tile(k + 3, stage_of(k + 3));
-    if (k > last) continue;
-    const char* cur = stage_of(k);
-    if (!ready) {
-      sphase(cur, pa);
-      load_mask(mka, k * 32);
-    }
-    vec8 sB[2], sdB[2];
-    vphase(k, pa, mka, needs_keymask(k), sB, sdB);
-    aphase(cur, sB, sdB);
-    ready = false;
-  }
-
-  if (qi < a.Nq) {
-    uint16_t* dq = static_cast<uint16_t*>(a.dq) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
-    uint16_t* dtq = static_cast<uint16_t*>(a.dtq) + int64_t(bh) * a.Nq * D + int64_t(qi) * D;
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dd = 32 * t + 8 * g + 4 * hlf;
-        const f32x16& A = accQ[t];
-        const f32x16& B = accTQ[t];
-        *reinterpret_cast<uint2*>(dq + dd) =
-            uint2{T::pack2(A[4 * g] * a.scale, A[4 * g + 1] * a.scale), T::pack2(A[4 * g + 2] * a.scale, A[4 * g + 3] * a.scale)};
-        if (a.dtq)
-          *reinterpret_cast<uint2*>(dtq + dd) = uint2{T::pack2(B[4 * g] * a.scale, B[4 * g + 1] * a.scale),
-                                                      T::pack2(B[4 * g + 2] * a.scale, B[4 * g + 3] * a.scale)};
-      }
-  }
-}
-
-template <typename T, int MASK, bool CAUSAL, bool POW2>
-__global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  bwd_dq_body<T, MASK, CAUSAL, POW2>(a);
-#endif
-}
-
-// ------------------------------------------------------------------ dkv
-//
-// Four waves, 32 keys each (128 per workgroup), a loop over 32-query tiles of
-// Q, dQ, G, Gd (same LDS format) plus the four row statistics of the tile.
-// Here lane = key column and 16 queries per lane:
-//   S = Q K^T, Sd = dQ K^T + Q dK^T, X = G V^T + Gd dV^T, D = Gd V^T   (24)
-//   dk^T += Q^T Sbar + dQ^T Sdbar, dtk^T += Q^T Sdbar,
-//   dv^T += G^T P + Gd^T Pd,       dtv^T += Gd^T P                      (24)
-// Row r of a lane's C registers is query 8*(r/4) + 4*(lane/32) + r%4.
-
-// Mask values (i, key) for this lane's key and the 16 queries of its rows.
-template <int MASK> struct MaskCol {};
-template <> struct MaskCol<JVPATTN_MASK_BOOL> { uint32_t w[16]; };
-template <> struct MaskCol<JVPATTN_MASK_ADDITIVE> { uint32_t w[16]; };
-
-template <typename T, int MASK, bool CAUSAL, bool POW2>
-__device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
-  constexpr int D = 64;
-  using L = Tile16<D>;
-  using vec8 = typename T::vec8;
-  constexpr int STATS = 4 * 32 * 4;                // four statistics of 32 rows
-  constexpr int SB = L::STAGE_BYTES + STATS;
-  __shared__ __attribute__((aligned(16))) char stage0[SB];
-  __shared__ __attribute__((aligned(16))) char stage1[SB];
-  __shared__ __attribute__((aligned(16))) char stage2[SB];
-  __shared__ __attribute__((aligned(16))) char stage3[SB];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c32 = lane & 31;
-  const int hlf = lane >> 5;
-
-  const int kb = int(blockIdx.x) / a.BHK;   // causal: early key blocks see the most queries
-  const int bhk = int(blockIdx.x) % a.BHK;  // key/value head; its query heads are bhk*grp .. +grp-1
-  const int b = bhk * a.grp / a.H;
-  const int k0 = kb * kBBlk;
-  const int kw0 = k0 + 32 * wave;
-  const int kj = kw0 + c32;                 // this lane's key
-  const bool wave_live = kw0 < a.Nk;
-
-  const int64_t khead = int64_t(bhk) * a.Nk * L::ROW;
-  const int64_t qbytes = int64_t(a.Nq) * L::ROW, kbytes = int64_t(a.Nk) * L::ROW;
-  auto at = [](const void* p, int64_t off) { return static_cast<const char*>(p) + off; };
-
-  // B operands of this wave's 32 keys: K, dK (scale folded in when exact), V, dV.
-  vec8 kB[L::NC], tkB[L::NC], vB[L::NC], tvB[L::NC];
-  {
-    const Rsrc rk = make_rsrc(at(a.k, khead), kbytes), rv = make_rsrc(at(a.v, khead), kbytes);
-    const Rsrc rtk = make_rsrc(a.tk ? at(a.tk, khead) : at(a.k, khead), a.tk ? kbytes : 0);
-    const Rsrc rtv = make_rsrc(a.tv ? at(a.tv, khead) : at(a.v, khead), a.tv ? kbytes : 0);
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) {
-      const int off = kj * L::ROW + (hlf * (D / 2) + 8 * c) * 2;
-      kB[c] = __builtin_bit_cast(vec8, ld128(rk, off));
-      tkB[c] = __builtin_bit_cast(vec8, ld128(rtk, off));
-      vB[c] = __builtin_bit_cast(vec8, ld128(rv, off));
-      tvB[c] = __builtin_bit_cast(vec8, ld128(rtv, off));
-      if constexpr (POW2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kB[c][e] = static_cast<__bf16>(static_cast<float>(kB[c][e]) * a.scale);
-          tkB[c][e] = static_cast<__bf16>(static_cast<float>(tkB[c][e]) * a.scale);
-        }
-      }
-    }
-  }
-  const float us = POW2 ? 1.0f : a.scale;
-
-  f32x16 accK[L::NT], accTK[L::NT], accV[L::NT], accTV[L::NT];
-#pragma unroll
-  for (int t = 0; t < L::NT; ++t) {
-    accK[t] = f32x16{};
-    accTK[t] = f32x16{};
-    accV[t] = f32x16{};
-    accTV[t] = f32x16{};
-  }
-  // Grouped key/value heads: the cotangents of this head's keys sum over the
-  // grp query heads that read them, one after the other (the tile pipeline
-  // drains and restarts at each change of query head).
-  for (int g = 0; g < a.grp; ++g) {
-    const int bh = bhk * a.grp + g;
-    const int h = bh % a.H;
-    const int64_t qhead = int64_t(bh) * a.Nq * L::ROW;
-    const Rsrc mr = mask_rsrc(a, b, h, MASK == JVPATTN_MASK_BOOL ? 1 : MASK == JVPATTN_MASK_BITS ? 4 : 2,
-                              nullptr, MASK == JVPATTN_MASK_BITS);
-    const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 2, a.tmask) : mr;
-
-    const int n_qt = (a.Nq + 31) / 32;
-    // causal: queries before the block's first key see none of its keys
-    const int t_begin = CAUSAL ? min(n_qt, k0 >> 5) : 0;
-    const int first = !wave_live ? n_qt : (CAUSAL ? max(t_begin, kw0 >> 5) : 0);   // first tile of this wave
-    auto needs_rowmask = [&](int t) { return (CAUSAL && t * 32 < kw0 + 32) || (t * 32 + 32 > a.Nq) || (kw0 + 32 > a.Nk); };
-
-    int dl_off[L::LOADS];
-#pragma unroll
-    for (int i = 0; i < L::LOADS; ++i) {
-      const int p = i * kBThreads + tid;
-      const int row = p / L::GR, pg = p % L::GR;
-      dl_off[i] = row * L::ROW + ((pg ^ swz(row)) << 4);
-    }
-    const Rsrc rq = make_rsrc(at(a.q, qhead), qbytes);
-    const Rsrc rtq = make_rsrc(a.tq ? at(a.tq, qhead) : at(a.q, qhead), a.tq ? qbytes : 0);
-    const Rsrc rg = make_rsrc(a.go ? at(a.go, qhead) : at(a.q, qhead), a.go ? qbytes : 0);
-    const Rsrc rtg = make_rsrc(a.gto ? at(a.gto, qhead) : at(a.q, qhead), a.gto ? qbytes : 0);
-    // Statistics of this head's rows: wave w loads statistic w of the tile (8 lanes x 16 bytes).
-    const int64_t srow = int64_t(bh) * a.Nq;
-    const Rsrc rstat = make_rsrc(a.ws + wave * a.ws_stride + srow, int64_t(a.Nq) * 4);
-    auto issue_tile = [&](int j, char* stage) {
-#pragma unroll
-      for (int i = 0; i < L::LOADS; ++i) {
-        const int off = j * L::TENSOR_BYTES + dl_off[i];
-        const int slot = (i * kBThreads + wave * 64) * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
-                                                 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rtq, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rg, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rtg, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-      }
-      // 32 floats of statistic `wave` for rows 32j .. 32j+31 (past Nq: zeros)
-      if (lane < 8)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rstat, (__attribute__((address_space(3))) void*)to_lds(stage + L::STAGE_BYTES + wave * 128), 16,
-            j * 128 + lane * 16, 0, 0, 0);
-    };
-
-    int kofs[L::NC];
-#pragma unroll
-    for (int c = 0; c < L::NC; ++c) kofs[c] = c32 * L::ROW + (((hlf * L::NC + c) ^ swz(c32)) << 4);
-    int vofs0[L::NT], vofs1[L::NT];
-    {
-      const int g16 = lane >> 4, i16 = lane & 15;
-      const int r0 = 4 * hlf + (i16 >> 2), r1 = r0 + 8;
-#pragma unroll
-      for (int t = 0; t < L::NT; ++t) {
-        const int gcol = 4 * t + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-        vofs0[t] = r0 * L::ROW + ((gcol ^ swz(r0)) << 4) + 8 * (i16 & 1);
-        vofs1[t] = r1 * L::ROW + ((gcol ^ swz(r1)) << 4) + 8 * (i16 & 1);
-      }
-    }
-    auto read_rows = [&](const char* sb, int tsr, vec8 (&x)[L::NC]) {
-#pragma unroll
-      for (int c = 0; c < L::NC; ++c) x[c] = __builtin_bit_cast(vec8, lds_load<uint4>(sb + tsr * L::TENSOR_BYTES, kofs[c]));
-    };
-    auto read_tr = [&](const char* sb, int tsr, vec8 (&x)[L::NT][2]) {
-      const char* base = sb + tsr * L::TENSOR_BYTES;
-#pragma unroll
-      for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const int o0 = 16 * kc * L::ROW + vofs0[t], o1 = 16 * kc * L::ROW + vofs1[t];
-          x[t][kc] = __builtin_bit_cast(
-              vec8, __builtin_shufflevector(lds_read_tr(base + o0), lds_read_tr(base + o1), 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-    };
-
-    auto tile = [&](int t_idx, const char* sb) {
-      const int i0 = t_idx * 32;   // first query of the tile
-      // Mask elements (query i0 + 8(r/4) + 4 hlf + r%4, key kj) are fetched before the score
-      // products so their latency hides behind them.
-      uint32_t mw[MASK == JVPATTN_MASK_NONE ? 1 : 16], tw[MASK == kMaskAddT ? 16 : 1];
-      if constexpr (MASK != JVPATTN_MASK_NONE) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
-          if constexpr (MASK == JVPATTN_MASK_BITS) {
-            mw[r] = __builtin_amdgcn_raw_buffer_load_b32(mr, (qrow * int(a.msq) + (kj >> 5)) * 4, 0, 0);
-          } else if constexpr (MASK == JVPATTN_MASK_BOOL) {
-            mw[r] = __builtin_amdgcn_raw_buffer_load_b8(mr, qrow * int(a.msq) + kj, 0, 0);
-          } else {
-            const int off = (qrow * int(a.msq) + kj) * 2;
-            mw[r] = __builtin_amdgcn_raw_buffer_load_b16(mr, off, 0, 0);
-            if constexpr (MASK == kMaskAddT) tw[r] = __builtin_amdgcn_raw_buffer_load_b16(mtr, off, 0, 0);
-          }
-        }
-      }
-      vec8 qa[L::NC], tqa[L::NC];
-      read_rows(sb, 0, qa);
-      read_rows(sb, 1, tqa);
-      f32x16 s = f32x16{}, sd = f32x16{}, x = f32x16{}, dm = f32x16{};
-#pragma unroll
-      for (int c = 0; c < L::NC; ++c) {
-        s = T::mfma(qa[c], kB[c], s);
-        sd = T::mfma(tqa[c], kB[c], sd);
-        sd = T::mfma(qa[c], tkB[c], sd);
-      }
-      vec8 ga[L::NC], tga[L::NC];
-      read_rows(sb, 2, ga);
-      read_rows(sb, 3, tga);
-#pragma unroll
-      for (int c = 0; c < L::NC; ++c) {
-        x = T::mfma(ga[c], vB[c], x);
-        x = T::mfma(tga[c], tvB[c], x);
-        dm = T::mfma(tga[c], vB[c], dm);
-      }
-      // masks: element (query i, key kj); hidden entries get score -inf
-      if constexpr (MASK == JVPATTN_MASK_BITS) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)   // bit kj % 32 of the row's word kj / 32
-          if (((mw[r] >> (kj & 31)) & 1u) == 0u) s[r] = -INFINITY;
-      } else if constexpr (MASK == JVPATTN_MASK_BOOL) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (mw[r] == 0u) s[r] = -INFINITY;
-      } else if constexpr (MASK != JVPATTN_MASK_NONE) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float m = T::widen(uint16_t(mw[r]));
-          s[r] = POW2 ? s[r] + m : fmaf(s[r], a.scale, m);
-          if constexpr (MASK == kMaskAddT)   // the mask's tangent joins the score tangent (sd * us = dS)
-            sd[r] = fmaf(T::widen(uint16_t(tw[r])), POW2 ? 1.0f : a.inv_scale, sd[r]);
-        }
-      }
-      if (needs_rowmask(t_idx)) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
-          bool hide = qrow >= a.Nq || kj >= a.Nk;
-          if constexpr (CAUSAL) hide = hide || kj > qrow;
-          if (hide) s[r] = -INFINITY;
-        }
-      }
-      // statistics of the 16 rows: for group g, rows 8g + 4*hlf + 0..3 (one 16-byte LDS read each)
-      const char* st = sb + L::STAGE_BYTES;
-      vec8 pB[2], pdB[2], sB[2], sdB[2];
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        uint32_t wp[4], wpd[4], ws[4], wsd[4];
-#pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {
-          const int g = 2 * kc + gg;
-          const int roff = (8 * g + 4 * hlf) * 4;
-          const f32x4 ng = lds_load<f32x4>(st, WS_NEGL * 128 + roff);
-          const f32x4 tl = lds_load<f32x4>(st, WS_TLSE * 128 + roff);
-          const f32x4 rr = lds_load<f32x4>(st, WS_R * 128 + roff);
-          const f32x4 dl = lds_load<f32x4>(st, WS_DEL * 128 + roff);
-          Cot c[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            c[e] = cotangents(s[r], sd[r], x[r], dm[r], a.cx, us, ng[e], tl[e], rr[e], dl[e]);
-          }
-          wp[2 * gg] = T::pack2(c[0].p, c[1].p);
-          wp[2 * gg + 1] = T::pack2(c[2].p, c[3].p);
-          wpd[2 * gg] = T::pack2(c[0].pd, c[1].pd);
-          wpd[2 * gg + 1] = T::pack2(c[2].pd, c[3].pd);
-          ws[2 * gg] = T::pack2(c[0].sbar, c[1].sbar);
-          ws[2 * gg + 1] = T::pack2(c[2].sbar, c[3].sbar);
-          wsd[2 * gg] = T::pack2(c[0].sdbar, c[1].sdbar);
-          wsd[2 * gg + 1] = T::pack2(c[2].sdbar, c[3].sdbar);
-        }
-        pB[kc] = __builtin_bit_cast(vec8, uint4{wp[0], wp[1], wp[2], wp[3]});
-        pdB[kc] = __builtin_bit_cast(vec8, uint4{wpd[0], wpd[1], wpd[2], wpd[3]});
-        sB[kc] = __builtin_bit_cast(vec8, uint4{ws[0], ws[1], ws[2], ws[3]});
-        sdB[kc] = __builtin_bit_cast(vec8, uint4{wsd[0], wsd[1], wsd[2], wsd[3]});
-      }
-      {
-        vec8 qt[L::NT][2], tqt[L::NT][2];
-        read_tr(sb, 0, qt);
-        read_tr(sb, 1, tqt);
-#pragma unroll
-        for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc) {
-            accK[t] = T::mfma(qt[t][kc], sB[kc], accK[t]);
-            accK[t] = T::mfma(tqt[t][kc], sdB[kc], accK[t]);
-            accTK[t] = T::mfma(qt[t][kc], sdB[kc], accTK[t]);
-          }
-      }
-      {
-        vec8 gt[L::NT][2], tgt[L::NT][2];
-        read_tr(sb, 2, gt);
-        read_tr(sb, 3, tgt);
-#pragma unroll
-        for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc) {
-            accV[t] = T::mfma(gt[t][kc], pB[kc], accV[t]);
-            accV[t] = T::mfma(tgt[t][kc], pdB[kc], accV[t]);
-            accTV[t] = T::mfma(tgt[t][kc], pB[kc], accTV[t]);
-          }
-      }
-    };
-
-    constexpr int TILE_VMEM = L::TILE_VMEM + 1;   // four tensors + this wave's statistic
-    // All waves issue the same count (the statistic load is exec-masked, not skipped).
-    // Before step t's wait, tiles t and t+1 may be in flight (t+2 is issued after it).
-    auto wait_tile = [&](int j) {
-      if (j + 1 < n_qt) wait_vmcnt<TILE_VMEM>();
-      else wait_vmcnt<0>();
-    };
-    const int n_steps = n_qt - t_begin;
-    if (n_steps > 0) issue_tile(t_begin, stage0);
-    if (n_steps > 1) issue_tile(t_begin + 1, stage1);
-    auto step = [&](int t_idx, const char* cur, char* dma) {
-      wait_tile(t_idx);
-      ring_barrier();
-      if (t_idx + 2 < n_qt) issue_tile(t_idx + 2, dma);
-      if (t_idx >= first) tile(t_idx, cur);
-    };
-    for (int i = 0; i < n_steps; i += 4) {
-      const int t_idx = t_begin + i;
-      step(t_idx, stage0, stage2);
-      if (i + 1 < n_steps) step(t_idx + 1, stage1, stage3);
-      if (i + 2 < n_steps) step(t_idx + 2, stage2, stage0);
-      if (i + 3 < n_steps) step(t_idx + 3, stage3, stage1);
-    }
-    // every wave is done reading the ring before the next head's loads land in it
-    if (g + 1 < a.grp) ring_barrier();
-  }
-
-  if (kj < a.Nk) {
-    const int64_t base = int64_t(bhk) * a.Nk * D + int64_t(kj) * D;
-    uint16_t* dk = static_cast<uint16_t*>(a.dk) + base;
-    uint16_t* dtk = static_cast<uint16_t*>(a.dtk) + base;
-    uint16_t* dv = static_cast<uint16_t*>(a.dv) + base;
-    uint16_t* dtv = static_cast<uint16_t*>(a.dtv) + base;
-    const float sc = a.scale;
-#pragma unroll
-    for (int t = 0; t < L::NT; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dd = 32 * t + 8 * g + 4 * hlf;
-        const int e = 4 * g;
-        *reinterpret_cast<uint2*>(dk + dd) = uint2{T::pack2(accK[t][e] * sc, accK[t][e + 1] * sc),
-                                                   T::pack2(accK[t][e + 2] * sc, accK[t][e + 3] * sc)};
-        if (a.dtk)
-          *reinterpret_cast<uint2*>(dtk + dd) = uint2{T::pack2(accTK[t][e] * sc, accTK[t][e + 1] * sc),
-                                                      T::pack2(accTK[t][e + 2] * sc, accTK[t][e + 3] * sc)};
-        *reinterpret_cast<uint2*>(dv + dd) =
-            uint2{T::pack2(accV[t][e], accV[t][e + 1]), T::pack2(accV[t][e + 2], accV[t][e + 3])};
-        if (a.dtv)
-          *reinterpret_cast<uint2*>(dtv + dd) =
-              uint2{T::pack2(accTV[t][e], accTV[t][e + 1]), T::pack2(accTV[t][e + 2], accTV[t][e + 3])};
-      }
-  }
-}
-
-template <typename T, int MASK, bool CAUSAL, bool POW2>
-__global__ __launch_bounds__(kBThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  bwd_dkv_body<T, MASK, CAUSAL, POW2>(a);
-#endif
-}
-
-// ------------------------------------------------------------------ launch
-
-template <typename T, int MASK, bool CAUSAL, bool POW2>
-hipError_t launch_tiles(BwdArgs a, hipStream_t s) {
-  const int64_t nkb = (a.Nk + kBBlk - 1) / kBBlk, nqb = (a.Nq + kBBlk - 1) / kBBlk;
-  if (nkb * a.BHK > INT32_MAX || nqb * a.BH > INT32_MAX) return hipErrorInvalidValue;
-  if (nkb > 0 && a.BHK > 0) {
-    BwdArgs ak = a;
-    ak.n_blk = static_cast<int>(nkb);
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, MASK, CAUSAL, POW2>), dim3(unsigned(nkb * a.BHK)), dim3(kBThreads), 0,
-                       s, ak);
-  }
-  if (nqb > 0 && a.BH > 0) {
-    BwdArgs aq = a;
-    aq.n_blk = static_cast<int>(nqb);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, MASK, CAUSAL, POW2>), dim3(unsigned(nqb * a.BH)), dim3(kBThreads), 0, s,
-                       aq);
-  }
-  return hipGetLastError();
-}
-
-template <typename T, int MASK>
-hipError_t launch_mask(const BwdArgs& a, bool causal, bool pow2, hipStream_t s) {
-  if constexpr (std::is_same_v<T, BF16>) {   // the scale fold is exact only in bfloat16
-    if (pow2) return causal ? launch_tiles<T, MASK, true, true>(a, s) : launch_tiles<T, MASK, false, true>(a, s);
-  }
-  return causal ? launch_tiles<T, MASK, true, false>(a, s) : launch_tiles<T, MASK, false, false>(a, s);
-}
-
-template <typename T>
-hipError_t launch_type(const BwdArgs& a, int mask_kind, bool causal, bool pow2, hipStream_t s) {
-  switch (mask_kind) {
-    case JVPATTN_MASK_NONE: return launch_mask<T, JVPATTN_MASK_NONE>(a, causal, pow2, s);
-    case JVPATTN_MASK_BOOL: return launch_mask<T, JVPATTN_MASK_BOOL>(a, causal, pow2, s);
-    case JVPATTN_MASK_BITS: return launch_mask<T, JVPATTN_MASK_BITS>(a, causal, pow2, s);
-    case kMaskAddT: return launch_mask<T, kMaskAddT>(a, causal, pow2, s);
-    default: return launch_mask<T, JVPATTN_MASK_ADDITIVE>(a, causal, pow2, s);
-  }
-}
+constexpr float kLog2e = 1.4426950408889634f;
 
 // Queue the reverse pass for arguments already validated; tmask: the
 // additive mask's tangent the forward carried, or NULL.
@@ -908,20 +75,14 @@ int bwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   a.cx = (additive || pow2) ? kLog2e : p->scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  if (sz.rows_q > 0) {
-    const int64_t nb = (sz.rows_q * 8 + kBThreads - 1) / kBThreads;   // eight lanes per row
-    if (nb > INT32_MAX) return JVPATTN_ERR_SHAPE;
-    if (p->dtype == JVPATTN_BF16)
-      hipLaunchKernelGGL((bwd_rows_kernel<BF16>), dim3(unsigned(nb)), dim3(kBThreads), 0, s, a, sz.rows_q);
-    else
-      hipLaunchKernelGGL((bwd_rows_kernel<F16>), dim3(unsigned(nb)), dim3(kBThreads), 0, s, a, sz.rows_q);
-  }
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess) {
-    const int kind = tmask ? kMaskAddT : p->mask_kind;
-    e = p->dtype == JVPATTN_BF16 ? launch_type<BF16>(a, kind, p->causal != 0, pow2, s)
-                                 : launch_type<F16>(a, kind, p->causal != 0, pow2, s);
-  }
+  const int kind = tmask ? kMaskAddT : p->mask_kind;
+  const jvpattn_dtype dt = static_cast<jvpattn_dtype>(p->dtype);
+  const bool c = p->causal != 0;
+  hipError_t e = p->d == 64 ? bwd_launch_part<kLaunchDkv, 64>(a, sz.rows_q, dt, kind, c, pow2, s)
+                            : bwd_launch_part<kLaunchDkv, 128>(a, sz.rows_q, dt, kind, c, pow2, s);
+  if (e == hipSuccess)
+    e = p->d == 64 ? bwd_launch_part<kLaunchDq, 64>(a, sz.rows_q, dt, kind, c, pow2, s)
+                   : bwd_launch_part<kLaunchDq, 128>(a, sz.rows_q, dt, kind, c, pow2, s);
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
     return JVPATTN_ERR_HIP;

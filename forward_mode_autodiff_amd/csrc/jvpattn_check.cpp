@@ -194,7 +194,7 @@ int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void*
   int rc = check_fwd(p, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, &sz);
   if (rc != JVPATTN_OK) return rc;
   if (p->dtype != JVPATTN_F16 && p->dtype != JVPATTN_BF16) return JVPATTN_ERR_DTYPE;
-  if (p->d != 64) return JVPATTN_ERR_HEADDIM;
+  if (p->d != 64 && p->d != 128) return JVPATTN_ERR_HEADDIM;
   const bool rows = sz.rows_q > 0, keys = sz.rows_k > 0;
   // go, gto may be NULL (zero cotangent); dtq, dtk, dtv may be NULL (not written)
   if (rows && (!tlse || !dq)) return JVPATTN_ERR_NULL;

@@ -184,7 +184,8 @@ __device__ inline v4i16 lds_read_tr(const char* p) {
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ inline void wait_vmcnt() {
-  static_assert(N == 0 || N == 2 || N == 4 || N == 5 || N == 6 || N == 8 || N == 10 || N == 12 || N == 16,
+  static_assert(N == 0 || N == 2 || N == 4 || N == 5 || N == 6 || N == 8 || N == 9 || N == 10 || N == 12 ||
+                    N == 16,
                 "unsupported count");
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
@@ -192,6 +193,7 @@ __device__ inline void wait_vmcnt() {
   if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
   if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
   if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
   if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");

@@ -150,6 +150,41 @@ def test_deterministic():
         assert np.array_equal(a[n], b[n]), n
 
 
+# ------------------------------------------------ d = 128
+# Its own kernel instances: the query side one block at a time (no overlap of
+# two blocks' products), the key side in two launches (dk, dtk, then dv, dtv).
+
+@pytest.mark.parametrize("std", [None, 1.0, 2.0])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_d128(dtype, causal, std):
+    check(I.Workload("d128", B=1, H=2, N=200, d=128, dtype=dtype, causal=causal, std=std, seed=61))
+
+
+@pytest.mark.parametrize("mask_kind", ["bool", "additive"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d128_masks(mask_kind, causal):
+    check(I.Workload("d128_mask", B=2, H=2, N=170, d=128, dtype="bf16", causal=causal, mask_kind=mask_kind,
+                     mask_heads=2 if mask_kind == "additive" else 1, keep=0.7, std=1.0, seed=62))
+
+
+@pytest.mark.parametrize("N", [1, 33, 129, 257])
+def test_d128_ragged_and_grouped(N):
+    check(I.Workload("d128_gqa", B=1, H=4, Hkv=2, N=N, Nk=N + 40, d=128, dtype="f16", causal=True, std=1.0,
+                     seed=63 + N))
+
+
+def test_d128_missing_tangents_and_mask_tangent():
+    w = I.Workload("d128_iso", B=1, H=2, N=150, d=128, dtype="bf16", std=1.0, seed=64)
+    check(w, tangents=("tq",))
+    check(w, tangents=("tv",))
+    wt = I.Workload("d128_tmask", B=1, H=2, N=150, d=128, dtype="f16", causal=True, mask_kind="additive",
+                    mask_heads=2, std=1.0, seed=65)
+    g = torch.Generator().manual_seed(66)
+    x = I.make_inputs(wt, cotangents=True)
+    check(wt, x=x, tmask=torch.randn(x["mask"].shape, generator=g).to(x["mask"].dtype))
+
+
 def test_errors_raise():
     x = I.make_inputs(W("err", N=64, dtype="bf16", seed=49), cotangents=True)
     d = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
