@@ -27,9 +27,9 @@ supplies tensors, the autograd graph and streams.
     Hessian-vector product of a loss is reverse mode over this pair.
 
 Inputs: q [B, H, N, d], k and v [B, Hkv, N, d] (Hkv dividing H: grouped
-key/value heads) CUDA tensors of one dtype (float16 / bfloat16 for the
-reverse pass, which supports d = 64 and 128; the forward also takes float32,
-and d = 32, 96 and 256 -- 256 in 16-bit types only). Masks as in ``jvpattn_fwd`` (bool: True = attend; additive: q's
+key/value heads) CUDA tensors of one dtype. The reverse pass takes float16
+/ bfloat16 with d = 64 or 128 and float32 with d = 64; the forward takes all
+three types with d = 32, 64, 96, 128, and d = 256 in the 16-bit types. Masks as in ``jvpattn_fwd`` (bool: True = attend; additive: q's
 dtype, no reverse-mode gradient).
 """
 from __future__ import annotations

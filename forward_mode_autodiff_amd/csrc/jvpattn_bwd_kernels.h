@@ -817,6 +817,442 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
 #endif
 }
 
+// ------------------------------------------------------------------ float32
+//
+// The reverse pass for float32 inputs (d = 64) on v_mfma_f32_32x32x2_f32, in
+// the float32 forward's style: each tile is staged through registers into
+// one LDS buffer per step (rows, and their transposes for the accumulating
+// products), and nothing is rounded below float32. Each product takes two
+// entries of its inner dimension per instruction: for the score-side products
+// lane half hlf supplies head-dim entry hlf*D/2 + i of product i; for the
+// accumulating products, product m contracts over the rows held in C
+// register m of each lane half, so the cotangents feed them as they are.
+
+template <int D>
+__device__ __forceinline__ void bwd_rows32_body(const BwdArgs& a, int64_t rows) {
+  constexpr int LPR = D / 4;   // lanes per row: one float4 of each tensor per lane
+  const int64_t t = int64_t(blockIdx.x) * kBThreads + threadIdx.x;
+  const int64_t row = t / LPR;
+  const int gi = threadIdx.x % LPR;
+  const bool live = row < rows;
+  const int64_t at = live ? row * LPR + gi : 0;
+  const f32x4 z{};
+  const f32x4 o = live ? static_cast<const f32x4*>(a.o)[at] : z;
+  const f32x4 to = live ? static_cast<const f32x4*>(a.to)[at] : z;
+  const f32x4 g = (live && a.go) ? static_cast<const f32x4*>(a.go)[at] : z;   // a NULL cotangent is zero
+  const f32x4 gd = (live && a.gto) ? static_cast<const f32x4*>(a.gto)[at] : z;
+  float r = 0.0f, go_o = 0.0f, gd_to = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r = fmaf(gd[e], o[e], r);
+    go_o = fmaf(g[e], o[e], go_o);
+    gd_to = fmaf(gd[e], to[e], gd_to);
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) {
+    r += __shfl_xor(r, m, LPR);
+    go_o += __shfl_xor(go_o, m, LPR);
+    gd_to += __shfl_xor(gd_to, m, LPR);
+  }
+  if (!live || gi != 0) return;
+  const float lse = a.lse[row], tl = a.tlse[row];
+  a.ws[WS_NEGL * a.ws_stride + row] = lse == -INFINITY ? -INFINITY : -lse * kLog2e;
+  a.ws[WS_TLSE * a.ws_stride + row] = tl;
+  a.ws[WS_R * a.ws_stride + row] = r;
+  a.ws[WS_DEL * a.ws_stride + row] = go_o + gd_to - tl * r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kBThreads) void bwd_rows32_kernel(BwdArgs a, int64_t rows) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  bwd_rows32_body<D>(a, rows);
+#endif
+}
+
+// One float4 of `p` (row `row`, granule g of D/4), zero past `n` rows or for a NULL tensor.
+template <int D>
+__device__ inline f32x4 row_granule(const float* p, int row, int n, int g) {
+  return (p && row < n) ? *reinterpret_cast<const f32x4*>(p + int64_t(row) * D + 4 * g) : f32x4{};
+}
+
+// Rows r0 .. r0+31 of up to four tensors into LDS: as rows (k32 layout) into
+// rows[i] and, where tr[i] is set, transposed (vt32 layout) as well.
+template <int D, int NTS>
+__device__ inline void stage32(const float* const (&src)[NTS], char* const (&rows)[NTS], char* const (&tr)[NTS],
+                               int r0, int n) {
+  using L = Tile32<D>;
+  for (int gi = threadIdx.x; gi < L::BN * L::GR; gi += kBThreads) {
+    const int row = gi / L::GR, g = gi % L::GR;
+#pragma unroll
+    for (int i = 0; i < NTS; ++i) {
+      const f32x4 x = row_granule<D>(src[i], r0 + row, n, g);
+      lds_store<f32x4>(rows[i], k32_off<D>(row, g), x);
+      if (tr[i]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lds_store<float>(tr[i], vt32_off(4 * g + e, row >> 2) + 4 * (row & 3), x[e]);
+      }
+    }
+  }
+}
+
+// dq kernel, float32: four waves of 32 queries, 32-key tiles of K, dK, V, dV
+// (rows) and K, dK (transposed); per tile and wave S^T, dS^T, X^T, D^T (the
+// forward's transposed layout: lane = query column, 16 keys per lane), the
+// cotangents per element, then dq^T += K^T Sbar^T + dK^T Sdbar^T and
+// dtq^T += K^T Sdbar^T.
+template <int D, int MASK, bool CAUSAL>
+__device__ __forceinline__ void bwd_dq32_body(const BwdArgs& a) {
+  using L = Tile32<D>;
+  constexpr int TB = L::TENSOR_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[6 * TB];
+  char* const sk = smem;
+  char* const stk = smem + TB;
+  char* const sv = smem + 2 * TB;
+  char* const stv = smem + 3 * TB;
+  char* const skt = smem + 4 * TB;
+  char* const stkt = smem + 5 * TB;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c32 = lane & 31;
+  const int hlf = lane >> 5;
+  const int qb = a.n_blk - 1 - int(blockIdx.x) / a.BH;   // heaviest first when causal
+  const int bh = int(blockIdx.x) % a.BH;
+  const int b = bh / a.H, h = bh % a.H;
+  const int q0 = qb * kBBlk;
+  const int qw0 = q0 + 32 * wave;
+  const int qi = qw0 + c32;
+  const bool wave_live = qw0 < a.Nq;
+
+  const int64_t qhead = int64_t(bh) * a.Nq * D, khead = int64_t(bh / a.grp) * a.Nk * D;
+  auto at = [](const void* p, int64_t off) { return p ? static_cast<const float*>(p) + off : nullptr; };
+  float qB[D / 2], tqB[D / 2], gB[D / 2], tgB[D / 2];
+  {
+    const float* src[4] = {at(a.q, qhead), at(a.tq, qhead), at(a.go, qhead), at(a.gto, qhead)};
+#pragma unroll
+    for (int i = 0; i < D / 2; i += 4) {
+      const int g = (hlf * (D / 2) + i) / 4;
+      const f32x4 x0 = row_granule<D>(src[0], qi, a.Nq, g), x1 = row_granule<D>(src[1], qi, a.Nq, g);
+      const f32x4 x2 = row_granule<D>(src[2], qi, a.Nq, g), x3 = row_granule<D>(src[3], qi, a.Nq, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qB[i + e] = x0[e];
+        tqB[i + e] = x1[e];
+        gB[i + e] = x2[e];
+        tgB[i + e] = x3[e];
+      }
+    }
+  }
+  float negl = -INFINITY, tl = 0.0f, rr = 0.0f, del = 0.0f;
+  if (qi < a.Nq) {
+    const int64_t ri = int64_t(bh) * a.Nq + qi;
+    negl = a.ws[WS_NEGL * a.ws_stride + ri];
+    tl = a.ws[WS_TLSE * a.ws_stride + ri];
+    rr = a.ws[WS_R * a.ws_stride + ri];
+    del = a.ws[WS_DEL * a.ws_stride + ri];
+  }
+
+  f32x16 accQ[L::NT], accTQ[L::NT];
+#pragma unroll
+  for (int t = 0; t < L::NT; ++t) {
+    accQ[t] = f32x16{};
+    accTQ[t] = f32x16{};
+  }
+  constexpr bool ADD = MASK == JVPATTN_MASK_ADDITIVE || MASK == kMaskAddT;
+  const Rsrc mr = mask_rsrc(a, b, h, mask_es<MASK>(4), nullptr, MASK == JVPATTN_MASK_BITS);
+  const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 4, a.tmask) : mr;
+
+  const int kv_end = CAUSAL ? min(a.Nk, q0 + kBBlk) : a.Nk;
+  const int n_tiles = (kv_end + L::BN - 1) / L::BN;
+  const float* const ksrc[4] = {at(a.k, khead), at(a.tk, khead), at(a.v, khead), at(a.tv, khead)};
+  char* const krows[4] = {sk, stk, sv, stv};
+  char* const ktr[4] = {skt, stkt, nullptr, nullptr};
+  for (int j = 0; j < n_tiles; ++j) {
+    const int k0 = j * L::BN;
+    stage32<D, 4>(ksrc, krows, ktr, k0, a.Nk);
+    __syncthreads();
+    if (wave_live && !(CAUSAL && k0 > qw0 + 31)) {
+      f32x16 s{}, sd{}, x{}, dm{};
+#pragma unroll
+      for (int i = 0; i < D / 2; i += 4) {
+        const int g = (hlf * (D / 2) + i) / 4;
+        const f32x4 ka = lds_load<f32x4>(sk, k32_off<D>(c32, g));
+        const f32x4 tka = lds_load<f32x4>(stk, k32_off<D>(c32, g));
+        const f32x4 va = lds_load<f32x4>(sv, k32_off<D>(c32, g));
+        const f32x4 tva = lds_load<f32x4>(stv, k32_off<D>(c32, g));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[e], qB[i + e], s, 0, 0, 0);
+          sd = __builtin_amdgcn_mfma_f32_32x32x2f32(tka[e], qB[i + e], sd, 0, 0, 0);
+          sd = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[e], tqB[i + e], sd, 0, 0, 0);
+          x = __builtin_amdgcn_mfma_f32_32x32x2f32(va[e], gB[i + e], x, 0, 0, 0);
+          x = __builtin_amdgcn_mfma_f32_32x32x2f32(tva[e], tgB[i + e], x, 0, 0, 0);
+          dm = __builtin_amdgcn_mfma_f32_32x32x2f32(va[e], tgB[i + e], dm, 0, 0, 0);
+        }
+      }
+      // masks: bool / bits / causal / ragged tail hide keys (-inf); additive: s = scale s + m
+      if constexpr (!ADD && MASK != JVPATTN_MASK_NONE) {
+        MaskVals<MASK> mk;
+        mask_load<MASK>(mk, a, mr, qi, k0, hlf);
+        mask_apply<F16, MASK, false>(s, mk, a.scale);
+      }
+      if ((CAUSAL && k0 + 31 > qw0) || (k0 + 32 > a.Nk)) hide_keys<CAUSAL>(s, a.Nk, qi, k0, hlf);
+      if constexpr (ADD) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + (r >> 2) * 8 + 4 * hlf + (r & 3);
+          const int off = (qi * int(a.msq) + key) * 4;
+          s[r] = fmaf(s[r], a.scale, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mr, off, 0, 0)));
+          if constexpr (MASK == kMaskAddT)   // the mask's tangent joins the score tangent (sd * scale = dS)
+            sd[r] = fmaf(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mtr, off, 0, 0)), a.inv_scale, sd[r]);
+        }
+      }
+      float sbar[16], sdbar[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const Cot c = cotangents(s[r], sd[r], x[r], dm[r], a.cx, a.scale, negl, tl, rr, del);
+        sbar[r] = c.sbar;
+        sdbar[r] = c.sdbar;
+      }
+#pragma unroll
+      for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int off = vt32_off(32 * t + c32, 2 * g + hlf);
+          const f32x4 kt = lds_load<f32x4>(skt, off);
+          const f32x4 tkt = lds_load<f32x4>(stkt, off);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = 4 * g + e;
+            accQ[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[e], sbar[m], accQ[t], 0, 0, 0);
+            accQ[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(tkt[e], sdbar[m], accQ[t], 0, 0, 0);
+            accTQ[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[e], sdbar[m], accTQ[t], 0, 0, 0);
+          }
+        }
+    }
+    __syncthreads();
+  }
+
+  if (qi < a.Nq) {
+    float* dq = static_cast<float*>(a.dq) + qhead + int64_t(qi) * D;
+    float* dtq = a.dtq ? static_cast<float*>(a.dtq) + qhead + int64_t(qi) * D : nullptr;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * t + 8 * g + 4 * hlf;
+        f32x4 u, w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u[e] = accQ[t][4 * g + e] * a.scale;
+          w[e] = accTQ[t][4 * g + e] * a.scale;
+        }
+        *reinterpret_cast<f32x4*>(dq + dd) = u;
+        if (dtq) *reinterpret_cast<f32x4*>(dtq + dd) = w;
+      }
+  }
+}
+
+template <int D, int MASK, bool CAUSAL>
+__global__ __launch_bounds__(kBThreads, 1) void bwd_dq32_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  bwd_dq32_body<D, MASK, CAUSAL>(a);
+#endif
+}
+
+// dkv kernel, float32: four waves of 32 keys, 32-query tiles of Q, dQ, G, Gd
+// (rows and transposed) plus the tile's four row statistics; lane = key
+// column, 16 queries per lane (row r of a lane's C registers is query
+// 8*(r/4) + 4*(lane/32) + r%4): S, dS, X, D, the cotangents, then
+// dk^T += Q^T Sbar + dQ^T Sdbar, dtk^T += Q^T Sdbar, dv^T += G^T P + Gd^T Pd,
+// dtv^T += Gd^T P. Grouped key/value heads sum over their query heads.
+template <int D, int MASK, bool CAUSAL>
+__device__ __forceinline__ void bwd_dkv32_body(const BwdArgs& a) {
+  using L = Tile32<D>;
+  constexpr int TB = L::TENSOR_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[8 * TB];
+  __shared__ float stats[4 * 32];
+  char* const sq = smem;
+  char* const stq = smem + TB;
+  char* const sg = smem + 2 * TB;
+  char* const stg = smem + 3 * TB;
+  char* const sqt = smem + 4 * TB;
+  char* const stqt = smem + 5 * TB;
+  char* const sgt = smem + 6 * TB;
+  char* const stgt = smem + 7 * TB;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c32 = lane & 31;
+  const int hlf = lane >> 5;
+  const int kb = int(blockIdx.x) / a.BHK;   // causal: early key blocks see the most queries
+  const int bhk = int(blockIdx.x) % a.BHK;
+  const int b = bhk * a.grp / a.H;
+  const int k0 = kb * kBBlk;
+  const int kw0 = k0 + 32 * wave;
+  const int kj = kw0 + c32;
+  const bool wave_live = kw0 < a.Nk;
+
+  const int64_t khead = int64_t(bhk) * a.Nk * D;
+  auto at = [](const void* p, int64_t off) { return p ? static_cast<const float*>(p) + off : nullptr; };
+  float kB[D / 2], tkB[D / 2], vB[D / 2], tvB[D / 2];
+  {
+    const float* src[4] = {at(a.k, khead), at(a.tk, khead), at(a.v, khead), at(a.tv, khead)};
+#pragma unroll
+    for (int i = 0; i < D / 2; i += 4) {
+      const int g = (hlf * (D / 2) + i) / 4;
+      const f32x4 x0 = row_granule<D>(src[0], kj, a.Nk, g), x1 = row_granule<D>(src[1], kj, a.Nk, g);
+      const f32x4 x2 = row_granule<D>(src[2], kj, a.Nk, g), x3 = row_granule<D>(src[3], kj, a.Nk, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kB[i + e] = x0[e];
+        tkB[i + e] = x1[e];
+        vB[i + e] = x2[e];
+        tvB[i + e] = x3[e];
+      }
+    }
+  }
+  f32x16 accK[L::NT], accTK[L::NT], accV[L::NT], accTV[L::NT];
+#pragma unroll
+  for (int t = 0; t < L::NT; ++t) {
+    accK[t] = f32x16{};
+    accTK[t] = f32x16{};
+    accV[t] = f32x16{};
+    accTV[t] = f32x16{};
+  }
+  constexpr bool ADD = MASK == JVPATTN_MASK_ADDITIVE || MASK == kMaskAddT;
+
+  for (int gq = 0; gq < a.grp; ++gq) {
+    const int bh = bhk * a.grp + gq;
+    const int h = bh % a.H;
+    const int64_t qhead = int64_t(bh) * a.Nq * D;
+    const Rsrc mr = mask_rsrc(a, b, h, mask_es<MASK>(4), nullptr, MASK == JVPATTN_MASK_BITS);
+    const Rsrc mtr = MASK == kMaskAddT ? mask_rsrc(a, b, h, 4, a.tmask) : mr;
+    const int n_qt = (a.Nq + 31) / 32;
+    const int t_begin = CAUSAL ? min(n_qt, k0 >> 5) : 0;   // queries before the block see none of its keys
+    const int first = !wave_live ? n_qt : (CAUSAL ? max(t_begin, kw0 >> 5) : 0);
+    const float* const qsrc[4] = {at(a.q, qhead), at(a.tq, qhead), at(a.go, qhead), at(a.gto, qhead)};
+    char* const qrows[4] = {sq, stq, sg, stg};
+    char* const qtr[4] = {sqt, stqt, sgt, stgt};
+    for (int t = t_begin; t < n_qt; ++t) {
+      const int i0 = t * 32;
+      stage32<D, 4>(qsrc, qrows, qtr, i0, a.Nq);
+      if (tid < 128) {   // statistic tid/32 of row i0 + tid%32 (rows past Nq: 0, never used)
+        const int row = i0 + (tid & 31);
+        stats[tid] = row < a.Nq ? a.ws[(tid >> 5) * a.ws_stride + int64_t(bh) * a.Nq + row] : 0.0f;
+      }
+      __syncthreads();
+      if (t >= first) {
+        f32x16 s{}, sd{}, x{}, dm{};
+#pragma unroll
+        for (int i = 0; i < D / 2; i += 4) {
+          const int g = (hlf * (D / 2) + i) / 4;
+          const f32x4 qa = lds_load<f32x4>(sq, k32_off<D>(c32, g));
+          const f32x4 tqa = lds_load<f32x4>(stq, k32_off<D>(c32, g));
+          const f32x4 ga = lds_load<f32x4>(sg, k32_off<D>(c32, g));
+          const f32x4 tga = lds_load<f32x4>(stg, k32_off<D>(c32, g));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[e], kB[i + e], s, 0, 0, 0);
+            sd = __builtin_amdgcn_mfma_f32_32x32x2f32(tqa[e], kB[i + e], sd, 0, 0, 0);
+            sd = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[e], tkB[i + e], sd, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[e], vB[i + e], x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_32x32x2f32(tga[e], tvB[i + e], x, 0, 0, 0);
+            dm = __builtin_amdgcn_mfma_f32_32x32x2f32(tga[e], vB[i + e], dm, 0, 0, 0);
+          }
+        }
+        // element (query i0 + 8(r/4) + 4 hlf + r%4, key kj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = i0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
+          if constexpr (MASK == JVPATTN_MASK_BITS) {
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(mr, (qrow * int(a.msq) + (kj >> 5)) * 4, 0, 0);
+            if (((w >> (kj & 31)) & 1u) == 0u) s[r] = -INFINITY;
+          } else if constexpr (MASK == JVPATTN_MASK_BOOL) {
+            if (__builtin_amdgcn_raw_buffer_load_b8(mr, qrow * int(a.msq) + kj, 0, 0) == 0) s[r] = -INFINITY;
+          } else if constexpr (ADD) {
+            const int off = (qrow * int(a.msq) + kj) * 4;
+            s[r] = fmaf(s[r], a.scale, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mr, off, 0, 0)));
+            if constexpr (MASK == kMaskAddT)
+              sd[r] = fmaf(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mtr, off, 0, 0)), a.inv_scale,
+                           sd[r]);
+          }
+          bool hide = qrow >= a.Nq || kj >= a.Nk;
+          if constexpr (CAUSAL) hide = hide || kj > qrow;
+          if (hide) s[r] = -INFINITY;
+        }
+        float p[16], pd[16], sbar[16], sdbar[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * hlf + (r & 3);
+          const Cot c = cotangents(s[r], sd[r], x[r], dm[r], a.cx, a.scale, stats[WS_NEGL * 32 + row],
+                                   stats[WS_TLSE * 32 + row], stats[WS_R * 32 + row], stats[WS_DEL * 32 + row]);
+          p[r] = c.p;
+          pd[r] = c.pd;
+          sbar[r] = c.sbar;
+          sdbar[r] = c.sdbar;
+        }
+#pragma unroll
+        for (int tt = 0; tt < L::NT; ++tt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int off = vt32_off(32 * tt + c32, 2 * g + hlf);
+            const f32x4 qt = lds_load<f32x4>(sqt, off);
+            const f32x4 tqt = lds_load<f32x4>(stqt, off);
+            const f32x4 gt = lds_load<f32x4>(sgt, off);
+            const f32x4 tgt = lds_load<f32x4>(stgt, off);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int m = 4 * g + e;
+              accK[tt] = __builtin_amdgcn_mfma_f32_32x32x2f32(qt[e], sbar[m], accK[tt], 0, 0, 0);
+              accK[tt] = __builtin_amdgcn_mfma_f32_32x32x2f32(tqt[e], sdbar[m], accK[tt], 0, 0, 0);
+              accTK[tt] = __builtin_amdgcn_mfma_f32_32x32x2f32(qt[e], sdbar[m], accTK[tt], 0, 0, 0);
+              accV[tt] = __builtin_amdgcn_mfma_f32_32x32x2f32(gt[e], p[m], accV[tt], 0, 0, 0);
+              accV[tt] = __builtin_amdgcn_mfma_f32_32x32x2f32(tgt[e], pd[m], accV[tt], 0, 0, 0);
+              accTV[tt] = __builtin_amdgcn_mfma_f32_32x32x2f32(tgt[e], p[m], accTV[tt], 0, 0, 0);
+            }
+          }
+      }
+      __syncthreads();
+    }
+  }
+
+  if (kj < a.Nk) {
+    const int64_t base = khead + int64_t(kj) * D;
+    float* dk = static_cast<float*>(a.dk) + base;
+    float* dv = static_cast<float*>(a.dv) + base;
+    float* dtk = a.dtk ? static_cast<float*>(a.dtk) + base : nullptr;
+    float* dtv = a.dtv ? static_cast<float*>(a.dtv) + base : nullptr;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * t + 8 * g + 4 * hlf;
+        f32x4 uk, utk, uv, utv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uk[e] = accK[t][4 * g + e] * a.scale;
+          utk[e] = accTK[t][4 * g + e] * a.scale;
+          uv[e] = accV[t][4 * g + e];
+          utv[e] = accTV[t][4 * g + e];
+        }
+        *reinterpret_cast<f32x4*>(dk + dd) = uk;
+        *reinterpret_cast<f32x4*>(dv + dd) = uv;
+        if (dtk) *reinterpret_cast<f32x4*>(dtk + dd) = utk;
+        if (dtv) *reinterpret_cast<f32x4*>(dtv + dd) = utv;
+      }
+  }
+}
+
+template <int D, int MASK, bool CAUSAL>
+__global__ __launch_bounds__(kBThreads, 1) void bwd_dkv32_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  bwd_dkv32_body<D, MASK, CAUSAL>(a);
+#endif
+}
+
 // ------------------------------------------------------------------ launch
 
 // WHICH: kLaunchDkv (the rows kernel, then dkv) or kLaunchDq.
@@ -870,9 +1306,61 @@ hipError_t launch_type(const BwdArgs& a, int mask_kind, bool causal, bool pow2, 
 
 }  // namespace
 
+// float32 (d = 64): the same sides with the float32 kernels.
+template <int WHICH, int D, int MASK, bool CAUSAL>
+hipError_t launch_tiles32(BwdArgs a, hipStream_t s) {
+  const int64_t nkb = (a.Nk + kBBlk - 1) / kBBlk, nqb = (a.Nq + kBBlk - 1) / kBBlk;
+  if (nkb * a.BHK > INT32_MAX || nqb * a.BH > INT32_MAX) return hipErrorInvalidValue;
+  if constexpr (WHICH == kLaunchDkv) {
+    if (nkb == 0 || a.BHK == 0) return hipSuccess;
+    a.n_blk = static_cast<int>(nkb);
+    hipLaunchKernelGGL((bwd_dkv32_kernel<D, MASK, CAUSAL>), dim3(unsigned(nkb * a.BHK)), dim3(kBThreads), 0, s, a);
+  }
+  if constexpr (WHICH == kLaunchDq) {
+    if (nqb == 0 || a.BH == 0) return hipSuccess;
+    a.n_blk = static_cast<int>(nqb);
+    hipLaunchKernelGGL((bwd_dq32_kernel<D, MASK, CAUSAL>), dim3(unsigned(nqb * a.BH)), dim3(kBThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int WHICH, int D>
+hipError_t launch_type32(const BwdArgs& a, int mask_kind, bool causal, hipStream_t s) {
+  switch (mask_kind) {
+    case JVPATTN_MASK_NONE:
+      return causal ? launch_tiles32<WHICH, D, JVPATTN_MASK_NONE, true>(a, s)
+                    : launch_tiles32<WHICH, D, JVPATTN_MASK_NONE, false>(a, s);
+    case JVPATTN_MASK_BOOL:
+      return causal ? launch_tiles32<WHICH, D, JVPATTN_MASK_BOOL, true>(a, s)
+                    : launch_tiles32<WHICH, D, JVPATTN_MASK_BOOL, false>(a, s);
+    case JVPATTN_MASK_BITS:
+      return causal ? launch_tiles32<WHICH, D, JVPATTN_MASK_BITS, true>(a, s)
+                    : launch_tiles32<WHICH, D, JVPATTN_MASK_BITS, false>(a, s);
+    case kMaskAddT:
+      return causal ? launch_tiles32<WHICH, D, kMaskAddT, true>(a, s) : launch_tiles32<WHICH, D, kMaskAddT, false>(a, s);
+    default:
+      return causal ? launch_tiles32<WHICH, D, JVPATTN_MASK_ADDITIVE, true>(a, s)
+                    : launch_tiles32<WHICH, D, JVPATTN_MASK_ADDITIVE, false>(a, s);
+  }
+}
+
 template <int WHICH, int D>
 hipError_t bwd_launch_part(const BwdArgs& a, int64_t rows_q, jvpattn_dtype dtype, int mask_kind, bool causal,
                            bool pow2, hipStream_t s) {
+  if (dtype == JVPATTN_F32) {
+    if constexpr (D == 64) {
+      if (WHICH == kLaunchDkv && rows_q > 0) {
+        const int64_t nb = (rows_q * (D / 4) + kBThreads - 1) / kBThreads;   // d/4 lanes per row
+        if (nb > INT32_MAX) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((bwd_rows32_kernel<D>), dim3(unsigned(nb)), dim3(kBThreads), 0, s, a, rows_q);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      return launch_type32<WHICH, D>(a, mask_kind, causal, s);
+    } else {
+      return hipErrorInvalidValue;   // the validator admits float32 at d = 64 only
+    }
+  }
   if (WHICH == kLaunchDkv && rows_q > 0) {   // the rows kernel builds with the key side
     const int64_t nb = (rows_q * (D / 8) + kBThreads - 1) / kBThreads;   // d/8 lanes per row
     if (nb > INT32_MAX) return hipErrorInvalidValue;

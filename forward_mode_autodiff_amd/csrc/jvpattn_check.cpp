@@ -193,8 +193,9 @@ int check_bwd(const jvpattn_params* p, const void* q, const void* k, const void*
   // from q..mask).
   int rc = check_fwd(p, q, k, v, tq, tk, tv, mask, o, to, lse, tlse, &sz);
   if (rc != JVPATTN_OK) return rc;
-  if (p->dtype != JVPATTN_F16 && p->dtype != JVPATTN_BF16) return JVPATTN_ERR_DTYPE;
-  if (p->d != 64 && p->d != 128) return JVPATTN_ERR_HEADDIM;
+  // float16 / bfloat16 with d = 64 or 128, float32 with d = 64
+  if (p->dtype != JVPATTN_F16 && p->dtype != JVPATTN_BF16 && p->dtype != JVPATTN_F32) return JVPATTN_ERR_DTYPE;
+  if (p->d != 64 && (p->d != 128 || p->dtype == JVPATTN_F32)) return JVPATTN_ERR_HEADDIM;
   const bool rows = sz.rows_q > 0, keys = sz.rows_k > 0;
   // go, gto may be NULL (zero cotangent); dtq, dtk, dtv may be NULL (not written)
   if (rows && (!tlse || !dq)) return JVPATTN_ERR_NULL;

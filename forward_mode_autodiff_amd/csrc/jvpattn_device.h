@@ -148,6 +148,33 @@ struct Tile16 {
   static_assert(LOADS * 16 * kTileThreads == TENSOR_BYTES, "tile must split evenly over the workgroup");
 };
 
+// Bytes per mask element: uint8 for bool, 32-bit words for bit-packed masks,
+// else the additive values (value_bytes).
+template <int MASK>
+constexpr int mask_es(int value_bytes) {
+  return MASK == JVPATTN_MASK_BOOL ? 1 : MASK == JVPATTN_MASK_BITS ? 4 : value_bytes;
+}
+
+// float32 tiles of 32 rows (keys, or queries in the reverse pass): rows as
+// 16-byte granules XOR-swizzled by row (the A operands of the score-like
+// products), and transposed tiles whose row is a head-dim index holding the
+// 32 rows' values, 4 per granule (the A operands of the accumulating products).
+template <int D>
+struct Tile32 {
+  static constexpr int BN = 32;                 // rows per LDS tile
+  static constexpr int NT = D / 32;
+  static constexpr int GR = D / 4;              // 16-byte granules per row
+  static constexpr int TENSOR_BYTES = BN * D * 4;
+  static constexpr int BUF_BYTES = 4 * TENSOR_BYTES;
+};
+
+template <int D>
+__device__ inline int k32_off(int row, int g) {
+  return row * (4 * D) + ((g ^ (row & 7)) << 4);
+}
+// transposed tile: row = head-dim index, 32 values (128 bytes, 8 granules)
+__device__ inline int vt32_off(int dd, int g) { return dd * 128 + ((g ^ (dd & 7)) << 4); }
+
 // LDS tiles (K, dK, V, dV) are row = key, 2*D bytes per row, with the 16-byte
 // granules of a row XOR-swizzled by swz(row). They are filled by direct
 // global->LDS loads: load slot p (16 bytes) of a tile lands at byte 16*p,

@@ -252,12 +252,6 @@ __device__ inline void key_tiles(const FwdArgs& a, Rsrc mr, int* red, int& t_lo,
   }
 }
 
-// Bytes per mask element: uint8 for bool, 32-bit words for bit-packed masks,
-// else the additive values (value_bytes).
-template <int MASK>
-constexpr int mask_es(int value_bytes) {
-  return MASK == JVPATTN_MASK_BOOL ? 1 : MASK == JVPATTN_MASK_BITS ? 4 : value_bytes;
-}
 
 // Per-row softmax state for one lane (both lanes of a query column hold the same m).
 struct RowState {
@@ -1514,21 +1508,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd16w_kernel(FwdArgs a) {
 // product i; for the value products, product m contracts over the keys held
 // in C register m of each lane half, so P^T and (P dS)^T are used as they are.
 
-template <int D>
-struct Tile32 {
-  static constexpr int BN = 32;                 // keys per LDS tile
-  static constexpr int NT = D / 32;
-  static constexpr int GR = D / 4;              // 16-byte granules per K row
-  static constexpr int TENSOR_BYTES = BN * D * 4;
-  static constexpr int BUF_BYTES = 4 * TENSOR_BYTES;
-};
-
-template <int D>
-__device__ inline int k32_off(int row, int g) {
-  return row * (4 * D) + ((g ^ (row & 7)) << 4);
-}
-// V^T row = head-dim index, 32 keys (128 bytes, 8 granules).
-__device__ inline int vt32_off(int dd, int g) { return dd * 128 + ((g ^ (dd & 7)) << 4); }
 
 template <int D, int MASK, bool CAUSAL>
 __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {

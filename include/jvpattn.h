@@ -186,14 +186,15 @@ int jvpattn_check_fwd_tmask(const jvpattn_params* params,
  *                      that may run at the same time need separate
  *                      workspaces.
  * Outputs are fully overwritten and must not overlap an input, each other
- * or the workspace. Supported: float16 and bfloat16 with d = 64 or 128
- * (other element types return JVPATTN_ERR_DTYPE, other d
- * JVPATTN_ERR_HEADDIM, before any work is queued), every mask kind, grouped
- * key/value heads.
- * Arithmetic: products on the matrix cores with float32 accumulation; the
- * recomputed softmax weights, their tangents and the score cotangents are
- * rounded to the input type before the products that consume them; results
- * are rounded to nearest even. */
+ * or the workspace. Supported: float16 and bfloat16 with d = 64 or 128,
+ * float32 with d = 64 (other element types return JVPATTN_ERR_DTYPE, other
+ * d JVPATTN_ERR_HEADDIM, before any work is queued), every mask kind,
+ * grouped key/value heads.
+ * Arithmetic: products on the matrix cores with float32 accumulation; for
+ * 16-bit inputs the recomputed softmax weights, their tangents and the score
+ * cotangents are rounded to the input type before the products that consume
+ * them (float32: float32 products throughout); results are rounded to
+ * nearest even. */
 
 /* Bytes of workspace jvpattn_bwd needs for these parameters, or a negative
  * JVPATTN_ERR_* code if the parameters are invalid for it. */

@@ -277,6 +277,8 @@ def test_bwd_workspace_size():
 
 @needs_lib
 def test_check_bwd_accepts_valid_calls():
+    p = good_params(dtype=J.JVPATTN_F32)
+    assert call_bwd(p, bwd_ptrs(p, 4)) == 0
     for dt in (J.JVPATTN_F16, J.JVPATTN_BF16):
         p = good_params(dtype=dt, d=128)
         assert call_bwd(p, bwd_ptrs(p)) == 0
@@ -296,14 +298,18 @@ def test_check_bwd_accepts_valid_calls():
 
 @needs_lib
 @pytest.mark.parametrize("case,code", [
-    ("f32", -3), ("d96", -4), ("d256", -4), ("dq_null", -1), ("tlse_null", -1), ("dv_null", -1), ("dq_misaligned", -6),
+    ("dtype", -3), ("f32_d128", -4), ("d96", -4), ("d256", -4), ("dq_null", -1), ("tlse_null", -1), ("dv_null", -1), ("dq_misaligned", -6),
     ("ws_null", -10), ("ws_small", -10), ("ws_misaligned", -10), ("ws_overlaps_go", -10), ("ws_overlaps_dk", -10),
     ("dq_is_q", -8), ("dk_overlaps_dv", -8), ("dtv_overlaps_gto", -8), ("q_null", -1), ("scale_nan", -7),
 ])
 def test_check_bwd_rejects(case, code):
     p = good_params()
-    if case == "f32":
-        p.dtype = J.JVPATTN_F32
+    if case == "dtype":
+        p.dtype = 7
+        assert call_bwd(p, bwd_ptrs(p)) == code
+        return
+    if case == "f32_d128":
+        p.dtype, p.d = J.JVPATTN_F32, 128
         assert call_bwd(p, bwd_ptrs(p, 4)) == code
         return
     if case in ("d96", "d256"):

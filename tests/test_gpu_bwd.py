@@ -185,6 +185,52 @@ def test_d128_missing_tangents_and_mask_tangent():
     check(wt, x=x, tmask=torch.randn(x["mask"].shape, generator=g).to(x["mask"].dtype))
 
 
+# ------------------------------------------------ float32 (d = 64)
+# Its own kernels: float32 products throughout, no rounding of the weights or
+# score cotangents (bar rho = 1e-4 of each element's term magnitude).
+
+@pytest.mark.parametrize("std", [None, 1.0, 2.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32(causal, std):
+    check(I.Workload("f32", B=1, H=2, N=200, d=64, dtype="f32", causal=causal, std=std, seed=71))
+
+
+@pytest.mark.parametrize("mask_kind,layout", [("bool", None), ("additive", None), ("bool", "pad_right")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_masks(mask_kind, layout, causal):
+    kw = {"mask_layout": layout} if layout else {"keep": 0.7}
+    check(I.Workload("f32_mask", B=2, H=2, N=170, d=64, dtype="f32", causal=causal, mask_kind=mask_kind,
+                     mask_heads=2 if mask_kind == "additive" else 1, std=1.0, seed=72, **kw))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_bit_packed_mask(causal):
+    from forward_mode_autodiff_amd.jvpattn import pack_mask_bits
+    w = I.Workload("f32_bits", B=2, H=2, N=150, d=64, dtype="f32", causal=causal, mask_kind="bool", keep=0.7,
+                   std=1.0, seed=73)
+    x = I.make_inputs(w, cotangents=True)
+    got = gpu_bwd(dict(x, mask=pack_mask_bits(x["mask"])), w, mask_kind="bits")
+    bad = bwd_failures(got, reference(x, w), magnitudes(x, w), w.dtype)
+    assert not bad, "; ".join(bad)
+
+
+@pytest.mark.parametrize("N", [1, 33, 129, 257])
+def test_f32_ragged_rectangular_grouped(N):
+    check(I.Workload("f32_gqa", B=1, H=4, Hkv=2, N=N, Nk=N + 40, d=64, dtype="f32", causal=True, std=1.0,
+                     seed=74 + N))
+
+
+def test_f32_missing_tangents_and_mask_tangent():
+    w = I.Workload("f32_iso", B=1, H=2, N=150, d=64, dtype="f32", std=1.0, seed=75)
+    check(w, tangents=("tk",))
+    check(w, tangents=())
+    wt = I.Workload("f32_tmask", B=1, H=2, N=150, d=64, dtype="f32", causal=True, mask_kind="additive",
+                    mask_heads=2, std=1.0, seed=76)
+    g = torch.Generator().manual_seed(77)
+    x = I.make_inputs(wt, cotangents=True)
+    check(wt, x=x, tmask=torch.randn(x["mask"].shape, generator=g).to(x["mask"].dtype))
+
+
 def test_errors_raise():
     x = I.make_inputs(W("err", N=64, dtype="bf16", seed=49), cotangents=True)
     d = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
