@@ -42,6 +42,18 @@ def test_noalloc_matches_workspace_call_twice_shrinking():
         assert not bad, (w.name, bad)
 
 
+def test_noalloc_other_head_dims_and_float32():
+    """The same entry on the d = 128 and float32 kernels (two calls, the second smaller)."""
+    for w in (I.Workload("noalloc_d128", B=2, H=2, N=300, d=128, dtype="bf16", causal=True, std=1.0, seed=73),
+              I.Workload("noalloc_f32", B=1, H=2, N=130, d=64, dtype="f32", std=1.0, seed=74)):
+        x, a, b = both(w)
+        for n, u, t in zip(BWD_NAMES, a, b):
+            assert torch.equal(u, t), (w.name, n)
+        got = {n: u.double().cpu().numpy() for n, u in zip(BWD_NAMES, a)}
+        bad = bwd_failures(got, reference(x, w), magnitudes(x, w), w.dtype)
+        assert not bad, (w.name, bad)
+
+
 def test_noalloc_rejects_more_rows_than_its_scratch():
     w = I.Workload("noalloc_huge", B=1, H=1, N=1, d=64, dtype="bf16", seed=72)
     x = I.make_inputs(w, cotangents=True)
