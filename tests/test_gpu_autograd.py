@@ -127,3 +127,31 @@ def test_torch_func_jvp_route(causal):
     errs = bwd_errors(dict(ref, dq=f64(grads[0]), dk=f64(grads[1]), dv=f64(grads[2])), ref, M, "bf16")
     for n in ("dq", "dk", "dv"):
         assert errs[n][0] <= 1.0, (n, errs[n])
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f32")])
+def test_attention_reverse_mode_other_dims_and_float32(d, dtype):
+    """attention() backward at d = 128 and in float32 equals the direct jvpattn_bwd call."""
+    w = I.Workload("ag_dims", B=1, H=2, N=150, d=d, dtype=dtype, causal=True, std=1.0, seed=67)
+    x = I.make_inputs(w, cotangents=True)
+    dd = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
+    q, k, v = (dd[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    attention(q, k, v, is_causal=True).backward(dd["do"])
+    o, to, lse, tlse = jvpattn_fwd(dd["q"], dd["k"], dd["v"], causal=True)
+    g = jvpattn_bwd(dd["q"], dd["k"], dd["v"], None, None, None, o, to, lse, tlse, dd["do"], None, causal=True)
+    torch.cuda.synchronize()
+    for t, r in zip((q, k, v), g[:3]):
+        assert torch.equal(t.grad, r)
+
+
+@pytest.mark.parametrize("d", [96, 256])
+def test_torch_func_jvp_other_dims(d):
+    """torch.func.jvp around attention() at d = 96 / 256 equals the direct forward."""
+    w = I.Workload("ag_jvp_dims", B=1, H=2, N=150, d=d, dtype="bf16", std=1.0, seed=68)
+    x = I.make_inputs(w)
+    dd = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
+    o, to = torch.func.jvp(lambda a, b, c: attention(a, b, c), (dd["q"], dd["k"], dd["v"]),
+                           (dd["tq"], dd["tk"], dd["tv"]))
+    o2, to2, _, _ = jvpattn_fwd(dd["q"], dd["k"], dd["v"], dd["tq"], dd["tk"], dd["tv"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(to, to2)

@@ -251,6 +251,39 @@ def test_head_dim_f16_large_score_tangents(d, causal):
     assert np.all(np.isfinite(got["to"].numpy()))
 
 
+@pytest.mark.parametrize("layout,extra,kind,causal", [
+    ("sliding", {"window": 70}, "bool", False),
+    ("blockdiag", {"block": 96}, "bits", True),
+    ("blockdiag", {"block": 128}, "additive", False),
+    ("pad_right", None, "bool", True),
+    ("window", None, "additive", False),
+])
+@pytest.mark.parametrize("d", [96, 256])
+def test_head_dim_mask_early_outs(d, layout, extra, kind, causal):
+    """Per-row (sliding, block-diagonal) and query-shared (key padding, window) masks at d = 96 / 256:
+    the early-outs on and off give the same bits, and the oracle's values."""
+    from forward_mode_autodiff_amd.jvpattn import pack_mask_bits
+    w = I.Workload(f"d{d}_mask_{layout}", B=2, H=2, N=300, d=d, dtype="bf16", causal=causal,
+                   mask_kind="bool" if kind == "bits" else kind, mask_layout=layout, std=1.0, seed=37 + d,
+                   **({"extra": extra} if extra else {}))
+    x = I.make_inputs(w)
+    dd = to_dev(x)
+    m = pack_mask_bits(dd["mask"]) if kind == "bits" else dd["mask"]
+    runs = []
+    for skip in (True, False):
+        jvpattn_fwd_set_algo(key_range=skip)
+        out = jvpattn_fwd(dd["q"], dd["k"], dd["v"], dd["tq"], dd["tk"], dd["tv"], mask=m, causal=causal,
+                          mask_kind="bits" if kind == "bits" else None)
+        torch.cuda.synchronize()
+        runs.append(tuple(t.clone() for t in out))
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+    o, to, lse, tlse = runs[0]
+    got = {"o": o.float().cpu(), "to": to.float().cpu(), "lse": lse.cpu(), "tlse": tlse.cpu()}
+    assert_parity(got, oracle_run(x, "bool" if kind == "bits" else kind, causal), "bf16", w.name,
+                  spec_spread=False)
+
+
 # ------------------------------------------------ edges
 
 @pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 130, 255, 256, 257, 511, 513])
