@@ -208,23 +208,22 @@ __device__ inline v4i16 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)to_lds(p));
 }
 
-// Wait until at most N vector-memory operations of this wave are outstanding.
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (loads and stores retire in issue order on this target, so this means all
+// but the N most recent have completed).
 template <int N>
 __device__ inline void wait_vmcnt() {
-  static_assert(N == 0 || N == 2 || N == 4 || N == 5 || N == 6 || N == 8 || N == 9 || N == 10 || N == 12 ||
-                    N == 16,
-                "unsupported count");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-  if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-  if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit count");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
 }
+
+// Buffer stores: offsets at or past the record count are dropped, so a
+// wave can issue a fixed number of stores whatever its rows and columns.
+__device__ inline void st64(Rsrc r, int off, uint2 v) {
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(v2u{v.x, v.y}, r, off, 0, 0);
+}
+__device__ inline void st32(Rsrc r, int off, uint32_t v) { __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0); }
 
 // Workgroup barrier for the LDS ring. The caller has already waited for its
 // own direct-to-LDS loads (wait_vmcnt); this waits for its LDS reads and

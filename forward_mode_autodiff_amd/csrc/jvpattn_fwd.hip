@@ -20,7 +20,21 @@ constexpr int kPPBM = 256;    // query rows per ping-pong workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Process-wide algorithm selection (jvpattn_fwd_set_algo); -1 = automatic.
-std::atomic<int> g_algo_kernel{-1}, g_algo_order{-1}, g_algo_key_range{-1};
+std::atomic<int> g_algo_kernel{-1}, g_algo_order{-1}, g_algo_key_range{-1}, g_max_workgroups{0};
+
+// Compute units of the current device (queried once per device), or 0.
+int cu_count() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cus[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) n = 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // Queue the forward for arguments already validated (sizes from the check).
 // tmask: the additive mask's tangent, or NULL.
@@ -113,13 +127,26 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   // wave: there the scan, one memory round trip before each workgroup's first
   // tile, costs more than it saves on a dense mask.
   a.row_range = mask != nullptr && p->mask_stride_q != 0 && mask_skips && pp;
-  const dim3 grid(static_cast<unsigned>(blocks));
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   const int kernel = pp ? kFwdPingPong : split == 2 ? kFwdSplit64 : split == 1 ? kFwdSplit : kFwdWG4;
   const bool c = p->causal != 0;
   int mk = p->mask_kind;
   if (mk == JVPATTN_MASK_ADDITIVE && tmask) mk = kMaskAddT;
+  // The mask-free 4-wave kernel at 128 columns (16-bit, d = 96 / 128, scale
+  // not a power of two) walks its row blocks with at most as many workgroups
+  // as the chip holds at once (one per CU), a multiple of 8 so each keeps its
+  // XCD: a block's loads then overlap the previous block's epilogue and
+  // stores. With one block per workgroup both latencies are exposed.
+  a.n_items = static_cast<int>(blocks);
+  int64_t wgs = blocks;
+  if (kernel == kFwdWG4 && mk == JVPATTN_MASK_NONE && p->dtype != JVPATTN_F32 && dphys == 128 && !pow2) {
+    const int forced = g_max_workgroups.load(std::memory_order_relaxed);
+    int64_t cap = forced > 0 ? forced : int64_t(cu_count());
+    if (cap >= 8) cap &= ~int64_t(7);
+    if (cap > 0 && cap < blocks) wgs = cap;
+  }
+  const dim3 grid(static_cast<unsigned>(wgs));
   hipError_t e;
   switch (mk) {
     case JVPATTN_MASK_NONE:
@@ -171,6 +198,13 @@ extern "C" int jvpattn_fwd_tmask(const jvpattn_params* p, const void* q, const v
   const int rc = check_fwd_tmask(p, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, &sz);
   if (rc != JVPATTN_OK) return rc;
   return fwd_launch(p, sz, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, stream);
+}
+
+extern "C" int jvpattn_fwd_set_workgroups(int max_workgroups) {
+  using namespace jvpattn;
+  if (max_workgroups < 0) return JVPATTN_ERR_ARG;
+  g_max_workgroups.store(max_workgroups, std::memory_order_relaxed);
+  return JVPATTN_OK;
 }
 
 extern "C" int jvpattn_fwd_set_algo(int kernel, int order, int key_range) {

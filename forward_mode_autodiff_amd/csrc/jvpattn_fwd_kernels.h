@@ -69,15 +69,15 @@ static_assert(kThreads == kTileThreads, "LDS tiles are laid out for the 4-wave k
 // With grouped key/value heads (xgrp > 1, B*H a multiple of 8*xgrp) the heads
 // are then permuted so that all query heads sharing a key/value head also
 // land on one XCD.
-__device__ inline void block_coords(const FwdArgs& a, int& qb, int& bh) {
+__device__ inline void block_coords(const FwdArgs& a, int x, int& qb, int& bh) {
   int r;
   if (a.head_major) {
-    const int x = int(blockIdx.x), slot = x >> 3;
+    const int slot = x >> 3;
     qb = a.n_qblk - 1 - slot % a.n_qblk;
     r = (slot / a.n_qblk) * 8 + (x & 7);
   } else {
-    qb = a.n_qblk - 1 - int(blockIdx.x) / a.BH;
-    r = int(blockIdx.x) % a.BH;
+    qb = a.n_qblk - 1 - x / a.BH;
+    r = x % a.BH;
   }
   if (a.xgrp > 1) {
     const int xcd = r & 7, j = r >> 3;
@@ -349,12 +349,44 @@ __device__ inline bool softmax_block(f32x16& s, f32x16& sd, RowState& st, float 
 //
 // WV = waves per group (32 query rows each): 4, or 2 for grids too small to
 // give every CU a 128-row block -- then 64-row blocks, twice the workgroups.
+//
+// `item` is the row block (through block_coords). A workgroup that walks
+// several (the grid holds fewer workgroups than there are blocks) passes the
+// next one as `next_item`: once its own loop is done it issues that block's
+// Q / dQ loads (into qB / tqB, which the caller keeps) and first three tiles,
+// then stores its results, so the next block's load latency overlaps this
+// one's epilogue and stores; the next call then has `loaded` set.
+// Whether the 4-wave kernel instance walks several row blocks per workgroup
+// (mask-free, 128 columns, scale not folded into Q): elsewhere the next
+// block's registers, live through the epilogue, would spill.
+template <int D, int MASK, bool POW2, int SPLIT>
+constexpr bool fwd16_walks() {
+  return SPLIT == 1 && MASK == JVPATTN_MASK_NONE && D == 128 && !POW2;
+}
+template <bool FIRST, typename X>
+__device__ __forceinline__ X& pick(X& a, X& b) {
+  if constexpr (FIRST) return a;
+  else return b;
+}
+
 template <typename T, int D, int MASK, bool CAUSAL, bool POW2, int SPLIT, int G, int WV>
-__device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi, char* stage0, char* stage1,
-                                           char* stage2, char* stage3, char* x0, char* x1, char* x2, char* x3,
-                                           float4* xst) {
+__device__ __forceinline__ void fwd16_body(const FwdArgs& a, int item, int next_item, bool loaded,
+                                           typename T::vec8 (&qBw)[Tile16<D>::NC],
+                                           typename T::vec8 (&tqBw)[Tile16<D>::NC], int t_lo, int t_hi,
+                                           char* stage0, char* stage1, char* stage2, char* stage3, char* x0,
+                                           char* x1, char* x2, char* x3, float4* xst) {
   using L = Tile16<D>;
   using vec8 = typename T::vec8;
+  // Q / dQ registers: the caller's when the workgroup walks blocks (they carry
+  // the next block's values over), else the body's own (the compiler keeps
+  // those in registers more tightly).
+  constexpr bool WALK = fwd16_walks<D, MASK, POW2, SPLIT>();
+  // A walking block's epilogue stores, the same count in every wave: O and
+  // dO per 4 x 4 tile group, lse, tlse.
+  constexpr int kEpStores = 2 * 4 * L::NT + 2;
+  vec8 qBl[L::NC], tqBl[L::NC];
+  vec8(&qB)[L::NC] = pick<WALK>(qBw, qBl);
+  vec8(&tqB)[L::NC] = pick<WALK>(tqBw, tqBl);
   constexpr int GT = 64 * WV;                           // threads per group
   constexpr int BMG = 32 * WV;                          // query rows per workgroup
   constexpr int LOADS = L::TENSOR_BYTES / (16 * GT);    // 16-byte tile loads per thread per tensor
@@ -368,7 +400,7 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   const int hlf = lane >> 5;
 
   int qb, bh;
-  block_coords(a, qb, bh);
+  block_coords(a, item, qb, bh);
   const int b = bh / a.H, h = bh % a.H;
   const int q0 = qb * BMG;
   const int qw0 = q0 + 32 * wave;
@@ -388,14 +420,14 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   const int64_t qbytes = int64_t(a.Nq) * a.grow;
 
   // Q and dQ as B operands: lane holds row qi, head-dim entries hlf*D/2 + 8c .. +7.
-  // With POW2 the scale (a power of two) is folded into them (T::scale8).
-  vec8 qB[L::NC], tqB[L::NC];
-  {
-    const Rsrc rq = make_rsrc(qp, qbytes), rtq = make_rsrc(tqp, a.tq ? qbytes : 0);
+  // With POW2 the scale (a power of two) is folded into them (T::scale8); a
+  // workgroup that walks several blocks (never with POW2) loads them ahead.
+  auto load_q = [&](const char* qp_, const char* tqp_, int qi_) {
+    const Rsrc rq = make_rsrc(qp_, qbytes), rtq = make_rsrc(tqp_, a.tq ? qbytes : 0);
 #pragma unroll
     for (int c = 0; c < L::NC; ++c) {
       const int col = hlf * (D / 2) + 8 * c;
-      const int off = col < a.dh ? qi * a.grow + col * 2 : kOutOfRange;
+      const int off = col < a.dh ? qi_ * a.grow + col * 2 : kOutOfRange;
       qB[c] = __builtin_bit_cast(vec8, ld128(rq, off));
       tqB[c] = __builtin_bit_cast(vec8, ld128(rtq, off));
       if constexpr (POW2) {
@@ -403,7 +435,8 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
         tqB[c] = T::scale8(tqB[c], a.scale);
       }
     }
-  }
+  };
+  if (!loaded) load_q(qp, tqp, qi);
 
   f32x16 accO[L::NT], accT[L::NT];
 #pragma unroll
@@ -450,23 +483,30 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
   // One buffer resource per tensor for the whole head: offsets past Nk rows
   // (ragged tail) or into an absent tangent (0-byte resource) read as zeros.
   const int64_t kbytes = int64_t(a.Nk) * a.grow;
-  const Rsrc rk = make_rsrc(kp, kbytes), rv = make_rsrc(vp, kbytes);
-  const Rsrc rtk = make_rsrc(tkp, a.tk ? kbytes : 0), rtv = make_rsrc(tvp, a.tv ? kbytes : 0);
-  auto issue_tile = [&](int j, char* stage) {
+  struct KvRsrc {
+    Rsrc k, tk, v, tv;
+  };
+  auto kv_rsrc = [&](const char* kp_, const char* tkp_, const char* vp_, const char* tvp_) {
+    return KvRsrc{make_rsrc(kp_, kbytes), make_rsrc(tkp_, a.tk ? kbytes : 0), make_rsrc(vp_, kbytes),
+                  make_rsrc(tvp_, a.tv ? kbytes : 0)};
+  };
+  const KvRsrc kv = kv_rsrc(kp, tkp, vp, tvp);
+  auto issue_from = [&](const KvRsrc& r, int kb_, int j, char* stage) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int off = dl_off[i] == kOutOfRange ? kOutOfRange : (kb + j) * tile_g + dl_off[i];
+      const int off = dl_off[i] == kOutOfRange ? kOutOfRange : (kb_ + j) * tile_g + dl_off[i];
       const int slot = (i * GT + wave * 64) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r.k, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
                                                16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rtk, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+          r.tk, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+          r.v, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rtv, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+          r.tv, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
     }
   };
+  auto issue_tile = [&](int j, char* stage) { issue_from(kv, kb, j, stage); };
 
   // LDS read offsets of this lane (constant over the loop).
   // K / dK A operand, chunk c: row c32, logical granule hlf*NC + c.
@@ -650,12 +690,20 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
 
   f32x16 sA, sdA, sB, sdB;
   // Prologue: tiles 0..2 in flight, wait for tile 0, settle block 0 if it needs no key mask.
-  if (n_tiles > 0) issue_tile(0, stage0);
-  if (n_tiles > 1) issue_tile(1, stage1);
-  if (n_tiles > 2) issue_tile(2, stage2);
-  if (n_tiles > 2) wait_vmcnt<2 * TILE_VMEM>();
-  else if (n_tiles > 1) wait_vmcnt<TILE_VMEM>();
-  else wait_vmcnt<0>();
+  if (!loaded) {
+    if (n_tiles > 0) issue_tile(0, stage0);
+    if (n_tiles > 1) issue_tile(1, stage1);
+    if (n_tiles > 2) issue_tile(2, stage2);
+    if (n_tiles > 2) wait_vmcnt<2 * TILE_VMEM>();
+    else if (n_tiles > 1) wait_vmcnt<TILE_VMEM>();
+    else wait_vmcnt<0>();
+  } else {
+    // Q, dQ and tiles 0..2 came with the previous block, ahead of its
+    // kEpStores stores, which may stay in flight.
+    if (n_tiles > 2) wait_vmcnt<2 * TILE_VMEM + kEpStores>();
+    else if (n_tiles > 1) wait_vmcnt<TILE_VMEM + kEpStores>();
+    else wait_vmcnt<kEpStores>();
+  }
   ring_barrier();
   bool ready = false;   // sA holds the current block's settled scores
   if (0 <= last && !needs_keymask(0)) {
@@ -763,10 +811,59 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int t_lo, int t_hi,
     }
   }
 
+  if (WALK && next_item >= 0) {
+    // The next block's Q, dQ and first tiles, once every wave is done with the ring.
+    ring_barrier();
+    int qb2, bh2;
+    block_coords(a, next_item, qb2, bh2);
+    const int64_t qh2 = int64_t(bh2) * a.Nq * a.grow, kh2 = int64_t(bh2 / a.grp) * a.Nk * a.grow;
+    const char* qp2 = static_cast<const char*>(a.q) + qh2;
+    const char* kp2 = static_cast<const char*>(a.k) + kh2;
+    const char* vp2 = static_cast<const char*>(a.v) + kh2;
+    load_q(qp2, a.tq ? static_cast<const char*>(a.tq) + qh2 : qp2, qb2 * BMG + 32 * wave + c32);
+    const KvRsrc kv2 = kv_rsrc(kp2, a.tk ? static_cast<const char*>(a.tk) + kh2 : kp2, vp2,
+                               a.tv ? static_cast<const char*>(a.tv) + kh2 : vp2);
+    const int kv_end2 = min(CAUSAL ? min(a.Nk, qb2 * BMG + BMG) : a.Nk, 32 * t_hi);
+    const int n2 = max(0, (kv_end2 + L::BN - 1) / L::BN - t_lo);
+    if (n2 > 0) issue_from(kv2, t_lo, 0, stage0);
+    if (n2 > 1) issue_from(kv2, t_lo, 1, stage1);
+    if (n2 > 2) issue_from(kv2, t_lo, 2, stage2);
+  }
+
   // Epilogue: combine the two lane halves of each query column, normalise, store.
   const float l = xhalf_sum(st.l);
   const float mu = xhalf_sum(st.mu);
-  if (qi < a.Nq) {
+  if constexpr (WALK) {
+    // Every wave issues kEpStores stores (rows past Nq, columns past dh and
+    // the second lane half's statistics land out of range and are dropped).
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float tl = mu * inv;
+    const int64_t hb = int64_t(bh) * a.Nq;
+    const Rsrc ro = make_rsrc(static_cast<char*>(a.o) + hb * a.grow, qbytes);
+    const Rsrc rto = make_rsrc(static_cast<char*>(a.to) + hb * a.grow, qbytes);
+    const Rsrc rl = make_rsrc(a.lse + hb, int64_t(a.Nq) * 4);
+    const Rsrc rtl = make_rsrc(a.tlse ? a.tlse + hb : a.lse, a.tlse ? int64_t(a.Nq) * 4 : 0);
+    const bool row = qi < a.Nq;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float ov[4], dv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ov[e] = accO[t][4 * g + e] * inv;
+          dv[e] = accT[t][4 * g + e] * inv - tl * ov[e];
+        }
+        const int dd = 32 * t + 8 * g + 4 * hlf;
+        const int off = row && dd < a.dh ? qi * a.grow + dd * 2 : kOutOfRange;
+        st64(ro, off, uint2{T::pack2(ov[0], ov[1]), T::pack2(ov[2], ov[3])});
+        st64(rto, off, uint2{T::pack2(dv[0], dv[1]), T::pack2(dv[2], dv[3])});
+      }
+    }
+    const int soff = row && hlf == 0 ? qi * 4 : kOutOfRange;
+    st32(rl, soff, __float_as_uint(l > 0.0f ? (st.moff + log2f(l)) * kLn2 : -INFINITY));
+    st32(rtl, soff, __float_as_uint(tl));
+  } else if (qi < a.Nq) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const float tl = mu * inv;   // mu sums e dS (float32 products)
     uint16_t* op = static_cast<uint16_t*>(a.o) + (int64_t(bh) * a.Nq + qi) * a.dh;
@@ -810,13 +907,28 @@ __global__ __launch_bounds__(64 * WV * SPLIT, (D == 64 && WV == 4) ? 2 : 1) void
   int t_lo, t_hi;
   {
     int qb, bh;
-    block_coords(a, qb, bh);
+    block_coords(a, int(blockIdx.x), qb, bh);
     const Rsrc mr = mask_rsrc(a, bh / a.H, bh % a.H, mask_es<MASK>(2), nullptr, MASK == JVPATTN_MASK_BITS);
     key_tiles<T, MASK, 2>(a, mr, kred, t_lo, t_hi, qb * 32 * WV, 32 * WV, CAUSAL);
   }
-  if constexpr (SPLIT == 1) {
-    fwd16_body<T, D, MASK, CAUSAL, POW2, 1, 0, WV>(a, t_lo, t_hi, s0, s1, s2, s3, nullptr, nullptr, nullptr,
-                                                   nullptr, nullptr);
+  using vec8 = typename T::vec8;
+  vec8 qB[L::NC], tqB[L::NC];
+  // A walking instance takes row blocks blockIdx.x + r * gridDim.x (the grid
+  // may be smaller than their count); on odd rounds the workgroups of each
+  // XCD take theirs in reverse, so heavy and light causal blocks pair up.
+  if constexpr (fwd16_walks<D, MASK, POW2, SPLIT>()) {
+    const int gsz = int(gridDim.x), b = int(blockIdx.x);
+    const int brev = (gsz & 7) == 0 ? (gsz / 8 - 1 - b / 8) * 8 + (b & 7) : b;
+    int it = b;
+    for (int r = 0; it < a.n_items; ++r) {
+      const int nx = (r + 1) * gsz + ((r & 1) ? b : brev);
+      fwd16_body<T, D, MASK, CAUSAL, POW2, 1, 0, WV>(a, it, nx < a.n_items ? nx : -1, r > 0, qB, tqB, t_lo, t_hi,
+                                                     s0, s1, s2, s3, nullptr, nullptr, nullptr, nullptr, nullptr);
+      it = nx;
+    }
+  } else if constexpr (SPLIT == 1) {
+    fwd16_body<T, D, MASK, CAUSAL, POW2, 1, 0, WV>(a, int(blockIdx.x), -1, false, qB, tqB, t_lo, t_hi, s0, s1, s2,
+                                                   s3, nullptr, nullptr, nullptr, nullptr, nullptr);
   } else {
     __shared__ __attribute__((aligned(16))) char s4[L::STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) char s5[L::STAGE_BYTES];
@@ -824,9 +936,11 @@ __global__ __launch_bounds__(64 * WV * SPLIT, (D == 64 && WV == 4) ? 2 : 1) void
     __shared__ __attribute__((aligned(16))) char s7[L::STAGE_BYTES];
     __shared__ float4 xst[kThreads];
     if (__builtin_amdgcn_readfirstlane(threadIdx.x / (64 * WV)) == 0)
-      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 0, WV>(a, t_lo, t_hi, s0, s1, s2, s3, s4, s5, s6, s7, xst);
+      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 0, WV>(a, int(blockIdx.x), -1, false, qB, tqB, t_lo, t_hi, s0, s1,
+                                                     s2, s3, s4, s5, s6, s7, xst);
     else
-      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 1, WV>(a, t_lo, t_hi, s4, s5, s6, s7, s4, s5, s6, s7, xst);
+      fwd16_body<T, D, MASK, CAUSAL, POW2, 2, 1, WV>(a, int(blockIdx.x), -1, false, qB, tqB, t_lo, t_hi, s4, s5,
+                                                     s6, s7, s4, s5, s6, s7, xst);
   }
 #endif
 }
@@ -872,7 +986,7 @@ __device__ __forceinline__ void fwd16pp_body(const FwdArgs& a) {
   const int hlf = lane >> 5;
 
   int qb, bh;
-  block_coords(a, qb, bh);
+  block_coords(a, int(blockIdx.x), qb, bh);
   const int b = bh / a.H, h = bh % a.H;
   const int q0 = qb * kPPBM;
   const int qw0 = q0 + 32 * wave;
@@ -1225,7 +1339,7 @@ __device__ __forceinline__ void fwd16w_body(const FwdArgs& a, int t_lo, int t_hi
   const int hlf = lane >> 5;
 
   int qb, bh;
-  block_coords(a, qb, bh);
+  block_coords(a, int(blockIdx.x), qb, bh);
   const int b = bh / a.H, h = bh % a.H;
   constexpr int NT = L::NT / 2;        // accumulator tiles of this wave's column half
   const int ch = wave & 1;             // column half: output columns 128 ch .. 128 ch + 127
@@ -1492,7 +1606,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd16w_kernel(FwdArgs a) {
   int t_lo, t_hi;
   {
     int qb, bh;
-    block_coords(a, qb, bh);
+    block_coords(a, int(blockIdx.x), qb, bh);
     const Rsrc mr = mask_rsrc(a, bh / a.H, bh % a.H, mask_es<MASK>(2), nullptr, MASK == JVPATTN_MASK_BITS);
     key_tiles<T, MASK, 2>(a, mr, reinterpret_cast<int*>(xchg), t_lo, t_hi, qb * kWideBM, kWideBM, CAUSAL);
   }
@@ -1521,7 +1635,7 @@ __device__ __forceinline__ void fwd32_body(const FwdArgs& a) {
   const int hlf = lane >> 5;
 
   int qb, bh;
-  block_coords(a, qb, bh);
+  block_coords(a, int(blockIdx.x), qb, bh);
   const int b = bh / a.H, h = bh % a.H;
   const int q0 = qb * kBM;
   const int qw0 = q0 + 32 * wave;

@@ -50,6 +50,8 @@ struct FwdArgs {
   int skip_hidden;    // 1: a wave skips the softmax and value products of a block its mask hides entirely
   int row_range;      // 1: one mask row per query; run only the key tiles visible to some row of the workgroup
   int n_qblk;
+  int n_items;        // row blocks in all (n_qblk * BH); the mask-free 4-wave kernel walks them with a
+                      // grid that may be smaller
   int mask_vec;       // 1: mask rows may be read 4 keys at a time
   int64_t msb, msh, msq;
   float scale;

@@ -86,6 +86,8 @@ def load_library(path: str = LIB_PATH):
     lib.jvpattn_bwd_noalloc.restype = ctypes.c_int
     lib.jvpattn_fwd_set_algo.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.jvpattn_fwd_set_algo.restype = ctypes.c_int
+    lib.jvpattn_fwd_set_workgroups.argtypes = [ctypes.c_int]
+    lib.jvpattn_fwd_set_workgroups.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -101,6 +103,15 @@ def jvpattn_fwd_set_algo(kernel=None, order=None, key_range=None) -> None:
     o = JVPATTN_ALGO_AUTO if order is None else {"qb": 0, "head": 1}[order]
     r = JVPATTN_ALGO_AUTO if key_range is None else int(bool(key_range))
     rc = load_library().jvpattn_fwd_set_algo(k, o, r)
+    if rc != 0:
+        raise JvpattnError(rc, jvpattn_strerror(rc))
+
+
+def jvpattn_fwd_set_workgroups(max_workgroups: int = 0) -> None:
+    """Cap the workgroups of the mask-free d = 96 / 128 forward kernel, which walks its 128-row
+    blocks with a grid smaller than their count (0 = the library's choice: one workgroup per CU).
+    Results do not depend on it; for tests and tuning."""
+    rc = load_library().jvpattn_fwd_set_workgroups(int(max_workgroups))
     if rc != 0:
         raise JvpattnError(rc, jvpattn_strerror(rc))
 

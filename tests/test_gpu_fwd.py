@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from forward_mode_autodiff_amd import inputs as I
-from forward_mode_autodiff_amd.jvpattn import jvpattn_fwd, jvpattn_fwd_set_algo
+from forward_mode_autodiff_amd.jvpattn import jvpattn_fwd, jvpattn_fwd_set_algo, jvpattn_fwd_set_workgroups
 from oracle import oracle_fwd
 from tests.parity import assert_parity, failures
 
@@ -32,8 +32,10 @@ KERNELS = ["pp", "wg4", "split", "split64"]
 def _automatic_plan():
     """Every test starts and ends with the library's own launch plan."""
     jvpattn_fwd_set_algo()
+    jvpattn_fwd_set_workgroups()
     yield
     jvpattn_fwd_set_algo()
+    jvpattn_fwd_set_workgroups()
 
 
 @pytest.fixture(params=KERNELS)
@@ -221,6 +223,29 @@ def test_head_dim_rectangular_grouped(d):
         w = I.Workload(f"d{d}rect", B=2, H=4, Hkv=2, N=Nq, Nk=Nk, d=d, dtype="bf16", causal=causal, std=1.0,
                        seed=5 + d)
         check(w)
+
+
+# The mask-free kernel at 128 columns walks several row blocks per workgroup
+# (the next block's Q and first tiles load during the current one's epilogue).
+# A small cap forces many rounds on small inputs: the walk must give the same
+# bits as one block per workgroup, and oracle parity.
+@pytest.mark.parametrize("cap", [8, 5, 24])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (128, "f16"), (96, "bf16")])
+def test_walking_row_blocks(d, dtype, causal, cap):
+    shapes = [dict(B=2, H=4, N=700), dict(B=4, H=8, Hkv=2, N=300), dict(B=1, H=3, N=200, Nk=450)]
+    for i, s in enumerate(shapes):
+        w = I.Workload(f"walk{d}_{i}", d=d, dtype=dtype, causal=causal, std=1.0, seed=40 + i, **s)
+        x = I.make_inputs(w)
+        for order in (None, "head"):
+            jvpattn_fwd_set_algo(order=order)
+            jvpattn_fwd_set_workgroups(1 << 30)   # one block per workgroup
+            one = gpu_run(x, causal)
+            jvpattn_fwd_set_workgroups(cap)
+            walk = gpu_run(x, causal)
+            for n in one:
+                assert torch.equal(one[n], walk[n]), (w.name, order, n)
+        assert_parity(walk, oracle_run(x, "none", causal), dtype, w.name, spec_spread=False)
 
 
 @pytest.mark.parametrize("case", ["ramp", "jump", "late"])
