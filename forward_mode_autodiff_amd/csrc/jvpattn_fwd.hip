@@ -133,14 +133,14 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   const bool c = p->causal != 0;
   int mk = p->mask_kind;
   if (mk == JVPATTN_MASK_ADDITIVE && tmask) mk = kMaskAddT;
-  // The mask-free 4-wave kernel at 128 columns (16-bit, d = 96 / 128, scale
+  // The mask-free 4-wave kernel at 128 columns (bfloat16, d = 96 / 128, scale
   // not a power of two) walks its row blocks with at most as many workgroups
   // as the chip holds at once (one per CU), a multiple of 8 so each keeps its
   // XCD: a block's loads then overlap the previous block's epilogue and
   // stores. With one block per workgroup both latencies are exposed.
   a.n_items = static_cast<int>(blocks);
   int64_t wgs = blocks;
-  if (kernel == kFwdWG4 && mk == JVPATTN_MASK_NONE && p->dtype != JVPATTN_F32 && dphys == 128 && !pow2) {
+  if (kernel == kFwdWG4 && mk == JVPATTN_MASK_NONE && p->dtype == JVPATTN_BF16 && dphys == 128 && !pow2) {
     const int forced = g_max_workgroups.load(std::memory_order_relaxed);
     int64_t cap = forced > 0 ? forced : int64_t(cu_count());
     if (cap >= 8) cap &= ~int64_t(7);

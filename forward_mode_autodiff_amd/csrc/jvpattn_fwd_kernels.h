@@ -357,11 +357,11 @@ __device__ inline bool softmax_block(f32x16& s, f32x16& sd, RowState& st, float 
 // then stores its results, so the next block's load latency overlaps this
 // one's epilogue and stores; the next call then has `loaded` set.
 // Whether the 4-wave kernel instance walks several row blocks per workgroup
-// (mask-free, 128 columns, scale not folded into Q): elsewhere the next
-// block's registers, live through the epilogue, would spill.
-template <int D, int MASK, bool POW2, int SPLIT>
+// (bfloat16, mask-free, 128 columns, scale not folded into Q): elsewhere the
+// extra state would spill registers (float16 keeps a guard of its own).
+template <typename T, int D, int MASK, bool POW2, int SPLIT>
 constexpr bool fwd16_walks() {
-  return SPLIT == 1 && MASK == JVPATTN_MASK_NONE && D == 128 && !POW2;
+  return std::is_same_v<T, BF16> && SPLIT == 1 && MASK == JVPATTN_MASK_NONE && D == 128 && !POW2;
 }
 template <bool FIRST, typename X>
 __device__ __forceinline__ X& pick(X& a, X& b) {
@@ -380,10 +380,12 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int item, int next_
   // Q / dQ registers: the caller's when the workgroup walks blocks (they carry
   // the next block's values over), else the body's own (the compiler keeps
   // those in registers more tightly).
-  constexpr bool WALK = fwd16_walks<D, MASK, POW2, SPLIT>();
+  constexpr bool WALK = fwd16_walks<T, D, MASK, POW2, SPLIT>();
   // A walking block's epilogue stores, the same count in every wave: O and
   // dO per 4 x 4 tile group, lse, tlse.
   constexpr int kEpStores = 2 * 4 * L::NT + 2;
+  // Direct loads that bring a walking block's 32 Q (and dQ) rows of this wave into LDS.
+  constexpr int kQDma = 32 * L::ROW / 1024;
   vec8 qBl[L::NC], tqBl[L::NC];
   vec8(&qB)[L::NC] = pick<WALK>(qBw, qBl);
   vec8(&tqB)[L::NC] = pick<WALK>(tqBw, tqBl);
@@ -698,11 +700,19 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int item, int next_
     else if (n_tiles > 1) wait_vmcnt<TILE_VMEM>();
     else wait_vmcnt<0>();
   } else {
-    // Q, dQ and tiles 0..2 came with the previous block, ahead of its
-    // kEpStores stores, which may stay in flight.
-    if (n_tiles > 2) wait_vmcnt<2 * TILE_VMEM + kEpStores>();
-    else if (n_tiles > 1) wait_vmcnt<TILE_VMEM + kEpStores>();
+    // Q and dQ (in stages 2 and 3) and tiles 0, 1 came with the previous
+    // block, ahead of its kEpStores stores, which may stay in flight. Each
+    // wave reads its own rows; tile 2 goes into stage 2 once all have.
+    if (n_tiles > 1) wait_vmcnt<TILE_VMEM + kEpStores>();
     else wait_vmcnt<kEpStores>();
+    const int qo = wave * 32 * L::ROW + c32 * L::ROW + hlf * (L::ROW / 2);
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) {
+      qB[c] = __builtin_bit_cast(vec8, lds_load<uint4>(stage2, qo + 16 * c));
+      tqB[c] = __builtin_bit_cast(vec8, lds_load<uint4>(stage3, qo + 16 * c));
+    }
+    ring_barrier();
+    if (n_tiles > 2) issue_tile(2, stage2);
   }
   ring_barrier();
   bool ready = false;   // sA holds the current block's settled scores
@@ -820,14 +830,26 @@ __device__ __forceinline__ void fwd16_body(const FwdArgs& a, int item, int next_
     const char* qp2 = static_cast<const char*>(a.q) + qh2;
     const char* kp2 = static_cast<const char*>(a.k) + kh2;
     const char* vp2 = static_cast<const char*>(a.v) + kh2;
-    load_q(qp2, a.tq ? static_cast<const char*>(a.tq) + qh2 : qp2, qb2 * BMG + 32 * wave + c32);
+    // Q and dQ rows straight into LDS (stages 2 and 3, this wave's 32 rows
+    // each; no register waits for them here), then tiles 0 and 1.
+    const Rsrc rq2 = make_rsrc(qp2, qbytes);
+    const Rsrc rtq2 = make_rsrc(a.tq ? static_cast<const char*>(a.tq) + qh2 : qp2, a.tq ? qbytes : 0);
+#pragma unroll
+    for (int j = 0; j < kQDma; ++j) {
+      const int r = j * (1024 / L::ROW) + lane / (L::ROW / 16), g = lane % (L::ROW / 16);
+      const int off = g < (a.dh >> 3) ? (qb2 * BMG + 32 * wave + r) * a.grow + 16 * g : kOutOfRange;
+      const int slot = wave * 32 * L::ROW + j * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq2, (__attribute__((address_space(3))) void*)to_lds(stage2 + slot),
+                                               16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rtq2, (__attribute__((address_space(3))) void*)to_lds(stage3 + slot),
+                                               16, off, 0, 0, 0);
+    }
     const KvRsrc kv2 = kv_rsrc(kp2, a.tk ? static_cast<const char*>(a.tk) + kh2 : kp2, vp2,
                                a.tv ? static_cast<const char*>(a.tv) + kh2 : vp2);
     const int kv_end2 = min(CAUSAL ? min(a.Nk, qb2 * BMG + BMG) : a.Nk, 32 * t_hi);
     const int n2 = max(0, (kv_end2 + L::BN - 1) / L::BN - t_lo);
     if (n2 > 0) issue_from(kv2, t_lo, 0, stage0);
     if (n2 > 1) issue_from(kv2, t_lo, 1, stage1);
-    if (n2 > 2) issue_from(kv2, t_lo, 2, stage2);
   }
 
   // Epilogue: combine the two lane halves of each query column, normalise, store.
@@ -916,7 +938,7 @@ __global__ __launch_bounds__(64 * WV * SPLIT, (D == 64 && WV == 4) ? 2 : 1) void
   // A walking instance takes row blocks blockIdx.x + r * gridDim.x (the grid
   // may be smaller than their count); on odd rounds the workgroups of each
   // XCD take theirs in reverse, so heavy and light causal blocks pair up.
-  if constexpr (fwd16_walks<D, MASK, POW2, SPLIT>()) {
+  if constexpr (fwd16_walks<T, D, MASK, POW2, SPLIT>()) {
     const int gsz = int(gridDim.x), b = int(blockIdx.x);
     const int brev = (gsz & 7) == 0 ? (gsz / 8 - 1 - b / 8) * 8 + (b & 7) : b;
     int it = b;

@@ -108,7 +108,7 @@ def jvpattn_fwd_set_algo(kernel=None, order=None, key_range=None) -> None:
 
 
 def jvpattn_fwd_set_workgroups(max_workgroups: int = 0) -> None:
-    """Cap the workgroups of the mask-free d = 96 / 128 forward kernel, which walks its 128-row
+    """Cap the workgroups of the mask-free bfloat16 d = 96 / 128 forward kernel, which walks its 128-row
     blocks with a grid smaller than their count (0 = the library's choice: one workgroup per CU).
     Results do not depend on it; for tests and tuning."""
     rc = load_library().jvpattn_fwd_set_workgroups(int(max_workgroups))

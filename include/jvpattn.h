@@ -312,7 +312,7 @@ typedef enum {
  * range. Not meant to be changed while another thread launches forwards. */
 int jvpattn_fwd_set_algo(int kernel, int order, int key_range);
 
-/* Cap the workgroups of the mask-free forward kernel for 16-bit d = 96 / 128
+/* Cap the workgroups of the mask-free forward kernel for bfloat16 d = 96 / 128
  * (scale not a power of two), which walks its 128-row blocks with a grid
  * smaller than their count: 0 (the default) = what the chip holds at once (one
  * workgroup per CU, rounded down to a multiple of 8); n > 0 = at most n
