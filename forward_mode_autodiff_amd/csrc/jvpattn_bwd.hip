@@ -58,6 +58,8 @@ int bwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   a.grp = sz.group;
   a.BHK = p->B * sz.hkv;
   a.n_blk = 0;
+  a.n_items = 0;
+  a.max_wgs = walk_workgroups();
   a.msb = p->mask_stride_b; a.msh = p->mask_stride_h; a.msq = p->mask_stride_q;
   a.scale = p->scale;
   a.inv_scale = 1.0f / p->scale;

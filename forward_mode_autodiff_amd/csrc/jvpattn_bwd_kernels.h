@@ -463,6 +463,67 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 //   dv^T += G^T P + Gd^T Pd,       dtv^T += Gd^T P                      (24)
 // Row r of a lane's C registers is query 8*(r/4) + 4*(lane/32) + r%4.
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// A walking key-side item's B operands (d = 64): four 16-byte LDS reads per
+// tensor (K, dK, V, dV rows 32 rows apart), in one block that also waits for
+// them. Read through the builtins, the compiler would order them behind
+// every outstanding load of the wave (it cannot tell that the direct loads
+// which filled the buffer are older than the previous item's stores); the
+// caller has already waited for those direct loads.
+__device__ inline void read_ops64(const char* p, u32x4 (&o)[16]) {
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(to_lds(p)));
+  asm volatile(
+      "ds_read_b128 %0, %16\n"
+      "ds_read_b128 %1, %16 offset:16\n"
+      "ds_read_b128 %2, %16 offset:32\n"
+      "ds_read_b128 %3, %16 offset:48\n"
+      "ds_read_b128 %4, %16 offset:4096\n"
+      "ds_read_b128 %5, %16 offset:4112\n"
+      "ds_read_b128 %6, %16 offset:4128\n"
+      "ds_read_b128 %7, %16 offset:4144\n"
+      "ds_read_b128 %8, %16 offset:8192\n"
+      "ds_read_b128 %9, %16 offset:8208\n"
+      "ds_read_b128 %10, %16 offset:8224\n"
+      "ds_read_b128 %11, %16 offset:8240\n"
+      "ds_read_b128 %12, %16 offset:12288\n"
+      "ds_read_b128 %13, %16 offset:12304\n"
+      "ds_read_b128 %14, %16 offset:12320\n"
+      "ds_read_b128 %15, %16 offset:12336\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]),
+        "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]),
+        "=&v"(o[15])
+      : "v"(a));   // no memory clobber: it would make the compiler drain the load queue first; as a
+                   // volatile asm it stays behind the caller's (volatile) wait for the direct loads
+}
+
+// One query tile j (Q, dQ, G, Gd rows; LOADS direct loads per tensor per
+// thread) and statistic `wave` of its 32 rows into stage.
+template <typename L>
+__device__ __forceinline__ void dkv_issue_tile(Rsrc rq, Rsrc rtq, Rsrc rg, Rsrc rtg, Rsrc rstat,
+                                               const int (&dl_off)[L::LOADS], int wave, int lane, int j,
+                                               char* stage) {
+#pragma unroll
+  for (int i = 0; i < L::LOADS; ++i) {
+    const int off = j * L::TENSOR_BYTES + dl_off[i];
+    const int slot = (i * kBThreads + wave * 64) * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)to_lds(stage + slot), 16,
+                                             off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rtq, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rg, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rtg, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
+  }
+  // 32 floats of statistic `wave` for rows 32j .. 32j+31 (past Nq: zeros)
+  if (lane < 8)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rstat, (__attribute__((address_space(3))) void*)to_lds(stage + L::STAGE_BYTES + wave * 128), 16,
+        j * 128 + lane * 16, 0, 0, 0);
+}
+
 // Mask values (i, key) for this lane's key and the 16 queries of its rows.
 template <int MASK> struct MaskCol {};
 template <> struct MaskCol<JVPATTN_MASK_BOOL> { uint32_t w[16]; };
@@ -474,10 +535,24 @@ template <> struct MaskCol<JVPATTN_MASK_ADDITIVE> { uint32_t w[16]; };
 // the weights P and P dS are needed, from S and dS).
 enum { kAllParts = 0, kKeyPart = 1, kValuePart = 2 };
 
+// Whether a key-side instance walks several (key block, K/V head) items per
+// workgroup: mask-free, d = 64, all four outputs. After its loops an item
+// loads the next item's K, dK, V, dV rows into an LDS buffer of their own
+// (direct loads, no register destinations) and the first two query tiles of
+// its first head; it then stores its gradients with a fixed count of buffer
+// stores per wave, so the next item waits only for its own loads.
+template <int D, int PART, int MASK>
+constexpr bool dkv_walks() {
+  return D == 64 && PART == kAllParts && MASK == JVPATTN_MASK_NONE;
+}
+
 template <typename T, int D, int PART, int MASK, bool CAUSAL, bool POW2>
-__device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
+__device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int item, int next_item, bool loaded) {
   using L = Tile16<D>;
   constexpr bool KP = PART != kValuePart, VP = PART != kKeyPart;
+  constexpr bool WALK = dkv_walks<D, PART, MASK>();
+  constexpr int kEpStores = 4 * 4 * L::NT;         // dk, dtk, dv, dtv per 4 x 4 tile group
+  constexpr int kOpsDma = 32 * L::ROW / 1024;      // direct loads of a wave's 32 rows of one tensor
   using vec8 = typename T::vec8;
   constexpr int STATS = 4 * 32 * 4;                // four statistics of 32 rows
   constexpr int SB = L::STAGE_BYTES + STATS;
@@ -485,6 +560,8 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
   __shared__ __attribute__((aligned(16))) char stage1[SB];
   __shared__ __attribute__((aligned(16))) char stage2[SB];
   __shared__ __attribute__((aligned(16))) char stage3[SB];
+  // a walking item's K, dK, V, dV rows: wave w's 32 keys of tensor i at (4 w + i) * 32 rows
+  __shared__ __attribute__((aligned(16))) char ops[WALK ? 4 * kBBlk * L::ROW : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -492,8 +569,8 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
   const int c32 = lane & 31;
   const int hlf = lane >> 5;
 
-  const int kb = int(blockIdx.x) / a.BHK;   // causal: early key blocks see the most queries
-  const int bhk = int(blockIdx.x) % a.BHK;  // key/value head; its query heads are bhk*grp .. +grp-1
+  const int kb = item / a.BHK;   // causal: early key blocks see the most queries
+  const int bhk = item % a.BHK;  // key/value head; its query heads are bhk*grp .. +grp-1
   const int b = bhk * a.grp / a.H;
   const int k0 = kb * kBBlk;
   const int kw0 = k0 + 32 * wave;
@@ -506,7 +583,77 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
 
   // B operands of this wave's 32 keys: K, dK (scale folded in when exact), V, dV.
   vec8 kB[L::NC], tkB[L::NC], vB[L::NC], tvB[L::NC];
-  {
+  constexpr int TILE_VMEM = L::TILE_VMEM + 1;   // four tensors + this wave's statistic
+  // A walking item's K, dK, V, dV rows (into ops) and its first head's
+  // query tiles t_begin, t_begin + 1 (into stages 0, 1), by direct loads.
+  auto prefetch = [&](int it) {
+    const int kb2 = it / a.BHK, bhk2 = it % a.BHK;
+    const int64_t kh2 = int64_t(bhk2) * a.Nk * L::ROW;
+    const Rsrc ro2[4] = {make_rsrc(at(a.k, kh2), kbytes),
+                         make_rsrc(a.tk ? at(a.tk, kh2) : at(a.k, kh2), a.tk ? kbytes : 0),
+                         make_rsrc(at(a.v, kh2), kbytes),
+                         make_rsrc(a.tv ? at(a.tv, kh2) : at(a.v, kh2), a.tv ? kbytes : 0)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kOpsDma; ++j) {
+        const int r = j * (1024 / L::ROW) + lane / (L::ROW / 16), gq = lane % (L::ROW / 16);
+        const int off = (kb2 * kBBlk + 32 * wave + r) * L::ROW + 16 * gq;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ro2[i], (__attribute__((address_space(3))) void*)to_lds(ops + (4 * wave + i) * 32 * L::ROW + j * 1024),
+            16, off, 0, 0, 0);
+      }
+    const int bh2 = bhk2 * a.grp;
+    const int64_t qh2 = int64_t(bh2) * a.Nq * L::ROW;
+    const Rsrc rq2 = make_rsrc(at(a.q, qh2), qbytes);
+    const Rsrc rtq2 = make_rsrc(a.tq ? at(a.tq, qh2) : at(a.q, qh2), a.tq ? qbytes : 0);
+    const Rsrc rg2 = make_rsrc(a.go ? at(a.go, qh2) : at(a.q, qh2), a.go ? qbytes : 0);
+    const Rsrc rtg2 = make_rsrc(a.gto ? at(a.gto, qh2) : at(a.q, qh2), a.gto ? qbytes : 0);
+    const Rsrc rstat2 = make_rsrc(a.ws + wave * a.ws_stride + int64_t(bh2) * a.Nq, int64_t(a.Nq) * 4);
+    int dl2[L::LOADS];
+#pragma unroll
+    for (int i = 0; i < L::LOADS; ++i) {
+      const int p = i * kBThreads + tid;
+      dl2[i] = (p / L::GR) * L::ROW + (((p % L::GR) ^ swz(p / L::GR)) << 4);
+    }
+    const int n_qt2 = (a.Nq + 31) / 32;
+    const int tb2 = CAUSAL ? min(n_qt2, (kb2 * kBBlk) >> 5) : 0;
+    if (tb2 < n_qt2) dkv_issue_tile<L>(rq2, rtq2, rg2, rtg2, rstat2, dl2, wave, lane, tb2, stage0);
+    if (tb2 + 1 < n_qt2) dkv_issue_tile<L>(rq2, rtq2, rg2, rtg2, rstat2, dl2, wave, lane, tb2 + 1, stage1);
+  };
+  if constexpr (WALK) {
+    // The first item fetches its own operands and tiles; later ones came with
+    // the previous item, ahead of its kEpStores stores, which may stay in
+    // flight. Tile t_begin + 1 may stay in flight too (with one query tile
+    // only, every load must have landed).
+    if (!loaded) prefetch(item);
+    const int n_qt0 = (a.Nq + 31) / 32;
+    const bool two = n_qt0 - (CAUSAL ? min(n_qt0, k0 >> 5) : 0) > 1;
+    if (loaded) {
+      if (two) wait_vmcnt<TILE_VMEM + kEpStores>();
+      else wait_vmcnt<kEpStores>();
+    } else {
+      if (two) wait_vmcnt<TILE_VMEM>();
+      else wait_vmcnt<0>();
+    }
+    static_assert(32 * L::ROW == 4096, "read_ops64 takes tensors 4 KB apart");
+    u32x4 o[16];
+    read_ops64(ops + wave * 4 * 32 * L::ROW + c32 * L::ROW + hlf * (L::ROW / 2), o);
+#pragma unroll
+    for (int c = 0; c < L::NC; ++c) {
+      kB[c] = __builtin_bit_cast(vec8, o[c]);
+      tkB[c] = __builtin_bit_cast(vec8, o[4 + c]);
+      vB[c] = __builtin_bit_cast(vec8, o[8 + c]);
+      tvB[c] = __builtin_bit_cast(vec8, o[12 + c]);
+      if constexpr (POW2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kB[c][e] = static_cast<__bf16>(static_cast<float>(kB[c][e]) * a.scale);
+          tkB[c][e] = static_cast<__bf16>(static_cast<float>(tkB[c][e]) * a.scale);
+        }
+      }
+    }
+  } else {
     const Rsrc rk = make_rsrc(at(a.k, khead), kbytes), rv = make_rsrc(at(a.v, khead), kbytes);
     const Rsrc rtk = make_rsrc(a.tk ? at(a.tk, khead) : at(a.k, khead), a.tk ? kbytes : 0);
     const Rsrc rtv = make_rsrc(a.tv ? at(a.tv, khead) : at(a.v, khead), a.tv ? kbytes : 0);
@@ -567,26 +714,7 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
     // Statistics of this head's rows: wave w loads statistic w of the tile (8 lanes x 16 bytes).
     const int64_t srow = int64_t(bh) * a.Nq;
     const Rsrc rstat = make_rsrc(a.ws + wave * a.ws_stride + srow, int64_t(a.Nq) * 4);
-    auto issue_tile = [&](int j, char* stage) {
-#pragma unroll
-      for (int i = 0; i < L::LOADS; ++i) {
-        const int off = j * L::TENSOR_BYTES + dl_off[i];
-        const int slot = (i * kBThreads + wave * 64) * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)to_lds(stage + slot),
-                                                 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rtq, (__attribute__((address_space(3))) void*)to_lds(stage + L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rg, (__attribute__((address_space(3))) void*)to_lds(stage + 2 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rtg, (__attribute__((address_space(3))) void*)to_lds(stage + 3 * L::TENSOR_BYTES + slot), 16, off, 0, 0, 0);
-      }
-      // 32 floats of statistic `wave` for rows 32j .. 32j+31 (past Nq: zeros)
-      if (lane < 8)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rstat, (__attribute__((address_space(3))) void*)to_lds(stage + L::STAGE_BYTES + wave * 128), 16,
-            j * 128 + lane * 16, 0, 0, 0);
-    };
+    auto issue_tile = [&](int j, char* stage) { dkv_issue_tile<L>(rq, rtq, rg, rtg, rstat, dl_off, wave, lane, j, stage); };
 
     int kofs[L::NC];
 #pragma unroll
@@ -752,7 +880,6 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
       }
     };
 
-    constexpr int TILE_VMEM = L::TILE_VMEM + 1;   // four tensors + this wave's statistic
     // All waves issue the same count (the statistic load is exec-masked, not skipped).
     // Before step t's wait, tiles t and t+1 may be in flight (t+2 is issued after it).
     auto wait_tile = [&](int j) {
@@ -760,10 +887,12 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
       else wait_vmcnt<0>();
     };
     const int n_steps = n_qt - t_begin;
-    if (n_steps > 0) issue_tile(t_begin, stage0);
-    if (n_steps > 1) issue_tile(t_begin + 1, stage1);
+    // A walking item's first head has its tiles t_begin, t_begin + 1 in flight already.
+    const bool pre = WALK && g == 0;
+    if (!pre && n_steps > 0) issue_tile(t_begin, stage0);
+    if (!pre && n_steps > 1) issue_tile(t_begin + 1, stage1);
     auto step = [&](int t_idx, const char* cur, char* dma) {
-      wait_tile(t_idx);
+      if (!(pre && t_idx == t_begin)) wait_tile(t_idx);   // else done before the K / V reads
       ring_barrier();
       if (t_idx + 2 < n_qt) issue_tile(t_idx + 2, dma);
       if (t_idx >= first) tile(t_idx, cur);
@@ -779,7 +908,35 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
     if (g + 1 < a.grp) ring_barrier();
   }
 
-  if (kj < a.Nk) {
+  if (WALK && next_item >= 0) {
+    ring_barrier();   // every wave is done with ops and the ring
+    prefetch(next_item);
+  }
+
+  if constexpr (WALK) {
+    // Every wave issues kEpStores stores (keys past Nk land out of range; an
+    // absent dtk / dtv has a 0-byte resource).
+    const int64_t ob = int64_t(bhk) * a.Nk * D * 2;
+    const int64_t ab = int64_t(a.Nk) * D * 2;
+    const Rsrc rdk = make_rsrc(static_cast<char*>(a.dk) + ob, ab), rdv = make_rsrc(static_cast<char*>(a.dv) + ob, ab);
+    const Rsrc rdtk = make_rsrc(a.dtk ? static_cast<char*>(a.dtk) + ob : static_cast<char*>(a.dk), a.dtk ? ab : 0);
+    const Rsrc rdtv = make_rsrc(a.dtv ? static_cast<char*>(a.dtv) + ob : static_cast<char*>(a.dv), a.dtv ? ab : 0);
+    const float sc = a.scale;
+#pragma unroll
+    for (int t = 0; t < L::NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * t + 8 * g + 4 * hlf;
+        const int e = 4 * g;
+        const int off = kj < a.Nk ? (kj * D + dd) * 2 : kOutOfRange;
+        st64(rdk, off, uint2{T::pack2(accK[t][e] * sc, accK[t][e + 1] * sc),
+                             T::pack2(accK[t][e + 2] * sc, accK[t][e + 3] * sc)});
+        st64(rdtk, off, uint2{T::pack2(accTK[t][e] * sc, accTK[t][e + 1] * sc),
+                              T::pack2(accTK[t][e + 2] * sc, accTK[t][e + 3] * sc)});
+        st64(rdv, off, uint2{T::pack2(accV[t][e], accV[t][e + 1]), T::pack2(accV[t][e + 2], accV[t][e + 3])});
+        st64(rdtv, off, uint2{T::pack2(accTV[t][e], accTV[t][e + 1]), T::pack2(accTV[t][e + 2], accTV[t][e + 3])});
+      }
+  } else if (kj < a.Nk) {
     const int64_t base = int64_t(bhk) * a.Nk * D + int64_t(kj) * D;
     uint16_t* dk = static_cast<uint16_t*>(a.dk) + base;
     uint16_t* dtk = static_cast<uint16_t*>(a.dtk) + base;
@@ -813,7 +970,20 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a) {
 template <typename T, int D, int PART, int MASK, bool CAUSAL, bool POW2>
 __global__ __launch_bounds__(kBThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  bwd_dkv_body<T, D, PART, MASK, CAUSAL, POW2>(a);
+  if constexpr (dkv_walks<D, PART, MASK>()) {
+    // Items blockIdx.x + r * gridDim.x, odd rounds reversed within each XCD
+    // so heavy and light causal key blocks pair up.
+    const int gsz = int(gridDim.x), bx = int(blockIdx.x);
+    const int brev = (gsz & 7) == 0 ? (gsz / 8 - 1 - bx / 8) * 8 + (bx & 7) : bx;
+    int it = bx;
+    for (int r = 0; it < a.n_items; ++r) {
+      const int nx = (r + 1) * gsz + ((r & 1) ? bx : brev);
+      bwd_dkv_body<T, D, PART, MASK, CAUSAL, POW2>(a, it, nx < a.n_items ? nx : -1, r > 0);
+      it = nx;
+    }
+  } else {
+    bwd_dkv_body<T, D, PART, MASK, CAUSAL, POW2>(a, int(blockIdx.x), -1, false);
+  }
 #endif
 }
 
@@ -1264,10 +1434,14 @@ hipError_t launch_tiles(BwdArgs a, hipStream_t s) {
     if (nkb == 0 || a.BHK == 0) return hipSuccess;
     BwdArgs ak = a;
     ak.n_blk = static_cast<int>(nkb);
-    const dim3 grid(unsigned(nkb * a.BHK));
+    ak.n_items = static_cast<int>(nkb * a.BHK);
     if constexpr (D == 64) {
+      // the walking instance runs at most a.max_wgs workgroups (a multiple of 8, so each keeps its XCD)
+      const int64_t cap = dkv_walks<D, kAllParts, MASK>() ? a.max_wgs : 0;
+      const dim3 grid(unsigned(cap > 0 && cap < ak.n_items ? cap : ak.n_items));
       hipLaunchKernelGGL((bwd_dkv_kernel<T, D, kAllParts, MASK, CAUSAL, POW2>), grid, dim3(kBThreads), 0, s, ak);
     } else {
+      const dim3 grid(unsigned(ak.n_items));
       hipLaunchKernelGGL((bwd_dkv_kernel<T, D, kKeyPart, MASK, CAUSAL, POW2>), grid, dim3(kBThreads), 0, s, ak);
       hipLaunchKernelGGL((bwd_dkv_kernel<T, D, kValuePart, MASK, CAUSAL, POW2>), grid, dim3(kBThreads), 0, s, ak);
     }

@@ -43,6 +43,8 @@ struct BwdArgs {
   int grp;            // query heads per key/value head (grouped-query attention; 1 = one each)
   int BHK;            // key/value heads in all: B * H / grp
   int n_blk;
+  int n_items;        // key-side items (key blocks x K/V heads) the walking dkv kernel covers
+  int max_wgs;        // grid of a walking kernel (0: one workgroup per item)
   int mask_vec;
   int64_t msb, msh, msq;
   float scale;

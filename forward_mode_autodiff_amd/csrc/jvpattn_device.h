@@ -99,6 +99,10 @@ struct F16 {
 __device__ inline uint32_t lo16(uint32_t x) { return x & 0xffffu; }
 __device__ inline uint32_t hi16(uint32_t x) { return x >> 16; }
 
+// A buffer offset past every record (one head is at most 2 GiB - 256 rows): loads read zeros,
+// stores are dropped.
+constexpr int kOutOfRange = 0x7ffffff0;
+
 // Buffer resources: loads at byte offsets >= the record count return zero, so
 // ragged tails and absent (NULL) tangents need no branches.
 typedef __amdgpu_buffer_rsrc_t Rsrc;

@@ -141,9 +141,7 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   a.n_items = static_cast<int>(blocks);
   int64_t wgs = blocks;
   if (kernel == kFwdWG4 && mk == JVPATTN_MASK_NONE && p->dtype == JVPATTN_BF16 && dphys == 128 && !pow2) {
-    const int forced = g_max_workgroups.load(std::memory_order_relaxed);
-    int64_t cap = forced > 0 ? forced : int64_t(cu_count());
-    if (cap >= 8) cap &= ~int64_t(7);
+    const int64_t cap = walk_workgroups();
     if (cap > 0 && cap < blocks) wgs = cap;
   }
   const dim3 grid(static_cast<unsigned>(wgs));
@@ -178,6 +176,14 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
 }
 
 }  // namespace
+
+int walk_workgroups() {
+  const int forced = g_max_workgroups.load(std::memory_order_relaxed);
+  int cap = forced > 0 ? forced : cu_count();
+  if (cap >= 8) cap &= ~7;
+  return cap;
+}
+
 }  // namespace jvpattn
 
 extern "C" int jvpattn_fwd(const jvpattn_params* p, const void* q, const void* k, const void* v,
@@ -200,7 +206,7 @@ extern "C" int jvpattn_fwd_tmask(const jvpattn_params* p, const void* q, const v
   return fwd_launch(p, sz, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, stream);
 }
 
-extern "C" int jvpattn_fwd_set_workgroups(int max_workgroups) {
+extern "C" int jvpattn_set_workgroups(int max_workgroups) {
   using namespace jvpattn;
   if (max_workgroups < 0) return JVPATTN_ERR_ARG;
   g_max_workgroups.store(max_workgroups, std::memory_order_relaxed);

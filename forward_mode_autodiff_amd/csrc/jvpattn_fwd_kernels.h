@@ -44,8 +44,6 @@
 namespace jvpattn {
 namespace {
 
-// A buffer offset past every record (one head is at most 2 GiB - 256 rows): loads read zeros.
-constexpr int kOutOfRange = 0x7ffffff0;
 
 constexpr int kWaves = 4;             // waves per workgroup
 constexpr int kThreads = 64 * kWaves;

@@ -54,4 +54,10 @@ extern thread_local int g_last_hip_error;
 // Workspace of jvpattn_bwd: four float32 arrays of B*H*Nq (see jvpattn_bwd.hip).
 int64_t bwd_workspace_bytes(int64_t rows_q);
 
+// Grid of the kernels that walk their blocks (several per workgroup): the
+// cap set by jvpattn_set_workgroups, else one workgroup per CU of the current
+// device; rounded down to a multiple of 8 (so each workgroup keeps its XCD)
+// when at least 8; 0 if unknown (then every block gets its own workgroup).
+int walk_workgroups();
+
 }  // namespace jvpattn

@@ -86,8 +86,8 @@ def load_library(path: str = LIB_PATH):
     lib.jvpattn_bwd_noalloc.restype = ctypes.c_int
     lib.jvpattn_fwd_set_algo.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.jvpattn_fwd_set_algo.restype = ctypes.c_int
-    lib.jvpattn_fwd_set_workgroups.argtypes = [ctypes.c_int]
-    lib.jvpattn_fwd_set_workgroups.restype = ctypes.c_int
+    lib.jvpattn_set_workgroups.argtypes = [ctypes.c_int]
+    lib.jvpattn_set_workgroups.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -107,11 +107,11 @@ def jvpattn_fwd_set_algo(kernel=None, order=None, key_range=None) -> None:
         raise JvpattnError(rc, jvpattn_strerror(rc))
 
 
-def jvpattn_fwd_set_workgroups(max_workgroups: int = 0) -> None:
-    """Cap the workgroups of the mask-free bfloat16 d = 96 / 128 forward kernel, which walks its 128-row
-    blocks with a grid smaller than their count (0 = the library's choice: one workgroup per CU).
-    Results do not depend on it; for tests and tuning."""
-    rc = load_library().jvpattn_fwd_set_workgroups(int(max_workgroups))
+def jvpattn_set_workgroups(max_workgroups: int = 0) -> None:
+    """Cap the workgroups of the kernels that walk several blocks per workgroup (the mask-free bfloat16
+    d = 96 / 128 forward, the mask-free d = 64 key side of the reverse pass); 0 = the library's choice,
+    one workgroup per CU. Results do not depend on it; for tests and tuning."""
+    rc = load_library().jvpattn_set_workgroups(int(max_workgroups))
     if rc != 0:
         raise JvpattnError(rc, jvpattn_strerror(rc))
 

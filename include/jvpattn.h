@@ -312,14 +312,16 @@ typedef enum {
  * range. Not meant to be changed while another thread launches forwards. */
 int jvpattn_fwd_set_algo(int kernel, int order, int key_range);
 
-/* Cap the workgroups of the mask-free forward kernel for bfloat16 d = 96 / 128
- * (scale not a power of two), which walks its 128-row blocks with a grid
- * smaller than their count: 0 (the default) = what the chip holds at once (one
- * workgroup per CU, rounded down to a multiple of 8); n > 0 = at most n
- * (rounded down to a multiple of 8 when n >= 8). Results do not depend on it.
- * A process-wide setting for later calls, like jvpattn_fwd_set_algo; for
- * tests and tuning. Returns JVPATTN_OK, or JVPATTN_ERR_ARG for n < 0. */
-int jvpattn_fwd_set_workgroups(int max_workgroups);
+/* Cap the workgroups of the kernels that walk several blocks per workgroup
+ * (with a grid smaller than their count): the mask-free forward kernel for
+ * bfloat16 d = 96 / 128 (scale not a power of two) and the mask-free key side
+ * of jvpattn_bwd / jvpattn_bwd_noalloc at d = 64. 0 (the default) = what the
+ * chip holds at once (one workgroup per CU, rounded down to a multiple of 8);
+ * n > 0 = at most n (rounded down to a multiple of 8 when n >= 8). Results do
+ * not depend on it. A process-wide setting for later calls, like
+ * jvpattn_fwd_set_algo; for tests and tuning. Returns JVPATTN_OK, or
+ * JVPATTN_ERR_ARG for n < 0. */
+int jvpattn_set_workgroups(int max_workgroups);
 
 /* A static, human-readable description of a return code. */
 const char* jvpattn_strerror(int code);

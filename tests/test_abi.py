@@ -27,7 +27,7 @@ def test_header_declares_entry_points():
                                     "jvpattn_bwd_workspace_bytes", "jvpattn_check_bwd", "jvpattn_check_bwd_tmask",
                                     "jvpattn_check_fwd",
                                     "jvpattn_check_fwd_tmask", "jvpattn_fwd", "jvpattn_fwd_set_algo",
-                                    "jvpattn_fwd_set_workgroups", "jvpattn_fwd_tmask", "jvpattn_last_hip_error",
+                                    "jvpattn_fwd_tmask", "jvpattn_last_hip_error", "jvpattn_set_workgroups",
                                     "jvpattn_strerror"]
 
 
@@ -432,14 +432,14 @@ def test_fwd_set_algo_rejects_out_of_range_values():
 
 
 @needs_lib
-def test_fwd_set_workgroups_rejects_negative_caps():
+def test_set_workgroups_rejects_negative_caps():
     lib = J.load_library()
-    assert lib.jvpattn_fwd_set_workgroups(-1) == -11
+    assert lib.jvpattn_set_workgroups(-1) == -11
     for n in (5, 8, 1 << 30, 0):
-        assert lib.jvpattn_fwd_set_workgroups(n) == 0, n
+        assert lib.jvpattn_set_workgroups(n) == 0, n
     with pytest.raises(J.JvpattnError):
-        J.jvpattn_fwd_set_workgroups(-3)
-    J.jvpattn_fwd_set_workgroups()
+        J.jvpattn_set_workgroups(-3)
+    J.jvpattn_set_workgroups()
 
 
 @needs_lib

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 from forward_mode_autodiff_amd import inputs as I
-from forward_mode_autodiff_amd.jvpattn import JvpattnError, jvpattn_bwd, jvpattn_fwd
+from forward_mode_autodiff_amd.jvpattn import JvpattnError, jvpattn_bwd, jvpattn_fwd, jvpattn_set_workgroups
 from tests.bwd_cases import HVP_HEADS, HVP_UNIT, SMALL, f64, magnitudes, reference, small as W
 from tests.parity import BWD_NAMES as NAMES, bwd_errors, bwd_failures
 
@@ -73,6 +73,36 @@ def check(w, x=None, tangents=("tq", "tk", "tv"), scale=None, heads=None, tmask=
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.dtype}-{'causal' if w.causal else 'full'}-std{w.std}")
 def test_small(w):
     check(w)
+
+
+@pytest.fixture
+def _walk_cap():
+    yield
+    jvpattn_set_workgroups()
+
+
+# The mask-free key side at d = 64 walks several (key block, K/V head) items
+# per workgroup: the next item's K, dK, V, dV rows and first query tiles load
+# during the current one's epilogue. A small cap forces many rounds on small
+# inputs: the same bits as one item per workgroup, and oracle parity.
+@pytest.mark.parametrize("cap", [8, 5, 24])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_walking_key_side(dtype, causal, cap, _walk_cap):
+    shapes = [dict(B=2, H=4, N=700), dict(B=4, H=8, Hkv=2, N=300), dict(B=1, H=3, N=200, Nk=450),
+              dict(B=2, H=2, N=40)]
+    for i, s in enumerate(shapes):
+        w = I.Workload(f"walkkv_{i}", d=64, dtype=dtype, causal=causal, std=1.0, seed=80 + i, **s)
+        x = I.make_inputs(w, cotangents=True)
+        jvpattn_set_workgroups(1 << 30)   # one item per workgroup
+        one = gpu_bwd(x, w)
+        jvpattn_set_workgroups(cap)
+        got = gpu_bwd(x, w)
+        for n in NAMES:
+            assert np.array_equal(one[n], got[n]), (w.name, n)
+        ref = reference(x, w)
+        bad = bwd_failures(got, ref, magnitudes(x, w), w.dtype)
+        assert not bad, f"{w.name}: " + "; ".join(bad)
 
 
 @pytest.mark.parametrize("N", [1, 31, 32, 33, 97, 128, 129, 257, 513])

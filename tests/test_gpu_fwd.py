@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from forward_mode_autodiff_amd import inputs as I
-from forward_mode_autodiff_amd.jvpattn import jvpattn_fwd, jvpattn_fwd_set_algo, jvpattn_fwd_set_workgroups
+from forward_mode_autodiff_amd.jvpattn import jvpattn_fwd, jvpattn_fwd_set_algo, jvpattn_set_workgroups
 from oracle import oracle_fwd
 from tests.parity import assert_parity, failures
 
@@ -32,10 +32,10 @@ KERNELS = ["pp", "wg4", "split", "split64"]
 def _automatic_plan():
     """Every test starts and ends with the library's own launch plan."""
     jvpattn_fwd_set_algo()
-    jvpattn_fwd_set_workgroups()
+    jvpattn_set_workgroups()
     yield
     jvpattn_fwd_set_algo()
-    jvpattn_fwd_set_workgroups()
+    jvpattn_set_workgroups()
 
 
 @pytest.fixture(params=KERNELS)
@@ -240,9 +240,9 @@ def test_walking_row_blocks(d, dtype, causal, cap):
         x = I.make_inputs(w)
         for order in (None, "head"):
             jvpattn_fwd_set_algo(order=order)
-            jvpattn_fwd_set_workgroups(1 << 30)   # one block per workgroup
+            jvpattn_set_workgroups(1 << 30)   # one block per workgroup
             one = gpu_run(x, causal)
-            jvpattn_fwd_set_workgroups(cap)
+            jvpattn_set_workgroups(cap)
             walk = gpu_run(x, causal)
             for n in one:
                 assert torch.equal(one[n], walk[n]), (w.name, order, n)
