@@ -27,7 +27,9 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "jvpattn.h"
 #include "jvpattn_bwd_launch.h"
@@ -39,13 +41,67 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Running the query side beside the key side. The two kernels share only
+// the rows kernel's output, so the query side may run on a second stream
+// that waits for the rows kernel, and the caller's stream waits for it in
+// turn: as the key side's workgroups finish, the query side's take their
+// compute units, instead of starting only after the last key-side workgroup.
+// The second stream and its two events are the library's, one set per
+// device, created on first use and kept until the process ends; a mutex
+// holds the record-wait-launch sequence together across host threads.
+// Mode (jvpattn_bwd_set_overlap): -1 automatic, 0 one stream, 1 two streams.
+// Automatic takes two streams for grouped K/V heads, whose key-side
+// workgroups each carry all query heads of a group and end far apart under
+// a causal limit, and at d = 128 (the key side in two launches); the
+// walking d = 64 key side ends nearly together, and there the second stream
+// only costs.
+std::atomic<int> g_overlap{-1};
+
+constexpr int kMaxSideDevices = 64;
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t rows = nullptr;   // recorded on the caller's stream after the rows kernel
+  hipEvent_t done = nullptr;   // recorded on the side stream after the query side
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxSideDevices];
+
+// The side stream set of `dev` (g_side_mu held).
+hipError_t side_stream(int dev, SideStream** out) {
+  if (dev < 0 || dev >= kMaxSideDevices) return hipErrorInvalidDevice;
+  SideStream& x = g_side[dev];
+  if (!x.s) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    SideStream n;
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.rows, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.done, hipEventDisableTiming);
+    if (cur >= 0 && cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) {
+      if (n.done) (void)hipEventDestroy(n.done);
+      if (n.rows) (void)hipEventDestroy(n.rows);
+      if (n.s) (void)hipStreamDestroy(n.s);
+      return e;
+    }
+    x = n;
+  }
+  *out = &x;
+  return hipSuccess;
+}
+
 // Queue the reverse pass for arguments already validated; tmask: the
 // additive mask's tangent the forward carried, or NULL.
+// may_fork: the query side may run on the library's second stream.
 int bwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const void* k, const void* v,
                const void* tq, const void* tk, const void* tv, const void* mask, const void* tmask,
                const void* o, const void* to, const float* lse, const float* tlse, const void* go,
                const void* gto, void* dq, void* dk, void* dv, void* dtq, void* dtk, void* dtv, void* workspace,
-               void* stream) {
+               void* stream, bool may_fork) {
   if (sz.rows_q == 0 && sz.rows_k == 0) return JVPATTN_OK;
 
   BwdArgs a;
@@ -80,11 +136,42 @@ int bwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   const int kind = tmask ? kMaskAddT : p->mask_kind;
   const jvpattn_dtype dt = static_cast<jvpattn_dtype>(p->dtype);
   const bool c = p->causal != 0;
-  hipError_t e = p->d == 64 ? bwd_launch_part<kLaunchDkv, 64>(a, sz.rows_q, dt, kind, c, pow2, s)
-                            : bwd_launch_part<kLaunchDkv, 128>(a, sz.rows_q, dt, kind, c, pow2, s);
-  if (e == hipSuccess)
-    e = p->d == 64 ? bwd_launch_part<kLaunchDq, 64>(a, sz.rows_q, dt, kind, c, pow2, s)
-                   : bwd_launch_part<kLaunchDq, 128>(a, sz.rows_q, dt, kind, c, pow2, s);
+  auto part = [&](auto which, hipStream_t st) {
+    constexpr int W = decltype(which)::value;
+    return p->d == 64 ? bwd_launch_part<W, 64>(a, sz.rows_q, dt, kind, c, pow2, st)
+                      : bwd_launch_part<W, 128>(a, sz.rows_q, dt, kind, c, pow2, st);
+  };
+  using Rows = std::integral_constant<int, kLaunchRows>;
+  using Dkv = std::integral_constant<int, kLaunchDkv>;
+  using Dq = std::integral_constant<int, kLaunchDq>;
+  const int mode = g_overlap.load(std::memory_order_relaxed);
+  bool fork = may_fork && sz.rows_q > 0 && sz.rows_k > 0 && (mode == 1 || (mode < 0 && (sz.group > 1 || p->d == 128)));
+  if (fork) {   // never inside a graph capture of the caller's stream
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t ce = hipStreamIsCapturing(s, &cs);
+    if (ce != hipSuccess) {
+      g_last_hip_error = static_cast<int>(ce);
+      return JVPATTN_ERR_HIP;
+    }
+    fork = cs == hipStreamCaptureStatusNone;
+  }
+  hipError_t e = part(Rows{}, s);
+  if (e == hipSuccess && fork) {
+    hipDevice_t dev = 0;
+    e = hipStreamGetDevice(s, &dev);
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* x = nullptr;
+    if (e == hipSuccess) e = side_stream(static_cast<int>(dev), &x);
+    if (e == hipSuccess) e = hipEventRecord(x->rows, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(x->s, x->rows, 0);
+    if (e == hipSuccess) e = part(Dkv{}, s);    // the key side is queued first
+    if (e == hipSuccess) e = part(Dq{}, x->s);
+    if (e == hipSuccess) e = hipEventRecord(x->done, x->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, x->done, 0);
+  } else if (e == hipSuccess) {
+    e = part(Dkv{}, s);
+    if (e == hipSuccess) e = part(Dq{}, s);
+  }
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
     return JVPATTN_ERR_HIP;
@@ -106,7 +193,7 @@ extern "C" int jvpattn_bwd(const jvpattn_params* p, const void* q, const void* k
                            workspace, workspace_bytes, &sz);
   if (rc != JVPATTN_OK) return rc;
   return bwd_launch(p, sz, q, k, v, tq, tk, tv, mask, nullptr, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk,
-                    dtv, workspace, stream);
+                    dtv, workspace, stream, true);
 }
 
 extern "C" int jvpattn_bwd_tmask(const jvpattn_params* p, const void* q, const void* k, const void* v,
@@ -121,7 +208,7 @@ extern "C" int jvpattn_bwd_tmask(const jvpattn_params* p, const void* q, const v
                                  dtk, dtv, workspace, workspace_bytes, &sz);
   if (rc != JVPATTN_OK) return rc;
   return bwd_launch(p, sz, q, k, v, tq, tk, tv, mask, tmask, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk,
-                    dtv, workspace, stream);
+                    dtv, workspace, stream, true);
 }
 
 // ------------------------------------------------- allocation-free variant
@@ -201,5 +288,11 @@ extern "C" int jvpattn_bwd_noalloc(const jvpattn_params* p, const void* q, const
                  static_cast<size_t>(kScratchBytes), &sz);
   if (rc != JVPATTN_OK) return rc;
   return bwd_launch(p, sz, q, k, v, tq, tk, tv, mask, nullptr, o, to, lse, tlse, go, gto, dq, dk, dv, dtq, dtk,
-                    dtv, ws, stream);
+                    dtv, ws, stream, false);   // no stream or event is created here
+}
+
+extern "C" int jvpattn_bwd_set_overlap(int mode) {
+  if (mode < -1 || mode > 1) return JVPATTN_ERR_ARG;
+  jvpattn::g_overlap.store(mode, std::memory_order_relaxed);
+  return JVPATTN_OK;
 }

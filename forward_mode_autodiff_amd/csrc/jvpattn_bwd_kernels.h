@@ -1523,30 +1523,32 @@ hipError_t bwd_launch_part(const BwdArgs& a, int64_t rows_q, jvpattn_dtype dtype
                            bool pow2, hipStream_t s) {
   if (dtype == JVPATTN_F32) {
     if constexpr (D == 64) {
-      if (WHICH == kLaunchDkv && rows_q > 0) {
+      if constexpr (WHICH == kLaunchRows) {
+        if (rows_q == 0) return hipSuccess;
         const int64_t nb = (rows_q * (D / 4) + kBThreads - 1) / kBThreads;   // d/4 lanes per row
         if (nb > INT32_MAX) return hipErrorInvalidValue;
         hipLaunchKernelGGL((bwd_rows32_kernel<D>), dim3(unsigned(nb)), dim3(kBThreads), 0, s, a, rows_q);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        return hipGetLastError();
+      } else {
+        return launch_type32<WHICH, D>(a, mask_kind, causal, s);
       }
-      return launch_type32<WHICH, D>(a, mask_kind, causal, s);
     } else {
       return hipErrorInvalidValue;   // the validator admits float32 at d = 64 only
     }
   }
-  if (WHICH == kLaunchDkv && rows_q > 0) {   // the rows kernel builds with the key side
+  if constexpr (WHICH == kLaunchRows) {   // built into the key side's object
+    if (rows_q == 0) return hipSuccess;
     const int64_t nb = (rows_q * (D / 8) + kBThreads - 1) / kBThreads;   // d/8 lanes per row
     if (nb > INT32_MAX) return hipErrorInvalidValue;
     if (dtype == JVPATTN_BF16)
       hipLaunchKernelGGL((bwd_rows_kernel<BF16, D>), dim3(unsigned(nb)), dim3(kBThreads), 0, s, a, rows_q);
     else
       hipLaunchKernelGGL((bwd_rows_kernel<F16, D>), dim3(unsigned(nb)), dim3(kBThreads), 0, s, a, rows_q);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+  } else {
+    return dtype == JVPATTN_BF16 ? launch_type<WHICH, BF16, D>(a, mask_kind, causal, pow2, s)
+                                 : launch_type<WHICH, F16, D>(a, mask_kind, causal, pow2, s);
   }
-  return dtype == JVPATTN_BF16 ? launch_type<WHICH, BF16, D>(a, mask_kind, causal, pow2, s)
-                               : launch_type<WHICH, F16, D>(a, mask_kind, causal, pow2, s);
 }
 
 

@@ -55,12 +55,13 @@ struct BwdArgs {
 enum { WS_NEGL = 0, WS_TLSE = 1, WS_R = 2, WS_DEL = 3 };
 
 // Queue the kernels of head dimension D (64 or 128) for validated
-// arguments: WHICH = kLaunchDkv the rows kernel (per-row statistics into the
-// workspace) and the key-side gradients, kLaunchDq the query-side ones, to be
-// called in that order on one stream. mask_kind may be kMaskAddT (an
-// additive mask with a tangent); pow2: the scale is a power of two (folded
-// into Q, K exactly in bfloat16).
-enum { kLaunchDkv = 0, kLaunchDq = 1 };
+// arguments: WHICH = kLaunchRows the rows kernel (per-row statistics into the
+// workspace), kLaunchDkv the key-side gradients, kLaunchDq the query-side
+// ones. Both sides read the workspace the rows kernel writes and nothing
+// else the other writes, so they may run in either order or at once once it
+// is done. mask_kind may be kMaskAddT (an additive mask with a tangent);
+// pow2: the scale is a power of two (folded into Q, K exactly in bfloat16).
+enum { kLaunchDkv = 0, kLaunchDq = 1, kLaunchRows = 2 };
 template <int WHICH, int D>
 hipError_t bwd_launch_part(const BwdArgs& a, int64_t rows_q, jvpattn_dtype dtype, int mask_kind, bool causal,
                            bool pow2, hipStream_t s);

@@ -88,6 +88,8 @@ def load_library(path: str = LIB_PATH):
     lib.jvpattn_fwd_set_algo.restype = ctypes.c_int
     lib.jvpattn_set_workgroups.argtypes = [ctypes.c_int]
     lib.jvpattn_set_workgroups.restype = ctypes.c_int
+    lib.jvpattn_bwd_set_overlap.argtypes = [ctypes.c_int]
+    lib.jvpattn_bwd_set_overlap.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -112,6 +114,17 @@ def jvpattn_set_workgroups(max_workgroups: int = 0) -> None:
     d = 96 / 128 forward, the mask-free d = 64 key side of the reverse pass); 0 = the library's choice,
     one workgroup per CU. Results do not depend on it; for tests and tuning."""
     rc = load_library().jvpattn_set_workgroups(int(max_workgroups))
+    if rc != 0:
+        raise JvpattnError(rc, jvpattn_strerror(rc))
+
+
+def jvpattn_bwd_set_overlap(overlap=None) -> None:
+    """How the reverse pass queues its key and query sides: False = one after the other on the
+    caller's stream, True = the query side on a second stream of the library's, beside the key side;
+    None = the library's choice (True for grouped key/value heads and d = 128). Results do not depend
+    on it."""
+    mode = -1 if overlap is None else int(bool(overlap))
+    rc = load_library().jvpattn_bwd_set_overlap(mode)
     if rc != 0:
         raise JvpattnError(rc, jvpattn_strerror(rc))
 

@@ -323,6 +323,23 @@ int jvpattn_fwd_set_algo(int kernel, int order, int key_range);
  * JVPATTN_ERR_ARG for n < 0. */
 int jvpattn_set_workgroups(int max_workgroups);
 
+/* How jvpattn_bwd / jvpattn_bwd_tmask queue their key-side and query-side
+ * kernels, which depend only on the per-row statistics both read:
+ *   0 : one after the other on the caller's stream;
+ *   1 : the query side on a second stream of the library's (one per device,
+ *       created with two events on the first such call and kept until the
+ *       process ends), which waits for the statistics on the caller's stream;
+ *       the caller's stream then waits for the query side, so work queued on
+ *       it afterwards sees every gradient, as in mode 0. The query side's
+ *       workgroups take the compute units the key side's release;
+ *  -1 : (the default) mode 1 for grouped key/value heads (Hkv < H), where the
+ *       key side's workgroups end far apart, and for d = 128; else mode 0.
+ * A call whose stream is being captured into a graph, and every
+ * jvpattn_bwd_noalloc call, uses mode 0. Results do not depend on the mode.
+ * Process-wide, for later calls. Returns JVPATTN_OK, or JVPATTN_ERR_ARG for
+ * another value. */
+int jvpattn_bwd_set_overlap(int mode);
+
 /* A static, human-readable description of a return code. */
 const char* jvpattn_strerror(int code);
 

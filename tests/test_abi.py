@@ -23,7 +23,8 @@ def declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["jvpattn_bwd", "jvpattn_bwd_noalloc", "jvpattn_bwd_tmask",
+    assert declared_functions() == ["jvpattn_bwd", "jvpattn_bwd_noalloc", "jvpattn_bwd_set_overlap",
+                                    "jvpattn_bwd_tmask",
                                     "jvpattn_bwd_workspace_bytes", "jvpattn_check_bwd", "jvpattn_check_bwd_tmask",
                                     "jvpattn_check_fwd",
                                     "jvpattn_check_fwd_tmask", "jvpattn_fwd", "jvpattn_fwd_set_algo",
@@ -429,6 +430,17 @@ def test_fwd_set_algo_rejects_out_of_range_values():
     assert lib.jvpattn_fwd_set_algo(-1, -1, -1) == 0
     with pytest.raises(KeyError):
         J.jvpattn_fwd_set_algo(kernel="nope")
+
+
+@needs_lib
+def test_bwd_set_overlap_rejects_other_modes():
+    lib = J.load_library()
+    for m in (-2, 2, 1 << 20):
+        assert lib.jvpattn_bwd_set_overlap(m) == -11, m
+    for m in (0, 1, -1):
+        assert lib.jvpattn_bwd_set_overlap(m) == 0, m
+    J.jvpattn_bwd_set_overlap(True)
+    J.jvpattn_bwd_set_overlap()
 
 
 @needs_lib

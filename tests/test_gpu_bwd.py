@@ -18,7 +18,8 @@ import pytest
 import torch
 
 from forward_mode_autodiff_amd import inputs as I
-from forward_mode_autodiff_amd.jvpattn import JvpattnError, jvpattn_bwd, jvpattn_fwd, jvpattn_set_workgroups
+from forward_mode_autodiff_amd.jvpattn import (JvpattnError, jvpattn_bwd, jvpattn_bwd_set_overlap, jvpattn_fwd,
+                                              jvpattn_set_workgroups)
 from tests.bwd_cases import HVP_HEADS, HVP_UNIT, SMALL, f64, magnitudes, reference, small as W
 from tests.parity import BWD_NAMES as NAMES, bwd_errors, bwd_failures
 
@@ -103,6 +104,64 @@ def test_walking_key_side(dtype, causal, cap, _walk_cap):
         ref = reference(x, w)
         bad = bwd_failures(got, ref, magnitudes(x, w), w.dtype)
         assert not bad, f"{w.name}: " + "; ".join(bad)
+
+
+@pytest.fixture
+def _overlap_auto():
+    yield
+    jvpattn_bwd_set_overlap()
+
+
+# The query side may run on a second stream beside the key side (the
+# default for grouped K/V heads): the same bits as one stream, for every
+# kernel family (d = 64 walking and masked, d = 128 in two key-side launches,
+# float32), and oracle parity on the two-stream results.
+@pytest.mark.parametrize("case", [
+    dict(B=2, H=4, N=700, d=64, dtype="bf16", causal=True),
+    dict(B=4, H=8, Hkv=2, N=300, d=64, dtype="f16", causal=True),
+    dict(B=1, H=4, Hkv=1, N=157, d=64, dtype="bf16", mask_kind="bool", mask_heads=4, keep=0.6),
+    dict(B=1, H=4, Hkv=2, N=200, Nk=260, d=128, dtype="bf16", causal=True),
+    dict(B=1, H=4, Hkv=2, N=150, d=64, dtype="f32", causal=True),
+], ids=["mha-walk", "gqa-walk-f16", "mqa-bool", "gqa-d128", "gqa-f32"])
+def test_overlap_modes_agree(case, _overlap_auto):
+    w = I.Workload("overlap", std=1.0, seed=90, **case)
+    x = I.make_inputs(w, cotangents=True)
+    jvpattn_bwd_set_overlap(False)
+    one = gpu_bwd(x, w)
+    jvpattn_bwd_set_overlap(True)
+    two = gpu_bwd(x, w)
+    for n in NAMES:
+        assert np.array_equal(one[n], two[n]), n
+    bad = bwd_failures(two, reference(x, w), magnitudes(x, w), w.dtype)
+    assert not bad, "; ".join(bad)
+
+
+def test_overlap_joins_the_callers_stream(_overlap_auto):
+    """Work queued on the caller's stream right after a two-stream call sees every gradient:
+    copies taken on a non-default stream with no host synchronisation in between, over
+    several calls in a row."""
+    w = I.Workload("overlap_join", B=4, H=8, Hkv=2, N=700, d=64, dtype="bf16", causal=True, std=1.0, seed=91)
+    x = I.make_inputs(w, cotangents=True)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in x.items()}
+    o, to, lse, tlse = jvpattn_fwd(d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], causal=True)
+    args = (d["q"], d["k"], d["v"], d["tq"], d["tk"], d["tv"], o, to, lse, tlse, d["do"], d["dto"])
+    jvpattn_bwd_set_overlap(False)
+    ref = [t.clone() for t in jvpattn_bwd(*args, causal=True)]
+    torch.cuda.synchronize()
+    jvpattn_bwd_set_overlap(True)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        copies = []
+        for _ in range(3):
+            g = jvpattn_bwd(*args, causal=True)
+            copies.append([t.clone() for t in g])
+            for t in g:
+                t.fill_(float("nan"))   # the next call must overwrite them after this, in stream order
+    torch.cuda.synchronize()
+    for c in copies:
+        for n, a, b in zip(NAMES, ref, c):
+            assert torch.equal(a, b), n
 
 
 @pytest.mark.parametrize("N", [1, 31, 32, 33, 97, 128, 129, 257, 513])
