@@ -50,12 +50,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 // device, created on first use and kept until the process ends; a mutex
 // holds the record-wait-launch sequence together across host threads.
 // Mode (jvpattn_bwd_set_overlap): -1 automatic, 0 one stream, 1 two streams.
-// Automatic takes two streams for grouped K/V heads, whose key-side
-// workgroups each carry all query heads of a group and end far apart under
-// a causal limit, and at d = 128 (the key side in two launches); the
-// walking d = 64 key side ends nearly together, and there the second stream
-// only costs.
+// Automatic takes two streams where the key side alone would leave compute
+// units idle: fewer key-side items (128-key blocks x K/V heads) than CUs;
+// under a causal limit, fewer than two per CU (one item per workgroup, the
+// first key blocks many times longer than the last; with two or more per
+// workgroup the walking order pairs long with short ones); and at d = 128
+// (the key side in two launches). Elsewhere the key side's workgroups end
+// nearly together and a second kernel only takes CUs from its last items.
 std::atomic<int> g_overlap{-1};
+
+// Compute units of the current device (queried once per device), or 0.
+int current_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cus[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) n = 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 constexpr int kMaxSideDevices = 64;
 struct SideStream {
@@ -145,7 +161,12 @@ int bwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   using Dkv = std::integral_constant<int, kLaunchDkv>;
   using Dq = std::integral_constant<int, kLaunchDq>;
   const int mode = g_overlap.load(std::memory_order_relaxed);
-  bool fork = may_fork && sz.rows_q > 0 && sz.rows_k > 0 && (mode == 1 || (mode < 0 && (sz.group > 1 || p->d == 128)));
+  bool fork = may_fork && sz.rows_q > 0 && sz.rows_k > 0 && mode != 0;
+  if (fork && mode < 0) {
+    const int64_t items = (int64_t(p->Nk) + kBBlk - 1) / kBBlk * a.BHK;
+    const int64_t cus = current_cus();
+    fork = p->d == 128 || items < cus || (c && items < 2 * cus);
+  }
   if (fork) {   // never inside a graph capture of the caller's stream
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     hipError_t ce = hipStreamIsCapturing(s, &cs);

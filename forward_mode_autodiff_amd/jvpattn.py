@@ -121,8 +121,8 @@ def jvpattn_set_workgroups(max_workgroups: int = 0) -> None:
 def jvpattn_bwd_set_overlap(overlap=None) -> None:
     """How the reverse pass queues its key and query sides: False = one after the other on the
     caller's stream, True = the query side on a second stream of the library's, beside the key side;
-    None = the library's choice (True for grouped key/value heads and d = 128). Results do not depend
-    on it."""
+    None = the library's choice (True where the key side alone would leave compute units idle, and for
+    d = 128). Results do not depend on it."""
     mode = -1 if overlap is None else int(bool(overlap))
     rc = load_library().jvpattn_bwd_set_overlap(mode)
     if rc != 0:

@@ -332,8 +332,10 @@ int jvpattn_set_workgroups(int max_workgroups);
  *       the caller's stream then waits for the query side, so work queued on
  *       it afterwards sees every gradient, as in mode 0. The query side's
  *       workgroups take the compute units the key side's release;
- *  -1 : (the default) mode 1 for grouped key/value heads (Hkv < H), where the
- *       key side's workgroups end far apart, and for d = 128; else mode 0.
+ *  -1 : (the default) mode 1 where the key side alone would leave compute
+ *       units idle -- fewer key-side items (128-key blocks times key/value
+ *       heads) than CUs, or with causal set fewer than two per CU -- and for
+ *       d = 128; else mode 0.
  * A call whose stream is being captured into a graph, and every
  * jvpattn_bwd_noalloc call, uses mode 0. Results do not depend on the mode.
  * Process-wide, for later calls. Returns JVPATTN_OK, or JVPATTN_ERR_ARG for
