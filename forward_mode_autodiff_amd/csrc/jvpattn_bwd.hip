@@ -132,6 +132,7 @@ int bwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   a.n_blk = 0;
   a.n_items = 0;
   a.max_wgs = walk_workgroups();
+  a.dq_two = 0;
   a.msb = p->mask_stride_b; a.msh = p->mask_stride_h; a.msq = p->mask_stride_q;
   a.scale = p->scale;
   a.inv_scale = 1.0f / p->scale;
@@ -175,6 +176,15 @@ int bwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
       return JVPATTN_ERR_HIP;
     }
     fork = cs == hipStreamCaptureStatusNone;
+  }
+  // The query side at d = 64 on its two-workgroups-per-CU kernel once its grid
+  // is four or more workgroups per CU and it has the chip to itself; the
+  // pipelined kernel (one per CU) is faster on smaller grids and beside the
+  // key side.
+  {
+    const int64_t qblocks = (int64_t(p->Nq) + kBBlk - 1) / kBBlk * a.BH;
+    const int64_t cus = current_cus();
+    a.dq_two = p->d == 64 && p->dtype != JVPATTN_F32 && !fork && cus > 0 && qblocks >= 4 * cus;
   }
   hipError_t e = part(Rows{}, s);
   if (e == hipSuccess && fork) {

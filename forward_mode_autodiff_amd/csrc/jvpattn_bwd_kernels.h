@@ -124,13 +124,15 @@ __device__ inline Cot cotangents(float s, float sd, float x, float dm, float cx,
 //   S^T = K Q^T, Sd^T = dK Q^T + K dQ^T, X^T = V G^T + dV Gd^T, D^T = V Gd^T
 // (24 products), the cotangents per element, then
 //   dq^T += K^T Sbar^T + dK^T Sdbar^T,  dtq^T += K^T Sdbar^T  (12 products).
-// At d = 64 the score-side products of the next block overlap the current
-// block's element-wise step; at d = 128 two blocks' products would not fit
-// the registers, so blocks go one at a time.
-template <typename T, int D, int MASK, bool CAUSAL, bool POW2>
+// PIPE (d = 64 only): the score-side products of the next block overlap the
+// current block's element-wise step, at one wave per SIMD; without it blocks
+// go one at a time, and at d = 64 that fits two waves per SIMD (two
+// workgroups per CU: bwd_dq2_kernel). At d = 128 two blocks' products would
+// not fit the registers.
+template <typename T, int D, int MASK, bool CAUSAL, bool POW2, bool PIPE = (D == 64)>
 __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   using L = Tile16<D>;
-  constexpr bool PIPE = D == 64;
+  static_assert(!PIPE || D == 64, "the pipelined query side is built for d = 64");
   using vec8 = typename T::vec8;
   __shared__ __attribute__((aligned(16))) char stage0[L::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) char stage1[L::STAGE_BYTES];
@@ -450,6 +452,16 @@ template <typename T, int D, int MASK, bool CAUSAL, bool POW2>
 __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   bwd_dq_body<T, D, MASK, CAUSAL, POW2>(a);
+#endif
+}
+
+// d = 64 without the pipeline, two waves per SIMD: for grids of several
+// workgroups per CU, where a second workgroup on the CU hides what the
+// pipeline hides within one.
+template <typename T, int MASK, bool CAUSAL, bool POW2>
+__global__ __launch_bounds__(kBThreads, 2) void bwd_dq2_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  bwd_dq_body<T, 64, MASK, CAUSAL, POW2, false>(a);
 #endif
 }
 
@@ -1450,8 +1462,13 @@ hipError_t launch_tiles(BwdArgs a, hipStream_t s) {
     if (nqb == 0 || a.BH == 0) return hipSuccess;
     BwdArgs aq = a;
     aq.n_blk = static_cast<int>(nqb);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, MASK, CAUSAL, POW2>), dim3(unsigned(nqb * a.BH)), dim3(kBThreads), 0,
-                       s, aq);
+    const dim3 grid(unsigned(nqb * a.BH));
+    bool two = false;
+    if constexpr (D == 64) two = a.dq_two != 0;
+    if constexpr (D == 64) {
+      if (two) hipLaunchKernelGGL((bwd_dq2_kernel<T, MASK, CAUSAL, POW2>), grid, dim3(kBThreads), 0, s, aq);
+    }
+    if (!two) hipLaunchKernelGGL((bwd_dq_kernel<T, D, MASK, CAUSAL, POW2>), grid, dim3(kBThreads), 0, s, aq);
   }
   return hipGetLastError();
 }

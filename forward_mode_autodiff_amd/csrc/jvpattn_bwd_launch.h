@@ -45,6 +45,7 @@ struct BwdArgs {
   int n_blk;
   int n_items;        // key-side items (key blocks x K/V heads) the walking dkv kernel covers
   int max_wgs;        // grid of a walking kernel (0: one workgroup per item)
+  int dq_two;         // d = 64: the query side without its pipeline, two workgroups per CU
   int mask_vec;
   int64_t msb, msh, msq;
   float scale;

@@ -136,6 +136,19 @@ def test_overlap_modes_agree(case, _overlap_auto):
     assert not bad, "; ".join(bad)
 
 
+def test_query_side_kernels_agree_at_the_hvp_shape(_overlap_auto):
+    """At the HVP shape the query side runs on its two-workgroups-per-CU kernel with one stream and on
+    the pipelined kernel beside the key side with two: the same bits (oracle parity of the one-stream
+    call is test_hvp_workload_sampled_heads)."""
+    x = I.make_inputs(I.HVP, cotangents=True)
+    jvpattn_bwd_set_overlap(False)
+    one = gpu_bwd(x, I.HVP)
+    jvpattn_bwd_set_overlap(True)
+    two = gpu_bwd(x, I.HVP)
+    for n in NAMES:
+        assert np.array_equal(one[n], two[n]), n
+
+
 def test_overlap_joins_the_callers_stream(_overlap_auto):
     """Work queued on the caller's stream right after a two-stream call sees every gradient:
     copies taken on a non-default stream with no host synchronisation in between, over
