@@ -20,6 +20,10 @@ CASES = {
     "mha-causal-bf16": dict(B=2, H=4, N=520, d=64, dtype="bf16", causal=True),
     "gqa-causal-f16": dict(B=2, H=8, Hkv=2, N=300, d=64, dtype="f16", causal=True),
     "gqa-d128-bf16": dict(B=1, H=4, Hkv=2, N=200, Nk=260, d=128, dtype="bf16"),
+    # the HVP shape: ping-pong forward, walking key side, two-per-CU query side
+    "hvp-shape": dict(B=4, H=16, N=2048, d=64, dtype="bf16", causal=True),
+    # Wide-like d = 128 rows: the walking d = 128 forward
+    "d128-walk": dict(B=16, H=8, N=512, d=128, dtype="bf16"),
 }
 
 
