@@ -59,20 +59,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // nearly together and a second kernel only takes CUs from its last items.
 std::atomic<int> g_overlap{-1};
 
-// Compute units of the current device (queried once per device), or 0.
-int current_cus() {
-  constexpr int kMaxDev = 64;
-  static std::atomic<int> cus[kMaxDev];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) n = 0;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 constexpr int kMaxSideDevices = 64;
 struct SideStream {
   hipStream_t s = nullptr;
@@ -165,7 +151,7 @@ int bwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   bool fork = may_fork && sz.rows_q > 0 && sz.rows_k > 0 && mode != 0;
   if (fork && mode < 0) {
     const int64_t items = (int64_t(p->Nk) + kBBlk - 1) / kBBlk * a.BHK;
-    const int64_t cus = current_cus();
+    const int64_t cus = cu_count();
     fork = p->d == 128 || items < cus || (c && items < 2 * cus);
   }
   if (fork) {   // never inside a graph capture of the caller's stream
@@ -183,7 +169,7 @@ int bwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
   // key side.
   {
     const int64_t qblocks = (int64_t(p->Nq) + kBBlk - 1) / kBBlk * a.BH;
-    const int64_t cus = current_cus();
+    const int64_t cus = cu_count();
     a.dq_two = p->d == 64 && p->dtype != JVPATTN_F32 && !fork && cus > 0 && qblocks >= 4 * cus;
   }
   hipError_t e = part(Rows{}, s);

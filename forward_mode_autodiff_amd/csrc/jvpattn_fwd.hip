@@ -22,20 +22,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Process-wide algorithm selection (jvpattn_fwd_set_algo); -1 = automatic.
 std::atomic<int> g_algo_kernel{-1}, g_algo_order{-1}, g_algo_key_range{-1}, g_max_workgroups{0};
 
-// Compute units of the current device (queried once per device), or 0.
-int cu_count() {
-  constexpr int kMaxDev = 64;
-  static std::atomic<int> cus[kMaxDev];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) n = 0;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 // Queue the forward for arguments already validated (sizes from the check).
 // tmask: the additive mask's tangent, or NULL.
 int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const void* k, const void* v,
@@ -176,6 +162,19 @@ int fwd_launch(const jvpattn_params* p, const FwdSizes& sz, const void* q, const
 }
 
 }  // namespace
+
+int cu_count() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cus[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) n = 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 int walk_workgroups() {
   const int forced = g_max_workgroups.load(std::memory_order_relaxed);

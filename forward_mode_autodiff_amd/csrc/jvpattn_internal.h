@@ -54,6 +54,9 @@ extern thread_local int g_last_hip_error;
 // Workspace of jvpattn_bwd: four float32 arrays of B*H*Nq (see jvpattn_bwd.hip).
 int64_t bwd_workspace_bytes(int64_t rows_q);
 
+// Compute units of the current device (queried once per device), or 0.
+int cu_count();
+
 // Grid of the kernels that walk their blocks (several per workgroup): the
 // cap set by jvpattn_set_workgroups, else one workgroup per CU of the current
 // device; rounded down to a multiple of 8 (so each workgroup keeps its XCD)
