@@ -189,6 +189,24 @@ def _tensor(name, t, shape, dtype, device, optional=False):
 
 MASK_KINDS = {"bool": JVPATTN_MASK_BOOL, "additive": JVPATTN_MASK_ADDITIVE, "bits": JVPATTN_MASK_BITS}
 
+# Mask-free parameter blocks of the library calls below, by (q shape, k shape, dtype, causal, scale):
+# built once by make_params, then only read (the library takes them as const), so repeated calls on
+# the same shapes skip rebuilding them. make_params itself always returns a fresh block.
+_PARAMS = {}
+
+
+def _params(q, k, mask, causal, scale, mask_kind):
+    if mask is None and mask_kind is None and type(q) is torch.Tensor and type(k) is torch.Tensor:
+        key = (q.shape, k.shape, q.dtype, bool(causal), scale)
+        p = _PARAMS.get(key)
+        if p is None:
+            p, _ = make_params(q, k, None, causal, scale, None)
+            if len(_PARAMS) >= 256:
+                _PARAMS.clear()
+            _PARAMS[key] = p
+        return p, None
+    return make_params(q, k, mask, causal, scale, mask_kind)
+
 
 def make_params(q, k, mask=None, causal=False, scale=None, mask_kind=None) -> tuple:
     """Fill jvpattn_params from tensors. Returns (params, mask tensor as passed to the library).
@@ -256,8 +274,24 @@ def make_params(q, k, mask=None, causal=False, scale=None, mask_kind=None) -> tu
     return p, mask
 
 
+def _all_like(ts, shape, dtype, device) -> bool:
+    """Quick test that every tensor of ts (None allowed) is a plain tensor of this shape, dtype and
+    device, contiguous; False sends the caller to the per-tensor checks, which name the problem."""
+    for t in ts:
+        if t is None:
+            continue
+        if type(t) is not torch.Tensor or t.shape != shape or t.dtype != dtype or t.device != device \
+                or not t.is_contiguous():
+            return False
+    return True
+
+
 def _check_inputs(q, k, v, tq, tk, tv):
     """q, k, v (and the tangents present) consistent with each other, on q's GPU, contiguous."""
+    if type(q) is torch.Tensor and type(k) is torch.Tensor and q.dim() == 4 and k.dim() == 4:
+        dt, dev = q.dtype, q.device
+        if _all_like((q, tq), q.shape, dt, dev) and _all_like((k, v, tk, tv), k.shape, dt, dev):
+            return
     if not isinstance(q, torch.Tensor):
         raise TypeError("q must be a tensor")
     if q.dim() != 4:
@@ -315,7 +349,7 @@ def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, sca
     """
     lib = load_library()
     _check_inputs(q, k, v, tq, tk, tv)
-    p, mask = make_params(q, k, mask, causal, scale, mask_kind)
+    p, mask = _params(q, k, mask, causal, scale, mask_kind)
     if tmask is not None:
         mask, tmask = _tmask_like(tmask, p, mask)
     stats = tuple(q.shape[:3])
@@ -326,10 +360,13 @@ def jvpattn_fwd(q, k, v, tq=None, tk=None, tv=None, mask=None, causal=False, sca
         tlse = torch.empty_like(lse) if want_tlse else None
     else:
         o, to, lse, tlse = out
-        _tensor("o", o, q.shape, q.dtype, q.device)
-        _tensor("to", to, q.shape, q.dtype, q.device)
-        _tensor("lse", lse, stats, torch.float32, q.device)
-        _tensor("tlse", tlse, stats, torch.float32, q.device, optional=True)
+        if not (o is not None and to is not None and lse is not None
+                and _all_like((o, to), q.shape, q.dtype, q.device)
+                and _all_like((lse, tlse), stats, torch.float32, q.device)):
+            _tensor("o", o, q.shape, q.dtype, q.device)
+            _tensor("to", to, q.shape, q.dtype, q.device)
+            _tensor("lse", lse, stats, torch.float32, q.device)
+            _tensor("tlse", tlse, stats, torch.float32, q.device, optional=True)
     _require_gpu(q)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     if tmask is not None:
@@ -398,7 +435,7 @@ def jvpattn_bwd(q, k, v, tq, tk, tv, o, to, lse, tlse, go, gto, mask=None, causa
     _tensor("tlse", tlse, stats, torch.float32, dev)
     _tensor("go", go, q.shape, q.dtype, dev, optional=True)
     _tensor("gto", gto, q.shape, q.dtype, dev, optional=True)
-    p, mask = make_params(q, k, mask, causal, scale, mask_kind)
+    p, mask = _params(q, k, mask, causal, scale, mask_kind)
     if tmask is not None:
         mask, tmask = _tmask_like(tmask, p, mask)
     if out is None:
