@@ -16,11 +16,15 @@
 // float64 oracle runs those steps one at a time; the two agree to rounding).
 // The N x N matrices are never stored: three kernels recompute them per tile.
 //   rows: per query row r, del and -lse*log2(e) and tlse into the workspace;
-//   dkv:  one workgroup per 128 keys, looping over 32-query tiles;
-//   dq:   one workgroup per 128 queries, looping over 32-key tiles.
+//   dkv:  128 keys (of one K/V head) per work item, looping over 32-query
+//         tiles (at d = 64 without a mask, one workgroup per CU walks
+//         several items);
+//   dq:   128 queries per workgroup, looping over 32-key tiles (large d = 64
+//         grids: two workgroups per CU, without the software pipeline).
 // Both tile kernels use the forward's MFMA layout (32x32x16 products, C
 // registers rounded to 16 bits reused as B operands, transpose reads of the
-// LDS tiles for the accumulating products).
+// LDS tiles for the accumulating products). They depend only on the rows
+// kernel, so the query side may run on a second stream beside the key side.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
