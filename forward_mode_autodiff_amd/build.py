@@ -27,9 +27,9 @@ ARCH = "gfx950"
 MASK_KINDS = {"none": 0, "bool": 1, "add": 2, "bits": 3, "addt": 4}
 SOURCES = [("jvpattn_fwd.hip", "jvpattn_fwd", []), ("jvpattn_bwd.hip", "jvpattn_bwd", []),
            ("jvpattn_check.cpp", "jvpattn_check", [])] + [
-    ("jvpattn_fwd_inst.hip", f"jvpattn_fwd_{name}_{'causal' if c else 'full'}",
-     [f"-DJVPATTN_INST_MASK={kind}", f"-DJVPATTN_INST_CAUSAL={c}"])
-    for name, kind in MASK_KINDS.items() for c in (1, 0)] + [
+    ("jvpattn_fwd_inst.hip", f"jvpattn_fwd_{fam}{name}_{'causal' if c else 'full'}",
+     [f"-DJVPATTN_INST_MASK={kind}", f"-DJVPATTN_INST_CAUSAL={c}", f"-DJVPATTN_INST_FAMILY={f}"])
+    for f, fam in ((0, ""), (1, "s64_")) for name, kind in MASK_KINDS.items() for c in (1, 0)] + [
     ("jvpattn_bwd_inst.hip", f"jvpattn_bwd_d{d}_{side}", [f"-DJVPATTN_BWD_D={d}", f"-DJVPATTN_BWD_PART={part}"])
     for d in (64, 128) for part, side in ((0, "dkv"), (1, "dq"))]
 
@@ -57,11 +57,14 @@ VGPR_FORM_OBJECTS = ("jvpattn_fwd", "jvpattn_bwd_d64", "jvpattn_bwd_d128_dq")
 # d = 64 objects and d = 128 query side: 2-16% faster per 16-bit call (most
 # with masks), the same bits. It makes the masked d = 64 key-side and the
 # float32 instances keep 20-56 bytes per lane in scratch, and the masked ones
-# still measured faster; float32 without a mask is ~4% slower. The forward
-# keeps the default strategy: under this one its 128-row split instances with
-# a mask spill 100-270 bytes and run up to 30% slower.
+# still measured faster; float32 without a mask is ~4% slower. In the forward
+# it suits only the 64-row split kernel with a bool or additive mask and no
+# causal limit (2-5% faster; its own objects): with a causal limit it changed
+# nothing or cost 1%, the 128-row split instances with a mask spill 100-270
+# bytes under it and run up to 30% slower, and the mask-free kernels gain
+# nothing.
 ILP_SCHED = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
-ILP_SCHED_OBJECTS = ("jvpattn_bwd_d64", "jvpattn_bwd_d128_dq")
+ILP_SCHED_OBJECTS = ("jvpattn_bwd_d64", "jvpattn_bwd_d128_dq", "jvpattn_fwd_s64_bool_full", "jvpattn_fwd_s64_add_full")
 
 
 def _compile(job, verbose: bool) -> str:

@@ -1846,14 +1846,12 @@ hipError_t launch_pp(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipSt
   return hipGetLastError();
 }
 
-// The 4-wave kernel for d = 64: whole key range (split = 0), halves over two
-// groups of four waves (split = 1), or halves over two groups of two waves on
-// 64-row blocks (split = 2).
+// The 4-wave kernel for d = 64: whole key range (split = 0), or halves over
+// two groups of four waves (split = 1). Halves over two groups of two waves on
+// 64-row blocks (split = 2) go to launch_fwd_split64.
 template <typename T, int MASK, bool CAUSAL, bool POW2>
 void launch_d64(int split, const FwdArgs& args, dim3 grid, hipStream_t stream) {
-  if (split == 2)
-    hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 2, 2>), grid, dim3(2 * 128), 0, stream, args);
-  else if (split == 1)
+  if (split == 1)
     hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 2, 4>), grid, dim3(2 * kThreads), 0, stream, args);
   else
     hipLaunchKernelGGL((fwd16_kernel<T, 64, MASK, CAUSAL, POW2, 1, 4>), grid, dim3(kThreads), 0, stream, args);
@@ -1873,6 +1871,8 @@ hipError_t launch_typed(int dtype, int d, bool pow2, int split, const FwdArgs& a
     }
     return hipGetLastError();
   }
+  if (d == 64 && split == 2 && dtype != JVPATTN_F32)
+    return launch_fwd_split64<MASK, CAUSAL>(dtype, pow2, args, grid, stream);
   if (dtype == JVPATTN_BF16) {
     if (pow2) {
       if (d == 64) launch_d64<BF16, MASK, CAUSAL, true>(split, args, grid, stream);
@@ -1905,6 +1905,21 @@ hipError_t launch_typed(int dtype, int d, bool pow2, int split, const FwdArgs& a
 }
 
 }  // namespace
+
+#if defined(JVPATTN_INST_FAMILY) && JVPATTN_INST_FAMILY == 1
+template <int MASK, bool CAUSAL>
+hipError_t launch_fwd_split64(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
+  const dim3 block(2 * 128);
+  if (dtype == JVPATTN_BF16) {
+    if (pow2) hipLaunchKernelGGL((fwd16_kernel<BF16, 64, MASK, CAUSAL, true, 2, 2>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16_kernel<BF16, 64, MASK, CAUSAL, false, 2, 2>), grid, block, 0, stream, args);
+  } else {
+    if (pow2) hipLaunchKernelGGL((fwd16_kernel<F16, 64, MASK, CAUSAL, true, 2, 2>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16_kernel<F16, 64, MASK, CAUSAL, false, 2, 2>), grid, block, 0, stream, args);
+  }
+  return hipGetLastError();
+}
+#endif
 
 // Launch the forward kernel `kernel` (FwdKernel) for this mask kind and causal
 // flag; the element type, head dimension and power-of-two scale select the

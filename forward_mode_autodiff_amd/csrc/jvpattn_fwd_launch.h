@@ -63,4 +63,10 @@ struct FwdArgs {
 template <int MASK, bool CAUSAL>
 hipError_t launch_fwd(int kernel, int dtype, int d, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream);
 
+// The 64-row split kernel (d = 64, 16-bit: two groups of two waves), which
+// launch_fwd hands over to; built in objects of its own, one per mask kind and
+// causal flag, so that they can take compiler flags of their own.
+template <int MASK, bool CAUSAL>
+hipError_t launch_fwd_split64(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream);
+
 }  // namespace jvpattn
