@@ -53,18 +53,19 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 # object builds without it: the compiler fails on two of its instances.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 VGPR_FORM_OBJECTS = ("jvpattn_fwd", "jvpattn_bwd_d64", "jvpattn_bwd_d128_dq")
-# The compiler's iterative ILP scheduling strategy for the reverse pass's
-# d = 64 objects and d = 128 query side: 2-16% faster per 16-bit call (most
-# with masks), the same bits. It makes the masked d = 64 key-side and the
-# float32 instances keep 20-56 bytes per lane in scratch, and the masked ones
-# still measured faster; float32 without a mask is ~4% slower. In the forward
+# The compiler's iterative ILP scheduling strategy for the reverse pass (every
+# object): 2-16% faster per 16-bit call (most with masks), the same bits. It
+# makes the masked d = 64 key-side and the float32 instances keep 20-56 bytes
+# per lane in scratch (the masked d = 128 key side 276-280 instead of
+# 188-304), and the masked ones still measured faster; float32 without a mask
+# is ~4% slower. In the forward
 # it suits only the 64-row split kernel with a bool or additive mask and no
 # causal limit (2-5% faster; its own objects): with a causal limit it changed
 # nothing or cost 1%, the 128-row split instances with a mask spill 100-270
 # bytes under it and run up to 30% slower, and the mask-free kernels gain
 # nothing.
 ILP_SCHED = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
-ILP_SCHED_OBJECTS = ("jvpattn_bwd_d64", "jvpattn_bwd_d128_dq", "jvpattn_fwd_s64_bool_full", "jvpattn_fwd_s64_add_full")
+ILP_SCHED_OBJECTS = ("jvpattn_bwd_d64", "jvpattn_bwd_d128", "jvpattn_fwd_s64_bool_full", "jvpattn_fwd_s64_add_full")
 
 
 def _compile(job, verbose: bool) -> str:
