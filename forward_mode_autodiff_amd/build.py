@@ -29,7 +29,7 @@ SOURCES = [("jvpattn_fwd.hip", "jvpattn_fwd", []), ("jvpattn_bwd.hip", "jvpattn_
            ("jvpattn_check.cpp", "jvpattn_check", [])] + [
     ("jvpattn_fwd_inst.hip", f"jvpattn_fwd_{fam}{name}_{'causal' if c else 'full'}",
      [f"-DJVPATTN_INST_MASK={kind}", f"-DJVPATTN_INST_CAUSAL={c}", f"-DJVPATTN_INST_FAMILY={f}"])
-    for f, fam in ((0, ""), (1, "s64_")) for name, kind in MASK_KINDS.items() for c in (1, 0)] + [
+    for f, fam in ((0, ""), (1, "s64_"), (2, "pp_")) for name, kind in MASK_KINDS.items() for c in (1, 0)] + [
     ("jvpattn_bwd_inst.hip", f"jvpattn_bwd_d{d}_{side}", [f"-DJVPATTN_BWD_D={d}", f"-DJVPATTN_BWD_PART={part}"])
     for d in (64, 128) for part, side in ((0, "dkv"), (1, "dq"))]
 
@@ -59,13 +59,15 @@ VGPR_FORM_OBJECTS = ("jvpattn_fwd", "jvpattn_bwd_d64", "jvpattn_bwd_d128_dq")
 # per lane in scratch (the masked d = 128 key side 276-280 instead of
 # 188-304), and the masked ones still measured faster; float32 without a mask
 # is ~4% slower. In the forward
-# it suits only the 64-row split kernel with a bool or additive mask and no
-# causal limit (2-5% faster; its own objects): with a causal limit it changed
-# nothing or cost 1%, the 128-row split instances with a mask spill 100-270
+# it suits the ping-pong kernel with a bool or additive mask (1-4% faster, no
+# scratch) and the 64-row split kernel with one and no causal limit (2-5%),
+# each in objects of their own: the 64-row split with a causal limit changed
+# nothing or lost 1%, the 128-row split instances with a mask spill 100-270
 # bytes under it and run up to 30% slower, and the mask-free kernels gain
 # nothing.
 ILP_SCHED = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
-ILP_SCHED_OBJECTS = ("jvpattn_bwd_d64", "jvpattn_bwd_d128", "jvpattn_fwd_s64_bool_full", "jvpattn_fwd_s64_add_full")
+ILP_SCHED_OBJECTS = ("jvpattn_bwd_d64", "jvpattn_bwd_d128", "jvpattn_fwd_s64_bool_full", "jvpattn_fwd_s64_add_full",
+                     "jvpattn_fwd_pp_bool_", "jvpattn_fwd_pp_add_")
 
 
 def _compile(job, verbose: bool) -> str:

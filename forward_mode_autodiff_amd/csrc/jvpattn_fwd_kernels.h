@@ -1833,19 +1833,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd32_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------- dispatch
 
-template <int MASK, bool CAUSAL>
-hipError_t launch_pp(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
-  const dim3 block(kPPThreads);
-  if (dtype == JVPATTN_BF16) {
-    if (pow2) hipLaunchKernelGGL((fwd16pp_kernel<BF16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
-    else hipLaunchKernelGGL((fwd16pp_kernel<BF16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
-  } else {
-    if (pow2) hipLaunchKernelGGL((fwd16pp_kernel<F16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
-    else hipLaunchKernelGGL((fwd16pp_kernel<F16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
-  }
-  return hipGetLastError();
-}
-
 // The 4-wave kernel for d = 64: whole key range (split = 0), or halves over
 // two groups of four waves (split = 1). Halves over two groups of two waves on
 // 64-row blocks (split = 2) go to launch_fwd_split64.
@@ -1906,6 +1893,21 @@ hipError_t launch_typed(int dtype, int d, bool pow2, int split, const FwdArgs& a
 
 }  // namespace
 
+#if defined(JVPATTN_INST_FAMILY) && JVPATTN_INST_FAMILY == 2
+template <int MASK, bool CAUSAL>
+hipError_t launch_fwd_pp(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
+  const dim3 block(kPPThreads);
+  if (dtype == JVPATTN_BF16) {
+    if (pow2) hipLaunchKernelGGL((fwd16pp_kernel<BF16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16pp_kernel<BF16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+  } else {
+    if (pow2) hipLaunchKernelGGL((fwd16pp_kernel<F16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16pp_kernel<F16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+  }
+  return hipGetLastError();
+}
+#endif
+
 #if defined(JVPATTN_INST_FAMILY) && JVPATTN_INST_FAMILY == 1
 template <int MASK, bool CAUSAL>
 hipError_t launch_fwd_split64(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
@@ -1926,7 +1928,7 @@ hipError_t launch_fwd_split64(int dtype, bool pow2, const FwdArgs& args, dim3 gr
 // instance. Arguments were validated and planned by the caller.
 template <int MASK, bool CAUSAL>
 hipError_t launch_fwd(int kernel, int dtype, int d, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
-  if (kernel == kFwdPingPong) return launch_pp<MASK, CAUSAL>(dtype, pow2, args, grid, stream);
+  if (kernel == kFwdPingPong) return launch_fwd_pp<MASK, CAUSAL>(dtype, pow2, args, grid, stream);
   const int split = kernel == kFwdSplit ? 1 : kernel == kFwdSplit64 ? 2 : 0;
   return launch_typed<MASK, CAUSAL>(dtype, d, pow2, split, args, grid, stream);
 }

@@ -69,4 +69,8 @@ hipError_t launch_fwd(int kernel, int dtype, int d, bool pow2, const FwdArgs& ar
 template <int MASK, bool CAUSAL>
 hipError_t launch_fwd_split64(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream);
 
+// The ping-pong kernel (d = 64, 16-bit), likewise in objects of its own.
+template <int MASK, bool CAUSAL>
+hipError_t launch_fwd_pp(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream);
+
 }  // namespace jvpattn
