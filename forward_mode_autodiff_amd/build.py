@@ -29,7 +29,8 @@ SOURCES = [("jvpattn_fwd.hip", "jvpattn_fwd", []), ("jvpattn_bwd.hip", "jvpattn_
            ("jvpattn_check.cpp", "jvpattn_check", [])] + [
     ("jvpattn_fwd_inst.hip", f"jvpattn_fwd_{fam}{name}_{'causal' if c else 'full'}",
      [f"-DJVPATTN_INST_MASK={kind}", f"-DJVPATTN_INST_CAUSAL={c}", f"-DJVPATTN_INST_FAMILY={f}"])
-    for f, fam in ((0, ""), (1, "s64_"), (2, "pp_")) for name, kind in MASK_KINDS.items() for c in (1, 0)] + [
+    for f, fam in ((0, ""), (1, "s64_"), (2, "pp_"), (3, "w128_"), (4, "w256_")) for name, kind in MASK_KINDS.items()
+    for c in (1, 0)] + [
     ("jvpattn_bwd_inst.hip", f"jvpattn_bwd_d{d}_{side}", [f"-DJVPATTN_BWD_D={d}", f"-DJVPATTN_BWD_PART={part}"])
     for d in (64, 128) for part, side in ((0, "dkv"), (1, "dq"))]
 
@@ -63,11 +64,13 @@ VGPR_FORM_OBJECTS = ("jvpattn_fwd", "jvpattn_bwd_d64", "jvpattn_bwd_d128_dq")
 # scratch) and the 64-row split kernel with one and no causal limit (2-5%),
 # each in objects of their own: the 64-row split with a causal limit changed
 # nothing or lost 1%, the 128-row split instances with a mask spill 100-270
-# bytes under it and run up to 30% slower, and the mask-free kernels gain
-# nothing.
+# bytes under it and run up to 30% slower. Of the mask-free kernels, the
+# d = 256 one gains 3% (objects of its own), while the 128-row split ones
+# keep 12-108 bytes per lane in scratch and the d = 128 four-wave one loses
+# 1.5%, so those stay at the default schedule.
 ILP_SCHED = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 ILP_SCHED_OBJECTS = ("jvpattn_bwd_d64", "jvpattn_bwd_d128", "jvpattn_fwd_s64_bool_full", "jvpattn_fwd_s64_add_full",
-                     "jvpattn_fwd_pp_bool_", "jvpattn_fwd_pp_add_")
+                     "jvpattn_fwd_pp_bool_", "jvpattn_fwd_pp_add_", "jvpattn_fwd_w256_none_")
 
 
 def _compile(job, verbose: bool) -> str:

@@ -1848,34 +1848,16 @@ template <int MASK, bool CAUSAL>
 hipError_t launch_typed(int dtype, int d, bool pow2, int split, const FwdArgs& args, dim3 grid,
                         hipStream_t stream) {
   const dim3 block(kThreads);
-  if (d == 256) {   // 16-bit only (the check rejects float32)
-    if (dtype == JVPATTN_BF16) {
-      if (pow2) hipLaunchKernelGGL((fwd16w_kernel<BF16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
-      else hipLaunchKernelGGL((fwd16w_kernel<BF16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
-    } else {
-      if (pow2) hipLaunchKernelGGL((fwd16w_kernel<F16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
-      else hipLaunchKernelGGL((fwd16w_kernel<F16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
-    }
-    return hipGetLastError();
-  }
+  if (d == 256) return launch_fwd_d256<MASK, CAUSAL>(dtype, pow2, args, grid, stream);  // 16-bit only
   if (d == 64 && split == 2 && dtype != JVPATTN_F32)
     return launch_fwd_split64<MASK, CAUSAL>(dtype, pow2, args, grid, stream);
+  if (d == 128 && dtype != JVPATTN_F32) return launch_fwd_d128<MASK, CAUSAL>(dtype, pow2, args, grid, stream);
   if (dtype == JVPATTN_BF16) {
-    if (pow2) {
-      if (d == 64) launch_d64<BF16, MASK, CAUSAL, true>(split, args, grid, stream);
-      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, true, 1, 4>), grid, block, 0, stream, args);
-    } else {
-      if (d == 64) launch_d64<BF16, MASK, CAUSAL, false>(split, args, grid, stream);
-      else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, false, 1, 4>), grid, block, 0, stream, args);
-    }
+    if (pow2) launch_d64<BF16, MASK, CAUSAL, true>(split, args, grid, stream);
+    else launch_d64<BF16, MASK, CAUSAL, false>(split, args, grid, stream);
   } else if (dtype == JVPATTN_F16) {
-    if (pow2) {
-      if (d == 64) launch_d64<F16, MASK, CAUSAL, true>(split, args, grid, stream);
-      else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, true, 1, 4>), grid, block, 0, stream, args);
-    } else {
-      if (d == 64) launch_d64<F16, MASK, CAUSAL, false>(split, args, grid, stream);
-      else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, false, 1, 4>), grid, block, 0, stream, args);
-    }
+    if (pow2) launch_d64<F16, MASK, CAUSAL, true>(split, args, grid, stream);
+    else launch_d64<F16, MASK, CAUSAL, false>(split, args, grid, stream);
   } else {
     if (d == 64) {
       hipLaunchKernelGGL((fwd32_kernel<64, MASK, CAUSAL>), grid, block, Tile32<64>::BUF_BYTES, stream, args);
@@ -1892,6 +1874,36 @@ hipError_t launch_typed(int dtype, int d, bool pow2, int split, const FwdArgs& a
 }
 
 }  // namespace
+
+#if defined(JVPATTN_INST_FAMILY) && JVPATTN_INST_FAMILY == 4
+template <int MASK, bool CAUSAL>
+hipError_t launch_fwd_d256(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
+  const dim3 block(kThreads);
+  if (dtype == JVPATTN_BF16) {
+    if (pow2) hipLaunchKernelGGL((fwd16w_kernel<BF16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16w_kernel<BF16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+  } else {
+    if (pow2) hipLaunchKernelGGL((fwd16w_kernel<F16, MASK, CAUSAL, true>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16w_kernel<F16, MASK, CAUSAL, false>), grid, block, 0, stream, args);
+  }
+  return hipGetLastError();
+}
+#endif
+
+#if defined(JVPATTN_INST_FAMILY) && JVPATTN_INST_FAMILY == 3
+template <int MASK, bool CAUSAL>
+hipError_t launch_fwd_d128(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream) {
+  const dim3 block(kThreads);
+  if (dtype == JVPATTN_BF16) {
+    if (pow2) hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, true, 1, 4>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16_kernel<BF16, 128, MASK, CAUSAL, false, 1, 4>), grid, block, 0, stream, args);
+  } else {
+    if (pow2) hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, true, 1, 4>), grid, block, 0, stream, args);
+    else hipLaunchKernelGGL((fwd16_kernel<F16, 128, MASK, CAUSAL, false, 1, 4>), grid, block, 0, stream, args);
+  }
+  return hipGetLastError();
+}
+#endif
 
 #if defined(JVPATTN_INST_FAMILY) && JVPATTN_INST_FAMILY == 2
 template <int MASK, bool CAUSAL>

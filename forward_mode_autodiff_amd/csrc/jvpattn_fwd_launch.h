@@ -69,8 +69,14 @@ hipError_t launch_fwd(int kernel, int dtype, int d, bool pow2, const FwdArgs& ar
 template <int MASK, bool CAUSAL>
 hipError_t launch_fwd_split64(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream);
 
-// The ping-pong kernel (d = 64, 16-bit), likewise in objects of its own.
+// The ping-pong kernel (d = 64, 16-bit), the 4-wave kernel at width 128
+// (d = 96 / 128, 16-bit) and the d = 256 kernel (16-bit), likewise in objects
+// of their own.
 template <int MASK, bool CAUSAL>
 hipError_t launch_fwd_pp(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream);
+template <int MASK, bool CAUSAL>
+hipError_t launch_fwd_d128(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream);
+template <int MASK, bool CAUSAL>
+hipError_t launch_fwd_d256(int dtype, bool pow2, const FwdArgs& args, dim3 grid, hipStream_t stream);
 
 }  // namespace jvpattn
