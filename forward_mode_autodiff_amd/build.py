@@ -64,13 +64,16 @@ VGPR_FORM_OBJECTS = ("jvpattn_fwd", "jvpattn_bwd_d64", "jvpattn_bwd_d128_dq")
 # scratch) and the 64-row split kernel with one and no causal limit (2-5%),
 # each in objects of their own: the 64-row split with a causal limit changed
 # nothing or lost 1%, the 128-row split instances with a mask spill 100-270
-# bytes under it and run up to 30% slower. Of the mask-free kernels, the
-# d = 256 one gains 3% (objects of its own), while the 128-row split ones
-# keep 12-108 bytes per lane in scratch and the d = 128 four-wave one loses
-# 1.5%, so those stay at the default schedule.
+# bytes under it and run up to 30% slower. The d = 256 kernel gains 3%
+# without a mask and 4-10% with one (objects of its own; with a mask tangent
+# it would keep 20 bytes per lane in scratch and stays as it is), while the
+# mask-free 128-row split instances keep 12-108 bytes per lane in scratch
+# and the d = 128 four-wave kernel loses 1.5% without a mask and moves
+# within +-2% with one, so those stay at the default schedule.
 ILP_SCHED = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 ILP_SCHED_OBJECTS = ("jvpattn_bwd_d64", "jvpattn_bwd_d128", "jvpattn_fwd_s64_bool_full", "jvpattn_fwd_s64_add_full",
-                     "jvpattn_fwd_pp_bool_", "jvpattn_fwd_pp_add_", "jvpattn_fwd_w256_none_")
+                     "jvpattn_fwd_pp_bool_", "jvpattn_fwd_pp_add_", "jvpattn_fwd_w256_none_",
+                     "jvpattn_fwd_w256_bool_", "jvpattn_fwd_w256_add_", "jvpattn_fwd_w256_bits_")
 
 
 def _compile(job, verbose: bool) -> str:
