@@ -69,8 +69,12 @@ VGPR_FORM_OBJECTS = ("jvpattn_fwd", "jvpattn_bwd_d64", "jvpattn_bwd_d128_dq")
 # it would keep 20 bytes per lane in scratch and stays as it is), while the
 # mask-free 128-row split instances keep 12-108 bytes per lane in scratch
 # and the d = 128 four-wave kernel loses 1.5% without a mask and moves
-# within +-2% with one, so those stay at the default schedule.
+# within +-2% with one, so those stay at the default schedule; without a
+# mask that kernel takes the max-ILP strategy instead (2% faster at
+# (4,16,2048,128), 0.3% at (256,8,512,128), the same bits).
 ILP_SCHED = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+MAX_ILP_SCHED = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+MAX_ILP_SCHED_OBJECTS = ("jvpattn_fwd_w128_none_",)
 ILP_SCHED_OBJECTS = ("jvpattn_bwd_d64", "jvpattn_bwd_d128", "jvpattn_fwd_s64_bool_full", "jvpattn_fwd_s64_add_full",
                      "jvpattn_fwd_pp_bool_", "jvpattn_fwd_pp_add_", "jvpattn_fwd_w256_none_",
                      "jvpattn_fwd_w256_bool_", "jvpattn_fwd_w256_add_", "jvpattn_fwd_w256_bits_")
@@ -82,7 +86,8 @@ def _compile(job, verbose: bool) -> str:
     cmd = [hipcc(), *COMMON, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = (["-x", "hip"] + DEVICE + (VGPR_FORM if name.startswith(VGPR_FORM_OBJECTS) else [])
-                    + (ILP_SCHED if name.startswith(ILP_SCHED_OBJECTS) else []))
+                    + (ILP_SCHED if name.startswith(ILP_SCHED_OBJECTS) else [])
+                    + (MAX_ILP_SCHED if name.startswith(MAX_ILP_SCHED_OBJECTS) else []))
     else:
         cmd[1:1] = ["-x", "c++"]
     if verbose:
